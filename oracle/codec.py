@@ -1,0 +1,261 @@
+"""CPU oracle of the lossless BF16 KV-cache format.
+
+TEST INFRASTRUCTURE ONLY: tests/, __graft_entry__.smoke() and bench.py's cpu_baseline leg
+may import this package; the library under decode_attention_losslessly_amd/ never does.
+It shares no code, constants or helpers with the HIP path.
+
+What the pages fix (ZipFusion: Fusing Lossless KV Decompression with Attention, the
+paperlayer.ai summary):
+  * §II.A "KV Cache and BF16": a BF16 value is 1 sign, 8 exponent and 7 fraction bits, and a
+    lossless format preserves every value's bit pattern.
+  * §III.B "Lossless KV Cache Format": values keep their sign and fraction information, the
+    exponent is coded as an offset from a per-block base, and the original bits come back
+    exactly with no floating-point rounding.
+  * §III.C "Attention over the Compressed KV Cache": the values are rebuilt with plain
+    integer bit operations.
+The layout itself is this repository's (the pages' own 12-bit layout is prior art):
+
+  group      the 64 values of one token row of one head, dims [64g, 64g + 64)
+  sm byte    (sign << 7) | mantissa, stored for every value, escaped or not
+  base b     of a group: among the group's own exponents, the one that maximises
+             cov(c) = #{j : 0 <= e_j - c <= 14}; ties go to the smallest exponent
+  offset     e - b when 0 <= e - b <= 14, else 15 = escape; an escaped value's 16 raw bits
+             go to the block's escape list
+  tile       16 consecutive tokens of a page (P is a multiple of 16)
+  storage    K: position tok*D + d inside a tile (token-major)
+  order      V: position d*16 + tok inside a tile (dim-major)
+  block      the P x D values of one page, one head, one of K / V: for each tile, its
+             16*D sm bytes in storage order, then 2*D little-endian u32 offset words;
+             word w holds positions 8w..8w+7 with position 8w+2k in bits 4k..4k+3 and
+             position 8w+2k+1 in bits 16+4k..16+4k+3
+  escapes    a block's escaped values in storage order (tiles in order)
+  unit       one (page, KV head): meta region, then the K block, then the V block
+  meta       [0, P*G)          K bases, byte t*16G + g*16 + tok for tile t
+             [P*G, 2P*G)       V bases, same order
+             [2PG, 2PG+4)      u32 number of K escapes
+             [2PG+4, 2PG+8)    u32 number of V escapes
+             [2PG+8, 2PG+16)   u64 escape-pool offset in u16 elements, or all ones when the
+                               escapes are inline
+             [2PG+16, MR)      inline escapes (K's then V's) when they fit, else zero
+             MR = round_up(2PG + 16, 128)
+"""
+from __future__ import annotations
+
+import numpy as np
+
+GROUP = 64
+TILE = 16
+ESCAPE = 15
+MAX_OFFSET = 14
+INLINE = 0xFFFF_FFFF_FFFF_FFFF
+K_KIND, V_KIND = 0, 1
+
+
+# ---------------------------------------------------------------- BF16 fields (§II.A)
+def exponent(x: np.ndarray) -> np.ndarray:
+    return ((np.asarray(x, np.uint16) >> 7) & 0xFF).astype(np.int32)
+
+
+def sm_byte(x: np.ndarray) -> np.ndarray:
+    x = np.asarray(x, np.uint16)
+    return (((x >> 8) & 0x80) | (x & 0x7F)).astype(np.uint8)
+
+
+def rebuild(sm: np.ndarray, e: np.ndarray) -> np.ndarray:
+    """BF16 bits from an sm byte and an 8-bit exponent: sign, exponent, mantissa."""
+    sm = np.asarray(sm, np.uint16)
+    e = np.asarray(e, np.uint16)
+    return (((sm & 0x80) << 8) | (e << 7) | (sm & 0x7F)).astype(np.uint16)
+
+
+# ---------------------------------------------------------------- group codec
+def coverage(exps: np.ndarray) -> np.ndarray:
+    """cov[..., i] = number of j with 0 <= e_j - e_i <= 14, for a [..., 64] exponent array."""
+    d = exps[..., None, :] - exps[..., :, None]          # d[..., i, j] = e_j - e_i
+    return ((d >= 0) & (d <= MAX_OFFSET)).sum(axis=-1)
+
+
+def choose_bases(exps: np.ndarray) -> np.ndarray:
+    """Base per group: the group exponent of largest coverage, smallest on ties."""
+    exps = np.asarray(exps, np.int32)
+    flat = exps.reshape(-1, GROUP)
+    out = np.empty(flat.shape[0], np.int32)
+    step = 4096
+    for s in range(0, flat.shape[0], step):
+        e = flat[s:s + step]
+        cov = coverage(e)
+        best = cov.max(axis=-1, keepdims=True)
+        cand = np.where(cov == best, e, 256)              # exponents reaching the best coverage
+        out[s:s + step] = cand.min(axis=-1)
+    return out.reshape(exps.shape[:-1])
+
+
+def offsets(exps: np.ndarray, bases: np.ndarray) -> np.ndarray:
+    d = np.asarray(exps, np.int32) - np.asarray(bases, np.int32)[..., None]
+    return np.where((d >= 0) & (d <= MAX_OFFSET), d, ESCAPE).astype(np.uint8)
+
+
+def encode_group(x: np.ndarray):
+    """One group of 64 BF16 values -> (base, offsets[64], sm[64], escaped values in order)."""
+    x = np.asarray(x, np.uint16)
+    assert x.shape == (GROUP,)
+    e = exponent(x)
+    b = int(choose_bases(e[None])[0])
+    off = offsets(e, np.int32(b))
+    return b, off, sm_byte(x), x[off == ESCAPE].copy()
+
+
+def decode_group(base: int, off: np.ndarray, sm: np.ndarray, escapes: np.ndarray) -> np.ndarray:
+    off = np.asarray(off, np.int32)
+    out = rebuild(sm, (base + np.minimum(off, MAX_OFFSET)) & 0xFF)
+    esc = off == ESCAPE
+    assert int(esc.sum()) == len(escapes)
+    out[esc] = np.asarray(escapes, np.uint16)
+    return out
+
+
+# ---------------------------------------------------------------- storage order
+def storage_order(P: int, D: int, kind: int) -> np.ndarray:
+    """Flat [P*D] token-major index of each storage position of a block, in storage order."""
+    idx = np.arange(P * D).reshape(P, D)
+    parts = []
+    for t in range(P // TILE):
+        tile = idx[t * TILE:(t + 1) * TILE]
+        parts.append(tile.reshape(-1) if kind == K_KIND else tile.T.reshape(-1))
+    return np.concatenate(parts)
+
+
+def pack_offsets(off: np.ndarray) -> np.ndarray:
+    """Offsets of consecutive storage positions -> little-endian u32 words (8 per word)."""
+    o = np.asarray(off, np.uint32).reshape(-1, 8)
+    w = np.zeros(o.shape[0], np.uint32)
+    for k in range(4):
+        w |= o[:, 2 * k] << np.uint32(4 * k)
+        w |= o[:, 2 * k + 1] << np.uint32(16 + 4 * k)
+    return w
+
+
+def unpack_offsets(words: np.ndarray) -> np.ndarray:
+    w = np.asarray(words, np.uint32)
+    o = np.zeros((w.shape[0], 8), np.uint8)
+    for k in range(4):
+        o[:, 2 * k] = (w >> np.uint32(4 * k)) & 0xF
+        o[:, 2 * k + 1] = (w >> np.uint32(16 + 4 * k)) & 0xF
+    return o.reshape(-1)
+
+
+def block_bytes(P: int, D: int) -> int:
+    return (P * D) + (P * D) // 2
+
+
+def meta_bytes(P: int, D: int) -> int:
+    used = 2 * P * (D // GROUP) + 16
+    return (used + 127) // 128 * 128
+
+
+def inline_capacity(P: int, D: int) -> int:
+    return (meta_bytes(P, D) - 2 * P * (D // GROUP) - 16) // 2
+
+
+def unit_bytes(P: int, D: int) -> int:
+    return meta_bytes(P, D) + 2 * block_bytes(P, D)
+
+
+def encode_block(X: np.ndarray, kind: int):
+    """Block [P][D] BF16 bits -> (base bytes [P*G], block payload bytes, escapes u16)."""
+    X = np.asarray(X, np.uint16)
+    P, D = X.shape
+    G = D // GROUP
+    e = exponent(X).reshape(P, G, GROUP)
+    base = choose_bases(e)                                   # [P][G]
+    off = offsets(e, base).reshape(P, D)
+    sm = sm_byte(X)
+    order = storage_order(P, D, kind)
+    sm_s, off_s, x_s = sm.reshape(-1)[order], off.reshape(-1)[order], X.reshape(-1)[order]
+    payload, per_tile = [], TILE * D
+    for t in range(P // TILE):
+        sl = slice(t * per_tile, (t + 1) * per_tile)
+        payload.append(sm_s[sl])
+        payload.append(pack_offsets(off_s[sl]).astype('<u4').view(np.uint8))
+    bases = np.concatenate([base[t * TILE:(t + 1) * TILE].T.reshape(-1) for t in range(P // TILE)])
+    return bases.astype(np.uint8), np.concatenate(payload), x_s[off_s == ESCAPE].copy()
+
+
+def decode_block(bases: np.ndarray, payload: np.ndarray, escapes: np.ndarray, P: int, D: int,
+                 kind: int) -> np.ndarray:
+    G = D // GROUP
+    per_tile = TILE * D
+    sm_s, off_s = [], []
+    for t in range(P // TILE):
+        chunk = payload[t * (per_tile + per_tile // 2):(t + 1) * (per_tile + per_tile // 2)]
+        sm_s.append(chunk[:per_tile])
+        off_s.append(unpack_offsets(chunk[per_tile:].view('<u4')))
+    sm_s, off_s = np.concatenate(sm_s), np.concatenate(off_s)
+    base = np.empty((P, G), np.int32)
+    for t in range(P // TILE):
+        base[t * TILE:(t + 1) * TILE] = bases[t * TILE * G:(t + 1) * TILE * G].reshape(G, TILE).T
+    order = storage_order(P, D, kind)
+    tok, dim = order // D, order % D
+    b_s = base[tok, dim // GROUP]
+    x_s = rebuild(sm_s, (b_s + np.minimum(off_s, MAX_OFFSET)) & 0xFF)
+    esc = off_s == ESCAPE
+    assert int(esc.sum()) == len(escapes)
+    x_s[esc] = escapes
+    X = np.empty(P * D, np.uint16)
+    X[order] = x_s
+    return X.reshape(P, D)
+
+
+def encode_unit(K: np.ndarray, V: np.ndarray, pool_offset: int | None = None):
+    """One (page, head) unit from its K and V blocks [P][D].
+
+    Returns (unit bytes uint8[unit_bytes], escapes that go to the pool: u16, K's then V's).
+    When the escapes do not fit inline they go to the pool at `pool_offset` (0 when None).
+    """
+    P, D = K.shape
+    G = D // GROUP
+    kb, kp, ke = encode_block(K, K_KIND)
+    vb, vp, ve = encode_block(V, V_KIND)
+    meta = np.zeros(meta_bytes(P, D), np.uint8)
+    meta[:P * G] = kb
+    meta[P * G:2 * P * G] = vb
+    h = 2 * P * G
+    meta[h:h + 8] = np.array([len(ke), len(ve)], '<u4').view(np.uint8)
+    esc = np.concatenate([ke, ve]).astype(np.uint16)
+    if len(esc) <= inline_capacity(P, D):
+        meta[h + 8:h + 16] = np.array([INLINE], '<u8').view(np.uint8)
+        meta[h + 16:h + 16 + 2 * len(esc)] = esc.astype('<u2').view(np.uint8)
+        pool = np.zeros(0, np.uint16)
+    else:
+        meta[h + 8:h + 16] = np.array([pool_offset or 0], '<u8').view(np.uint8)
+        pool = esc
+    return np.concatenate([meta, kp, vp]), pool
+
+
+def unit_header(unit: np.ndarray, P: int, D: int):
+    """(K escape count, V escape count, pool offset or INLINE)."""
+    h = 2 * P * (D // GROUP)
+    kc, vc = np.asarray(unit[h:h + 8]).view('<u4')
+    off = int(np.asarray(unit[h + 8:h + 16]).view('<u8')[0])
+    return int(kc), int(vc), off
+
+
+def unit_escapes(unit: np.ndarray, pool: np.ndarray | None, P: int, D: int):
+    kc, vc, off = unit_header(unit, P, D)
+    if off == INLINE:
+        h = 2 * P * (D // GROUP) + 16
+        esc = np.asarray(unit[h:h + 2 * (kc + vc)]).view('<u2').astype(np.uint16)
+    else:
+        esc = np.asarray(pool[off:off + kc + vc], np.uint16)
+    return esc[:kc], esc[kc:]
+
+
+def decode_unit(unit: np.ndarray, pool: np.ndarray | None, P: int, D: int):
+    """Unit bytes (+ escape pool) -> (K [P][D], V [P][D]) BF16 bits."""
+    unit = np.asarray(unit, np.uint8)
+    G = D // GROUP
+    mb, bb = meta_bytes(P, D), block_bytes(P, D)
+    ke, ve = unit_escapes(unit, pool, P, D)
+    K = decode_block(unit[:P * G], unit[mb:mb + bb], ke, P, D, K_KIND)
+    V = decode_block(unit[P * G:2 * P * G], unit[mb + bb:mb + 2 * bb], ve, P, D, V_KIND)
+    return K, V
