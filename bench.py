@@ -1,0 +1,293 @@
+#!/usr/bin/env python3
+"""Decode attention over a losslessly compressed BF16 KV cache on one MI355X.
+
+Workload (default): 32 requests x 32 heads (one KV head per query head), head_dim 128, 8192
+cached tokens per request plus one appended token (8193), 16-token pages with a shuffled page
+table; K and V ~ N(0, 1) times a per-channel log-uniform scale in [0.1, 10]. Synthetic data.
+
+One step = the decode-attention hot path over that batch: the split kernel (compressed blocks
+rebuilt in registers, split-K partials) and the merge kernel, which is what the pages time for
+attention (ZipFusion summary, §IV.B: attention, fused reconstruction and split merge). Prefill,
+the initial compression and the append are set-up (excluded there too, §IV.A) and are reported
+as separate fields.
+
+Prints one JSON line. `python bench.py --gpus N` with N > 1 exits with a message: this build
+runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0
+WORKLOADS = {3: "mha_ctx8k_b32", 2: "llama7b_b1_ctx4k", 4: "gqa28x4_b64", 5: "escape_stress_ctx32k_b4", 1: "tiny"}
+
+
+def source_digest() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "decode_attention_losslessly_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=3, help="workload number (3 = the headline workload)")
+    ap.add_argument("--no-dense", action="store_true", help="skip the uncompressed baseline")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-requests", type=int, default=32, help="requests in the CPU baseline sample")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only copy MIB MiB device-to-device 5 times (calibrates HBM byte counters) and exit")
+    return ap.parse_args()
+
+
+def main() -> int:
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "this build has no multi-GPU path", file=sys.stderr, flush=True)
+        return 2
+
+    import numpy as np
+    import torch
+
+    dev = torch.device("cuda:0")
+    if args.copy_probe:
+        a = torch.ones(args.copy_probe << 20, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": a.numel(), "launches": 5}), flush=True)
+        return 0
+
+    import decode_attention_losslessly_amd as kvz
+    from synth import make_workload
+
+    log = lambda *a: print("[bench]", *a, file=sys.stderr, flush=True)
+    t16 = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16 if a.dtype == np.uint16 else a.dtype)).to(dev)
+
+    w = make_workload(args.config)
+    B, Hq, H, D, P = w.B, w.Hq, w.Hkv, w.D, w.P
+    t0 = time.perf_counter()
+    kp, vp = w.pages(0), w.pages(1)
+    log(f"workload {w.name}: {w.num_pages} pages generated in {time.perf_counter() - t0:.1f}s")
+
+    # ---- set-up: dense pages on the device, compression of the full pages, tails, append
+    L = w.seq_lens.astype(np.int64)
+    L0 = (w.seq_lens - w.n_append).astype(np.int32)
+    kd, vd = t16(kp), t16(vp)
+    ids = np.array([w.page_table[r, i] for r in range(B) for i in range(int(L0[r]) // P)], np.int32)
+    n_units = len(ids) * H
+    frac = 0.6 if w.k_dist == "log_uniform" else 0.02
+    cache = kvz.Cache.allocate(P, H, D, w.num_pages, B, int(n_units * 2 * P * D * frac) + (1 << 20), device=dev)
+    ids_d = t16(ids)
+    torch.cuda.synchronize()
+    c0 = time.perf_counter()
+    kvz.compress_pages(cache, kd[ids_d.long()], vd[ids_d.long()], ids_d)
+    torch.cuda.synchronize()
+    compress_s = time.perf_counter() - c0
+    tk = np.zeros((B, H, P, D), np.uint16)
+    tv = np.zeros_like(tk)
+    for r in range(B):
+        if L0[r] % P:
+            tk[r], tv[r] = kp[w.page_table[r, L0[r] // P]], vp[w.page_table[r, L0[r] // P]]
+    cache.k_tail.copy_(t16(tk))
+    cache.v_tail.copy_(t16(tv))
+    lens = t16(L0)
+    table = t16(w.page_table)
+    append_us = None
+    if w.n_append:
+        ka, va = t16(w.appended(0)), t16(w.appended(1))
+        torch.cuda.synchronize()
+        a0 = time.perf_counter()
+        kvz.append_token(cache, ka, va, table, lens)
+        torch.cuda.synchronize()
+        append_us = (time.perf_counter() - a0) * 1e6
+    assert np.array_equal(lens.cpu().numpy(), w.seq_lens), "append did not advance the lengths"
+    status = int(cache.status.item())
+    assert status == 0, f"cache status {status}"
+    q = t16(w.q())
+    log(f"compressed {n_units} units in {compress_s * 1e3:.1f} ms")
+
+    # ---- algorithmic bytes of one split-kernel launch
+    U = kvz.unit_bytes(P, D)
+    G = D // 64
+    hdr = 2 * P * G
+    full = (w.seq_lens // P).astype(np.int64)
+    live = np.array([w.page_table[r, i] for r in range(B) for i in range(int(full[r]))], np.int64)
+    heads = cache.units[:, :, hdr:hdr + 16][torch.from_numpy(live).to(dev)].contiguous()
+    cnt = heads[:, :, :8].view(torch.int32).to(torch.int64).sum(-1)
+    off = heads[:, :, 8:16].view(torch.int64).squeeze(-1)
+    pool_esc = int(torch.where(off != -1, cnt, torch.zeros_like(cnt)).sum().item())
+    S = kvz.num_splits(B, Hq, H, D, P, w.max_pages)
+    units_bytes = int(full.sum()) * H * U
+    tail_bytes = int((w.seq_lens % P).sum()) * H * D * 2 * 2
+    small_bytes = int(full.sum()) * H * 4 + B * Hq * D * 2 + B * Hq * S * (D + 2) * 4
+    comp_bytes = units_bytes + 2 * pool_esc + tail_bytes + small_bytes
+    dense_kv_bytes = int(L.sum()) * H * D * 2 * 2
+    dense_bytes = dense_kv_bytes + int(((L + P - 1) // P).sum()) * H * 4 + B * Hq * D * 2 + B * Hq * S * (D + 2) * 4
+
+    ws = torch.empty(kvz.workspace_bytes(B, Hq, H, D, P, w.max_pages), dtype=torch.uint8, device=dev)
+    out = torch.empty((B, Hq, D), dtype=torch.int16, device=dev)
+
+    def run_loop(split_fn, merge_fn, steps):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+               torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        torch.cuda.synchronize()
+        s0 = time.perf_counter()
+        for e0, e1, e2 in ev:
+            e0.record()
+            split_fn()
+            e1.record()
+            merge_fn()
+            e2.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - s0
+        attn = np.array([a.elapsed_time(b) for a, b, _ in ev]) * 1e3
+        merge = np.array([b.elapsed_time(c) for _, b, c in ev]) * 1e3
+        return wall, attn, merge
+
+    c_split = lambda: kvz.decode_attention_splits(q, cache, table, lens, w.sm_scale, ws)
+    c_merge = lambda: kvz.merge_splits(ws, lens, B, Hq, H, D, P, w.max_pages, out)
+    for _ in range(args.warmup):
+        c_split()
+        c_merge()
+    wall, attn_us, merge_us = run_loop(c_split, c_merge, args.steps)
+    ms_per_step = wall / args.steps * 1e3
+    assert int(cache.status.item()) == 0
+
+    # same kernel with the caches flushed before every launch (the pages clear L2, §IV.B)
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    cold = []
+    for _ in range(min(args.steps, 20)):
+        flush.zero_()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        c_split()
+        e1.record()
+        c_merge()
+        torch.cuda.synchronize()
+        cold.append(e0.elapsed_time(e1) * 1e3)
+    cold = np.array(cold)
+    del flush
+
+    dense = None
+    if not args.no_dense:
+        d_split = lambda: kvz.decode_attention_dense_splits(q, kd, vd, table, lens, w.sm_scale, ws)
+        d_merge = lambda: kvz.merge_splits(ws, lens, B, Hq, H, D, P, w.max_pages, out, dense=True)
+        for _ in range(args.warmup):
+            d_split()
+            d_merge()
+        dwall, dattn, dmerge = run_loop(d_split, d_merge, args.steps)
+        dense = dict(ms_per_step=dwall / args.steps * 1e3, attn_us=float(np.median(dattn)),
+                     merge_us=float(np.median(dmerge)), bytes=dense_bytes,
+                     gbps=dense_bytes / (np.mean(dattn) * 1e-6) / 1e9,
+                     pct_peak=100 * dense_bytes / (np.mean(dattn) * 1e-6) / 1e9 / PEAK_HBM_GBPS,
+                     tokens_per_s=B / (dwall / args.steps))
+
+    attn_mean = float(np.mean(attn_us))
+    achieved = comp_bytes / (attn_mean * 1e-6) / 1e9
+    traffic = None
+    tfile = os.path.join(ROOT, "profiles", f"traffic_{w.name}.json")
+    if os.path.exists(tfile):
+        t = json.load(open(tfile))
+        if t.get("source_digest") == source_digest():
+            traffic = t.get("bytes_per_launch")
+    roofline = dict(kernel="attn_mha_kernel<128>" if Hq == H else "attn_gqa_kernel", bound="hbm",
+                    achieved=round(achieved, 1), peak=PEAK_HBM_GBPS, unit="GB/s",
+                    frac=round(achieved / PEAK_HBM_GBPS, 4), traffic=traffic,
+                    algorithmic_bytes_per_launch=comp_bytes, attn_us_mean=round(attn_mean, 2))
+
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(w, kp, vp, min(args.cpu_requests, B), log)
+
+    res = {
+        "metric": "decode-attn tokens/s + compressed HBM GB/s (% peak), 8K ctx batch 32",
+        "value": round(B / (ms_per_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": B, "q_heads": Hq, "kv_heads": H, "head_dim": D,
+                   "context": int(w.seq_lens.max()), "page_size": P, "splits": S, "parallelism": "none (1 GPU)"},
+        "compressed_gbps": round(achieved, 1),
+        "pct_peak_hbm": round(100 * achieved / PEAK_HBM_GBPS, 2),
+        "uncompressed_equiv_gbps": round(dense_kv_bytes / (attn_mean * 1e-6) / 1e9, 1),
+        "attn_us": {"median": round(float(np.median(attn_us)), 2), "p10": round(float(np.percentile(attn_us, 10)), 2),
+                    "p90": round(float(np.percentile(attn_us, 90)), 2), "cold_median": round(float(np.median(cold)), 2)},
+        "merge_us": round(float(np.median(merge_us)), 2),
+        "compressed_bytes": comp_bytes,
+        "dense_kv_bytes": dense_kv_bytes,
+        "compression_ratio": round(comp_bytes / dense_bytes, 4),
+        "pool_escapes": pool_esc,
+        "dense": dense,
+        "speedup_vs_dense": round(dense["ms_per_step"] / ms_per_step, 4) if dense else None,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "append_us": round(append_us, 1) if append_us is not None else None,
+        "compress_gbps_dense_input": round(len(ids) * H * P * D * 4 / compress_s / 1e9, 1),
+        "gpu": f"{torch.cuda.get_device_name(0)} ({torch.cuda.get_device_properties(0).gcnArchName})",
+        "source_digest": source_digest(),
+    }
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+def cpu_baseline(w, kp, vp, n_req, log):
+    """The C oracle (scalar decode of the compressed units + fp64 attention, OpenMP over rows) on
+    the rows of the first n_req requests; scaled to the whole batch."""
+    import numpy as np
+
+    from oracle import c_oracle
+    L = w.seq_lens
+    full = L // w.P
+    reqs = list(range(n_req))
+    ids = np.array([w.page_table[r, i] for r in reqs for i in range(int(full[r]))], np.int32)
+    t0 = time.perf_counter()
+    units_s, pool_s, _ = c_oracle.encode_pages(kp[ids], vp[ids])
+    enc_s = time.perf_counter() - t0
+    # units indexed by physical id as the oracle expects
+    units = np.zeros((w.num_pages, w.Hkv, units_s.shape[2]), np.uint8)
+    units[ids] = units_s
+    tk = np.zeros((w.B, w.Hkv, w.P, w.D), np.uint16)
+    tv = np.zeros_like(tk)
+    for r in reqs:
+        if L[r] % w.P:
+            tk[r], tv[r] = kp[w.page_table[r, L[r] // w.P]], vp[w.page_table[r, L[r] // w.P]]
+    rows = [(r, h) for r in reqs for h in range(w.Hq)]
+    q = w.q()
+    t0 = time.perf_counter()
+    c_oracle.decode_attention_rows(q, units, pool_s, w.page_table, L, tk, tv, w.Hkv, w.P, w.sm_scale, rows)
+    dt = time.perf_counter() - t0
+    threads = c_oracle.num_threads()
+    step_s = dt * (w.B * w.Hq) / len(rows)
+    log(f"cpu oracle: {len(rows)} rows in {dt:.2f}s on {threads} threads (encode set-up {enc_s:.1f}s)")
+    return {"value": round(w.B / step_s, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{len(rows)} of {w.B * w.Hq} (request, head) rows: scalar decode of their compressed "
+                      f"pages + fp64 attention, {dt:.2f}s wall, scaled to the full batch",
+            "cpu_seconds": round(dt * threads, 2)}
+
+
+if __name__ == "__main__":
+    sys.exit(main())

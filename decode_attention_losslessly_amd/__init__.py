@@ -1,0 +1,11 @@
+"""Lossless compressed-KV decode attention for AMD MI355X (gfx950).
+
+The compute path is the HIP library libkvz.so (C ABI in include/kvz.h); `kvz` is its thin Python
+binding. Importing this package does not load the library; the first call does, and raises when
+the library is not built.
+"""
+from . import kvz  # noqa: F401
+from .kvz import (Cache, KvzError, append_token, compress_pages, decode_attention,  # noqa: F401
+                  decode_attention_dense, decode_attention_dense_splits, decode_attention_splits,
+                  decompress_pages, merge_splits, inline_capacity, meta_bytes, num_splits, unit_bytes,
+                  workspace_bytes)

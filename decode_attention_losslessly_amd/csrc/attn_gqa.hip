@@ -1,0 +1,349 @@
+// Decode attention when several query heads share one KV head (grouped-query attention).
+//
+// With g query heads per KV head, a 16-token tile of K times the g query rows is a real small
+// GEMM, so this path uses the CDNA4 matrix cores (the pages' kernel feeds H100 Tensor Cores from
+// operands rebuilt in registers: ZipFusion summary, §III.C "Attention over the Compressed KV
+// Cache"). One wave per (request, KV head, chunk of up to 8 query heads, split):
+//
+//   * S^T = K Q^T with v_mfma_f32_16x16x32_bf16: lane l rebuilds (or loads) 32 dims of token
+//     l%16, which is the A-operand layout; Q^T is the B operand, query rows 8..15 repeat rows
+//     0..7;
+//   * the 16x16 result sits in lanes exactly as the A operand of the P.V product needs it
+//     (lane l: query row l%16, tokens 4*(l/16)..+3), so probabilities never move between lanes;
+//     rows 0..7 carry bf16(p) and rows 8..15 carry bf16(p - bf16(p)), which keeps the P.V
+//     product accurate to ~2^-16 relative at no extra instruction;
+//   * V is rebuilt with the multi-head lane layout (lane l: dims l, l+64, all 16 tokens as token
+//     pairs), written to LDS as [dim][pair] and read back in the B-operand layout of
+//     v_mfma_f32_16x16x16_bf16 (4 tokens of one dim per lane), 8 dim tiles per token tile;
+//   * output rows r and r+8 are summed at the end.
+#include "attn_common.hpp"
+#include "kvz_lanes.hpp"
+
+namespace kvz {
+
+constexpr int kGqaWaves = 4;
+constexpr int kGqaRows = 8;
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+
+struct GqaState {
+  float m;          // running max of query row l%16 (log2 domain)
+  float l;          // this lane's share of that row's denominator
+  f32x4 o[8];       // output tile j: rows 4*(l/16)+i, dim 16j + l%16
+  uint32_t q[16];   // B operand: query row l%16, dims 32*(l/16)..+31
+};
+
+// One token tile: kp = this lane's K pairs (token l%16, dims 32*(l/16)..), vdim[2]/vp[2][8] =
+// V token pairs of two dims owned by this lane; `rows` valid tokens.
+__device__ __forceinline__ void gqa_tile(GqaState& st, const uint32_t (&kp)[16], const int (&vdim)[2],
+                                         const uint32_t (&vp)[2][8], int rows, float scale, uint32_t* vlds,
+                                         int lane) {
+  // scores S^T[token][row]
+  f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const u32x4 a = {kp[4 * c], kp[4 * c + 1], kp[4 * c + 2], kp[4 * c + 3]};
+    const u32x4 b = {st.q[4 * c], st.q[4 * c + 1], st.q[4 * c + 2], st.q[4 * c + 3]};
+    sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), sc,
+                                                  0, 0, 0);
+  }
+  const int tok0 = 4 * (lane >> 4);
+  float s[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) s[i] = (tok0 + i < rows) ? sc[i] * scale : -INFINITY;
+  // online softmax per query row (column l%16; the 4 lanes l%16 + 16k share it)
+  const bool up = (s[0] > st.m) | (s[1] > st.m) | (s[2] > st.m) | (s[3] > st.m);
+  if (ballot(up)) {
+    float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mn = fmaxf(st.m, mx);
+    const float alpha = (mn == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(st.m - mn);
+    st.l *= alpha;
+    st.m = mn;
+    // output rows of this lane are 4*(l/16)+i: fetch their alphas
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float ai = __shfl(alpha, tok0 + i);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) st.o[j][i] *= ai;
+    }
+  }
+  float p[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) p[i] = (s[i] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(s[i] - st.m);
+  const uint32_t h01 = pack_bf16(p[0], p[1]), h23 = pack_bf16(p[2], p[3]);
+  const float h[4] = {bf16lo_to_f32(h01), bf16hi_to_f32(h01), bf16lo_to_f32(h23), bf16hi_to_f32(h23)};
+  const uint32_t l01 = pack_bf16(p[0] - h[0], p[1] - h[1]), l23 = pack_bf16(p[2] - h[2], p[3] - h[3]);
+  st.l += (h[0] + bf16lo_to_f32(l01)) + (h[1] + bf16hi_to_f32(l01)) + (h[2] + bf16lo_to_f32(l23)) +
+          (h[3] + bf16hi_to_f32(l23));
+  const bool lo_row = (lane & 15) >= kGqaRows;
+  const u32x2 pa = {lo_row ? l01 : h01, lo_row ? l23 : h23};
+  // V -> LDS [dim][pair] (8 u32 per dim), then B operands: tokens 4q..4q+3 of dim 16j + l%16
+#pragma unroll
+  for (int g = 0; g < 2; ++g) {
+    uint4* dst = reinterpret_cast<uint4*>(vlds + vdim[g] * 8);
+    dst[0] = make_uint4(vp[g][0], vp[g][1], vp[g][2], vp[g][3]);
+    dst[1] = make_uint4(vp[g][4], vp[g][5], vp[g][6], vp[g][7]);
+  }
+  wave_lds_sync();
+  const bf16x4 A = __builtin_bit_cast(bf16x4, pa);
+  const int qg = lane >> 4;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const uint2 bv = *reinterpret_cast<const uint2*>(vlds + (16 * j + (lane & 15)) * 8 + 2 * qg);
+    const u32x2 b = {bv.x, bv.y};
+    st.o[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(A, __builtin_bit_cast(bf16x4, b), st.o[j], 0, 0, 0);
+  }
+  wave_lds_sync();
+}
+
+// ---------------------------------------------------------------- compressed source
+struct GqaCStage {
+  const uint8_t* unit;
+  UnitHeader hdr;
+  int tile;
+  KRaw<128> k;
+  VRaw<128> v;
+};
+
+__device__ __forceinline__ void gqa_c_load(GqaCStage& st, const GqaCStage& prev, const uint8_t* units,
+                                           const int32_t* pt_row, int page, int tile, int H, int h, int P,
+                                           int num_pages, int lane, uint32_t* status) {
+  if (tile == 0) {
+    const int pid = sload<int32_t>(pt_row + page);
+    if (pid < 0 || pid >= num_pages) {
+      if (lane == 0) atomicOr(status, kStatusBadPage);
+      st.unit = nullptr;
+    } else {
+      st.unit = units + ((size_t)pid * H + h) * unit_bytes(P, 128);
+      st.hdr = load_header(st.unit, P, 128);
+    }
+  } else {
+    st.unit = prev.unit;
+    st.hdr = prev.hdr;
+  }
+  st.tile = tile;
+  if (st.unit) {
+    load_k<128, true>(st.unit, P, tile, lane, st.k);
+    load_v<128>(st.unit, P, tile, lane, st.v);
+  }
+}
+
+__device__ __forceinline__ void gqa_c_compute(GqaState& st, const GqaCStage& stg, int P, uint32_t& krank,
+                                              uint32_t& vrank, uint16_t* esc_lds, uint32_t* vlds,
+                                              const uint16_t* pool, float scale, int lane) {
+  if (!stg.unit) return;
+  if (stg.tile == 0) { krank = 0; vrank = 0; }
+  uint32_t kp[16], kf[4];
+  decode_k<128>(stg.k, kp, kf);
+  if (stg.hdr.kc) patch_k_tile<128, true>(kp, kf, stg.unit, P, stg.hdr, krank, esc_lds, pool, lane);
+  uint32_t vp[2][8], vf[2][2];
+#pragma unroll
+  for (int g = 0; g < 2; ++g) {
+    const VBases b = v_bases(stg.unit, P, 128, stg.tile, g);
+    decode_v_seg(stg.v.seg[g], b, vp[g], vf[g]);
+  }
+  if (stg.hdr.vc) patch_v_tile<128>(vp, vf, stg.unit, P, stg.hdr, vrank, esc_lds, pool, lane);
+  const int vdim[2] = {lane, lane + 64};
+  gqa_tile(st, kp, vdim, vp, kTile, scale, vlds, lane);
+}
+
+// ---------------------------------------------------------------- raw (dense / tail) source
+// K: token l%16, dims 32*(l/16)..+31 (64 B); V: dims 2l, 2l+1 of all 16 tokens, regrouped into
+// token pairs. Rows >= `rows` are read as zeros.
+__device__ __forceinline__ void gqa_raw_tile(GqaState& st, const uint16_t* kpage, const uint16_t* vpage, int tok0,
+                                             int rows, float scale, uint32_t* vlds, int lane) {
+  uint32_t kp[16];
+  const int tok = lane & 15;
+  const bool ok = tok < rows;
+  const uint4* kr = reinterpret_cast<const uint4*>(kpage + (size_t)(tok0 + tok) * 128 + 32 * (lane >> 4));
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint4 x = ok ? kr[j] : make_uint4(0, 0, 0, 0);
+    kp[4 * j] = x.x; kp[4 * j + 1] = x.y; kp[4 * j + 2] = x.z; kp[4 * j + 3] = x.w;
+  }
+  uint32_t raw[16];
+  const uint32_t* vr = reinterpret_cast<const uint32_t*>(vpage + (size_t)tok0 * 128) + lane;
+#pragma unroll
+  for (int t = 0; t < 16; ++t) raw[t] = t < rows ? vr[(size_t)t * 64] : 0u;
+  uint32_t vp[2][8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    vp[0][k] = __builtin_amdgcn_perm(raw[2 * k + 1], raw[2 * k], 0x05040100u);
+    vp[1][k] = __builtin_amdgcn_perm(raw[2 * k + 1], raw[2 * k], 0x07060302u);
+  }
+  const int vdim[2] = {2 * lane, 2 * lane + 1};
+  gqa_tile(st, kp, vdim, vp, rows, scale, vlds, lane);
+}
+
+// ---------------------------------------------------------------- kernels
+__device__ __forceinline__ void gqa_init(GqaState& st, const uint16_t* q, int r, int Hq, int hq0, int nq, int lane) {
+  st.m = -INFINITY;
+  st.l = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) st.o[j] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  const int row = (lane & 15) % kGqaRows;
+  const bool ok = row < nq;
+  const uint4* qr = reinterpret_cast<const uint4*>(q + ((size_t)r * Hq + hq0 + (ok ? row : 0)) * 128 + 32 * (lane >> 4));
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint4 x = ok ? qr[j] : make_uint4(0, 0, 0, 0);
+    st.q[4 * j] = x.x; st.q[4 * j + 1] = x.y; st.q[4 * j + 2] = x.z; st.q[4 * j + 3] = x.w;
+  }
+}
+
+__device__ __forceinline__ void gqa_store(const GqaState& st, int r, int Hq, int hq0, int nq, int S, int s,
+                                          float* ws_acc, float* ws_ml, int lane) {
+  // denominators: row n = l%16 (< 8), summed over the 4 lane groups
+  float l = st.l;
+  l += __shfl_xor(l, 16);
+  l += __shfl_xor(l, 32);
+  // outputs: rows 4*(l/16)+i; add row + 8 (lanes l + 32) to rows < 8
+  f32x4 o[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[j][i] = st.o[j][i] + __shfl_xor(st.o[j][i], 32);
+  }
+  if (lane < 32) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int n = 4 * (lane >> 4) + i;
+      if (n < nq) {
+        float* acc = ws_acc + (((size_t)r * Hq + hq0 + n) * S + s) * 128;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[16 * j + (lane & 15)] = o[j][i];
+      }
+    }
+  }
+  if (lane < nq) {
+    float* ml = ws_ml + (((size_t)r * Hq + hq0 + lane) * S + s) * 2;
+    ml[0] = st.m;
+    ml[1] = l;
+  }
+}
+
+__global__ __launch_bounds__(64 * kGqaWaves) void attn_gqa_kernel(
+    const uint16_t* __restrict__ q, const uint8_t* __restrict__ units, const uint16_t* __restrict__ pool,
+    const uint16_t* __restrict__ k_tail, const uint16_t* __restrict__ v_tail, const int32_t* __restrict__ page_table,
+    int max_pages, const int32_t* __restrict__ seq_lens, int B, int Hq, int H, int P, int num_pages, int S, int C,
+    float scale, float* __restrict__ ws_acc, float* __restrict__ ws_ml, uint32_t* __restrict__ status) {
+  __shared__ uint16_t esc_all[kGqaWaves][16 * 128];
+  __shared__ uint32_t vlds_all[kGqaWaves][128 * 8];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int grp = Hq / H, nchunks = (grp + kGqaRows - 1) / kGqaRows;
+  const int item = (int)uniform(blockIdx.x * kGqaWaves + wave);
+  if (item >= B * H * nchunks * S) return;
+  const int s = item % S, qc = (item / S) % nchunks, h = (item / (S * nchunks)) % H, r = item / (S * nchunks * H);
+  const int hq0 = h * grp + qc * kGqaRows, nq = min(kGqaRows, grp - qc * kGqaRows);
+  int L = sload<int32_t>(seq_lens + r);
+  if (L > max_pages * P || L < 0) {
+    if (lane == 0 && s == 0 && h == 0 && qc == 0) atomicOr(status, kStatusSeqTooLong);
+    L = L < 0 ? 0 : max_pages * P;
+  }
+  const int nfull = L / P, rows = L % P;
+  const int Sr = active_splits(nfull, C);
+  if (s >= Sr) return;
+  const int p0 = s * C, p1 = min(p0 + C, nfull);
+  GqaState st;
+  gqa_init(st, q, r, Hq, hq0, nq, lane);
+  const int32_t* pt_row = page_table + (size_t)r * max_pages;
+  const int T = P / kTile;
+  const int nsteps = (p1 > p0 ? p1 - p0 : 0) * T;
+  uint32_t krank = 0, vrank = 0;
+  uint16_t* esc_lds = esc_all[wave];
+  uint32_t* vlds = vlds_all[wave];
+  if (nsteps > 0) {
+    GqaCStage a, b;
+    gqa_c_load(a, a, units, pt_row, p0, 0, H, h, P, num_pages, lane, status);
+    for (int i = 0; i < nsteps; i += 2) {
+      if (i + 1 < nsteps) gqa_c_load(b, a, units, pt_row, p0 + (i + 1) / T, (i + 1) % T, H, h, P, num_pages, lane, status);
+      gqa_c_compute(st, a, P, krank, vrank, esc_lds, vlds, pool, scale, lane);
+      if (i + 1 >= nsteps) break;
+      if (i + 2 < nsteps) gqa_c_load(a, b, units, pt_row, p0 + (i + 2) / T, (i + 2) % T, H, h, P, num_pages, lane, status);
+      gqa_c_compute(st, b, P, krank, vrank, esc_lds, vlds, pool, scale, lane);
+    }
+  }
+  if (s == Sr - 1 && rows > 0) {
+    const size_t toff = ((size_t)r * H + h) * P * 128;
+    for (int t0 = 0; t0 < rows; t0 += kTile)
+      gqa_raw_tile(st, k_tail + toff, v_tail + toff, t0, min(kTile, rows - t0), scale, vlds, lane);
+  }
+  gqa_store(st, r, Hq, hq0, nq, S, s, ws_acc, ws_ml, lane);
+}
+
+__global__ __launch_bounds__(64 * kGqaWaves) void attn_dense_gqa_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_pages, const uint16_t* __restrict__ v_pages,
+    const int32_t* __restrict__ page_table, int max_pages, const int32_t* __restrict__ seq_lens, int B, int Hq, int H,
+    int P, int num_pages, int S, int C, float scale, float* __restrict__ ws_acc, float* __restrict__ ws_ml,
+    uint32_t* __restrict__ status) {
+  __shared__ uint32_t vlds_all[kGqaWaves][128 * 8];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int grp = Hq / H, nchunks = (grp + kGqaRows - 1) / kGqaRows;
+  const int item = (int)uniform(blockIdx.x * kGqaWaves + wave);
+  if (item >= B * H * nchunks * S) return;
+  const int s = item % S, qc = (item / S) % nchunks, h = (item / (S * nchunks)) % H, r = item / (S * nchunks * H);
+  const int hq0 = h * grp + qc * kGqaRows, nq = min(kGqaRows, grp - qc * kGqaRows);
+  int L = sload<int32_t>(seq_lens + r);
+  if (L > max_pages * P || L < 0) {
+    if (lane == 0 && s == 0 && h == 0 && qc == 0 && status) atomicOr(status, kStatusSeqTooLong);
+    L = L < 0 ? 0 : max_pages * P;
+  }
+  const int npages = (L + P - 1) / P;
+  const int Sr = active_splits(npages, C);
+  if (s >= Sr) return;
+  const int p0 = s * C, p1 = min(p0 + C, npages);
+  GqaState st;
+  gqa_init(st, q, r, Hq, hq0, nq, lane);
+  uint32_t* vlds = vlds_all[wave];
+  for (int pg = p0; pg < p1; ++pg) {
+    const int pid = sload<int32_t>(page_table + (size_t)r * max_pages + pg);
+    if (pid < 0 || pid >= num_pages) {
+      if (lane == 0 && status) atomicOr(status, kStatusBadPage);
+      continue;
+    }
+    const uint16_t* kpage = k_pages + ((size_t)pid * H + h) * P * 128;
+    const uint16_t* vpage = v_pages + ((size_t)pid * H + h) * P * 128;
+    for (int t0 = 0; t0 < P; t0 += kTile) {
+      const int rows = min(kTile, L - pg * P - t0);
+      if (rows <= 0) break;
+      gqa_raw_tile(st, kpage, vpage, t0, rows, scale, vlds, lane);
+    }
+  }
+  gqa_store(st, r, Hq, hq0, nq, S, s, ws_acc, ws_ml, lane);
+}
+
+static unsigned gqa_blocks(int B, int Hq, int H, int S) {
+  const int grp = Hq / H, nchunks = (grp + kGqaRows - 1) / kGqaRows;
+  const long items = (long)B * H * nchunks * S;
+  return (unsigned)((items + kGqaWaves - 1) / kGqaWaves);
+}
+
+int launch_attn_gqa(const uint16_t* q, const uint8_t* units, const uint16_t* pool, const uint16_t* k_tail,
+                    const uint16_t* v_tail, const int32_t* page_table, int max_pages, const int32_t* seq_lens,
+                    int B, int Hq, int H, int D, int P, int num_pages, int S, int C, float scale, float* ws_acc,
+                    float* ws_ml, uint32_t* status, hipStream_t stream) {
+  if (D != 128) return -2;
+  hipLaunchKernelGGL(attn_gqa_kernel, dim3(gqa_blocks(B, Hq, H, S)), dim3(64 * kGqaWaves), 0, stream, q, units, pool,
+                     k_tail, v_tail, page_table, max_pages, seq_lens, B, Hq, H, P, num_pages, S, C, scale, ws_acc,
+                     ws_ml, status);
+  return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
+int launch_attn_dense_gqa(const uint16_t* q, const uint16_t* k_pages, const uint16_t* v_pages, const int32_t* pt,
+                          int max_pages, const int32_t* seq_lens, int B, int Hq, int H, int D, int P, int num_pages,
+                          int S, int C, float scale, float* ws_acc, float* ws_ml, uint32_t* status,
+                          hipStream_t stream) {
+  if (D != 128) return -2;
+  hipLaunchKernelGGL(attn_dense_gqa_kernel, dim3(gqa_blocks(B, Hq, H, S)), dim3(64 * kGqaWaves), 0, stream, q,
+                     k_pages, v_pages, pt, max_pages, seq_lens, B, Hq, H, P, num_pages, S, C, scale, ws_acc, ws_ml,
+                     status);
+  return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
+}  // namespace kvz

@@ -1,0 +1,264 @@
+// Decode attention over the compressed cache, one query head per KV head (multi-head).
+//
+// The compressed blocks are read straight from HBM and rebuilt in registers with integer bit
+// operations just before use; nothing is decompressed to memory (ZipFusion summary, §III.C
+// "Attention over the Compressed KV Cache"). The pages' kernel is built for H100 Tensor Cores;
+// this one is organised for CDNA4 wave64 VALU work, because with one query row per KV head the
+// contraction is a matrix-vector product that does not fill a matrix core:
+//
+//   * one wave per (request, head, split); four independent waves per workgroup;
+//   * K tile (16 tokens x D): lane l rebuilds the D/4 values of token l/4, dims (l%4)*D/4..,
+//     dots them with q in v_dot2_f32_bf16 and a quad DPP sum gives the token's score in all 4
+//     lanes of the quad;
+//   * online softmax in the log2 domain; the wave-wide max is only taken when a score exceeds
+//     the running maximum (the rescale is exact, it is just skipped when it would multiply by 1);
+//   * probabilities are split into hi = bf16(p) and lo = bf16(p - hi), and token pairs of each
+//     are broadcast to SGPRs with readlane;
+//   * V tile: lane l rebuilds dims l (+64) for all 16 tokens as packed token pairs and
+//     accumulates dot2(pair, hi) + dot2(pair, lo) in fp32, so every lane owns complete sums for
+//     its dims and no cross-lane reduction of the output is needed;
+//   * the next tile's compressed bytes are loaded before the current tile is computed.
+#include "attn_common.hpp"
+#include "kvz_lanes.hpp"
+
+namespace kvz {
+
+constexpr int kWavesPerBlock = 4;
+
+template <int D>
+struct MhaStage {
+  const uint8_t* unit;
+  UnitHeader hdr;
+  int tile;
+  KRaw<D> k;
+  VRaw<D> v;
+};
+
+// Issues the loads of one (page, tile) step. Tile 0 of a page reads the page id and header;
+// later tiles of the same page reuse `prev`'s.
+template <int D>
+__device__ __forceinline__ void mha_load(MhaStage<D>& st, const MhaStage<D>& prev, const uint8_t* units,
+                                         const int32_t* pt_row, int page, int tile, int H, int h, int P,
+                                         int num_pages, int lane, uint32_t* status) {
+  if (tile == 0) {
+    const int pid = sload<int32_t>(pt_row + page);
+    if (pid < 0 || pid >= num_pages) {
+      if (lane == 0) atomicOr(status, kStatusBadPage);
+      st.unit = nullptr;
+    } else {
+      st.unit = units + ((size_t)pid * H + h) * unit_bytes(P, D);
+      st.hdr = load_header(st.unit, P, D);
+    }
+  } else {
+    st.unit = prev.unit;
+    st.hdr = prev.hdr;
+  }
+  st.tile = tile;
+  if (st.unit) {
+    load_k<D, false>(st.unit, P, tile, lane, st.k);
+    load_v<D>(st.unit, P, tile, lane, st.v);
+  }
+}
+
+template <int D>
+struct MhaState {
+  float m;          // running max, log2 domain (wave-uniform)
+  float l;          // this lane's share of the denominator (its token's terms)
+  float acc[D / 64];
+  uint32_t q[KRaw<D>::VK / 2];
+};
+
+// Softmax update for one tile given this lane's score s (-inf for a masked token); returns the
+// hi/lo probability pairs of the 8 token pairs as wave-uniform values.
+template <int D>
+__device__ __forceinline__ void mha_softmax(MhaState<D>& st, float s, uint32_t (&phi)[8], uint32_t (&plo)[8]) {
+  if (ballot(s > st.m)) {
+    const float mt = wave_max(s);
+    const float mn = fmaxf(st.m, mt);
+    const float alpha = __builtin_amdgcn_exp2f(st.m - mn);
+    st.l *= alpha;
+#pragma unroll
+    for (int i = 0; i < D / 64; ++i) st.acc[i] *= alpha;
+    st.m = mn;
+  }
+  const float p = s == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(s - st.m);
+  const float pn = dpp_f<kRowShl4>(p);               // token of the quad 4 lanes up
+  const uint32_t hi = pack_bf16(p, pn);
+  const float h_own = bf16lo_to_f32(hi), h_nb = bf16hi_to_f32(hi);
+  const uint32_t lo = pack_bf16(p - h_own, pn - h_nb);
+  st.l += h_own + bf16lo_to_f32(lo);
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    phi[k] = readlane(hi, 8 * k);
+    plo[k] = readlane(lo, 8 * k);
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void mha_accumulate_v(MhaState<D>& st, const uint32_t (&vp)[D / 64][8],
+                                                 const uint32_t (&phi)[8], const uint32_t (&plo)[8]) {
+#pragma unroll
+  for (int s = 0; s < D / 64; ++s) {
+    float a = st.acc[s], b = 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      a = dot2_bf16(vp[s][k], phi[k], a);
+      b = dot2_bf16(vp[s][k], plo[k], b);
+    }
+    st.acc[s] = a + b;
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void mha_compute(MhaState<D>& st, const MhaStage<D>& stg, int P, uint32_t& krank,
+                                            uint32_t& vrank, uint16_t* lds, const uint16_t* pool, float scale,
+                                            int lane) {
+  if (!stg.unit) return;
+  constexpr int VK = KRaw<D>::VK, NW = KRaw<D>::NW, NS = D / 64;
+  if (stg.tile == 0) { krank = 0; vrank = 0; }
+  uint32_t kp[VK / 2], kf[NW];
+  decode_k<D>(stg.k, kp, kf);
+  if (stg.hdr.kc) patch_k_tile<D, false>(kp, kf, stg.unit, P, stg.hdr, krank, lds, pool, lane);
+  float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+  for (int j = 0; j < VK / 2; j += 2) {
+    a0 = dot2_bf16(kp[j], st.q[j], a0);
+    a1 = dot2_bf16(kp[j + 1], st.q[j + 1], a1);
+  }
+  const float s = quad_sum(a0 + a1) * scale;
+  uint32_t phi[8], plo[8];
+  mha_softmax<D>(st, s, phi, plo);
+  uint32_t vp[NS][8], vf[NS][2];
+#pragma unroll
+  for (int g = 0; g < NS; ++g) {
+    const VBases b = v_bases(stg.unit, P, D, stg.tile, g);
+    decode_v_seg(stg.v.seg[g], b, vp[g], vf[g]);
+  }
+  if (stg.hdr.vc) patch_v_tile<D>(vp, vf, stg.unit, P, stg.hdr, vrank, lds, pool, lane);
+  mha_accumulate_v<D>(st, vp, phi, plo);
+}
+
+// The uncompressed tail rows (at most P-1 tokens) of one request and head, one 16-token tile at
+// a time; rows >= `rows` are masked.
+template <int D>
+__device__ __forceinline__ void mha_tail(MhaState<D>& st, const uint16_t* tk, const uint16_t* tv, int rows,
+                                         float scale, int lane) {
+  constexpr int VK = KRaw<D>::VK, NS = D / 64;
+  for (int t0 = 0; t0 < rows; t0 += kTile) {
+    const int tok = t0 + lane / 4;
+    const bool valid = tok < rows;
+    uint32_t kp[VK / 2];
+    const uint32_t* krow = reinterpret_cast<const uint32_t*>(tk + (size_t)tok * D + (lane & 3) * VK);
+#pragma unroll
+    for (int j = 0; j < VK / 2; ++j) kp[j] = valid ? krow[j] : 0u;
+    float a = 0.f;
+#pragma unroll
+    for (int j = 0; j < VK / 2; ++j) a = dot2_bf16(kp[j], st.q[j], a);
+    float s = quad_sum(a) * scale;
+    s = valid ? s : -INFINITY;
+    uint32_t phi[8], plo[8];
+    mha_softmax<D>(st, s, phi, plo);
+    uint32_t vp[NS][8];
+#pragma unroll
+    for (int g = 0; g < NS; ++g) {
+      const int d = lane + 64 * g;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int t_a = t0 + 2 * k, t_b = t_a + 1;
+        const uint32_t va = t_a < rows ? tv[(size_t)t_a * D + d] : 0u;
+        const uint32_t vb = t_b < rows ? tv[(size_t)t_b * D + d] : 0u;
+        vp[g][k] = va | (vb << 16);
+      }
+    }
+    mha_accumulate_v<D>(st, vp, phi, plo);
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(64 * kWavesPerBlock) void attn_mha_kernel(
+    const uint16_t* __restrict__ q, const uint8_t* __restrict__ units, const uint16_t* __restrict__ pool,
+    const uint16_t* __restrict__ k_tail, const uint16_t* __restrict__ v_tail, const int32_t* __restrict__ page_table,
+    int max_pages, const int32_t* __restrict__ seq_lens, int B, int H, int P, int num_pages, int S, int C,
+    float scale, float* __restrict__ ws_acc, float* __restrict__ ws_ml, uint32_t* __restrict__ status) {
+  __shared__ uint16_t lds_all[kWavesPerBlock][16 * D];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int item = (int)uniform(blockIdx.x * kWavesPerBlock + wave);
+  if (item >= B * H * S) return;
+  const int s = item % S, h = (item / S) % H, r = item / (S * H);
+  uint16_t* lds = lds_all[wave];
+  int L = sload<int32_t>(seq_lens + r);
+  if (L > max_pages * P || L < 0) {
+    if (lane == 0 && s == 0 && h == 0) atomicOr(status, kStatusSeqTooLong);
+    L = L < 0 ? 0 : max_pages * P;
+  }
+  const int nfull = L / P, rows = L % P;
+  const int Sr = active_splits(nfull, C);
+  if (s >= Sr) return;
+  const int p0 = s * C, p1 = min(p0 + C, nfull);
+  constexpr int VK = KRaw<D>::VK;
+
+  MhaState<D> st;
+  st.m = -INFINITY;
+  st.l = 0.f;
+#pragma unroll
+  for (int i = 0; i < D / 64; ++i) st.acc[i] = 0.f;
+  {
+    const uint32_t* qrow = reinterpret_cast<const uint32_t*>(q + ((size_t)r * H + h) * D + (lane & 3) * VK);
+#pragma unroll
+    for (int j = 0; j < VK / 2; ++j) st.q[j] = qrow[j];
+  }
+  const int32_t* pt_row = page_table + (size_t)r * max_pages;
+  const int T = P / kTile;
+  const int nsteps = (p1 > p0 ? p1 - p0 : 0) * T;
+  uint32_t krank = 0, vrank = 0;
+  if (nsteps > 0) {
+    MhaStage<D> a, b;
+    mha_load<D>(a, a, units, pt_row, p0, 0, H, h, P, num_pages, lane, status);
+    for (int i = 0; i < nsteps; i += 2) {
+      if (i + 1 < nsteps)
+        mha_load<D>(b, a, units, pt_row, p0 + (i + 1) / T, (i + 1) % T, H, h, P, num_pages, lane, status);
+      mha_compute<D>(st, a, P, krank, vrank, lds, pool, scale, lane);
+      if (i + 1 >= nsteps) break;
+      if (i + 2 < nsteps)
+        mha_load<D>(a, b, units, pt_row, p0 + (i + 2) / T, (i + 2) % T, H, h, P, num_pages, lane, status);
+      mha_compute<D>(st, b, P, krank, vrank, lds, pool, scale, lane);
+    }
+  }
+  if (s == Sr - 1 && rows > 0) {
+    const size_t toff = ((size_t)r * H + h) * P * D;
+    mha_tail<D>(st, k_tail + toff, v_tail + toff, rows, scale, lane);
+  }
+  // partials: l summed over one lane per quad (each quad holds one token's terms)
+  float lsum = (lane & 3) == 0 ? st.l : 0.f;
+  lsum += __shfl_xor(lsum, 4);
+  lsum += __shfl_xor(lsum, 8);
+  lsum += __shfl_xor(lsum, 16);
+  lsum += __shfl_xor(lsum, 32);
+  const size_t row = (size_t)r * H + h;
+  float* acc = ws_acc + (row * S + s) * D;
+#pragma unroll
+  for (int g = 0; g < D / 64; ++g) acc[lane + 64 * g] = st.acc[g];
+  if (lane == 0) {
+    ws_ml[(row * S + s) * 2 + 0] = st.m;
+    ws_ml[(row * S + s) * 2 + 1] = lsum;
+  }
+}
+
+int launch_attn_mha(const uint16_t* q, const uint8_t* units, const uint16_t* pool, const uint16_t* k_tail,
+                    const uint16_t* v_tail, const int32_t* page_table, int max_pages, const int32_t* seq_lens,
+                    int B, int H, int D, int P, int num_pages, int S, int C, float scale, float* ws_acc,
+                    float* ws_ml, uint32_t* status, hipStream_t stream) {
+  const int items = B * H * S;
+  dim3 grid((unsigned)(items + kWavesPerBlock - 1) / kWavesPerBlock), block(64 * kWavesPerBlock);
+  if (D == 128)
+    hipLaunchKernelGGL((attn_mha_kernel<128>), grid, block, 0, stream, q, units, pool, k_tail, v_tail, page_table,
+                       max_pages, seq_lens, B, H, P, num_pages, S, C, scale, ws_acc, ws_ml, status);
+  else if (D == 64)
+    hipLaunchKernelGGL((attn_mha_kernel<64>), grid, block, 0, stream, q, units, pool, k_tail, v_tail, page_table,
+                       max_pages, seq_lens, B, H, P, num_pages, S, C, scale, ws_acc, ws_ml, status);
+  else
+    return -2;
+  return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
+}  // namespace kvz

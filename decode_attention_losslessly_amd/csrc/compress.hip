@@ -1,0 +1,100 @@
+// kvz_compress_pages and kvz_append_token kernels.
+#include "compress.hpp"
+
+namespace kvz {
+
+__global__ __launch_bounds__(kCompressThreads) void compress_pages_kernel(
+    const uint16_t* __restrict__ k_src, const uint16_t* __restrict__ v_src, const int32_t* __restrict__ dst_ids,
+    int H, int P, int D, int num_pages, uint8_t* __restrict__ units, uint16_t* __restrict__ pool, int64_t pool_cap,
+    uint64_t* __restrict__ cursor, uint32_t* __restrict__ status) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  __shared__ CompressShared sh;
+  const int i = blockIdx.x / H, h = blockIdx.x % H;
+  const int pid = dst_ids[i];
+  if (pid < 0 || pid >= num_pages) {
+    if (threadIdx.x == 0) atomicOr(status, kStatusBadPage);
+    return;
+  }
+  const size_t blk = (size_t)P * D;
+  compress_unit<0>(k_src + ((size_t)i * H + h) * blk, v_src + ((size_t)i * H + h) * blk, P, D,
+                   units + ((size_t)pid * H + h) * unit_bytes(P, D), pool, pool_cap, cursor, status,
+                   reinterpret_cast<uint16_t*>(smem), smem + 4 * blk, sh);
+}
+
+// One workgroup per (request, head): write the new row into the tail; if that fills the tail,
+// compress it into the unit named by the page table.
+__global__ __launch_bounds__(kCompressThreads) void append_kernel(
+    const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new, const int32_t* __restrict__ page_table,
+    int max_pages, const int32_t* __restrict__ seq_lens, int H, int P, int D, int num_pages,
+    uint8_t* __restrict__ units, uint16_t* __restrict__ pool, int64_t pool_cap, uint64_t* __restrict__ cursor,
+    uint16_t* __restrict__ k_tail, uint16_t* __restrict__ v_tail, uint32_t* __restrict__ status) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  __shared__ CompressShared sh;
+  const int r = blockIdx.x / H, h = blockIdx.x % H;
+  const int L = seq_lens[r];
+  if (L < 0 || L >= max_pages * P) {
+    if (threadIdx.x == 0 && h == 0) atomicOr(status, kStatusSeqTooLong);
+    return;
+  }
+  const int slot = L % P;
+  const size_t blk = (size_t)P * D;
+  uint16_t* tk = k_tail + ((size_t)r * H + h) * blk;
+  uint16_t* tv = v_tail + ((size_t)r * H + h) * blk;
+  const uint16_t* kn = k_new + ((size_t)r * H + h) * D;
+  const uint16_t* vn = v_new + ((size_t)r * H + h) * D;
+  for (int d = threadIdx.x; d < D; d += kCompressThreads) {
+    tk[(size_t)slot * D + d] = kn[d];
+    tv[(size_t)slot * D + d] = vn[d];
+  }
+  if (slot != P - 1) return;
+  __threadfence_block();
+  __syncthreads();
+  const int pid = page_table[(size_t)r * max_pages + L / P];
+  if (pid < 0 || pid >= num_pages) {
+    if (threadIdx.x == 0) atomicOr(status, kStatusBadPage);
+    return;
+  }
+  compress_unit<0>(tk, tv, P, D, units + ((size_t)pid * H + h) * unit_bytes(P, D), pool, pool_cap, cursor,
+                   status, reinterpret_cast<uint16_t*>(smem), smem + 4 * blk, sh);
+}
+
+__global__ void bump_lens_kernel(int32_t* __restrict__ seq_lens, int B, int limit) {
+  const int r = blockIdx.x * blockDim.x + threadIdx.x;
+  if (r < B) {
+    const int L = seq_lens[r];
+    if (L >= 0 && L < limit) seq_lens[r] = L + 1;
+  }
+}
+
+static size_t compress_smem(int P, int D) { return 4 * (size_t)P * D + 2 * (size_t)P * (D / kGroup); }
+
+int launch_compress(const uint16_t* k_src, const uint16_t* v_src, const int32_t* ids, int n, int H, int P, int D,
+                    int num_pages, uint8_t* units, uint16_t* pool, int64_t pool_cap, uint64_t* cursor,
+                    uint32_t* status, hipStream_t stream) {
+  const size_t smem = compress_smem(P, D);
+  if (hipFuncSetAttribute((const void*)compress_pages_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                          (int)smem) != hipSuccess)
+    return -4;
+  hipLaunchKernelGGL(compress_pages_kernel, dim3((unsigned)n * H), dim3(kCompressThreads), smem, stream, k_src,
+                     v_src, ids, H, P, D, num_pages, units, pool, pool_cap, cursor, status);
+  return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
+int launch_append(const uint16_t* k_new, const uint16_t* v_new, const int32_t* page_table, int max_pages,
+                  int32_t* seq_lens, int B, int H, int P, int D, int num_pages, uint8_t* units, uint16_t* pool,
+                  int64_t pool_cap, uint64_t* cursor, uint16_t* k_tail, uint16_t* v_tail, uint32_t* status,
+                  hipStream_t stream) {
+  const size_t smem = compress_smem(P, D);
+  if (hipFuncSetAttribute((const void*)append_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem) !=
+      hipSuccess)
+    return -4;
+  hipLaunchKernelGGL(append_kernel, dim3((unsigned)B * H), dim3(kCompressThreads), smem, stream, k_new, v_new,
+                     page_table, max_pages, seq_lens, H, P, D, num_pages, units, pool, pool_cap, cursor, k_tail,
+                     v_tail, status);
+  if (hipGetLastError() != hipSuccess) return -4;
+  hipLaunchKernelGGL(bump_lens_kernel, dim3((unsigned)(B + 255) / 256), dim3(256), 0, stream, seq_lens, B,
+                     max_pages * P);
+  return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
+}  // namespace kvz

@@ -1,0 +1,181 @@
+// Compression of one full page of one head into a unit (§III.B "Lossless KV Cache Format":
+// exponents coded as offsets from a base, sign and fraction kept; §III.D: a page is compressed
+// once it is full). Used by kvz_compress_pages and by kvz_append_token when a tail fills.
+//
+// One 256-thread workgroup per unit:
+//   1. both source blocks [P][D] are staged in LDS;
+//   2. each wave takes groups (64 values = 64 lanes): every lane counts how many group
+//      exponents fall in [e, e+14] for its own exponent e; the largest count wins, the smallest
+//      exponent on ties; escapes are counted;
+//   3. the escape list goes inline when K + V escapes fit the meta region, else to the pool at
+//      an atomically bumped cursor;
+//   4. storage positions are encoded 8 per thread (one offset word, 8 sm bytes) in storage
+//      order, with a workgroup scan giving each escape its rank.
+#pragma once
+
+#include "kvz_device.hpp"
+
+namespace kvz {
+
+constexpr int kCompressThreads = 256;
+
+struct CompressShared {
+  uint32_t esc_count[2];
+  uint32_t wave_sum[kCompressThreads / 64];
+  uint64_t dest;        // pool offset, kInline, or ~1 when the pool is full
+  uint32_t drop;        // 1 when escapes are dropped (pool full)
+};
+
+// exclusive scan over the workgroup; returns this thread's prefix, *total gets the sum
+__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, CompressShared& sh, uint32_t* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint32_t inc = wave_incl_scan(v);
+  if (lane == 63) sh.wave_sum[wave] = inc;
+  __syncthreads();
+  uint32_t before = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < kCompressThreads / 64; ++w) {
+    const uint32_t s = sh.wave_sum[w];
+    before += (w < wave) ? s : 0u;
+    all += s;
+  }
+  __syncthreads();
+  *total = all;
+  return before + inc - v;
+}
+
+// storage position s (within one block) -> token-major index tok*D + d
+template <bool IsV>
+__device__ __forceinline__ int storage_to_index(int s, int D) {
+  const int t = s / (kTile * D), r = s % (kTile * D);
+  int tok, d;
+  if (IsV) { d = r / kTile; tok = r % kTile; } else { tok = r / D; d = r % D; }
+  return (t * kTile + tok) * D + d;
+}
+
+template <bool IsV>
+__device__ void encode_block(const uint16_t* X, const uint8_t* bases_meta, int P, int D,
+                             uint8_t* payload, uint16_t* esc_dst, bool keep_esc, CompressShared& sh) {
+  const int G = D / kGroup;
+  const int nchunks = P * D / 8;
+  uint32_t rank = 0;
+  for (int c0 = 0; c0 < nchunks; c0 += kCompressThreads) {
+    const int c = c0 + (int)threadIdx.x;
+    uint32_t word = 0, ne = 0;
+    uint32_t sm_lo = 0, sm_hi = 0;
+    uint16_t xs[8];
+    uint32_t escmask = 0;
+    if (c < nchunks) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int s = 8 * c + j;
+        const int idx = storage_to_index<IsV>(s, D);
+        const int tok = idx / D, d = idx % D;
+        const uint16_t x = X[idx];
+        xs[j] = x;
+        const int b = bases_meta[(tok / kTile) * kTile * G + (d / kGroup) * kTile + (tok % kTile)];
+        const int e = (x >> 7) & 0xFF;
+        int off = e - b;
+        if (off < 0 || off > 14) { off = kEscape; escmask |= 1u << j; ++ne; }
+        const int bit = (j & 1) ? (16 + 4 * (j >> 1)) : (4 * (j >> 1));
+        word |= (uint32_t)off << bit;
+        const uint32_t sm = ((x >> 8) & 0x80u) | (x & 0x7Fu);
+        if (j < 4) sm_lo |= sm << (8 * j); else sm_hi |= sm << (8 * (j - 4));
+      }
+      const int t = (8 * c) / (kTile * D), r = (8 * c) % (kTile * D);
+      uint8_t* tb = payload + (size_t)t * tile_bytes(D);
+      *reinterpret_cast<uint2*>(tb + r) = make_uint2(sm_lo, sm_hi);
+      *reinterpret_cast<uint32_t*>(tb + 16 * D + r / 2) = word;
+    }
+    uint32_t total;
+    uint32_t pre = block_excl_scan(ne, sh, &total);
+    if (keep_esc && escmask) {
+      uint32_t k = rank + pre;
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (escmask & (1u << j)) esc_dst[k++] = xs[j];
+    }
+    rank += total;
+  }
+}
+
+// Compresses src_k, src_v ([P][D] token-major raw BF16) into `unit`.
+template <int MaxPD>
+__device__ void compress_unit(const uint16_t* __restrict__ src_k, const uint16_t* __restrict__ src_v, int P,
+                              int D, uint8_t* __restrict__ unit, uint16_t* __restrict__ pool, int64_t pool_cap,
+                              uint64_t* __restrict__ cursor, uint32_t* __restrict__ status,
+                              uint16_t* sh_x /* [2*P*D] */, uint8_t* sh_base /* [2*P*G] */, CompressShared& sh) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int G = D / kGroup, PD = P * D;
+  // 1. stage
+  for (int i = tid; i < PD / 8; i += kCompressThreads) {
+    reinterpret_cast<uint4*>(sh_x)[i] = reinterpret_cast<const uint4*>(src_k)[i];
+    reinterpret_cast<uint4*>(sh_x + PD)[i] = reinterpret_cast<const uint4*>(src_v)[i];
+  }
+  if (tid < 2) sh.esc_count[tid] = 0;
+  __syncthreads();
+  // 2. bases, one group per wave at a time
+  uint32_t cnt[2] = {0, 0};
+  const int ngroups = 2 * P * G;
+  for (int q = wave; q < ngroups; q += kCompressThreads / 64) {
+    const int tensor = q / (P * G), rem = q % (P * G), tok = rem / G, g = rem % G;
+    const uint16_t x = sh_x[tensor * PD + tok * D + g * kGroup + lane];
+    const uint32_t e = (x >> 7) & 0xFFu;
+    uint32_t cov = 0;
+#pragma unroll
+    for (int j = 0; j < 64; ++j) {
+      const uint32_t ej = readlane(e, j);
+      cov += (ej - e) <= 14u ? 1u : 0u;
+    }
+    uint32_t key = (cov << 8) | (255u - e);
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) key = max(key, (uint32_t)__shfl_xor((int)key, m));
+    const uint32_t b = 255u - (uniform(key) & 0xFFu);
+    const uint64_t escm = ballot((e - b) > 14u);
+    cnt[tensor] += (uint32_t)__builtin_popcountll(escm);
+    if (lane == 0) sh_base[tensor * P * G + (tok / kTile) * kTile * G + g * kTile + (tok % kTile)] = (uint8_t)b;
+  }
+  if (lane == 0) {
+    atomicAdd(&sh.esc_count[0], cnt[0]);
+    atomicAdd(&sh.esc_count[1], cnt[1]);
+  }
+  __syncthreads();
+  // 3. where the escapes go
+  const uint32_t kc = sh.esc_count[0], vc = sh.esc_count[1], total = kc + vc;
+  const int cap = inline_capacity(P, D);
+  const uint32_t hdr = hdr_offset(P, D);
+  if (tid == 0) {
+    sh.drop = 0;
+    if ((int)total <= cap) {
+      sh.dest = kInline;
+    } else {
+      const uint64_t off = atomicAdd((unsigned long long*)cursor, (unsigned long long)total);
+      if (off + total > (uint64_t)pool_cap) {
+        atomicOr(status, kStatusPoolFull);
+        sh.drop = 1;
+        sh.dest = kInline;
+      } else {
+        sh.dest = off;
+      }
+    }
+  }
+  __syncthreads();
+  const uint64_t dest = sh.dest;
+  const bool keep = sh.drop == 0;
+  uint16_t* esc = (dest == kInline) ? reinterpret_cast<uint16_t*>(unit + hdr + 16) : pool + dest;
+  // 4. payload and escapes
+  encode_block<false>(sh_x, sh_base, P, D, unit + kblock_offset(P, D), esc, keep, sh);
+  encode_block<true>(sh_x + PD, sh_base + P * G, P, D, unit + vblock_offset(P, D), esc + kc, keep, sh);
+  // 5. meta: bases, header, zero tail of the inline area
+  for (int i = tid; i < 2 * P * G; i += kCompressThreads) unit[i] = sh_base[i];
+  const uint32_t used = (dest == kInline && keep) ? 2 * total : 0;
+  for (uint32_t i = hdr + 16 + used + tid; i < meta_bytes(P, D); i += kCompressThreads) unit[i] = 0;
+  if (tid == 0) {
+    uint32_t* h = reinterpret_cast<uint32_t*>(unit + hdr);
+    h[0] = keep ? kc : 0;
+    h[1] = keep ? vc : 0;
+    *reinterpret_cast<uint64_t*>(unit + hdr + 8) = dest;
+  }
+}
+
+}  // namespace kvz

@@ -1,0 +1,84 @@
+// Test-only kernel: the attention kernels' in-register decode of K and V, written back as raw
+// BF16 so that it can be compared bit for bit with the source of the compressed pages.
+// One wave per (unit, head); per tile: load, rebuild, patch escapes, store.
+#include "kvz_lanes.hpp"
+
+namespace kvz {
+
+template <int D, bool GQA>
+__global__ __launch_bounds__(64) void decompress_kernel(const uint8_t* __restrict__ units,
+                                                        const uint16_t* __restrict__ pool,
+                                                        const int32_t* __restrict__ page_ids, int H,
+                                                        int P, int num_pages, uint16_t* __restrict__ k_dst,
+                                                        uint16_t* __restrict__ v_dst,
+                                                        uint32_t* __restrict__ status) {
+  __shared__ uint16_t lds[16 * D];
+  const int lane = threadIdx.x;
+  const int i = blockIdx.x / H, h = blockIdx.x % H;
+  const int pid = sload<int32_t>(page_ids + i);
+  if (pid < 0 || pid >= num_pages) {
+    if (lane == 0) atomicOr(status, kStatusBadPage);
+    return;
+  }
+  const uint8_t* unit = units + ((size_t)pid * H + h) * unit_bytes(P, D);
+  const UnitHeader hdr = load_header(unit, P, D);
+  uint16_t* kd = k_dst + ((size_t)i * H + h) * P * D;
+  uint16_t* vd = v_dst + ((size_t)i * H + h) * P * D;
+  uint32_t krank = 0, vrank = 0;
+  for (int t = 0; t < P / kTile; ++t) {
+    // K
+    KRaw<D> kr;
+    load_k<D, GQA>(unit, P, t, lane, kr);
+    uint32_t kp[KRaw<D>::VK / 2], kf[KRaw<D>::NW];
+    decode_k<D>(kr, kp, kf);
+    if (hdr.kc) patch_k_tile<D, GQA>(kp, kf, unit, P, hdr, krank, lds, pool, lane);
+    {
+      constexpr int VK = KRaw<D>::VK;
+      const int c = k_chunk<D, GQA>(lane);
+      const int tok = c / (D / VK), dim0 = (c % (D / VK)) * VK;
+      uint32_t* dst = reinterpret_cast<uint32_t*>(kd + (size_t)(t * kTile + tok) * D + dim0);
+#pragma unroll
+      for (int j = 0; j < VK / 2; ++j) dst[j] = kp[j];
+    }
+    // V
+    VRaw<D> vr;
+    load_v<D>(unit, P, t, lane, vr);
+    constexpr int NS = D / 64;
+    uint32_t vp[NS][8], vf[NS][2];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      VBases b = v_bases(unit, P, D, t, s);
+      decode_v_seg(vr.seg[s], b, vp[s], vf[s]);
+    }
+    if (hdr.vc) patch_v_tile<D>(vp, vf, unit, P, hdr, vrank, lds, pool, lane);
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const int d = lane + 64 * s;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        vd[(size_t)(t * kTile + 2 * k) * D + d] = (uint16_t)(vp[s][k] & 0xFFFFu);
+        vd[(size_t)(t * kTile + 2 * k + 1) * D + d] = (uint16_t)(vp[s][k] >> 16);
+      }
+    }
+  }
+}
+
+int launch_decompress(const uint8_t* units, const uint16_t* pool, const int32_t* page_ids, int n, int H,
+                      int P, int D, int num_pages, int lane_map, uint16_t* k_dst, uint16_t* v_dst,
+                      uint32_t* status, hipStream_t stream) {
+  dim3 grid((unsigned)n * H), block(64);
+  if (D == 128 && lane_map == 1)
+    hipLaunchKernelGGL((decompress_kernel<128, true>), grid, block, 0, stream, units, pool, page_ids, H, P,
+                       num_pages, k_dst, v_dst, status);
+  else if (D == 128)
+    hipLaunchKernelGGL((decompress_kernel<128, false>), grid, block, 0, stream, units, pool, page_ids, H, P,
+                       num_pages, k_dst, v_dst, status);
+  else if (D == 64 && lane_map == 0)
+    hipLaunchKernelGGL((decompress_kernel<64, false>), grid, block, 0, stream, units, pool, page_ids, H, P,
+                       num_pages, k_dst, v_dst, status);
+  else
+    return -2;
+  return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
+}  // namespace kvz

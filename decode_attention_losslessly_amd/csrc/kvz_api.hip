@@ -1,0 +1,240 @@
+// C ABI of libkvz: argument validation, split sizing and kernel launches. The library never
+// allocates device memory and never synchronises; every call enqueues on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include "kvz.h"
+#include "kvz_device.hpp"
+
+namespace kvz {
+int launch_decompress(const uint8_t* units, const uint16_t* pool, const int32_t* page_ids, int n, int H, int P,
+                      int D, int num_pages, int lane_map, uint16_t* k_dst, uint16_t* v_dst, uint32_t* status,
+                      hipStream_t stream);
+int launch_compress(const uint16_t* k_src, const uint16_t* v_src, const int32_t* ids, int n, int H, int P, int D,
+                    int num_pages, uint8_t* units, uint16_t* pool, int64_t pool_cap, uint64_t* cursor,
+                    uint32_t* status, hipStream_t stream);
+int launch_append(const uint16_t* k_new, const uint16_t* v_new, const int32_t* page_table, int max_pages,
+                  int32_t* seq_lens, int B, int H, int P, int D, int num_pages, uint8_t* units, uint16_t* pool,
+                  int64_t pool_cap, uint64_t* cursor, uint16_t* k_tail, uint16_t* v_tail, uint32_t* status,
+                  hipStream_t stream);
+int launch_attn_mha(const uint16_t* q, const uint8_t* units, const uint16_t* pool, const uint16_t* k_tail,
+                    const uint16_t* v_tail, const int32_t* page_table, int max_pages, const int32_t* seq_lens,
+                    int B, int H, int D, int P, int num_pages, int S, int C, float scale, float* ws_acc,
+                    float* ws_ml, uint32_t* status, hipStream_t stream);
+int launch_attn_gqa(const uint16_t* q, const uint8_t* units, const uint16_t* pool, const uint16_t* k_tail,
+                    const uint16_t* v_tail, const int32_t* page_table, int max_pages, const int32_t* seq_lens,
+                    int B, int Hq, int Hkv, int D, int P, int num_pages, int S, int C, float scale, float* ws_acc,
+                    float* ws_ml, uint32_t* status, hipStream_t stream);
+int launch_attn_dense_mha(const uint16_t* q, const uint16_t* k_pages, const uint16_t* v_pages, const int32_t* pt,
+                          int max_pages, const int32_t* seq_lens, int B, int H, int D, int P, int num_pages, int S,
+                          int C, float scale, float* ws_acc, float* ws_ml, uint32_t* status, hipStream_t stream);
+int launch_attn_dense_gqa(const uint16_t* q, const uint16_t* k_pages, const uint16_t* v_pages, const int32_t* pt,
+                          int max_pages, const int32_t* seq_lens, int B, int Hq, int Hkv, int D, int P,
+                          int num_pages, int S, int C, float scale, float* ws_acc, float* ws_ml, uint32_t* status,
+                          hipStream_t stream);
+int launch_merge(const float* ws_acc, const float* ws_ml, const int32_t* seq_lens, int B, int Hq, int D, int P,
+                 int max_pages, int S, int C, int dense, uint16_t* out, float* out_f32, hipStream_t stream);
+}  // namespace kvz
+
+namespace {
+
+constexpr int kTargetItems = 4096;   // work items aimed for: ~16 waves per CU on 256 CUs
+constexpr int kGqaRows = 8;          // query heads per grouped-query wave
+
+int work_items_per_split(int B, int Hq, int Hkv) {
+  const int grp = Hq / Hkv;
+  const int chunks = grp > 1 ? (grp + kGqaRows - 1) / kGqaRows : 1;
+  return B * Hkv * chunks;
+}
+
+int pages_per_split(int B, int Hq, int Hkv, int P, int max_pages, int pps) {
+  if (pps > 0) return pps;
+  const long items = work_items_per_split(B, Hq, Hkv);
+  const long s_target = items >= kTargetItems ? 1 : (kTargetItems + items - 1) / items;
+  const int min_c = P >= 64 ? 1 : 64 / P;
+  long c = (max_pages + s_target - 1) / s_target;
+  if (c < min_c) c = min_c;
+  if (c < 1) c = 1;
+  return (int)c;
+}
+
+int split_count(int max_pages, int C) { return max_pages > 0 ? (max_pages + C - 1) / C : 1; }
+
+bool shape_ok(int P, int D) { return P > 0 && P % 16 == 0 && D > 0 && D % 64 == 0; }
+
+bool cache_ok(const kvz_cache* c) {
+  return c && c->units && c->status && shape_ok(c->page_size, c->head_dim) && c->num_kv_heads > 0 &&
+         c->num_pages >= 0 && c->max_batch >= 0 && c->esc_capacity >= 0 && c->esc_cursor;
+}
+
+hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+}  // namespace
+
+extern "C" {
+
+size_t kvz_unit_bytes(int32_t P, int32_t D) { return shape_ok(P, D) ? kvz::unit_bytes(P, D) : 0; }
+size_t kvz_meta_bytes(int32_t P, int32_t D) { return shape_ok(P, D) ? kvz::meta_bytes(P, D) : 0; }
+int32_t kvz_inline_capacity(int32_t P, int32_t D) { return shape_ok(P, D) ? kvz::inline_capacity(P, D) : 0; }
+
+int32_t kvz_num_splits(int32_t B, int32_t H_q, int32_t H_kv, int32_t D, int32_t P, int32_t max_pages_per_seq,
+                       int32_t pps) {
+  if (B <= 0 || H_q <= 0 || H_kv <= 0 || H_q % H_kv || !shape_ok(P, D) || max_pages_per_seq < 0) return 0;
+  return split_count(max_pages_per_seq, pages_per_split(B, H_q, H_kv, P, max_pages_per_seq, pps));
+}
+
+size_t kvz_workspace_bytes(int32_t B, int32_t H_q, int32_t H_kv, int32_t D, int32_t P, int32_t max_pages_per_seq,
+                           int32_t pps) {
+  const int S = kvz_num_splits(B, H_q, H_kv, D, P, max_pages_per_seq, pps);
+  return (size_t)B * H_q * S * (D + 2) * sizeof(float);
+}
+
+int kvz_compress_pages(const kvz_cache* c, const uint16_t* k_src, const uint16_t* v_src, const int32_t* ids,
+                       int32_t n, void* stream) {
+  if (!cache_ok(c) || n < 0 || (n > 0 && (!k_src || !v_src || !ids))) return KVZ_ERR_INVALID_ARG;
+  if ((size_t)c->page_size * c->head_dim > 32768) return KVZ_ERR_UNSUPPORTED;
+  if (n == 0) return KVZ_OK;
+  return kvz::launch_compress(k_src, v_src, ids, n, c->num_kv_heads, c->page_size, c->head_dim, c->num_pages,
+                              c->units, c->esc_pool, c->esc_capacity, c->esc_cursor, c->status, as_stream(stream));
+}
+
+int kvz_append_token(const kvz_cache* c, const uint16_t* k_new, const uint16_t* v_new, const int32_t* page_table,
+                     int32_t max_pages, int32_t* seq_lens, int32_t B, void* stream) {
+  if (!cache_ok(c) || B < 0 || max_pages < 0 || !c->k_tail || !c->v_tail) return KVZ_ERR_INVALID_ARG;
+  if (B > 0 && (!k_new || !v_new || !page_table || !seq_lens)) return KVZ_ERR_INVALID_ARG;
+  if (B > c->max_batch) return KVZ_ERR_INVALID_ARG;
+  if ((size_t)c->page_size * c->head_dim > 32768) return KVZ_ERR_UNSUPPORTED;
+  if (B == 0) return KVZ_OK;
+  return kvz::launch_append(k_new, v_new, page_table, max_pages, seq_lens, B, c->num_kv_heads, c->page_size,
+                            c->head_dim, c->num_pages, c->units, c->esc_pool, c->esc_capacity, c->esc_cursor,
+                            c->k_tail, c->v_tail, c->status, as_stream(stream));
+}
+
+static int check_attention_shape(int B, int Hq, int Hkv, int D, int P, int max_pages) {
+  if (B < 0 || Hq <= 0 || Hkv <= 0 || max_pages < 0) return KVZ_ERR_INVALID_ARG;
+  if (!shape_ok(P, D) || Hq % Hkv) return KVZ_ERR_UNSUPPORTED;
+  if (D != 64 && D != 128) return KVZ_ERR_UNSUPPORTED;
+  const int grp = Hq / Hkv;
+  if (grp > 1 && (D != 128 || grp > 16)) return KVZ_ERR_UNSUPPORTED;
+  return KVZ_OK;
+}
+
+int kvz_decode_attention_splits(const uint16_t* q, const kvz_cache* c, const int32_t* page_table, int32_t max_pages,
+                                const int32_t* seq_lens, int32_t B, int32_t H_q, float sm_scale, int32_t pps,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  if (!cache_ok(c)) return KVZ_ERR_INVALID_ARG;
+  const int H = c->num_kv_heads, D = c->head_dim, P = c->page_size;
+  int rc = check_attention_shape(B, H_q, H, D, P, max_pages);
+  if (rc) return rc;
+  if (B == 0) return KVZ_OK;
+  if (!q || !page_table || !seq_lens || !workspace || !c->k_tail || !c->v_tail || pps < 0)
+    return KVZ_ERR_INVALID_ARG;
+  if (B > c->max_batch) return KVZ_ERR_INVALID_ARG;
+  const int C = pages_per_split(B, H_q, H, P, max_pages, pps);
+  const int S = split_count(max_pages, C);
+  if (workspace_bytes < (size_t)B * H_q * S * (D + 2) * sizeof(float)) return KVZ_ERR_WORKSPACE;
+  float* ws_acc = reinterpret_cast<float*>(workspace);
+  float* ws_ml = ws_acc + (size_t)B * H_q * S * D;
+  const float scale = sm_scale * 1.4426950408889634f;
+  if (H_q == H)
+    rc = kvz::launch_attn_mha(q, c->units, c->esc_pool, c->k_tail, c->v_tail, page_table, max_pages, seq_lens, B, H,
+                              D, P, c->num_pages, S, C, scale, ws_acc, ws_ml, c->status, as_stream(stream));
+  else
+    rc = kvz::launch_attn_gqa(q, c->units, c->esc_pool, c->k_tail, c->v_tail, page_table, max_pages, seq_lens, B,
+                              H_q, H, D, P, c->num_pages, S, C, scale, ws_acc, ws_ml, c->status, as_stream(stream));
+  return rc ? (rc == -2 ? KVZ_ERR_UNSUPPORTED : KVZ_ERR_HIP) : KVZ_OK;
+}
+
+int kvz_decode_attention_dense_splits(const uint16_t* q, const uint16_t* k_pages, const uint16_t* v_pages,
+                                      int32_t num_pages, int32_t H, int32_t D, int32_t P, const int32_t* page_table,
+                                      int32_t max_pages, const int32_t* seq_lens, int32_t B, int32_t H_q,
+                                      float sm_scale, int32_t pps, void* workspace, size_t workspace_bytes,
+                                      uint32_t* status, void* stream) {
+  int rc = check_attention_shape(B, H_q, H, D, P, max_pages);
+  if (rc) return rc;
+  if (B == 0) return KVZ_OK;
+  if (!q || !k_pages || !v_pages || !page_table || !seq_lens || !workspace || num_pages < 0 || pps < 0)
+    return KVZ_ERR_INVALID_ARG;
+  const int C = pages_per_split(B, H_q, H, P, max_pages, pps);
+  const int S = split_count(max_pages, C);
+  if (workspace_bytes < (size_t)B * H_q * S * (D + 2) * sizeof(float)) return KVZ_ERR_WORKSPACE;
+  float* ws_acc = reinterpret_cast<float*>(workspace);
+  float* ws_ml = ws_acc + (size_t)B * H_q * S * D;
+  const float scale = sm_scale * 1.4426950408889634f;
+  if (H_q == H)
+    rc = kvz::launch_attn_dense_mha(q, k_pages, v_pages, page_table, max_pages, seq_lens, B, H, D, P, num_pages, S, C,
+                                    scale, ws_acc, ws_ml, status, as_stream(stream));
+  else
+    rc = kvz::launch_attn_dense_gqa(q, k_pages, v_pages, page_table, max_pages, seq_lens, B, H_q, H, D, P, num_pages,
+                                    S, C, scale, ws_acc, ws_ml, status, as_stream(stream));
+  return rc ? (rc == -2 ? KVZ_ERR_UNSUPPORTED : KVZ_ERR_HIP) : KVZ_OK;
+}
+
+int kvz_merge_splits(const void* workspace, size_t workspace_bytes, const int32_t* seq_lens, int32_t B, int32_t H_q,
+                     int32_t H, int32_t D, int32_t P, int32_t max_pages, int32_t pps, int32_t dense, uint16_t* out,
+                     float* out_f32, void* stream) {
+  int rc = check_attention_shape(B, H_q, H, D, P, max_pages);
+  if (rc) return rc;
+  if (B == 0) return KVZ_OK;
+  if (!workspace || !seq_lens || !out || pps < 0) return KVZ_ERR_INVALID_ARG;
+  const int C = pages_per_split(B, H_q, H, P, max_pages, pps);
+  const int S = split_count(max_pages, C);
+  if (workspace_bytes < (size_t)B * H_q * S * (D + 2) * sizeof(float)) return KVZ_ERR_WORKSPACE;
+  const float* ws_acc = reinterpret_cast<const float*>(workspace);
+  const float* ws_ml = ws_acc + (size_t)B * H_q * S * D;
+  rc = kvz::launch_merge(ws_acc, ws_ml, seq_lens, B, H_q, D, P, max_pages, S, C, dense ? 1 : 0, out, out_f32,
+                         as_stream(stream));
+  return rc ? KVZ_ERR_HIP : KVZ_OK;
+}
+
+int kvz_decode_attention(const uint16_t* q, const kvz_cache* c, const int32_t* page_table, int32_t max_pages,
+                         const int32_t* seq_lens, int32_t B, int32_t H_q, float sm_scale, int32_t pps,
+                         uint16_t* out, float* out_f32, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!cache_ok(c)) return KVZ_ERR_INVALID_ARG;
+  if (B > 0 && !out) return KVZ_ERR_INVALID_ARG;
+  int rc = kvz_decode_attention_splits(q, c, page_table, max_pages, seq_lens, B, H_q, sm_scale, pps, workspace,
+                                       workspace_bytes, stream);
+  if (rc || B == 0) return rc;
+  return kvz_merge_splits(workspace, workspace_bytes, seq_lens, B, H_q, c->num_kv_heads, c->head_dim, c->page_size,
+                          max_pages, pps, 0, out, out_f32, stream);
+}
+
+int kvz_decode_attention_dense(const uint16_t* q, const uint16_t* k_pages, const uint16_t* v_pages, int32_t num_pages,
+                               int32_t H, int32_t D, int32_t P, const int32_t* page_table, int32_t max_pages,
+                               const int32_t* seq_lens, int32_t B, int32_t H_q, float sm_scale, int32_t pps,
+                               uint16_t* out, float* out_f32, void* workspace, size_t workspace_bytes,
+                               uint32_t* status, void* stream) {
+  if (B > 0 && !out) {
+    const int rc = check_attention_shape(B, H_q, H, D, P, max_pages);
+    return rc ? rc : KVZ_ERR_INVALID_ARG;
+  }
+  int rc = kvz_decode_attention_dense_splits(q, k_pages, v_pages, num_pages, H, D, P, page_table, max_pages, seq_lens,
+                                             B, H_q, sm_scale, pps, workspace, workspace_bytes, status, stream);
+  if (rc || B == 0) return rc;
+  return kvz_merge_splits(workspace, workspace_bytes, seq_lens, B, H_q, H, D, P, max_pages, pps, 1, out, out_f32,
+                          stream);
+}
+
+int kvz_decompress_pages(const kvz_cache* c, const int32_t* page_ids, int32_t n, int32_t lane_map, uint16_t* k_dst,
+                         uint16_t* v_dst, void* stream) {
+  if (!cache_ok(c) || n < 0 || (n > 0 && (!page_ids || !k_dst || !v_dst))) return KVZ_ERR_INVALID_ARG;
+  if (lane_map != 0 && lane_map != 1) return KVZ_ERR_INVALID_ARG;
+  const int D = c->head_dim;
+  if ((D != 64 && D != 128) || (lane_map == 1 && D != 128)) return KVZ_ERR_UNSUPPORTED;
+  if (n == 0) return KVZ_OK;
+  const int rc = kvz::launch_decompress(c->units, c->esc_pool, page_ids, n, c->num_kv_heads, c->page_size, D,
+                                        c->num_pages, lane_map, k_dst, v_dst, c->status, as_stream(stream));
+  return rc == -2 ? KVZ_ERR_UNSUPPORTED : (rc ? KVZ_ERR_HIP : KVZ_OK);
+}
+
+const char* kvz_strerror(int code) {
+  switch (code) {
+    case KVZ_OK: return "ok";
+    case KVZ_ERR_INVALID_ARG: return "invalid argument";
+    case KVZ_ERR_UNSUPPORTED: return "unsupported shape";
+    case KVZ_ERR_WORKSPACE: return "workspace too small";
+    case KVZ_ERR_HIP: return "HIP runtime error";
+    default: return "unknown error";
+  }
+}
+
+}  // extern "C"

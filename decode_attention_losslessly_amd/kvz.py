@@ -1,0 +1,253 @@
+"""Python binding of libkvz (include/kvz.h): argument marshalling only.
+
+Every step of the path runs in the HIP library; this module turns torch tensors into device
+pointers and the current HIP stream into the `stream` argument. PyTorch is used for device
+memory and streams only. There is no CPU fallback: without the built library every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkvz.so")
+
+KVZ_OK, KVZ_ERR_INVALID_ARG, KVZ_ERR_UNSUPPORTED, KVZ_ERR_WORKSPACE, KVZ_ERR_HIP = 0, -1, -2, -3, -4
+STATUS_ESC_POOL_FULL, STATUS_BAD_PAGE_ID, STATUS_SEQ_TOO_LONG = 1, 2, 4
+
+EXPORTS = ("kvz_unit_bytes", "kvz_meta_bytes", "kvz_inline_capacity", "kvz_workspace_bytes", "kvz_num_splits",
+           "kvz_compress_pages", "kvz_append_token", "kvz_decode_attention", "kvz_decode_attention_dense",
+           "kvz_decompress_pages", "kvz_strerror", "kvz_decode_attention_splits",
+           "kvz_decode_attention_dense_splits", "kvz_merge_splits")
+
+
+class KvzError(RuntimeError):
+    def __init__(self, code: int, what: str):
+        super().__init__(f"{what}: {strerror(code)} ({code})")
+        self.code = code
+
+
+class _CacheStruct(ctypes.Structure):
+    _fields_ = [("page_size", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("num_pages", ctypes.c_int32), ("max_batch", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("units", ctypes.c_void_p), ("esc_pool", ctypes.c_void_p), ("esc_capacity", ctypes.c_int64),
+                ("esc_cursor", ctypes.c_void_p), ("k_tail", ctypes.c_void_p), ("v_tail", ctypes.c_void_p),
+                ("status", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libkvz.so (torch is imported first so that one HIP runtime serves both)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run `python __graft_entry__.py build`")
+        L = ctypes.CDLL(LIB_PATH)
+        i32, i64, sz, f32, vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float, ctypes.c_void_p
+        cp = ctypes.POINTER(_CacheStruct)
+        sig = {
+            "kvz_unit_bytes": (sz, [i32, i32]),
+            "kvz_meta_bytes": (sz, [i32, i32]),
+            "kvz_inline_capacity": (i32, [i32, i32]),
+            "kvz_workspace_bytes": (sz, [i32, i32, i32, i32, i32, i32, i32]),
+            "kvz_num_splits": (i32, [i32, i32, i32, i32, i32, i32, i32]),
+            "kvz_compress_pages": (ctypes.c_int, [cp, vp, vp, vp, i32, vp]),
+            "kvz_append_token": (ctypes.c_int, [cp, vp, vp, vp, i32, vp, i32, vp]),
+            "kvz_decode_attention": (ctypes.c_int, [vp, cp, vp, i32, vp, i32, i32, f32, i32, vp, vp, vp, sz, vp]),
+            "kvz_decode_attention_dense": (ctypes.c_int, [vp, vp, vp, i32, i32, i32, i32, vp, i32, vp, i32, i32,
+                                                          f32, i32, vp, vp, vp, sz, vp, vp]),
+            "kvz_decompress_pages": (ctypes.c_int, [cp, vp, i32, i32, vp, vp, vp]),
+            "kvz_decode_attention_splits": (ctypes.c_int, [vp, cp, vp, i32, vp, i32, i32, f32, i32, vp, sz, vp]),
+            "kvz_decode_attention_dense_splits": (ctypes.c_int, [vp, vp, vp, i32, i32, i32, i32, vp, i32, vp, i32,
+                                                                 i32, f32, i32, vp, sz, vp, vp]),
+            "kvz_merge_splits": (ctypes.c_int, [vp, sz, vp, i32, i32, i32, i32, i32, i32, i32, i32, vp, vp, vp]),
+            "kvz_strerror": (ctypes.c_char_p, [ctypes.c_int]),
+        }
+        for name, (res, args) in sig.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def strerror(code: int) -> str:
+    return lib().kvz_strerror(code).decode()
+
+
+def _ptr(t: torch.Tensor | None):
+    if t is None:
+        return None
+    assert t.is_contiguous(), "tensors passed to libkvz must be contiguous"
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check(rc: int, what: str):
+    if rc != KVZ_OK:
+        raise KvzError(rc, what)
+
+
+# ---------------------------------------------------------------- sizes
+def unit_bytes(P: int, D: int) -> int:
+    return int(lib().kvz_unit_bytes(P, D))
+
+
+def meta_bytes(P: int, D: int) -> int:
+    return int(lib().kvz_meta_bytes(P, D))
+
+
+def inline_capacity(P: int, D: int) -> int:
+    return int(lib().kvz_inline_capacity(P, D))
+
+
+def workspace_bytes(B, Hq, Hkv, D, P, max_pages, pages_per_split=0) -> int:
+    return int(lib().kvz_workspace_bytes(B, Hq, Hkv, D, P, max_pages, pages_per_split))
+
+
+def num_splits(B, Hq, Hkv, D, P, max_pages, pages_per_split=0) -> int:
+    return int(lib().kvz_num_splits(B, Hq, Hkv, D, P, max_pages, pages_per_split))
+
+
+# ---------------------------------------------------------------- cache
+@dataclass
+class Cache:
+    """Device buffers of a compressed cache (owned by torch), described to libkvz per call."""
+    P: int
+    H: int
+    D: int
+    num_pages: int
+    max_batch: int
+    units: torch.Tensor        # uint8 [num_pages, H, unit_bytes]
+    esc_pool: torch.Tensor     # int16 [esc_capacity]
+    esc_cursor: torch.Tensor   # int64 [1]
+    k_tail: torch.Tensor       # int16 [max_batch, H, P, D]
+    v_tail: torch.Tensor
+    status: torch.Tensor       # int32 [1]
+
+    @classmethod
+    def allocate(cls, P: int, H: int, D: int, num_pages: int, max_batch: int, esc_capacity: int,
+                 device="cuda") -> "Cache":
+        U = unit_bytes(P, D)
+        if U == 0:
+            raise KvzError(KVZ_ERR_UNSUPPORTED, "Cache.allocate")
+        z = dict(device=device)
+        return cls(P, H, D, num_pages, max_batch,
+                   units=torch.zeros((num_pages, H, U), dtype=torch.uint8, **z),
+                   esc_pool=torch.zeros(max(1, esc_capacity), dtype=torch.int16, **z),
+                   esc_cursor=torch.zeros(1, dtype=torch.int64, **z),
+                   k_tail=torch.zeros((max_batch, H, P, D), dtype=torch.int16, **z),
+                   v_tail=torch.zeros((max_batch, H, P, D), dtype=torch.int16, **z),
+                   status=torch.zeros(1, dtype=torch.int32, **z))
+
+    @property
+    def esc_capacity(self) -> int:
+        return int(self.esc_pool.numel())
+
+    def struct(self) -> _CacheStruct:
+        return _CacheStruct(self.P, self.H, self.D, self.num_pages, self.max_batch, 0, self.units.data_ptr(),
+                            self.esc_pool.data_ptr(), self.esc_capacity, self.esc_cursor.data_ptr(),
+                            self.k_tail.data_ptr(), self.v_tail.data_ptr(), self.status.data_ptr())
+
+
+# ---------------------------------------------------------------- entry points
+def compress_pages(cache: Cache, k_src: torch.Tensor, v_src: torch.Tensor, dst_page_ids: torch.Tensor,
+                   stream=None) -> None:
+    """k_src, v_src: int16 [n, H, P, D]; dst_page_ids: int32 [n]."""
+    n = int(dst_page_ids.numel())
+    cs = cache.struct()
+    _check(lib().kvz_compress_pages(ctypes.byref(cs), _ptr(k_src), _ptr(v_src), _ptr(dst_page_ids), n,
+                                    _stream(stream)), "kvz_compress_pages")
+
+
+def append_token(cache: Cache, k_new: torch.Tensor, v_new: torch.Tensor, page_table: torch.Tensor,
+                 seq_lens: torch.Tensor, stream=None) -> None:
+    """k_new, v_new: int16 [B, H, D]; page_table int32 [B, max_pages]; seq_lens int32 [B] (updated)."""
+    B, max_pages = page_table.shape
+    cs = cache.struct()
+    _check(lib().kvz_append_token(ctypes.byref(cs), _ptr(k_new), _ptr(v_new), _ptr(page_table), max_pages,
+                                  _ptr(seq_lens), B, _stream(stream)), "kvz_append_token")
+
+
+def decode_attention(q: torch.Tensor, cache: Cache, page_table: torch.Tensor, seq_lens: torch.Tensor,
+                     sm_scale: float, out: torch.Tensor, out_f32: torch.Tensor | None = None,
+                     workspace: torch.Tensor | None = None, pages_per_split: int = 0, stream=None) -> None:
+    """q, out: int16 [B, Hq, D] (BF16 bits); out_f32 optional float32 [B, Hq, D]."""
+    B, Hq, D = q.shape
+    max_pages = page_table.shape[1]
+    need = workspace_bytes(B, Hq, cache.H, D, cache.P, max_pages, pages_per_split)
+    if workspace is None:
+        workspace = torch.empty(max(need, 4), dtype=torch.uint8, device=q.device)
+    cs = cache.struct()
+    _check(lib().kvz_decode_attention(_ptr(q), ctypes.byref(cs), _ptr(page_table), max_pages, _ptr(seq_lens), B, Hq,
+                                      float(sm_scale), pages_per_split, _ptr(out), _ptr(out_f32), _ptr(workspace),
+                                      workspace.numel() * workspace.element_size(), _stream(stream)),
+           "kvz_decode_attention")
+
+
+def decode_attention_dense(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Tensor, page_table: torch.Tensor,
+                           seq_lens: torch.Tensor, sm_scale: float, out: torch.Tensor,
+                           out_f32: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                           status: torch.Tensor | None = None, pages_per_split: int = 0, stream=None) -> None:
+    """k_pages, v_pages: int16 [num_pages, H, P, D]; other arguments as decode_attention."""
+    B, Hq, D = q.shape
+    num_pages, H, P, _ = k_pages.shape
+    max_pages = page_table.shape[1]
+    need = workspace_bytes(B, Hq, H, D, P, max_pages, pages_per_split)
+    if workspace is None:
+        workspace = torch.empty(max(need, 4), dtype=torch.uint8, device=q.device)
+    _check(lib().kvz_decode_attention_dense(_ptr(q), _ptr(k_pages), _ptr(v_pages), num_pages, H, D, P,
+                                            _ptr(page_table), max_pages, _ptr(seq_lens), B, Hq, float(sm_scale),
+                                            pages_per_split, _ptr(out), _ptr(out_f32), _ptr(workspace),
+                                            workspace.numel() * workspace.element_size(), _ptr(status),
+                                            _stream(stream)), "kvz_decode_attention_dense")
+
+
+def decode_attention_splits(q: torch.Tensor, cache: Cache, page_table: torch.Tensor, seq_lens: torch.Tensor,
+                            sm_scale: float, workspace: torch.Tensor, pages_per_split: int = 0, stream=None) -> None:
+    """First phase of decode_attention: the split kernel, partials into `workspace`."""
+    B, Hq, D = q.shape
+    cs = cache.struct()
+    _check(lib().kvz_decode_attention_splits(_ptr(q), ctypes.byref(cs), _ptr(page_table), page_table.shape[1],
+                                             _ptr(seq_lens), B, Hq, float(sm_scale), pages_per_split,
+                                             _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                             _stream(stream)), "kvz_decode_attention_splits")
+
+
+def decode_attention_dense_splits(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Tensor,
+                                  page_table: torch.Tensor, seq_lens: torch.Tensor, sm_scale: float,
+                                  workspace: torch.Tensor, status: torch.Tensor | None = None,
+                                  pages_per_split: int = 0, stream=None) -> None:
+    B, Hq, D = q.shape
+    num_pages, H, P, _ = k_pages.shape
+    _check(lib().kvz_decode_attention_dense_splits(_ptr(q), _ptr(k_pages), _ptr(v_pages), num_pages, H, D, P,
+                                                   _ptr(page_table), page_table.shape[1], _ptr(seq_lens), B, Hq,
+                                                   float(sm_scale), pages_per_split, _ptr(workspace),
+                                                   workspace.numel() * workspace.element_size(), _ptr(status),
+                                                   _stream(stream)), "kvz_decode_attention_dense_splits")
+
+
+def merge_splits(workspace: torch.Tensor, seq_lens: torch.Tensor, B: int, Hq: int, H: int, D: int, P: int,
+                 max_pages: int, out: torch.Tensor, out_f32: torch.Tensor | None = None, dense: bool = False,
+                 pages_per_split: int = 0, stream=None) -> None:
+    """Second phase: merges the partials left by one of the split kernels."""
+    _check(lib().kvz_merge_splits(_ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(seq_lens), B,
+                                  Hq, H, D, P, max_pages, pages_per_split, 1 if dense else 0, _ptr(out),
+                                  _ptr(out_f32), _stream(stream)), "kvz_merge_splits")
+
+
+def decompress_pages(cache: Cache, page_ids: torch.Tensor, k_dst: torch.Tensor, v_dst: torch.Tensor,
+                     lane_map: int = 0, stream=None) -> None:
+    """Test entry point: the attention kernels' in-register decode written out as BF16 bits."""
+    cs = cache.struct()
+    _check(lib().kvz_decompress_pages(ctypes.byref(cs), _ptr(page_ids), int(page_ids.numel()), lane_map,
+                                      _ptr(k_dst), _ptr(v_dst), _stream(stream)), "kvz_decompress_pages")

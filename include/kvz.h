@@ -1,0 +1,204 @@
+/*
+ * kvz — single-token decode attention over a paged BF16 KV cache kept in a lossless
+ * compressed form, for AMD Instinct MI355X (gfx950). C ABI.
+ *
+ * The method (ZipFusion: Fusing Lossless KV Decompression with Attention for Efficient LLM
+ * Decoding, paperlayer.ai summary of arXiv 2610.33719v1):
+ *   - the cache format is lossless: every BF16 bit pattern comes back (§II.A "KV Cache and
+ *     BF16"; §III.B "Lossless KV Cache Format");
+ *   - attention reads the compressed blocks and rebuilds each value in registers with plain
+ *     bit operations, with no separate decompression pass and no uncompressed copy in device
+ *     memory (§III.C "Attention over the Compressed KV Cache");
+ *   - partially filled pages stay uncompressed so decoding can append to them, and a page is
+ *     compressed once it is full (§III.D "KV Cache Management and Scheduling");
+ *   - split results are merged by a second reduction and that merge is part of attention's
+ *     cost (§IV.B "Attention Kernel Performance").
+ *
+ * Format (this library's own layout). P = page size in tokens (multiple of 16), D = head
+ * dimension (multiple of 64), G = D / 64, H = number of KV heads.
+ *   group     the 64 values of one token row of one head, dims [64g, 64g + 64)
+ *   sm byte   (sign << 7) | 7-bit mantissa, kept for every value
+ *   base      per group: the group exponent with the most group exponents in [base, base+14],
+ *             the smallest such exponent on ties
+ *   offset    4 bits: exponent - base when 0..14, else 15 = escape; the value's raw 16 bits
+ *             then sit in the block's escape list
+ *   tile      16 consecutive tokens of a page; storage position inside a tile is
+ *             tok*D + d for K (token-major) and d*16 + tok for V (dim-major)
+ *   block     one (page, head, K or V): per tile, 16*D sm bytes in storage order, then 2*D
+ *             little-endian u32 offset words; word w holds position 8w+2k in bits 4k..4k+3
+ *             and position 8w+2k+1 in bits 16+4k..16+4k+3 (k = 0..3)
+ *   escapes   a block's escaped values, in storage order
+ *   unit      one (page, head), kvz_unit_bytes(P, D) bytes at offset (page*H + head) * that:
+ *             meta region of kvz_meta_bytes(P, D) bytes, then the K block, then the V block
+ *   meta      [0, P*G)         K bases, byte tile*16*G + g*16 + tok
+ *             [P*G, 2*P*G)     V bases, same order
+ *             [2PG, 2PG+4)     u32 number of K escapes
+ *             [2PG+4, 2PG+8)   u32 number of V escapes
+ *             [2PG+8, 2PG+16)  u64 offset (in u16 elements) of the unit's escapes in the pool,
+ *                              or all ones when they are inline
+ *             [2PG+16, end)    inline escapes, K's then V's, when all of them fit
+ *                              (kvz_inline_capacity); unused bytes are zero
+ *   tail      per request row r and head h, P raw BF16 rows [P][D] (token-major, K and V
+ *             alike) holding the L mod P newest tokens
+ *
+ * Conventions for every entry point:
+ *   - pointers are device pointers unless marked (host); the caller owns all memory;
+ *   - calls are asynchronous on `stream` (a hipStream_t passed as void*; NULL = the default
+ *     stream); the library never allocates device memory and never synchronises;
+ *   - a negative return value means nothing was enqueued; see kvz_strerror;
+ *   - device-side conditions set sticky bits in *status with atomic OR and leave the
+ *     affected outputs unspecified: KVZ_STATUS_* below;
+ *   - calls on different streams must not write the same memory.
+ */
+#ifndef KVZ_H
+#define KVZ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  KVZ_OK = 0,
+  KVZ_ERR_INVALID_ARG = -1, /* null pointer, negative size, bad stride */
+  KVZ_ERR_UNSUPPORTED = -2, /* shape outside what the kernels handle (see each call) */
+  KVZ_ERR_WORKSPACE = -3,   /* workspace smaller than kvz_workspace_bytes(...) */
+  KVZ_ERR_HIP = -4          /* a HIP runtime call failed */
+};
+
+enum {
+  KVZ_STATUS_ESC_POOL_FULL = 1u,  /* a unit's escapes did not fit the pool; its escaped
+                                     values decode to unspecified values */
+  KVZ_STATUS_BAD_PAGE_ID = 2u,    /* a page id outside [0, num_pages) was met and skipped */
+  KVZ_STATUS_SEQ_TOO_LONG = 4u    /* seq_len > max_pages_per_seq * P (clamped) */
+};
+
+/* Host-side description of a compressed cache; read at call time, not kept. */
+typedef struct kvz_cache {
+  int32_t page_size;     /* P: multiple of 16 */
+  int32_t num_kv_heads;  /* H */
+  int32_t head_dim;      /* D: multiple of 64 */
+  int32_t num_pages;     /* unit slots per head */
+  int32_t max_batch;     /* tail rows */
+  int32_t reserved;
+  uint8_t* units;        /* [num_pages][H][kvz_unit_bytes(P, D)], 256-byte aligned */
+  uint16_t* esc_pool;    /* escape pool, esc_capacity u16 elements */
+  int64_t esc_capacity;
+  uint64_t* esc_cursor;  /* [1] u16 elements of the pool in use; bumped by the library */
+  uint16_t* k_tail;      /* [max_batch][H][P][D] raw BF16 */
+  uint16_t* v_tail;      /* [max_batch][H][P][D] raw BF16 */
+  uint32_t* status;      /* [1] sticky KVZ_STATUS_* bits */
+} kvz_cache;
+
+/* Sizes of the format (host functions, no device work). */
+size_t kvz_unit_bytes(int32_t P, int32_t D);
+size_t kvz_meta_bytes(int32_t P, int32_t D);
+int32_t kvz_inline_capacity(int32_t P, int32_t D);
+
+/* Bytes of scratch kvz_decode_attention / kvz_decode_attention_dense need: split partials
+ * (m, l, acc[D]) in float for every (request, query head, split). pages_per_split = 0 lets the
+ * library choose; the same value must be passed to the attention call. */
+size_t kvz_workspace_bytes(int32_t B, int32_t H_q, int32_t H_kv, int32_t D, int32_t P,
+                           int32_t max_pages_per_seq, int32_t pages_per_split);
+
+/* Number of splits the attention calls use for these arguments (host function). */
+int32_t kvz_num_splits(int32_t B, int32_t H_q, int32_t H_kv, int32_t D, int32_t P,
+                       int32_t max_pages_per_seq, int32_t pages_per_split);
+
+/* Compresses n full dense pages into units (the format above; §III.B, §III.D: a page is
+ * encoded once it is full).
+ *   k_src, v_src   [n][H][P][D] raw BF16, token-major
+ *   dst_page_ids   [n] unit slots to write, each in [0, num_pages)
+ * Escapes that do not fit inline are appended to the pool at *esc_cursor (bumped atomically,
+ * so their place in the pool depends on scheduling; everything else is deterministic).
+ * Errors: KVZ_ERR_INVALID_ARG, KVZ_ERR_UNSUPPORTED (P % 16, D % 64). Device status:
+ * ESC_POOL_FULL, BAD_PAGE_ID. */
+int kvz_compress_pages(const kvz_cache* cache, const uint16_t* k_src, const uint16_t* v_src,
+                       const int32_t* dst_page_ids, int32_t n, void* stream);
+
+/* Appends one token to each of B requests (§III.D: decoding appends to the uncompressed
+ * partial page). For request row r with L = seq_lens[r]: writes k_new[r], v_new[r] into tail
+ * row L mod P of row r; when that fills the tail (L mod P == P-1) the tail is compressed into
+ * unit page_table[r][L / P] (which the caller has set to a free slot); then seq_lens[r] = L+1.
+ *   k_new, v_new   [B][H][D] raw BF16
+ *   page_table     [B][max_pages_per_seq]
+ *   seq_lens       [B], updated on the device
+ * B must not exceed max_batch. Errors: KVZ_ERR_INVALID_ARG, KVZ_ERR_UNSUPPORTED. Device status:
+ * ESC_POOL_FULL, BAD_PAGE_ID, SEQ_TOO_LONG (no write). */
+int kvz_append_token(const kvz_cache* cache, const uint16_t* k_new, const uint16_t* v_new,
+                     const int32_t* page_table, int32_t max_pages_per_seq, int32_t* seq_lens,
+                     int32_t B, void* stream);
+
+/* Decode attention over the compressed cache (§III.C: values rebuilt in registers inside the
+ * kernel; §IV.B: split partials merged by a second kernel).
+ *   q            [B][H_q][D] BF16; query head h reads KV head h / (H_q / H)
+ *   page_table   [B][max_pages_per_seq]; entries i < seq_lens[r] / P are units
+ *   seq_lens     [B] tokens per request: full pages, then seq_lens[r] mod P tail rows of row r
+ *   out          [B][H_q][D] BF16 (round to nearest even); a request with no token gets zeros
+ *   out_f32      nullable [B][H_q][D] float, the same result before rounding
+ *   workspace    >= kvz_workspace_bytes(B, H_q, H, D, P, max_pages_per_seq, pages_per_split)
+ * Supported: D in {64, 128}; for H_q > H (grouped queries) D = 128 and H_q / H <= 16.
+ * Errors: KVZ_ERR_INVALID_ARG, KVZ_ERR_UNSUPPORTED, KVZ_ERR_WORKSPACE. Device status:
+ * BAD_PAGE_ID, SEQ_TOO_LONG. */
+int kvz_decode_attention(const uint16_t* q, const kvz_cache* cache, const int32_t* page_table,
+                         int32_t max_pages_per_seq, const int32_t* seq_lens, int32_t B,
+                         int32_t H_q, float sm_scale, int32_t pages_per_split, uint16_t* out,
+                         float* out_f32, void* workspace, size_t workspace_bytes, void* stream);
+
+/* The same attention over an uncompressed paged cache: the baseline the compressed path is
+ * measured against (the pages compare with production FlashInfer, §IV.B).
+ *   k_pages, v_pages  [num_pages][H][P][D] raw BF16, token-major
+ *   page_table        [B][max_pages_per_seq]; the first ceil(seq_lens[r] / P) entries are used
+ *   status            nullable [1] sticky bits (BAD_PAGE_ID, SEQ_TOO_LONG)
+ * Other arguments as kvz_decode_attention. Supported: D in {64, 128}; H_q / H <= 16. */
+int kvz_decode_attention_dense(const uint16_t* q, const uint16_t* k_pages,
+                               const uint16_t* v_pages, int32_t num_pages, int32_t H,
+                               int32_t D, int32_t P, const int32_t* page_table,
+                               int32_t max_pages_per_seq, const int32_t* seq_lens, int32_t B,
+                               int32_t H_q, float sm_scale, int32_t pages_per_split,
+                               uint16_t* out, float* out_f32, void* workspace,
+                               size_t workspace_bytes, uint32_t* status, void* stream);
+
+/* The two phases of kvz_decode_attention / kvz_decode_attention_dense as separate calls, for
+ * callers that schedule them apart (and for timing the split kernel alone).
+ *   kvz_decode_attention_splits        the compressed split kernel: partials into workspace
+ *   kvz_decode_attention_dense_splits  the dense split kernel: partials into workspace
+ *   kvz_merge_splits                   merges the partials of either into out / out_f32;
+ *                                      dense = 1 when they came from the dense kernel
+ * Arguments mean what they mean in the one-call forms; B, H_q, H, D, P, max_pages_per_seq and
+ * pages_per_split must be the same in both phases. Errors and status as the one-call forms. */
+int kvz_decode_attention_splits(const uint16_t* q, const kvz_cache* cache, const int32_t* page_table,
+                                int32_t max_pages_per_seq, const int32_t* seq_lens, int32_t B,
+                                int32_t H_q, float sm_scale, int32_t pages_per_split,
+                                void* workspace, size_t workspace_bytes, void* stream);
+int kvz_decode_attention_dense_splits(const uint16_t* q, const uint16_t* k_pages,
+                                      const uint16_t* v_pages, int32_t num_pages, int32_t H,
+                                      int32_t D, int32_t P, const int32_t* page_table,
+                                      int32_t max_pages_per_seq, const int32_t* seq_lens,
+                                      int32_t B, int32_t H_q, float sm_scale,
+                                      int32_t pages_per_split, void* workspace,
+                                      size_t workspace_bytes, uint32_t* status, void* stream);
+int kvz_merge_splits(const void* workspace, size_t workspace_bytes, const int32_t* seq_lens,
+                     int32_t B, int32_t H_q, int32_t H, int32_t D, int32_t P,
+                     int32_t max_pages_per_seq, int32_t pages_per_split, int32_t dense,
+                     uint16_t* out, float* out_f32, void* stream);
+
+/* Test entry point: runs the attention kernels' own in-register decode on n units and writes
+ * the rebuilt values, so that decode can be compared bit for bit.
+ *   page_ids      [n]
+ *   lane_map      0: the lane layout of the multi-head kernel, 1: that of the grouped-query
+ *                 kernel (D = 128 only) for K
+ *   k_dst, v_dst  [n][H][P][D] raw BF16, token-major
+ * Supported: D in {64, 128}. */
+int kvz_decompress_pages(const kvz_cache* cache, const int32_t* page_ids, int32_t n,
+                         int32_t lane_map, uint16_t* k_dst, uint16_t* v_dst, void* stream);
+
+const char* kvz_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVZ_H */

@@ -11,3 +11,31 @@ if ROOT not in sys.path:
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
     config.addinivalue_line("markers", "slow: full-size workload")
+
+
+_FULL = {}
+
+
+@pytest.fixture(scope="session")
+def full_workloads():
+    """Full-size workload `cfg`, built once: (workload, K pages, V pages, device cache, seq_lens).
+    Only the most recent one is kept, so host and device memory hold one full cache at a time."""
+    def get(cfg):
+        if cfg not in _FULL:
+            import gc
+
+            import torch
+
+            from kvz_testlib import build_cache
+            from synth import make_workload
+            _FULL.clear()
+            gc.collect()
+            torch.cuda.empty_cache()
+            w = make_workload(cfg)
+            print(f"\n[full workload {cfg}: {w.name}, generating {w.num_pages} pages]", flush=True)
+            kp, vp = w.pages(0), w.pages(1)
+            cache, lens = build_cache(w, kp, vp)
+            _FULL[cfg] = (w, kp, vp, cache, lens)
+        return _FULL[cfg]
+    yield get
+    _FULL.clear()

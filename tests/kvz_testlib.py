@@ -1,0 +1,111 @@
+"""Helpers shared by the GPU tests: moving workloads to the device, building caches through the
+library, and checking outputs against the CPU oracle's tolerance."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import decode_attention_losslessly_amd as kvz
+from oracle import attention as oa
+from oracle import codec
+
+DEV = torch.device("cuda:0")
+
+BF16_ABS, BF16_REL = 2e-2, 2.0 ** -7     # |out - o| <= max(2e-2, 2^-7 |o|)
+F32_NORMWISE = 1e-4                       # max_d |out32 - o| <= 1e-4 max_d |o|
+
+
+def dev(a: np.ndarray) -> torch.Tensor:
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(a).to(DEV)
+
+
+def host16(t: torch.Tensor) -> np.ndarray:
+    return t.cpu().numpy().view(np.uint16)
+
+
+def escape_capacity(w, n_units: int) -> int:
+    frac = 0.6 if w.k_dist == "log_uniform" else 0.02
+    return int(n_units * 2 * w.P * w.D * frac) + (1 << 16)
+
+
+def full_page_ids(w, lens=None):
+    """(request, logical page) -> physical id of every full page, in request order."""
+    lens = w.seq_lens if lens is None else lens
+    return np.array([w.page_table[r, i] for r in range(w.B) for i in range(int(lens[r]) // w.P)], np.int32)
+
+
+def tails(w, kp, vp, lens=None):
+    lens = w.seq_lens if lens is None else lens
+    tk = np.zeros((w.B, w.Hkv, w.P, w.D), np.uint16)
+    tv = np.zeros_like(tk)
+    for r in range(w.B):
+        L = int(lens[r])
+        if L % w.P:
+            pid = w.page_table[r, L // w.P]
+            tk[r], tv[r] = kp[pid], vp[pid]
+    return tk, tv
+
+
+def build_cache(w, kp, vp, esc_capacity=None):
+    """Compressed cache of workload w on the device: full pages through kvz_compress_pages, the
+    tail rows copied raw, then the appended token (if any) through kvz_append_token.
+    Returns (cache, seq_lens tensor)."""
+    L0 = w.seq_lens - w.n_append
+    ids = full_page_ids(w, L0)
+    cap = escape_capacity(w, max(1, len(ids) * w.Hkv)) if esc_capacity is None else esc_capacity
+    cache = kvz.Cache.allocate(w.P, w.Hkv, w.D, w.num_pages, w.B, cap, device=DEV)
+    if len(ids):
+        step = max(1, (1 << 30) // (w.Hkv * w.P * w.D * 2))      # ~1 GiB of each of K, V per copy
+        for s in range(0, len(ids), step):
+            sl = ids[s:s + step]
+            kvz.compress_pages(cache, dev(kp[sl]), dev(vp[sl]), dev(sl))
+            torch.cuda.synchronize()
+    tk, tv = tails(w, kp, vp, L0)
+    cache.k_tail.copy_(dev(tk))
+    cache.v_tail.copy_(dev(tv))
+    lens = dev(L0.astype(np.int32))
+    if w.n_append:
+        kvz.append_token(cache, dev(w.appended(0)), dev(w.appended(1)), dev(w.page_table), lens)
+    torch.cuda.synchronize()
+    return cache, lens
+
+
+def oracle_rows(w, kp, vp, q, rows):
+    """fp64 oracle outputs for (request, query head) pairs, from the raw tokens."""
+    from oracle import c_oracle
+    return c_oracle.dense_attention_rows(q, kp, vp, w.page_table, w.seq_lens, w.sm_scale, rows)
+
+
+def check_rows(out_bf16: np.ndarray, out_f32: np.ndarray, ref: np.ndarray, what: str):
+    """out_bf16 uint16 [n, D], out_f32 float32 [n, D], ref float64 [n, D]."""
+    got = oa.bf16_to_f64(out_bf16)
+    tol = np.maximum(BF16_ABS, BF16_REL * np.abs(ref))
+    bad = np.abs(got - ref) > tol
+    assert not bad.any(), f"{what}: bf16 out of tolerance at {np.argwhere(bad)[:5].tolist()}, " \
+                          f"max err {np.abs(got - ref).max():.3e}"
+    nrm = np.abs(ref).max(axis=-1)
+    err = np.abs(out_f32.astype(np.float64) - ref).max(axis=-1)
+    worst = float((err / np.where(nrm > 0, nrm, 1.0)).max())
+    assert np.all(err <= F32_NORMWISE * nrm + 1e-30), f"{what}: fp32 normwise error {worst:.3e}"
+    return worst
+
+
+def unit_equal(gpu_unit: np.ndarray, gpu_pool: np.ndarray, ref_unit: np.ndarray, ref_pool: np.ndarray, P, D):
+    """Byte equality of a unit except the pool offset, plus equality of the escape lists."""
+    h = 2 * P * (D // 64)
+    a = gpu_unit.copy()
+    b = ref_unit.copy()
+    ka, va, oa_ = codec.unit_header(a, P, D)
+    kb, vb, ob = codec.unit_header(b, P, D)
+    if (ka, va) != (kb, vb) or (oa_ == codec.INLINE) != (ob == codec.INLINE):
+        return False
+    a[h + 8:h + 16] = 0
+    b[h + 8:h + 16] = 0
+    if not np.array_equal(a, b):
+        return False
+    ea = codec.unit_escapes(gpu_unit, gpu_pool, P, D)
+    eb = codec.unit_escapes(ref_unit, ref_pool, P, D)
+    return all(np.array_equal(x, y) for x, y in zip(ea, eb))

@@ -1,0 +1,89 @@
+"""The C ABI library loads, exports every entry point include/kvz.h declares, and its host-side
+size and argument checks agree with the format and with the oracle. No device work is done."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch  # noqa: F401  (one HIP runtime for torch and libkvz)
+
+import decode_attention_losslessly_amd as kvz
+from decode_attention_losslessly_amd import kvz as binding
+from oracle import codec
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvz.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kvz_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = _declared()
+    assert len(names) >= 10
+    L = ctypes.CDLL(binding.LIB_PATH)
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(binding.EXPORTS) == set(names)
+
+
+@pytest.mark.parametrize("P,D", [(16, 64), (16, 128), (32, 128), (256, 64), (16, 256)])
+def test_sizes_agree_with_format(P, D):
+    assert kvz.unit_bytes(P, D) == codec.unit_bytes(P, D)
+    assert kvz.meta_bytes(P, D) == codec.meta_bytes(P, D)
+    assert kvz.inline_capacity(P, D) == codec.inline_capacity(P, D)
+
+
+def test_unsupported_shapes_have_zero_size():
+    assert kvz.unit_bytes(15, 128) == 0
+    assert kvz.unit_bytes(16, 96) == 0
+
+
+def test_split_geometry():
+    # the workspace holds (D + 2) floats per (request, query head, split)
+    for args in [(32, 32, 32, 128, 16, 513), (1, 32, 32, 128, 16, 256), (64, 28, 4, 128, 16, 512),
+                 (4, 32, 32, 128, 16, 2048), (1, 2, 2, 64, 256, 1)]:
+        S = kvz.num_splits(*args)
+        B, Hq, _, D, _, mp = args
+        assert S >= 1
+        assert kvz.workspace_bytes(*args) == B * Hq * S * (D + 2) * 4
+        assert kvz.num_splits(*args, pages_per_split=mp) == 1
+        assert kvz.num_splits(*args, pages_per_split=1) == mp
+    # batch-1 context: enough splits to spread one request over the chip
+    assert kvz.num_splits(1, 32, 32, 128, 16, 256) >= 32
+
+
+def test_invalid_arguments_enqueue_nothing():
+    L = binding.lib()
+    assert L.kvz_compress_pages(None, None, None, None, 0, None) == binding.KVZ_ERR_INVALID_ARG
+    assert L.kvz_decode_attention(None, None, None, 0, None, 0, 1, 1.0, 0, None, None, None, 0, None) == \
+        binding.KVZ_ERR_INVALID_ARG
+    # shape checks happen before any pointer is used
+    rc = L.kvz_decode_attention_dense(None, None, None, 0, 4, 96, 16, None, 0, None, 1, 4, 1.0, 0, None, None, None,
+                                      0, None, None)
+    assert rc == binding.KVZ_ERR_UNSUPPORTED
+    rc = L.kvz_decode_attention_dense(None, None, None, 0, 4, 128, 16, None, 0, None, 1, 6, 1.0, 0, None, None, None,
+                                      0, None, None)
+    assert rc == binding.KVZ_ERR_UNSUPPORTED       # 6 query heads on 4 KV heads
+    rc = L.kvz_decode_attention_dense(None, None, None, 0, 1, 128, 16, None, 0, None, 1, 32, 1.0, 0, None, None,
+                                      None, 0, None, None)
+    assert rc == binding.KVZ_ERR_UNSUPPORTED       # group of 32 > 16
+    assert kvz.kvz.strerror(binding.KVZ_ERR_WORKSPACE) == "workspace too small"
+
+
+def test_cache_struct_layout_matches_header():
+    # field order and sizes of kvz_cache: 6 int32, then pointers/int64 (8 bytes each)
+    s = binding._CacheStruct
+    assert ctypes.sizeof(s) == 6 * 4 + 7 * 8
+    assert s.units.offset == 24 and s.status.offset == 24 + 6 * 8
+
+
+def test_package_has_no_cpu_fallback():
+    src = open(os.path.join(ROOT, "decode_attention_losslessly_amd", "kvz.py")).read()
+    assert "oracle" not in src
+    for f in os.listdir(os.path.join(ROOT, "decode_attention_losslessly_amd")):
+        if f.endswith(".py"):
+            assert "import oracle" not in open(os.path.join(ROOT, "decode_attention_losslessly_amd", f)).read()

@@ -1,0 +1,75 @@
+"""GPU append parity: kvz_append_token writes the new row into the uncompressed tail and, when the
+tail fills, compresses it into the unit the page table names (ZipFusion summary, §III.D "KV Cache
+Management and Scheduling": partially filled pages stay uncompressed; a full page is compressed).
+The units it writes are byte-exact against the oracle and attention afterwards matches it."""
+import numpy as np
+import pytest
+import torch
+
+import decode_attention_losslessly_amd as kvz
+from oracle import c_oracle
+from synth import make_workload
+
+from kvz_testlib import DEV, check_rows, dev, full_page_ids, host16, oracle_rows, tails, unit_equal
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("cfg,H,Hq", [(3, 4, 4), (4, 2, 14), (5, 2, 2)])
+def test_append_across_page_fill(cfg, H, Hq):
+    n_app = 19
+    L0 = np.array([14, 15, 31, 0, 40], np.int32)
+    w = make_workload(cfg, B=5, lens=L0 + n_app, Hq=Hq, Hkv=H, n_append=0)
+    kp, vp = w.pages(0), w.pages(1)
+    ids0 = full_page_ids(w, L0)
+    cache = kvz.Cache.allocate(w.P, w.Hkv, w.D, w.num_pages, w.B, esc_capacity=1 << 22, device=DEV)
+    if len(ids0):
+        kvz.compress_pages(cache, dev(kp[ids0]), dev(vp[ids0]), dev(ids0))
+    tk, tv = tails(w, kp, vp, L0)
+    cache.k_tail.copy_(dev(tk))
+    cache.v_tail.copy_(dev(tv))
+    lens = dev(L0)
+    table = dev(w.page_table)
+    for j in range(n_app):
+        kn = np.stack([w.token(r, int(L0[r]) + j, 0) for r in range(w.B)])
+        vn = np.stack([w.token(r, int(L0[r]) + j, 1) for r in range(w.B)])
+        kvz.append_token(cache, dev(kn), dev(vn), table, lens)
+    torch.cuda.synchronize()
+    assert int(cache.status.item()) == 0
+    assert np.array_equal(lens.cpu().numpy(), L0 + n_app)
+    # every full page (old and newly filled) matches the oracle's encoding of the raw page
+    ids = full_page_ids(w)
+    units = cache.units.cpu().numpy()
+    pool = cache.esc_pool.cpu().numpy().view(np.uint16)
+    ref_units, ref_pool, _ = c_oracle.encode_pages(kp[ids], vp[ids])
+    for i, pid in enumerate(ids):
+        for h in range(w.Hkv):
+            assert unit_equal(units[pid, h], pool, ref_units[i, h], ref_pool, w.P, w.D), (pid, h)
+    # tails hold the rows of the partial page
+    tk2, tv2 = tails(w, kp, vp)
+    Lf = L0 + n_app
+    gk, gv = host16(cache.k_tail), host16(cache.v_tail)
+    for r in range(w.B):
+        rows = int(Lf[r]) % w.P
+        assert np.array_equal(gk[r, :, :rows], tk2[r, :, :rows])
+        assert np.array_equal(gv[r, :, :rows], tv2[r, :, :rows])
+    # attention over the appended cache
+    q = w.q()
+    out = torch.zeros((w.B, w.Hq, w.D), dtype=torch.int16, device=DEV)
+    out32 = torch.zeros((w.B, w.Hq, w.D), dtype=torch.float32, device=DEV)
+    kvz.decode_attention(dev(q), cache, table, lens, w.sm_scale, out, out32)
+    torch.cuda.synchronize()
+    rows = [(r, h) for r in range(w.B) for h in range(w.Hq)]
+    ref = oracle_rows(w, kp, vp, q, rows)
+    check_rows(host16(out).reshape(-1, w.D), out32.cpu().numpy().reshape(-1, w.D), ref, "after append")
+
+
+def test_append_past_page_table_sets_status():
+    w = make_workload(2, B=1, L=32, Hq=2, Hkv=2)
+    cache = kvz.Cache.allocate(w.P, w.Hkv, w.D, w.num_pages, 1, esc_capacity=1 << 12, device=DEV)
+    lens = dev(np.array([32], np.int32))                     # 2 pages of 16: the table is full
+    kn = dev(np.zeros((1, 2, w.D), np.uint16))
+    kvz.append_token(cache, kn, kn, dev(w.page_table), lens)
+    torch.cuda.synchronize()
+    assert int(cache.status.item()) & kvz.kvz.STATUS_SEQ_TOO_LONG
+    assert int(lens.item()) == 32

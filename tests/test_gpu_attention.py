@@ -1,0 +1,211 @@
+"""GPU attention parity: the compressed kernels (kvz_decode_attention) and the dense baseline
+(kvz_decode_attention_dense) against the fp64 CPU oracle, within the stated tolerance:
+|out_bf16 - o| <= max(2e-2, 2^-7 |o|) per element and max_d |out_f32 - o| <= 1e-4 max_d |o| per row."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import decode_attention_losslessly_amd as kvz
+from oracle import attention as oa
+from synth import f32_to_bf16_bits, make_workload
+
+from kvz_testlib import DEV, build_cache, check_rows, dev, host16, oracle_rows
+
+pytestmark = pytest.mark.gpu
+
+SMALL = {
+    1: dict(),
+    2: dict(L=333),
+    3: dict(B=3, L=161),
+    4: dict(B=6, lens=[1, 15, 16, 17, 300, 1024]),
+    5: dict(B=2, L=517),
+}
+
+
+def _run(w, cache, lens, q, dense_pages=None, pages_per_split=0):
+    out = torch.zeros((w.B, w.Hq, w.D), dtype=torch.int16, device=DEV)
+    out32 = torch.full((w.B, w.Hq, w.D), float("nan"), dtype=torch.float32, device=DEV)
+    if dense_pages is None:
+        kvz.decode_attention(dev(q), cache, dev(w.page_table), lens, w.sm_scale, out, out32,
+                             pages_per_split=pages_per_split)
+    else:
+        status = torch.zeros(1, dtype=torch.int32, device=DEV)
+        kvz.decode_attention_dense(dev(q), dense_pages[0], dense_pages[1], dev(w.page_table), lens, w.sm_scale, out,
+                                   out32, status=status, pages_per_split=pages_per_split)
+        torch.cuda.synchronize()
+        assert int(status.item()) == 0
+    torch.cuda.synchronize()
+    return host16(out), out32.cpu().numpy()
+
+
+def _all_rows(w):
+    return [(r, h) for r in range(w.B) for h in range(w.Hq)]
+
+
+@pytest.mark.parametrize("cfg", sorted(SMALL))
+def test_compressed_matches_oracle(cfg):
+    w = make_workload(cfg, **SMALL[cfg])
+    kp, vp = w.pages(0), w.pages(1)
+    cache, lens = build_cache(w, kp, vp)
+    q = w.q()
+    o16, o32 = _run(w, cache, lens, q)
+    assert int(cache.status.item()) == 0
+    rows = _all_rows(w)
+    ref = oracle_rows(w, kp, vp, q, rows)
+    check_rows(o16.reshape(-1, w.D), o32.reshape(-1, w.D), ref, f"cfg{cfg} compressed")
+
+
+@pytest.mark.parametrize("cfg", sorted(SMALL))
+def test_dense_matches_oracle(cfg):
+    w = make_workload(cfg, **SMALL[cfg])
+    kp, vp = w.pages(0), w.pages(1)
+    q = w.q()
+    o16, o32 = _run(w, None, dev(w.seq_lens), q, dense_pages=(dev(kp), dev(vp)))
+    rows = _all_rows(w)
+    ref = oracle_rows(w, kp, vp, q, rows)
+    check_rows(o16.reshape(-1, w.D), o32.reshape(-1, w.D), ref, f"cfg{cfg} dense")
+
+
+@pytest.mark.parametrize("cfg", [2, 4])
+def test_split_count_and_page_order_do_not_change_the_result(cfg):
+    w = make_workload(cfg, **SMALL[cfg])
+    kp, vp = w.pages(0), w.pages(1)
+    cache, lens = build_cache(w, kp, vp)
+    q = w.q()
+    base16, base32 = _run(w, cache, lens, q)
+    for pps in [1, 3, 64, 100000]:
+        o16, o32 = _run(w, cache, lens, q, pages_per_split=pps)
+        nrm = np.abs(base32).max(axis=-1, keepdims=True)
+        assert np.all(np.abs(o32 - base32) <= 1e-5 * nrm), pps     # fp32 reduction order only
+    again16, again32 = _run(w, cache, lens, q)
+    assert np.array_equal(again32.view(np.uint32), base32.view(np.uint32))    # repeatable bit for bit
+    assert np.array_equal(again16, base16)
+
+
+def test_dense_and_compressed_agree():
+    w = make_workload(3, **SMALL[3])
+    kp, vp = w.pages(0), w.pages(1)
+    cache, lens = build_cache(w, kp, vp)
+    q = w.q()
+    c16, c32 = _run(w, cache, lens, q)
+    d16, d32 = _run(w, None, dev(w.seq_lens), q, dense_pages=(dev(kp), dev(vp)))
+    nrm = np.abs(d32).max(axis=-1, keepdims=True)
+    assert np.all(np.abs(c32 - d32) <= 2e-5 * nrm + 1e-30)
+
+
+def _synthetic_cache(B, H, Hq, D, P, L, K, V, q):
+    """Cache and dense pages from explicit token arrays K, V [B][L][H][D] (BF16 bits)."""
+    npg = (L + P - 1) // P
+    table = np.arange(B * npg, dtype=np.int32).reshape(B, npg)
+    kp = np.zeros((B * npg, H, P, D), np.uint16)
+    vp = np.zeros_like(kp)
+    for r in range(B):
+        for t in range(L):
+            kp[table[r, t // P], :, t % P] = K[r, t]
+            vp[table[r, t // P], :, t % P] = V[r, t]
+
+    class W:
+        pass
+    w = W()
+    w.B, w.Hq, w.Hkv, w.D, w.P, w.page_table = B, Hq, H, D, P, table
+    w.seq_lens = np.full(B, L, np.int32)
+    w.n_append, w.num_pages, w.sm_scale, w.k_dist = 0, B * npg, 1 / math.sqrt(D), "x"
+    w.appended = None
+    cache, lens = build_cache(w, kp, vp)
+    return w, cache, lens, kp, vp
+
+
+@pytest.mark.parametrize("Hq,H", [(4, 4), (8, 2)])
+def test_closed_forms(Hq, H):
+    rng = np.random.default_rng(7)
+    B, D, P = 3, 128, 16
+    q = f32_to_bf16_bits(rng.standard_normal((B, Hq, D)).astype(np.float32))
+    # 1) a single token returns that token's V exactly
+    K = f32_to_bf16_bits(rng.standard_normal((B, 1, H, D)).astype(np.float32) * 4)
+    V = f32_to_bf16_bits(rng.standard_normal((B, 1, H, D)).astype(np.float32))
+    w, cache, lens, kp, vp = _synthetic_cache(B, H, Hq, D, P, 1, K, V, q)
+    o16, o32 = _run(w, cache, lens, q)
+    want = np.repeat(V[:, 0], Hq // H, axis=1)
+    assert np.array_equal(o16, want)
+    assert np.array_equal(o32, oa.bf16_to_f64(want).astype(np.float32))
+    # 2) V constant along the tokens returns that constant exactly (in BF16)
+    L = 77
+    K = f32_to_bf16_bits(rng.standard_normal((B, L, H, D)).astype(np.float32) * 3)
+    row = f32_to_bf16_bits(rng.standard_normal((B, 1, H, D)).astype(np.float32))
+    V = np.repeat(row, L, axis=1)
+    w, cache, lens, kp, vp = _synthetic_cache(B, H, Hq, D, P, L, K, V, q)
+    o16, o32 = _run(w, cache, lens, q)
+    assert np.array_equal(o16, np.repeat(row[:, 0], Hq // H, axis=1))
+    # 3) q = 0 gives uniform weights: the mean of V
+    V = f32_to_bf16_bits(rng.standard_normal((B, L, H, D)).astype(np.float32))
+    w, cache, lens, kp, vp = _synthetic_cache(B, H, Hq, D, P, L, K, V, q)
+    qz = np.zeros_like(q)
+    o16, o32 = _run(w, cache, lens, qz)
+    mean = np.repeat(oa.bf16_to_f64(V).mean(axis=1), Hq // H, axis=1)
+    assert np.all(np.abs(o32 - mean) <= 1e-5 * np.abs(mean).max(axis=-1, keepdims=True))
+
+
+def test_empty_and_short_requests():
+    w = make_workload(2, B=4, lens=[0, 1, 15, 16], Hq=4, Hkv=4)
+    kp, vp = w.pages(0), w.pages(1)
+    cache, lens = build_cache(w, kp, vp)
+    q = w.q()
+    o16, o32 = _run(w, cache, lens, q)
+    assert not o16[0].any() and not o32[0].any()
+    rows = [(r, h) for r in range(1, 4) for h in range(w.Hq)]
+    ref = oracle_rows(w, kp, vp, q, rows)
+    check_rows(o16[1:].reshape(-1, w.D), o32[1:].reshape(-1, w.D), ref, "short")
+    d16, d32 = _run(w, None, dev(w.seq_lens), q, dense_pages=(dev(kp), dev(vp)))
+    assert not d16[0].any()
+
+
+def test_bad_page_id_sets_status():
+    w = make_workload(2, B=1, L=64, Hq=2, Hkv=2)
+    kp, vp = w.pages(0), w.pages(1)
+    cache, lens = build_cache(w, kp, vp)
+    table = w.page_table.copy()
+    table[0, 1] = 10 ** 6
+    out = torch.zeros((1, 2, w.D), dtype=torch.int16, device=DEV)
+    kvz.decode_attention(dev(w.q()), cache, dev(table), lens, w.sm_scale, out)
+    torch.cuda.synchronize()
+    assert int(cache.status.item()) & kvz.kvz.STATUS_BAD_PAGE_ID
+
+
+def _sampled_rows(w, n, seed):
+    rng = np.random.default_rng(seed)
+    rs = rng.integers(0, w.B, size=n)
+    hs = rng.integers(0, w.Hq, size=n)
+    return sorted(set(zip(rs.tolist(), hs.tolist())))
+
+
+@pytest.mark.parametrize("cfg", [2, 3, 4, 5])
+def test_full_size_sampled_rows(cfg, full_workloads):
+    """Full shapes, the launch configuration the benchmark times, sampled (request, head) rows."""
+    w, kp, vp, cache, lens = full_workloads(cfg)
+    q = w.q()
+    o16, o32 = _run(w, cache, lens, q)
+    assert int(cache.status.item()) == 0
+    rows = _sampled_rows(w, 24, cfg)
+    ref = oracle_rows(w, kp, vp, q, rows)
+    idx = tuple(np.array(rows).T)
+    check_rows(o16[idx], o32[idx], ref, f"cfg{cfg} full compressed")
+    assert np.isfinite(o32).all()
+    d16, d32 = _run(w, None, dev(w.seq_lens), q, dense_pages=(dev(kp), dev(vp)))
+    check_rows(d16[idx], d32[idx], ref, f"cfg{cfg} full dense")
+
+
+def test_two_phase_calls_equal_the_one_call():
+    w = make_workload(4, **SMALL[4])
+    kp, vp = w.pages(0), w.pages(1)
+    cache, lens = build_cache(w, kp, vp)
+    q = dev(w.q())
+    o16, o32 = _run(w, cache, lens, w.q())
+    ws = torch.empty(kvz.workspace_bytes(w.B, w.Hq, w.Hkv, w.D, w.P, w.max_pages), dtype=torch.uint8, device=DEV)
+    out = torch.zeros((w.B, w.Hq, w.D), dtype=torch.int16, device=DEV)
+    out32 = torch.zeros((w.B, w.Hq, w.D), dtype=torch.float32, device=DEV)
+    kvz.decode_attention_splits(q, cache, dev(w.page_table), lens, w.sm_scale, ws)
+    kvz.merge_splits(ws, lens, w.B, w.Hq, w.Hkv, w.D, w.P, w.max_pages, out, out32)
+    torch.cuda.synchronize()
+    assert np.array_equal(host16(out), o16) and np.array_equal(out32.cpu().numpy(), o32)
