@@ -105,8 +105,8 @@ __device__ __forceinline__ void gqa_tile(GqaState& st, const uint32_t (&kp)[16],
 // ---------------------------------------------------------------- compressed source
 struct GqaCStage {
   const uint8_t* unit;
-  UnitHeader hdr;
   int tile;
+  uint32_t meta;
   KRaw<128> k;
   VRaw<128> v;
 };
@@ -121,14 +121,13 @@ __device__ __forceinline__ void gqa_c_load(GqaCStage& st, const GqaCStage& prev,
       st.unit = nullptr;
     } else {
       st.unit = units + ((size_t)pid * H + h) * unit_bytes(P, 128);
-      st.hdr = load_header(st.unit, P, 128);
     }
   } else {
     st.unit = prev.unit;
-    st.hdr = prev.hdr;
   }
   st.tile = tile;
   if (st.unit) {
+    st.meta = load_meta(st.unit, P, 128, tile, lane);
     load_k<128, true>(st.unit, P, tile, lane, st.k);
     load_v<128>(st.unit, P, tile, lane, st.v);
   }
@@ -139,16 +138,20 @@ __device__ __forceinline__ void gqa_c_compute(GqaState& st, const GqaCStage& stg
                                               const uint16_t* pool, float scale, int lane) {
   if (!stg.unit) return;
   if (stg.tile == 0) { krank = 0; vrank = 0; }
-  uint32_t kp[16], kf[4];
-  decode_k<128>(stg.k, kp, kf);
-  if (stg.hdr.kc) patch_k_tile<128, true>(kp, kf, stg.unit, P, stg.hdr, krank, esc_lds, pool, lane);
-  uint32_t vp[2][8], vf[2][2];
+  const UnitHeader hdr = header_from_meta<128>(stg.meta);
+  uint32_t kp[16];
+  decode_k<128>(stg.k, k_base_from_meta<128, true>(stg.meta, lane), kp);
+  if (hdr.kc) patch_k_tile<128, true>(kp, stg.k, stg.meta, hdr, P, stg.tile, krank, esc_lds, pool, lane);
+  uint32_t vflat[16];
 #pragma unroll
-  for (int g = 0; g < 2; ++g) {
-    const VBases b = v_bases(stg.unit, P, 128, stg.tile, g);
-    decode_v_seg(stg.v.seg[g], b, vp[g], vf[g]);
+  for (int g = 0; g < 2; ++g) decode_v_seg(stg.v.seg[g], v_bases<128>(stg.meta, g), &vflat[8 * g]);
+  if (hdr.vc) patch_v_tile<128>(vflat, stg.v, stg.meta, hdr, P, stg.tile, vrank, esc_lds, pool, lane);
+  uint32_t vp[2][8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    vp[0][k] = vflat[k];
+    vp[1][k] = vflat[8 + k];
   }
-  if (stg.hdr.vc) patch_v_tile<128>(vp, vf, stg.unit, P, stg.hdr, vrank, esc_lds, pool, lane);
   const int vdim[2] = {lane, lane + 64};
   gqa_tile(st, kp, vdim, vp, kTile, scale, vlds, lane);
 }

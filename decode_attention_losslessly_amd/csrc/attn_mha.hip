@@ -28,14 +28,14 @@ constexpr int kWavesPerBlock = 4;
 template <int D>
 struct MhaStage {
   const uint8_t* unit;
-  UnitHeader hdr;
   int tile;
+  uint32_t meta;   // this lane's dword of the tile's meta window
   KRaw<D> k;
   VRaw<D> v;
 };
 
-// Issues the loads of one (page, tile) step. Tile 0 of a page reads the page id and header;
-// later tiles of the same page reuse `prev`'s.
+// Issues the loads of one (page, tile) step. Tile 0 of a page reads the page id; later tiles of
+// the same page reuse `prev`'s unit.
 template <int D>
 __device__ __forceinline__ void mha_load(MhaStage<D>& st, const MhaStage<D>& prev, const uint8_t* units,
                                          const int32_t* pt_row, int page, int tile, int H, int h, int P,
@@ -47,14 +47,13 @@ __device__ __forceinline__ void mha_load(MhaStage<D>& st, const MhaStage<D>& pre
       st.unit = nullptr;
     } else {
       st.unit = units + ((size_t)pid * H + h) * unit_bytes(P, D);
-      st.hdr = load_header(st.unit, P, D);
     }
   } else {
     st.unit = prev.unit;
-    st.hdr = prev.hdr;
   }
   st.tile = tile;
   if (st.unit) {
+    st.meta = load_meta(st.unit, P, D, tile, lane);
     load_k<D, false>(st.unit, P, tile, lane, st.k);
     load_v<D>(st.unit, P, tile, lane, st.v);
   }
@@ -95,15 +94,15 @@ __device__ __forceinline__ void mha_softmax(MhaState<D>& st, float s, uint32_t (
 }
 
 template <int D>
-__device__ __forceinline__ void mha_accumulate_v(MhaState<D>& st, const uint32_t (&vp)[D / 64][8],
+__device__ __forceinline__ void mha_accumulate_v(MhaState<D>& st, const uint32_t (&vp)[D / 8],
                                                  const uint32_t (&phi)[8], const uint32_t (&plo)[8]) {
 #pragma unroll
   for (int s = 0; s < D / 64; ++s) {
     float a = st.acc[s], b = 0.f;
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      a = dot2_bf16(vp[s][k], phi[k], a);
-      b = dot2_bf16(vp[s][k], plo[k], b);
+      a = dot2_bf16(vp[8 * s + k], phi[k], a);
+      b = dot2_bf16(vp[8 * s + k], plo[k], b);
     }
     st.acc[s] = a + b;
   }
@@ -114,11 +113,12 @@ __device__ __forceinline__ void mha_compute(MhaState<D>& st, const MhaStage<D>& 
                                             uint32_t& vrank, uint16_t* lds, const uint16_t* pool, float scale,
                                             int lane) {
   if (!stg.unit) return;
-  constexpr int VK = KRaw<D>::VK, NW = KRaw<D>::NW, NS = D / 64;
+  constexpr int VK = KRaw<D>::VK, NS = D / 64;
   if (stg.tile == 0) { krank = 0; vrank = 0; }
-  uint32_t kp[VK / 2], kf[NW];
-  decode_k<D>(stg.k, kp, kf);
-  if (stg.hdr.kc) patch_k_tile<D, false>(kp, kf, stg.unit, P, stg.hdr, krank, lds, pool, lane);
+  const UnitHeader hdr = header_from_meta<D>(stg.meta);
+  uint32_t kp[VK / 2];
+  decode_k<D>(stg.k, k_base_from_meta<D, false>(stg.meta, lane), kp);
+  if (hdr.kc) patch_k_tile<D, false>(kp, stg.k, stg.meta, hdr, P, stg.tile, krank, lds, pool, lane);
   float a0 = 0.f, a1 = 0.f;
 #pragma unroll
   for (int j = 0; j < VK / 2; j += 2) {
@@ -128,13 +128,10 @@ __device__ __forceinline__ void mha_compute(MhaState<D>& st, const MhaStage<D>& 
   const float s = quad_sum(a0 + a1) * scale;
   uint32_t phi[8], plo[8];
   mha_softmax<D>(st, s, phi, plo);
-  uint32_t vp[NS][8], vf[NS][2];
+  uint32_t vp[NS * 8];
 #pragma unroll
-  for (int g = 0; g < NS; ++g) {
-    const VBases b = v_bases(stg.unit, P, D, stg.tile, g);
-    decode_v_seg(stg.v.seg[g], b, vp[g], vf[g]);
-  }
-  if (stg.hdr.vc) patch_v_tile<D>(vp, vf, stg.unit, P, stg.hdr, vrank, lds, pool, lane);
+  for (int g = 0; g < NS; ++g) decode_v_seg(stg.v.seg[g], v_bases<D>(stg.meta, g), &vp[8 * g]);
+  if (hdr.vc) patch_v_tile<D>(vp, stg.v, stg.meta, hdr, P, stg.tile, vrank, lds, pool, lane);
   mha_accumulate_v<D>(st, vp, phi, plo);
 }
 
@@ -158,7 +155,7 @@ __device__ __forceinline__ void mha_tail(MhaState<D>& st, const uint16_t* tk, co
     s = valid ? s : -INFINITY;
     uint32_t phi[8], plo[8];
     mha_softmax<D>(st, s, phi, plo);
-    uint32_t vp[NS][8];
+    uint32_t vp[NS * 8];
 #pragma unroll
     for (int g = 0; g < NS; ++g) {
       const int d = lane + 64 * g;
@@ -167,7 +164,7 @@ __device__ __forceinline__ void mha_tail(MhaState<D>& st, const uint16_t* tk, co
         const int t_a = t0 + 2 * k, t_b = t_a + 1;
         const uint32_t va = t_a < rows ? tv[(size_t)t_a * D + d] : 0u;
         const uint32_t vb = t_b < rows ? tv[(size_t)t_b * D + d] : 0u;
-        vp[g][k] = va | (vb << 16);
+        vp[8 * g + k] = va | (vb << 16);
       }
     }
     mha_accumulate_v<D>(st, vp, phi, plo);

@@ -53,9 +53,11 @@ __device__ __forceinline__ int storage_to_index(int s, int D) {
   return (t * kTile + tok) * D + d;
 }
 
+// Writes the block's payload; its escapes go to `inline_dst` as value | position << 16 entries
+// or to `pool_dst` as values (whichever is non-null), starting at entry/element 0.
 template <bool IsV>
 __device__ void encode_block(const uint16_t* X, const uint8_t* bases_meta, int P, int D,
-                             uint8_t* payload, uint16_t* esc_dst, bool keep_esc, CompressShared& sh) {
+                             uint8_t* payload, uint32_t* inline_dst, uint16_t* pool_dst, CompressShared& sh) {
   const int G = D / kGroup;
   const int nchunks = P * D / 8;
   uint32_t rank = 0;
@@ -89,11 +91,16 @@ __device__ void encode_block(const uint16_t* X, const uint8_t* bases_meta, int P
     }
     uint32_t total;
     uint32_t pre = block_excl_scan(ne, sh, &total);
-    if (keep_esc && escmask) {
+    if (escmask && (inline_dst || pool_dst)) {
       uint32_t k = rank + pre;
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
-        if (escmask & (1u << j)) esc_dst[k++] = xs[j];
+      for (int j = 0; j < 8; ++j) {
+        if (escmask & (1u << j)) {
+          if (inline_dst) inline_dst[k] = (uint32_t)xs[j] | ((uint32_t)(8 * c + j) << 16);
+          else pool_dst[k] = xs[j];
+          ++k;
+        }
+      }
     }
     rank += total;
   }
@@ -162,13 +169,15 @@ __device__ void compress_unit(const uint16_t* __restrict__ src_k, const uint16_t
   __syncthreads();
   const uint64_t dest = sh.dest;
   const bool keep = sh.drop == 0;
-  uint16_t* esc = (dest == kInline) ? reinterpret_cast<uint16_t*>(unit + hdr + 16) : pool + dest;
+  uint32_t* inl = (keep && dest == kInline) ? reinterpret_cast<uint32_t*>(unit + hdr + 16) : nullptr;
+  uint16_t* pl = (keep && dest != kInline) ? pool + dest : nullptr;
   // 4. payload and escapes
-  encode_block<false>(sh_x, sh_base, P, D, unit + kblock_offset(P, D), esc, keep, sh);
-  encode_block<true>(sh_x + PD, sh_base + P * G, P, D, unit + vblock_offset(P, D), esc + kc, keep, sh);
+  encode_block<false>(sh_x, sh_base, P, D, unit + kblock_offset(P, D), inl, pl, sh);
+  encode_block<true>(sh_x + PD, sh_base + P * G, P, D, unit + vblock_offset(P, D), inl ? inl + kc : nullptr,
+                     pl ? pl + kc : nullptr, sh);
   // 5. meta: bases, header, zero tail of the inline area
   for (int i = tid; i < 2 * P * G; i += kCompressThreads) unit[i] = sh_base[i];
-  const uint32_t used = (dest == kInline && keep) ? 2 * total : 0;
+  const uint32_t used = inl ? 4 * total : 0;
   for (uint32_t i = hdr + 16 + used + tid; i < meta_bytes(P, D); i += kCompressThreads) unit[i] = 0;
   if (tid == 0) {
     uint32_t* h = reinterpret_cast<uint32_t*>(unit + hdr);

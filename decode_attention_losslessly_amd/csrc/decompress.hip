@@ -21,17 +21,18 @@ __global__ __launch_bounds__(64) void decompress_kernel(const uint8_t* __restric
     return;
   }
   const uint8_t* unit = units + ((size_t)pid * H + h) * unit_bytes(P, D);
-  const UnitHeader hdr = load_header(unit, P, D);
   uint16_t* kd = k_dst + ((size_t)i * H + h) * P * D;
   uint16_t* vd = v_dst + ((size_t)i * H + h) * P * D;
   uint32_t krank = 0, vrank = 0;
   for (int t = 0; t < P / kTile; ++t) {
     // K
+    const uint32_t meta = load_meta(unit, P, D, t, lane);
+    const UnitHeader hdr = header_from_meta<D>(meta);
     KRaw<D> kr;
     load_k<D, GQA>(unit, P, t, lane, kr);
-    uint32_t kp[KRaw<D>::VK / 2], kf[KRaw<D>::NW];
-    decode_k<D>(kr, kp, kf);
-    if (hdr.kc) patch_k_tile<D, GQA>(kp, kf, unit, P, hdr, krank, lds, pool, lane);
+    uint32_t kp[KRaw<D>::VK / 2];
+    decode_k<D>(kr, k_base_from_meta<D, GQA>(meta, lane), kp);
+    if (hdr.kc) patch_k_tile<D, GQA>(kp, kr, meta, hdr, P, t, krank, lds, pool, lane);
     {
       constexpr int VK = KRaw<D>::VK;
       const int c = k_chunk<D, GQA>(lane);
@@ -44,20 +45,17 @@ __global__ __launch_bounds__(64) void decompress_kernel(const uint8_t* __restric
     VRaw<D> vr;
     load_v<D>(unit, P, t, lane, vr);
     constexpr int NS = D / 64;
-    uint32_t vp[NS][8], vf[NS][2];
+    uint32_t vp[NS * 8];
 #pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      VBases b = v_bases(unit, P, D, t, s);
-      decode_v_seg(vr.seg[s], b, vp[s], vf[s]);
-    }
-    if (hdr.vc) patch_v_tile<D>(vp, vf, unit, P, hdr, vrank, lds, pool, lane);
+    for (int s = 0; s < NS; ++s) decode_v_seg(vr.seg[s], v_bases<D>(meta, s), &vp[8 * s]);
+    if (hdr.vc) patch_v_tile<D>(vp, vr, meta, hdr, P, t, vrank, lds, pool, lane);
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       const int d = lane + 64 * s;
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        vd[(size_t)(t * kTile + 2 * k) * D + d] = (uint16_t)(vp[s][k] & 0xFFFFu);
-        vd[(size_t)(t * kTile + 2 * k + 1) * D + d] = (uint16_t)(vp[s][k] >> 16);
+        vd[(size_t)(t * kTile + 2 * k) * D + d] = (uint16_t)(vp[8 * s + k] & 0xFFFFu);
+        vd[(size_t)(t * kTile + 2 * k + 1) * D + d] = (uint16_t)(vp[8 * s + k] >> 16);
       }
     }
   }

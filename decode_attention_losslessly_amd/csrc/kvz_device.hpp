@@ -28,8 +28,9 @@ __host__ __device__ constexpr uint32_t tile_bytes(int D) { return (uint32_t)(24 
 __host__ __device__ constexpr uint32_t unit_bytes(int P, int D) {
   return meta_bytes(P, D) + 2 * block_bytes(P, D);
 }
+// inline escapes are 4-byte entries: value | (storage position in its block << 16)
 __host__ __device__ constexpr int inline_capacity(int P, int D) {
-  return (int)(meta_bytes(P, D) - 2 * P * (D / kGroup) - 16) / 2;
+  return (int)(meta_bytes(P, D) - 2 * P * (D / kGroup) - 16) / 4;
 }
 // byte offsets inside a unit
 __host__ __device__ constexpr uint32_t hdr_offset(int P, int D) { return (uint32_t)(2 * P * (D / kGroup)); }
@@ -170,72 +171,12 @@ __device__ __forceinline__ uint32_t set_half(uint32_t v, int half, uint32_t x) {
   return half ? ((v & 0x0000FFFFu) | (x << 16)) : ((v & 0xFFFF0000u) | (x & 0xFFFFu));
 }
 
-// Patch register p (wave-uniform index) of lane `lane` with value x in the given half.
+// Sets half `half` of register `reg` of lane `lane` to x; reg, lane, half and x are
+// wave-uniform, so the register is addressed through the GPR index mode, not a branch tree.
 template <int N>
-__device__ __forceinline__ void patch_pair(uint32_t (&pairs)[N], int p, int lane, int half, uint32_t x) {
-#pragma unroll
-  for (int i = 0; i < N; ++i) {
-    if (i == p) {
-      uint32_t old = readlane(pairs[i], lane);
-      pairs[i] = writelane(pairs[i], set_half(old, half, x), lane);
-    }
-  }
-}
-
-// Escape value `rank` (u16 index) stored inline in a unit's meta region.
-__device__ __forceinline__ uint32_t inline_escape(const uint8_t* inline_base, uint32_t rank) {
-  uintptr_t a = reinterpret_cast<uintptr_t>(inline_base) + 2u * rank;
-  uint32_t w = sload<uint32_t>(reinterpret_cast<const void*>(a & ~(uintptr_t)3));
-  return (a & 2) ? (w >> 16) : (w & 0xFFFFu);
-}
-
-// Patches escaped values whose list is inline, walking the lanes that hold escapes in storage
-// order with wave-uniform control (cheap when escapes are rare).
-//   pairs[NP]     this lane's rebuilt pairs of one segment (NP = 4 * NW)
-//   flags[NW]     escape_flags of this lane's offset words
-//   gqa_order     lane l holds storage chunk 4*(l%16) + l/16 instead of chunk l
-//   rank0         index in the inline list of the segment's first escape
-//   limit         one past the last index the list holds; reads never go beyond it
-// Returns the number of escapes met (patched or, past `limit`, left as placeholders).
-template <int NW>
-__device__ __forceinline__ uint32_t patch_inline(uint32_t (&pairs)[4 * NW], const uint32_t (&flags)[NW],
-                                                 bool gqa_order, const uint8_t* inline_base, uint32_t rank0,
-                                                 uint32_t limit) {
-  uint32_t any = 0;
-#pragma unroll
-  for (int w = 0; w < NW; ++w) any |= flags[w];
-  uint64_t m = ballot(any != 0);
-  if (m == 0) return 0;
-  if (gqa_order) {
-    uint64_t mc = 0;
-    while (m) {
-      int l = __builtin_ctzll(m);
-      m &= m - 1;
-      mc |= 1ull << (4 * (l & 15) + (l >> 4));
-    }
-    m = mc;
-  }
-  uint32_t rank = rank0;
-  while (m) {
-    int c = __builtin_ctzll(m);
-    m &= m - 1;
-    int l = gqa_order ? (16 * (c & 3) + (c >> 2)) : c;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      uint32_t f = readlane(flags[w], l);
-      if (f == 0) continue;
-      for (int j = 0; j < 8; ++j) {
-        if (f & flag_bit(j)) {
-          if (rank < limit) {
-            uint32_t x = inline_escape(inline_base, rank);
-            patch_pair<4 * NW>(pairs, 4 * w + (j >> 1), l, j & 1, x);
-          }
-          ++rank;
-        }
-      }
-    }
-  }
-  return rank - rank0;
+__device__ __forceinline__ void patch_one(uint32_t (&pairs)[N], int reg, int lane, int half, uint32_t x) {
+  const uint32_t old = pairs[reg];
+  pairs[reg] = lane_id() == lane ? set_half(old, half, x) : old;
 }
 
 // Patches escaped values from a list staged in LDS (any number of escapes), per lane.

@@ -23,7 +23,6 @@ struct KRaw {
   static constexpr int NW = VK / 8;                 // offset words per lane
   uint32_t sm[VK / 4];
   uint32_t nib[NW];
-  uint32_t base;
 };
 
 // chunk index (storage order, units of VK values) of this lane
@@ -52,18 +51,43 @@ __device__ __forceinline__ void load_k(const uint8_t* unit, int P, int tile, int
     uint2 n = *reinterpret_cast<const uint2*>(tb + 16 * D + c * (VK / 2));
     r.nib[0] = n.x; r.nib[1] = n.y;
   }
-  r.base = unit[kbase_offset(D, tile) + (dim0 / kGroup) * kTile + tok];
+}
+
+// ---------------------------------------------------------------- meta window
+// One dword per lane of the tile's metadata, loaded with the payload:
+//   lanes [0, 4G)         K bases of the tile (16*G bytes)
+//   lanes [4G, 8G)        V bases of the tile
+//   lanes [8G, 8G + 32)   header (4 dwords) then the inline escapes
+// (lanes past the meta region read bytes of the unit that are not used).
+__device__ __forceinline__ uint32_t load_meta(const uint8_t* unit, int P, int D, int tile, int lane) {
+  const int G = D / kGroup;
+  uint32_t off;
+  if (lane < 4 * G) off = kbase_offset(D, tile) + 4 * lane;
+  else if (lane < 8 * G) off = vbase_offset(P, D, tile) + 4 * (lane - 4 * G);
+  else if (lane < 8 * G + 32) off = hdr_offset(P, D) + 4 * (lane - 8 * G);
+  else off = 0;
+  return *reinterpret_cast<const uint32_t*>(unit + off);
+}
+template <int D>
+__device__ __forceinline__ int hdr_lane() { return 8 * (D / kGroup); }
+
+// base of the group this lane's K chunk lies in
+template <int D, bool GQA>
+__device__ __forceinline__ uint32_t k_base_from_meta(uint32_t meta, int lane) {
+  constexpr int VK = KRaw<D>::VK;
+  const int c = k_chunk<D, GQA>(lane);
+  const int tok = c / (D / VK), g = ((c % (D / VK)) * VK) / kGroup;
+  const int byte = g * kTile + tok;
+  const uint32_t w = (uint32_t)__builtin_amdgcn_ds_bpermute(4 * (byte >> 2), (int)meta);
+  return (w >> (8 * (byte & 3))) & 0xFFu;
 }
 
 template <int D>
-__device__ __forceinline__ void decode_k(const KRaw<D>& r, uint32_t (&pairs)[KRaw<D>::VK / 2],
-                                         uint32_t (&flags)[KRaw<D>::NW]) {
-  const uint32_t bb = r.base * 0x00800080u;
+__device__ __forceinline__ void decode_k(const KRaw<D>& r, uint32_t base, uint32_t (&pairs)[KRaw<D>::VK / 2]) {
+  const uint32_t bb = base * 0x00800080u;
 #pragma unroll
-  for (int w = 0; w < KRaw<D>::NW; ++w) {
+  for (int w = 0; w < KRaw<D>::NW; ++w)
     decode8(r.sm[2 * w], r.sm[2 * w + 1], r.nib[w], bb, bb, bb, bb, &pairs[4 * w]);
-    flags[w] = escape_flags(r.nib[w]);
-  }
 }
 
 // ---------------------------------------------------------------- V
@@ -94,11 +118,13 @@ struct VBases {
   uint32_t bb[8];
 };
 
-__device__ __forceinline__ VBases v_bases(const uint8_t* unit, int P, int D, int tile, int g) {
-  const uint8_t* b = unit + vbase_offset(P, D, tile) + g * kTile;
-  uint4 w = sload4(b);
+template <int D>
+__device__ __forceinline__ VBases v_bases(uint32_t meta, int g) {
+  constexpr int G = D / kGroup;
   VBases r;
-  const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+  uint32_t ws[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) ws[i] = readlane(meta, 4 * G + 4 * g + i);
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
     const uint32_t word = ws[k >> 1];
@@ -108,12 +134,10 @@ __device__ __forceinline__ VBases v_bases(const uint8_t* unit, int P, int D, int
   return r;
 }
 
-__device__ __forceinline__ void decode_v_seg(const VSeg& s, const VBases& b, uint32_t (&pairs)[8],
-                                             uint32_t (&flags)[2]) {
+// rebuilds the 16 tokens of one dim into pairs[0..7] (token pairs 2k, 2k+1)
+__device__ __forceinline__ void decode_v_seg(const VSeg& s, const VBases& b, uint32_t* pairs) {
   decode8(s.sm.x, s.sm.y, s.nib.x, b.bb[0], b.bb[1], b.bb[2], b.bb[3], &pairs[0]);
   decode8(s.sm.z, s.sm.w, s.nib.y, b.bb[4], b.bb[5], b.bb[6], b.bb[7], &pairs[4]);
-  flags[0] = escape_flags(s.nib.x);
-  flags[1] = escape_flags(s.nib.y);
 }
 
 // ---------------------------------------------------------------- unit header
@@ -122,33 +146,62 @@ struct UnitHeader {
   uint64_t off;             // pool offset or kInline
 };
 
-__device__ __forceinline__ UnitHeader load_header(const uint8_t* unit, int P, int D) {
-  uint4 h = sload4(unit + hdr_offset(P, D));
+template <int D>
+__device__ __forceinline__ UnitHeader header_from_meta(uint32_t meta) {
+  constexpr int hl = 8 * (D / kGroup);
   UnitHeader r;
-  r.kc = h.x;
-  r.vc = h.y;
-  r.off = ((uint64_t)h.w << 32) | h.z;
+  r.kc = readlane(meta, hl);
+  r.vc = readlane(meta, hl + 1);
+  r.off = ((uint64_t)readlane(meta, hl + 3) << 32) | readlane(meta, hl + 2);
   return r;
 }
 
 // ---------------------------------------------------------------- escape patching per tile
-// Escapes of one tile of one block: count and patch. `rank` is the block-level rank of the
-// tile's first escape and is advanced past the tile. Inline lists use the wave-uniform walk;
-// pool lists are staged into `lds` (room for 16*D values) and patched per lane.
+// A unit's escapes are either inline (K's entries then V's, each value | position << 16, in
+// storage order, in the header area of the meta window) or in the pool (values only).
+//   inline: the entries of this tile are walked with wave-uniform control; each names its lane,
+//           register and half directly, so no lane has to search its offsets;
+//   pool:   every lane finds its escape codes, a wave scan ranks them in storage order, the
+//           tile's part of the list is staged in `lds` (room for 16*D values) and each lane
+//           patches its own registers.
+// `cursor` is the block-level index of the tile's first escape and is advanced past the tile.
+
+// K, multi-head layout: storage position p of a tile -> lane p / VK, value p % VK.
+// K, grouped-query layout: chunk p / 32 sits in lane 16*(chunk%4) + chunk/4.
+template <int D, bool GQA>
+__device__ __forceinline__ void k_position(uint32_t p, int& lane, int& reg, int& half) {
+  constexpr int VK = KRaw<D>::VK;
+  const int c = (int)p / VK, j = (int)p % VK;
+  lane = GQA ? (16 * (c & 3) + (c >> 2)) : c;
+  reg = j >> 1;
+  half = j & 1;
+}
 
 template <int D, bool GQA>
-__device__ __forceinline__ void patch_k_tile(uint32_t (&pairs)[KRaw<D>::VK / 2],
-                                             const uint32_t (&flags)[KRaw<D>::NW], const uint8_t* unit,
-                                             int P, const UnitHeader& h, uint32_t& rank, uint16_t* lds,
-                                             const uint16_t* pool, int lane) {
+__device__ __forceinline__ void patch_k_tile(uint32_t (&pairs)[KRaw<D>::VK / 2], const KRaw<D>& raw,
+                                             uint32_t meta, const UnitHeader& h, int P, int tile,
+                                             uint32_t& cursor, uint16_t* lds, const uint16_t* pool, int lane) {
   constexpr int NW = KRaw<D>::NW;
+  const uint32_t lo = (uint32_t)tile * kTile * D, hi = lo + kTile * D;
   if (h.off == kInline) {
-    rank += patch_inline<NW>(pairs, flags, GQA, unit + hdr_offset(P, D) + 16, rank, h.kc);
+    const uint32_t end = min(h.kc, (uint32_t)inline_capacity(P, D));
+    while (cursor < end) {
+      const uint32_t ent = readlane(meta, hdr_lane<D>() + 4 + (int)cursor);
+      const uint32_t p = ent >> 16;
+      if (p >= hi) break;
+      int l, reg, half;
+      k_position<D, GQA>(p - lo, l, reg, half);
+      patch_one<KRaw<D>::VK / 2>(pairs, reg, l, half, ent & 0xFFFFu);
+      ++cursor;
+    }
     return;
   }
-  uint32_t c = 0;
+  uint32_t flags[NW], c = 0;
 #pragma unroll
-  for (int w = 0; w < NW; ++w) c += popc_flags(flags[w]);
+  for (int w = 0; w < NW; ++w) {
+    flags[w] = escape_flags(raw.nib[w]);
+    c += popc_flags(flags[w]);
+  }
   // counts in storage order -> exclusive scan -> back to this lane
   const int src = GQA ? (16 * (lane & 3) + (lane >> 2)) : lane;      // lane holding chunk `lane`
   const uint32_t c_ord = GQA ? (uint32_t)__shfl((int)c, src) : c;
@@ -158,45 +211,62 @@ __device__ __forceinline__ void patch_k_tile(uint32_t (&pairs)[KRaw<D>::VK / 2],
   const uint32_t exc = GQA ? (uint32_t)__shfl((int)exc_ord, k_chunk<D, GQA>(lane)) : exc_ord;
   if (total == 0) return;
   // never read past this block's list, even if the offsets disagree with the header
-  const uint32_t avail = h.kc > rank ? min(total, h.kc - rank) : 0u;
-  const uint16_t* src_list = pool + h.off + rank;
+  const uint32_t avail = h.kc > cursor ? min(total, h.kc - cursor) : 0u;
+  const uint16_t* src_list = pool + h.off + cursor;
   for (uint32_t i = lane; i < avail; i += 64) lds[i] = src_list[i];
   wave_lds_sync();
   patch_lds<NW>(pairs, flags, lds, exc, avail);
   wave_lds_sync();
-  rank += total;
+  cursor += total;
 }
 
-// V: segments s = 0 .. D/64-1 (dims lane + 64 s), storage order segment-major then lane.
+// V: segments s = 0 .. D/64-1 (dims lane + 64 s), storage order segment-major then lane;
+// pairs[s * 8 + k] holds tokens 2k, 2k+1 of dim lane + 64 s.
 template <int D>
-__device__ __forceinline__ void patch_v_tile(uint32_t (&pairs)[D / 64][8], const uint32_t (&flags)[D / 64][2],
-                                             const uint8_t* unit, int P, const UnitHeader& h, uint32_t& rank,
-                                             uint16_t* lds, const uint16_t* pool, int lane) {
+__device__ __forceinline__ void patch_v_tile(uint32_t (&pairs)[D / 8], const VRaw<D>& raw, uint32_t meta,
+                                             const UnitHeader& h, int P, int tile, uint32_t& cursor, uint16_t* lds,
+                                             const uint16_t* pool, int lane) {
   constexpr int NS = D / 64;
+  const uint32_t lo = (uint32_t)tile * kTile * D, hi = lo + kTile * D;
   if (h.off == kInline) {
-#pragma unroll
-    for (int s = 0; s < NS; ++s)
-      rank += patch_inline<2>(pairs[s], flags[s], false, unit + hdr_offset(P, D) + 16, h.kc + rank,
-                              h.kc + h.vc);
+    const uint32_t end = min(h.kc + h.vc, (uint32_t)inline_capacity(P, D));
+    while (h.kc + cursor < end) {
+      const uint32_t ent = readlane(meta, hdr_lane<D>() + 4 + (int)(h.kc + cursor));
+      const uint32_t p = ent >> 16;
+      if (p >= hi) break;
+      const int q = (int)(p - lo), d = q >> 4, tok = q & 15;
+      patch_one<D / 8>(pairs, (d >> 6) * 8 + (tok >> 1), d & 63, tok & 1, ent & 0xFFFFu);
+      ++cursor;
+    }
     return;
   }
-  uint32_t packed = 0;
+  uint32_t flags[NS][2], packed = 0;
 #pragma unroll
-  for (int s = 0; s < NS; ++s) packed |= (popc_flags(flags[s][0]) + popc_flags(flags[s][1])) << (16 * s);
+  for (int s = 0; s < NS; ++s) {
+    flags[s][0] = escape_flags(raw.seg[s].nib.x);
+    flags[s][1] = escape_flags(raw.seg[s].nib.y);
+    packed |= (popc_flags(flags[s][0]) + popc_flags(flags[s][1])) << (16 * s);
+  }
   const uint32_t inc = wave_incl_scan(packed);
   const uint32_t tot = readlane(inc, 63);
   const uint32_t exc = inc - packed;
   const uint32_t t0 = tot & 0xFFFFu;
   const uint32_t total = t0 + (tot >> 16);
   if (total == 0) return;
-  const uint32_t avail = h.vc > rank ? min(total, h.vc - rank) : 0u;
-  const uint16_t* src_list = pool + h.off + h.kc + rank;
+  const uint32_t avail = h.vc > cursor ? min(total, h.vc - cursor) : 0u;
+  const uint16_t* src_list = pool + h.off + h.kc + cursor;
   for (uint32_t i = lane; i < avail; i += 64) lds[i] = src_list[i];
   wave_lds_sync();
-  patch_lds<2>(pairs[0], flags[0], lds, exc & 0xFFFFu, avail);
-  if constexpr (NS > 1) patch_lds<2>(pairs[1], flags[1], lds, t0 + (exc >> 16), avail);
+  {
+    uint32_t(&p0)[8] = *reinterpret_cast<uint32_t(*)[8]>(&pairs[0]);
+    patch_lds<2>(p0, flags[0], lds, exc & 0xFFFFu, avail);
+  }
+  if constexpr (NS > 1) {
+    uint32_t(&p1)[8] = *reinterpret_cast<uint32_t(*)[8]>(&pairs[8]);
+    patch_lds<2>(p1, flags[1], lds, t0 + (exc >> 16), avail);
+  }
   wave_lds_sync();
-  rank += total;
+  cursor += total;
 }
 
 }  // namespace kvz

@@ -15,8 +15,9 @@
  *    a tile is 16*D sm bytes then 2*D u32 offset words, word w holding position 8w+2k in bits
  *    4k..4k+3 and 8w+2k+1 in bits 16+4k..16+4k+3.
  *  - unit (page, head) = meta region (K bases, V bases in [tile][group][tok] order, u32 K
- *    escape count, u32 V escape count, u64 pool offset or all ones when inline, inline
- *    escapes; rounded up to 128 bytes), then the K block, then the V block.
+ *    escape count, u32 V escape count, u64 pool offset or all ones when inline, then, when
+ *    inline, one u32 per escape = value | (storage position in its block << 16); rounded up to
+ *    128 bytes), then the K block, then the V block.
  *  - attention: s_t = scale * q.k_t; o = sum_t exp(s_t - max) v_t / sum_t exp(s_t - max), over
  *    the full pages of the page table then the uncompressed tail rows (§III.D: partially filled
  *    pages stay uncompressed); query head h reads KV head h / (Hq / Hkv).
@@ -47,7 +48,7 @@ size_t kvzo_meta_bytes(int P, int D) {
 size_t kvzo_block_bytes(int P, int D) { return (size_t)P * D + (size_t)P * D / 2; }
 size_t kvzo_unit_bytes(int P, int D) { return kvzo_meta_bytes(P, D) + 2 * kvzo_block_bytes(P, D); }
 int kvzo_inline_capacity(int P, int D) {
-  return (int)((kvzo_meta_bytes(P, D) - 2 * (size_t)P * (D / GRP) - 16) / 2);
+  return (int)((kvzo_meta_bytes(P, D) - 2 * (size_t)P * (D / GRP) - 16) / 4);
 }
 
 /* base of one group of 64 exponents: largest coverage, smallest exponent on ties */
@@ -74,7 +75,7 @@ static int pos_to_index(int s, int D, int is_v) {
 
 /* one block: writes bases (P*G bytes), payload, escapes; returns the escape count */
 static int encode_block(const uint16_t* X, int P, int D, int is_v, uint8_t* bases,
-                        uint8_t* payload, uint16_t* esc) {
+                        uint8_t* payload, uint16_t* esc, uint32_t* pos) {
   int G = D / GRP, n = 0;
   int* base = (int*)malloc(sizeof(int) * P * G);
   int e[GRP];
@@ -92,7 +93,7 @@ static int encode_block(const uint16_t* X, int P, int D, int is_v, uint8_t* base
     int tok = idx / D, d = idx % D;
     uint16_t x = X[idx];
     int off = expo(x) - base[tok * G + d / GRP];
-    if (off < 0 || off > 14) { off = ESC_CODE; esc[n++] = x; }
+    if (off < 0 || off > 14) { off = ESC_CODE; pos[n] = (uint32_t)s; esc[n++] = x; }
     size_t t = s / per_tile, r = s % per_tile;
     uint8_t* tile = payload + t * (per_tile + per_tile / 2);
     tile[r] = smb(x);
@@ -134,9 +135,10 @@ int64_t kvzo_encode_unit(const uint16_t* K, const uint16_t* V, int P, int D, uin
   int G = D / GRP;
   size_t mb = kvzo_meta_bytes(P, D), bb = kvzo_block_bytes(P, D);
   uint16_t* esc = (uint16_t*)malloc(sizeof(uint16_t) * 2 * (size_t)P * D);
+  uint32_t* pos = (uint32_t*)malloc(sizeof(uint32_t) * 2 * (size_t)P * D);
   memset(unit, 0, kvzo_unit_bytes(P, D));
-  int kc = encode_block(K, P, D, 0, unit, unit + mb, esc);
-  int vc = encode_block(V, P, D, 1, unit + (size_t)P * G, unit + mb + bb, esc + kc);
+  int kc = encode_block(K, P, D, 0, unit, unit + mb, esc, pos);
+  int vc = encode_block(V, P, D, 1, unit + (size_t)P * G, unit + mb + bb, esc + kc, pos + kc);
   uint8_t* h = unit + 2 * (size_t)P * G;
   uint32_t c[2] = {(uint32_t)kc, (uint32_t)vc};
   memcpy(h, c, 8);
@@ -144,13 +146,17 @@ int64_t kvzo_encode_unit(const uint16_t* K, const uint16_t* V, int P, int D, uin
   if (kc + vc <= kvzo_inline_capacity(P, D)) {
     uint64_t o = ALL_ONES;
     memcpy(h + 8, &o, 8);
-    memcpy(h + 16, esc, 2 * (size_t)(kc + vc));
+    for (int i = 0; i < kc + vc; i++) {
+      uint32_t e = (uint32_t)esc[i] | (pos[i] << 16);
+      memcpy(h + 16 + 4 * (size_t)i, &e, 4);
+    }
   } else {
     memcpy(h + 8, &pool_offset, 8);
     memcpy(pool_esc, esc, 2 * (size_t)(kc + vc));
     ret = kc + vc;
   }
   free(esc);
+  free(pos);
   return ret;
 }
 
@@ -193,8 +199,15 @@ void kvzo_decode_unit(const uint8_t* unit, const uint16_t* pool, int P, int D, u
   memcpy(c, h, 8);
   memcpy(&off, h + 8, 8);
   uint16_t* esc = (uint16_t*)malloc(sizeof(uint16_t) * (c[0] + c[1] + 1));
-  if (off == ALL_ONES) memcpy(esc, h + 16, 2 * (size_t)(c[0] + c[1]));
-  else memcpy(esc, pool + off, 2 * (size_t)(c[0] + c[1]));
+  if (off == ALL_ONES) {
+    for (uint32_t i = 0; i < c[0] + c[1]; i++) {
+      uint32_t e;
+      memcpy(&e, h + 16 + 4 * (size_t)i, 4);
+      esc[i] = (uint16_t)(e & 0xFFFF);
+    }
+  } else {
+    memcpy(esc, pool + off, 2 * (size_t)(c[0] + c[1]));
+  }
   decode_block(unit, unit + mb, esc, P, D, 0, K);
   decode_block(unit + (size_t)P * G, unit + mb + bb, esc + c[0], P, D, 1, V);
   free(esc);

@@ -36,7 +36,10 @@ The layout itself is this repository's (the pages' own 12-bit layout is prior ar
              [2PG+4, 2PG+8)    u32 number of V escapes
              [2PG+8, 2PG+16)   u64 escape-pool offset in u16 elements, or all ones when the
                                escapes are inline
-             [2PG+16, MR)      inline escapes (K's then V's) when they fit, else zero
+             [2PG+16, MR)      when all escapes fit, one little-endian u32 entry per escape,
+                               K's then V's in list order: value | (storage position << 16),
+                               the position (within its block) repeating what the offset
+                               codes already say; unused bytes zero
              MR = round_up(2PG + 16, 128)
 """
 from __future__ import annotations
@@ -154,15 +157,17 @@ def meta_bytes(P: int, D: int) -> int:
 
 
 def inline_capacity(P: int, D: int) -> int:
-    return (meta_bytes(P, D) - 2 * P * (D // GROUP) - 16) // 2
+    """Escapes a unit can hold inline: 4-byte (value, position) entries after the header."""
+    return (meta_bytes(P, D) - 2 * P * (D // GROUP) - 16) // 4
 
 
 def unit_bytes(P: int, D: int) -> int:
     return meta_bytes(P, D) + 2 * block_bytes(P, D)
 
 
-def encode_block(X: np.ndarray, kind: int):
-    """Block [P][D] BF16 bits -> (base bytes [P*G], block payload bytes, escapes u16)."""
+def encode_block(X: np.ndarray, kind: int, with_positions: bool = False):
+    """Block [P][D] BF16 bits -> (base bytes [P*G], block payload bytes, escapes u16
+    [, storage positions of the escapes])."""
     X = np.asarray(X, np.uint16)
     P, D = X.shape
     G = D // GROUP
@@ -178,7 +183,11 @@ def encode_block(X: np.ndarray, kind: int):
         payload.append(sm_s[sl])
         payload.append(pack_offsets(off_s[sl]).astype('<u4').view(np.uint8))
     bases = np.concatenate([base[t * TILE:(t + 1) * TILE].T.reshape(-1) for t in range(P // TILE)])
-    return bases.astype(np.uint8), np.concatenate(payload), x_s[off_s == ESCAPE].copy()
+    esc = off_s == ESCAPE
+    out = (bases.astype(np.uint8), np.concatenate(payload), x_s[esc].copy())
+    if with_positions:
+        out = out + (np.nonzero(esc)[0].astype(np.uint32),)
+    return out
 
 
 def decode_block(bases: np.ndarray, payload: np.ndarray, escapes: np.ndarray, P: int, D: int,
@@ -214,8 +223,8 @@ def encode_unit(K: np.ndarray, V: np.ndarray, pool_offset: int | None = None):
     """
     P, D = K.shape
     G = D // GROUP
-    kb, kp, ke = encode_block(K, K_KIND)
-    vb, vp, ve = encode_block(V, V_KIND)
+    kb, kp, ke, kpos = encode_block(K, K_KIND, with_positions=True)
+    vb, vp, ve, vpos = encode_block(V, V_KIND, with_positions=True)
     meta = np.zeros(meta_bytes(P, D), np.uint8)
     meta[:P * G] = kb
     meta[P * G:2 * P * G] = vb
@@ -224,7 +233,9 @@ def encode_unit(K: np.ndarray, V: np.ndarray, pool_offset: int | None = None):
     esc = np.concatenate([ke, ve]).astype(np.uint16)
     if len(esc) <= inline_capacity(P, D):
         meta[h + 8:h + 16] = np.array([INLINE], '<u8').view(np.uint8)
-        meta[h + 16:h + 16 + 2 * len(esc)] = esc.astype('<u2').view(np.uint8)
+        pos = np.concatenate([kpos, vpos]).astype(np.uint32)
+        entries = esc.astype(np.uint32) | (pos << np.uint32(16))
+        meta[h + 16:h + 16 + 4 * len(esc)] = entries.astype('<u4').view(np.uint8)
         pool = np.zeros(0, np.uint16)
     else:
         meta[h + 8:h + 16] = np.array([pool_offset or 0], '<u8').view(np.uint8)
@@ -244,10 +255,21 @@ def unit_escapes(unit: np.ndarray, pool: np.ndarray | None, P: int, D: int):
     kc, vc, off = unit_header(unit, P, D)
     if off == INLINE:
         h = 2 * P * (D // GROUP) + 16
-        esc = np.asarray(unit[h:h + 2 * (kc + vc)]).view('<u2').astype(np.uint16)
+        entries = np.asarray(unit[h:h + 4 * (kc + vc)]).view('<u4')
+        esc = (entries & 0xFFFF).astype(np.uint16)
     else:
         esc = np.asarray(pool[off:off + kc + vc], np.uint16)
     return esc[:kc], esc[kc:]
+
+
+def inline_positions(unit: np.ndarray, P: int, D: int):
+    """Storage positions recorded with inline escapes (K's, V's), or None for a pool list."""
+    kc, vc, off = unit_header(unit, P, D)
+    if off != INLINE:
+        return None
+    h = 2 * P * (D // GROUP) + 16
+    pos = (np.asarray(unit[h:h + 4 * (kc + vc)]).view('<u4') >> 16).astype(np.int64)
+    return pos[:kc], pos[kc:]
 
 
 def decode_unit(unit: np.ndarray, pool: np.ndarray | None, P: int, D: int):

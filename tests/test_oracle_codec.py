@@ -167,11 +167,31 @@ def test_escape_order_is_storage_order():
     assert list(ve) == [0x7F00, 0x7E80]
 
 
+def test_inline_positions_repeat_the_offset_codes():
+    # the position recorded with each inline escape is where its offset code 15 sits
+    w = make_workload(3, B=1, L=64, Hq=4, Hkv=4)
+    K, V = w.pages(0), w.pages(1)
+    seen = 0
+    for p in range(K.shape[0]):
+        for h in range(w.Hkv):
+            unit, pool = codec.encode_unit(K[p, h], V[p, h])
+            pos = codec.inline_positions(unit, w.P, w.D)
+            assert pos is not None
+            for kind, X, ps in ((codec.K_KIND, K[p, h], pos[0]), (codec.V_KIND, V[p, h], pos[1])):
+                order = codec.storage_order(w.P, w.D, kind)
+                off = codec.offsets(codec.exponent(X).reshape(w.P, -1, 64),
+                                    codec.choose_bases(codec.exponent(X).reshape(w.P, -1, 64))).reshape(-1)
+                assert list(ps) == list(np.nonzero(off[order] == 15)[0])
+                seen += len(ps)
+    assert seen > 0
+
+
 def test_sizes():
     assert codec.block_bytes(16, 128) == 3072
-    assert codec.meta_bytes(16, 128) == 128 and codec.inline_capacity(16, 128) == 24
+    # meta = bases (2*P*D/64 bytes) + 16-byte header + 4-byte inline entries, rounded to 128
+    assert codec.meta_bytes(16, 128) == 128 and codec.inline_capacity(16, 128) == 12
     assert codec.unit_bytes(16, 128) == 128 + 6144
-    assert codec.meta_bytes(256, 64) == 640 and codec.inline_capacity(256, 64) == 56
+    assert codec.meta_bytes(256, 64) == 640 and codec.inline_capacity(256, 64) == 28
     for P, D in [(16, 64), (16, 128), (32, 256), (256, 64)]:
         assert c_oracle.unit_bytes(P, D) == codec.unit_bytes(P, D)
         assert c_oracle.inline_capacity(P, D) == codec.inline_capacity(P, D)
