@@ -133,19 +133,23 @@ __device__ __forceinline__ void gqa_c_load(GqaCStage& st, const GqaCStage& prev,
   }
 }
 
-__device__ __forceinline__ void gqa_c_compute(GqaState& st, const GqaCStage& stg, int P, uint32_t& krank,
+// Returns false, leaving the state untouched, when the unit's escapes are in the pool and POOL
+// is off.
+template <bool POOL>
+__device__ __forceinline__ bool gqa_c_compute(GqaState& st, const GqaCStage& stg, int P, uint32_t& krank,
                                               uint32_t& vrank, uint16_t* esc_lds, uint32_t* vlds,
                                               const uint16_t* pool, float scale, int lane) {
-  if (!stg.unit) return;
-  if (stg.tile == 0) { krank = 0; vrank = 0; }
+  if (!stg.unit) return true;
   const UnitHeader hdr = header_from_meta<128>(stg.meta);
+  if (!POOL && hdr.off != kInline) return false;
+  if (stg.tile == 0) { krank = 0; vrank = 0; }
   uint32_t kp[16];
   decode_k<128>(stg.k, k_base_from_meta<128, true>(stg.meta, lane), kp);
-  if (hdr.kc) patch_k_tile<128, true>(kp, stg.k, stg.meta, hdr, P, stg.tile, krank, esc_lds, pool, lane);
+  if (hdr.kc) patch_k_tile<128, true, POOL>(kp, stg.k, stg.meta, hdr, P, stg.tile, krank, esc_lds, pool, lane);
   uint32_t vflat[16];
 #pragma unroll
   for (int g = 0; g < 2; ++g) decode_v_seg(stg.v.seg[g], v_bases<128>(stg.meta, g), &vflat[8 * g]);
-  if (hdr.vc) patch_v_tile<128>(vflat, stg.v, stg.meta, hdr, P, stg.tile, vrank, esc_lds, pool, lane);
+  if (hdr.vc) patch_v_tile<128, POOL>(vflat, stg.v, stg.meta, hdr, P, stg.tile, vrank, esc_lds, pool, lane);
   uint32_t vp[2][8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
@@ -154,6 +158,7 @@ __device__ __forceinline__ void gqa_c_compute(GqaState& st, const GqaCStage& stg
   }
   const int vdim[2] = {lane, lane + 64};
   gqa_tile(st, kp, vdim, vp, kTile, scale, vlds, lane);
+  return true;
 }
 
 // ---------------------------------------------------------------- raw (dense / tail) source
@@ -231,51 +236,113 @@ __device__ __forceinline__ void gqa_store(const GqaState& st, int r, int Hq, int
   }
 }
 
+// Loads a partial stored by gqa_store back into the state: rows 0..7 of the output take the
+// stored rows (rows 8..15, which gqa_store adds to them, start from zero) and the denominator
+// goes to the lanes of the first lane group.
+__device__ __forceinline__ void gqa_resume(GqaState& st, int r, int Hq, int hq0, int nq, int S, int s,
+                                           const float* ws_acc, const float* ws_ml, int lane) {
+  const int row = (lane & 15) % kGqaRows;
+  if (row < nq) {
+    const float* ml = ws_ml + (((size_t)r * Hq + hq0 + row) * S + s) * 2;
+    st.m = ml[0];
+    st.l = lane < 16 ? ml[1] : 0.f;
+  } else {
+    st.m = -INFINITY;
+    st.l = 0.f;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int n = 4 * (lane >> 4) + i;
+    const bool have = lane < 32 && n < nq;
+    const float* acc = ws_acc + (((size_t)r * Hq + hq0 + (have ? n : 0)) * S + s) * 128;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) st.o[j][i] = have ? acc[16 * j + (lane & 15)] : 0.f;
+  }
+}
+
+// Fast (POOL = false) and general (POOL = true) instances, as for the multi-head kernel: the
+// fast one skips units whose escapes are in the pool and marks the item; the general one
+// resumes the marked items from their stored partials and adds only those units.
+template <bool POOL>
 __global__ __launch_bounds__(64 * kGqaWaves) void attn_gqa_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ units, const uint16_t* __restrict__ pool,
     const uint16_t* __restrict__ k_tail, const uint16_t* __restrict__ v_tail, const int32_t* __restrict__ page_table,
     int max_pages, const int32_t* __restrict__ seq_lens, int B, int Hq, int H, int P, int num_pages, int S, int C,
-    float scale, float* __restrict__ ws_acc, float* __restrict__ ws_ml, uint32_t* __restrict__ status) {
-  __shared__ uint16_t esc_all[kGqaWaves][16 * 128];
+    float scale, float* __restrict__ ws_acc, float* __restrict__ ws_ml, uint32_t* __restrict__ deferred,
+    uint32_t* __restrict__ status) {
+  __shared__ uint16_t esc_all[kGqaWaves][POOL ? esc_lds_elems<128>() : 1];
   __shared__ uint32_t vlds_all[kGqaWaves][128 * 8];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int grp = Hq / H, nchunks = (grp + kGqaRows - 1) / kGqaRows;
   const int item = (int)uniform(blockIdx.x * kGqaWaves + wave);
   if (item >= B * H * nchunks * S) return;
+  if constexpr (POOL) {
+    if (sload<uint32_t>(deferred + item) == 0) return;
+  }
   const int s = item % S, qc = (item / S) % nchunks, h = (item / (S * nchunks)) % H, r = item / (S * nchunks * H);
   const int hq0 = h * grp + qc * kGqaRows, nq = min(kGqaRows, grp - qc * kGqaRows);
   int L = sload<int32_t>(seq_lens + r);
   if (L > max_pages * P || L < 0) {
-    if (lane == 0 && s == 0 && h == 0 && qc == 0) atomicOr(status, kStatusSeqTooLong);
+    if (!POOL && lane == 0 && s == 0 && h == 0 && qc == 0) atomicOr(status, kStatusSeqTooLong);
     L = L < 0 ? 0 : max_pages * P;
   }
   const int nfull = L / P, rows = L % P;
   const int Sr = active_splits(nfull, C);
-  if (s >= Sr) return;
+  if (s >= Sr) {
+    if (!POOL && lane == 0) deferred[item] = 0;
+    return;
+  }
   const int p0 = s * C, p1 = min(p0 + C, nfull);
   GqaState st;
   gqa_init(st, q, r, Hq, hq0, nq, lane);
   const int32_t* pt_row = page_table + (size_t)r * max_pages;
   const int T = P / kTile;
-  const int nsteps = (p1 > p0 ? p1 - p0 : 0) * T;
   uint32_t krank = 0, vrank = 0;
   uint16_t* esc_lds = esc_all[wave];
   uint32_t* vlds = vlds_all[wave];
-  if (nsteps > 0) {
-    GqaCStage a, b;
-    gqa_c_load(a, a, units, pt_row, p0, 0, H, h, P, num_pages, lane, status);
-    for (int i = 0; i < nsteps; i += 2) {
-      if (i + 1 < nsteps) gqa_c_load(b, a, units, pt_row, p0 + (i + 1) / T, (i + 1) % T, H, h, P, num_pages, lane, status);
-      gqa_c_compute(st, a, P, krank, vrank, esc_lds, vlds, pool, scale, lane);
-      if (i + 1 >= nsteps) break;
-      if (i + 2 < nsteps) gqa_c_load(a, b, units, pt_row, p0 + (i + 2) / T, (i + 2) % T, H, h, P, num_pages, lane, status);
-      gqa_c_compute(st, b, P, krank, vrank, esc_lds, vlds, pool, scale, lane);
+  if constexpr (!POOL) {
+    const int nsteps = (p1 > p0 ? p1 - p0 : 0) * T;
+    bool skipped = false;
+    if (nsteps > 0) {
+      GqaCStage a, b;
+      gqa_c_load(a, a, units, pt_row, p0, 0, H, h, P, num_pages, lane, status);
+      for (int i = 0; i < nsteps; i += 2) {
+        if (i + 1 < nsteps) gqa_c_load(b, a, units, pt_row, p0 + (i + 1) / T, (i + 1) % T, H, h, P, num_pages, lane, status);
+        skipped |= !gqa_c_compute<false>(st, a, P, krank, vrank, esc_lds, vlds, pool, scale, lane);
+        if (i + 1 >= nsteps) break;
+        if (i + 2 < nsteps) gqa_c_load(a, b, units, pt_row, p0 + (i + 2) / T, (i + 2) % T, H, h, P, num_pages, lane, status);
+        skipped |= !gqa_c_compute<false>(st, b, P, krank, vrank, esc_lds, vlds, pool, scale, lane);
+      }
     }
-  }
-  if (s == Sr - 1 && rows > 0) {
-    const size_t toff = ((size_t)r * H + h) * P * 128;
-    for (int t0 = 0; t0 < rows; t0 += kTile)
-      gqa_raw_tile(st, k_tail + toff, v_tail + toff, t0, min(kTile, rows - t0), scale, vlds, lane);
+    if (lane == 0) deferred[item] = skipped ? 1u : 0u;
+    if (s == Sr - 1 && rows > 0) {
+      const size_t toff = ((size_t)r * H + h) * P * 128;
+      for (int t0 = 0; t0 < rows; t0 += kTile)
+        gqa_raw_tile(st, k_tail + toff, v_tail + toff, t0, min(kTile, rows - t0), scale, vlds, lane);
+    }
+  } else {
+    gqa_resume(st, r, Hq, hq0, nq, S, s, ws_acc, ws_ml, lane);
+    const uint32_t hdr_off = hdr_offset(P, 128) + 8;
+    for (int c0 = p0; c0 < p1; c0 += 64) {
+      const int pg = c0 + lane;
+      bool in_pool = false;
+      if (pg < p1) {
+        const int pid = pt_row[pg];
+        if (pid >= 0 && pid < num_pages)
+          in_pool = *reinterpret_cast<const uint64_t*>(units + ((size_t)pid * H + h) * unit_bytes(P, 128) + hdr_off) !=
+                    kInline;
+      }
+      uint64_t todo = ballot(in_pool);
+      while (todo) {
+        const int page = c0 + __builtin_ctzll(todo);
+        todo &= todo - 1;
+        for (int t = 0; t < T; ++t) {
+          GqaCStage a;
+          gqa_c_load(a, a, units, pt_row, page, t, H, h, P, num_pages, lane, status);
+          gqa_c_compute<true>(st, a, P, krank, vrank, esc_lds, vlds, pool, scale, lane);
+        }
+      }
+    }
   }
   gqa_store(st, r, Hq, hq0, nq, S, s, ws_acc, ws_ml, lane);
 }
@@ -330,11 +397,14 @@ static unsigned gqa_blocks(int B, int Hq, int H, int S) {
 int launch_attn_gqa(const uint16_t* q, const uint8_t* units, const uint16_t* pool, const uint16_t* k_tail,
                     const uint16_t* v_tail, const int32_t* page_table, int max_pages, const int32_t* seq_lens,
                     int B, int Hq, int H, int D, int P, int num_pages, int S, int C, float scale, float* ws_acc,
-                    float* ws_ml, uint32_t* status, hipStream_t stream) {
+                    float* ws_ml, uint32_t* deferred, uint32_t* status, hipStream_t stream) {
   if (D != 128) return -2;
-  hipLaunchKernelGGL(attn_gqa_kernel, dim3(gqa_blocks(B, Hq, H, S)), dim3(64 * kGqaWaves), 0, stream, q, units, pool,
-                     k_tail, v_tail, page_table, max_pages, seq_lens, B, Hq, H, P, num_pages, S, C, scale, ws_acc,
-                     ws_ml, status);
+  hipLaunchKernelGGL(attn_gqa_kernel<false>, dim3(gqa_blocks(B, Hq, H, S)), dim3(64 * kGqaWaves), 0, stream, q, units,
+                     pool, k_tail, v_tail, page_table, max_pages, seq_lens, B, Hq, H, P, num_pages, S, C, scale, ws_acc,
+                     ws_ml, deferred, status);
+  hipLaunchKernelGGL(attn_gqa_kernel<true>, dim3(gqa_blocks(B, Hq, H, S)), dim3(64 * kGqaWaves), 0, stream, q, units,
+                     pool, k_tail, v_tail, page_table, max_pages, seq_lens, B, Hq, H, P, num_pages, S, C, scale, ws_acc,
+                     ws_ml, deferred, status);
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 

@@ -108,17 +108,20 @@ __device__ __forceinline__ void mha_accumulate_v(MhaState<D>& st, const uint32_t
   }
 }
 
-template <int D>
-__device__ __forceinline__ void mha_compute(MhaState<D>& st, const MhaStage<D>& stg, int P, uint32_t& krank,
+// Returns false, leaving the state untouched, when the unit's escapes are in the pool and POOL
+// is off.
+template <int D, bool POOL>
+__device__ __forceinline__ bool mha_compute(MhaState<D>& st, const MhaStage<D>& stg, int P, uint32_t& krank,
                                             uint32_t& vrank, uint16_t* lds, const uint16_t* pool, float scale,
                                             int lane) {
-  if (!stg.unit) return;
+  if (!stg.unit) return true;
   constexpr int VK = KRaw<D>::VK, NS = D / 64;
-  if (stg.tile == 0) { krank = 0; vrank = 0; }
   const UnitHeader hdr = header_from_meta<D>(stg.meta);
+  if (!POOL && hdr.off != kInline) return false;
+  if (stg.tile == 0) { krank = 0; vrank = 0; }
   uint32_t kp[VK / 2];
   decode_k<D>(stg.k, k_base_from_meta<D, false>(stg.meta, lane), kp);
-  if (hdr.kc) patch_k_tile<D, false>(kp, stg.k, stg.meta, hdr, P, stg.tile, krank, lds, pool, lane);
+  if (hdr.kc) patch_k_tile<D, false, POOL>(kp, stg.k, stg.meta, hdr, P, stg.tile, krank, lds, pool, lane);
   float a0 = 0.f, a1 = 0.f;
 #pragma unroll
   for (int j = 0; j < VK / 2; j += 2) {
@@ -131,8 +134,9 @@ __device__ __forceinline__ void mha_compute(MhaState<D>& st, const MhaStage<D>& 
   uint32_t vp[NS * 8];
 #pragma unroll
   for (int g = 0; g < NS; ++g) decode_v_seg(stg.v.seg[g], v_bases<D>(stg.meta, g), &vp[8 * g]);
-  if (hdr.vc) patch_v_tile<D>(vp, stg.v, stg.meta, hdr, P, stg.tile, vrank, lds, pool, lane);
+  if (hdr.vc) patch_v_tile<D, POOL>(vp, stg.v, stg.meta, hdr, P, stg.tile, vrank, lds, pool, lane);
   mha_accumulate_v<D>(st, vp, phi, plo);
+  return true;
 }
 
 // The uncompressed tail rows (at most P-1 tokens) of one request and head, one 16-token tile at
@@ -171,34 +175,46 @@ __device__ __forceinline__ void mha_tail(MhaState<D>& st, const uint16_t* tk, co
   }
 }
 
-template <int D>
+// Two instances. POOL = false is the fast kernel: it handles units whose escapes are inline
+// and skips a unit whose escapes are in the pool, marking the item in `deferred` (written for
+// every item). POOL = true then runs only the marked items: it resumes from the partial the
+// fast instance stored and adds the skipped units, which it finds by reading the headers of
+// the split's units 64 at a time. Keeping the pool path out of the fast instance keeps its
+// register count, and so its occupancy, at what the inline path needs, while the rare pool
+// units cost only their own work.
+template <int D, bool POOL>
 __global__ __launch_bounds__(64 * kWavesPerBlock) void attn_mha_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ units, const uint16_t* __restrict__ pool,
     const uint16_t* __restrict__ k_tail, const uint16_t* __restrict__ v_tail, const int32_t* __restrict__ page_table,
     int max_pages, const int32_t* __restrict__ seq_lens, int B, int H, int P, int num_pages, int S, int C,
-    float scale, float* __restrict__ ws_acc, float* __restrict__ ws_ml, uint32_t* __restrict__ status) {
-  __shared__ uint16_t lds_all[kWavesPerBlock][16 * D];
+    float scale, float* __restrict__ ws_acc, float* __restrict__ ws_ml, uint32_t* __restrict__ deferred,
+    uint32_t* __restrict__ status) {
+  __shared__ uint16_t lds_all[kWavesPerBlock][POOL ? esc_lds_elems<D>() : 1];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int item = (int)uniform(blockIdx.x * kWavesPerBlock + wave);
   if (item >= B * H * S) return;
+  if constexpr (POOL) {
+    if (sload<uint32_t>(deferred + item) == 0) return;
+  }
   const int s = item % S, h = (item / S) % H, r = item / (S * H);
   uint16_t* lds = lds_all[wave];
   int L = sload<int32_t>(seq_lens + r);
   if (L > max_pages * P || L < 0) {
-    if (lane == 0 && s == 0 && h == 0) atomicOr(status, kStatusSeqTooLong);
+    if (!POOL && lane == 0 && s == 0 && h == 0) atomicOr(status, kStatusSeqTooLong);
     L = L < 0 ? 0 : max_pages * P;
   }
   const int nfull = L / P, rows = L % P;
   const int Sr = active_splits(nfull, C);
-  if (s >= Sr) return;
+  if (s >= Sr) {
+    if (!POOL && lane == 0) deferred[item] = 0;
+    return;
+  }
   const int p0 = s * C, p1 = min(p0 + C, nfull);
   constexpr int VK = KRaw<D>::VK;
+  const size_t slot = ((size_t)r * H + h) * S + s;
+  float* acc = ws_acc + slot * D;
 
   MhaState<D> st;
-  st.m = -INFINITY;
-  st.l = 0.f;
-#pragma unroll
-  for (int i = 0; i < D / 64; ++i) st.acc[i] = 0.f;
   {
     const uint32_t* qrow = reinterpret_cast<const uint32_t*>(q + ((size_t)r * H + h) * D + (lane & 3) * VK);
 #pragma unroll
@@ -206,24 +222,59 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void attn_mha_kernel(
   }
   const int32_t* pt_row = page_table + (size_t)r * max_pages;
   const int T = P / kTile;
-  const int nsteps = (p1 > p0 ? p1 - p0 : 0) * T;
   uint32_t krank = 0, vrank = 0;
-  if (nsteps > 0) {
-    MhaStage<D> a, b;
-    mha_load<D>(a, a, units, pt_row, p0, 0, H, h, P, num_pages, lane, status);
-    for (int i = 0; i < nsteps; i += 2) {
-      if (i + 1 < nsteps)
-        mha_load<D>(b, a, units, pt_row, p0 + (i + 1) / T, (i + 1) % T, H, h, P, num_pages, lane, status);
-      mha_compute<D>(st, a, P, krank, vrank, lds, pool, scale, lane);
-      if (i + 1 >= nsteps) break;
-      if (i + 2 < nsteps)
-        mha_load<D>(a, b, units, pt_row, p0 + (i + 2) / T, (i + 2) % T, H, h, P, num_pages, lane, status);
-      mha_compute<D>(st, b, P, krank, vrank, lds, pool, scale, lane);
+  if constexpr (!POOL) {
+    st.m = -INFINITY;
+    st.l = 0.f;
+#pragma unroll
+    for (int i = 0; i < D / 64; ++i) st.acc[i] = 0.f;
+    const int nsteps = (p1 > p0 ? p1 - p0 : 0) * T;
+    bool skipped = false;
+    if (nsteps > 0) {
+      MhaStage<D> a, b;
+      mha_load<D>(a, a, units, pt_row, p0, 0, H, h, P, num_pages, lane, status);
+      for (int i = 0; i < nsteps; i += 2) {
+        if (i + 1 < nsteps)
+          mha_load<D>(b, a, units, pt_row, p0 + (i + 1) / T, (i + 1) % T, H, h, P, num_pages, lane, status);
+        skipped |= !mha_compute<D, false>(st, a, P, krank, vrank, lds, pool, scale, lane);
+        if (i + 1 >= nsteps) break;
+        if (i + 2 < nsteps)
+          mha_load<D>(a, b, units, pt_row, p0 + (i + 2) / T, (i + 2) % T, H, h, P, num_pages, lane, status);
+        skipped |= !mha_compute<D, false>(st, b, P, krank, vrank, lds, pool, scale, lane);
+      }
     }
-  }
-  if (s == Sr - 1 && rows > 0) {
-    const size_t toff = ((size_t)r * H + h) * P * D;
-    mha_tail<D>(st, k_tail + toff, v_tail + toff, rows, scale, lane);
+    if (lane == 0) deferred[item] = skipped ? 1u : 0u;
+    if (s == Sr - 1 && rows > 0) {
+      const size_t toff = ((size_t)r * H + h) * P * D;
+      mha_tail<D>(st, k_tail + toff, v_tail + toff, rows, scale, lane);
+    }
+  } else {
+    // resume: the stored l is the whole denominator, held here by lane 0 (a quad leader)
+    st.m = ws_ml[slot * 2 + 0];
+    st.l = lane == 0 ? ws_ml[slot * 2 + 1] : 0.f;
+#pragma unroll
+    for (int g = 0; g < D / 64; ++g) st.acc[g] = acc[lane + 64 * g];
+    const uint32_t hdr_off = hdr_offset(P, D) + 8;
+    for (int c0 = p0; c0 < p1; c0 += 64) {
+      const int pg = c0 + lane;
+      bool in_pool = false;
+      if (pg < p1) {
+        const int pid = pt_row[pg];
+        if (pid >= 0 && pid < num_pages)
+          in_pool = *reinterpret_cast<const uint64_t*>(units + ((size_t)pid * H + h) * unit_bytes(P, D) + hdr_off) !=
+                    kInline;
+      }
+      uint64_t todo = ballot(in_pool);
+      while (todo) {
+        const int page = c0 + __builtin_ctzll(todo);
+        todo &= todo - 1;
+        for (int t = 0; t < T; ++t) {
+          MhaStage<D> a;
+          mha_load<D>(a, a, units, pt_row, page, t, H, h, P, num_pages, lane, status);
+          mha_compute<D, true>(st, a, P, krank, vrank, lds, pool, scale, lane);
+        }
+      }
+    }
   }
   // partials: l summed over one lane per quad (each quad holds one token's terms)
   float lsum = (lane & 3) == 0 ? st.l : 0.f;
@@ -231,30 +282,34 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void attn_mha_kernel(
   lsum += __shfl_xor(lsum, 8);
   lsum += __shfl_xor(lsum, 16);
   lsum += __shfl_xor(lsum, 32);
-  const size_t row = (size_t)r * H + h;
-  float* acc = ws_acc + (row * S + s) * D;
 #pragma unroll
   for (int g = 0; g < D / 64; ++g) acc[lane + 64 * g] = st.acc[g];
   if (lane == 0) {
-    ws_ml[(row * S + s) * 2 + 0] = st.m;
-    ws_ml[(row * S + s) * 2 + 1] = lsum;
+    ws_ml[slot * 2 + 0] = st.m;
+    ws_ml[slot * 2 + 1] = lsum;
   }
 }
 
 int launch_attn_mha(const uint16_t* q, const uint8_t* units, const uint16_t* pool, const uint16_t* k_tail,
                     const uint16_t* v_tail, const int32_t* page_table, int max_pages, const int32_t* seq_lens,
                     int B, int H, int D, int P, int num_pages, int S, int C, float scale, float* ws_acc,
-                    float* ws_ml, uint32_t* status, hipStream_t stream) {
+                    float* ws_ml, uint32_t* deferred, uint32_t* status, hipStream_t stream) {
   const int items = B * H * S;
   dim3 grid((unsigned)(items + kWavesPerBlock - 1) / kWavesPerBlock), block(64 * kWavesPerBlock);
-  if (D == 128)
-    hipLaunchKernelGGL((attn_mha_kernel<128>), grid, block, 0, stream, q, units, pool, k_tail, v_tail, page_table,
-                       max_pages, seq_lens, B, H, P, num_pages, S, C, scale, ws_acc, ws_ml, status);
-  else if (D == 64)
-    hipLaunchKernelGGL((attn_mha_kernel<64>), grid, block, 0, stream, q, units, pool, k_tail, v_tail, page_table,
-                       max_pages, seq_lens, B, H, P, num_pages, S, C, scale, ws_acc, ws_ml, status);
-  else
+#define KVZ_LAUNCH_MHA(DD, POOLV)                                                                                 \
+  hipLaunchKernelGGL((attn_mha_kernel<DD, POOLV>), grid, block, 0, stream, q, units, pool, k_tail, v_tail,     \
+                     page_table, max_pages, seq_lens, B, H, P, num_pages, S, C, scale, ws_acc, ws_ml, deferred, \
+                     status)
+  if (D == 128) {
+    KVZ_LAUNCH_MHA(128, false);
+    KVZ_LAUNCH_MHA(128, true);
+  } else if (D == 64) {
+    KVZ_LAUNCH_MHA(64, false);
+    KVZ_LAUNCH_MHA(64, true);
+  } else {
     return -2;
+  }
+#undef KVZ_LAUNCH_MHA
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 

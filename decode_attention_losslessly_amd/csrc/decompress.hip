@@ -12,7 +12,7 @@ __global__ __launch_bounds__(64) void decompress_kernel(const uint8_t* __restric
                                                         int P, int num_pages, uint16_t* __restrict__ k_dst,
                                                         uint16_t* __restrict__ v_dst,
                                                         uint32_t* __restrict__ status) {
-  __shared__ uint16_t lds[16 * D];
+  __shared__ uint16_t lds[esc_lds_elems<D>()];
   const int lane = threadIdx.x;
   const int i = blockIdx.x / H, h = blockIdx.x % H;
   const int pid = sload<int32_t>(page_ids + i);

@@ -19,11 +19,11 @@ int launch_append(const uint16_t* k_new, const uint16_t* v_new, const int32_t* p
 int launch_attn_mha(const uint16_t* q, const uint8_t* units, const uint16_t* pool, const uint16_t* k_tail,
                     const uint16_t* v_tail, const int32_t* page_table, int max_pages, const int32_t* seq_lens,
                     int B, int H, int D, int P, int num_pages, int S, int C, float scale, float* ws_acc,
-                    float* ws_ml, uint32_t* status, hipStream_t stream);
+                    float* ws_ml, uint32_t* deferred, uint32_t* status, hipStream_t stream);
 int launch_attn_gqa(const uint16_t* q, const uint8_t* units, const uint16_t* pool, const uint16_t* k_tail,
                     const uint16_t* v_tail, const int32_t* page_table, int max_pages, const int32_t* seq_lens,
                     int B, int Hq, int Hkv, int D, int P, int num_pages, int S, int C, float scale, float* ws_acc,
-                    float* ws_ml, uint32_t* status, hipStream_t stream);
+                    float* ws_ml, uint32_t* deferred, uint32_t* status, hipStream_t stream);
 int launch_attn_dense_mha(const uint16_t* q, const uint16_t* k_pages, const uint16_t* v_pages, const int32_t* pt,
                           int max_pages, const int32_t* seq_lens, int B, int H, int D, int P, int num_pages, int S,
                           int C, float scale, float* ws_acc, float* ws_ml, uint32_t* status, hipStream_t stream);
@@ -82,10 +82,14 @@ int32_t kvz_num_splits(int32_t B, int32_t H_q, int32_t H_kv, int32_t D, int32_t 
   return split_count(max_pages_per_seq, pages_per_split(B, H_q, H_kv, P, max_pages_per_seq, pps));
 }
 
+// workspace per (request, query head, split): acc[D] and (m, l) as float, then one u32 per work
+// item (at most one item per (request, query head, split)) for the fast kernel's deferrals
+static size_t ws_bytes(int B, int Hq, int S, int D) { return (size_t)B * Hq * S * (D + 3) * sizeof(float); }
+
 size_t kvz_workspace_bytes(int32_t B, int32_t H_q, int32_t H_kv, int32_t D, int32_t P, int32_t max_pages_per_seq,
                            int32_t pps) {
   const int S = kvz_num_splits(B, H_q, H_kv, D, P, max_pages_per_seq, pps);
-  return (size_t)B * H_q * S * (D + 2) * sizeof(float);
+  return ws_bytes(B, H_q, S, D);
 }
 
 int kvz_compress_pages(const kvz_cache* c, const uint16_t* k_src, const uint16_t* v_src, const int32_t* ids,
@@ -131,16 +135,18 @@ int kvz_decode_attention_splits(const uint16_t* q, const kvz_cache* c, const int
   if (B > c->max_batch) return KVZ_ERR_INVALID_ARG;
   const int C = pages_per_split(B, H_q, H, P, max_pages, pps);
   const int S = split_count(max_pages, C);
-  if (workspace_bytes < (size_t)B * H_q * S * (D + 2) * sizeof(float)) return KVZ_ERR_WORKSPACE;
+  if (workspace_bytes < ws_bytes(B, H_q, S, D)) return KVZ_ERR_WORKSPACE;
   float* ws_acc = reinterpret_cast<float*>(workspace);
   float* ws_ml = ws_acc + (size_t)B * H_q * S * D;
+  uint32_t* deferred = reinterpret_cast<uint32_t*>(ws_ml + (size_t)B * H_q * S * 2);
   const float scale = sm_scale * 1.4426950408889634f;
   if (H_q == H)
     rc = kvz::launch_attn_mha(q, c->units, c->esc_pool, c->k_tail, c->v_tail, page_table, max_pages, seq_lens, B, H,
-                              D, P, c->num_pages, S, C, scale, ws_acc, ws_ml, c->status, as_stream(stream));
+                              D, P, c->num_pages, S, C, scale, ws_acc, ws_ml, deferred, c->status, as_stream(stream));
   else
     rc = kvz::launch_attn_gqa(q, c->units, c->esc_pool, c->k_tail, c->v_tail, page_table, max_pages, seq_lens, B,
-                              H_q, H, D, P, c->num_pages, S, C, scale, ws_acc, ws_ml, c->status, as_stream(stream));
+                              H_q, H, D, P, c->num_pages, S, C, scale, ws_acc, ws_ml, deferred, c->status,
+                              as_stream(stream));
   return rc ? (rc == -2 ? KVZ_ERR_UNSUPPORTED : KVZ_ERR_HIP) : KVZ_OK;
 }
 
@@ -156,7 +162,7 @@ int kvz_decode_attention_dense_splits(const uint16_t* q, const uint16_t* k_pages
     return KVZ_ERR_INVALID_ARG;
   const int C = pages_per_split(B, H_q, H, P, max_pages, pps);
   const int S = split_count(max_pages, C);
-  if (workspace_bytes < (size_t)B * H_q * S * (D + 2) * sizeof(float)) return KVZ_ERR_WORKSPACE;
+  if (workspace_bytes < ws_bytes(B, H_q, S, D)) return KVZ_ERR_WORKSPACE;
   float* ws_acc = reinterpret_cast<float*>(workspace);
   float* ws_ml = ws_acc + (size_t)B * H_q * S * D;
   const float scale = sm_scale * 1.4426950408889634f;
@@ -178,7 +184,7 @@ int kvz_merge_splits(const void* workspace, size_t workspace_bytes, const int32_
   if (!workspace || !seq_lens || !out || pps < 0) return KVZ_ERR_INVALID_ARG;
   const int C = pages_per_split(B, H_q, H, P, max_pages, pps);
   const int S = split_count(max_pages, C);
-  if (workspace_bytes < (size_t)B * H_q * S * (D + 2) * sizeof(float)) return KVZ_ERR_WORKSPACE;
+  if (workspace_bytes < ws_bytes(B, H_q, S, D)) return KVZ_ERR_WORKSPACE;
   const float* ws_acc = reinterpret_cast<const float*>(workspace);
   const float* ws_ml = ws_acc + (size_t)B * H_q * S * D;
   rc = kvz::launch_merge(ws_acc, ws_ml, seq_lens, B, H_q, D, P, max_pages, S, C, dense ? 1 : 0, out, out_f32,

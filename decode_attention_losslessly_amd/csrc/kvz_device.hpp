@@ -175,8 +175,11 @@ __device__ __forceinline__ uint32_t set_half(uint32_t v, int half, uint32_t x) {
 // wave-uniform, so the register is addressed through the GPR index mode, not a branch tree.
 template <int N>
 __device__ __forceinline__ void patch_one(uint32_t (&pairs)[N], int reg, int lane, int half, uint32_t x) {
+  reg = (int)uniform((uint32_t)reg);
+  const uint32_t keep = uniform(half ? 0x0000FFFFu : 0xFFFF0000u);
+  const uint32_t put = uniform(half ? (x << 16) : (x & 0xFFFFu));
   const uint32_t old = pairs[reg];
-  pairs[reg] = lane_id() == lane ? set_half(old, half, x) : old;
+  pairs[reg] = lane_id() == lane ? ((old & keep) | put) : old;
 }
 
 // Patches escaped values from a list staged in LDS (any number of escapes), per lane.
@@ -199,6 +202,13 @@ __device__ __forceinline__ void patch_lds(uint32_t (&pairs)[4 * NW], const uint3
 }
 
 __device__ __forceinline__ uint32_t popc_flags(uint32_t f) { return (uint32_t)__builtin_popcount(f); }
+
+// Escape flags with bit order = storage order: position j of the word goes to bit
+// 4*(j/2) + (j%2), so that walking set bits from the lowest visits positions in list order.
+__device__ __forceinline__ uint32_t flags_in_order(uint32_t f) {
+  return ((f & 0x8888u) >> 3) | (((f >> 16) & 0x8888u) >> 2);
+}
+__device__ __forceinline__ int ordered_bit_to_pos(int b) { return 2 * (b >> 2) + (b & 1); }
 
 // ---------------------------------------------------------------- BF16 helpers
 __device__ __forceinline__ float bf16lo_to_f32(uint32_t p) { return __builtin_bit_cast(float, p << 16); }

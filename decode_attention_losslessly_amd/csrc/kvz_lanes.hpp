@@ -162,111 +162,177 @@ __device__ __forceinline__ UnitHeader header_from_meta(uint32_t meta) {
 //   inline: the entries of this tile are walked with wave-uniform control; each names its lane,
 //           register and half directly, so no lane has to search its offsets;
 //   pool:   every lane finds its escape codes, a wave scan ranks them in storage order, the
-//           tile's part of the list is staged in `lds` (room for 16*D values) and each lane
-//           patches its own registers.
+//           tile's part of the list and a copy of the pairs go to `lds` (16*D u16 of values,
+//           then 64 lanes x (D/4 or D/8) u32 of pairs) and each lane patches its own copy.
 // `cursor` is the block-level index of the tile's first escape and is advanced past the tile.
 
 // K, multi-head layout: storage position p of a tile -> lane p / VK, value p % VK.
 // K, grouped-query layout: chunk p / 32 sits in lane 16*(chunk%4) + chunk/4.
 template <int D, bool GQA>
 __device__ __forceinline__ void k_position(uint32_t p, int& lane, int& reg, int& half) {
-  constexpr int VK = KRaw<D>::VK;
-  const int c = (int)p / VK, j = (int)p % VK;
-  lane = GQA ? (16 * (c & 3) + (c >> 2)) : c;
-  reg = j >> 1;
-  half = j & 1;
+  constexpr uint32_t VK = KRaw<D>::VK;
+  const uint32_t c = p / VK, j = p % VK;
+  lane = (int)(GQA ? (16 * (c & 3) + (c >> 2)) : c);
+  reg = (int)(j >> 1);
+  half = (int)(j & 1);
+}
+
+// Pool lists (many escapes, values only) are patched through LDS with loops that keep few
+// registers live, so that this rarely-hot path does not raise the register count of the main
+// loop. `lds` holds, per wave, the tile's escape values (16*D u16) followed by a copy of the
+// lane's pairs (64 lanes x N u32).
+//   chunks(lane)  the storage chunks this lane holds, in storage order, each `span` positions
+//                 long and read from `nib` words of 8 positions
+
+// u16 elements of the per-wave LDS area the escape paths use: 16*D values + 64 lanes x D/8 pairs
+template <int D>
+constexpr int esc_lds_elems() { return 32 * D; }
+
+// Writes escape x of position j (within this lane's run of pairs) into the LDS copy.
+__device__ __forceinline__ void lds_pair_half(uint32_t* mine, int j, uint32_t x) {
+  reinterpret_cast<uint16_t*>(mine)[j] = (uint16_t)x;   // pair j/2, half j%2 (little-endian)
 }
 
 template <int D, bool GQA>
-__device__ __forceinline__ void patch_k_tile(uint32_t (&pairs)[KRaw<D>::VK / 2], const KRaw<D>& raw,
-                                             uint32_t meta, const UnitHeader& h, int P, int tile,
-                                             uint32_t& cursor, uint16_t* lds, const uint16_t* pool, int lane) {
-  constexpr int NW = KRaw<D>::NW;
-  const uint32_t lo = (uint32_t)tile * kTile * D, hi = lo + kTile * D;
-  if (h.off == kInline) {
-    const uint32_t end = min(h.kc, (uint32_t)inline_capacity(P, D));
-    while (cursor < end) {
-      const uint32_t ent = readlane(meta, hdr_lane<D>() + 4 + (int)cursor);
-      const uint32_t p = ent >> 16;
-      if (p >= hi) break;
-      int l, reg, half;
-      k_position<D, GQA>(p - lo, l, reg, half);
-      patch_one<KRaw<D>::VK / 2>(pairs, reg, l, half, ent & 0xFFFFu);
-      ++cursor;
-    }
-    return;
-  }
-  uint32_t flags[NW], c = 0;
+__device__ __forceinline__ void pool_patch_k(uint32_t (&pairs)[KRaw<D>::VK / 2], const KRaw<D>& raw,
+                                             const UnitHeader& h, uint32_t& cursor, uint16_t* lds,
+                                             const uint16_t* pool, int lane) {
+  constexpr int N = KRaw<D>::VK / 2, NW = KRaw<D>::NW;
+  uint32_t c = 0;
 #pragma unroll
-  for (int w = 0; w < NW; ++w) {
-    flags[w] = escape_flags(raw.nib[w]);
-    c += popc_flags(flags[w]);
-  }
-  // counts in storage order -> exclusive scan -> back to this lane
-  const int src = GQA ? (16 * (lane & 3) + (lane >> 2)) : lane;      // lane holding chunk `lane`
+  for (int w = 0; w < NW; ++w) c += popc_flags(escape_flags(raw.nib[w]));
+  // ranks in storage order (chunk order; the grouped-query layout permutes lanes)
+  const int src = GQA ? (16 * (lane & 3) + (lane >> 2)) : lane;
   const uint32_t c_ord = GQA ? (uint32_t)__shfl((int)c, src) : c;
   const uint32_t inc = wave_incl_scan(c_ord);
   const uint32_t total = readlane(inc, 63);
   const uint32_t exc_ord = inc - c_ord;
-  const uint32_t exc = GQA ? (uint32_t)__shfl((int)exc_ord, k_chunk<D, GQA>(lane)) : exc_ord;
+  uint32_t rank = GQA ? (uint32_t)__shfl((int)exc_ord, k_chunk<D, GQA>(lane)) : exc_ord;
   if (total == 0) return;
-  // never read past this block's list, even if the offsets disagree with the header
-  const uint32_t avail = h.kc > cursor ? min(total, h.kc - cursor) : 0u;
-  const uint16_t* src_list = pool + h.off + cursor;
+  const uint32_t cur = uniform(cursor);
+  const uint32_t avail = h.kc > cur ? min(total, h.kc - cur) : 0u;
+  const uint16_t* src_list = pool + h.off + cur;
   for (uint32_t i = lane; i < avail; i += 64) lds[i] = src_list[i];
+  uint32_t* mine = reinterpret_cast<uint32_t*>(lds + 16 * D) + lane * N;
+#pragma unroll
+  for (int i = 0; i < N; i += 4) *reinterpret_cast<uint4*>(mine + i) = make_uint4(pairs[i], pairs[i + 1], pairs[i + 2], pairs[i + 3]);
   wave_lds_sync();
-  patch_lds<NW>(pairs, flags, lds, exc, avail);
+  for (int w = 0; w < NW; ++w) {
+    uint32_t f = flags_in_order(escape_flags(raw.nib[w]));
+    while (f) {                                    // positions of the word in list order
+      const int pos = ordered_bit_to_pos(__builtin_ctz(f));
+      f &= f - 1;
+      if (rank < avail) lds_pair_half(mine, 8 * w + pos, lds[rank]);
+      ++rank;
+    }
+  }
   wave_lds_sync();
-  cursor += total;
+#pragma unroll
+  for (int i = 0; i < N; i += 4) {
+    const uint4 v = *reinterpret_cast<const uint4*>(mine + i);
+    pairs[i] = v.x; pairs[i + 1] = v.y; pairs[i + 2] = v.z; pairs[i + 3] = v.w;
+  }
+  wave_lds_sync();
+  cursor = cur + total;
 }
 
-// V: segments s = 0 .. D/64-1 (dims lane + 64 s), storage order segment-major then lane;
-// pairs[s * 8 + k] holds tokens 2k, 2k+1 of dim lane + 64 s.
 template <int D>
-__device__ __forceinline__ void patch_v_tile(uint32_t (&pairs)[D / 8], const VRaw<D>& raw, uint32_t meta,
-                                             const UnitHeader& h, int P, int tile, uint32_t& cursor, uint16_t* lds,
-                                             const uint16_t* pool, int lane) {
-  constexpr int NS = D / 64;
-  const uint32_t lo = (uint32_t)tile * kTile * D, hi = lo + kTile * D;
-  if (h.off == kInline) {
-    const uint32_t end = min(h.kc + h.vc, (uint32_t)inline_capacity(P, D));
-    while (h.kc + cursor < end) {
-      const uint32_t ent = readlane(meta, hdr_lane<D>() + 4 + (int)(h.kc + cursor));
-      const uint32_t p = ent >> 16;
-      if (p >= hi) break;
-      const int q = (int)(p - lo), d = q >> 4, tok = q & 15;
-      patch_one<D / 8>(pairs, (d >> 6) * 8 + (tok >> 1), d & 63, tok & 1, ent & 0xFFFFu);
-      ++cursor;
-    }
-    return;
-  }
-  uint32_t flags[NS][2], packed = 0;
+__device__ __forceinline__ void pool_patch_v(uint32_t (&pairs)[D / 8], const VRaw<D>& raw, const UnitHeader& h,
+                                             uint32_t& cursor, uint16_t* lds, const uint16_t* pool, int lane) {
+  constexpr int NS = D / 64, N = D / 8;
+  uint32_t packed = 0;
 #pragma unroll
-  for (int s = 0; s < NS; ++s) {
-    flags[s][0] = escape_flags(raw.seg[s].nib.x);
-    flags[s][1] = escape_flags(raw.seg[s].nib.y);
-    packed |= (popc_flags(flags[s][0]) + popc_flags(flags[s][1])) << (16 * s);
-  }
+  for (int s = 0; s < NS; ++s)
+    packed |= (popc_flags(escape_flags(raw.seg[s].nib.x)) + popc_flags(escape_flags(raw.seg[s].nib.y))) << (16 * s);
   const uint32_t inc = wave_incl_scan(packed);
   const uint32_t tot = readlane(inc, 63);
   const uint32_t exc = inc - packed;
   const uint32_t t0 = tot & 0xFFFFu;
   const uint32_t total = t0 + (tot >> 16);
   if (total == 0) return;
-  const uint32_t avail = h.vc > cursor ? min(total, h.vc - cursor) : 0u;
-  const uint16_t* src_list = pool + h.off + h.kc + cursor;
+  const uint32_t cur = uniform(cursor);
+  const uint32_t avail = h.vc > cur ? min(total, h.vc - cur) : 0u;
+  const uint16_t* src_list = pool + h.off + h.kc + cur;
   for (uint32_t i = lane; i < avail; i += 64) lds[i] = src_list[i];
+  uint32_t* mine = reinterpret_cast<uint32_t*>(lds + 16 * D) + lane * N;
+#pragma unroll
+  for (int i = 0; i < N; i += 4) *reinterpret_cast<uint4*>(mine + i) = make_uint4(pairs[i], pairs[i + 1], pairs[i + 2], pairs[i + 3]);
   wave_lds_sync();
-  {
-    uint32_t(&p0)[8] = *reinterpret_cast<uint32_t(*)[8]>(&pairs[0]);
-    patch_lds<2>(p0, flags[0], lds, exc & 0xFFFFu, avail);
-  }
-  if constexpr (NS > 1) {
-    uint32_t(&p1)[8] = *reinterpret_cast<uint32_t(*)[8]>(&pairs[8]);
-    patch_lds<2>(p1, flags[1], lds, t0 + (exc >> 16), avail);
+  for (int s = 0; s < NS; ++s) {
+    uint32_t rank = s == 0 ? (exc & 0xFFFFu) : t0 + (exc >> 16);
+    for (int w = 0; w < 2; ++w) {
+      uint32_t f = flags_in_order(escape_flags(w == 0 ? raw.seg[s].nib.x : raw.seg[s].nib.y));
+      while (f) {                                  // positions of the word in list order
+        const int pos = ordered_bit_to_pos(__builtin_ctz(f));
+        f &= f - 1;
+        if (rank < avail) lds_pair_half(mine, 16 * s + 8 * w + pos, lds[rank]);
+        ++rank;
+      }
+    }
   }
   wave_lds_sync();
-  cursor += total;
+#pragma unroll
+  for (int i = 0; i < N; i += 4) {
+    const uint4 v = *reinterpret_cast<const uint4*>(mine + i);
+    pairs[i] = v.x; pairs[i + 1] = v.y; pairs[i + 2] = v.z; pairs[i + 3] = v.w;
+  }
+  wave_lds_sync();
+  cursor = cur + total;
+}
+
+// Returns false, patching nothing, when the unit's list is in the pool and POOL is off: the
+// caller then leaves the work item to the general kernel.
+template <int D, bool GQA, bool POOL = true>
+__device__ __forceinline__ bool patch_k_tile(uint32_t (&pairs)[KRaw<D>::VK / 2], const KRaw<D>& raw,
+                                             uint32_t meta, const UnitHeader& h, int P, int tile,
+                                             uint32_t& cursor, uint16_t* lds, const uint16_t* pool, int lane) {
+  constexpr int N = KRaw<D>::VK / 2;
+  // everything that names an escape is wave-uniform: keep it in SGPRs
+  const uint32_t lo = uniform((uint32_t)tile * kTile * D), hi = lo + kTile * D;
+  if (h.off == kInline) {
+    const uint32_t end = uniform(min(h.kc, (uint32_t)inline_capacity(P, D)));
+    uint32_t e = uniform(cursor);
+    while (e < end) {
+      const uint32_t ent = readlane(meta, hdr_lane<D>() + 4 + (int)e);
+      const uint32_t p = ent >> 16;
+      if (p >= hi) break;
+      int l, reg, half;
+      k_position<D, GQA>(p - lo, l, reg, half);
+      patch_one<N>(pairs, reg, l, half, ent & 0xFFFFu);
+      ++e;
+    }
+    cursor = e;
+    return true;
+  }
+  if constexpr (!POOL) return false;
+  pool_patch_k<D, GQA>(pairs, raw, h, cursor, lds, pool, lane);
+  return true;
+}
+
+// V: segments s = 0 .. D/64-1 (dims lane + 64 s), storage order segment-major then lane;
+// pairs[s * 8 + k] holds tokens 2k, 2k+1 of dim lane + 64 s.
+template <int D, bool POOL = true>
+__device__ __forceinline__ bool patch_v_tile(uint32_t (&pairs)[D / 8], const VRaw<D>& raw, uint32_t meta,
+                                             const UnitHeader& h, int P, int tile, uint32_t& cursor, uint16_t* lds,
+                                             const uint16_t* pool, int lane) {
+  const uint32_t lo = uniform((uint32_t)tile * kTile * D), hi = lo + kTile * D;
+  if (h.off == kInline) {
+    const uint32_t end = uniform(min(h.kc + h.vc, (uint32_t)inline_capacity(P, D)));
+    uint32_t e = uniform(h.kc + cursor);
+    while (e < end) {
+      const uint32_t ent = readlane(meta, hdr_lane<D>() + 4 + (int)e);
+      const uint32_t p = ent >> 16;
+      if (p >= hi) break;
+      const uint32_t q = p - lo, d = q >> 4, tok = q & 15;
+      patch_one<D / 8>(pairs, (int)((d >> 6) * 8 + (tok >> 1)), (int)(d & 63), (int)(tok & 1), ent & 0xFFFFu);
+      ++e;
+    }
+    cursor = e - h.kc;
+    return true;
+  }
+  if constexpr (!POOL) return false;
+  pool_patch_v<D>(pairs, raw, h, cursor, lds, pool, lane);
+  return true;
 }
 
 }  // namespace kvz
