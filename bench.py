@@ -48,6 +48,8 @@ def parse():
     ap.add_argument("--no-dense", action="store_true", help="skip the uncompressed baseline")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-requests", type=int, default=32, help="requests in the CPU baseline sample")
+    ap.add_argument("--cold-steps", type=int, default=20,
+                    help="extra launches timed after a 1 GiB cache flush each (reported as attn_us.cold_median)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only copy MIB MiB device-to-device 5 times (calibrates HBM byte counters) and exit")
     return ap.parse_args()
@@ -136,7 +138,9 @@ def main() -> int:
     S = kvz.num_splits(B, Hq, H, D, P, w.max_pages)
     units_bytes = int(full.sum()) * H * U
     tail_bytes = int((w.seq_lens % P).sum()) * H * D * 2 * 2
-    small_bytes = int(full.sum()) * H * 4 + B * Hq * D * 2 + B * Hq * S * (D + 2) * 4
+    # page-table entries, q, the (m, l, acc) partials and the hand-off flag of every work item
+    # (written by the fast kernel, read by the pool pass)
+    small_bytes = int(full.sum()) * H * 4 + B * Hq * D * 2 + B * Hq * S * ((D + 2) * 4 + 8)
     comp_bytes = units_bytes + 2 * pool_esc + tail_bytes + small_bytes
     dense_kv_bytes = int(L.sum()) * H * D * 2 * 2
     dense_bytes = dense_kv_bytes + int(((L + P - 1) // P).sum()) * H * 4 + B * Hq * D * 2 + B * Hq * S * (D + 2) * 4
@@ -173,7 +177,7 @@ def main() -> int:
     # same kernel with the caches flushed before every launch (the pages clear L2, §IV.B)
     flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
     cold = []
-    for _ in range(min(args.steps, 20)):
+    for _ in range(args.cold_steps):
         flush.zero_()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
@@ -182,7 +186,7 @@ def main() -> int:
         c_merge()
         torch.cuda.synchronize()
         cold.append(e0.elapsed_time(e1) * 1e3)
-    cold = np.array(cold)
+    cold = np.array(cold) if cold else np.array([np.nan])
     del flush
 
     dense = None
@@ -207,7 +211,11 @@ def main() -> int:
         t = json.load(open(tfile))
         if t.get("source_digest") == source_digest():
             traffic = t.get("bytes_per_launch")
-    roofline = dict(kernel="attn_mha_kernel<128>" if Hq == H else "attn_gqa_kernel", bound="hbm",
+    # the split step is two launches: the fast kernel and the pool pass (which, for work items
+    # without pool units, only reads their flag); both are inside the timed events
+    kname = "attn_mha_kernel<128, false> + attn_mha_kernel<128, true>" if Hq == H else \
+        "attn_gqa_kernel<false> + attn_gqa_kernel<true>"
+    roofline = dict(kernel=kname, bound="hbm",
                     achieved=round(achieved, 1), peak=PEAK_HBM_GBPS, unit="GB/s",
                     frac=round(achieved / PEAK_HBM_GBPS, 4), traffic=traffic,
                     algorithmic_bytes_per_launch=comp_bytes, attn_us_mean=round(attn_mean, 2))
@@ -235,7 +243,7 @@ def main() -> int:
         "pct_peak_hbm": round(100 * achieved / PEAK_HBM_GBPS, 2),
         "uncompressed_equiv_gbps": round(dense_kv_bytes / (attn_mean * 1e-6) / 1e9, 1),
         "attn_us": {"median": round(float(np.median(attn_us)), 2), "p10": round(float(np.percentile(attn_us, 10)), 2),
-                    "p90": round(float(np.percentile(attn_us, 90)), 2), "cold_median": round(float(np.median(cold)), 2)},
+                    "p90": round(float(np.percentile(attn_us, 90)), 2), "cold_median": round(float(np.median(cold)), 2) if args.cold_steps else None},
         "merge_us": round(float(np.median(merge_us)), 2),
         "compressed_bytes": comp_bytes,
         "dense_kv_bytes": dense_kv_bytes,

@@ -37,7 +37,11 @@
  *             [2PG+8, 2PG+16)  u64 offset (in u16 elements) of the unit's escapes in the pool,
  *                              or all ones when they are inline
  *             [2PG+16, end)    inline escapes, K's then V's, when all of them fit
- *                              (kvz_inline_capacity); unused bytes are zero
+ *                              (kvz_inline_capacity): one u32 each, the raw BF16 value in
+ *                              bits 0..15 and its storage position in its block in bits
+ *                              16..31; unused bytes are zero
+ *             the meta region is 2PG+16 bytes rounded up to a multiple of 128
+ *   pool      u16 raw values only: a unit's K escapes then its V escapes, contiguous
  *   tail      per request row r and head h, P raw BF16 rows [P][D] (token-major, K and V
  *             alike) holding the L mod P newest tokens
  *
