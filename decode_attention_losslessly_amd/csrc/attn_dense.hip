@@ -47,13 +47,15 @@ __device__ __forceinline__ void dense_load(DenseStage<D>& st, const DenseStage<D
   if (!st.kpage) return;
   constexpr int VK = D / 4;
   const int tok = tile * kTile + lane / 4;
+  // K: each load covers a quarter of every lane's 64-byte run, so the four loads share cache
+  // lines and go through the caches normally; V rows are read whole and streamed.
   const uint4* kr = reinterpret_cast<const uint4*>(st.kpage + (size_t)tok * D + (lane & 3) * VK);
 #pragma unroll
   for (int j = 0; j < VK / 8; ++j) st.k[j] = kr[j];
   const int dp = (D == 128) ? lane : (lane & 31);
   const uint32_t* vr = reinterpret_cast<const uint32_t*>(st.vpage + (size_t)tile * kTile * D) + dp;
 #pragma unroll
-  for (int t = 0; t < 16; ++t) st.v[t] = vr[(size_t)t * (D / 2)];
+  for (int t = 0; t < 16; ++t) st.v[t] = stream4(vr + (size_t)t * (D / 2));
 }
 
 struct DenseState {

@@ -169,6 +169,7 @@ __device__ __forceinline__ void gqa_raw_tile(GqaState& st, const uint16_t* kpage
   uint32_t kp[16];
   const int tok = lane & 15;
   const bool ok = tok < rows;
+  // K loads share cache lines with each other (cached); V rows are read whole (streamed)
   const uint4* kr = reinterpret_cast<const uint4*>(kpage + (size_t)(tok0 + tok) * 128 + 32 * (lane >> 4));
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -178,7 +179,7 @@ __device__ __forceinline__ void gqa_raw_tile(GqaState& st, const uint16_t* kpage
   uint32_t raw[16];
   const uint32_t* vr = reinterpret_cast<const uint32_t*>(vpage + (size_t)tok0 * 128) + lane;
 #pragma unroll
-  for (int t = 0; t < 16; ++t) raw[t] = t < rows ? vr[(size_t)t * 64] : 0u;
+  for (int t = 0; t < 16; ++t) raw[t] = t < rows ? stream4(vr + (size_t)t * 64) : 0u;
   uint32_t vp[2][8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) {

@@ -29,34 +29,26 @@ template <int D>
 struct MhaStage {
   const uint8_t* unit;
   int tile;
+  bool ok;         // false when the page id was out of range: a stand-in unit was read
   uint32_t meta;   // this lane's dword of the tile's meta window
+  uint32_t kbase;  // base of this lane's K group
   KRaw<D> k;
   VRaw<D> v;
 };
 
-// Issues the loads of one (page, tile) step. Tile 0 of a page reads the page id; later tiles of
-// the same page reuse `prev`'s unit.
+// Issues the loads of one (page, tile) step. The loads are unconditional (a bad page id reads
+// unit 0 instead and marks the stage), so that every path through the main loop has the same
+// loads in flight and the next step's loads can overlap the current step's compute.
 template <int D>
-__device__ __forceinline__ void mha_load(MhaStage<D>& st, const MhaStage<D>& prev, const uint8_t* units,
-                                         const int32_t* pt_row, int page, int tile, int H, int h, int P,
-                                         int num_pages, int lane, uint32_t* status) {
-  if (tile == 0) {
-    const int pid = sload<int32_t>(pt_row + page);
-    if (pid < 0 || pid >= num_pages) {
-      if (lane == 0) atomicOr(status, kStatusBadPage);
-      st.unit = nullptr;
-    } else {
-      st.unit = units + ((size_t)pid * H + h) * unit_bytes(P, D);
-    }
-  } else {
-    st.unit = prev.unit;
-  }
+__device__ __forceinline__ void mha_issue(MhaStage<D>& st, const uint8_t* units, int pid, int tile, int H, int h,
+                                          int P, int num_pages, int lane) {
+  st.ok = pid >= 0 && pid < num_pages;
+  st.unit = units + ((size_t)(st.ok ? pid : 0) * H + h) * unit_bytes(P, D);
   st.tile = tile;
-  if (st.unit) {
-    st.meta = load_meta(st.unit, P, D, tile, lane);
-    load_k<D, false>(st.unit, P, tile, lane, st.k);
-    load_v<D>(st.unit, P, tile, lane, st.v);
-  }
+  st.meta = load_meta(st.unit, P, D, tile, lane);
+  st.kbase = load_k_base<D, false>(st.unit, tile, lane);
+  load_k<D, false>(st.unit, P, tile, lane, st.k);
+  load_v<D>(st.unit, P, tile, lane, st.v);
 }
 
 template <int D>
@@ -114,13 +106,13 @@ template <int D, bool POOL>
 __device__ __forceinline__ bool mha_compute(MhaState<D>& st, const MhaStage<D>& stg, int P, uint32_t& krank,
                                             uint32_t& vrank, uint16_t* lds, const uint16_t* pool, float scale,
                                             int lane) {
-  if (!stg.unit) return true;
+  if (!stg.ok) return true;
   constexpr int VK = KRaw<D>::VK, NS = D / 64;
   const UnitHeader hdr = header_from_meta<D>(stg.meta);
   if (!POOL && hdr.off != kInline) return false;
   if (stg.tile == 0) { krank = 0; vrank = 0; }
   uint32_t kp[VK / 2];
-  decode_k<D>(stg.k, k_base_from_meta<D, false>(stg.meta, lane), kp);
+  decode_k<D>(stg.k, stg.kbase, kp);
   if (hdr.kc) patch_k_tile<D, false, POOL>(kp, stg.k, stg.meta, hdr, P, stg.tile, krank, lds, pool, lane);
   float a0 = 0.f, a1 = 0.f;
 #pragma unroll
@@ -229,20 +221,38 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void attn_mha_kernel(
 #pragma unroll
     for (int i = 0; i < D / 64; ++i) st.acc[i] = 0.f;
     const int nsteps = (p1 > p0 ? p1 - p0 : 0) * T;
-    bool skipped = false;
+    bool skipped = false, bad = false;
     if (nsteps > 0) {
+      // load cursor: step ln = (page lp, tile lt); it stays on the last step once there, so
+      // the loads issued past the end re-read that step (from cache) and are never computed
+      int ln = 0, lp = p0, lt = 0;
+      const int last = nsteps - 1;
+      auto advance = [&]() {
+        if (ln < last) {
+          ++ln;
+          if (++lt == T) { lt = 0; ++lp; }
+        }
+      };
       MhaStage<D> a, b;
-      mha_load<D>(a, a, units, pt_row, p0, 0, H, h, P, num_pages, lane, status);
+      int pid = sload<int32_t>(pt_row + lp);
+      mha_issue<D>(a, units, pid, lt, H, h, P, num_pages, lane);
+      advance();
+      pid = sload<int32_t>(pt_row + lp);   // one step ahead of its use
       for (int i = 0; i < nsteps; i += 2) {
-        if (i + 1 < nsteps)
-          mha_load<D>(b, a, units, pt_row, p0 + (i + 1) / T, (i + 1) % T, H, h, P, num_pages, lane, status);
+        mha_issue<D>(b, units, pid, lt, H, h, P, num_pages, lane);
+        advance();
+        pid = sload<int32_t>(pt_row + lp);
+        bad |= !a.ok;
         skipped |= !mha_compute<D, false>(st, a, P, krank, vrank, lds, pool, scale, lane);
         if (i + 1 >= nsteps) break;
-        if (i + 2 < nsteps)
-          mha_load<D>(a, b, units, pt_row, p0 + (i + 2) / T, (i + 2) % T, H, h, P, num_pages, lane, status);
+        mha_issue<D>(a, units, pid, lt, H, h, P, num_pages, lane);
+        advance();
+        pid = sload<int32_t>(pt_row + lp);
+        bad |= !b.ok;
         skipped |= !mha_compute<D, false>(st, b, P, krank, vrank, lds, pool, scale, lane);
       }
     }
+    if (bad && lane == 0) atomicOr(status, kStatusBadPage);
     if (lane == 0) deferred[item] = skipped ? 1u : 0u;
     if (s == Sr - 1 && rows > 0) {
       const size_t toff = ((size_t)r * H + h) * P * D;
@@ -268,9 +278,10 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void attn_mha_kernel(
       while (todo) {
         const int page = c0 + __builtin_ctzll(todo);
         todo &= todo - 1;
+        const int pid = sload<int32_t>(pt_row + page);
         for (int t = 0; t < T; ++t) {
           MhaStage<D> a;
-          mha_load<D>(a, a, units, pt_row, page, t, H, h, P, num_pages, lane, status);
+          mha_issue<D>(a, units, pid, t, H, h, P, num_pages, lane);
           mha_compute<D, true>(st, a, P, krank, vrank, lds, pool, scale, lane);
         }
       }

@@ -135,7 +135,6 @@ __device__ __forceinline__ float wave_max(float v) {
 constexpr uint32_t kSmMask = 0x807F807Fu;
 
 // Base term for a packed pair whose low value has base b0 and high value base b1.
-__device__ __forceinline__ uint32_t pair_base(uint32_t b0, uint32_t b1) { return (b0 << 7) | (b1 << 23); }
 
 // Rebuilds the 8 values of one offset word: S0 holds the sm bytes of positions 0..3, S1 those
 // of 4..7, W the offset word; bb[k] the base term of pair k. out[k] = (pos 2k, pos 2k+1) as a

@@ -16,6 +16,25 @@
 
 namespace kvz {
 
+// ---------------------------------------------------------------- streaming loads
+// The compressed units are read once per attention call and are far larger than the caches,
+// so their loads carry the non-temporal hint: they then do not displace the page table, q
+// and the partials in L2 and the Infinity Cache.
+typedef uint32_t nt_u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t nt_u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint4 stream16(const void* p) {
+  const nt_u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const nt_u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint2 stream8(const void* p) {
+  const nt_u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const nt_u32x2*>(p));
+  return make_uint2(v.x, v.y);
+}
+__device__ __forceinline__ uint32_t stream4(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
+}
+__device__ __forceinline__ uint32_t stream1(const uint8_t* p) { return __builtin_nontemporal_load(p); }
+
 // ---------------------------------------------------------------- K
 template <int D>
 struct KRaw {
@@ -38,17 +57,17 @@ __device__ __forceinline__ void load_k(const uint8_t* unit, int P, int tile, int
   const int c = k_chunk<D, GQA>(lane);
   const int tok = c / (D / VK), dim0 = (c % (D / VK)) * VK;
   const uint8_t* tb = unit + kblock_offset(P, D) + tile * tile_bytes(D);
-  const uint4* s = reinterpret_cast<const uint4*>(tb + c * VK);
+  const uint8_t* s = tb + c * VK;
   if constexpr (VK == 32) {
-    uint4 a = s[0], b = s[1];
+    const uint4 a = stream16(s), b = stream16(s + 16);
     r.sm[0] = a.x; r.sm[1] = a.y; r.sm[2] = a.z; r.sm[3] = a.w;
     r.sm[4] = b.x; r.sm[5] = b.y; r.sm[6] = b.z; r.sm[7] = b.w;
-    uint4 n = *reinterpret_cast<const uint4*>(tb + 16 * D + c * (VK / 2));
+    const uint4 n = stream16(tb + 16 * D + c * (VK / 2));
     r.nib[0] = n.x; r.nib[1] = n.y; r.nib[2] = n.z; r.nib[3] = n.w;
   } else {
-    uint4 a = s[0];
+    const uint4 a = stream16(s);
     r.sm[0] = a.x; r.sm[1] = a.y; r.sm[2] = a.z; r.sm[3] = a.w;
-    uint2 n = *reinterpret_cast<const uint2*>(tb + 16 * D + c * (VK / 2));
+    const uint2 n = stream8(tb + 16 * D + c * (VK / 2));
     r.nib[0] = n.x; r.nib[1] = n.y;
   }
 }
@@ -66,7 +85,7 @@ __device__ __forceinline__ uint32_t load_meta(const uint8_t* unit, int P, int D,
   else if (lane < 8 * G) off = vbase_offset(P, D, tile) + 4 * (lane - 4 * G);
   else if (lane < 8 * G + 32) off = hdr_offset(P, D) + 4 * (lane - 8 * G);
   else off = 0;
-  return *reinterpret_cast<const uint32_t*>(unit + off);
+  return stream4(unit + off);
 }
 template <int D>
 __device__ __forceinline__ int hdr_lane() { return 8 * (D / kGroup); }
@@ -80,6 +99,15 @@ __device__ __forceinline__ uint32_t k_base_from_meta(uint32_t meta, int lane) {
   const int byte = g * kTile + tok;
   const uint32_t w = (uint32_t)__builtin_amdgcn_ds_bpermute(4 * (byte >> 2), (int)meta);
   return (w >> (8 * (byte & 3))) & 0xFFu;
+}
+
+// this lane's K base, read from the unit's meta region with the tile's other loads
+template <int D, bool GQA>
+__device__ __forceinline__ uint32_t load_k_base(const uint8_t* unit, int tile, int lane) {
+  constexpr int VK = KRaw<D>::VK;
+  const int c = k_chunk<D, GQA>(lane);
+  const int tok = c / (D / VK), g = ((c % (D / VK)) * VK) / kGroup;
+  return stream1(unit + kbase_offset(D, tile) + g * kTile + tok);
 }
 
 template <int D>
@@ -108,12 +136,15 @@ __device__ __forceinline__ void load_v(const uint8_t* unit, int P, int tile, int
 #pragma unroll
   for (int s = 0; s < VRaw<D>::NS; ++s) {
     const int d = lane + 64 * s;
-    r.seg[s].sm = *reinterpret_cast<const uint4*>(tb + 16 * d);
-    r.seg[s].nib = *reinterpret_cast<const uint2*>(tb + 16 * D + 8 * d);
+    r.seg[s].sm = stream16(tb + 16 * d);
+    r.seg[s].nib = stream8(tb + 16 * D + 8 * d);
   }
 }
 
-// Base terms of the 8 token pairs of group g in tile `tile` (wave-uniform, from SGPRs).
+// Base terms of the 8 token pairs of group g in tile `tile` (wave-uniform, in SGPRs). Every
+// lane of the meta window spreads its 4 base bytes into two pair terms with one v_perm each
+// (bytes b0, b1 -> b0 << 7 | b1 << 23, likewise b2, b3); the terms of group g are then read
+// from lanes 4G + 4g .. 4G + 4g + 3.
 struct VBases {
   uint32_t bb[8];
 };
@@ -121,15 +152,13 @@ struct VBases {
 template <int D>
 __device__ __forceinline__ VBases v_bases(uint32_t meta, int g) {
   constexpr int G = D / kGroup;
+  const uint32_t lo = __builtin_amdgcn_perm(0u, meta, 0x0C010C00u) << 7;
+  const uint32_t hi = __builtin_amdgcn_perm(0u, meta, 0x0C030C02u) << 7;
   VBases r;
-  uint32_t ws[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) ws[i] = readlane(meta, 4 * G + 4 * g + i);
-#pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    const uint32_t word = ws[k >> 1];
-    const int sh = (k & 1) * 16;
-    r.bb[k] = pair_base((word >> sh) & 0xFFu, (word >> (sh + 8)) & 0xFFu);
+  for (int i = 0; i < 4; ++i) {
+    r.bb[2 * i] = readlane(lo, 4 * G + 4 * g + i);
+    r.bb[2 * i + 1] = readlane(hi, 4 * G + 4 * g + i);
   }
   return r;
 }
