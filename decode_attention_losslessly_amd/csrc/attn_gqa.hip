@@ -105,32 +105,27 @@ __device__ __forceinline__ void gqa_tile(GqaState& st, const uint32_t (&kp)[16],
 // ---------------------------------------------------------------- compressed source
 struct GqaCStage {
   const uint8_t* unit;
+  int page;         // index in the request's page table
   int tile;
+  bool ok;          // false when the page id was out of range: a stand-in unit was read
   uint32_t meta;
+  uint32_t kbase;
   KRaw<128> k;
   VRaw<128> v;
 };
 
-__device__ __forceinline__ void gqa_c_load(GqaCStage& st, const GqaCStage& prev, const uint8_t* units,
-                                           const int32_t* pt_row, int page, int tile, int H, int h, int P,
-                                           int num_pages, int lane, uint32_t* status) {
-  if (tile == 0) {
-    const int pid = sload<int32_t>(pt_row + page);
-    if (pid < 0 || pid >= num_pages) {
-      if (lane == 0) atomicOr(status, kStatusBadPage);
-      st.unit = nullptr;
-    } else {
-      st.unit = units + ((size_t)pid * H + h) * unit_bytes(P, 128);
-    }
-  } else {
-    st.unit = prev.unit;
-  }
+// Issues the loads of one (page, tile) step, unconditionally (as in the multi-head kernel), so
+// that the next step's loads stay in flight while the current step is computed.
+__device__ __forceinline__ void gqa_c_issue(GqaCStage& st, const uint8_t* units, int pid, int page, int tile, int H,
+                                            int h, int P, int num_pages, int lane) {
+  st.ok = pid >= 0 && pid < num_pages;
+  st.page = page;
+  st.unit = units + ((size_t)(st.ok ? pid : 0) * H + h) * unit_bytes(P, 128);
   st.tile = tile;
-  if (st.unit) {
-    st.meta = load_meta(st.unit, P, 128, tile, lane);
-    load_k<128, true>(st.unit, P, tile, lane, st.k);
-    load_v<128>(st.unit, P, tile, lane, st.v);
-  }
+  st.meta = load_meta(st.unit, P, 128, tile, lane);
+  st.kbase = load_k_base<128, true>(st.unit, tile, lane);
+  load_k<128, true>(st.unit, P, tile, lane, st.k);
+  load_v<128>(st.unit, P, tile, lane, st.v);
 }
 
 // Returns false, leaving the state untouched, when the unit's escapes are in the pool and POOL
@@ -139,12 +134,12 @@ template <bool POOL>
 __device__ __forceinline__ bool gqa_c_compute(GqaState& st, const GqaCStage& stg, int P, uint32_t& krank,
                                               uint32_t& vrank, uint16_t* esc_lds, uint32_t* vlds,
                                               const uint16_t* pool, float scale, int lane) {
-  if (!stg.unit) return true;
+  if (!stg.ok) return true;
   const UnitHeader hdr = header_from_meta<128>(stg.meta);
   if (!POOL && hdr.off != kInline) return false;
   if (stg.tile == 0) { krank = 0; vrank = 0; }
   uint32_t kp[16];
-  decode_k<128>(stg.k, k_base_from_meta<128, true>(stg.meta, lane), kp);
+  decode_k<128>(stg.k, stg.kbase, kp);
   if (hdr.kc) patch_k_tile<128, true, POOL>(kp, stg.k, stg.meta, hdr, P, stg.tile, krank, esc_lds, pool, lane);
   uint32_t vflat[16];
 #pragma unroll
@@ -164,22 +159,38 @@ __device__ __forceinline__ bool gqa_c_compute(GqaState& st, const GqaCStage& stg
 // ---------------------------------------------------------------- raw (dense / tail) source
 // K: token l%16, dims 32*(l/16)..+31 (64 B); V: dims 2l, 2l+1 of all 16 tokens, regrouped into
 // token pairs. Rows >= `rows` are read as zeros.
-__device__ __forceinline__ void gqa_raw_tile(GqaState& st, const uint16_t* kpage, const uint16_t* vpage, int tok0,
-                                             int rows, float scale, uint32_t* vlds, int lane) {
-  uint32_t kp[16];
+struct GqaRawStage {
+  uint4 k[4];
+  uint32_t v[16];
+  int rows;
+};
+
+__device__ __forceinline__ void gqa_raw_load(GqaRawStage& st, const uint16_t* kpage, const uint16_t* vpage, int tok0,
+                                             int rows, int lane) {
+  st.rows = rows;
   const int tok = lane & 15;
   const bool ok = tok < rows;
   // K loads share cache lines with each other (cached); V rows are read whole (streamed)
-  const uint4* kr = reinterpret_cast<const uint4*>(kpage + (size_t)(tok0 + tok) * 128 + 32 * (lane >> 4));
+  const uint4* kr = reinterpret_cast<const uint4*>(kpage + (size_t)(tok0 + (ok ? tok : 0)) * 128 + 32 * (lane >> 4));
+#pragma unroll
+  for (int j = 0; j < 4; ++j) st.k[j] = kr[j];
+  const uint32_t* vr = reinterpret_cast<const uint32_t*>(vpage + (size_t)tok0 * 128) + lane;
+#pragma unroll
+  for (int t = 0; t < 16; ++t) st.v[t] = stream4(vr + (size_t)(t < rows ? t : 0) * 64);
+}
+
+__device__ __forceinline__ void gqa_raw_compute(GqaState& st, const GqaRawStage& stg, float scale, uint32_t* vlds,
+                                                int lane) {
+  const bool ok = (lane & 15) < stg.rows;
+  uint32_t kp[16];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const uint4 x = ok ? kr[j] : make_uint4(0, 0, 0, 0);
+    const uint4 x = ok ? stg.k[j] : make_uint4(0, 0, 0, 0);
     kp[4 * j] = x.x; kp[4 * j + 1] = x.y; kp[4 * j + 2] = x.z; kp[4 * j + 3] = x.w;
   }
   uint32_t raw[16];
-  const uint32_t* vr = reinterpret_cast<const uint32_t*>(vpage + (size_t)tok0 * 128) + lane;
 #pragma unroll
-  for (int t = 0; t < 16; ++t) raw[t] = t < rows ? stream4(vr + (size_t)t * 64) : 0u;
+  for (int t = 0; t < 16; ++t) raw[t] = t < stg.rows ? stg.v[t] : 0u;
   uint32_t vp[2][8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
@@ -187,7 +198,14 @@ __device__ __forceinline__ void gqa_raw_tile(GqaState& st, const uint16_t* kpage
     vp[1][k] = __builtin_amdgcn_perm(raw[2 * k + 1], raw[2 * k], 0x07060302u);
   }
   const int vdim[2] = {2 * lane, 2 * lane + 1};
-  gqa_tile(st, kp, vdim, vp, rows, scale, vlds, lane);
+  gqa_tile(st, kp, vdim, vp, stg.rows, scale, vlds, lane);
+}
+
+__device__ __forceinline__ void gqa_raw_tile(GqaState& st, const uint16_t* kpage, const uint16_t* vpage, int tok0,
+                                             int rows, float scale, uint32_t* vlds, int lane) {
+  GqaRawStage stg;
+  gqa_raw_load(stg, kpage, vpage, tok0, rows, lane);
+  gqa_raw_compute(st, stg, scale, vlds, lane);
 }
 
 // ---------------------------------------------------------------- kernels
@@ -262,8 +280,9 @@ __device__ __forceinline__ void gqa_resume(GqaState& st, int r, int Hq, int hq0,
 }
 
 // Fast (POOL = false) and general (POOL = true) instances, as for the multi-head kernel: the
-// fast one skips units whose escapes are in the pool and marks the item; the general one
-// resumes the marked items from their stored partials and adds only those units.
+// fast one skips units whose escapes are in the pool and records the first and last of them;
+// the general one resumes the marked items from their stored partials and adds only those
+// units.
 template <bool POOL>
 __global__ __launch_bounds__(64 * kGqaWaves) void attn_gqa_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ units, const uint16_t* __restrict__ pool,
@@ -287,7 +306,12 @@ __global__ __launch_bounds__(64 * kGqaWaves) void attn_gqa_kernel(
     if (!POOL && lane == 0 && s == 0 && h == 0 && qc == 0) atomicOr(status, kStatusSeqTooLong);
     L = L < 0 ? 0 : max_pages * P;
   }
-  const int nfull = L / P, rows = L % P;
+  int nfull = L / P;
+  const int rows = L % P;
+  if (num_pages <= 0 && nfull > 0) {   // no unit slots: every full page is a bad id
+    if (!POOL && lane == 0 && s == 0 && h == 0 && qc == 0) atomicOr(status, kStatusBadPage);
+    nfull = 0;
+  }
   const int Sr = active_splits(nfull, C);
   if (s >= Sr) {
     if (!POOL && lane == 0) deferred[item] = 0;
@@ -303,19 +327,43 @@ __global__ __launch_bounds__(64 * kGqaWaves) void attn_gqa_kernel(
   uint32_t* vlds = vlds_all[wave];
   if constexpr (!POOL) {
     const int nsteps = (p1 > p0 ? p1 - p0 : 0) * T;
-    bool skipped = false;
+    int first_skip = -1, last_skip = -1;
+    bool bad = false;
+    auto note = [&](const GqaCStage& stg) {
+      if (first_skip < 0) first_skip = stg.page - p0;
+      last_skip = stg.page - p0;
+    };
     if (nsteps > 0) {
+      // load cursor as in the multi-head kernel: stays on the last step once there
+      int ln = 0, lp = p0, lt = 0;
+      const int last = nsteps - 1;
+      auto advance = [&]() {
+        if (ln < last) {
+          ++ln;
+          if (++lt == T) { lt = 0; ++lp; }
+        }
+      };
       GqaCStage a, b;
-      gqa_c_load(a, a, units, pt_row, p0, 0, H, h, P, num_pages, lane, status);
+      int pid = sload<int32_t>(pt_row + lp);
+      gqa_c_issue(a, units, pid, lp, lt, H, h, P, num_pages, lane);
+      advance();
+      pid = sload<int32_t>(pt_row + lp);
       for (int i = 0; i < nsteps; i += 2) {
-        if (i + 1 < nsteps) gqa_c_load(b, a, units, pt_row, p0 + (i + 1) / T, (i + 1) % T, H, h, P, num_pages, lane, status);
-        skipped |= !gqa_c_compute<false>(st, a, P, krank, vrank, esc_lds, vlds, pool, scale, lane);
+        gqa_c_issue(b, units, pid, lp, lt, H, h, P, num_pages, lane);
+        advance();
+        pid = sload<int32_t>(pt_row + lp);
+        bad |= !a.ok;
+        if (!gqa_c_compute<false>(st, a, P, krank, vrank, esc_lds, vlds, pool, scale, lane)) note(a);
         if (i + 1 >= nsteps) break;
-        if (i + 2 < nsteps) gqa_c_load(a, b, units, pt_row, p0 + (i + 2) / T, (i + 2) % T, H, h, P, num_pages, lane, status);
-        skipped |= !gqa_c_compute<false>(st, b, P, krank, vrank, esc_lds, vlds, pool, scale, lane);
+        gqa_c_issue(a, units, pid, lp, lt, H, h, P, num_pages, lane);
+        advance();
+        pid = sload<int32_t>(pt_row + lp);
+        bad |= !b.ok;
+        if (!gqa_c_compute<false>(st, b, P, krank, vrank, esc_lds, vlds, pool, scale, lane)) note(b);
       }
     }
-    if (lane == 0) deferred[item] = skipped ? 1u : 0u;
+    if (bad && lane == 0) atomicOr(status, kStatusBadPage);
+    if (lane == 0) deferred[item] = skip_flag(first_skip, last_skip);
     if (s == Sr - 1 && rows > 0) {
       const size_t toff = ((size_t)r * H + h) * P * 128;
       for (int t0 = 0; t0 < rows; t0 += kTile)
@@ -323,11 +371,29 @@ __global__ __launch_bounds__(64 * kGqaWaves) void attn_gqa_kernel(
     }
   } else {
     gqa_resume(st, r, Hq, hq0, nq, S, s, ws_acc, ws_ml, lane);
+    auto do_page = [&](int page) {
+      const int pid = sload<int32_t>(pt_row + page);
+      for (int t = 0; t < T; ++t) {
+        GqaCStage a;
+        gqa_c_issue(a, units, pid, page, t, H, h, P, num_pages, lane);
+        gqa_c_compute<true>(st, a, P, krank, vrank, esc_lds, vlds, pool, scale, lane);
+      }
+    };
+    // the recorded pages, then any pool unit strictly between them
+    const uint32_t flag = sload<uint32_t>(deferred + item);
+    int lo = p0, hi = p1;
+    if (flag != kScanAll) {
+      const int f = p0 + (int)(flag & 0xFFFFu) - 1, l = p0 + (int)(flag >> 16) - 1;
+      do_page(f);
+      if (l != f) do_page(l);
+      lo = f + 1;
+      hi = l;
+    }
     const uint32_t hdr_off = hdr_offset(P, 128) + 8;
-    for (int c0 = p0; c0 < p1; c0 += 64) {
+    for (int c0 = lo; c0 < hi; c0 += 64) {
       const int pg = c0 + lane;
       bool in_pool = false;
-      if (pg < p1) {
+      if (pg < hi) {
         const int pid = pt_row[pg];
         if (pid >= 0 && pid < num_pages)
           in_pool = *reinterpret_cast<const uint64_t*>(units + ((size_t)pid * H + h) * unit_bytes(P, 128) + hdr_off) !=
@@ -337,11 +403,7 @@ __global__ __launch_bounds__(64 * kGqaWaves) void attn_gqa_kernel(
       while (todo) {
         const int page = c0 + __builtin_ctzll(todo);
         todo &= todo - 1;
-        for (int t = 0; t < T; ++t) {
-          GqaCStage a;
-          gqa_c_load(a, a, units, pt_row, page, t, H, h, P, num_pages, lane, status);
-          gqa_c_compute<true>(st, a, P, krank, vrank, esc_lds, vlds, pool, scale, lane);
-        }
+        do_page(page);
       }
     }
   }
@@ -365,27 +427,59 @@ __global__ __launch_bounds__(64 * kGqaWaves) void attn_dense_gqa_kernel(
     if (lane == 0 && s == 0 && h == 0 && qc == 0 && status) atomicOr(status, kStatusSeqTooLong);
     L = L < 0 ? 0 : max_pages * P;
   }
-  const int npages = (L + P - 1) / P;
+  int npages = (L + P - 1) / P;
+  if (num_pages <= 0 && npages > 0) {   // no pages: every page id is bad
+    if (lane == 0 && s == 0 && h == 0 && qc == 0 && status) atomicOr(status, kStatusBadPage);
+    npages = 0;
+  }
   const int Sr = active_splits(npages, C);
   if (s >= Sr) return;
   const int p0 = s * C, p1 = min(p0 + C, npages);
   GqaState st;
   gqa_init(st, q, r, Hq, hq0, nq, lane);
   uint32_t* vlds = vlds_all[wave];
-  for (int pg = p0; pg < p1; ++pg) {
-    const int pid = sload<int32_t>(page_table + (size_t)r * max_pages + pg);
-    if (pid < 0 || pid >= num_pages) {
-      if (lane == 0 && status) atomicOr(status, kStatusBadPage);
-      continue;
-    }
-    const uint16_t* kpage = k_pages + ((size_t)pid * H + h) * P * 128;
-    const uint16_t* vpage = v_pages + ((size_t)pid * H + h) * P * 128;
-    for (int t0 = 0; t0 < P; t0 += kTile) {
-      const int rows = min(kTile, L - pg * P - t0);
-      if (rows <= 0) break;
-      gqa_raw_tile(st, kpage, vpage, t0, rows, scale, vlds, lane);
+  const int32_t* pt_row = page_table + (size_t)r * max_pages;
+  const int T = P / kTile;
+  // steps of 16 tokens; the last page may end early (rows < 16, or no rows at all)
+  const int nsteps = (p1 > p0 ? p1 - p0 : 0) * T;
+  bool bad = false;
+  if (nsteps > 0) {
+    int ln = 0, lp = p0, lt = 0;
+    const int last = nsteps - 1;
+    auto advance = [&]() {
+      if (ln < last) {
+        ++ln;
+        if (++lt == T) { lt = 0; ++lp; }
+      }
+    };
+    // loads of one step, unconditional: a bad page id reads page 0 and the step is skipped
+    auto issue = [&](GqaRawStage& stg, int pid, bool& ok) {
+      ok = pid >= 0 && pid < num_pages;
+      const size_t base = ((size_t)(ok ? pid : 0) * H + h) * P * 128;
+      const int rows = max(0, min(kTile, L - lp * P - lt * kTile));
+      gqa_raw_load(stg, k_pages + base, v_pages + base, lt * kTile, rows, lane);
+    };
+    GqaRawStage a, b;
+    bool aok, bok;
+    int pid = sload<int32_t>(pt_row + lp);
+    issue(a, pid, aok);
+    advance();
+    pid = sload<int32_t>(pt_row + lp);
+    for (int i = 0; i < nsteps; i += 2) {
+      issue(b, pid, bok);
+      advance();
+      pid = sload<int32_t>(pt_row + lp);
+      bad |= !aok;
+      if (aok && a.rows > 0) gqa_raw_compute(st, a, scale, vlds, lane);
+      if (i + 1 >= nsteps) break;
+      issue(a, pid, aok);
+      advance();
+      pid = sload<int32_t>(pt_row + lp);
+      bad |= !bok;
+      if (bok && b.rows > 0) gqa_raw_compute(st, b, scale, vlds, lane);
     }
   }
+  if (bad && lane == 0 && status) atomicOr(status, kStatusBadPage);
   gqa_store(st, r, Hq, hq0, nq, S, s, ws_acc, ws_ml, lane);
 }
 

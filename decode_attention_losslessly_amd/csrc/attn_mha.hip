@@ -28,6 +28,7 @@ constexpr int kWavesPerBlock = 4;
 template <int D>
 struct MhaStage {
   const uint8_t* unit;
+  int page;        // index in the request's page table
   int tile;
   bool ok;         // false when the page id was out of range: a stand-in unit was read
   uint32_t meta;   // this lane's dword of the tile's meta window
@@ -40,9 +41,10 @@ struct MhaStage {
 // unit 0 instead and marks the stage), so that every path through the main loop has the same
 // loads in flight and the next step's loads can overlap the current step's compute.
 template <int D>
-__device__ __forceinline__ void mha_issue(MhaStage<D>& st, const uint8_t* units, int pid, int tile, int H, int h,
-                                          int P, int num_pages, int lane) {
+__device__ __forceinline__ void mha_issue(MhaStage<D>& st, const uint8_t* units, int pid, int page, int tile, int H,
+                                          int h, int P, int num_pages, int lane) {
   st.ok = pid >= 0 && pid < num_pages;
+  st.page = page;
   st.unit = units + ((size_t)(st.ok ? pid : 0) * H + h) * unit_bytes(P, D);
   st.tile = tile;
   st.meta = load_meta(st.unit, P, D, tile, lane);
@@ -168,10 +170,10 @@ __device__ __forceinline__ void mha_tail(MhaState<D>& st, const uint16_t* tk, co
 }
 
 // Two instances. POOL = false is the fast kernel: it handles units whose escapes are inline
-// and skips a unit whose escapes are in the pool, marking the item in `deferred` (written for
-// every item). POOL = true then runs only the marked items: it resumes from the partial the
-// fast instance stored and adds the skipped units, which it finds by reading the headers of
-// the split's units 64 at a time. Keeping the pool path out of the fast instance keeps its
+// and skips a unit whose escapes are in the pool, recording the first and last skipped page of
+// the item in `deferred` (written for every item). POOL = true then runs only the marked
+// items: it resumes from the partial the fast instance stored and adds those two pages and any
+// other pool unit between them, found by reading the unit headers 64 at a time. Keeping the pool path out of the fast instance keeps its
 // register count, and so its occupancy, at what the inline path needs, while the rare pool
 // units cost only their own work.
 template <int D, bool POOL>
@@ -195,7 +197,12 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void attn_mha_kernel(
     if (!POOL && lane == 0 && s == 0 && h == 0) atomicOr(status, kStatusSeqTooLong);
     L = L < 0 ? 0 : max_pages * P;
   }
-  const int nfull = L / P, rows = L % P;
+  int nfull = L / P;
+  const int rows = L % P;
+  if (num_pages <= 0 && nfull > 0) {   // no unit slots: every full page is a bad id
+    if (!POOL && lane == 0 && s == 0 && h == 0) atomicOr(status, kStatusBadPage);
+    nfull = 0;
+  }
   const int Sr = active_splits(nfull, C);
   if (s >= Sr) {
     if (!POOL && lane == 0) deferred[item] = 0;
@@ -221,7 +228,12 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void attn_mha_kernel(
 #pragma unroll
     for (int i = 0; i < D / 64; ++i) st.acc[i] = 0.f;
     const int nsteps = (p1 > p0 ? p1 - p0 : 0) * T;
-    bool skipped = false, bad = false;
+    int first_skip = -1, last_skip = -1;
+    bool bad = false;
+    auto note = [&](const MhaStage<D>& stg) {
+      if (first_skip < 0) first_skip = stg.page - p0;
+      last_skip = stg.page - p0;
+    };
     if (nsteps > 0) {
       // load cursor: step ln = (page lp, tile lt); it stays on the last step once there, so
       // the loads issued past the end re-read that step (from cache) and are never computed
@@ -235,25 +247,25 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void attn_mha_kernel(
       };
       MhaStage<D> a, b;
       int pid = sload<int32_t>(pt_row + lp);
-      mha_issue<D>(a, units, pid, lt, H, h, P, num_pages, lane);
+      mha_issue<D>(a, units, pid, lp, lt, H, h, P, num_pages, lane);
       advance();
       pid = sload<int32_t>(pt_row + lp);   // one step ahead of its use
       for (int i = 0; i < nsteps; i += 2) {
-        mha_issue<D>(b, units, pid, lt, H, h, P, num_pages, lane);
+        mha_issue<D>(b, units, pid, lp, lt, H, h, P, num_pages, lane);
         advance();
         pid = sload<int32_t>(pt_row + lp);
         bad |= !a.ok;
-        skipped |= !mha_compute<D, false>(st, a, P, krank, vrank, lds, pool, scale, lane);
+        if (!mha_compute<D, false>(st, a, P, krank, vrank, lds, pool, scale, lane)) note(a);
         if (i + 1 >= nsteps) break;
-        mha_issue<D>(a, units, pid, lt, H, h, P, num_pages, lane);
+        mha_issue<D>(a, units, pid, lp, lt, H, h, P, num_pages, lane);
         advance();
         pid = sload<int32_t>(pt_row + lp);
         bad |= !b.ok;
-        skipped |= !mha_compute<D, false>(st, b, P, krank, vrank, lds, pool, scale, lane);
+        if (!mha_compute<D, false>(st, b, P, krank, vrank, lds, pool, scale, lane)) note(b);
       }
     }
     if (bad && lane == 0) atomicOr(status, kStatusBadPage);
-    if (lane == 0) deferred[item] = skipped ? 1u : 0u;
+    if (lane == 0) deferred[item] = skip_flag(first_skip, last_skip);
     if (s == Sr - 1 && rows > 0) {
       const size_t toff = ((size_t)r * H + h) * P * D;
       mha_tail<D>(st, k_tail + toff, v_tail + toff, rows, scale, lane);
@@ -264,11 +276,29 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void attn_mha_kernel(
     st.l = lane == 0 ? ws_ml[slot * 2 + 1] : 0.f;
 #pragma unroll
     for (int g = 0; g < D / 64; ++g) st.acc[g] = acc[lane + 64 * g];
+    auto do_page = [&](int page) {
+      const int pid = sload<int32_t>(pt_row + page);
+      for (int t = 0; t < T; ++t) {
+        MhaStage<D> a;
+        mha_issue<D>(a, units, pid, page, t, H, h, P, num_pages, lane);
+        mha_compute<D, true>(st, a, P, krank, vrank, lds, pool, scale, lane);
+      }
+    };
+    // the recorded pages, then any pool unit strictly between them
+    const uint32_t flag = sload<uint32_t>(deferred + item);
+    int lo = p0, hi = p1;
+    if (flag != kScanAll) {
+      const int f = p0 + (int)(flag & 0xFFFFu) - 1, l = p0 + (int)(flag >> 16) - 1;
+      do_page(f);
+      if (l != f) do_page(l);
+      lo = f + 1;
+      hi = l;
+    }
     const uint32_t hdr_off = hdr_offset(P, D) + 8;
-    for (int c0 = p0; c0 < p1; c0 += 64) {
+    for (int c0 = lo; c0 < hi; c0 += 64) {
       const int pg = c0 + lane;
       bool in_pool = false;
-      if (pg < p1) {
+      if (pg < hi) {
         const int pid = pt_row[pg];
         if (pid >= 0 && pid < num_pages)
           in_pool = *reinterpret_cast<const uint64_t*>(units + ((size_t)pid * H + h) * unit_bytes(P, D) + hdr_off) !=
@@ -278,12 +308,7 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void attn_mha_kernel(
       while (todo) {
         const int page = c0 + __builtin_ctzll(todo);
         todo &= todo - 1;
-        const int pid = sload<int32_t>(pt_row + page);
-        for (int t = 0; t < T; ++t) {
-          MhaStage<D> a;
-          mha_issue<D>(a, units, pid, t, H, h, P, num_pages, lane);
-          mha_compute<D, true>(st, a, P, krank, vrank, lds, pool, scale, lane);
-        }
+        do_page(page);
       }
     }
   }
