@@ -109,7 +109,6 @@ struct GqaCStage {
   int tile;
   bool ok;          // false when the page id was out of range: a stand-in unit was read
   uint32_t meta;
-  uint32_t kbase;
   KRaw<128> k;
   VRaw<128> v;
 };
@@ -123,7 +122,6 @@ __device__ __forceinline__ void gqa_c_issue(GqaCStage& st, const uint8_t* units,
   st.unit = units + ((size_t)(st.ok ? pid : 0) * H + h) * unit_bytes(P, 128);
   st.tile = tile;
   st.meta = load_meta(st.unit, P, 128, tile, lane);
-  st.kbase = load_k_base<128, true>(st.unit, tile, lane);
   load_k<128, true>(st.unit, P, tile, lane, st.k);
   load_v<128>(st.unit, P, tile, lane, st.v);
 }
@@ -139,7 +137,7 @@ __device__ __forceinline__ bool gqa_c_compute(GqaState& st, const GqaCStage& stg
   if (!POOL && hdr.off != kInline) return false;
   if (stg.tile == 0) { krank = 0; vrank = 0; }
   uint32_t kp[16];
-  decode_k<128>(stg.k, stg.kbase, kp);
+  decode_k<128>(stg.k, kp);
   if (hdr.kc) patch_k_tile<128, true, POOL>(kp, stg.k, stg.meta, hdr, P, stg.tile, krank, esc_lds, pool, lane);
   uint32_t vflat[16];
 #pragma unroll

@@ -7,9 +7,10 @@
 // contraction is a matrix-vector product that does not fill a matrix core:
 //
 //   * one wave per (request, head, split); four independent waves per workgroup;
-//   * K tile (16 tokens x D): lane l rebuilds the D/4 values of token l/4, dims (l%4)*D/4..,
-//     dots them with q in v_dot2_f32_bf16 and a quad DPP sum gives the token's score in all 4
-//     lanes of the quad;
+//   * K tile (16 tokens x D): lane l rebuilds the storage pieces l + 64 i (16 dims of one
+//     token each: tokens l/8 and 8 + l/8 at D = 128, token l/4 at D = 64), so every load
+//     instruction reads whole cache lines; it dots them with its 16 dims of q in
+//     v_dot2_f32_bf16 and a DPP sum over the D/16 lanes that share a token gives the score;
 //   * online softmax in the log2 domain; the wave-wide max is only taken when a score exceeds
 //     the running maximum (the rescale is exact, it is just skipped when it would multiply by 1);
 //   * probabilities are split into hi = bf16(p) and lo = bf16(p - hi), and token pairs of each
@@ -32,7 +33,6 @@ struct MhaStage {
   int tile;
   bool ok;         // false when the page id was out of range: a stand-in unit was read
   uint32_t meta;   // this lane's dword of the tile's meta window
-  uint32_t kbase;  // base of this lane's K group
   KRaw<D> k;
   VRaw<D> v;
 };
@@ -48,7 +48,6 @@ __device__ __forceinline__ void mha_issue(MhaStage<D>& st, const uint8_t* units,
   st.unit = units + ((size_t)(st.ok ? pid : 0) * H + h) * unit_bytes(P, D);
   st.tile = tile;
   st.meta = load_meta(st.unit, P, D, tile, lane);
-  st.kbase = load_k_base<D, false>(st.unit, tile, lane);
   load_k<D, false>(st.unit, P, tile, lane, st.k);
   load_v<D>(st.unit, P, tile, lane, st.v);
 }
@@ -56,17 +55,29 @@ __device__ __forceinline__ void mha_issue(MhaStage<D>& st, const uint8_t* units,
 template <int D>
 struct MhaState {
   float m;          // running max, log2 domain (wave-uniform)
-  float l;          // this lane's share of the denominator (its token's terms)
+  float l;          // this lane's share of the denominator (its tokens' terms)
   float acc[D / 64];
-  uint32_t q[KRaw<D>::VK / 2];
+  uint32_t q[8];    // dims 16*l % D .. +16 of the query, as bf16 pairs
 };
 
-// Softmax update for one tile given this lane's score s (-inf for a masked token); returns the
-// hi/lo probability pairs of the 8 token pairs as wave-uniform values.
+// lanes that hold pieces of one token, and the score of that token in all of them
 template <int D>
-__device__ __forceinline__ void mha_softmax(MhaState<D>& st, float s, uint32_t (&phi)[8], uint32_t (&plo)[8]) {
-  if (ballot(s > st.m)) {
-    const float mt = wave_max(s);
+__device__ __forceinline__ float token_sum(float v) {
+  if constexpr (D == 128) return octet_sum(v);
+  else return quad_sum(v);
+}
+
+// Softmax update for one tile given this lane's scores s[i] (token of piece i; -inf when
+// masked); returns the hi/lo probability pairs of the 8 token pairs as wave-uniform values.
+template <int D>
+__device__ __forceinline__ void mha_softmax(MhaState<D>& st, const float (&s)[D / 64], uint32_t (&phi)[8],
+                                            uint32_t (&plo)[8]) {
+  constexpr int NP = D / 64, LPT = D / 16;   // pieces per lane, lanes per token
+  float smax = s[0];
+#pragma unroll
+  for (int i = 1; i < NP; ++i) smax = fmaxf(smax, s[i]);
+  if (ballot(smax > st.m)) {
+    const float mt = wave_max(smax);
     const float mn = fmaxf(st.m, mt);
     const float alpha = __builtin_amdgcn_exp2f(st.m - mn);
     st.l *= alpha;
@@ -74,16 +85,20 @@ __device__ __forceinline__ void mha_softmax(MhaState<D>& st, float s, uint32_t (
     for (int i = 0; i < D / 64; ++i) st.acc[i] *= alpha;
     st.m = mn;
   }
-  const float p = s == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(s - st.m);
-  const float pn = dpp_f<kRowShl4>(p);               // token of the quad 4 lanes up
-  const uint32_t hi = pack_bf16(p, pn);
-  const float h_own = bf16lo_to_f32(hi), h_nb = bf16hi_to_f32(hi);
-  const uint32_t lo = pack_bf16(p - h_own, pn - h_nb);
-  st.l += h_own + bf16lo_to_f32(lo);
 #pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    phi[k] = readlane(hi, 8 * k);
-    plo[k] = readlane(lo, 8 * k);
+  for (int i = 0; i < NP; ++i) {
+    // piece i holds tokens (64 / LPT) i + l / LPT; the next token sits LPT lanes up
+    const float p = s[i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(s[i] - st.m);
+    const float pn = dpp_f<LPT == 8 ? kRowShl8 : kRowShl4>(p);
+    const uint32_t hi = pack_bf16(p, pn);
+    const float h_own = bf16lo_to_f32(hi), h_nb = bf16hi_to_f32(hi);
+    const uint32_t lo = pack_bf16(p - h_own, pn - h_nb);
+    st.l += h_own + bf16lo_to_f32(lo);
+#pragma unroll
+    for (int k = 0; k < 8 / NP; ++k) {
+      phi[(8 / NP) * i + k] = readlane(hi, 2 * LPT * k);
+      plo[(8 / NP) * i + k] = readlane(lo, 2 * LPT * k);
+    }
   }
 }
 
@@ -102,6 +117,22 @@ __device__ __forceinline__ void mha_accumulate_v(MhaState<D>& st, const uint32_t
   }
 }
 
+// scores of this lane's pieces from their rebuilt (or raw) K pairs
+template <int D>
+__device__ __forceinline__ void mha_scores(const MhaState<D>& st, const uint32_t (&kp)[D / 8], float scale,
+                                           float (&s)[D / 64]) {
+#pragma unroll
+  for (int i = 0; i < D / 64; ++i) {
+    float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; j += 2) {
+      a0 = dot2_bf16(kp[8 * i + j], st.q[j], a0);
+      a1 = dot2_bf16(kp[8 * i + j + 1], st.q[j + 1], a1);
+    }
+    s[i] = token_sum<D>(a0 + a1) * scale;
+  }
+}
+
 // Returns false, leaving the state untouched, when the unit's escapes are in the pool and POOL
 // is off.
 template <int D, bool POOL>
@@ -114,17 +145,12 @@ __device__ __forceinline__ bool mha_compute(MhaState<D>& st, const MhaStage<D>& 
   if (!POOL && hdr.off != kInline) return false;
   if (stg.tile == 0) { krank = 0; vrank = 0; }
   uint32_t kp[VK / 2];
-  decode_k<D>(stg.k, stg.kbase, kp);
+  decode_k<D>(stg.k, kp);
   if (hdr.kc) patch_k_tile<D, false, POOL>(kp, stg.k, stg.meta, hdr, P, stg.tile, krank, lds, pool, lane);
-  float a0 = 0.f, a1 = 0.f;
-#pragma unroll
-  for (int j = 0; j < VK / 2; j += 2) {
-    a0 = dot2_bf16(kp[j], st.q[j], a0);
-    a1 = dot2_bf16(kp[j + 1], st.q[j + 1], a1);
-  }
-  const float s = quad_sum(a0 + a1) * scale;
+  float sc[D / 64];
+  mha_scores<D>(st, kp, scale, sc);
   uint32_t phi[8], plo[8];
-  mha_softmax<D>(st, s, phi, plo);
+  mha_softmax<D>(st, sc, phi, plo);
   uint32_t vp[NS * 8];
 #pragma unroll
   for (int g = 0; g < NS; ++g) decode_v_seg(stg.v.seg[g], v_bases<D>(stg.meta, g), &vp[8 * g]);
@@ -134,25 +160,30 @@ __device__ __forceinline__ bool mha_compute(MhaState<D>& st, const MhaStage<D>& 
 }
 
 // The uncompressed tail rows (at most P-1 tokens) of one request and head, one 16-token tile at
-// a time; rows >= `rows` are masked.
+// a time, in the same lane layout as the compressed K; rows >= `rows` are masked.
 template <int D>
 __device__ __forceinline__ void mha_tail(MhaState<D>& st, const uint16_t* tk, const uint16_t* tv, int rows,
                                          float scale, int lane) {
-  constexpr int VK = KRaw<D>::VK, NS = D / 64;
+  constexpr int NP = D / 64, NS = D / 64;
   for (int t0 = 0; t0 < rows; t0 += kTile) {
-    const int tok = t0 + lane / 4;
-    const bool valid = tok < rows;
-    uint32_t kp[VK / 2];
-    const uint32_t* krow = reinterpret_cast<const uint32_t*>(tk + (size_t)tok * D + (lane & 3) * VK);
+    uint32_t kp[D / 8];
+    bool valid[NP];
 #pragma unroll
-    for (int j = 0; j < VK / 2; ++j) kp[j] = valid ? krow[j] : 0u;
-    float a = 0.f;
+    for (int i = 0; i < NP; ++i) {
+      const int pc = k_piece<D, false>(lane, i);
+      const int tok = t0 + piece_token<D>(pc);
+      valid[i] = tok < rows;
+      const uint4* krow = reinterpret_cast<const uint4*>(tk + (size_t)(valid[i] ? tok : 0) * D + piece_dim<D>(pc));
+      const uint4 a = krow[0], b = krow[1];
+      kp[8 * i] = a.x; kp[8 * i + 1] = a.y; kp[8 * i + 2] = a.z; kp[8 * i + 3] = a.w;
+      kp[8 * i + 4] = b.x; kp[8 * i + 5] = b.y; kp[8 * i + 6] = b.z; kp[8 * i + 7] = b.w;
+    }
+    float sc[NP];
+    mha_scores<D>(st, kp, scale, sc);
 #pragma unroll
-    for (int j = 0; j < VK / 2; ++j) a = dot2_bf16(kp[j], st.q[j], a);
-    float s = quad_sum(a) * scale;
-    s = valid ? s : -INFINITY;
+    for (int i = 0; i < NP; ++i) sc[i] = valid[i] ? sc[i] : -INFINITY;
     uint32_t phi[8], plo[8];
-    mha_softmax<D>(st, s, phi, plo);
+    mha_softmax<D>(st, sc, phi, plo);
     uint32_t vp[NS * 8];
 #pragma unroll
     for (int g = 0; g < NS; ++g) {
@@ -209,15 +240,15 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void attn_mha_kernel(
     return;
   }
   const int p0 = s * C, p1 = min(p0 + C, nfull);
-  constexpr int VK = KRaw<D>::VK;
   const size_t slot = ((size_t)r * H + h) * S + s;
   float* acc = ws_acc + slot * D;
 
   MhaState<D> st;
   {
-    const uint32_t* qrow = reinterpret_cast<const uint32_t*>(q + ((size_t)r * H + h) * D + (lane & 3) * VK);
-#pragma unroll
-    for (int j = 0; j < VK / 2; ++j) st.q[j] = qrow[j];
+    const uint4* qrow = reinterpret_cast<const uint4*>(q + ((size_t)r * H + h) * D + (16 * lane) % D);
+    const uint4 a = qrow[0], b = qrow[1];
+    st.q[0] = a.x; st.q[1] = a.y; st.q[2] = a.z; st.q[3] = a.w;
+    st.q[4] = b.x; st.q[5] = b.y; st.q[6] = b.z; st.q[7] = b.w;
   }
   const int32_t* pt_row = page_table + (size_t)r * max_pages;
   const int T = P / kTile;
@@ -271,7 +302,7 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void attn_mha_kernel(
       mha_tail<D>(st, k_tail + toff, v_tail + toff, rows, scale, lane);
     }
   } else {
-    // resume: the stored l is the whole denominator, held here by lane 0 (a quad leader)
+    // resume: the stored l is the whole denominator, held here by lane 0 (a token-group leader)
     st.m = ws_ml[slot * 2 + 0];
     st.l = lane == 0 ? ws_ml[slot * 2 + 1] : 0.f;
 #pragma unroll
@@ -312,12 +343,12 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void attn_mha_kernel(
       }
     }
   }
-  // partials: l summed over one lane per quad (each quad holds one token's terms)
-  float lsum = (lane & 3) == 0 ? st.l : 0.f;
-  lsum += __shfl_xor(lsum, 4);
-  lsum += __shfl_xor(lsum, 8);
-  lsum += __shfl_xor(lsum, 16);
-  lsum += __shfl_xor(lsum, 32);
+  // partials: l summed over one lane per token group (the D/16 lanes of a token hold the
+  // same terms)
+  constexpr int LPT = D / 16;
+  float lsum = (lane % LPT) == 0 ? st.l : 0.f;
+#pragma unroll
+  for (int o = LPT; o < 64; o <<= 1) lsum += __shfl_xor(lsum, o);
 #pragma unroll
   for (int g = 0; g < D / 64; ++g) acc[lane + 64 * g] = st.acc[g];
   if (lane == 0) {

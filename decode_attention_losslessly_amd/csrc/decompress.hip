@@ -31,15 +31,14 @@ __global__ __launch_bounds__(64) void decompress_kernel(const uint8_t* __restric
     KRaw<D> kr;
     load_k<D, GQA>(unit, P, t, lane, kr);
     uint32_t kp[KRaw<D>::VK / 2];
-    decode_k<D>(kr, k_base_from_meta<D, GQA>(meta, lane), kp);
+    decode_k<D>(kr, kp);
     if (hdr.kc) patch_k_tile<D, GQA>(kp, kr, meta, hdr, P, t, krank, lds, pool, lane);
-    {
-      constexpr int VK = KRaw<D>::VK;
-      const int c = k_chunk<D, GQA>(lane);
-      const int tok = c / (D / VK), dim0 = (c % (D / VK)) * VK;
-      uint32_t* dst = reinterpret_cast<uint32_t*>(kd + (size_t)(t * kTile + tok) * D + dim0);
 #pragma unroll
-      for (int j = 0; j < VK / 2; ++j) dst[j] = kp[j];
+    for (int i = 0; i < KRaw<D>::NP; ++i) {
+      const int pc = k_piece<D, GQA>(lane, i);
+      uint32_t* dst = reinterpret_cast<uint32_t*>(kd + (size_t)(t * kTile + piece_token<D>(pc)) * D + piece_dim<D>(pc));
+#pragma unroll
+      for (int j = 0; j < 8; ++j) dst[j] = kp[8 * i + j];
     }
     // V
     VRaw<D> vr;

@@ -77,7 +77,8 @@ __device__ __forceinline__ uint32_t writelane(uint32_t v, uint32_t val, int lane
 constexpr int kQuadXor1 = 0xB1;    // quad_perm [1,0,3,2]
 constexpr int kQuadXor2 = 0x4E;    // quad_perm [2,3,0,1]
 constexpr int kRowShr1 = 0x111, kRowShr2 = 0x112, kRowShr3 = 0x113, kRowShr4 = 0x114, kRowShr8 = 0x118;
-constexpr int kRowShl4 = 0x104;
+constexpr int kRowShl4 = 0x104, kRowShl8 = 0x108;
+constexpr int kRowHalfMirror = 0x141;   // lane j of each 8-lane half-row <- lane 7 - j
 constexpr int kRowRor4 = 0x124, kRowRor8 = 0x128;
 constexpr int kRowBcast15 = 0x142, kRowBcast31 = 0x143;
 
@@ -95,6 +96,14 @@ __device__ __forceinline__ uint32_t dpp_u(uint32_t v) {
 __device__ __forceinline__ float quad_sum(float v) {
   v += dpp_f<kQuadXor1>(v);
   v += dpp_f<kQuadXor2>(v);
+  return v;
+}
+
+// sum over the 8 lanes of a half-row (lanes 8k .. 8k+7), result in every one of them: the quad
+// sums, then each lane adds the other quad's sum through the half-row mirror
+__device__ __forceinline__ float octet_sum(float v) {
+  v = quad_sum(v);
+  v += dpp_f<kRowHalfMirror>(v);
   return v;
 }
 

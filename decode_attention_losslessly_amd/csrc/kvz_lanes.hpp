@@ -1,10 +1,14 @@
 // Lane layouts of the attention kernels: which storage positions each lane of a wave loads
-// and rebuilds, for one 16-token tile of one unit.
+// and rebuilds, for one 16-token tile of one unit. A K tile is cut into pieces of 16 storage
+// positions (16 dims of one token); lane l holds the pieces k_piece(l, i), i < D/64:
 //
-//   K, multi-head layout      lane l -> token l/4, dims (l%4)*D/4 .. +D/4: storage positions
-//                             [l*D/4, (l+1)*D/4) of the tile, in lane order.
-//   K, grouped-query layout   (D = 128) lane l -> token l%16, dims 32*(l/16) .. +32: the MFMA
-//                             operand layout; storage chunk 4*(l%16) + l/16.
+//   K, multi-head layout      pieces l + 64*i: with D = 128, token l/8 and token 8 + l/8, dims
+//                             16*(l%8) .. +16 of both; with D = 64, token l/4, dims 16*(l%4)..
+//                             Every load instruction of the wave reads 64 consecutive pieces,
+//                             i.e. whole cache lines.
+//   K, grouped-query layout   (D = 128) the MFMA operand layout: lane l -> token l%16, dims
+//                             32*(l/16) .. +32, i.e. pieces 2c and 2c + 1 of chunk
+//                             c = 4*(l%16) + l/16.
 //   V                         lane l -> dims l + 64*s (s < D/64), all 16 tokens: storage
 //                             positions [16*d, 16*d + 16), segment s in lane order.
 //
@@ -38,37 +42,48 @@ __device__ __forceinline__ uint32_t stream1(const uint8_t* p) { return __builtin
 // ---------------------------------------------------------------- K
 template <int D>
 struct KRaw {
-  static constexpr int VK = (D == 128) ? 32 : 16;   // values per lane
-  static constexpr int NW = VK / 8;                 // offset words per lane
+  static constexpr int VK = 2 * (D / kGroup) * 8;   // values per lane: D / 4
+  static constexpr int NP = VK / 16;                 // pieces per lane
+  static constexpr int NW = VK / 8;                  // offset words per lane
   uint32_t sm[VK / 4];
   uint32_t nib[NW];
+  uint32_t base[NP];   // base of each piece's group (the grouped-query pieces share one)
 };
 
-// chunk index (storage order, units of VK values) of this lane
+// storage piece (16 positions) held as piece i by this lane
 template <int D, bool GQA>
-__device__ __forceinline__ int k_chunk(int lane) {
-  if constexpr (GQA) return 4 * (lane & 15) + (lane >> 4);
-  else return lane;
+__device__ __forceinline__ int k_piece(int lane, int i) {
+  if constexpr (GQA) return 2 * (4 * (lane & 15) + (lane >> 4)) + i;
+  else return lane + 64 * i;
 }
+
+// token and first dim of a storage piece
+template <int D>
+__device__ __forceinline__ int piece_token(int piece) { return (16 * piece) / D; }
+template <int D>
+__device__ __forceinline__ int piece_dim(int piece) { return (16 * piece) % D; }
 
 template <int D, bool GQA>
 __device__ __forceinline__ void load_k(const uint8_t* unit, int P, int tile, int lane, KRaw<D>& r) {
-  constexpr int VK = KRaw<D>::VK;
-  const int c = k_chunk<D, GQA>(lane);
-  const int tok = c / (D / VK), dim0 = (c % (D / VK)) * VK;
+  constexpr int NP = KRaw<D>::NP;
   const uint8_t* tb = unit + kblock_offset(P, D) + tile * tile_bytes(D);
-  const uint8_t* s = tb + c * VK;
-  if constexpr (VK == 32) {
-    const uint4 a = stream16(s), b = stream16(s + 16);
-    r.sm[0] = a.x; r.sm[1] = a.y; r.sm[2] = a.z; r.sm[3] = a.w;
-    r.sm[4] = b.x; r.sm[5] = b.y; r.sm[6] = b.z; r.sm[7] = b.w;
-    const uint4 n = stream16(tb + 16 * D + c * (VK / 2));
+  const uint8_t* bases = unit + kbase_offset(D, tile);
+#pragma unroll
+  for (int i = 0; i < NP; ++i) {
+    const int pc = k_piece<D, GQA>(lane, i);
+    const uint4 a = stream16(tb + 16 * pc);
+    r.sm[4 * i] = a.x; r.sm[4 * i + 1] = a.y; r.sm[4 * i + 2] = a.z; r.sm[4 * i + 3] = a.w;
+    if constexpr (!GQA) {
+      const uint2 n = stream8(tb + 16 * D + 8 * pc);
+      r.nib[2 * i] = n.x; r.nib[2 * i + 1] = n.y;
+      r.base[i] = stream1(bases + (piece_dim<D>(pc) / kGroup) * kTile + piece_token<D>(pc));
+    }
+  }
+  if constexpr (GQA) {   // the two pieces are adjacent: one 16-byte offset load, one base
+    const int pc = k_piece<D, GQA>(lane, 0);
+    const uint4 n = stream16(tb + 16 * D + 8 * pc);
     r.nib[0] = n.x; r.nib[1] = n.y; r.nib[2] = n.z; r.nib[3] = n.w;
-  } else {
-    const uint4 a = stream16(s);
-    r.sm[0] = a.x; r.sm[1] = a.y; r.sm[2] = a.z; r.sm[3] = a.w;
-    const uint2 n = stream8(tb + 16 * D + c * (VK / 2));
-    r.nib[0] = n.x; r.nib[1] = n.y;
+    r.base[0] = r.base[1] = stream1(bases + (piece_dim<D>(pc) / kGroup) * kTile + piece_token<D>(pc));
   }
 }
 
@@ -90,32 +105,14 @@ __device__ __forceinline__ uint32_t load_meta(const uint8_t* unit, int P, int D,
 template <int D>
 __device__ __forceinline__ int hdr_lane() { return 8 * (D / kGroup); }
 
-// base of the group this lane's K chunk lies in
-template <int D, bool GQA>
-__device__ __forceinline__ uint32_t k_base_from_meta(uint32_t meta, int lane) {
-  constexpr int VK = KRaw<D>::VK;
-  const int c = k_chunk<D, GQA>(lane);
-  const int tok = c / (D / VK), g = ((c % (D / VK)) * VK) / kGroup;
-  const int byte = g * kTile + tok;
-  const uint32_t w = (uint32_t)__builtin_amdgcn_ds_bpermute(4 * (byte >> 2), (int)meta);
-  return (w >> (8 * (byte & 3))) & 0xFFu;
-}
-
-// this lane's K base, read from the unit's meta region with the tile's other loads
-template <int D, bool GQA>
-__device__ __forceinline__ uint32_t load_k_base(const uint8_t* unit, int tile, int lane) {
-  constexpr int VK = KRaw<D>::VK;
-  const int c = k_chunk<D, GQA>(lane);
-  const int tok = c / (D / VK), g = ((c % (D / VK)) * VK) / kGroup;
-  return stream1(unit + kbase_offset(D, tile) + g * kTile + tok);
-}
-
 template <int D>
-__device__ __forceinline__ void decode_k(const KRaw<D>& r, uint32_t base, uint32_t (&pairs)[KRaw<D>::VK / 2]) {
-  const uint32_t bb = base * 0x00800080u;
+__device__ __forceinline__ void decode_k(const KRaw<D>& r, uint32_t (&pairs)[KRaw<D>::VK / 2]) {
 #pragma unroll
-  for (int w = 0; w < KRaw<D>::NW; ++w)
-    decode8(r.sm[2 * w], r.sm[2 * w + 1], r.nib[w], bb, bb, bb, bb, &pairs[4 * w]);
+  for (int i = 0; i < KRaw<D>::NP; ++i) {
+    const uint32_t bb = r.base[i] * 0x00800080u;
+    decode8(r.sm[4 * i], r.sm[4 * i + 1], r.nib[2 * i], bb, bb, bb, bb, &pairs[8 * i]);
+    decode8(r.sm[4 * i + 2], r.sm[4 * i + 3], r.nib[2 * i + 1], bb, bb, bb, bb, &pairs[8 * i + 4]);
+  }
 }
 
 // ---------------------------------------------------------------- V
@@ -195,14 +192,21 @@ __device__ __forceinline__ UnitHeader header_from_meta(uint32_t meta) {
 //           then 64 lanes x (D/4 or D/8) u32 of pairs) and each lane patches its own copy.
 // `cursor` is the block-level index of the tile's first escape and is advanced past the tile.
 
-// K, multi-head layout: storage position p of a tile -> lane p / VK, value p % VK.
-// K, grouped-query layout: chunk p / 32 sits in lane 16*(chunk%4) + chunk/4.
+// Storage position p of a K tile -> (lane, register, half) through its piece (see k_piece).
 template <int D, bool GQA>
 __device__ __forceinline__ void k_position(uint32_t p, int& lane, int& reg, int& half) {
-  constexpr uint32_t VK = KRaw<D>::VK;
-  const uint32_t c = p / VK, j = p % VK;
-  lane = (int)(GQA ? (16 * (c & 3) + (c >> 2)) : c);
-  reg = (int)(j >> 1);
+  const uint32_t pc = p / 16, j = p % 16;
+  uint32_t l, i;
+  if constexpr (GQA) {
+    const uint32_t c = pc / 2;
+    l = 16 * (c & 3) + (c >> 2);
+    i = pc & 1;
+  } else {
+    l = pc % 64;
+    i = pc / 64;
+  }
+  lane = (int)l;
+  reg = (int)(8 * i + j / 2);
   half = (int)(j & 1);
 }
 
@@ -226,17 +230,29 @@ template <int D, bool GQA>
 __device__ __forceinline__ void pool_patch_k(uint32_t (&pairs)[KRaw<D>::VK / 2], const KRaw<D>& raw,
                                              const UnitHeader& h, uint32_t& cursor, uint16_t* lds,
                                              const uint16_t* pool, int lane) {
-  constexpr int N = KRaw<D>::VK / 2, NW = KRaw<D>::NW;
-  uint32_t c = 0;
+  constexpr int N = KRaw<D>::VK / 2, NP = KRaw<D>::NP;
+  // rank (in storage order) of each piece's first escape
+  uint32_t cnt[NP], rank[NP], total = 0;
 #pragma unroll
-  for (int w = 0; w < NW; ++w) c += popc_flags(escape_flags(raw.nib[w]));
-  // ranks in storage order (chunk order; the grouped-query layout permutes lanes)
-  const int src = GQA ? (16 * (lane & 3) + (lane >> 2)) : lane;
-  const uint32_t c_ord = GQA ? (uint32_t)__shfl((int)c, src) : c;
-  const uint32_t inc = wave_incl_scan(c_ord);
-  const uint32_t total = readlane(inc, 63);
-  const uint32_t exc_ord = inc - c_ord;
-  uint32_t rank = GQA ? (uint32_t)__shfl((int)exc_ord, k_chunk<D, GQA>(lane)) : exc_ord;
+  for (int i = 0; i < NP; ++i) cnt[i] = popc_flags(escape_flags(raw.nib[2 * i])) + popc_flags(escape_flags(raw.nib[2 * i + 1]));
+  if constexpr (GQA) {
+    // pieces 2c, 2c + 1 are adjacent: scan whole chunks in chunk order (lane 16*(c%4) + c/4)
+    const uint32_t cl = cnt[0] + cnt[1];
+    const uint32_t c_ord = (uint32_t)__shfl((int)cl, 16 * (lane & 3) + (lane >> 2));
+    const uint32_t inc = wave_incl_scan(c_ord);
+    total = readlane(inc, 63);
+    const uint32_t first = (uint32_t)__shfl((int)(inc - c_ord), 4 * (lane & 15) + (lane >> 4));
+    rank[0] = first;
+    rank[1] = first + cnt[0];
+  } else {
+    // piece i of every lane precedes piece i + 1 of any lane
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      const uint32_t inc = wave_incl_scan(cnt[i]);
+      rank[i] = total + inc - cnt[i];
+      total += readlane(inc, 63);
+    }
+  }
   if (total == 0) return;
   const uint32_t cur = uniform(cursor);
   const uint32_t avail = h.kc > cur ? min(total, h.kc - cur) : 0u;
@@ -246,13 +262,16 @@ __device__ __forceinline__ void pool_patch_k(uint32_t (&pairs)[KRaw<D>::VK / 2],
 #pragma unroll
   for (int i = 0; i < N; i += 4) *reinterpret_cast<uint4*>(mine + i) = make_uint4(pairs[i], pairs[i + 1], pairs[i + 2], pairs[i + 3]);
   wave_lds_sync();
-  for (int w = 0; w < NW; ++w) {
-    uint32_t f = flags_in_order(escape_flags(raw.nib[w]));
-    while (f) {                                    // positions of the word in list order
-      const int pos = ordered_bit_to_pos(__builtin_ctz(f));
-      f &= f - 1;
-      if (rank < avail) lds_pair_half(mine, 8 * w + pos, lds[rank]);
-      ++rank;
+  for (int i = 0; i < NP; ++i) {
+    uint32_t rk = rank[i];
+    for (int w = 0; w < 2; ++w) {
+      uint32_t f = flags_in_order(escape_flags(raw.nib[2 * i + w]));
+      while (f) {                                  // positions of the word in list order
+        const int pos = ordered_bit_to_pos(__builtin_ctz(f));
+        f &= f - 1;
+        if (rk < avail) lds_pair_half(mine, 16 * i + 8 * w + pos, lds[rk]);
+        ++rk;
+      }
     }
   }
   wave_lds_sync();
