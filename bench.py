@@ -139,9 +139,8 @@ def main() -> int:
     S = kvz.num_splits(B, Hq, H, D, P, w.max_pages)
     units_bytes = int(full.sum()) * H * U
     tail_bytes = int((w.seq_lens % P).sum()) * H * D * 2 * 2
-    # page-table entries, q, the (m, l, acc) partials and the hand-off flag of every work item
-    # (written by the fast kernel, read by the pool pass)
-    small_bytes = int(full.sum()) * H * 4 + B * Hq * D * 2 + B * Hq * S * ((D + 2) * 4 + 8)
+    # page-table entries, q and the (m, l, acc) partials
+    small_bytes = int(full.sum()) * H * 4 + B * Hq * D * 2 + B * Hq * S * (D + 2) * 4
     comp_bytes = units_bytes + 2 * pool_esc + tail_bytes + small_bytes
     dense_kv_bytes = int(L.sum()) * H * D * 2 * 2
     dense_bytes = dense_kv_bytes + int(((L + P - 1) // P).sum()) * H * 4 + B * Hq * D * 2 + B * Hq * S * (D + 2) * 4
@@ -212,10 +211,7 @@ def main() -> int:
         t = json.load(open(tfile))
         if t.get("source_digest") == source_digest():
             traffic = t.get("bytes_per_launch")
-    # the split step is two launches: the fast kernel and the pool pass (which, for work items
-    # without pool units, only reads their flag); both are inside the timed events
-    kname = "attn_mha_kernel<128, false> + attn_mha_kernel<128, true>" if Hq == H else \
-        "attn_gqa_kernel<false> + attn_gqa_kernel<true>"
+    kname = f"attn_mha_kernel<{D}>" if Hq == H else "attn_gqa_kernel"
     roofline = dict(kernel=kname, bound="hbm",
                     achieved=round(achieved, 1), peak=PEAK_HBM_GBPS, unit="GB/s",
                     frac=round(achieved / PEAK_HBM_GBPS, 4), traffic=traffic,

@@ -18,16 +18,6 @@ constexpr float kLog2e = 1.4426950408889634f;
 // (m = -inf, l = 0) partial and the merge can produce zeros
 __device__ __forceinline__ int active_splits(int nfull, int C) { return nfull > 0 ? (nfull + C - 1) / C : 1; }
 
-// Hand-off flag of a work item from the fast kernel to the pool pass: 0 = nothing skipped;
-// otherwise the first and last skipped pages of the split (relative to its first page, plus
-// one) in the low and high half-words, or all ones when they do not fit (scan the split).
-constexpr uint32_t kScanAll = 0xFFFFFFFFu;
-__device__ __forceinline__ uint32_t skip_flag(int first, int last) {
-  if (first < 0) return 0u;
-  if (last + 1 > 0xFFFF) return kScanAll;
-  return (uint32_t)(first + 1) | ((uint32_t)(last + 1) << 16);
-}
-
 struct Partials {
   float* acc;   // [rows][S][D]
   float* ml;    // [rows][S][2]

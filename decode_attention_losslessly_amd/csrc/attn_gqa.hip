@@ -253,68 +253,40 @@ __device__ __forceinline__ void gqa_store(const GqaState& st, int r, int Hq, int
   }
 }
 
-// Loads a partial stored by gqa_store back into the state: rows 0..7 of the output take the
-// stored rows (rows 8..15, which gqa_store adds to them, start from zero) and the denominator
-// goes to the lanes of the first lane group.
-__device__ __forceinline__ void gqa_resume(GqaState& st, int r, int Hq, int hq0, int nq, int S, int s,
-                                           const float* ws_acc, const float* ws_ml, int lane) {
-  const int row = (lane & 15) % kGqaRows;
-  if (row < nq) {
-    const float* ml = ws_ml + (((size_t)r * Hq + hq0 + row) * S + s) * 2;
-    st.m = ml[0];
-    st.l = lane < 16 ? ml[1] : 0.f;
-  } else {
-    st.m = -INFINITY;
-    st.l = 0.f;
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int n = 4 * (lane >> 4) + i;
-    const bool have = lane < 32 && n < nq;
-    const float* acc = ws_acc + (((size_t)r * Hq + hq0 + (have ? n : 0)) * S + s) * 128;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) st.o[j][i] = have ? acc[16 * j + (lane & 15)] : 0.f;
-  }
-}
+// Both grouped-query kernels ask for 3 waves per SIMD: the compiler then keeps the MFMA
+// accumulators in architectural VGPRs and fits in 168 registers without spilling (left alone
+// it moves them to AGPRs and lands at 2 waves per SIMD).
+#define KVZ_GQA_OCCUPANCY __attribute__((amdgpu_waves_per_eu(3)))
 
-// Fast (POOL = false) and general (POOL = true) instances, as for the multi-head kernel: the
-// fast one skips units whose escapes are in the pool and records the first and last of them;
-// the general one resumes the marked items from their stored partials and adds only those
-// units.
-template <bool POOL>
-__global__ __launch_bounds__(64 * kGqaWaves) void attn_gqa_kernel(
+// One wave per (request, KV head, chunk of query heads, split). As in the multi-head kernel,
+// the main loop skips units whose escapes are in the pool, and the wave adds them after the
+// loop, when the pipeline's registers are free.
+__global__ __launch_bounds__(64 * kGqaWaves) KVZ_GQA_OCCUPANCY void attn_gqa_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ units, const uint16_t* __restrict__ pool,
     const uint16_t* __restrict__ k_tail, const uint16_t* __restrict__ v_tail, const int32_t* __restrict__ page_table,
     int max_pages, const int32_t* __restrict__ seq_lens, int B, int Hq, int H, int P, int num_pages, int S, int C,
-    float scale, float* __restrict__ ws_acc, float* __restrict__ ws_ml, uint32_t* __restrict__ deferred,
-    uint32_t* __restrict__ status) {
-  __shared__ uint16_t esc_all[kGqaWaves][POOL ? esc_lds_elems<128>() : 1];
+    float scale, float* __restrict__ ws_acc, float* __restrict__ ws_ml, uint32_t* __restrict__ status) {
+  __shared__ uint16_t esc_all[kGqaWaves][esc_lds_elems<128>()];
   __shared__ uint32_t vlds_all[kGqaWaves][128 * 8];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int grp = Hq / H, nchunks = (grp + kGqaRows - 1) / kGqaRows;
   const int item = (int)uniform(blockIdx.x * kGqaWaves + wave);
   if (item >= B * H * nchunks * S) return;
-  if constexpr (POOL) {
-    if (sload<uint32_t>(deferred + item) == 0) return;
-  }
   const int s = item % S, qc = (item / S) % nchunks, h = (item / (S * nchunks)) % H, r = item / (S * nchunks * H);
   const int hq0 = h * grp + qc * kGqaRows, nq = min(kGqaRows, grp - qc * kGqaRows);
   int L = sload<int32_t>(seq_lens + r);
   if (L > max_pages * P || L < 0) {
-    if (!POOL && lane == 0 && s == 0 && h == 0 && qc == 0) atomicOr(status, kStatusSeqTooLong);
+    if (lane == 0 && s == 0 && h == 0 && qc == 0) atomicOr(status, kStatusSeqTooLong);
     L = L < 0 ? 0 : max_pages * P;
   }
   int nfull = L / P;
   const int rows = L % P;
   if (num_pages <= 0 && nfull > 0) {   // no unit slots: every full page is a bad id
-    if (!POOL && lane == 0 && s == 0 && h == 0 && qc == 0) atomicOr(status, kStatusBadPage);
+    if (lane == 0 && s == 0 && h == 0 && qc == 0) atomicOr(status, kStatusBadPage);
     nfull = 0;
   }
   const int Sr = active_splits(nfull, C);
-  if (s >= Sr) {
-    if (!POOL && lane == 0) deferred[item] = 0;
-    return;
-  }
+  if (s >= Sr) return;
   const int p0 = s * C, p1 = min(p0 + C, nfull);
   GqaState st;
   gqa_init(st, q, r, Hq, hq0, nq, lane);
@@ -323,52 +295,45 @@ __global__ __launch_bounds__(64 * kGqaWaves) void attn_gqa_kernel(
   uint32_t krank = 0, vrank = 0;
   uint16_t* esc_lds = esc_all[wave];
   uint32_t* vlds = vlds_all[wave];
-  if constexpr (!POOL) {
-    const int nsteps = (p1 > p0 ? p1 - p0 : 0) * T;
-    int first_skip = -1, last_skip = -1;
-    bool bad = false;
-    auto note = [&](const GqaCStage& stg) {
-      if (first_skip < 0) first_skip = stg.page - p0;
-      last_skip = stg.page - p0;
+  const int nsteps = (p1 > p0 ? p1 - p0 : 0) * T;
+  int first_skip = -1, last_skip = -1;
+  bool bad = false;
+  auto note = [&](const GqaCStage& stg) {
+    if (first_skip < 0) first_skip = stg.page;
+    last_skip = stg.page;
+  };
+  if (nsteps > 0) {
+    // load cursor as in the multi-head kernel: stays on the last step once there
+    int ln = 0, lp = p0, lt = 0;
+    const int last = nsteps - 1;
+    auto advance = [&]() {
+      if (ln < last) {
+        ++ln;
+        if (++lt == T) { lt = 0; ++lp; }
+      }
     };
-    if (nsteps > 0) {
-      // load cursor as in the multi-head kernel: stays on the last step once there
-      int ln = 0, lp = p0, lt = 0;
-      const int last = nsteps - 1;
-      auto advance = [&]() {
-        if (ln < last) {
-          ++ln;
-          if (++lt == T) { lt = 0; ++lp; }
-        }
-      };
-      GqaCStage a, b;
-      int pid = sload<int32_t>(pt_row + lp);
+    GqaCStage a, b;
+    int pid = sload<int32_t>(pt_row + lp);
+    gqa_c_issue(a, units, pid, lp, lt, H, h, P, num_pages, lane);
+    advance();
+    pid = sload<int32_t>(pt_row + lp);
+    for (int i = 0; i < nsteps; i += 2) {
+      gqa_c_issue(b, units, pid, lp, lt, H, h, P, num_pages, lane);
+      advance();
+      pid = sload<int32_t>(pt_row + lp);
+      bad |= !a.ok;
+      if (!gqa_c_compute<false>(st, a, P, krank, vrank, esc_lds, vlds, pool, scale, lane)) note(a);
+      if (i + 1 >= nsteps) break;
       gqa_c_issue(a, units, pid, lp, lt, H, h, P, num_pages, lane);
       advance();
       pid = sload<int32_t>(pt_row + lp);
-      for (int i = 0; i < nsteps; i += 2) {
-        gqa_c_issue(b, units, pid, lp, lt, H, h, P, num_pages, lane);
-        advance();
-        pid = sload<int32_t>(pt_row + lp);
-        bad |= !a.ok;
-        if (!gqa_c_compute<false>(st, a, P, krank, vrank, esc_lds, vlds, pool, scale, lane)) note(a);
-        if (i + 1 >= nsteps) break;
-        gqa_c_issue(a, units, pid, lp, lt, H, h, P, num_pages, lane);
-        advance();
-        pid = sload<int32_t>(pt_row + lp);
-        bad |= !b.ok;
-        if (!gqa_c_compute<false>(st, b, P, krank, vrank, esc_lds, vlds, pool, scale, lane)) note(b);
-      }
+      bad |= !b.ok;
+      if (!gqa_c_compute<false>(st, b, P, krank, vrank, esc_lds, vlds, pool, scale, lane)) note(b);
     }
-    if (bad && lane == 0) atomicOr(status, kStatusBadPage);
-    if (lane == 0) deferred[item] = skip_flag(first_skip, last_skip);
-    if (s == Sr - 1 && rows > 0) {
-      const size_t toff = ((size_t)r * H + h) * P * 128;
-      for (int t0 = 0; t0 < rows; t0 += kTile)
-        gqa_raw_tile(st, k_tail + toff, v_tail + toff, t0, min(kTile, rows - t0), scale, vlds, lane);
-    }
-  } else {
-    gqa_resume(st, r, Hq, hq0, nq, S, s, ws_acc, ws_ml, lane);
+  }
+  if (bad && lane == 0) atomicOr(status, kStatusBadPage);
+  if (first_skip >= 0) {
+    // units whose escapes are in the pool: the recorded pages, then any between them
     auto do_page = [&](int page) {
       const int pid = sload<int32_t>(pt_row + page);
       for (int t = 0; t < T; ++t) {
@@ -377,21 +342,13 @@ __global__ __launch_bounds__(64 * kGqaWaves) void attn_gqa_kernel(
         gqa_c_compute<true>(st, a, P, krank, vrank, esc_lds, vlds, pool, scale, lane);
       }
     };
-    // the recorded pages, then any pool unit strictly between them
-    const uint32_t flag = sload<uint32_t>(deferred + item);
-    int lo = p0, hi = p1;
-    if (flag != kScanAll) {
-      const int f = p0 + (int)(flag & 0xFFFFu) - 1, l = p0 + (int)(flag >> 16) - 1;
-      do_page(f);
-      if (l != f) do_page(l);
-      lo = f + 1;
-      hi = l;
-    }
+    do_page(first_skip);
+    if (last_skip != first_skip) do_page(last_skip);
     const uint32_t hdr_off = hdr_offset(P, 128) + 8;
-    for (int c0 = lo; c0 < hi; c0 += 64) {
+    for (int c0 = first_skip + 1; c0 < last_skip; c0 += 64) {
       const int pg = c0 + lane;
       bool in_pool = false;
-      if (pg < hi) {
+      if (pg < last_skip) {
         const int pid = pt_row[pg];
         if (pid >= 0 && pid < num_pages)
           in_pool = *reinterpret_cast<const uint64_t*>(units + ((size_t)pid * H + h) * unit_bytes(P, 128) + hdr_off) !=
@@ -405,10 +362,15 @@ __global__ __launch_bounds__(64 * kGqaWaves) void attn_gqa_kernel(
       }
     }
   }
+  if (s == Sr - 1 && rows > 0) {
+    const size_t toff = ((size_t)r * H + h) * P * 128;
+    for (int t0 = 0; t0 < rows; t0 += kTile)
+      gqa_raw_tile(st, k_tail + toff, v_tail + toff, t0, min(kTile, rows - t0), scale, vlds, lane);
+  }
   gqa_store(st, r, Hq, hq0, nq, S, s, ws_acc, ws_ml, lane);
 }
 
-__global__ __launch_bounds__(64 * kGqaWaves) void attn_dense_gqa_kernel(
+__global__ __launch_bounds__(64 * kGqaWaves) KVZ_GQA_OCCUPANCY void attn_dense_gqa_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_pages, const uint16_t* __restrict__ v_pages,
     const int32_t* __restrict__ page_table, int max_pages, const int32_t* __restrict__ seq_lens, int B, int Hq, int H,
     int P, int num_pages, int S, int C, float scale, float* __restrict__ ws_acc, float* __restrict__ ws_ml,
@@ -490,14 +452,11 @@ static unsigned gqa_blocks(int B, int Hq, int H, int S) {
 int launch_attn_gqa(const uint16_t* q, const uint8_t* units, const uint16_t* pool, const uint16_t* k_tail,
                     const uint16_t* v_tail, const int32_t* page_table, int max_pages, const int32_t* seq_lens,
                     int B, int Hq, int H, int D, int P, int num_pages, int S, int C, float scale, float* ws_acc,
-                    float* ws_ml, uint32_t* deferred, uint32_t* status, hipStream_t stream) {
+                    float* ws_ml, uint32_t* status, hipStream_t stream) {
   if (D != 128) return -2;
-  hipLaunchKernelGGL(attn_gqa_kernel<false>, dim3(gqa_blocks(B, Hq, H, S)), dim3(64 * kGqaWaves), 0, stream, q, units,
-                     pool, k_tail, v_tail, page_table, max_pages, seq_lens, B, Hq, H, P, num_pages, S, C, scale, ws_acc,
-                     ws_ml, deferred, status);
-  hipLaunchKernelGGL(attn_gqa_kernel<true>, dim3(gqa_blocks(B, Hq, H, S)), dim3(64 * kGqaWaves), 0, stream, q, units,
-                     pool, k_tail, v_tail, page_table, max_pages, seq_lens, B, Hq, H, P, num_pages, S, C, scale, ws_acc,
-                     ws_ml, deferred, status);
+  hipLaunchKernelGGL(attn_gqa_kernel, dim3(gqa_blocks(B, Hq, H, S)), dim3(64 * kGqaWaves), 0, stream, q, units, pool,
+                     k_tail, v_tail, page_table, max_pages, seq_lens, B, Hq, H, P, num_pages, S, C, scale, ws_acc,
+                     ws_ml, status);
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 

@@ -200,48 +200,39 @@ __device__ __forceinline__ void mha_tail(MhaState<D>& st, const uint16_t* tk, co
   }
 }
 
-// Two instances. POOL = false is the fast kernel: it handles units whose escapes are inline
-// and skips a unit whose escapes are in the pool, recording the first and last skipped page of
-// the item in `deferred` (written for every item). POOL = true then runs only the marked
-// items: it resumes from the partial the fast instance stored and adds those two pages and any
-// other pool unit between them, found by reading the unit headers 64 at a time. Keeping the pool path out of the fast instance keeps its
-// register count, and so its occupancy, at what the inline path needs, while the rare pool
-// units cost only their own work.
-template <int D, bool POOL>
+// One wave per (request, head, split). The main loop handles units whose escapes are inline
+// and skips a unit whose escapes are in the pool, remembering the first and last such page;
+// after the loop (when the pipeline's registers are free again) the wave adds those two pages
+// and any other pool unit between them, found by reading the unit headers 64 at a time. The
+// pool path thus costs registers only outside the loop, and the rare pool unit costs only its
+// own work.
+template <int D>
 __global__ __launch_bounds__(64 * kWavesPerBlock) void attn_mha_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ units, const uint16_t* __restrict__ pool,
     const uint16_t* __restrict__ k_tail, const uint16_t* __restrict__ v_tail, const int32_t* __restrict__ page_table,
     int max_pages, const int32_t* __restrict__ seq_lens, int B, int H, int P, int num_pages, int S, int C,
-    float scale, float* __restrict__ ws_acc, float* __restrict__ ws_ml, uint32_t* __restrict__ deferred,
-    uint32_t* __restrict__ status) {
-  __shared__ uint16_t lds_all[kWavesPerBlock][POOL ? esc_lds_elems<D>() : 1];
+    float scale, float* __restrict__ ws_acc, float* __restrict__ ws_ml, uint32_t* __restrict__ status) {
+  __shared__ uint16_t lds_all[kWavesPerBlock][esc_lds_elems<D>()];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int item = (int)uniform(blockIdx.x * kWavesPerBlock + wave);
   if (item >= B * H * S) return;
-  if constexpr (POOL) {
-    if (sload<uint32_t>(deferred + item) == 0) return;
-  }
   const int s = item % S, h = (item / S) % H, r = item / (S * H);
   uint16_t* lds = lds_all[wave];
   int L = sload<int32_t>(seq_lens + r);
   if (L > max_pages * P || L < 0) {
-    if (!POOL && lane == 0 && s == 0 && h == 0) atomicOr(status, kStatusSeqTooLong);
+    if (lane == 0 && s == 0 && h == 0) atomicOr(status, kStatusSeqTooLong);
     L = L < 0 ? 0 : max_pages * P;
   }
   int nfull = L / P;
   const int rows = L % P;
   if (num_pages <= 0 && nfull > 0) {   // no unit slots: every full page is a bad id
-    if (!POOL && lane == 0 && s == 0 && h == 0) atomicOr(status, kStatusBadPage);
+    if (lane == 0 && s == 0 && h == 0) atomicOr(status, kStatusBadPage);
     nfull = 0;
   }
   const int Sr = active_splits(nfull, C);
-  if (s >= Sr) {
-    if (!POOL && lane == 0) deferred[item] = 0;
-    return;
-  }
+  if (s >= Sr) return;
   const int p0 = s * C, p1 = min(p0 + C, nfull);
   const size_t slot = ((size_t)r * H + h) * S + s;
-  float* acc = ws_acc + slot * D;
 
   MhaState<D> st;
   {
@@ -250,63 +241,53 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void attn_mha_kernel(
     st.q[0] = a.x; st.q[1] = a.y; st.q[2] = a.z; st.q[3] = a.w;
     st.q[4] = b.x; st.q[5] = b.y; st.q[6] = b.z; st.q[7] = b.w;
   }
+  st.m = -INFINITY;
+  st.l = 0.f;
+#pragma unroll
+  for (int i = 0; i < D / 64; ++i) st.acc[i] = 0.f;
   const int32_t* pt_row = page_table + (size_t)r * max_pages;
   const int T = P / kTile;
+  const int nsteps = (p1 > p0 ? p1 - p0 : 0) * T;
   uint32_t krank = 0, vrank = 0;
-  if constexpr (!POOL) {
-    st.m = -INFINITY;
-    st.l = 0.f;
-#pragma unroll
-    for (int i = 0; i < D / 64; ++i) st.acc[i] = 0.f;
-    const int nsteps = (p1 > p0 ? p1 - p0 : 0) * T;
-    int first_skip = -1, last_skip = -1;
-    bool bad = false;
-    auto note = [&](const MhaStage<D>& stg) {
-      if (first_skip < 0) first_skip = stg.page - p0;
-      last_skip = stg.page - p0;
+  int first_skip = -1, last_skip = -1;
+  bool bad = false;
+  auto note = [&](const MhaStage<D>& stg) {
+    if (first_skip < 0) first_skip = stg.page;
+    last_skip = stg.page;
+  };
+  if (nsteps > 0) {
+    // load cursor: step ln = (page lp, tile lt); it stays on the last step once there, so the
+    // loads issued past the end re-read that step (from cache) and are never computed
+    int ln = 0, lp = p0, lt = 0;
+    const int last = nsteps - 1;
+    auto advance = [&]() {
+      if (ln < last) {
+        ++ln;
+        if (++lt == T) { lt = 0; ++lp; }
+      }
     };
-    if (nsteps > 0) {
-      // load cursor: step ln = (page lp, tile lt); it stays on the last step once there, so
-      // the loads issued past the end re-read that step (from cache) and are never computed
-      int ln = 0, lp = p0, lt = 0;
-      const int last = nsteps - 1;
-      auto advance = [&]() {
-        if (ln < last) {
-          ++ln;
-          if (++lt == T) { lt = 0; ++lp; }
-        }
-      };
-      MhaStage<D> a, b;
-      int pid = sload<int32_t>(pt_row + lp);
+    MhaStage<D> a, b;
+    int pid = sload<int32_t>(pt_row + lp);
+    mha_issue<D>(a, units, pid, lp, lt, H, h, P, num_pages, lane);
+    advance();
+    pid = sload<int32_t>(pt_row + lp);   // one step ahead of its use
+    for (int i = 0; i < nsteps; i += 2) {
+      mha_issue<D>(b, units, pid, lp, lt, H, h, P, num_pages, lane);
+      advance();
+      pid = sload<int32_t>(pt_row + lp);
+      bad |= !a.ok;
+      if (!mha_compute<D, false>(st, a, P, krank, vrank, lds, pool, scale, lane)) note(a);
+      if (i + 1 >= nsteps) break;
       mha_issue<D>(a, units, pid, lp, lt, H, h, P, num_pages, lane);
       advance();
-      pid = sload<int32_t>(pt_row + lp);   // one step ahead of its use
-      for (int i = 0; i < nsteps; i += 2) {
-        mha_issue<D>(b, units, pid, lp, lt, H, h, P, num_pages, lane);
-        advance();
-        pid = sload<int32_t>(pt_row + lp);
-        bad |= !a.ok;
-        if (!mha_compute<D, false>(st, a, P, krank, vrank, lds, pool, scale, lane)) note(a);
-        if (i + 1 >= nsteps) break;
-        mha_issue<D>(a, units, pid, lp, lt, H, h, P, num_pages, lane);
-        advance();
-        pid = sload<int32_t>(pt_row + lp);
-        bad |= !b.ok;
-        if (!mha_compute<D, false>(st, b, P, krank, vrank, lds, pool, scale, lane)) note(b);
-      }
+      pid = sload<int32_t>(pt_row + lp);
+      bad |= !b.ok;
+      if (!mha_compute<D, false>(st, b, P, krank, vrank, lds, pool, scale, lane)) note(b);
     }
-    if (bad && lane == 0) atomicOr(status, kStatusBadPage);
-    if (lane == 0) deferred[item] = skip_flag(first_skip, last_skip);
-    if (s == Sr - 1 && rows > 0) {
-      const size_t toff = ((size_t)r * H + h) * P * D;
-      mha_tail<D>(st, k_tail + toff, v_tail + toff, rows, scale, lane);
-    }
-  } else {
-    // resume: the stored l is the whole denominator, held here by lane 0 (a token-group leader)
-    st.m = ws_ml[slot * 2 + 0];
-    st.l = lane == 0 ? ws_ml[slot * 2 + 1] : 0.f;
-#pragma unroll
-    for (int g = 0; g < D / 64; ++g) st.acc[g] = acc[lane + 64 * g];
+  }
+  if (bad && lane == 0) atomicOr(status, kStatusBadPage);
+  if (first_skip >= 0) {
+    // units whose escapes are in the pool: the recorded pages, then any between them
     auto do_page = [&](int page) {
       const int pid = sload<int32_t>(pt_row + page);
       for (int t = 0; t < T; ++t) {
@@ -315,21 +296,13 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void attn_mha_kernel(
         mha_compute<D, true>(st, a, P, krank, vrank, lds, pool, scale, lane);
       }
     };
-    // the recorded pages, then any pool unit strictly between them
-    const uint32_t flag = sload<uint32_t>(deferred + item);
-    int lo = p0, hi = p1;
-    if (flag != kScanAll) {
-      const int f = p0 + (int)(flag & 0xFFFFu) - 1, l = p0 + (int)(flag >> 16) - 1;
-      do_page(f);
-      if (l != f) do_page(l);
-      lo = f + 1;
-      hi = l;
-    }
+    do_page(first_skip);
+    if (last_skip != first_skip) do_page(last_skip);
     const uint32_t hdr_off = hdr_offset(P, D) + 8;
-    for (int c0 = lo; c0 < hi; c0 += 64) {
+    for (int c0 = first_skip + 1; c0 < last_skip; c0 += 64) {
       const int pg = c0 + lane;
       bool in_pool = false;
-      if (pg < hi) {
+      if (pg < last_skip) {
         const int pid = pt_row[pg];
         if (pid >= 0 && pid < num_pages)
           in_pool = *reinterpret_cast<const uint64_t*>(units + ((size_t)pid * H + h) * unit_bytes(P, D) + hdr_off) !=
@@ -343,12 +316,17 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void attn_mha_kernel(
       }
     }
   }
+  if (s == Sr - 1 && rows > 0) {
+    const size_t toff = ((size_t)r * H + h) * P * D;
+    mha_tail<D>(st, k_tail + toff, v_tail + toff, rows, scale, lane);
+  }
   // partials: l summed over one lane per token group (the D/16 lanes of a token hold the
   // same terms)
   constexpr int LPT = D / 16;
   float lsum = (lane % LPT) == 0 ? st.l : 0.f;
 #pragma unroll
   for (int o = LPT; o < 64; o <<= 1) lsum += __shfl_xor(lsum, o);
+  float* acc = ws_acc + slot * D;
 #pragma unroll
   for (int g = 0; g < D / 64; ++g) acc[lane + 64 * g] = st.acc[g];
   if (lane == 0) {
@@ -360,23 +338,17 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void attn_mha_kernel(
 int launch_attn_mha(const uint16_t* q, const uint8_t* units, const uint16_t* pool, const uint16_t* k_tail,
                     const uint16_t* v_tail, const int32_t* page_table, int max_pages, const int32_t* seq_lens,
                     int B, int H, int D, int P, int num_pages, int S, int C, float scale, float* ws_acc,
-                    float* ws_ml, uint32_t* deferred, uint32_t* status, hipStream_t stream) {
+                    float* ws_ml, uint32_t* status, hipStream_t stream) {
   const int items = B * H * S;
   dim3 grid((unsigned)(items + kWavesPerBlock - 1) / kWavesPerBlock), block(64 * kWavesPerBlock);
-#define KVZ_LAUNCH_MHA(DD, POOLV)                                                                                 \
-  hipLaunchKernelGGL((attn_mha_kernel<DD, POOLV>), grid, block, 0, stream, q, units, pool, k_tail, v_tail,     \
-                     page_table, max_pages, seq_lens, B, H, P, num_pages, S, C, scale, ws_acc, ws_ml, deferred, \
-                     status)
-  if (D == 128) {
-    KVZ_LAUNCH_MHA(128, false);
-    KVZ_LAUNCH_MHA(128, true);
-  } else if (D == 64) {
-    KVZ_LAUNCH_MHA(64, false);
-    KVZ_LAUNCH_MHA(64, true);
-  } else {
+  if (D == 128)
+    hipLaunchKernelGGL((attn_mha_kernel<128>), grid, block, 0, stream, q, units, pool, k_tail, v_tail, page_table,
+                       max_pages, seq_lens, B, H, P, num_pages, S, C, scale, ws_acc, ws_ml, status);
+  else if (D == 64)
+    hipLaunchKernelGGL((attn_mha_kernel<64>), grid, block, 0, stream, q, units, pool, k_tail, v_tail, page_table,
+                       max_pages, seq_lens, B, H, P, num_pages, S, C, scale, ws_acc, ws_ml, status);
+  else
     return -2;
-  }
-#undef KVZ_LAUNCH_MHA
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 

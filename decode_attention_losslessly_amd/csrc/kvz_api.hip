@@ -19,11 +19,11 @@ int launch_append(const uint16_t* k_new, const uint16_t* v_new, const int32_t* p
 int launch_attn_mha(const uint16_t* q, const uint8_t* units, const uint16_t* pool, const uint16_t* k_tail,
                     const uint16_t* v_tail, const int32_t* page_table, int max_pages, const int32_t* seq_lens,
                     int B, int H, int D, int P, int num_pages, int S, int C, float scale, float* ws_acc,
-                    float* ws_ml, uint32_t* deferred, uint32_t* status, hipStream_t stream);
+                    float* ws_ml, uint32_t* status, hipStream_t stream);
 int launch_attn_gqa(const uint16_t* q, const uint8_t* units, const uint16_t* pool, const uint16_t* k_tail,
                     const uint16_t* v_tail, const int32_t* page_table, int max_pages, const int32_t* seq_lens,
                     int B, int Hq, int Hkv, int D, int P, int num_pages, int S, int C, float scale, float* ws_acc,
-                    float* ws_ml, uint32_t* deferred, uint32_t* status, hipStream_t stream);
+                    float* ws_ml, uint32_t* status, hipStream_t stream);
 int launch_attn_dense_mha(const uint16_t* q, const uint16_t* k_pages, const uint16_t* v_pages, const int32_t* pt,
                           int max_pages, const int32_t* seq_lens, int B, int H, int D, int P, int num_pages, int S,
                           int C, float scale, float* ws_acc, float* ws_ml, uint32_t* status, hipStream_t stream);
@@ -82,9 +82,8 @@ int32_t kvz_num_splits(int32_t B, int32_t H_q, int32_t H_kv, int32_t D, int32_t 
   return split_count(max_pages_per_seq, pages_per_split(B, H_q, H_kv, P, max_pages_per_seq, pps));
 }
 
-// workspace per (request, query head, split): acc[D] and (m, l) as float, then one u32 per work
-// item (at most one item per (request, query head, split)) for the fast kernel's deferrals
-static size_t ws_bytes(int B, int Hq, int S, int D) { return (size_t)B * Hq * S * (D + 3) * sizeof(float); }
+// workspace per (request, query head, split): acc[D] and (m, l) as float
+static size_t ws_bytes(int B, int Hq, int S, int D) { return (size_t)B * Hq * S * (D + 2) * sizeof(float); }
 
 size_t kvz_workspace_bytes(int32_t B, int32_t H_q, int32_t H_kv, int32_t D, int32_t P, int32_t max_pages_per_seq,
                            int32_t pps) {
@@ -138,14 +137,13 @@ int kvz_decode_attention_splits(const uint16_t* q, const kvz_cache* c, const int
   if (workspace_bytes < ws_bytes(B, H_q, S, D)) return KVZ_ERR_WORKSPACE;
   float* ws_acc = reinterpret_cast<float*>(workspace);
   float* ws_ml = ws_acc + (size_t)B * H_q * S * D;
-  uint32_t* deferred = reinterpret_cast<uint32_t*>(ws_ml + (size_t)B * H_q * S * 2);
   const float scale = sm_scale * 1.4426950408889634f;
   if (H_q == H)
     rc = kvz::launch_attn_mha(q, c->units, c->esc_pool, c->k_tail, c->v_tail, page_table, max_pages, seq_lens, B, H,
-                              D, P, c->num_pages, S, C, scale, ws_acc, ws_ml, deferred, c->status, as_stream(stream));
+                              D, P, c->num_pages, S, C, scale, ws_acc, ws_ml, c->status, as_stream(stream));
   else
     rc = kvz::launch_attn_gqa(q, c->units, c->esc_pool, c->k_tail, c->v_tail, page_table, max_pages, seq_lens, B,
-                              H_q, H, D, P, c->num_pages, S, C, scale, ws_acc, ws_ml, deferred, c->status,
+                              H_q, H, D, P, c->num_pages, S, C, scale, ws_acc, ws_ml, c->status,
                               as_stream(stream));
   return rc ? (rc == -2 ? KVZ_ERR_UNSUPPORTED : KVZ_ERR_HIP) : KVZ_OK;
 }

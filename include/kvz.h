@@ -102,9 +102,8 @@ size_t kvz_meta_bytes(int32_t P, int32_t D);
 int32_t kvz_inline_capacity(int32_t P, int32_t D);
 
 /* Bytes of scratch kvz_decode_attention / kvz_decode_attention_dense need: split partials
- * (acc[D], m, l) in float for every (request, query head, split), then one u32 per work item
- * (the compressed path's record of which items its general kernel must run). Its content needs
- * no initialisation. pages_per_split = 0 lets the library choose; the same value must be passed
+ * (acc[D], m, l) in float for every (request, query head, split). Its content needs no
+ * initialisation. pages_per_split = 0 lets the library choose; the same value must be passed
  * to the attention call. */
 size_t kvz_workspace_bytes(int32_t B, int32_t H_q, int32_t H_kv, int32_t D, int32_t P,
                            int32_t max_pages_per_seq, int32_t pages_per_split);
