@@ -68,13 +68,18 @@ __global__ void bump_lens_kernel(int32_t* __restrict__ seq_lens, int B, int limi
 
 static size_t compress_smem(int P, int D) { return 4 * (size_t)P * D + 2 * (size_t)P * (D / kGroup); }
 
+// Dynamic LDS beyond 64 KB must be opted into per kernel. Below that nothing is called, so that
+// the usual page sizes launch with stream operations only (a caller may capture them in a graph).
+static bool allow_smem(const void* kernel, size_t smem) {
+  if (smem <= 65536) return true;
+  return hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem) == hipSuccess;
+}
+
 int launch_compress(const uint16_t* k_src, const uint16_t* v_src, const int32_t* ids, int n, int H, int P, int D,
                     int num_pages, uint8_t* units, uint16_t* pool, int64_t pool_cap, uint64_t* cursor,
                     uint32_t* status, hipStream_t stream) {
   const size_t smem = compress_smem(P, D);
-  if (hipFuncSetAttribute((const void*)compress_pages_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                          (int)smem) != hipSuccess)
-    return -4;
+  if (!allow_smem((const void*)compress_pages_kernel, smem)) return -4;
   hipLaunchKernelGGL(compress_pages_kernel, dim3((unsigned)n * H), dim3(kCompressThreads), smem, stream, k_src,
                      v_src, ids, H, P, D, num_pages, units, pool, pool_cap, cursor, status);
   return hipGetLastError() == hipSuccess ? 0 : -4;
@@ -85,9 +90,7 @@ int launch_append(const uint16_t* k_new, const uint16_t* v_new, const int32_t* p
                   int64_t pool_cap, uint64_t* cursor, uint16_t* k_tail, uint16_t* v_tail, uint32_t* status,
                   hipStream_t stream) {
   const size_t smem = compress_smem(P, D);
-  if (hipFuncSetAttribute((const void*)append_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem) !=
-      hipSuccess)
-    return -4;
+  if (!allow_smem((const void*)append_kernel, smem)) return -4;
   hipLaunchKernelGGL(append_kernel, dim3((unsigned)B * H), dim3(kCompressThreads), smem, stream, k_new, v_new,
                      page_table, max_pages, seq_lens, H, P, D, num_pages, units, pool, pool_cap, cursor, k_tail,
                      v_tail, status);

@@ -1,0 +1,82 @@
+"""One decode step (append a token to every request, then attention and merge) captured once in
+a HIP graph and replayed step after step: every replay gives exactly what the same step gives
+run eagerly, including steps whose append fills a page and compresses it. The library launches
+only stream work (no allocation, no synchronisation, no memset) and reads sequence lengths from
+device memory, so a single captured step serves every later step of a decode loop."""
+import numpy as np
+import pytest
+import torch
+
+import decode_attention_losslessly_amd as kvz
+from kvz_testlib import DEV, check_rows, dev, escape_capacity, full_page_ids, host16, oracle_rows, tails
+from synth import make_workload
+
+pytestmark = pytest.mark.gpu
+
+N_STEPS = 24
+
+
+def _copy(c: kvz.Cache) -> kvz.Cache:
+    return kvz.Cache(c.P, c.H, c.D, c.num_pages, c.max_batch, c.units.clone(), c.esc_pool.clone(),
+                     c.esc_cursor.clone(), c.k_tail.clone(), c.v_tail.clone(), c.status.clone())
+
+
+@pytest.mark.parametrize("cfg,Hq,Hkv,lens", [(3, 4, 4, [100, 37, 250]), (4, 8, 2, [60, 17, 200])])
+def test_replayed_decode_steps_match_eager(cfg, Hq, Hkv, lens):
+    # the workload holds the final lengths; the cache starts N_STEPS tokens shorter
+    w = make_workload(cfg, B=len(lens), lens=np.array(lens) + N_STEPS, Hq=Hq, Hkv=Hkv, D=128, n_append=0)
+    kp, vp = w.pages(0), w.pages(1)
+    L0 = (w.seq_lens - N_STEPS).astype(np.int32)
+    ids = full_page_ids(w, L0)
+    cache = kvz.Cache.allocate(w.P, w.Hkv, w.D, w.num_pages, w.B, escape_capacity(w, len(w.page_table.ravel()) * w.Hkv),
+                               device=DEV)
+    kvz.compress_pages(cache, dev(kp[ids]), dev(vp[ids]), dev(ids))
+    tk, tv = tails(w, kp, vp, L0)
+    cache.k_tail.copy_(dev(tk))
+    cache.v_tail.copy_(dev(tv))
+    table, q = dev(w.page_table), dev(w.q())
+    new_k = [dev(np.stack([w.token(r, int(L0[r]) + i, 0) for r in range(w.B)])) for i in range(N_STEPS)]
+    new_v = [dev(np.stack([w.token(r, int(L0[r]) + i, 1) for r in range(w.B)])) for i in range(N_STEPS)]
+    ws = torch.empty(kvz.workspace_bytes(w.B, w.Hq, w.Hkv, w.D, w.P, w.max_pages), dtype=torch.uint8, device=DEV)
+    torch.cuda.synchronize()
+
+    # eager
+    ce, le = _copy(cache), dev(L0)
+    eager = []
+    for i in range(N_STEPS):
+        out = torch.empty((w.B, w.Hq, w.D), dtype=torch.int16, device=DEV)
+        out32 = torch.empty((w.B, w.Hq, w.D), dtype=torch.float32, device=DEV)
+        kvz.append_token(ce, new_k[i], new_v[i], table, le)
+        kvz.decode_attention(q, ce, table, le, w.sm_scale, out, out32, workspace=ws)
+        eager.append((out, out32))
+    torch.cuda.synchronize()
+
+    # one captured step, replayed with the next token copied into its static inputs each time
+    cg, lg = _copy(cache), dev(L0)
+    k_in, v_in = torch.empty_like(new_k[0]), torch.empty_like(new_v[0])
+    out_g = torch.empty((w.B, w.Hq, w.D), dtype=torch.int16, device=DEV)
+    out32_g = torch.empty((w.B, w.Hq, w.D), dtype=torch.float32, device=DEV)
+    ws_g = torch.empty_like(ws)
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            kvz.append_token(cg, k_in, v_in, table, lg)
+            kvz.decode_attention(q, cg, table, lg, w.sm_scale, out_g, out32_g, workspace=ws_g)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    assert np.array_equal(lg.cpu().numpy(), L0), "capturing must not run the step"
+    for i in range(N_STEPS):
+        k_in.copy_(new_k[i])
+        v_in.copy_(new_v[i])
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out_g, eager[i][0]), f"bf16 output differs at step {i}"
+        assert torch.equal(out32_g, eager[i][1]), f"fp32 output differs at step {i}"
+    assert np.array_equal(lg.cpu().numpy(), w.seq_lens) and np.array_equal(le.cpu().numpy(), w.seq_lens)
+    assert int(cg.status.item()) == 0 and int(ce.status.item()) == 0
+    # and the last step is the attention of the full workload
+    rows = [(r, h) for r in range(w.B) for h in range(w.Hq)]
+    o = oracle_rows(w, kp, vp, w.q(), rows)
+    check_rows(host16(out_g).reshape(-1, w.D), out32_g.cpu().numpy().reshape(-1, w.D), o, "graph replay")
