@@ -27,7 +27,6 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0
-WORKLOADS = {3: "mha_ctx8k_b32", 2: "llama7b_b1_ctx4k", 4: "gqa28x4_b64", 5: "escape_stress_ctx32k_b4", 1: "tiny"}
 
 
 def source_digest() -> str:
@@ -46,6 +45,8 @@ def parse():
     # the first ~30 launches after set-up run up to 20 % slower while the clocks settle
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--config", type=int, default=3, help="workload number (3 = the headline workload)")
+    ap.add_argument("--batch", type=int, default=None, help="override the workload's batch size")
+    ap.add_argument("--context", type=int, default=None, help="override the workload's context length")
     ap.add_argument("--no-dense", action="store_true", help="skip the uncompressed baseline")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-requests", type=int, default=32, help="requests in the CPU baseline sample")
@@ -83,7 +84,9 @@ def main() -> int:
     log = lambda *a: print("[bench]", *a, file=sys.stderr, flush=True)
     t16 = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16 if a.dtype == np.uint16 else a.dtype)).to(dev)
 
-    w = make_workload(args.config)
+    w = make_workload(args.config, B=args.batch, L=args.context)
+    if args.batch is not None or args.context is not None:
+        w.name = f"{w.name}@b{w.B}_ctx{int(w.seq_lens.max())}"
     B, Hq, H, D, P = w.B, w.Hq, w.Hkv, w.D, w.P
     t0 = time.perf_counter()
     kp, vp = w.pages(0), w.pages(1)

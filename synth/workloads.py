@@ -40,6 +40,10 @@ CONFIGS = {
             k_dist="student_t3", v_dist="normal_half"),
     5: dict(name="escape_stress_ctx32k_b4", B=4, Hq=32, Hkv=32, D=128, P=16, L=32768, append=0,
             k_dist="log_uniform", v_dist="log_uniform"),
+    # the attention-benchmark shape of the ZipFusion summary (§IV.B: 32 query / 8 KV heads,
+    # head_dim 128, 16-token pages, 8192-token context, batch 64), K with outlier channels
+    6: dict(name="gqa32x8_b64_ctx8k", B=64, Hq=32, Hkv=8, D=128, P=16, L=8192, append=0,
+            k_dist="outlier_normal", v_dist="normal"),
 }
 
 

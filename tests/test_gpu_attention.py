@@ -21,6 +21,7 @@ SMALL = {
     3: dict(B=3, L=161),
     4: dict(B=6, lens=[1, 15, 16, 17, 300, 1024]),
     5: dict(B=2, L=517),
+    6: dict(B=3, L=161),
 }
 
 
@@ -180,7 +181,7 @@ def _sampled_rows(w, n, seed):
     return sorted(set(zip(rs.tolist(), hs.tolist())))
 
 
-@pytest.mark.parametrize("cfg", [2, 3, 4, 5])
+@pytest.mark.parametrize("cfg", [2, 3, 4, 5, 6])
 def test_full_size_sampled_rows(cfg, full_workloads):
     """Full shapes, the launch configuration the benchmark times, sampled (request, head) rows."""
     w, kp, vp, cache, lens = full_workloads(cfg)

@@ -18,6 +18,7 @@ SMALL = {
     3: dict(B=3, L=97),
     4: dict(B=5, lens=[1, 16, 33, 150, 47]),
     5: dict(B=2, L=70),
+    6: dict(B=2, L=70),
 }
 
 

@@ -235,7 +235,7 @@ def test_every_pattern_round_trips_in_c_oracle():
     assert seen.all()
 
 
-@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5, 6])
 def test_python_and_c_oracles_agree_on_configs(cfg):
     w = make_workload(cfg)
     ids = np.arange(min(6, w.num_pages))
