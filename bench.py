@@ -29,12 +29,21 @@ sys.path.insert(0, ROOT)
 PEAK_HBM_GBPS = 8000.0
 
 
-def source_digest() -> str:
-    h = hashlib.sha256()
+def source_digest(kernel_source: str = "attn_mha.hip") -> str:
+    """Digest of one attention kernel's sources: its translation unit and the headers it
+    includes (the counters in profiles/ stay valid while these are unchanged)."""
     csrc = os.path.join(ROOT, "decode_attention_losslessly_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(f.encode() + fh.read())
+    h = hashlib.sha256()
+    seen, todo = set(), [kernel_source]
+    while todo:
+        f = todo.pop()
+        if f in seen or not os.path.exists(os.path.join(csrc, f)):
+            continue
+        seen.add(f)
+        text = open(os.path.join(csrc, f), "rb").read()
+        todo += [ln.split(b'"')[1].decode() for ln in text.splitlines() if ln.startswith(b'#include "')]
+    for f in sorted(seen):
+        h.update(f.encode() + open(os.path.join(csrc, f), "rb").read())
     return h.hexdigest()[:16]
 
 
@@ -209,10 +218,11 @@ def main() -> int:
     attn_mean = float(np.mean(attn_us))
     achieved = comp_bytes / (attn_mean * 1e-6) / 1e9
     traffic = None
+    ksrc = "attn_mha.hip" if Hq == H else "attn_gqa.hip"
     tfile = os.path.join(ROOT, "profiles", f"traffic_{w.name}.json")
     if os.path.exists(tfile):
         t = json.load(open(tfile))
-        if t.get("source_digest") == source_digest():
+        if t.get("source_digest") == source_digest(ksrc):
             traffic = t.get("bytes_per_launch")
     kname = f"attn_mha_kernel<{D}>" if Hq == H else "attn_gqa_kernel"
     roofline = dict(kernel=kname, bound="hbm",
@@ -256,7 +266,7 @@ def main() -> int:
         "append_us": round(append_us, 1) if append_us is not None else None,
         "compress_gbps_dense_input": round(len(ids) * H * P * D * 4 / compress_s / 1e9, 1),
         "gpu": f"{torch.cuda.get_device_name(0)} ({torch.cuda.get_device_properties(0).gcnArchName})",
-        "source_digest": source_digest(),
+        "source_digest": source_digest("attn_mha.hip" if Hq == H else "attn_gqa.hip"),
     }
     print(json.dumps(res), flush=True)
     return 0
