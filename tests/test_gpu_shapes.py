@@ -1,0 +1,49 @@
+"""Attention parity on shapes the five workloads do not reach: pages of several 16-token tiles
+(including a count that is not a power of two), query groups of 2 and 16 heads (16 = two MFMA
+row chunks), head_dim 64, and ragged lengths around page boundaries. Compressed and dense paths
+against the fp64 oracle within the stated tolerance."""
+import numpy as np
+import pytest
+import torch
+
+import decode_attention_losslessly_amd as kvz
+from kvz_testlib import DEV, build_cache, check_rows, dev, host16, oracle_rows
+from synth import make_workload
+
+pytestmark = pytest.mark.gpu
+
+SHAPES = [  # (P, D, Hq, Hkv)
+    (32, 128, 8, 2),
+    (48, 128, 6, 3),
+    (64, 128, 32, 2),
+    (256, 128, 4, 1),
+    (16, 64, 4, 4),
+    (64, 64, 8, 8),
+]
+
+
+@pytest.mark.parametrize("P,D,Hq,Hkv", SHAPES)
+def test_shapes_match_oracle(P, D, Hq, Hkv):
+    lens = [1, P - 1, P, P + 1, 5 * P + 3, 2 * P]
+    for cfg in (1, 5):   # smooth per-channel scales, and the escape-stress distribution (pool path)
+        w = make_workload(cfg, B=len(lens), lens=lens, Hq=Hq, Hkv=Hkv, D=D, P=P, n_append=0)
+        kp, vp = w.pages(0), w.pages(1)
+        cache, seq = build_cache(w, kp, vp)
+        q = w.q()
+        rows = [(r, h) for r in range(w.B) for h in range(w.Hq)]
+        ref = oracle_rows(w, kp, vp, q, rows)
+        for pps in (0, 1, 3):
+            out = torch.zeros((w.B, w.Hq, w.D), dtype=torch.int16, device=DEV)
+            out32 = torch.full((w.B, w.Hq, w.D), float("nan"), dtype=torch.float32, device=DEV)
+            kvz.decode_attention(dev(q), cache, dev(w.page_table), seq, w.sm_scale, out, out32, pages_per_split=pps)
+            torch.cuda.synchronize()
+            assert int(cache.status.item()) == 0
+            check_rows(host16(out).reshape(-1, D), out32.cpu().numpy().reshape(-1, D), ref,
+                       f"cfg{cfg} P{P} D{D} {Hq}/{Hkv} pps{pps} compressed")
+        status = torch.zeros(1, dtype=torch.int32, device=DEV)
+        kvz.decode_attention_dense(dev(q), dev(kp), dev(vp), dev(w.page_table), dev(w.seq_lens), w.sm_scale, out,
+                                   out32, status=status)
+        torch.cuda.synchronize()
+        assert int(status.item()) == 0
+        check_rows(host16(out).reshape(-1, D), out32.cpu().numpy().reshape(-1, D), ref,
+                   f"cfg{cfg} P{P} D{D} {Hq}/{Hkv} dense")
