@@ -1,0 +1,288 @@
+// Decode attention over a cache in ZipFusion's block format (zf.hpp), multi-head (one query head
+// per KV head). Same organisation as the main multi-head kernel (attn_mha.hip): one wave per
+// (request, head, split), lane l holding K pieces l + 64 i and V dims l + 64 s, the next tile's
+// loads issued before the current tile is computed, scores / softmax / P.V from mha_core.hpp.
+// Compressed blocks are rebuilt in registers (§III.C of the ZipFusion summary: four high bytes
+// per 32-bit add, combined with the kept low bytes). A unit with any raw block is skipped by
+// the main loop and added after it, its raw blocks read from the pool (the pages' format keeps
+// such blocks uncompressed and reads them without a rebuild).
+//
+// Also the test kernel that writes the rebuilt values of whole units back out.
+#include "mha_core.hpp"
+#include "zf.hpp"
+
+namespace kvz {
+
+constexpr int kZfWaves = 4;
+
+template <int D>
+struct ZStage {
+  const uint8_t* unit;
+  int page, tile;
+  bool ok;           // false when the page id was out of range: a stand-in unit was read
+  uint32_t rawlo;    // low dword of the unit's raw-pool offset: all ones when it has no raw block
+  ZPiece k[D / 64];
+  ZPiece v[D / 64];
+};
+
+// Unconditional loads of one (page, tile) step (see the main kernel for why).
+template <int D>
+__device__ __forceinline__ void zf_issue(ZStage<D>& st, const uint8_t* units, int pid, int page, int tile, int H,
+                                         int h, int P, int num_pages, int lane) {
+  st.ok = pid >= 0 && pid < num_pages;
+  st.page = page;
+  st.tile = tile;
+  st.unit = units + ((size_t)(st.ok ? pid : 0) * H + h) * zf_unit_bytes(P, D);
+  st.rawlo = stream4(st.unit + zf_rawoff_offset(P, D));
+#pragma unroll
+  for (int i = 0; i < D / 64; ++i) zf_load_piece(st.unit, P, D, false, tile, k_piece<D, false>(lane, i), st.k[i]);
+#pragma unroll
+  for (int s = 0; s < D / 64; ++s) zf_load_piece(st.unit, P, D, true, tile, lane + 64 * s, st.v[s]);
+}
+
+// Rebuilds this lane's K and V pairs; with RAW, raw blocks are read from the pool (bounds-checked
+// against its capacity; a unit whose raw blocks were dropped reads zeros).
+template <int D, bool RAW>
+__device__ __forceinline__ void zf_rebuild(const ZStage<D>& stg, int P, const uint16_t* pool, int64_t pool_cap,
+                                           int lane, uint32_t (&kp)[D / 8], uint32_t (&vp)[D / 8]) {
+  uint64_t off = 0;
+  if constexpr (RAW) off = zf_raw_offset(stg.unit, P, D);
+#pragma unroll
+  for (int i = 0; i < D / 64; ++i) {
+    if (RAW && stg.k[i].meta == kZfRaw) {
+      const int pc = k_piece<D, false>(lane, i);
+      const uint32_t rank = zf_raw_rank(stg.unit, zf_block_index(false, P, D, stg.tile, (16 * pc) / kZfBlock));
+      if (off != kInline && off + (uint64_t)(rank + 1) * kZfBlock <= (uint64_t)pool_cap)
+        zf_raw_piece(pool, off, rank, pc, &kp[8 * i]);
+      else
+        for (int j = 0; j < 8; ++j) kp[8 * i + j] = 0;
+    } else {
+      zf_decode_piece(stg.k[i], &kp[8 * i]);
+    }
+  }
+#pragma unroll
+  for (int s = 0; s < D / 64; ++s) {
+    if (RAW && stg.v[s].meta == kZfRaw) {
+      const int d = lane + 64 * s;
+      const uint32_t rank = zf_raw_rank(stg.unit, zf_block_index(true, P, D, stg.tile, (16 * d) / kZfBlock));
+      if (off != kInline && off + (uint64_t)(rank + 1) * kZfBlock <= (uint64_t)pool_cap)
+        zf_raw_piece(pool, off, rank, d, &vp[8 * s]);
+      else
+        for (int j = 0; j < 8; ++j) vp[8 * s + j] = 0;
+    } else {
+      zf_decode_piece(stg.v[s], &vp[8 * s]);
+    }
+  }
+}
+
+// Returns false, leaving the state untouched, when the unit has raw blocks and RAW is off.
+template <int D, bool RAW>
+__device__ __forceinline__ bool zf_compute(MhaState<D>& st, const ZStage<D>& stg, int P, const uint16_t* pool,
+                                           int64_t pool_cap, float scale, int lane) {
+  if (!stg.ok) return true;
+  if (!RAW && uniform(stg.rawlo) != 0xFFFFFFFFu) return false;
+  uint32_t kp[D / 8], vp[D / 8];
+  zf_rebuild<D, RAW>(stg, P, pool, pool_cap, lane, kp, vp);
+  float sc[D / 64];
+  mha_scores<D>(st, kp, scale, sc);
+  uint32_t phi[8], plo[8];
+  mha_softmax<D>(st, sc, phi, plo);
+  mha_accumulate_v<D>(st, vp, phi, plo);
+  return true;
+}
+
+template <int D>
+__global__ __launch_bounds__(64 * kZfWaves) void attn_zf_kernel(
+    const uint16_t* __restrict__ q, const uint8_t* __restrict__ units, const uint16_t* __restrict__ pool,
+    int64_t pool_cap, const uint16_t* __restrict__ k_tail, const uint16_t* __restrict__ v_tail,
+    const int32_t* __restrict__ page_table, int max_pages, const int32_t* __restrict__ seq_lens, int B, int H, int P,
+    int num_pages, int S, int C, float scale, float* __restrict__ ws_acc, float* __restrict__ ws_ml,
+    uint32_t* __restrict__ status) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int item = (int)uniform(blockIdx.x * kZfWaves + wave);
+  if (item >= B * H * S) return;
+  const int s = item % S, h = (item / S) % H, r = item / (S * H);
+  int L = sload<int32_t>(seq_lens + r);
+  if (L > max_pages * P || L < 0) {
+    if (lane == 0 && s == 0 && h == 0) atomicOr(status, kStatusSeqTooLong);
+    L = L < 0 ? 0 : max_pages * P;
+  }
+  int nfull = L / P;
+  const int rows = L % P;
+  if (num_pages <= 0 && nfull > 0) {
+    if (lane == 0 && s == 0 && h == 0) atomicOr(status, kStatusBadPage);
+    nfull = 0;
+  }
+  const int Sr = active_splits(nfull, C);
+  if (s >= Sr) return;
+  const int p0 = s * C, p1 = min(p0 + C, nfull);
+  const size_t slot = ((size_t)r * H + h) * S + s;
+
+  MhaState<D> st;
+  {
+    const uint4* qrow = reinterpret_cast<const uint4*>(q + ((size_t)r * H + h) * D + (16 * lane) % D);
+    const uint4 a = qrow[0], b = qrow[1];
+    st.q[0] = a.x; st.q[1] = a.y; st.q[2] = a.z; st.q[3] = a.w;
+    st.q[4] = b.x; st.q[5] = b.y; st.q[6] = b.z; st.q[7] = b.w;
+  }
+  st.m = -INFINITY;
+  st.l = 0.f;
+#pragma unroll
+  for (int i = 0; i < D / 64; ++i) st.acc[i] = 0.f;
+  const int32_t* pt_row = page_table + (size_t)r * max_pages;
+  const int T = P / kTile;
+  const int nsteps = (p1 > p0 ? p1 - p0 : 0) * T;
+  int first_skip = -1, last_skip = -1;
+  bool bad = false;
+  auto note = [&](const ZStage<D>& stg) {
+    if (first_skip < 0) first_skip = stg.page;
+    last_skip = stg.page;
+  };
+  if (nsteps > 0) {
+    int ln = 0, lp = p0, lt = 0;
+    const int last = nsteps - 1;
+    auto advance = [&]() {
+      if (ln < last) {
+        ++ln;
+        if (++lt == T) { lt = 0; ++lp; }
+      }
+    };
+    ZStage<D> a, b;
+    int pid = sload<int32_t>(pt_row + lp);
+    zf_issue<D>(a, units, pid, lp, lt, H, h, P, num_pages, lane);
+    advance();
+    pid = sload<int32_t>(pt_row + lp);
+    for (int i = 0; i < nsteps; i += 2) {
+      zf_issue<D>(b, units, pid, lp, lt, H, h, P, num_pages, lane);
+      advance();
+      pid = sload<int32_t>(pt_row + lp);
+      bad |= !a.ok;
+      if (!zf_compute<D, false>(st, a, P, pool, pool_cap, scale, lane)) note(a);
+      if (i + 1 >= nsteps) break;
+      zf_issue<D>(a, units, pid, lp, lt, H, h, P, num_pages, lane);
+      advance();
+      pid = sload<int32_t>(pt_row + lp);
+      bad |= !b.ok;
+      if (!zf_compute<D, false>(st, b, P, pool, pool_cap, scale, lane)) note(b);
+    }
+  }
+  if (bad && lane == 0) atomicOr(status, kStatusBadPage);
+  if (first_skip >= 0) {
+    // units with raw blocks: the recorded pages, then any between them
+    auto do_page = [&](int page) {
+      const int pid = sload<int32_t>(pt_row + page);
+      for (int t = 0; t < T; ++t) {
+        ZStage<D> a;
+        zf_issue<D>(a, units, pid, page, t, H, h, P, num_pages, lane);
+        zf_compute<D, true>(st, a, P, pool, pool_cap, scale, lane);
+      }
+    };
+    do_page(first_skip);
+    if (last_skip != first_skip) do_page(last_skip);
+    for (int c0 = first_skip + 1; c0 < last_skip; c0 += 64) {
+      const int pg = c0 + lane;
+      bool has_raw = false;
+      if (pg < last_skip) {
+        const int pid = pt_row[pg];
+        if (pid >= 0 && pid < num_pages)
+          has_raw = zf_raw_offset(units + ((size_t)pid * H + h) * zf_unit_bytes(P, D), P, D) != kInline;
+      }
+      uint64_t todo = ballot(has_raw);
+      while (todo) {
+        const int page = c0 + __builtin_ctzll(todo);
+        todo &= todo - 1;
+        do_page(page);
+      }
+    }
+  }
+  if (s == Sr - 1 && rows > 0) {
+    const size_t toff = ((size_t)r * H + h) * P * D;
+    mha_tail<D>(st, k_tail + toff, v_tail + toff, rows, scale, lane);
+  }
+  constexpr int LPT = D / 16;
+  float lsum = (lane % LPT) == 0 ? st.l : 0.f;
+#pragma unroll
+  for (int o = LPT; o < 64; o <<= 1) lsum += __shfl_xor(lsum, o);
+  float* acc = ws_acc + slot * D;
+#pragma unroll
+  for (int g = 0; g < D / 64; ++g) acc[lane + 64 * g] = st.acc[g];
+  if (lane == 0) {
+    ws_ml[slot * 2 + 0] = st.m;
+    ws_ml[slot * 2 + 1] = lsum;
+  }
+}
+
+// Test kernel: one wave per (unit, head) writes the rebuilt K and V of whole units (the same
+// loads and rebuild as the attention kernel, raw blocks from the pool).
+template <int D>
+__global__ __launch_bounds__(64) void decompress_zf_kernel(const uint8_t* __restrict__ units,
+                                                           const uint16_t* __restrict__ pool, int64_t pool_cap,
+                                                           const int32_t* __restrict__ page_ids, int H, int P,
+                                                           int num_pages, uint16_t* __restrict__ k_dst,
+                                                           uint16_t* __restrict__ v_dst, uint32_t* __restrict__ status) {
+  const int lane = threadIdx.x;
+  const int i = blockIdx.x / H, h = blockIdx.x % H;
+  const int pid = sload<int32_t>(page_ids + i);
+  if (pid < 0 || pid >= num_pages) {
+    if (lane == 0) atomicOr(status, kStatusBadPage);
+    return;
+  }
+  uint16_t* kd = k_dst + ((size_t)i * H + h) * P * D;
+  uint16_t* vd = v_dst + ((size_t)i * H + h) * P * D;
+  for (int t = 0; t < P / kTile; ++t) {
+    ZStage<D> st;
+    zf_issue<D>(st, units, pid, 0, t, H, h, P, num_pages, lane);
+    uint32_t kp[D / 8], vp[D / 8];
+    zf_rebuild<D, true>(st, P, pool, pool_cap, lane, kp, vp);
+#pragma unroll
+    for (int p = 0; p < D / 64; ++p) {
+      const int pc = k_piece<D, false>(lane, p);
+      uint32_t* dst = reinterpret_cast<uint32_t*>(kd + (size_t)(t * kTile + piece_token<D>(pc)) * D + piece_dim<D>(pc));
+#pragma unroll
+      for (int j = 0; j < 8; ++j) dst[j] = kp[8 * p + j];
+    }
+#pragma unroll
+    for (int s = 0; s < D / 64; ++s) {
+      const int d = lane + 64 * s;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        vd[(size_t)(t * kTile + 2 * k) * D + d] = (uint16_t)(vp[8 * s + k] & 0xFFFFu);
+        vd[(size_t)(t * kTile + 2 * k + 1) * D + d] = (uint16_t)(vp[8 * s + k] >> 16);
+      }
+    }
+  }
+}
+
+int launch_attn_zf(const uint16_t* q, const uint8_t* units, const uint16_t* pool, int64_t pool_cap,
+                   const uint16_t* k_tail, const uint16_t* v_tail, const int32_t* page_table, int max_pages,
+                   const int32_t* seq_lens, int B, int H, int D, int P, int num_pages, int S, int C, float scale,
+                   float* ws_acc, float* ws_ml, uint32_t* status, hipStream_t stream) {
+  const int items = B * H * S;
+  dim3 grid((unsigned)(items + kZfWaves - 1) / kZfWaves), block(64 * kZfWaves);
+  if (D == 128)
+    hipLaunchKernelGGL((attn_zf_kernel<128>), grid, block, 0, stream, q, units, pool, pool_cap, k_tail, v_tail,
+                       page_table, max_pages, seq_lens, B, H, P, num_pages, S, C, scale, ws_acc, ws_ml, status);
+  else if (D == 64)
+    hipLaunchKernelGGL((attn_zf_kernel<64>), grid, block, 0, stream, q, units, pool, pool_cap, k_tail, v_tail,
+                       page_table, max_pages, seq_lens, B, H, P, num_pages, S, C, scale, ws_acc, ws_ml, status);
+  else
+    return -2;
+  return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
+int launch_decompress_zf(const uint8_t* units, const uint16_t* pool, int64_t pool_cap, const int32_t* page_ids, int n,
+                         int H, int P, int D, int num_pages, uint16_t* k_dst, uint16_t* v_dst, uint32_t* status,
+                         hipStream_t stream) {
+  dim3 grid((unsigned)n * H), block(64);
+  if (D == 128)
+    hipLaunchKernelGGL((decompress_zf_kernel<128>), grid, block, 0, stream, units, pool, pool_cap, page_ids, H, P,
+                       num_pages, k_dst, v_dst, status);
+  else if (D == 64)
+    hipLaunchKernelGGL((decompress_zf_kernel<64>), grid, block, 0, stream, units, pool, pool_cap, page_ids, H, P,
+                       num_pages, k_dst, v_dst, status);
+  else
+    return -2;
+  return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
+}  // namespace kvz

@@ -1,12 +1,32 @@
-// kvz_compress_pages and kvz_append_token kernels.
+// kvz_compress_pages and kvz_append_token kernels, for both cache formats (0: exponent offsets
+// with escapes, compress.hpp; 1: ZipFusion blocks, zf.hpp).
 #include "compress.hpp"
+#include "zf.hpp"
 
 namespace kvz {
+
+// one unit of either format; smem holds 2*P*D u16 of staged values, then the per-group (or
+// per-block) bytes
+__device__ __forceinline__ void compress_any(const uint16_t* k, const uint16_t* v, int P, int D, uint8_t* units,
+                                             int pid, int H, int h, uint16_t* pool, int64_t pool_cap,
+                                             uint64_t* cursor, uint32_t* status, uint8_t* smem, CompressShared& sh,
+                                             int format) {
+  const size_t blk = (size_t)P * D;
+  uint16_t* sx = reinterpret_cast<uint16_t*>(smem);
+  if (format == 1) {
+    const int nb = zf_nblocks(P, D);
+    compress_unit_zf(k, v, P, D, units + ((size_t)pid * H + h) * zf_unit_bytes(P, D), pool, pool_cap, cursor, status,
+                     sx, smem + 4 * blk, reinterpret_cast<uint16_t*>(smem + 4 * blk + (nb + 1) / 2 * 2), sh);
+  } else {
+    compress_unit<0>(k, v, P, D, units + ((size_t)pid * H + h) * unit_bytes(P, D), pool, pool_cap, cursor, status,
+                     sx, smem + 4 * blk, sh);
+  }
+}
 
 __global__ __launch_bounds__(kCompressThreads) void compress_pages_kernel(
     const uint16_t* __restrict__ k_src, const uint16_t* __restrict__ v_src, const int32_t* __restrict__ dst_ids,
     int H, int P, int D, int num_pages, uint8_t* __restrict__ units, uint16_t* __restrict__ pool, int64_t pool_cap,
-    uint64_t* __restrict__ cursor, uint32_t* __restrict__ status) {
+    uint64_t* __restrict__ cursor, uint32_t* __restrict__ status, int format) {
   extern __shared__ __align__(16) uint8_t smem[];
   __shared__ CompressShared sh;
   const int i = blockIdx.x / H, h = blockIdx.x % H;
@@ -16,9 +36,8 @@ __global__ __launch_bounds__(kCompressThreads) void compress_pages_kernel(
     return;
   }
   const size_t blk = (size_t)P * D;
-  compress_unit<0>(k_src + ((size_t)i * H + h) * blk, v_src + ((size_t)i * H + h) * blk, P, D,
-                   units + ((size_t)pid * H + h) * unit_bytes(P, D), pool, pool_cap, cursor, status,
-                   reinterpret_cast<uint16_t*>(smem), smem + 4 * blk, sh);
+  compress_any(k_src + ((size_t)i * H + h) * blk, v_src + ((size_t)i * H + h) * blk, P, D, units, pid, H, h, pool,
+               pool_cap, cursor, status, smem, sh, format);
 }
 
 // One workgroup per (request, head): write the new row into the tail; if that fills the tail,
@@ -27,7 +46,7 @@ __global__ __launch_bounds__(kCompressThreads) void append_kernel(
     const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new, const int32_t* __restrict__ page_table,
     int max_pages, const int32_t* __restrict__ seq_lens, int H, int P, int D, int num_pages,
     uint8_t* __restrict__ units, uint16_t* __restrict__ pool, int64_t pool_cap, uint64_t* __restrict__ cursor,
-    uint16_t* __restrict__ k_tail, uint16_t* __restrict__ v_tail, uint32_t* __restrict__ status) {
+    uint16_t* __restrict__ k_tail, uint16_t* __restrict__ v_tail, uint32_t* __restrict__ status, int format) {
   extern __shared__ __align__(16) uint8_t smem[];
   __shared__ CompressShared sh;
   const int r = blockIdx.x / H, h = blockIdx.x % H;
@@ -54,8 +73,7 @@ __global__ __launch_bounds__(kCompressThreads) void append_kernel(
     if (threadIdx.x == 0) atomicOr(status, kStatusBadPage);
     return;
   }
-  compress_unit<0>(tk, tv, P, D, units + ((size_t)pid * H + h) * unit_bytes(P, D), pool, pool_cap, cursor,
-                   status, reinterpret_cast<uint16_t*>(smem), smem + 4 * blk, sh);
+  compress_any(tk, tv, P, D, units, pid, H, h, pool, pool_cap, cursor, status, smem, sh, format);
 }
 
 __global__ void bump_lens_kernel(int32_t* __restrict__ seq_lens, int B, int limit) {
@@ -77,23 +95,23 @@ static bool allow_smem(const void* kernel, size_t smem) {
 
 int launch_compress(const uint16_t* k_src, const uint16_t* v_src, const int32_t* ids, int n, int H, int P, int D,
                     int num_pages, uint8_t* units, uint16_t* pool, int64_t pool_cap, uint64_t* cursor,
-                    uint32_t* status, hipStream_t stream) {
+                    uint32_t* status, int format, hipStream_t stream) {
   const size_t smem = compress_smem(P, D);
   if (!allow_smem((const void*)compress_pages_kernel, smem)) return -4;
   hipLaunchKernelGGL(compress_pages_kernel, dim3((unsigned)n * H), dim3(kCompressThreads), smem, stream, k_src,
-                     v_src, ids, H, P, D, num_pages, units, pool, pool_cap, cursor, status);
+                     v_src, ids, H, P, D, num_pages, units, pool, pool_cap, cursor, status, format);
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 
 int launch_append(const uint16_t* k_new, const uint16_t* v_new, const int32_t* page_table, int max_pages,
                   int32_t* seq_lens, int B, int H, int P, int D, int num_pages, uint8_t* units, uint16_t* pool,
                   int64_t pool_cap, uint64_t* cursor, uint16_t* k_tail, uint16_t* v_tail, uint32_t* status,
-                  hipStream_t stream) {
+                  int format, hipStream_t stream) {
   const size_t smem = compress_smem(P, D);
   if (!allow_smem((const void*)append_kernel, smem)) return -4;
   hipLaunchKernelGGL(append_kernel, dim3((unsigned)B * H), dim3(kCompressThreads), smem, stream, k_new, v_new,
                      page_table, max_pages, seq_lens, H, P, D, num_pages, units, pool, pool_cap, cursor, k_tail,
-                     v_tail, status);
+                     v_tail, status, format);
   if (hipGetLastError() != hipSuccess) return -4;
   hipLaunchKernelGGL(bump_lens_kernel, dim3((unsigned)(B + 255) / 256), dim3(256), 0, stream, seq_lens, B,
                      max_pages * P);

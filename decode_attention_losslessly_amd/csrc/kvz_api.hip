@@ -4,6 +4,7 @@
 
 #include "kvz.h"
 #include "kvz_device.hpp"
+#include "zf.hpp"
 
 namespace kvz {
 int launch_decompress(const uint8_t* units, const uint16_t* pool, const int32_t* page_ids, int n, int H, int P,
@@ -11,11 +12,18 @@ int launch_decompress(const uint8_t* units, const uint16_t* pool, const int32_t*
                       hipStream_t stream);
 int launch_compress(const uint16_t* k_src, const uint16_t* v_src, const int32_t* ids, int n, int H, int P, int D,
                     int num_pages, uint8_t* units, uint16_t* pool, int64_t pool_cap, uint64_t* cursor,
-                    uint32_t* status, hipStream_t stream);
+                    uint32_t* status, int format, hipStream_t stream);
 int launch_append(const uint16_t* k_new, const uint16_t* v_new, const int32_t* page_table, int max_pages,
                   int32_t* seq_lens, int B, int H, int P, int D, int num_pages, uint8_t* units, uint16_t* pool,
                   int64_t pool_cap, uint64_t* cursor, uint16_t* k_tail, uint16_t* v_tail, uint32_t* status,
-                  hipStream_t stream);
+                  int format, hipStream_t stream);
+int launch_attn_zf(const uint16_t* q, const uint8_t* units, const uint16_t* pool, int64_t pool_cap,
+                   const uint16_t* k_tail, const uint16_t* v_tail, const int32_t* page_table, int max_pages,
+                   const int32_t* seq_lens, int B, int H, int D, int P, int num_pages, int S, int C, float scale,
+                   float* ws_acc, float* ws_ml, uint32_t* status, hipStream_t stream);
+int launch_decompress_zf(const uint8_t* units, const uint16_t* pool, int64_t pool_cap, const int32_t* page_ids, int n,
+                         int H, int P, int D, int num_pages, uint16_t* k_dst, uint16_t* v_dst, uint32_t* status,
+                         hipStream_t stream);
 int launch_attn_mha(const uint16_t* q, const uint8_t* units, const uint16_t* pool, const uint16_t* k_tail,
                     const uint16_t* v_tail, const int32_t* page_table, int max_pages, const int32_t* seq_lens,
                     int B, int H, int D, int P, int num_pages, int S, int C, float scale, float* ws_acc,
@@ -63,7 +71,8 @@ bool shape_ok(int P, int D) { return P > 0 && P % 16 == 0 && D > 0 && D % 64 == 
 
 bool cache_ok(const kvz_cache* c) {
   return c && c->units && c->status && shape_ok(c->page_size, c->head_dim) && c->num_kv_heads > 0 &&
-         c->num_pages >= 0 && c->max_batch >= 0 && c->esc_capacity >= 0 && c->esc_cursor;
+         c->num_pages >= 0 && c->max_batch >= 0 && c->esc_capacity >= 0 && c->esc_cursor &&
+         (c->format == KVZ_FORMAT_ESCAPE || c->format == KVZ_FORMAT_ZIPFUSION);
 }
 
 hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
@@ -73,6 +82,12 @@ hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 extern "C" {
 
 size_t kvz_unit_bytes(int32_t P, int32_t D) { return shape_ok(P, D) ? kvz::unit_bytes(P, D) : 0; }
+size_t kvz_unit_bytes_for(int32_t format, int32_t P, int32_t D) {
+  if (!shape_ok(P, D)) return 0;
+  if (format == KVZ_FORMAT_ESCAPE) return kvz::unit_bytes(P, D);
+  if (format == KVZ_FORMAT_ZIPFUSION) return kvz::zf_unit_bytes(P, D);
+  return 0;
+}
 size_t kvz_meta_bytes(int32_t P, int32_t D) { return shape_ok(P, D) ? kvz::meta_bytes(P, D) : 0; }
 int32_t kvz_inline_capacity(int32_t P, int32_t D) { return shape_ok(P, D) ? kvz::inline_capacity(P, D) : 0; }
 
@@ -97,7 +112,8 @@ int kvz_compress_pages(const kvz_cache* c, const uint16_t* k_src, const uint16_t
   if ((size_t)c->page_size * c->head_dim > 32768) return KVZ_ERR_UNSUPPORTED;
   if (n == 0) return KVZ_OK;
   return kvz::launch_compress(k_src, v_src, ids, n, c->num_kv_heads, c->page_size, c->head_dim, c->num_pages,
-                              c->units, c->esc_pool, c->esc_capacity, c->esc_cursor, c->status, as_stream(stream));
+                              c->units, c->esc_pool, c->esc_capacity, c->esc_cursor, c->status, c->format,
+                              as_stream(stream));
 }
 
 int kvz_append_token(const kvz_cache* c, const uint16_t* k_new, const uint16_t* v_new, const int32_t* page_table,
@@ -109,7 +125,7 @@ int kvz_append_token(const kvz_cache* c, const uint16_t* k_new, const uint16_t* 
   if (B == 0) return KVZ_OK;
   return kvz::launch_append(k_new, v_new, page_table, max_pages, seq_lens, B, c->num_kv_heads, c->page_size,
                             c->head_dim, c->num_pages, c->units, c->esc_pool, c->esc_capacity, c->esc_cursor,
-                            c->k_tail, c->v_tail, c->status, as_stream(stream));
+                            c->k_tail, c->v_tail, c->status, c->format, as_stream(stream));
 }
 
 static int check_attention_shape(int B, int Hq, int Hkv, int D, int P, int max_pages) {
@@ -138,7 +154,12 @@ int kvz_decode_attention_splits(const uint16_t* q, const kvz_cache* c, const int
   float* ws_acc = reinterpret_cast<float*>(workspace);
   float* ws_ml = ws_acc + (size_t)B * H_q * S * D;
   const float scale = sm_scale * 1.4426950408889634f;
-  if (H_q == H)
+  if (c->format == KVZ_FORMAT_ZIPFUSION) {
+    if (H_q != H) return KVZ_ERR_UNSUPPORTED;
+    rc = kvz::launch_attn_zf(q, c->units, c->esc_pool, c->esc_capacity, c->k_tail, c->v_tail, page_table, max_pages,
+                             seq_lens, B, H, D, P, c->num_pages, S, C, scale, ws_acc, ws_ml, c->status,
+                             as_stream(stream));
+  } else if (H_q == H)
     rc = kvz::launch_attn_mha(q, c->units, c->esc_pool, c->k_tail, c->v_tail, page_table, max_pages, seq_lens, B, H,
                               D, P, c->num_pages, S, C, scale, ws_acc, ws_ml, c->status, as_stream(stream));
   else
@@ -225,6 +246,13 @@ int kvz_decompress_pages(const kvz_cache* c, const int32_t* page_ids, int32_t n,
   const int D = c->head_dim;
   if ((D != 64 && D != 128) || (lane_map == 1 && D != 128)) return KVZ_ERR_UNSUPPORTED;
   if (n == 0) return KVZ_OK;
+  if (c->format == KVZ_FORMAT_ZIPFUSION) {
+    if (lane_map != 0) return KVZ_ERR_UNSUPPORTED;
+    const int rc = kvz::launch_decompress_zf(c->units, c->esc_pool, c->esc_capacity, page_ids, n, c->num_kv_heads,
+                                             c->page_size, D, c->num_pages, k_dst, v_dst, c->status,
+                                             as_stream(stream));
+    return rc == -2 ? KVZ_ERR_UNSUPPORTED : (rc ? KVZ_ERR_HIP : KVZ_OK);
+  }
   const int rc = kvz::launch_decompress(c->units, c->esc_pool, page_ids, n, c->num_kv_heads, c->page_size, D,
                                         c->num_pages, lane_map, k_dst, v_dst, c->status, as_stream(stream));
   return rc == -2 ? KVZ_ERR_UNSUPPORTED : (rc ? KVZ_ERR_HIP : KVZ_OK);

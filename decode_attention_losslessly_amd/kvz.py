@@ -17,11 +17,12 @@ LIB_PATH = os.path.join(_HERE, "libkvz.so")
 
 KVZ_OK, KVZ_ERR_INVALID_ARG, KVZ_ERR_UNSUPPORTED, KVZ_ERR_WORKSPACE, KVZ_ERR_HIP = 0, -1, -2, -3, -4
 STATUS_ESC_POOL_FULL, STATUS_BAD_PAGE_ID, STATUS_SEQ_TOO_LONG = 1, 2, 4
+FORMAT_ESCAPE, FORMAT_ZIPFUSION = 0, 1
 
 EXPORTS = ("kvz_unit_bytes", "kvz_meta_bytes", "kvz_inline_capacity", "kvz_workspace_bytes", "kvz_num_splits",
            "kvz_compress_pages", "kvz_append_token", "kvz_decode_attention", "kvz_decode_attention_dense",
            "kvz_decompress_pages", "kvz_strerror", "kvz_decode_attention_splits",
-           "kvz_decode_attention_dense_splits", "kvz_merge_splits")
+           "kvz_decode_attention_dense_splits", "kvz_merge_splits", "kvz_unit_bytes_for")
 
 
 class KvzError(RuntimeError):
@@ -32,7 +33,7 @@ class KvzError(RuntimeError):
 
 class _CacheStruct(ctypes.Structure):
     _fields_ = [("page_size", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
-                ("num_pages", ctypes.c_int32), ("max_batch", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("num_pages", ctypes.c_int32), ("max_batch", ctypes.c_int32), ("format", ctypes.c_int32),
                 ("units", ctypes.c_void_p), ("esc_pool", ctypes.c_void_p), ("esc_capacity", ctypes.c_int64),
                 ("esc_cursor", ctypes.c_void_p), ("k_tail", ctypes.c_void_p), ("v_tail", ctypes.c_void_p),
                 ("status", ctypes.c_void_p)]
@@ -52,6 +53,7 @@ def lib() -> ctypes.CDLL:
         cp = ctypes.POINTER(_CacheStruct)
         sig = {
             "kvz_unit_bytes": (sz, [i32, i32]),
+            "kvz_unit_bytes_for": (sz, [i32, i32, i32]),
             "kvz_meta_bytes": (sz, [i32, i32]),
             "kvz_inline_capacity": (i32, [i32, i32]),
             "kvz_workspace_bytes": (sz, [i32, i32, i32, i32, i32, i32, i32]),
@@ -98,8 +100,8 @@ def _check(rc: int, what: str):
 
 
 # ---------------------------------------------------------------- sizes
-def unit_bytes(P: int, D: int) -> int:
-    return int(lib().kvz_unit_bytes(P, D))
+def unit_bytes(P: int, D: int, fmt: int = FORMAT_ESCAPE) -> int:
+    return int(lib().kvz_unit_bytes_for(fmt, P, D))
 
 
 def meta_bytes(P: int, D: int) -> int:
@@ -133,11 +135,12 @@ class Cache:
     k_tail: torch.Tensor       # int16 [max_batch, H, P, D]
     v_tail: torch.Tensor
     status: torch.Tensor       # int32 [1]
+    fmt: int = FORMAT_ESCAPE   # FORMAT_ESCAPE or FORMAT_ZIPFUSION (esc_pool then holds raw blocks)
 
     @classmethod
     def allocate(cls, P: int, H: int, D: int, num_pages: int, max_batch: int, esc_capacity: int,
-                 device="cuda") -> "Cache":
-        U = unit_bytes(P, D)
+                 device="cuda", fmt: int = FORMAT_ESCAPE) -> "Cache":
+        U = unit_bytes(P, D, fmt)
         if U == 0:
             raise KvzError(KVZ_ERR_UNSUPPORTED, "Cache.allocate")
         z = dict(device=device)
@@ -147,14 +150,14 @@ class Cache:
                    esc_cursor=torch.zeros(1, dtype=torch.int64, **z),
                    k_tail=torch.zeros((max_batch, H, P, D), dtype=torch.int16, **z),
                    v_tail=torch.zeros((max_batch, H, P, D), dtype=torch.int16, **z),
-                   status=torch.zeros(1, dtype=torch.int32, **z))
+                   status=torch.zeros(1, dtype=torch.int32, **z), fmt=fmt)
 
     @property
     def esc_capacity(self) -> int:
         return int(self.esc_pool.numel())
 
     def struct(self) -> _CacheStruct:
-        return _CacheStruct(self.P, self.H, self.D, self.num_pages, self.max_batch, 0, self.units.data_ptr(),
+        return _CacheStruct(self.P, self.H, self.D, self.num_pages, self.max_batch, self.fmt, self.units.data_ptr(),
                             self.esc_pool.data_ptr(), self.esc_capacity, self.esc_cursor.data_ptr(),
                             self.k_tail.data_ptr(), self.v_tail.data_ptr(), self.status.data_ptr())
 

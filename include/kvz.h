@@ -45,6 +45,21 @@
  *   tail      per request row r and head h, P raw BF16 rows [P][D] (token-major, K and V
  *             alike) holding the L mod P newest tokens
  *
+ * Second format, kvz_cache.format = KVZ_FORMAT_ZIPFUSION: ZipFusion's own block format
+ * (§III.B), for comparison with the pages' design. Multi-head attention only.
+ *   block     512 consecutive storage positions of a tile (same storage order as above: K
+ *             token-major, V dim-major); compressed when every exponent lies in [b, b+15],
+ *             b = the block's smallest exponent rounded down to even, else kept raw
+ *   value     low byte (lowest exponent bit + 7 mantissa bits) and a 4-bit code
+ *             sign << 3 | (e/2 - b/2); compressed block = 512 low bytes then 256 code bytes
+ *             (even position in the low nibble), 768 bytes
+ *   unit      kvz_unit_bytes_for(KVZ_FORMAT_ZIPFUSION, P, D) bytes: block bytes (b/2, or 0xFF =
+ *             raw) for K's blocks of every tile then V's, padded to 8 bytes; u64 pool offset (u16
+ *             elements) of the unit's raw blocks, all ones if none; zero padding to a multiple of
+ *             128; then one 768-byte slot per block in the same order (zero for a raw block)
+ *   pool      esc_pool holds raw blocks, 512 values each, a unit's raw blocks contiguous in
+ *             block order; esc_cursor must start at a multiple of 8
+ *
  * Conventions for every entry point:
  *   - pointers are device pointers unless marked (host); the caller owns all memory;
  *   - calls are asynchronous on `stream` (a hipStream_t passed as void*; NULL = the default
@@ -73,6 +88,11 @@ enum {
 };
 
 enum {
+  KVZ_FORMAT_ESCAPE = 0,     /* exponent offsets with escapes (the format described above) */
+  KVZ_FORMAT_ZIPFUSION = 1   /* ZipFusion's block format (see above) */
+};
+
+enum {
   KVZ_STATUS_ESC_POOL_FULL = 1u,  /* a unit's escapes did not fit the pool; its escaped
                                      values decode to unspecified values */
   KVZ_STATUS_BAD_PAGE_ID = 2u,    /* a page id outside [0, num_pages) was met and skipped */
@@ -86,7 +106,7 @@ typedef struct kvz_cache {
   int32_t head_dim;      /* D: multiple of 64 */
   int32_t num_pages;     /* unit slots per head */
   int32_t max_batch;     /* tail rows */
-  int32_t reserved;
+  int32_t format;        /* KVZ_FORMAT_* of the units and the pool */
   uint8_t* units;        /* [num_pages][H][kvz_unit_bytes(P, D)], 256-byte aligned */
   uint16_t* esc_pool;    /* escape pool, esc_capacity u16 elements */
   int64_t esc_capacity;
@@ -98,6 +118,8 @@ typedef struct kvz_cache {
 
 /* Sizes of the format (host functions, no device work). */
 size_t kvz_unit_bytes(int32_t P, int32_t D);
+/* unit size in the given format (0 for an unsupported shape or format) */
+size_t kvz_unit_bytes_for(int32_t format, int32_t P, int32_t D);
 size_t kvz_meta_bytes(int32_t P, int32_t D);
 int32_t kvz_inline_capacity(int32_t P, int32_t D);
 

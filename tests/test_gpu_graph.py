@@ -18,7 +18,7 @@ N_STEPS = 24
 
 def _copy(c: kvz.Cache) -> kvz.Cache:
     return kvz.Cache(c.P, c.H, c.D, c.num_pages, c.max_batch, c.units.clone(), c.esc_pool.clone(),
-                     c.esc_cursor.clone(), c.k_tail.clone(), c.v_tail.clone(), c.status.clone())
+                     c.esc_cursor.clone(), c.k_tail.clone(), c.v_tail.clone(), c.status.clone(), c.fmt)
 
 
 @pytest.mark.parametrize("cfg,Hq,Hkv,lens", [(3, 4, 4, [100, 37, 250]), (4, 8, 2, [60, 17, 200])])
