@@ -54,6 +54,8 @@ def parse():
     # the first ~30 launches after set-up run up to 20 % slower while the clocks settle
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--config", type=int, default=3, help="workload number (3 = the headline workload)")
+    ap.add_argument("--format", choices=["escape", "zipfusion"], default="escape",
+                    help="cache format: exponent offsets with escapes (the library's), or ZipFusion's blocks")
     ap.add_argument("--batch", type=int, default=None, help="override the workload's batch size")
     ap.add_argument("--context", type=int, default=None, help="override the workload's context length")
     ap.add_argument("--no-dense", action="store_true", help="skip the uncompressed baseline")
@@ -107,8 +109,17 @@ def main() -> int:
     kd, vd = t16(kp), t16(vp)
     ids = np.array([w.page_table[r, i] for r in range(B) for i in range(int(L0[r]) // P)], np.int32)
     n_units = len(ids) * H
-    frac = 0.6 if w.k_dist == "log_uniform" else 0.02
-    cache = kvz.Cache.allocate(P, H, D, w.num_pages, B, int(n_units * 2 * P * D * frac) + (1 << 20), device=dev)
+    fmt = kvz.FORMAT_ZIPFUSION if args.format == "zipfusion" else kvz.FORMAT_ESCAPE
+    if fmt == kvz.FORMAT_ZIPFUSION:
+        if Hq != H:
+            print("the ZipFusion-format kernel is multi-head only", file=sys.stderr, flush=True)
+            return 2
+        w.name = f"{w.name}+zipfusion"
+        pool_cap = (n_units + B * H) * 2 * P * D          # room for every block raw
+    else:
+        frac = 0.6 if w.k_dist == "log_uniform" else 0.02
+        pool_cap = int(n_units * 2 * P * D * frac) + (1 << 20)
+    cache = kvz.Cache.allocate(P, H, D, w.num_pages, B, pool_cap, device=dev, fmt=fmt)
     ids_d = t16(ids)
     torch.cuda.synchronize()
     c0 = time.perf_counter()
@@ -139,15 +150,24 @@ def main() -> int:
     log(f"compressed {n_units} units in {compress_s * 1e3:.1f} ms")
 
     # ---- algorithmic bytes of one split-kernel launch
-    U = kvz.unit_bytes(P, D)
-    G = D // 64
-    hdr = 2 * P * G
+    U = kvz.unit_bytes(P, D, fmt)
     full = (w.seq_lens // P).astype(np.int64)
     live = np.array([w.page_table[r, i] for r in range(B) for i in range(int(full[r]))], np.int64)
-    heads = cache.units[:, :, hdr:hdr + 16][torch.from_numpy(live).to(dev)].contiguous()
-    cnt = heads[:, :, :8].view(torch.int32).to(torch.int64).sum(-1)
-    off = heads[:, :, 8:16].view(torch.int64).squeeze(-1)
-    pool_esc = int(torch.where(off != -1, cnt, torch.zeros_like(cnt)).sum().item())
+    if fmt == kvz.FORMAT_ZIPFUSION:
+        # pool elements read = raw blocks of the live units (512 values each)
+        nb = 2 * (P // 16) * (D // 32)
+        metas = cache.units[:, :, :nb][torch.from_numpy(live).to(dev)]
+        n_raw = int((metas == 0xFF).sum().item())
+        pool_esc = n_raw * 512
+        raw_frac = n_raw / max(1, metas.numel())
+    else:
+        G = D // 64
+        hdr = 2 * P * G
+        heads = cache.units[:, :, hdr:hdr + 16][torch.from_numpy(live).to(dev)].contiguous()
+        cnt = heads[:, :, :8].view(torch.int32).to(torch.int64).sum(-1)
+        off = heads[:, :, 8:16].view(torch.int64).squeeze(-1)
+        pool_esc = int(torch.where(off != -1, cnt, torch.zeros_like(cnt)).sum().item())
+        raw_frac = None
     S = kvz.num_splits(B, Hq, H, D, P, w.max_pages)
     units_bytes = int(full.sum()) * H * U
     tail_bytes = int((w.seq_lens % P).sum()) * H * D * 2 * 2
@@ -218,20 +238,21 @@ def main() -> int:
     attn_mean = float(np.mean(attn_us))
     achieved = comp_bytes / (attn_mean * 1e-6) / 1e9
     traffic = None
-    ksrc = "attn_mha.hip" if Hq == H else "attn_gqa.hip"
+    ksrc = "attn_zf.hip" if fmt == kvz.FORMAT_ZIPFUSION else ("attn_mha.hip" if Hq == H else "attn_gqa.hip")
     tfile = os.path.join(ROOT, "profiles", f"traffic_{w.name}.json")
     if os.path.exists(tfile):
         t = json.load(open(tfile))
         if t.get("source_digest") == source_digest(ksrc):
             traffic = t.get("bytes_per_launch")
-    kname = f"attn_mha_kernel<{D}>" if Hq == H else "attn_gqa_kernel"
+    kname = f"attn_zf_kernel<{D}>" if fmt == kvz.FORMAT_ZIPFUSION else (f"attn_mha_kernel<{D}>" if Hq == H
+                                                                        else "attn_gqa_kernel")
     roofline = dict(kernel=kname, bound="hbm",
                     achieved=round(achieved, 1), peak=PEAK_HBM_GBPS, unit="GB/s",
                     frac=round(achieved / PEAK_HBM_GBPS, 4), traffic=traffic,
                     algorithmic_bytes_per_launch=comp_bytes, attn_us_mean=round(attn_mean, 2))
 
     cpu = None
-    if not args.no_cpu:
+    if not args.no_cpu and fmt == kvz.FORMAT_ESCAPE:   # the CPU oracle baseline decodes the library's format
         cpu = cpu_baseline(w, kp, vp, min(args.cpu_requests, B), log)
 
     res = {
@@ -258,7 +279,9 @@ def main() -> int:
         "compressed_bytes": comp_bytes,
         "dense_kv_bytes": dense_kv_bytes,
         "compression_ratio": round(comp_bytes / dense_bytes, 4),
+        "format": args.format,
         "pool_escapes": pool_esc,
+        "raw_block_fraction": raw_frac,
         "dense": dense,
         "speedup_vs_dense": round(dense["ms_per_step"] / ms_per_step, 4) if dense else None,
         "roofline": roofline,
@@ -266,7 +289,7 @@ def main() -> int:
         "append_us": round(append_us, 1) if append_us is not None else None,
         "compress_gbps_dense_input": round(len(ids) * H * P * D * 4 / compress_s / 1e9, 1),
         "gpu": f"{torch.cuda.get_device_name(0)} ({torch.cuda.get_device_properties(0).gcnArchName})",
-        "source_digest": source_digest("attn_mha.hip" if Hq == H else "attn_gqa.hip"),
+        "source_digest": source_digest(ksrc),
     }
     print(json.dumps(res), flush=True)
     return 0

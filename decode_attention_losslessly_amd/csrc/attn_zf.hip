@@ -3,9 +3,11 @@
 // (request, head, split), lane l holding K pieces l + 64 i and V dims l + 64 s, the next tile's
 // loads issued before the current tile is computed, scores / softmax / P.V from mha_core.hpp.
 // Compressed blocks are rebuilt in registers (§III.C of the ZipFusion summary: four high bytes
-// per 32-bit add, combined with the kept low bytes). A unit with any raw block is skipped by
-// the main loop and added after it, its raw blocks read from the pool (the pages' format keeps
-// such blocks uncompressed and reads them without a rebuild).
+// per 32-bit add, combined with the kept low bytes). A raw block's pieces are read from the pool
+// when its tile is computed (the pages' format keeps such blocks uncompressed and uses them
+// without a rebuild): a load that depends on the unit's meta, whose latency the other waves of
+// the SIMD cover. Handling them in the main loop measured faster than a second sweep after it,
+// because with this format most units hold some raw block.
 //
 // Also the test kernel that writes the rebuilt values of whole units back out.
 #include "mha_core.hpp"
@@ -75,20 +77,18 @@ __device__ __forceinline__ void zf_rebuild(const ZStage<D>& stg, int P, const ui
   }
 }
 
-// Returns false, leaving the state untouched, when the unit has raw blocks and RAW is off.
-template <int D, bool RAW>
-__device__ __forceinline__ bool zf_compute(MhaState<D>& st, const ZStage<D>& stg, int P, const uint16_t* pool,
+template <int D>
+__device__ __forceinline__ void zf_compute(MhaState<D>& st, const ZStage<D>& stg, int P, const uint16_t* pool,
                                            int64_t pool_cap, float scale, int lane) {
-  if (!stg.ok) return true;
-  if (!RAW && uniform(stg.rawlo) != 0xFFFFFFFFu) return false;
+  if (!stg.ok) return;
   uint32_t kp[D / 8], vp[D / 8];
-  zf_rebuild<D, RAW>(stg, P, pool, pool_cap, lane, kp, vp);
+  if (uniform(stg.rawlo) == 0xFFFFFFFFu) zf_rebuild<D, false>(stg, P, pool, pool_cap, lane, kp, vp);
+  else zf_rebuild<D, true>(stg, P, pool, pool_cap, lane, kp, vp);
   float sc[D / 64];
   mha_scores<D>(st, kp, scale, sc);
   uint32_t phi[8], plo[8];
   mha_softmax<D>(st, sc, phi, plo);
   mha_accumulate_v<D>(st, vp, phi, plo);
-  return true;
 }
 
 template <int D>
@@ -132,12 +132,7 @@ __global__ __launch_bounds__(64 * kZfWaves) void attn_zf_kernel(
   const int32_t* pt_row = page_table + (size_t)r * max_pages;
   const int T = P / kTile;
   const int nsteps = (p1 > p0 ? p1 - p0 : 0) * T;
-  int first_skip = -1, last_skip = -1;
   bool bad = false;
-  auto note = [&](const ZStage<D>& stg) {
-    if (first_skip < 0) first_skip = stg.page;
-    last_skip = stg.page;
-  };
   if (nsteps > 0) {
     int ln = 0, lp = p0, lt = 0;
     const int last = nsteps - 1;
@@ -157,44 +152,16 @@ __global__ __launch_bounds__(64 * kZfWaves) void attn_zf_kernel(
       advance();
       pid = sload<int32_t>(pt_row + lp);
       bad |= !a.ok;
-      if (!zf_compute<D, false>(st, a, P, pool, pool_cap, scale, lane)) note(a);
+      zf_compute<D>(st, a, P, pool, pool_cap, scale, lane);
       if (i + 1 >= nsteps) break;
       zf_issue<D>(a, units, pid, lp, lt, H, h, P, num_pages, lane);
       advance();
       pid = sload<int32_t>(pt_row + lp);
       bad |= !b.ok;
-      if (!zf_compute<D, false>(st, b, P, pool, pool_cap, scale, lane)) note(b);
+      zf_compute<D>(st, b, P, pool, pool_cap, scale, lane);
     }
   }
   if (bad && lane == 0) atomicOr(status, kStatusBadPage);
-  if (first_skip >= 0) {
-    // units with raw blocks: the recorded pages, then any between them
-    auto do_page = [&](int page) {
-      const int pid = sload<int32_t>(pt_row + page);
-      for (int t = 0; t < T; ++t) {
-        ZStage<D> a;
-        zf_issue<D>(a, units, pid, page, t, H, h, P, num_pages, lane);
-        zf_compute<D, true>(st, a, P, pool, pool_cap, scale, lane);
-      }
-    };
-    do_page(first_skip);
-    if (last_skip != first_skip) do_page(last_skip);
-    for (int c0 = first_skip + 1; c0 < last_skip; c0 += 64) {
-      const int pg = c0 + lane;
-      bool has_raw = false;
-      if (pg < last_skip) {
-        const int pid = pt_row[pg];
-        if (pid >= 0 && pid < num_pages)
-          has_raw = zf_raw_offset(units + ((size_t)pid * H + h) * zf_unit_bytes(P, D), P, D) != kInline;
-      }
-      uint64_t todo = ballot(has_raw);
-      while (todo) {
-        const int page = c0 + __builtin_ctzll(todo);
-        todo &= todo - 1;
-        do_page(page);
-      }
-    }
-  }
   if (s == Sr - 1 && rows > 0) {
     const size_t toff = ((size_t)r * H + h) * P * D;
     mha_tail<D>(st, k_tail + toff, v_tail + toff, rows, scale, lane);
