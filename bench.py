@@ -295,6 +295,16 @@ def main() -> int:
     return 0
 
 
+def _host_cpu() -> str:
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w, kp, vp, n_req, log):
     """The C oracle (scalar decode of the compressed units + fp64 attention, OpenMP over rows) on
     the rows of the first n_req requests; scaled to the whole batch."""
@@ -324,10 +334,22 @@ def cpu_baseline(w, kp, vp, n_req, log):
     threads = c_oracle.num_threads()
     step_s = dt * (w.B * w.Hq) / len(rows)
     log(f"cpu oracle: {len(rows)} rows in {dt:.2f}s on {threads} threads (encode set-up {enc_s:.1f}s)")
+    # the same oracle on one core, over the first request's rows
+    one = rows[:w.Hq]
+    c_oracle.set_num_threads(1)
+    t0 = time.perf_counter()
+    c_oracle.decode_attention_rows(q, units, pool_s, w.page_table, L, tk, tv, w.Hkv, w.P, w.sm_scale, one)
+    dt1 = time.perf_counter() - t0
+    c_oracle.set_num_threads(threads)
+    step1_s = dt1 * (w.B * w.Hq) / len(one)
+    log(f"cpu oracle on 1 core: {len(one)} rows in {dt1:.2f}s")
     return {"value": round(w.B / step_s, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"{len(rows)} of {w.B * w.Hq} (request, head) rows: scalar decode of their compressed "
                       f"pages + fp64 attention, {dt:.2f}s wall, scaled to the full batch",
-            "cpu_seconds": round(dt * threads, 2)}
+            "cpu_seconds": round(dt * threads, 2),
+            "one_core": {"value": round(w.B / step1_s, 3), "unit": "tokens/s",
+                         "sample": f"{len(one)} rows of request 0, {dt1:.2f}s, scaled to the full batch"},
+            "host_cpu": _host_cpu()}
 
 
 if __name__ == "__main__":

@@ -317,6 +317,15 @@ void kvzo_dense_attention_rows(const uint16_t* q, const uint16_t* k_pages, const
   }
 }
 
+/* threads the parallel loops use from now on (n <= 0: the OpenMP default) */
+void kvzo_set_num_threads(int n) {
+#ifdef _OPENMP
+  if (n > 0) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
+
 int kvzo_num_threads(void) {
 #ifdef _OPENMP
   return omp_get_max_threads();

@@ -150,3 +150,7 @@ def dense_attention_rows(q, k_pages, v_pages, page_table, seq_lens, sm_scale, ro
 
 def num_threads() -> int:
     return int(lib().kvzo_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    lib().kvzo_set_num_threads(int(n))
