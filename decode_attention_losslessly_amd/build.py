@@ -14,7 +14,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 OUT = os.path.join(HERE, "libkvz.so")
 SOURCES = ["kvz_api.hip", "compress.hip", "decompress.hip", "attn_mha.hip", "attn_gqa.hip", "attn_dense.hip",
-           "merge.hip", "attn_zf.hip"]
+           "merge.hip", "attn_zf.hip", "pool.hip"]
 ARCH = os.environ.get("KVZ_OFFLOAD_ARCH", "gfx950")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-mcode-object-version=5",

@@ -131,10 +131,11 @@ __device__ __forceinline__ void gqa_c_issue(GqaCStage& st, const uint8_t* units,
 template <bool POOL>
 __device__ __forceinline__ bool gqa_c_compute(GqaState& st, const GqaCStage& stg, int P, uint32_t& krank,
                                               uint32_t& vrank, uint16_t* esc_lds, uint32_t* vlds,
-                                              const uint16_t* pool, float scale, int lane) {
+                                              const uint16_t* pool, int64_t pool_cap, float scale, int lane) {
   if (!stg.ok) return true;
-  const UnitHeader hdr = header_from_meta<128>(stg.meta);
+  UnitHeader hdr = header_from_meta<128>(stg.meta);
   if (!POOL && hdr.off != kInline) return false;
+  if (POOL) clamp_to_pool(hdr, pool_cap);
   if (stg.tile == 0) { krank = 0; vrank = 0; }
   uint32_t kp[16];
   decode_k<128>(stg.k, kp);
@@ -263,9 +264,10 @@ __device__ __forceinline__ void gqa_store(const GqaState& st, int r, int Hq, int
 // loop, when the pipeline's registers are free.
 __global__ __launch_bounds__(64 * kGqaWaves) KVZ_GQA_OCCUPANCY void attn_gqa_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ units, const uint16_t* __restrict__ pool,
-    const uint16_t* __restrict__ k_tail, const uint16_t* __restrict__ v_tail, const int32_t* __restrict__ page_table,
-    int max_pages, const int32_t* __restrict__ seq_lens, int B, int Hq, int H, int P, int num_pages, int S, int C,
-    float scale, float* __restrict__ ws_acc, float* __restrict__ ws_ml, uint32_t* __restrict__ status) {
+    int64_t pool_cap, const uint16_t* __restrict__ k_tail, const uint16_t* __restrict__ v_tail,
+    const int32_t* __restrict__ page_table, int max_pages, const int32_t* __restrict__ seq_lens, int B, int Hq, int H,
+    int P, int num_pages, int S, int C, float scale, float* __restrict__ ws_acc, float* __restrict__ ws_ml,
+    uint32_t* __restrict__ status) {
   __shared__ uint16_t esc_all[kGqaWaves][esc_lds_elems<128>()];
   __shared__ uint32_t vlds_all[kGqaWaves][128 * 8];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -322,13 +324,13 @@ __global__ __launch_bounds__(64 * kGqaWaves) KVZ_GQA_OCCUPANCY void attn_gqa_ker
       advance();
       pid = sload<int32_t>(pt_row + lp);
       bad |= !a.ok;
-      if (!gqa_c_compute<false>(st, a, P, krank, vrank, esc_lds, vlds, pool, scale, lane)) note(a);
+      if (!gqa_c_compute<false>(st, a, P, krank, vrank, esc_lds, vlds, pool, pool_cap, scale, lane)) note(a);
       if (i + 1 >= nsteps) break;
       gqa_c_issue(a, units, pid, lp, lt, H, h, P, num_pages, lane);
       advance();
       pid = sload<int32_t>(pt_row + lp);
       bad |= !b.ok;
-      if (!gqa_c_compute<false>(st, b, P, krank, vrank, esc_lds, vlds, pool, scale, lane)) note(b);
+      if (!gqa_c_compute<false>(st, b, P, krank, vrank, esc_lds, vlds, pool, pool_cap, scale, lane)) note(b);
     }
   }
   if (bad && lane == 0) atomicOr(status, kStatusBadPage);
@@ -339,7 +341,7 @@ __global__ __launch_bounds__(64 * kGqaWaves) KVZ_GQA_OCCUPANCY void attn_gqa_ker
       for (int t = 0; t < T; ++t) {
         GqaCStage a;
         gqa_c_issue(a, units, pid, page, t, H, h, P, num_pages, lane);
-        gqa_c_compute<true>(st, a, P, krank, vrank, esc_lds, vlds, pool, scale, lane);
+        gqa_c_compute<true>(st, a, P, krank, vrank, esc_lds, vlds, pool, pool_cap, scale, lane);
       }
     };
     do_page(first_skip);
@@ -449,13 +451,13 @@ static unsigned gqa_blocks(int B, int Hq, int H, int S) {
   return (unsigned)((items + kGqaWaves - 1) / kGqaWaves);
 }
 
-int launch_attn_gqa(const uint16_t* q, const uint8_t* units, const uint16_t* pool, const uint16_t* k_tail,
+int launch_attn_gqa(const uint16_t* q, const uint8_t* units, const uint16_t* pool, int64_t pool_cap, const uint16_t* k_tail,
                     const uint16_t* v_tail, const int32_t* page_table, int max_pages, const int32_t* seq_lens,
                     int B, int Hq, int H, int D, int P, int num_pages, int S, int C, float scale, float* ws_acc,
                     float* ws_ml, uint32_t* status, hipStream_t stream) {
   if (D != 128) return -2;
   hipLaunchKernelGGL(attn_gqa_kernel, dim3(gqa_blocks(B, Hq, H, S)), dim3(64 * kGqaWaves), 0, stream, q, units, pool,
-                     k_tail, v_tail, page_table, max_pages, seq_lens, B, Hq, H, P, num_pages, S, C, scale, ws_acc,
+                     pool_cap, k_tail, v_tail, page_table, max_pages, seq_lens, B, Hq, H, P, num_pages, S, C, scale, ws_acc,
                      ws_ml, status);
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }

@@ -57,12 +57,13 @@ __device__ __forceinline__ void mha_issue(MhaStage<D>& st, const uint8_t* units,
 // is off.
 template <int D, bool POOL>
 __device__ __forceinline__ bool mha_compute(MhaState<D>& st, const MhaStage<D>& stg, int P, uint32_t& krank,
-                                            uint32_t& vrank, uint16_t* lds, const uint16_t* pool, float scale,
-                                            int lane) {
+                                            uint32_t& vrank, uint16_t* lds, const uint16_t* pool, int64_t pool_cap,
+                                            float scale, int lane) {
   if (!stg.ok) return true;
   constexpr int VK = KRaw<D>::VK, NS = D / 64;
-  const UnitHeader hdr = header_from_meta<D>(stg.meta);
+  UnitHeader hdr = header_from_meta<D>(stg.meta);
   if (!POOL && hdr.off != kInline) return false;
+  if (POOL) clamp_to_pool(hdr, pool_cap);
   if (stg.tile == 0) { krank = 0; vrank = 0; }
   uint32_t kp[VK / 2];
   decode_k<D>(stg.k, kp);
@@ -88,9 +89,10 @@ __device__ __forceinline__ bool mha_compute(MhaState<D>& st, const MhaStage<D>& 
 template <int D>
 __global__ __launch_bounds__(64 * kWavesPerBlock) void attn_mha_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ units, const uint16_t* __restrict__ pool,
-    const uint16_t* __restrict__ k_tail, const uint16_t* __restrict__ v_tail, const int32_t* __restrict__ page_table,
-    int max_pages, const int32_t* __restrict__ seq_lens, int B, int H, int P, int num_pages, int S, int C,
-    float scale, float* __restrict__ ws_acc, float* __restrict__ ws_ml, uint32_t* __restrict__ status) {
+    int64_t pool_cap, const uint16_t* __restrict__ k_tail, const uint16_t* __restrict__ v_tail,
+    const int32_t* __restrict__ page_table, int max_pages, const int32_t* __restrict__ seq_lens, int B, int H, int P,
+    int num_pages, int S, int C, float scale, float* __restrict__ ws_acc, float* __restrict__ ws_ml,
+    uint32_t* __restrict__ status) {
   __shared__ uint16_t lds_all[kWavesPerBlock][esc_lds_elems<D>()];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int item = (int)uniform(blockIdx.x * kWavesPerBlock + wave);
@@ -155,13 +157,13 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void attn_mha_kernel(
       advance();
       pid = sload<int32_t>(pt_row + lp);
       bad |= !a.ok;
-      if (!mha_compute<D, false>(st, a, P, krank, vrank, lds, pool, scale, lane)) note(a);
+      if (!mha_compute<D, false>(st, a, P, krank, vrank, lds, pool, pool_cap, scale, lane)) note(a);
       if (i + 1 >= nsteps) break;
       mha_issue<D>(a, units, pid, lp, lt, H, h, P, num_pages, lane);
       advance();
       pid = sload<int32_t>(pt_row + lp);
       bad |= !b.ok;
-      if (!mha_compute<D, false>(st, b, P, krank, vrank, lds, pool, scale, lane)) note(b);
+      if (!mha_compute<D, false>(st, b, P, krank, vrank, lds, pool, pool_cap, scale, lane)) note(b);
     }
   }
   if (bad && lane == 0) atomicOr(status, kStatusBadPage);
@@ -172,7 +174,7 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void attn_mha_kernel(
       for (int t = 0; t < T; ++t) {
         MhaStage<D> a;
         mha_issue<D>(a, units, pid, page, t, H, h, P, num_pages, lane);
-        mha_compute<D, true>(st, a, P, krank, vrank, lds, pool, scale, lane);
+        mha_compute<D, true>(st, a, P, krank, vrank, lds, pool, pool_cap, scale, lane);
       }
     };
     do_page(first_skip);
@@ -214,17 +216,17 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void attn_mha_kernel(
   }
 }
 
-int launch_attn_mha(const uint16_t* q, const uint8_t* units, const uint16_t* pool, const uint16_t* k_tail,
+int launch_attn_mha(const uint16_t* q, const uint8_t* units, const uint16_t* pool, int64_t pool_cap, const uint16_t* k_tail,
                     const uint16_t* v_tail, const int32_t* page_table, int max_pages, const int32_t* seq_lens,
                     int B, int H, int D, int P, int num_pages, int S, int C, float scale, float* ws_acc,
                     float* ws_ml, uint32_t* status, hipStream_t stream) {
   const int items = B * H * S;
   dim3 grid((unsigned)(items + kWavesPerBlock - 1) / kWavesPerBlock), block(64 * kWavesPerBlock);
   if (D == 128)
-    hipLaunchKernelGGL((attn_mha_kernel<128>), grid, block, 0, stream, q, units, pool, k_tail, v_tail, page_table,
+    hipLaunchKernelGGL((attn_mha_kernel<128>), grid, block, 0, stream, q, units, pool, pool_cap, k_tail, v_tail, page_table,
                        max_pages, seq_lens, B, H, P, num_pages, S, C, scale, ws_acc, ws_ml, status);
   else if (D == 64)
-    hipLaunchKernelGGL((attn_mha_kernel<64>), grid, block, 0, stream, q, units, pool, k_tail, v_tail, page_table,
+    hipLaunchKernelGGL((attn_mha_kernel<64>), grid, block, 0, stream, q, units, pool, pool_cap, k_tail, v_tail, page_table,
                        max_pages, seq_lens, B, H, P, num_pages, S, C, scale, ws_acc, ws_ml, status);
   else
     return -2;

@@ -7,7 +7,7 @@ namespace kvz {
 
 template <int D, bool GQA>
 __global__ __launch_bounds__(64) void decompress_kernel(const uint8_t* __restrict__ units,
-                                                        const uint16_t* __restrict__ pool,
+                                                        const uint16_t* __restrict__ pool, int64_t pool_cap,
                                                         const int32_t* __restrict__ page_ids, int H,
                                                         int P, int num_pages, uint16_t* __restrict__ k_dst,
                                                         uint16_t* __restrict__ v_dst,
@@ -27,7 +27,8 @@ __global__ __launch_bounds__(64) void decompress_kernel(const uint8_t* __restric
   for (int t = 0; t < P / kTile; ++t) {
     // K
     const uint32_t meta = load_meta(unit, P, D, t, lane);
-    const UnitHeader hdr = header_from_meta<D>(meta);
+    UnitHeader hdr = header_from_meta<D>(meta);
+    clamp_to_pool(hdr, pool_cap);
     KRaw<D> kr;
     load_k<D, GQA>(unit, P, t, lane, kr);
     uint32_t kp[KRaw<D>::VK / 2];
@@ -60,18 +61,18 @@ __global__ __launch_bounds__(64) void decompress_kernel(const uint8_t* __restric
   }
 }
 
-int launch_decompress(const uint8_t* units, const uint16_t* pool, const int32_t* page_ids, int n, int H,
+int launch_decompress(const uint8_t* units, const uint16_t* pool, int64_t pool_cap, const int32_t* page_ids, int n, int H,
                       int P, int D, int num_pages, int lane_map, uint16_t* k_dst, uint16_t* v_dst,
                       uint32_t* status, hipStream_t stream) {
   dim3 grid((unsigned)n * H), block(64);
   if (D == 128 && lane_map == 1)
-    hipLaunchKernelGGL((decompress_kernel<128, true>), grid, block, 0, stream, units, pool, page_ids, H, P,
+    hipLaunchKernelGGL((decompress_kernel<128, true>), grid, block, 0, stream, units, pool, pool_cap, page_ids, H, P,
                        num_pages, k_dst, v_dst, status);
   else if (D == 128)
-    hipLaunchKernelGGL((decompress_kernel<128, false>), grid, block, 0, stream, units, pool, page_ids, H, P,
+    hipLaunchKernelGGL((decompress_kernel<128, false>), grid, block, 0, stream, units, pool, pool_cap, page_ids, H, P,
                        num_pages, k_dst, v_dst, status);
   else if (D == 64 && lane_map == 0)
-    hipLaunchKernelGGL((decompress_kernel<64, false>), grid, block, 0, stream, units, pool, page_ids, H, P,
+    hipLaunchKernelGGL((decompress_kernel<64, false>), grid, block, 0, stream, units, pool, pool_cap, page_ids, H, P,
                        num_pages, k_dst, v_dst, status);
   else
     return -2;

@@ -7,7 +7,7 @@
 #include "zf.hpp"
 
 namespace kvz {
-int launch_decompress(const uint8_t* units, const uint16_t* pool, const int32_t* page_ids, int n, int H, int P,
+int launch_decompress(const uint8_t* units, const uint16_t* pool, int64_t pool_cap, const int32_t* page_ids, int n, int H, int P,
                       int D, int num_pages, int lane_map, uint16_t* k_dst, uint16_t* v_dst, uint32_t* status,
                       hipStream_t stream);
 int launch_compress(const uint16_t* k_src, const uint16_t* v_src, const int32_t* ids, int n, int H, int P, int D,
@@ -24,11 +24,11 @@ int launch_attn_zf(const uint16_t* q, const uint8_t* units, const uint16_t* pool
 int launch_decompress_zf(const uint8_t* units, const uint16_t* pool, int64_t pool_cap, const int32_t* page_ids, int n,
                          int H, int P, int D, int num_pages, uint16_t* k_dst, uint16_t* v_dst, uint32_t* status,
                          hipStream_t stream);
-int launch_attn_mha(const uint16_t* q, const uint8_t* units, const uint16_t* pool, const uint16_t* k_tail,
+int launch_attn_mha(const uint16_t* q, const uint8_t* units, const uint16_t* pool, int64_t pool_cap, const uint16_t* k_tail,
                     const uint16_t* v_tail, const int32_t* page_table, int max_pages, const int32_t* seq_lens,
                     int B, int H, int D, int P, int num_pages, int S, int C, float scale, float* ws_acc,
                     float* ws_ml, uint32_t* status, hipStream_t stream);
-int launch_attn_gqa(const uint16_t* q, const uint8_t* units, const uint16_t* pool, const uint16_t* k_tail,
+int launch_attn_gqa(const uint16_t* q, const uint8_t* units, const uint16_t* pool, int64_t pool_cap, const uint16_t* k_tail,
                     const uint16_t* v_tail, const int32_t* page_table, int max_pages, const int32_t* seq_lens,
                     int B, int Hq, int Hkv, int D, int P, int num_pages, int S, int C, float scale, float* ws_acc,
                     float* ws_ml, uint32_t* status, hipStream_t stream);
@@ -39,6 +39,9 @@ int launch_attn_dense_gqa(const uint16_t* q, const uint16_t* k_pages, const uint
                           int max_pages, const int32_t* seq_lens, int B, int Hq, int Hkv, int D, int P,
                           int num_pages, int S, int C, float scale, float* ws_acc, float* ws_ml, uint32_t* status,
                           hipStream_t stream);
+int launch_compact_pool(uint8_t* units, const uint16_t* pool, int64_t pool_cap, const int32_t* page_ids, int n, int H,
+                        int P, int D, int num_pages, int format, uint16_t* new_pool, int64_t new_cap,
+                        uint64_t* new_cursor, uint32_t* status, hipStream_t stream);
 int launch_merge(const float* ws_acc, const float* ws_ml, const int32_t* seq_lens, int B, int Hq, int D, int P,
                  int max_pages, int S, int C, int dense, uint16_t* out, float* out_f32, hipStream_t stream);
 }  // namespace kvz
@@ -160,10 +163,10 @@ int kvz_decode_attention_splits(const uint16_t* q, const kvz_cache* c, const int
                              seq_lens, B, H, D, P, c->num_pages, S, C, scale, ws_acc, ws_ml, c->status,
                              as_stream(stream));
   } else if (H_q == H)
-    rc = kvz::launch_attn_mha(q, c->units, c->esc_pool, c->k_tail, c->v_tail, page_table, max_pages, seq_lens, B, H,
+    rc = kvz::launch_attn_mha(q, c->units, c->esc_pool, c->esc_capacity, c->k_tail, c->v_tail, page_table, max_pages, seq_lens, B, H,
                               D, P, c->num_pages, S, C, scale, ws_acc, ws_ml, c->status, as_stream(stream));
   else
-    rc = kvz::launch_attn_gqa(q, c->units, c->esc_pool, c->k_tail, c->v_tail, page_table, max_pages, seq_lens, B,
+    rc = kvz::launch_attn_gqa(q, c->units, c->esc_pool, c->esc_capacity, c->k_tail, c->v_tail, page_table, max_pages, seq_lens, B,
                               H_q, H, D, P, c->num_pages, S, C, scale, ws_acc, ws_ml, c->status,
                               as_stream(stream));
   return rc ? (rc == -2 ? KVZ_ERR_UNSUPPORTED : KVZ_ERR_HIP) : KVZ_OK;
@@ -253,9 +256,20 @@ int kvz_decompress_pages(const kvz_cache* c, const int32_t* page_ids, int32_t n,
                                              as_stream(stream));
     return rc == -2 ? KVZ_ERR_UNSUPPORTED : (rc ? KVZ_ERR_HIP : KVZ_OK);
   }
-  const int rc = kvz::launch_decompress(c->units, c->esc_pool, page_ids, n, c->num_kv_heads, c->page_size, D,
+  const int rc = kvz::launch_decompress(c->units, c->esc_pool, c->esc_capacity, page_ids, n, c->num_kv_heads, c->page_size, D,
                                         c->num_pages, lane_map, k_dst, v_dst, c->status, as_stream(stream));
   return rc == -2 ? KVZ_ERR_UNSUPPORTED : (rc ? KVZ_ERR_HIP : KVZ_OK);
+}
+
+int kvz_compact_pool(const kvz_cache* c, const int32_t* page_ids, int32_t n, uint16_t* new_pool,
+                     int64_t new_capacity, uint64_t* new_cursor, void* stream) {
+  if (!cache_ok(c) || n < 0 || new_capacity < 0 || !new_cursor) return KVZ_ERR_INVALID_ARG;
+  if (n > 0 && (!page_ids || !new_pool || !c->esc_pool)) return KVZ_ERR_INVALID_ARG;
+  if (n == 0) return KVZ_OK;
+  const int rc = kvz::launch_compact_pool(c->units, c->esc_pool, c->esc_capacity, page_ids, n, c->num_kv_heads,
+                                          c->page_size, c->head_dim, c->num_pages, c->format, new_pool, new_capacity,
+                                          new_cursor, c->status, as_stream(stream));
+  return rc ? KVZ_ERR_HIP : KVZ_OK;
 }
 
 const char* kvz_strerror(int code) {

@@ -172,6 +172,12 @@ struct UnitHeader {
   uint64_t off;             // pool offset or kInline
 };
 
+// A pool extent that does not fit the pool (a damaged or dropped header) is treated as no escapes,
+// so that no pool read ever leaves the pool.
+__device__ __forceinline__ void clamp_to_pool(UnitHeader& h, int64_t pool_cap) {
+  if (h.off != kInline && h.off + (uint64_t)h.kc + h.vc > (uint64_t)pool_cap) h.kc = h.vc = 0;
+}
+
 template <int D>
 __device__ __forceinline__ UnitHeader header_from_meta(uint32_t meta) {
   constexpr int hl = 8 * (D / kGroup);

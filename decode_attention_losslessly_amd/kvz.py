@@ -22,7 +22,7 @@ FORMAT_ESCAPE, FORMAT_ZIPFUSION = 0, 1
 EXPORTS = ("kvz_unit_bytes", "kvz_meta_bytes", "kvz_inline_capacity", "kvz_workspace_bytes", "kvz_num_splits",
            "kvz_compress_pages", "kvz_append_token", "kvz_decode_attention", "kvz_decode_attention_dense",
            "kvz_decompress_pages", "kvz_strerror", "kvz_decode_attention_splits",
-           "kvz_decode_attention_dense_splits", "kvz_merge_splits", "kvz_unit_bytes_for")
+           "kvz_decode_attention_dense_splits", "kvz_merge_splits", "kvz_unit_bytes_for", "kvz_compact_pool")
 
 
 class KvzError(RuntimeError):
@@ -54,6 +54,7 @@ def lib() -> ctypes.CDLL:
         sig = {
             "kvz_unit_bytes": (sz, [i32, i32]),
             "kvz_unit_bytes_for": (sz, [i32, i32, i32]),
+            "kvz_compact_pool": (ctypes.c_int, [cp, vp, i32, vp, i64, vp, vp]),
             "kvz_meta_bytes": (sz, [i32, i32]),
             "kvz_inline_capacity": (i32, [i32, i32]),
             "kvz_workspace_bytes": (sz, [i32, i32, i32, i32, i32, i32, i32]),
@@ -246,6 +247,17 @@ def merge_splits(workspace: torch.Tensor, seq_lens: torch.Tensor, B: int, Hq: in
     _check(lib().kvz_merge_splits(_ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(seq_lens), B,
                                   Hq, H, D, P, max_pages, pages_per_split, 1 if dense else 0, _ptr(out),
                                   _ptr(out_f32), _stream(stream)), "kvz_merge_splits")
+
+
+def compact_pool(cache: Cache, page_ids: torch.Tensor, new_capacity: int, stream=None) -> None:
+    """Moves the pool data of the units page_ids (int32 [n], all heads) into a new pool of
+    new_capacity u16 elements and installs it in `cache` (the old pool is then released)."""
+    new_pool = torch.zeros(max(1, new_capacity), dtype=torch.int16, device=cache.esc_pool.device)
+    new_cursor = torch.zeros(1, dtype=torch.int64, device=cache.esc_pool.device)
+    cs = cache.struct()
+    _check(lib().kvz_compact_pool(ctypes.byref(cs), _ptr(page_ids), int(page_ids.numel()), _ptr(new_pool),
+                                  new_pool.numel(), _ptr(new_cursor), _stream(stream)), "kvz_compact_pool")
+    cache.esc_pool, cache.esc_cursor = new_pool, new_cursor
 
 
 def decompress_pages(cache: Cache, page_ids: torch.Tensor, k_dst: torch.Tensor, v_dst: torch.Tensor,

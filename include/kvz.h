@@ -222,6 +222,22 @@ int kvz_merge_splits(const void* workspace, size_t workspace_bytes, const int32_
 int kvz_decompress_pages(const kvz_cache* cache, const int32_t* page_ids, int32_t n,
                          int32_t lane_map, uint16_t* k_dst, uint16_t* v_dst, void* stream);
 
+/* Moves the pool data of the listed units (their escape lists, or raw blocks in the ZipFusion
+ * format) into a new pool and points the units at it, so that the pool space of units that are
+ * no longer used can be released: the caller then installs new_pool / new_capacity /
+ * new_cursor in its kvz_cache and frees the old pool (§III.D: memory given back for reuse).
+ *   page_ids      [n] distinct unit slots to keep (every head of each); units not listed keep
+ *                 pointing into the old pool and must not be used with the new one
+ *   new_pool      u16 [new_capacity], must not overlap the old pool
+ *   new_cursor    [1] u16 elements of new_pool in use, bumped atomically (0 for an empty pool;
+ *                 a multiple of 8 for the ZipFusion format)
+ * Placement in the new pool depends on scheduling; contents and results do not. Must not run
+ * concurrently with other calls on the same cache. Errors: KVZ_ERR_INVALID_ARG. Device status:
+ * BAD_PAGE_ID, ESC_POOL_FULL (new pool too small, or a header pointing outside the old pool:
+ * that unit's pool data is dropped, as when compression finds the pool full). */
+int kvz_compact_pool(const kvz_cache* cache, const int32_t* page_ids, int32_t n, uint16_t* new_pool,
+                     int64_t new_capacity, uint64_t* new_cursor, void* stream);
+
 const char* kvz_strerror(int code);
 
 #ifdef __cplusplus

@@ -71,6 +71,7 @@ def test_invalid_arguments_enqueue_nothing():
     rc = L.kvz_decode_attention_dense(None, None, None, 0, 1, 128, 16, None, 0, None, 1, 32, 1.0, 0, None, None,
                                       None, 0, None, None)
     assert rc == binding.KVZ_ERR_UNSUPPORTED       # group of 32 > 16
+    assert L.kvz_compact_pool(None, None, 0, None, 0, None, None) == binding.KVZ_ERR_INVALID_ARG
     assert kvz.kvz.strerror(binding.KVZ_ERR_WORKSPACE) == "workspace too small"
 
 

@@ -1,0 +1,80 @@
+"""kvz_compact_pool: the pool data of the units still in use moves to a new, smaller pool and the
+units point at it; attention of the live requests is bit-identical before and after, with the old
+pool overwritten so that any read of it would show. Both cache formats (escape lists; ZipFusion
+raw blocks), on escape-heavy data. An undersized new pool drops the data of the units that do not
+fit (status bit set) and nothing reads past a pool."""
+import numpy as np
+import pytest
+import torch
+
+import decode_attention_losslessly_amd as kvz
+from kvz_testlib import DEV, build_cache, dev, full_page_ids
+from synth import make_workload
+
+pytestmark = pytest.mark.gpu
+
+
+def _attend(w, cache, lens, q):
+    out = torch.zeros((w.B, w.Hq, w.D), dtype=torch.int16, device=DEV)
+    out32 = torch.zeros((w.B, w.Hq, w.D), dtype=torch.float32, device=DEV)
+    kvz.decode_attention(q, cache, dev(w.page_table), lens, w.sm_scale, out, out32)
+    torch.cuda.synchronize()
+    return out.clone(), out32.clone()
+
+
+def _pool_use(cache, w, ids, fmt):
+    """pool elements the units `ids` own, read from their headers"""
+    u = cache.units.cpu().numpy()
+    P, D = w.P, w.D
+    total = 0
+    for pid in ids:
+        for h in range(w.Hkv):
+            b = u[pid, h]
+            if fmt == kvz.FORMAT_ZIPFUSION:
+                nb = 2 * (P // 16) * (D // 32)
+                total += 512 * int((b[:nb] == 0xFF).sum())
+            else:
+                hdr = 2 * P * (D // 64)
+                off = int(b[hdr + 8:hdr + 16].view(np.uint64)[0])
+                if off != (1 << 64) - 1:
+                    total += int(b[hdr:hdr + 8].view(np.uint32).sum())
+    return total
+
+
+@pytest.mark.parametrize("fmt", [kvz.FORMAT_ESCAPE, kvz.FORMAT_ZIPFUSION])
+def test_compaction_keeps_live_results(fmt):
+    w = make_workload(5, B=4, lens=[70, 45, 100, 33], Hq=4, Hkv=4, D=128)
+    kp, vp = w.pages(0), w.pages(1)
+    cache, lens = build_cache(w, kp, vp, fmt=fmt)
+    q = dev(w.q())
+    o16, o32 = _attend(w, cache, lens, q)
+    live_rows = [0, 2]
+    lens_live = lens.clone()
+    lens_live[[1, 3]] = 0
+    live = np.array([w.page_table[r, i] for r in live_rows for i in range(int(w.seq_lens[r]) // w.P)], np.int32)
+    need = _pool_use(cache, w, live, fmt)
+    used_before = int(cache.esc_cursor.item())
+    assert 0 < need < used_before
+    old_pool = cache.esc_pool
+    kvz.compact_pool(cache, dev(live), new_capacity=need)
+    torch.cuda.synchronize()
+    assert int(cache.status.item()) == 0
+    assert int(cache.esc_cursor.item()) == need and cache.esc_capacity == need
+    old_pool.fill_(0x7F7F)      # nothing may read the old pool any more
+    n16, n32 = _attend(w, cache, lens_live, q)
+    for r in live_rows:
+        assert torch.equal(n16[r], o16[r]) and torch.equal(n32[r], o32[r])
+    assert not n16[[1, 3]].any()
+
+
+@pytest.mark.parametrize("fmt", [kvz.FORMAT_ESCAPE, kvz.FORMAT_ZIPFUSION])
+def test_undersized_pool_drops_and_stays_in_bounds(fmt):
+    w = make_workload(5, B=2, L=64, Hq=4, Hkv=4, D=128)
+    kp, vp = w.pages(0), w.pages(1)
+    cache, lens = build_cache(w, kp, vp, fmt=fmt)
+    ids = full_page_ids(w)
+    kvz.compact_pool(cache, dev(ids), new_capacity=1000)
+    torch.cuda.synchronize()
+    assert int(cache.status.item()) & kvz.kvz.STATUS_ESC_POOL_FULL
+    assert int(cache.esc_cursor.item()) > 1000          # the cursor counts every request
+    _attend(w, cache, lens, dev(w.q()))   # outputs unspecified (status says so); the run must stay in bounds
