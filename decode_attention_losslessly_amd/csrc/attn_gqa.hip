@@ -139,11 +139,11 @@ __device__ __forceinline__ bool gqa_c_compute(GqaState& st, const GqaCStage& stg
   if (stg.tile == 0) { krank = 0; vrank = 0; }
   uint32_t kp[16];
   decode_k<128>(stg.k, kp);
-  if (hdr.kc) patch_k_tile<128, true, POOL>(kp, stg.k, stg.meta, hdr, P, stg.tile, krank, esc_lds, pool, lane);
+  if (hdr.kc) patch_k_tile<128, true, POOL>(kp, stg.k, stg.meta, hdr, P, stg.tile, krank, esc_lds, pool, pool_cap, lane);
   uint32_t vflat[16];
 #pragma unroll
   for (int g = 0; g < 2; ++g) decode_v_seg(stg.v.seg[g], v_bases<128>(stg.meta, g), &vflat[8 * g]);
-  if (hdr.vc) patch_v_tile<128, POOL>(vflat, stg.v, stg.meta, hdr, P, stg.tile, vrank, esc_lds, pool, lane);
+  if (hdr.vc) patch_v_tile<128, POOL, 2>(vflat, stg.v, stg.meta, hdr, P, stg.tile, vrank, esc_lds, pool, pool_cap, lane);
   uint32_t vp[2][8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
@@ -268,7 +268,7 @@ __global__ __launch_bounds__(64 * kGqaWaves) KVZ_GQA_OCCUPANCY void attn_gqa_ker
     const int32_t* __restrict__ page_table, int max_pages, const int32_t* __restrict__ seq_lens, int B, int Hq, int H,
     int P, int num_pages, int S, int C, float scale, float* __restrict__ ws_acc, float* __restrict__ ws_ml,
     uint32_t* __restrict__ status) {
-  __shared__ uint16_t esc_all[kGqaWaves][esc_lds_elems<128>()];
+  __shared__ __align__(16) uint16_t esc_all[kGqaWaves][esc_lds_elems<128>()];
   __shared__ uint32_t vlds_all[kGqaWaves][128 * 8];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int grp = Hq / H, nchunks = (grp + kGqaRows - 1) / kGqaRows;

@@ -67,7 +67,7 @@ __device__ __forceinline__ bool mha_compute(MhaState<D>& st, const MhaStage<D>& 
   if (stg.tile == 0) { krank = 0; vrank = 0; }
   uint32_t kp[VK / 2];
   decode_k<D>(stg.k, kp);
-  if (hdr.kc) patch_k_tile<D, false, POOL>(kp, stg.k, stg.meta, hdr, P, stg.tile, krank, lds, pool, lane);
+  if (hdr.kc) patch_k_tile<D, false, POOL>(kp, stg.k, stg.meta, hdr, P, stg.tile, krank, lds, pool, pool_cap, lane);
   float sc[D / 64];
   mha_scores<D>(st, kp, scale, sc);
   uint32_t phi[8], plo[8];
@@ -75,7 +75,7 @@ __device__ __forceinline__ bool mha_compute(MhaState<D>& st, const MhaStage<D>& 
   uint32_t vp[NS * 8];
 #pragma unroll
   for (int g = 0; g < NS; ++g) decode_v_seg(stg.v.seg[g], v_bases<D>(stg.meta, g), &vp[8 * g]);
-  if (hdr.vc) patch_v_tile<D, POOL>(vp, stg.v, stg.meta, hdr, P, stg.tile, vrank, lds, pool, lane);
+  if (hdr.vc) patch_v_tile<D, POOL>(vp, stg.v, stg.meta, hdr, P, stg.tile, vrank, lds, pool, pool_cap, lane);
   mha_accumulate_v<D>(st, vp, phi, plo);
   return true;
 }
@@ -93,7 +93,7 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void attn_mha_kernel(
     const int32_t* __restrict__ page_table, int max_pages, const int32_t* __restrict__ seq_lens, int B, int H, int P,
     int num_pages, int S, int C, float scale, float* __restrict__ ws_acc, float* __restrict__ ws_ml,
     uint32_t* __restrict__ status) {
-  __shared__ uint16_t lds_all[kWavesPerBlock][esc_lds_elems<D>()];
+  __shared__ __align__(16) uint16_t lds_all[kWavesPerBlock][esc_lds_elems<D>()];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int item = (int)uniform(blockIdx.x * kWavesPerBlock + wave);
   if (item >= B * H * S) return;

@@ -12,7 +12,7 @@ __global__ __launch_bounds__(64) void decompress_kernel(const uint8_t* __restric
                                                         int P, int num_pages, uint16_t* __restrict__ k_dst,
                                                         uint16_t* __restrict__ v_dst,
                                                         uint32_t* __restrict__ status) {
-  __shared__ uint16_t lds[esc_lds_elems<D>()];
+  __shared__ __align__(16) uint16_t lds[esc_lds_elems<D>()];
   const int lane = threadIdx.x;
   const int i = blockIdx.x / H, h = blockIdx.x % H;
   const int pid = sload<int32_t>(page_ids + i);
@@ -33,7 +33,7 @@ __global__ __launch_bounds__(64) void decompress_kernel(const uint8_t* __restric
     load_k<D, GQA>(unit, P, t, lane, kr);
     uint32_t kp[KRaw<D>::VK / 2];
     decode_k<D>(kr, kp);
-    if (hdr.kc) patch_k_tile<D, GQA>(kp, kr, meta, hdr, P, t, krank, lds, pool, lane);
+    if (hdr.kc) patch_k_tile<D, GQA>(kp, kr, meta, hdr, P, t, krank, lds, pool, pool_cap, lane);
 #pragma unroll
     for (int i = 0; i < KRaw<D>::NP; ++i) {
       const int pc = k_piece<D, GQA>(lane, i);
@@ -48,7 +48,7 @@ __global__ __launch_bounds__(64) void decompress_kernel(const uint8_t* __restric
     uint32_t vp[NS * 8];
 #pragma unroll
     for (int s = 0; s < NS; ++s) decode_v_seg(vr.seg[s], v_bases<D>(meta, s), &vp[8 * s]);
-    if (hdr.vc) patch_v_tile<D>(vp, vr, meta, hdr, P, t, vrank, lds, pool, lane);
+    if (hdr.vc) patch_v_tile<D>(vp, vr, meta, hdr, P, t, vrank, lds, pool, pool_cap, lane);
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       const int d = lane + 64 * s;

@@ -190,25 +190,6 @@ __device__ __forceinline__ void patch_one(uint32_t (&pairs)[N], int reg, int lan
   pairs[reg] = lane_id() == lane ? ((old & keep) | put) : old;
 }
 
-// Patches escaped values from a list staged in LDS (any number of escapes), per lane.
-//   lds       the escapes of this segment set, indexed from `rank` (this lane's first escape)
-template <int NW>
-__device__ __forceinline__ void patch_lds(uint32_t (&pairs)[4 * NW], const uint32_t (&flags)[NW],
-                                          const uint16_t* lds, uint32_t rank, uint32_t limit) {
-#pragma unroll
-  for (int w = 0; w < NW; ++w) {
-    const uint32_t f = flags[w];
-    if (f == 0) continue;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      if (f & flag_bit(j)) {
-        if (rank < limit) pairs[4 * w + (j >> 1)] = set_half(pairs[4 * w + (j >> 1)], j & 1, lds[rank]);
-        ++rank;
-      }
-    }
-  }
-}
-
 __device__ __forceinline__ uint32_t popc_flags(uint32_t f) { return (uint32_t)__builtin_popcount(f); }
 
 // Escape flags with bit order = storage order: position j of the word goes to bit

@@ -223,9 +223,55 @@ __device__ __forceinline__ void k_position(uint32_t p, int& lane, int& reg, int&
 //   chunks(lane)  the storage chunks this lane holds, in storage order, each `span` positions
 //                 long and read from `nib` words of 8 positions
 
-// u16 elements of the per-wave LDS area the escape paths use: 16*D values + 64 lanes x D/8 pairs
+// u16 elements of the per-wave LDS area the escape paths use: a tile's escape list (at most 16*D
+// values, staged from a 16-byte aligned start: + 16 of slack), then 64 lanes x D/8 pairs
 template <int D>
-constexpr int esc_lds_elems() { return 32 * D; }
+constexpr int esc_lds_elems() { return 32 * D + 16; }
+template <int D>
+constexpr int esc_pairs_at() { return 16 * D + 16; }
+
+// Copies pool[first, first + n) into lds, the element `first` landing at lds[first % 8]: every
+// lane loads its 16-byte chunks of the aligned range, kBatch chunks at a time with
+// all loads of a batch issued before its LDS writes (two round trips for the longest list instead
+// of one per element; a batch, not the whole range, so that the registers held stay few); a chunk
+// that would cross the end of the pool is read element by element up to that end.
+// Returns first % 8.
+template <int D, int kBatch>
+__device__ __forceinline__ uint32_t stage_list(const uint16_t* pool, int64_t pool_cap, uint64_t first, uint32_t n,
+                                               uint16_t* lds, int lane) {
+  constexpr int kChunks = (2 * D + 2 + 63) / 64;   // 16-byte chunks per lane for n <= 16*D
+  const uint64_t a0 = first & ~7ull;
+  const uint32_t mis = (uint32_t)(first - a0);
+  const uint32_t nch = (mis + n + 7) / 8;
+#pragma unroll
+  for (int c0 = 0; c0 < kChunks; c0 += kBatch) {
+    if ((uint32_t)(64 * c0) >= nch) break;
+    uint4 v[kBatch];
+#pragma unroll
+    for (int c = 0; c < kBatch; ++c) {
+      const uint32_t ch = (uint32_t)lane + 64u * (c0 + c);
+      const uint64_t e0 = a0 + 8ull * ch;
+      v[c] = make_uint4(0, 0, 0, 0);
+      if (c0 + c < kChunks && ch < nch) {
+        if (e0 + 8 <= (uint64_t)pool_cap) {
+          v[c] = *reinterpret_cast<const uint4*>(pool + e0);
+        } else {
+          uint32_t w[4] = {0, 0, 0, 0};
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (e0 + e < (uint64_t)pool_cap) w[e >> 1] |= (uint32_t)pool[e0 + e] << (16 * (e & 1));
+          v[c] = make_uint4(w[0], w[1], w[2], w[3]);
+        }
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < kBatch; ++c) {
+      const uint32_t ch = (uint32_t)lane + 64u * (c0 + c);
+      if (c0 + c < kChunks && ch < nch) *reinterpret_cast<uint4*>(lds + 8 * ch) = v[c];
+    }
+  }
+  return mis;
+}
 
 // Writes escape x of position j (within this lane's run of pairs) into the LDS copy.
 __device__ __forceinline__ void lds_pair_half(uint32_t* mine, int j, uint32_t x) {
@@ -235,7 +281,7 @@ __device__ __forceinline__ void lds_pair_half(uint32_t* mine, int j, uint32_t x)
 template <int D, bool GQA>
 __device__ __forceinline__ void pool_patch_k(uint32_t (&pairs)[KRaw<D>::VK / 2], const KRaw<D>& raw,
                                              const UnitHeader& h, uint32_t& cursor, uint16_t* lds,
-                                             const uint16_t* pool, int lane) {
+                                             const uint16_t* pool, int64_t pool_cap, int lane) {
   constexpr int N = KRaw<D>::VK / 2, NP = KRaw<D>::NP;
   // rank (in storage order) of each piece's first escape
   uint32_t cnt[NP], rank[NP], total = 0;
@@ -262,9 +308,8 @@ __device__ __forceinline__ void pool_patch_k(uint32_t (&pairs)[KRaw<D>::VK / 2],
   if (total == 0) return;
   const uint32_t cur = uniform(cursor);
   const uint32_t avail = h.kc > cur ? min(total, h.kc - cur) : 0u;
-  const uint16_t* src_list = pool + h.off + cur;
-  for (uint32_t i = lane; i < avail; i += 64) lds[i] = src_list[i];
-  uint32_t* mine = reinterpret_cast<uint32_t*>(lds + 16 * D) + lane * N;
+  const uint32_t mis = stage_list<D, GQA ? 2 : 3>(pool, pool_cap, h.off + cur, avail, lds, lane);
+  uint32_t* mine = reinterpret_cast<uint32_t*>(lds + esc_pairs_at<D>()) + lane * N;
 #pragma unroll
   for (int i = 0; i < N; i += 4) *reinterpret_cast<uint4*>(mine + i) = make_uint4(pairs[i], pairs[i + 1], pairs[i + 2], pairs[i + 3]);
   wave_lds_sync();
@@ -275,7 +320,7 @@ __device__ __forceinline__ void pool_patch_k(uint32_t (&pairs)[KRaw<D>::VK / 2],
       while (f) {                                  // positions of the word in list order
         const int pos = ordered_bit_to_pos(__builtin_ctz(f));
         f &= f - 1;
-        if (rk < avail) lds_pair_half(mine, 16 * i + 8 * w + pos, lds[rk]);
+        if (rk < avail) lds_pair_half(mine, 16 * i + 8 * w + pos, lds[mis + rk]);
         ++rk;
       }
     }
@@ -290,9 +335,10 @@ __device__ __forceinline__ void pool_patch_k(uint32_t (&pairs)[KRaw<D>::VK / 2],
   cursor = cur + total;
 }
 
-template <int D>
+template <int D, int kBatch>
 __device__ __forceinline__ void pool_patch_v(uint32_t (&pairs)[D / 8], const VRaw<D>& raw, const UnitHeader& h,
-                                             uint32_t& cursor, uint16_t* lds, const uint16_t* pool, int lane) {
+                                             uint32_t& cursor, uint16_t* lds, const uint16_t* pool, int64_t pool_cap,
+                                             int lane) {
   constexpr int NS = D / 64, N = D / 8;
   uint32_t packed = 0;
 #pragma unroll
@@ -306,9 +352,8 @@ __device__ __forceinline__ void pool_patch_v(uint32_t (&pairs)[D / 8], const VRa
   if (total == 0) return;
   const uint32_t cur = uniform(cursor);
   const uint32_t avail = h.vc > cur ? min(total, h.vc - cur) : 0u;
-  const uint16_t* src_list = pool + h.off + h.kc + cur;
-  for (uint32_t i = lane; i < avail; i += 64) lds[i] = src_list[i];
-  uint32_t* mine = reinterpret_cast<uint32_t*>(lds + 16 * D) + lane * N;
+  const uint32_t mis = stage_list<D, kBatch>(pool, pool_cap, h.off + h.kc + cur, avail, lds, lane);
+  uint32_t* mine = reinterpret_cast<uint32_t*>(lds + esc_pairs_at<D>()) + lane * N;
 #pragma unroll
   for (int i = 0; i < N; i += 4) *reinterpret_cast<uint4*>(mine + i) = make_uint4(pairs[i], pairs[i + 1], pairs[i + 2], pairs[i + 3]);
   wave_lds_sync();
@@ -319,7 +364,7 @@ __device__ __forceinline__ void pool_patch_v(uint32_t (&pairs)[D / 8], const VRa
       while (f) {                                  // positions of the word in list order
         const int pos = ordered_bit_to_pos(__builtin_ctz(f));
         f &= f - 1;
-        if (rank < avail) lds_pair_half(mine, 16 * s + 8 * w + pos, lds[rank]);
+        if (rank < avail) lds_pair_half(mine, 16 * s + 8 * w + pos, lds[mis + rank]);
         ++rank;
       }
     }
@@ -339,7 +384,8 @@ __device__ __forceinline__ void pool_patch_v(uint32_t (&pairs)[D / 8], const VRa
 template <int D, bool GQA, bool POOL = true>
 __device__ __forceinline__ bool patch_k_tile(uint32_t (&pairs)[KRaw<D>::VK / 2], const KRaw<D>& raw,
                                              uint32_t meta, const UnitHeader& h, int P, int tile,
-                                             uint32_t& cursor, uint16_t* lds, const uint16_t* pool, int lane) {
+                                             uint32_t& cursor, uint16_t* lds, const uint16_t* pool,
+                                             int64_t pool_cap, int lane) {
   constexpr int N = KRaw<D>::VK / 2;
   // everything that names an escape is wave-uniform: keep it in SGPRs
   const uint32_t lo = uniform((uint32_t)tile * kTile * D), hi = lo + kTile * D;
@@ -359,16 +405,17 @@ __device__ __forceinline__ bool patch_k_tile(uint32_t (&pairs)[KRaw<D>::VK / 2],
     return true;
   }
   if constexpr (!POOL) return false;
-  pool_patch_k<D, GQA>(pairs, raw, h, cursor, lds, pool, lane);
+  pool_patch_k<D, GQA>(pairs, raw, h, cursor, lds, pool, pool_cap, lane);
   return true;
 }
 
 // V: segments s = 0 .. D/64-1 (dims lane + 64 s), storage order segment-major then lane;
 // pairs[s * 8 + k] holds tokens 2k, 2k+1 of dim lane + 64 s.
-template <int D, bool POOL = true>
+// kBatch: 16-byte pool chunks per lane held in registers at a time while staging the list
+template <int D, bool POOL = true, int kBatch = 3>
 __device__ __forceinline__ bool patch_v_tile(uint32_t (&pairs)[D / 8], const VRaw<D>& raw, uint32_t meta,
                                              const UnitHeader& h, int P, int tile, uint32_t& cursor, uint16_t* lds,
-                                             const uint16_t* pool, int lane) {
+                                             const uint16_t* pool, int64_t pool_cap, int lane) {
   const uint32_t lo = uniform((uint32_t)tile * kTile * D), hi = lo + kTile * D;
   if (h.off == kInline) {
     const uint32_t end = uniform(min(h.kc + h.vc, (uint32_t)inline_capacity(P, D)));
@@ -385,7 +432,7 @@ __device__ __forceinline__ bool patch_v_tile(uint32_t (&pairs)[D / 8], const VRa
     return true;
   }
   if constexpr (!POOL) return false;
-  pool_patch_v<D>(pairs, raw, h, cursor, lds, pool, lane);
+  pool_patch_v<D, kBatch>(pairs, raw, h, cursor, lds, pool, pool_cap, lane);
   return true;
 }
 
