@@ -56,6 +56,8 @@ def parse():
     ap.add_argument("--config", type=int, default=3, help="workload number (3 = the headline workload)")
     ap.add_argument("--format", choices=["escape", "zipfusion"], default="escape",
                     help="cache format: exponent offsets with escapes (the library's), or ZipFusion's blocks")
+    ap.add_argument("--pages-per-split", type=int, default=0,
+                    help="pages per split-K work item (0: the library's choice)")
     ap.add_argument("--batch", type=int, default=None, help="override the workload's batch size")
     ap.add_argument("--context", type=int, default=None, help="override the workload's context length")
     ap.add_argument("--no-dense", action="store_true", help="skip the uncompressed baseline")
@@ -168,7 +170,7 @@ def main() -> int:
         off = heads[:, :, 8:16].view(torch.int64).squeeze(-1)
         pool_esc = int(torch.where(off != -1, cnt, torch.zeros_like(cnt)).sum().item())
         raw_frac = None
-    S = kvz.num_splits(B, Hq, H, D, P, w.max_pages)
+    S = kvz.num_splits(B, Hq, H, D, P, w.max_pages, args.pages_per_split)
     units_bytes = int(full.sum()) * H * U
     tail_bytes = int((w.seq_lens % P).sum()) * H * D * 2 * 2
     # page-table entries, q and the (m, l, acc) partials
@@ -177,7 +179,8 @@ def main() -> int:
     dense_kv_bytes = int(L.sum()) * H * D * 2 * 2
     dense_bytes = dense_kv_bytes + int(((L + P - 1) // P).sum()) * H * 4 + B * Hq * D * 2 + B * Hq * S * (D + 2) * 4
 
-    ws = torch.empty(kvz.workspace_bytes(B, Hq, H, D, P, w.max_pages), dtype=torch.uint8, device=dev)
+    pps = args.pages_per_split
+    ws = torch.empty(kvz.workspace_bytes(B, Hq, H, D, P, w.max_pages, pps), dtype=torch.uint8, device=dev)
     out = torch.empty((B, Hq, D), dtype=torch.int16, device=dev)
 
     def run_loop(split_fn, merge_fn, steps):
@@ -197,8 +200,8 @@ def main() -> int:
         merge = np.array([b.elapsed_time(c) for _, b, c in ev]) * 1e3
         return wall, attn, merge
 
-    c_split = lambda: kvz.decode_attention_splits(q, cache, table, lens, w.sm_scale, ws)
-    c_merge = lambda: kvz.merge_splits(ws, lens, B, Hq, H, D, P, w.max_pages, out)
+    c_split = lambda: kvz.decode_attention_splits(q, cache, table, lens, w.sm_scale, ws, pages_per_split=pps)
+    c_merge = lambda: kvz.merge_splits(ws, lens, B, Hq, H, D, P, w.max_pages, out, pages_per_split=pps)
     for _ in range(args.warmup):
         c_split()
         c_merge()
@@ -223,8 +226,10 @@ def main() -> int:
 
     dense = None
     if not args.no_dense:
-        d_split = lambda: kvz.decode_attention_dense_splits(q, kd, vd, table, lens, w.sm_scale, ws)
-        d_merge = lambda: kvz.merge_splits(ws, lens, B, Hq, H, D, P, w.max_pages, out, dense=True)
+        d_split = lambda: kvz.decode_attention_dense_splits(q, kd, vd, table, lens, w.sm_scale, ws,
+                                                            pages_per_split=pps)
+        d_merge = lambda: kvz.merge_splits(ws, lens, B, Hq, H, D, P, w.max_pages, out, dense=True,
+                                           pages_per_split=pps)
         for _ in range(args.warmup):
             d_split()
             d_merge()
