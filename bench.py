@@ -65,6 +65,9 @@ def parse():
     ap.add_argument("--cpu-requests", type=int, default=32, help="requests in the CPU baseline sample")
     ap.add_argument("--cold-steps", type=int, default=20,
                     help="extra launches timed after a 1 GiB cache flush each (reported as attn_us.cold_median)")
+    ap.add_argument("--graph-layers", type=int, default=0, metavar="N",
+                    help="also time N layers of attention (N copies of the cache) launched eagerly and "
+                         "replayed as one HIP graph")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only copy MIB MiB device-to-device 5 times (calibrates HBM byte counters) and exit")
     return ap.parse_args()
@@ -224,6 +227,8 @@ def main() -> int:
     cold = np.array(cold) if cold else np.array([np.nan])
     del flush
 
+    layers = layer_loop(kvz, cache, q, table, lens, w, ws, pps, args.graph_layers, dev) if args.graph_layers > 0 else None
+
     dense = None
     if not args.no_dense:
         d_split = lambda: kvz.decode_attention_dense_splits(q, kd, vd, table, lens, w.sm_scale, ws,
@@ -291,6 +296,7 @@ def main() -> int:
         "speedup_vs_dense": round(dense["ms_per_step"] / ms_per_step, 4) if dense else None,
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "layers": layers,
         "append_us": round(append_us, 1) if append_us is not None else None,
         "compress_gbps_dense_input": round(len(ids) * H * P * D * 4 / compress_s / 1e9, 1),
         "gpu": f"{torch.cuda.get_device_name(0)} ({torch.cuda.get_device_properties(0).gcnArchName})",
@@ -298,6 +304,55 @@ def main() -> int:
     }
     print(json.dumps(res), flush=True)
     return 0
+
+
+def layer_loop(kvz, cache, q, table, lens, w, ws, pps, nl, dev, reps=20):
+    """One decode step of an nl-layer model's attention: nl calls of decode_attention (split
+    kernel + merge), one per layer, each on its own copy of the cache (separate memory, as the
+    layers of a model hold). Timed launched one call after another from Python, then captured
+    once as a HIP graph and replayed; the replayed outputs must equal the eager ones bit for bit.
+    Launch overhead is what a decode step at batch 1 pays per layer."""
+    import torch
+
+    caches = [cache] + [kvz.Cache(cache.P, cache.H, cache.D, cache.num_pages, cache.max_batch, cache.units.clone(),
+                                  cache.esc_pool.clone(), cache.esc_cursor.clone(), cache.k_tail.clone(),
+                                  cache.v_tail.clone(), cache.status.clone(), cache.fmt) for _ in range(nl - 1)]
+    B, Hq, D = q.shape
+    outs = torch.empty((nl, B, Hq, D), dtype=torch.int16, device=dev)
+
+    def step():
+        for i, c in enumerate(caches):
+            kvz.decode_attention(q, c, table, lens, w.sm_scale, outs[i], workspace=ws, pages_per_split=pps)
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / reps / nl
+
+    eager_us = timed(step)
+    ref = outs.clone()
+    outs.zero_()
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph_us = timed(graph.replay)
+    assert torch.equal(outs, ref), "graph replay differs from the eager layers"
+    assert all(int(c.status.item()) == 0 for c in caches)
+    del graph, caches
+    return {"layers": nl, "eager_us_per_layer": round(eager_us, 2), "graph_us_per_layer": round(graph_us, 2),
+            "graph_tokens_per_s": round(B / (graph_us * 1e-6), 1)}
 
 
 def _host_cpu() -> str:

@@ -80,3 +80,53 @@ def test_replayed_decode_steps_match_eager(cfg, Hq, Hkv, lens):
     rows = [(r, h) for r in range(w.B) for h in range(w.Hq)]
     o = oracle_rows(w, kp, vp, w.q(), rows)
     check_rows(host16(out_g).reshape(-1, w.D), out32_g.cpu().numpy().reshape(-1, w.D), o, "graph replay")
+
+
+@pytest.mark.parametrize("cfgs,Hq,Hkv", [((2, 3, 5), 4, 4), ((4, 3, 5), 8, 2)])
+def test_layers_in_one_graph(cfgs, Hq, Hkv):
+    """A decode step over several layers, each with its own cache, page table and queries (here
+    the workloads of different configurations at one shape, so the layers differ in their
+    escapes and pool use), captured as one graph. Every replay, with other eager work in between,
+    equals the eager layers bit for bit, and the layers match the oracle."""
+    from kvz_testlib import build_cache
+    lens = [100, 37, 250]
+    layers = []
+    for c in cfgs:
+        w = make_workload(c, B=len(lens), lens=np.array(lens), Hq=Hq, Hkv=Hkv, D=128, n_append=0)
+        kp, vp = w.pages(0), w.pages(1)
+        cache, lt = build_cache(w, kp, vp)
+        layers.append((w, kp, vp, cache, lt, dev(w.page_table), dev(w.q())))
+    w0 = layers[0][0]
+    ws = torch.empty(kvz.workspace_bytes(w0.B, Hq, Hkv, 128, w0.P, w0.max_pages), dtype=torch.uint8, device=DEV)
+    nl = len(layers)
+    out = torch.empty((nl, w0.B, Hq, 128), dtype=torch.int16, device=DEV)
+    out32 = torch.empty((nl, w0.B, Hq, 128), dtype=torch.float32, device=DEV)
+
+    def step(o, o32):
+        for i, (w, _, _, cache, lt, table, q) in enumerate(layers):
+            kvz.decode_attention(q, cache, table, lt, w.sm_scale, o[i], o32[i], workspace=ws)
+
+    eo, eo32 = torch.empty_like(out), torch.empty_like(out32)
+    step(eo, eo32)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            step(out, out32)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    scratch_o, scratch_o32 = torch.empty_like(out), torch.empty_like(out32)
+    for rep in range(3):
+        out.zero_()
+        out32.zero_()
+        graph.replay()
+        step(scratch_o, scratch_o32)     # eager work between replays, on the same workspace
+        torch.cuda.synchronize()
+        assert torch.equal(out, eo) and torch.equal(out32, eo32), f"replay {rep} differs from the eager layers"
+    for i, (w, kp, vp, cache, _, _, _) in enumerate(layers):
+        assert int(cache.status.item()) == 0
+        rows = [(r, h) for r in range(w.B) for h in range(w.Hq)]
+        o = oracle_rows(w, kp, vp, w.q(), rows)
+        check_rows(host16(eo[i]).reshape(-1, w.D), eo32[i].cpu().numpy().reshape(-1, w.D), o, f"layer {i} (config {cfgs[i]})")
