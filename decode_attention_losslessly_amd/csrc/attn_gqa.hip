@@ -83,19 +83,23 @@ __device__ __forceinline__ void gqa_tile(GqaState& st, const uint32_t (&kp)[16],
           (h[3] + bf16hi_to_f32(l23));
   const bool lo_row = (lane & 15) >= kGqaRows;
   const u32x2 pa = {lo_row ? l01 : h01, lo_row ? l23 : h23};
-  // V -> LDS [dim][pair] (8 u32 per dim), then B operands: tokens 4q..4q+3 of dim 16j + l%16
+  // V -> LDS [dim][pair] (8 u32 per dim), then B operands: tokens 4q..4q+3 of dim 16j + l%16.
+  // Dims with bit 3 set keep their two 16-byte halves in swapped places, so that dims d and d+8,
+  // whose rows are 64 dwords apart, use different banks on the stores and on the reads.
 #pragma unroll
   for (int g = 0; g < 2; ++g) {
-    uint4* dst = reinterpret_cast<uint4*>(vlds + vdim[g] * 8);
-    dst[0] = make_uint4(vp[g][0], vp[g][1], vp[g][2], vp[g][3]);
-    dst[1] = make_uint4(vp[g][4], vp[g][5], vp[g][6], vp[g][7]);
+    const int sw = (vdim[g] >> 1) & 4;
+    uint32_t* row = vlds + vdim[g] * 8;
+    *reinterpret_cast<uint4*>(row + sw) = make_uint4(vp[g][0], vp[g][1], vp[g][2], vp[g][3]);
+    *reinterpret_cast<uint4*>(row + (4 ^ sw)) = make_uint4(vp[g][4], vp[g][5], vp[g][6], vp[g][7]);
   }
   wave_lds_sync();
   const bf16x4 A = __builtin_bit_cast(bf16x4, pa);
   const int qg = lane >> 4;
+  const int rd_off = (2 * qg) ^ ((lane >> 1) & 4);   // bit 3 of the dim is bit 3 of l%16
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    const uint2 bv = *reinterpret_cast<const uint2*>(vlds + (16 * j + (lane & 15)) * 8 + 2 * qg);
+    const uint2 bv = *reinterpret_cast<const uint2*>(vlds + (16 * j + (lane & 15)) * 8 + rd_off);
     const u32x2 b = {bv.x, bv.y};
     st.o[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(A, __builtin_bit_cast(bf16x4, b), st.o[j], 0, 0, 0);
   }

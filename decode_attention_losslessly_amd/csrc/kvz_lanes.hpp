@@ -39,6 +39,31 @@ __device__ __forceinline__ uint32_t stream4(const void* p) {
 }
 __device__ __forceinline__ uint32_t stream1(const uint8_t* p) { return __builtin_nontemporal_load(p); }
 
+// Loads of one unit go through a buffer resource whose base is the unit (wave-uniform, so it
+// sits in SGPRs) and whose extent is the unit's size. The lane's part of an offset is the same
+// for every tile and every unit, so it is computed once; the tile's part is a scalar offset.
+// No vector instruction is then spent on addresses, and a read past the unit returns zeros.
+typedef __amdgpu_buffer_rsrc_t UnitRsrc;
+constexpr int kRsrcWord3 = 0x00020000;   // raw buffer: no swizzle, 32-bit data format field
+constexpr int kNonTemporal = 2;          // cache-policy operand: non-temporal
+__device__ __forceinline__ UnitRsrc unit_rsrc(const uint8_t* unit, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(unit), 0, (int)bytes, kRsrcWord3);
+}
+__device__ __forceinline__ uint4 uload16(UnitRsrc r, uint32_t voff, uint32_t soff) {
+  const nt_u32x4 v = __builtin_bit_cast(nt_u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, kNonTemporal));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint2 uload8(UnitRsrc r, uint32_t voff, uint32_t soff) {
+  const nt_u32x2 v = __builtin_bit_cast(nt_u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, (int)soff, kNonTemporal));
+  return make_uint2(v.x, v.y);
+}
+__device__ __forceinline__ uint32_t uload4(UnitRsrc r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, kNonTemporal);
+}
+__device__ __forceinline__ uint32_t uload1(UnitRsrc r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b8(r, (int)voff, (int)soff, kNonTemporal);
+}
+
 // ---------------------------------------------------------------- K
 template <int D>
 struct KRaw {
@@ -66,24 +91,25 @@ __device__ __forceinline__ int piece_dim(int piece) { return (16 * piece) % D; }
 template <int D, bool GQA>
 __device__ __forceinline__ void load_k(const uint8_t* unit, int P, int tile, int lane, KRaw<D>& r) {
   constexpr int NP = KRaw<D>::NP;
-  const uint8_t* tb = unit + kblock_offset(P, D) + tile * tile_bytes(D);
-  const uint8_t* bases = unit + kbase_offset(D, tile);
+  const UnitRsrc u = unit_rsrc(unit, unit_bytes(P, D));
+  const uint32_t tb = kblock_offset(P, D) + tile * tile_bytes(D);   // scalar parts
+  const uint32_t bases = kbase_offset(D, tile);
 #pragma unroll
   for (int i = 0; i < NP; ++i) {
     const int pc = k_piece<D, GQA>(lane, i);
-    const uint4 a = stream16(tb + 16 * pc);
+    const uint4 a = uload16(u, 16 * pc, tb);
     r.sm[4 * i] = a.x; r.sm[4 * i + 1] = a.y; r.sm[4 * i + 2] = a.z; r.sm[4 * i + 3] = a.w;
     if constexpr (!GQA) {
-      const uint2 n = stream8(tb + 16 * D + 8 * pc);
+      const uint2 n = uload8(u, 16 * D + 8 * pc, tb);
       r.nib[2 * i] = n.x; r.nib[2 * i + 1] = n.y;
-      r.base[i] = stream1(bases + (piece_dim<D>(pc) / kGroup) * kTile + piece_token<D>(pc));
+      r.base[i] = uload1(u, (piece_dim<D>(pc) / kGroup) * kTile + piece_token<D>(pc), bases);
     }
   }
   if constexpr (GQA) {   // the two pieces are adjacent: one 16-byte offset load, one base
     const int pc = k_piece<D, GQA>(lane, 0);
-    const uint4 n = stream16(tb + 16 * D + 8 * pc);
+    const uint4 n = uload16(u, 16 * D + 8 * pc, tb);
     r.nib[0] = n.x; r.nib[1] = n.y; r.nib[2] = n.z; r.nib[3] = n.w;
-    r.base[0] = r.base[1] = stream1(bases + (piece_dim<D>(pc) / kGroup) * kTile + piece_token<D>(pc));
+    r.base[0] = r.base[1] = uload1(u, (piece_dim<D>(pc) / kGroup) * kTile + piece_token<D>(pc), bases);
   }
 }
 
@@ -95,12 +121,15 @@ __device__ __forceinline__ void load_k(const uint8_t* unit, int P, int tile, int
 // (lanes past the meta region read bytes of the unit that are not used).
 __device__ __forceinline__ uint32_t load_meta(const uint8_t* unit, int P, int D, int tile, int lane) {
   const int G = D / kGroup;
+  // the K and V base tables both advance by kTile*G bytes per tile (the scalar offset); the
+  // header lanes take it back out
+  const uint32_t toff = kbase_offset(D, tile);
   uint32_t off;
-  if (lane < 4 * G) off = kbase_offset(D, tile) + 4 * lane;
-  else if (lane < 8 * G) off = vbase_offset(P, D, tile) + 4 * (lane - 4 * G);
-  else if (lane < 8 * G + 32) off = hdr_offset(P, D) + 4 * (lane - 8 * G);
-  else off = 0;
-  return stream4(unit + off);
+  if (lane < 4 * G) off = kbase_offset(D, 0) + 4 * lane;
+  else if (lane < 8 * G) off = vbase_offset(P, D, 0) + 4 * (lane - 4 * G);
+  else if (lane < 8 * G + 32) off = hdr_offset(P, D) + 4 * (lane - 8 * G) - toff;
+  else off = -toff;
+  return uload4(unit_rsrc(unit, unit_bytes(P, D)), off, toff);
 }
 template <int D>
 __device__ __forceinline__ int hdr_lane() { return 8 * (D / kGroup); }
@@ -129,12 +158,13 @@ struct VRaw {
 
 template <int D>
 __device__ __forceinline__ void load_v(const uint8_t* unit, int P, int tile, int lane, VRaw<D>& r) {
-  const uint8_t* tb = unit + vblock_offset(P, D) + tile * tile_bytes(D);
+  const UnitRsrc u = unit_rsrc(unit, unit_bytes(P, D));
+  const uint32_t tb = vblock_offset(P, D) + tile * tile_bytes(D);
 #pragma unroll
   for (int s = 0; s < VRaw<D>::NS; ++s) {
     const int d = lane + 64 * s;
-    r.seg[s].sm = stream16(tb + 16 * d);
-    r.seg[s].nib = stream8(tb + 16 * D + 8 * d);
+    r.seg[s].sm = uload16(u, 16 * d, tb);
+    r.seg[s].nib = uload8(u, 16 * D + 8 * d, tb);
   }
 }
 
