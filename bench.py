@@ -173,14 +173,15 @@ def main() -> int:
         off = heads[:, :, 8:16].view(torch.int64).squeeze(-1)
         pool_esc = int(torch.where(off != -1, cnt, torch.zeros_like(cnt)).sum().item())
         raw_frac = None
-    S = kvz.num_splits(B, Hq, H, D, P, w.max_pages, args.pages_per_split)
+    S = kvz.num_splits(B, Hq, H, D, P, w.max_pages, args.pages_per_split)   # split slots per row
     units_bytes = int(full.sum()) * H * U
     tail_bytes = int((w.seq_lens % P).sum()) * H * D * 2 * 2
-    # page-table entries, q and the (m, l, acc) partials
-    small_bytes = int(full.sum()) * H * 4 + B * Hq * D * 2 + B * Hq * S * (D + 2) * 4
-    comp_bytes = units_bytes + 2 * pool_esc + tail_bytes + small_bytes
     dense_kv_bytes = int(L.sum()) * H * D * 2 * 2
-    dense_bytes = dense_kv_bytes + int(((L + P - 1) // P).sum()) * H * 4 + B * Hq * D * 2 + B * Hq * S * (D + 2) * 4
+
+    def partial_bytes(C, pages):
+        # (m, l, acc) written per (request, query head, split) at C pages per split
+        splits = np.where(pages > 0, (pages + C - 1) // C, 1)
+        return int(splits.sum()) * Hq * (D + 2) * 4, int(splits.max())
 
     pps = args.pages_per_split
     ws = torch.empty(kvz.workspace_bytes(B, Hq, H, D, P, w.max_pages, pps), dtype=torch.uint8, device=dev)
@@ -208,6 +209,12 @@ def main() -> int:
     for _ in range(args.warmup):
         c_split()
         c_merge()
+    # the split size the kernel chose for this batch, and the bytes that follow from it:
+    # page-table entries, q and the partials
+    C_used = kvz.chosen_pages_per_split(ws, B, Hq, H, D, P, w.max_pages, pps)
+    part_bytes, splits_used = partial_bytes(C_used, full)
+    small_bytes = int(full.sum()) * H * 4 + B * Hq * D * 2 + part_bytes
+    comp_bytes = units_bytes + 2 * pool_esc + tail_bytes + small_bytes
     wall, attn_us, merge_us = run_loop(c_split, c_merge, args.steps)
     ms_per_step = wall / args.steps * 1e3
     assert int(cache.status.item()) == 0
@@ -238,6 +245,9 @@ def main() -> int:
         for _ in range(args.warmup):
             d_split()
             d_merge()
+        dC = kvz.chosen_pages_per_split(ws, B, Hq, H, D, P, w.max_pages, pps)
+        dpages = (L + P - 1) // P
+        dense_bytes = dense_kv_bytes + int(dpages.sum()) * H * 4 + B * Hq * D * 2 + partial_bytes(dC, dpages)[0]
         dwall, dattn, dmerge = run_loop(d_split, d_merge, args.steps)
         dense = dict(ms_per_step=dwall / args.steps * 1e3, attn_us=float(np.median(dattn)),
                      merge_us=float(np.median(dmerge)), bytes=dense_bytes,
@@ -279,7 +289,8 @@ def main() -> int:
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": w.name, "batch": B, "q_heads": Hq, "kv_heads": H, "head_dim": D,
-                   "context": int(w.seq_lens.max()), "page_size": P, "splits": S, "parallelism": "none (1 GPU)"},
+                   "context": int(w.seq_lens.max()), "page_size": P, "splits": splits_used,
+                   "pages_per_split": C_used, "parallelism": "none (1 GPU)"},
         "compressed_gbps": round(achieved, 1),
         "pct_peak_hbm": round(100 * achieved / PEAK_HBM_GBPS, 2),
         "uncompressed_equiv_gbps": round(dense_kv_bytes / (attn_mean * 1e-6) / 1e9, 1),
@@ -288,7 +299,7 @@ def main() -> int:
         "merge_us": round(float(np.median(merge_us)), 2),
         "compressed_bytes": comp_bytes,
         "dense_kv_bytes": dense_kv_bytes,
-        "compression_ratio": round(comp_bytes / dense_bytes, 4),
+        "compression_ratio": round((units_bytes + 2 * pool_esc + tail_bytes) / dense_kv_bytes, 4),
         "format": args.format,
         "pool_escapes": pool_esc,
         "raw_block_fraction": raw_frac,

@@ -18,6 +18,105 @@ constexpr float kLog2e = 1.4426950408889634f;
 // (m = -inf, l = 0) partial and the merge can produce zeros
 __device__ __forceinline__ int active_splits(int nfull, int C) { return nfull > 0 ? (nfull + C - 1) / C : 1; }
 
+// ---------------------------------------------------------------- split schedule
+// How one call's work is cut. Request r holds `ipr` work items (its KV heads, times the chunks
+// of query heads in the grouped-query kernels), each over the request's np_r pages (its full
+// pages; every page for the uncompressed baseline), and an item is cut into splits of C pages.
+// C is chosen on the device from the sequence lengths: the smallest C in [C_lo, C_hi] whose
+// splits, over the whole batch, fit the waves the kernel keeps resident at once (`slots`), so
+// that a batch of uneven lengths still fills the GPU in one pass rather than leaving waves idle
+// behind its longest requests. C_lo bounds the splits of one item (the workspace holds S of
+// them); C_lo == C_hi fixes C. The launch's first wave records C after the partials, where the
+// merge reads it.
+struct SplitPlan {
+  int S;           // partial slots per (request, query head)
+  int C_lo, C_hi;  // bounds on the pages per split
+  int slots;       // waves of the kernel resident at once on the device
+  int* chosen;     // the pages per split used, written by the launch's first wave
+};
+
+struct WorkItem {
+  int r;    // request
+  int k;    // item within the request
+  int s;    // split of the item
+  int C;    // pages per split
+};
+
+__device__ __forceinline__ int plan_pages(int32_t L, int P, int max_pages, bool dense) {
+  L = L < 0 ? 0 : min(L, max_pages * P);
+  return dense ? (L + P - 1) / P : L / P;
+}
+
+// splits of all requests at C pages per split (one item each), wave-uniform
+__device__ __forceinline__ uint64_t plan_total(const int32_t* seq_lens, int B, int P, int max_pages, bool dense, int C,
+                                               int lane) {
+  uint64_t t = 0;
+  for (int b0 = 0; b0 < B; b0 += 64) {
+    const int r = b0 + lane;
+    const uint32_t n = r < B ? (uint32_t)active_splits(plan_pages(seq_lens[r], P, max_pages, dense), C) : 0u;
+    t += readlane(wave_incl_scan(n), 63);
+  }
+  return t;
+}
+
+// This wave's split (waves are numbered request by request, item by item, split by split);
+// false when the wave has none.
+__device__ __forceinline__ bool plan_work(const SplitPlan& pl, const int32_t* seq_lens, int B, int P, int max_pages,
+                                          bool dense, int ipr, int wave_id, int lane, WorkItem& w) {
+  int C = pl.C_lo;
+  if (pl.C_hi > pl.C_lo && plan_total(seq_lens, B, P, max_pages, dense, C, lane) * ipr > (uint64_t)pl.slots) {
+    int lo = pl.C_lo + 1, hi = pl.C_hi;   // the total only falls as C grows
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (plan_total(seq_lens, B, P, max_pages, dense, mid, lane) * ipr <= (uint64_t)pl.slots) hi = mid;
+      else lo = mid + 1;
+    }
+    C = lo;
+  }
+  if (wave_id == 0 && lane == 0) *pl.chosen = C;
+  uint64_t base = 0;
+  for (int b0 = 0; b0 < B; b0 += 64) {
+    const int r = b0 + lane;
+    const uint32_t sr = r < B ? (uint32_t)active_splits(plan_pages(seq_lens[r], P, max_pages, dense), C) : 0u;
+    const uint32_t cnt = sr * (uint32_t)ipr;
+    const uint32_t incl = wave_incl_scan(cnt);
+    const uint64_t hit = ballot(base + incl > (uint64_t)wave_id);
+    if (hit) {
+      const int l = __builtin_ctzll(hit);
+      const uint32_t local = (uint32_t)((uint64_t)wave_id - base) - readlane(incl - cnt, l);
+      const uint32_t n = readlane(sr, l);
+      w.r = b0 + l;
+      w.k = (int)(local / n);
+      w.s = (int)(local % n);
+      w.C = C;
+      return true;
+    }
+    base += readlane(incl, 63);
+  }
+  return false;
+}
+
+// waves of `kernel` (launched with `threads` per workgroup) resident at once on the current
+// device, cached per device in `cache`; 0 when the runtime cannot say
+template <typename F>
+inline int resident_waves(F kernel, int threads, int* cache, int ncache) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= ncache) return 0;
+  if (cache[dev] > 0) return cache[dev];
+  int blocks = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, kernel, threads, 0) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  cache[dev] = blocks * (threads / 64) * cus;
+  return cache[dev];
+}
+
+// workgroups to launch: every split the plan can produce gets a wave
+inline unsigned plan_blocks(const SplitPlan& pl, long items, int waves_per_block) {
+  const long fixed = items * pl.S;                                   // C fixed: at most S per item
+  const long waves = pl.C_hi > pl.C_lo ? (pl.slots > items ? (long)pl.slots : items) : fixed;
+  return (unsigned)((waves + waves_per_block - 1) / waves_per_block);
+}
+
 struct Partials {
   float* acc;   // [rows][S][D]
   float* ml;    // [rows][S][2]

@@ -114,12 +114,13 @@ template <int D>
 __global__ __launch_bounds__(64 * kDenseWaves) void attn_dense_mha_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_pages, const uint16_t* __restrict__ v_pages,
     const int32_t* __restrict__ page_table, int max_pages, const int32_t* __restrict__ seq_lens, int B, int H, int P,
-    int num_pages, int S, int C, float scale, float* __restrict__ ws_acc, float* __restrict__ ws_ml,
+    int num_pages, SplitPlan plan, float scale, float* __restrict__ ws_acc, float* __restrict__ ws_ml,
     uint32_t* __restrict__ status) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int item = (int)uniform(blockIdx.x * kDenseWaves + wave);
-  if (item >= B * H * S) return;
-  const int s = item % S, h = (item / S) % H, r = item / (S * H);
+  WorkItem wi;
+  if (!plan_work(plan, seq_lens, B, P, max_pages, true, H, (int)uniform(blockIdx.x * kDenseWaves + wave), lane, wi))
+    return;
+  const int S = plan.S, C = wi.C, s = wi.s, h = wi.k, r = wi.r;
   int L = sload<int32_t>(seq_lens + r);
   if (L > max_pages * P || L < 0) {
     if (lane == 0 && s == 0 && h == 0 && status) atomicOr(status, kStatusSeqTooLong);
@@ -179,18 +180,26 @@ __global__ __launch_bounds__(64 * kDenseWaves) void attn_dense_mha_kernel(
 }
 
 int launch_attn_dense_mha(const uint16_t* q, const uint16_t* k_pages, const uint16_t* v_pages, const int32_t* pt,
-                          int max_pages, const int32_t* seq_lens, int B, int H, int D, int P, int num_pages, int S,
-                          int C, float scale, float* ws_acc, float* ws_ml, uint32_t* status, hipStream_t stream) {
-  const int items = B * H * S;
-  dim3 grid((unsigned)(items + kDenseWaves - 1) / kDenseWaves), block(64 * kDenseWaves);
+                          int max_pages, const int32_t* seq_lens, int B, int H, int D, int P, int num_pages,
+                          SplitPlan plan, float scale, float* ws_acc, float* ws_ml, uint32_t* status,
+                          hipStream_t stream) {
+  static int slots128[64], slots64[64];
+  const dim3 block(64 * kDenseWaves);
+  if (D == 128) {
+    plan.slots = resident_waves(attn_dense_mha_kernel<128>, block.x, slots128, 64);
+  } else if (D == 64) {
+    plan.slots = resident_waves(attn_dense_mha_kernel<64>, block.x, slots64, 64);
+  } else {
+    return -2;
+  }
+  if (plan.slots <= 0) plan.slots = B * H * plan.S;
+  const dim3 grid(plan_blocks(plan, (long)B * H, kDenseWaves));
   if (D == 128)
     hipLaunchKernelGGL((attn_dense_mha_kernel<128>), grid, block, 0, stream, q, k_pages, v_pages, pt, max_pages,
-                       seq_lens, B, H, P, num_pages, S, C, scale, ws_acc, ws_ml, status);
-  else if (D == 64)
-    hipLaunchKernelGGL((attn_dense_mha_kernel<64>), grid, block, 0, stream, q, k_pages, v_pages, pt, max_pages,
-                       seq_lens, B, H, P, num_pages, S, C, scale, ws_acc, ws_ml, status);
+                       seq_lens, B, H, P, num_pages, plan, scale, ws_acc, ws_ml, status);
   else
-    return -2;
+    hipLaunchKernelGGL((attn_dense_mha_kernel<64>), grid, block, 0, stream, q, k_pages, v_pages, pt, max_pages,
+                       seq_lens, B, H, P, num_pages, plan, scale, ws_acc, ws_ml, status);
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 

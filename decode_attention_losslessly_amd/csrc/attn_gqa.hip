@@ -270,15 +270,17 @@ __global__ __launch_bounds__(64 * kGqaWaves) KVZ_GQA_OCCUPANCY void attn_gqa_ker
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ units, const uint16_t* __restrict__ pool,
     int64_t pool_cap, const uint16_t* __restrict__ k_tail, const uint16_t* __restrict__ v_tail,
     const int32_t* __restrict__ page_table, int max_pages, const int32_t* __restrict__ seq_lens, int B, int Hq, int H,
-    int P, int num_pages, int S, int C, float scale, float* __restrict__ ws_acc, float* __restrict__ ws_ml,
+    int P, int num_pages, SplitPlan plan, float scale, float* __restrict__ ws_acc, float* __restrict__ ws_ml,
     uint32_t* __restrict__ status) {
   __shared__ __align__(16) uint16_t esc_all[kGqaWaves][esc_lds_elems<128>()];
   __shared__ uint32_t vlds_all[kGqaWaves][128 * 8];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int grp = Hq / H, nchunks = (grp + kGqaRows - 1) / kGqaRows;
-  const int item = (int)uniform(blockIdx.x * kGqaWaves + wave);
-  if (item >= B * H * nchunks * S) return;
-  const int s = item % S, qc = (item / S) % nchunks, h = (item / (S * nchunks)) % H, r = item / (S * nchunks * H);
+  WorkItem wi;
+  if (!plan_work(plan, seq_lens, B, P, max_pages, false, H * nchunks, (int)uniform(blockIdx.x * kGqaWaves + wave),
+                 lane, wi))
+    return;
+  const int S = plan.S, C = wi.C, s = wi.s, qc = wi.k % nchunks, h = wi.k / nchunks, r = wi.r;
   const int hq0 = h * grp + qc * kGqaRows, nq = min(kGqaRows, grp - qc * kGqaRows);
   int L = sload<int32_t>(seq_lens + r);
   if (L > max_pages * P || L < 0) {
@@ -379,14 +381,16 @@ __global__ __launch_bounds__(64 * kGqaWaves) KVZ_GQA_OCCUPANCY void attn_gqa_ker
 __global__ __launch_bounds__(64 * kGqaWaves) KVZ_GQA_OCCUPANCY void attn_dense_gqa_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_pages, const uint16_t* __restrict__ v_pages,
     const int32_t* __restrict__ page_table, int max_pages, const int32_t* __restrict__ seq_lens, int B, int Hq, int H,
-    int P, int num_pages, int S, int C, float scale, float* __restrict__ ws_acc, float* __restrict__ ws_ml,
+    int P, int num_pages, SplitPlan plan, float scale, float* __restrict__ ws_acc, float* __restrict__ ws_ml,
     uint32_t* __restrict__ status) {
   __shared__ uint32_t vlds_all[kGqaWaves][128 * 8];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int grp = Hq / H, nchunks = (grp + kGqaRows - 1) / kGqaRows;
-  const int item = (int)uniform(blockIdx.x * kGqaWaves + wave);
-  if (item >= B * H * nchunks * S) return;
-  const int s = item % S, qc = (item / S) % nchunks, h = (item / (S * nchunks)) % H, r = item / (S * nchunks * H);
+  WorkItem wi;
+  if (!plan_work(plan, seq_lens, B, P, max_pages, true, H * nchunks, (int)uniform(blockIdx.x * kGqaWaves + wave),
+                 lane, wi))
+    return;
+  const int S = plan.S, C = wi.C, s = wi.s, qc = wi.k % nchunks, h = wi.k / nchunks, r = wi.r;
   const int hq0 = h * grp + qc * kGqaRows, nq = min(kGqaRows, grp - qc * kGqaRows);
   int L = sload<int32_t>(seq_lens + r);
   if (L > max_pages * P || L < 0) {
@@ -449,30 +453,34 @@ __global__ __launch_bounds__(64 * kGqaWaves) KVZ_GQA_OCCUPANCY void attn_dense_g
   gqa_store(st, r, Hq, hq0, nq, S, s, ws_acc, ws_ml, lane);
 }
 
-static unsigned gqa_blocks(int B, int Hq, int H, int S) {
-  const int grp = Hq / H, nchunks = (grp + kGqaRows - 1) / kGqaRows;
-  const long items = (long)B * H * nchunks * S;
-  return (unsigned)((items + kGqaWaves - 1) / kGqaWaves);
-}
+static int gqa_items(int B, int Hq, int H) { return B * H * ((Hq / H + kGqaRows - 1) / kGqaRows); }
 
 int launch_attn_gqa(const uint16_t* q, const uint8_t* units, const uint16_t* pool, int64_t pool_cap, const uint16_t* k_tail,
                     const uint16_t* v_tail, const int32_t* page_table, int max_pages, const int32_t* seq_lens,
-                    int B, int Hq, int H, int D, int P, int num_pages, int S, int C, float scale, float* ws_acc,
+                    int B, int Hq, int H, int D, int P, int num_pages, SplitPlan plan, float scale, float* ws_acc,
                     float* ws_ml, uint32_t* status, hipStream_t stream) {
   if (D != 128) return -2;
-  hipLaunchKernelGGL(attn_gqa_kernel, dim3(gqa_blocks(B, Hq, H, S)), dim3(64 * kGqaWaves), 0, stream, q, units, pool,
-                     pool_cap, k_tail, v_tail, page_table, max_pages, seq_lens, B, Hq, H, P, num_pages, S, C, scale, ws_acc,
-                     ws_ml, status);
+  static int slots[64];
+  const dim3 block(64 * kGqaWaves);
+  plan.slots = resident_waves(attn_gqa_kernel, block.x, slots, 64);
+  if (plan.slots <= 0) plan.slots = gqa_items(B, Hq, H) * plan.S;
+  hipLaunchKernelGGL(attn_gqa_kernel, dim3(plan_blocks(plan, gqa_items(B, Hq, H), kGqaWaves)), block, 0, stream, q, units,
+                     pool, pool_cap, k_tail, v_tail, page_table, max_pages, seq_lens, B, Hq, H, P, num_pages, plan, scale,
+                     ws_acc, ws_ml, status);
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 
 int launch_attn_dense_gqa(const uint16_t* q, const uint16_t* k_pages, const uint16_t* v_pages, const int32_t* pt,
                           int max_pages, const int32_t* seq_lens, int B, int Hq, int H, int D, int P, int num_pages,
-                          int S, int C, float scale, float* ws_acc, float* ws_ml, uint32_t* status,
+                          SplitPlan plan, float scale, float* ws_acc, float* ws_ml, uint32_t* status,
                           hipStream_t stream) {
   if (D != 128) return -2;
-  hipLaunchKernelGGL(attn_dense_gqa_kernel, dim3(gqa_blocks(B, Hq, H, S)), dim3(64 * kGqaWaves), 0, stream, q,
-                     k_pages, v_pages, pt, max_pages, seq_lens, B, Hq, H, P, num_pages, S, C, scale, ws_acc, ws_ml,
+  static int slots[64];
+  const dim3 block(64 * kGqaWaves);
+  plan.slots = resident_waves(attn_dense_gqa_kernel, block.x, slots, 64);
+  if (plan.slots <= 0) plan.slots = gqa_items(B, Hq, H) * plan.S;
+  hipLaunchKernelGGL(attn_dense_gqa_kernel, dim3(plan_blocks(plan, gqa_items(B, Hq, H), kGqaWaves)), block, 0, stream,
+                     q, k_pages, v_pages, pt, max_pages, seq_lens, B, Hq, H, P, num_pages, plan, scale, ws_acc, ws_ml,
                      status);
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }

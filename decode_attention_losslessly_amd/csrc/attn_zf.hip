@@ -96,12 +96,13 @@ __global__ __launch_bounds__(64 * kZfWaves) void attn_zf_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ units, const uint16_t* __restrict__ pool,
     int64_t pool_cap, const uint16_t* __restrict__ k_tail, const uint16_t* __restrict__ v_tail,
     const int32_t* __restrict__ page_table, int max_pages, const int32_t* __restrict__ seq_lens, int B, int H, int P,
-    int num_pages, int S, int C, float scale, float* __restrict__ ws_acc, float* __restrict__ ws_ml,
+    int num_pages, SplitPlan plan, float scale, float* __restrict__ ws_acc, float* __restrict__ ws_ml,
     uint32_t* __restrict__ status) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int item = (int)uniform(blockIdx.x * kZfWaves + wave);
-  if (item >= B * H * S) return;
-  const int s = item % S, h = (item / S) % H, r = item / (S * H);
+  WorkItem wi;
+  if (!plan_work(plan, seq_lens, B, P, max_pages, false, H, (int)uniform(blockIdx.x * kZfWaves + wave), lane, wi))
+    return;
+  const int S = plan.S, C = wi.C, s = wi.s, h = wi.k, r = wi.r;
   int L = sload<int32_t>(seq_lens + r);
   if (L > max_pages * P || L < 0) {
     if (lane == 0 && s == 0 && h == 0) atomicOr(status, kStatusSeqTooLong);
@@ -222,18 +223,25 @@ __global__ __launch_bounds__(64) void decompress_zf_kernel(const uint8_t* __rest
 
 int launch_attn_zf(const uint16_t* q, const uint8_t* units, const uint16_t* pool, int64_t pool_cap,
                    const uint16_t* k_tail, const uint16_t* v_tail, const int32_t* page_table, int max_pages,
-                   const int32_t* seq_lens, int B, int H, int D, int P, int num_pages, int S, int C, float scale,
+                   const int32_t* seq_lens, int B, int H, int D, int P, int num_pages, SplitPlan plan, float scale,
                    float* ws_acc, float* ws_ml, uint32_t* status, hipStream_t stream) {
-  const int items = B * H * S;
-  dim3 grid((unsigned)(items + kZfWaves - 1) / kZfWaves), block(64 * kZfWaves);
+  static int slots128[64], slots64[64];
+  const dim3 block(64 * kZfWaves);
+  if (D == 128) {
+    plan.slots = resident_waves(attn_zf_kernel<128>, block.x, slots128, 64);
+  } else if (D == 64) {
+    plan.slots = resident_waves(attn_zf_kernel<64>, block.x, slots64, 64);
+  } else {
+    return -2;
+  }
+  if (plan.slots <= 0) plan.slots = B * H * plan.S;
+  const dim3 grid(plan_blocks(plan, (long)B * H, kZfWaves));
   if (D == 128)
     hipLaunchKernelGGL((attn_zf_kernel<128>), grid, block, 0, stream, q, units, pool, pool_cap, k_tail, v_tail,
-                       page_table, max_pages, seq_lens, B, H, P, num_pages, S, C, scale, ws_acc, ws_ml, status);
-  else if (D == 64)
-    hipLaunchKernelGGL((attn_zf_kernel<64>), grid, block, 0, stream, q, units, pool, pool_cap, k_tail, v_tail,
-                       page_table, max_pages, seq_lens, B, H, P, num_pages, S, C, scale, ws_acc, ws_ml, status);
+                       page_table, max_pages, seq_lens, B, H, P, num_pages, plan, scale, ws_acc, ws_ml, status);
   else
-    return -2;
+    hipLaunchKernelGGL((attn_zf_kernel<64>), grid, block, 0, stream, q, units, pool, pool_cap, k_tail, v_tail,
+                       page_table, max_pages, seq_lens, B, H, P, num_pages, plan, scale, ws_acc, ws_ml, status);
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 

@@ -3,7 +3,7 @@
 #include <hip/hip_runtime.h>
 
 #include "kvz.h"
-#include "kvz_device.hpp"
+#include "attn_common.hpp"
 #include "zf.hpp"
 
 namespace kvz {
@@ -19,36 +19,38 @@ int launch_append(const uint16_t* k_new, const uint16_t* v_new, const int32_t* p
                   int format, hipStream_t stream);
 int launch_attn_zf(const uint16_t* q, const uint8_t* units, const uint16_t* pool, int64_t pool_cap,
                    const uint16_t* k_tail, const uint16_t* v_tail, const int32_t* page_table, int max_pages,
-                   const int32_t* seq_lens, int B, int H, int D, int P, int num_pages, int S, int C, float scale,
+                   const int32_t* seq_lens, int B, int H, int D, int P, int num_pages, SplitPlan plan, float scale,
                    float* ws_acc, float* ws_ml, uint32_t* status, hipStream_t stream);
 int launch_decompress_zf(const uint8_t* units, const uint16_t* pool, int64_t pool_cap, const int32_t* page_ids, int n,
                          int H, int P, int D, int num_pages, uint16_t* k_dst, uint16_t* v_dst, uint32_t* status,
                          hipStream_t stream);
 int launch_attn_mha(const uint16_t* q, const uint8_t* units, const uint16_t* pool, int64_t pool_cap, const uint16_t* k_tail,
                     const uint16_t* v_tail, const int32_t* page_table, int max_pages, const int32_t* seq_lens,
-                    int B, int H, int D, int P, int num_pages, int S, int C, float scale, float* ws_acc,
+                    int B, int H, int D, int P, int num_pages, SplitPlan plan, float scale, float* ws_acc,
                     float* ws_ml, uint32_t* status, hipStream_t stream);
 int launch_attn_gqa(const uint16_t* q, const uint8_t* units, const uint16_t* pool, int64_t pool_cap, const uint16_t* k_tail,
                     const uint16_t* v_tail, const int32_t* page_table, int max_pages, const int32_t* seq_lens,
-                    int B, int Hq, int Hkv, int D, int P, int num_pages, int S, int C, float scale, float* ws_acc,
+                    int B, int Hq, int Hkv, int D, int P, int num_pages, SplitPlan plan, float scale, float* ws_acc,
                     float* ws_ml, uint32_t* status, hipStream_t stream);
 int launch_attn_dense_mha(const uint16_t* q, const uint16_t* k_pages, const uint16_t* v_pages, const int32_t* pt,
-                          int max_pages, const int32_t* seq_lens, int B, int H, int D, int P, int num_pages, int S,
-                          int C, float scale, float* ws_acc, float* ws_ml, uint32_t* status, hipStream_t stream);
+                          int max_pages, const int32_t* seq_lens, int B, int H, int D, int P, int num_pages,
+                          SplitPlan plan, float scale, float* ws_acc, float* ws_ml, uint32_t* status,
+                          hipStream_t stream);
 int launch_attn_dense_gqa(const uint16_t* q, const uint16_t* k_pages, const uint16_t* v_pages, const int32_t* pt,
                           int max_pages, const int32_t* seq_lens, int B, int Hq, int Hkv, int D, int P,
-                          int num_pages, int S, int C, float scale, float* ws_acc, float* ws_ml, uint32_t* status,
+                          int num_pages, SplitPlan plan, float scale, float* ws_acc, float* ws_ml, uint32_t* status,
                           hipStream_t stream);
 int launch_compact_pool(uint8_t* units, const uint16_t* pool, int64_t pool_cap, const int32_t* page_ids, int n, int H,
                         int P, int D, int num_pages, int format, uint16_t* new_pool, int64_t new_cap,
                         uint64_t* new_cursor, uint32_t* status, hipStream_t stream);
 int launch_merge(const float* ws_acc, const float* ws_ml, const int32_t* seq_lens, int B, int Hq, int D, int P,
-                 int max_pages, int S, int C, int dense, uint16_t* out, float* out_f32, hipStream_t stream);
+                 int max_pages, int S, const int32_t* chosen, int dense, uint16_t* out, float* out_f32,
+                 hipStream_t stream);
 }  // namespace kvz
 
 namespace {
 
-constexpr int kTargetItems = 4096;   // work items aimed for: ~16 waves per CU on 256 CUs
+constexpr int kTargetItems = 4096;   // splits aimed for: ~16 waves per CU on 256 CUs
 constexpr int kGqaRows = 8;          // query heads per grouped-query wave
 
 int work_items_per_split(int B, int Hq, int Hkv) {
@@ -57,12 +59,17 @@ int work_items_per_split(int B, int Hq, int Hkv) {
   return B * Hkv * chunks;
 }
 
+// Pages per split: `pps` when the caller fixes it, else the smallest the kernels may choose.
+// The kernels pick the split size per call from the sequence lengths (the smallest one whose
+// splits fit their resident waves); this lower bound keeps the splits of one item, and so the
+// workspace, to about twice the split count that would fill kTargetItems waves with the batch's
+// items, and a split to at least 64 tokens.
 int pages_per_split(int B, int Hq, int Hkv, int P, int max_pages, int pps) {
   if (pps > 0) return pps;
   const long items = work_items_per_split(B, Hq, Hkv);
-  const long s_target = items >= kTargetItems ? 1 : (kTargetItems + items - 1) / items;
+  const long s_cap = items >= 2 * kTargetItems ? 1 : (2 * kTargetItems + items - 1) / items;
   const int min_c = P >= 64 ? 1 : 64 / P;
-  long c = (max_pages + s_target - 1) / s_target;
+  long c = (max_pages + s_cap - 1) / s_cap;
   if (c < min_c) c = min_c;
   if (c < 1) c = 1;
   return (int)c;
@@ -100,8 +107,22 @@ int32_t kvz_num_splits(int32_t B, int32_t H_q, int32_t H_kv, int32_t D, int32_t 
   return split_count(max_pages_per_seq, pages_per_split(B, H_q, H_kv, P, max_pages_per_seq, pps));
 }
 
-// workspace per (request, query head, split): acc[D] and (m, l) as float
-static size_t ws_bytes(int B, int Hq, int S, int D) { return (size_t)B * Hq * S * (D + 2) * sizeof(float); }
+// workspace: per (request, query head, split) acc[D] and (m, l) as float, then one 16-byte slot
+// where the split kernel records the pages per split it used
+static size_t ws_partial_bytes(int B, int Hq, int S, int D) { return (size_t)B * Hq * S * (D + 2) * sizeof(float); }
+static size_t ws_bytes(int B, int Hq, int S, int D) { return ws_partial_bytes(B, Hq, S, D) + 16; }
+static int32_t* ws_chosen(void* ws, int B, int Hq, int S, int D) {
+  return reinterpret_cast<int32_t*>(static_cast<char*>(ws) + ws_partial_bytes(B, Hq, S, D));
+}
+static kvz::SplitPlan make_plan(int C, int S, int max_pages, bool fixed, int32_t* chosen) {
+  kvz::SplitPlan p;
+  p.S = S;
+  p.C_lo = C;
+  p.C_hi = fixed ? C : (max_pages > C ? max_pages : C);
+  p.slots = 0;   // filled in by the launch from the kernel's occupancy
+  p.chosen = chosen;
+  return p;
+}
 
 size_t kvz_workspace_bytes(int32_t B, int32_t H_q, int32_t H_kv, int32_t D, int32_t P, int32_t max_pages_per_seq,
                            int32_t pps) {
@@ -157,17 +178,18 @@ int kvz_decode_attention_splits(const uint16_t* q, const kvz_cache* c, const int
   float* ws_acc = reinterpret_cast<float*>(workspace);
   float* ws_ml = ws_acc + (size_t)B * H_q * S * D;
   const float scale = sm_scale * 1.4426950408889634f;
+  const kvz::SplitPlan plan = make_plan(C, S, max_pages, pps > 0, ws_chosen(workspace, B, H_q, S, D));
   if (c->format == KVZ_FORMAT_ZIPFUSION) {
     if (H_q != H) return KVZ_ERR_UNSUPPORTED;
     rc = kvz::launch_attn_zf(q, c->units, c->esc_pool, c->esc_capacity, c->k_tail, c->v_tail, page_table, max_pages,
-                             seq_lens, B, H, D, P, c->num_pages, S, C, scale, ws_acc, ws_ml, c->status,
+                             seq_lens, B, H, D, P, c->num_pages, plan, scale, ws_acc, ws_ml, c->status,
                              as_stream(stream));
   } else if (H_q == H)
     rc = kvz::launch_attn_mha(q, c->units, c->esc_pool, c->esc_capacity, c->k_tail, c->v_tail, page_table, max_pages, seq_lens, B, H,
-                              D, P, c->num_pages, S, C, scale, ws_acc, ws_ml, c->status, as_stream(stream));
+                              D, P, c->num_pages, plan, scale, ws_acc, ws_ml, c->status, as_stream(stream));
   else
     rc = kvz::launch_attn_gqa(q, c->units, c->esc_pool, c->esc_capacity, c->k_tail, c->v_tail, page_table, max_pages, seq_lens, B,
-                              H_q, H, D, P, c->num_pages, S, C, scale, ws_acc, ws_ml, c->status,
+                              H_q, H, D, P, c->num_pages, plan, scale, ws_acc, ws_ml, c->status,
                               as_stream(stream));
   return rc ? (rc == -2 ? KVZ_ERR_UNSUPPORTED : KVZ_ERR_HIP) : KVZ_OK;
 }
@@ -188,12 +210,13 @@ int kvz_decode_attention_dense_splits(const uint16_t* q, const uint16_t* k_pages
   float* ws_acc = reinterpret_cast<float*>(workspace);
   float* ws_ml = ws_acc + (size_t)B * H_q * S * D;
   const float scale = sm_scale * 1.4426950408889634f;
+  const kvz::SplitPlan plan = make_plan(C, S, max_pages, pps > 0, ws_chosen(workspace, B, H_q, S, D));
   if (H_q == H)
-    rc = kvz::launch_attn_dense_mha(q, k_pages, v_pages, page_table, max_pages, seq_lens, B, H, D, P, num_pages, S, C,
+    rc = kvz::launch_attn_dense_mha(q, k_pages, v_pages, page_table, max_pages, seq_lens, B, H, D, P, num_pages, plan,
                                     scale, ws_acc, ws_ml, status, as_stream(stream));
   else
     rc = kvz::launch_attn_dense_gqa(q, k_pages, v_pages, page_table, max_pages, seq_lens, B, H_q, H, D, P, num_pages,
-                                    S, C, scale, ws_acc, ws_ml, status, as_stream(stream));
+                                    plan, scale, ws_acc, ws_ml, status, as_stream(stream));
   return rc ? (rc == -2 ? KVZ_ERR_UNSUPPORTED : KVZ_ERR_HIP) : KVZ_OK;
 }
 
@@ -209,7 +232,8 @@ int kvz_merge_splits(const void* workspace, size_t workspace_bytes, const int32_
   if (workspace_bytes < ws_bytes(B, H_q, S, D)) return KVZ_ERR_WORKSPACE;
   const float* ws_acc = reinterpret_cast<const float*>(workspace);
   const float* ws_ml = ws_acc + (size_t)B * H_q * S * D;
-  rc = kvz::launch_merge(ws_acc, ws_ml, seq_lens, B, H_q, D, P, max_pages, S, C, dense ? 1 : 0, out, out_f32,
+  rc = kvz::launch_merge(ws_acc, ws_ml, seq_lens, B, H_q, D, P, max_pages, S,
+                         ws_chosen(const_cast<void*>(workspace), B, H_q, S, D), dense ? 1 : 0, out, out_f32,
                          as_stream(stream));
   return rc ? KVZ_ERR_HIP : KVZ_OK;
 }

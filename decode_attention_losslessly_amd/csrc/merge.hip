@@ -2,6 +2,7 @@
 // (the pages merge split results after attention and count the merge in its time: ZipFusion
 // summary, §IV.B "Attention Kernel Performance").
 //   M = max_s m_s,  w_s = 2^(m_s - M),  o = sum_s w_s acc_s / sum_s w_s l_s
+// The pages per split that the split kernel used are read from where it recorded them.
 // Output in BF16 (round to nearest even) and optionally in fp32; zeros when the request is empty.
 //
 // W waves per row: every wave reads all the maxima (one vector load per 64 splits) and takes the
@@ -17,8 +18,9 @@ namespace kvz {
 template <int D, int W, int R>
 __global__ __launch_bounds__(64 * W * R) void merge_kernel(const float* __restrict__ ws_acc, const float* __restrict__ ws_ml,
                                                        const int32_t* __restrict__ seq_lens, int B, int Hq, int P,
-                                                       int max_pages, int S, int C, int dense,
-                                                       uint16_t* __restrict__ out, float* __restrict__ out_f32) {
+                                                       int max_pages, int S, const int32_t* __restrict__ chosen,
+                                                       int dense, uint16_t* __restrict__ out,
+                                                       float* __restrict__ out_f32) {
   constexpr int NV = D / 64;
   __shared__ float sh_num[W][D];
   __shared__ float sh_den[W];
@@ -31,7 +33,7 @@ __global__ __launch_bounds__(64 * W * R) void merge_kernel(const float* __restri
   int L = sload<int32_t>(seq_lens + r);
   L = L < 0 ? 0 : min(L, max_pages * P);
   const int npages = dense ? (L + P - 1) / P : L / P;
-  const int Sr = active_splits(npages, C);
+  const int Sr = min(active_splits(npages, max(1, sload<int32_t>(chosen))), S);
   const float* ml = ws_ml + (size_t)row * S * 2;
   const float* acc = ws_acc + (size_t)row * S * D;
   float M = -INFINITY;
@@ -90,14 +92,15 @@ __global__ __launch_bounds__(64 * W * R) void merge_kernel(const float* __restri
 }
 
 int launch_merge(const float* ws_acc, const float* ws_ml, const int32_t* seq_lens, int B, int Hq, int D, int P,
-                 int max_pages, int S, int C, int dense, uint16_t* out, float* out_f32, hipStream_t stream) {
+                 int max_pages, int S, const int32_t* chosen, int dense, uint16_t* out, float* out_f32,
+                 hipStream_t stream) {
   const int rows = B * Hq;
   const int shape = S <= 8 ? 0 : (rows < 1024 ? 2 : 1);   // 0: a wave per row, 1: 4 waves, 2: 16 waves
   const unsigned blocks = shape == 0 ? (unsigned)(rows + 3) / 4 : (unsigned)rows;
   const unsigned threads = shape == 2 ? 1024 : 256;
 #define KVZ_MERGE(DD, WW, RR)                                                                                  \
   hipLaunchKernelGGL((merge_kernel<DD, WW, RR>), dim3(blocks), dim3(threads), 0, stream, ws_acc, ws_ml, seq_lens, \
-                     B, Hq, P, max_pages, S, C, dense, out, out_f32)
+                     B, Hq, P, max_pages, S, chosen, dense, out, out_f32)
   if (D == 128) {
     if (shape == 0) KVZ_MERGE(128, 1, 4); else if (shape == 1) KVZ_MERGE(128, 4, 1); else KVZ_MERGE(128, 16, 1);
   } else if (D == 64) {

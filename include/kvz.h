@@ -124,13 +124,18 @@ size_t kvz_meta_bytes(int32_t P, int32_t D);
 int32_t kvz_inline_capacity(int32_t P, int32_t D);
 
 /* Bytes of scratch kvz_decode_attention / kvz_decode_attention_dense need: split partials
- * (acc[D], m, l) in float for every (request, query head, split). Its content needs no
- * initialisation. pages_per_split = 0 lets the library choose; the same value must be passed
- * to the attention call. */
+ * (acc[D], m, l) in float for every (request, query head, split slot), then 16 bytes where the
+ * split kernel records the pages per split it used, for the merge. Its content needs no
+ * initialisation. pages_per_split > 0 fixes the pages per split; 0 lets the kernels choose per
+ * call from the sequence lengths: the smallest split, no smaller than a bound the library sets
+ * from the shapes, whose splits over the whole batch fit the waves the kernel keeps resident,
+ * so that batches of uneven lengths fill the GPU in one pass. The same value must be passed to
+ * the attention call. */
 size_t kvz_workspace_bytes(int32_t B, int32_t H_q, int32_t H_kv, int32_t D, int32_t P,
                            int32_t max_pages_per_seq, int32_t pages_per_split);
 
-/* Number of splits the attention calls use for these arguments (host function). */
+/* Split slots per (request, query head) in the workspace: the most splits an attention call
+ * with these arguments can use (host function). */
 int32_t kvz_num_splits(int32_t B, int32_t H_q, int32_t H_kv, int32_t D, int32_t P,
                        int32_t max_pages_per_seq, int32_t pages_per_split);
 
@@ -195,7 +200,9 @@ int kvz_decode_attention_dense(const uint16_t* q, const uint16_t* k_pages,
  *   kvz_merge_splits                   merges the partials of either into out / out_f32;
  *                                      dense = 1 when they came from the dense kernel
  * Arguments mean what they mean in the one-call forms; B, H_q, H, D, P, max_pages_per_seq and
- * pages_per_split must be the same in both phases. Errors and status as the one-call forms. */
+ * pages_per_split must be the same in both phases, and the workspace must not change between
+ * them (the merge reads the split size the split kernel recorded there). Errors and status as
+ * the one-call forms. */
 int kvz_decode_attention_splits(const uint16_t* q, const kvz_cache* cache, const int32_t* page_table,
                                 int32_t max_pages_per_seq, const int32_t* seq_lens, int32_t B,
                                 int32_t H_q, float sm_scale, int32_t pages_per_split,

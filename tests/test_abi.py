@@ -43,13 +43,14 @@ def test_unsupported_shapes_have_zero_size():
 
 
 def test_split_geometry():
-    # the workspace holds (D + 2) floats per (request, query head, split)
+    # the workspace holds (D + 2) floats per (request, query head, split slot), then the
+    # 16-byte slot where the split kernel records the split size it chose
     for args in [(32, 32, 32, 128, 16, 513), (1, 32, 32, 128, 16, 256), (64, 28, 4, 128, 16, 512),
                  (4, 32, 32, 128, 16, 2048), (1, 2, 2, 64, 256, 1)]:
         S = kvz.num_splits(*args)
         B, Hq, _, D, _, mp = args
         assert S >= 1
-        assert kvz.workspace_bytes(*args) == B * Hq * S * (D + 2) * 4
+        assert kvz.workspace_bytes(*args) == B * Hq * S * (D + 2) * 4 + 16
         assert kvz.num_splits(*args, pages_per_split=mp) == 1
         assert kvz.num_splits(*args, pages_per_split=1) == mp
     # batch-1 context: enough splits to spread one request over the chip
