@@ -47,15 +47,46 @@ __device__ __forceinline__ int plan_pages(int32_t L, int P, int max_pages, bool 
   return dense ? (L + P - 1) / P : L / P;
 }
 
-// splits of all requests at C pages per split (one item each), wave-uniform
-__device__ __forceinline__ uint64_t plan_total(const int32_t* seq_lens, int B, int P, int max_pages, bool dense, int C,
+// Pages of the requests, read once: up to kPlanRegs requests per lane are held in registers
+// (a batch of up to 256), larger batches are re-read from memory at every use.
+constexpr int kPlanRegs = 4;
+struct PlanPages {
+  int np[kPlanRegs];
+  bool held;
+};
+
+__device__ __forceinline__ PlanPages plan_load(const int32_t* seq_lens, int B, int P, int max_pages, bool dense,
                                                int lane) {
-  uint64_t t = 0;
-  for (int b0 = 0; b0 < B; b0 += 64) {
-    const int r = b0 + lane;
-    const uint32_t n = r < B ? (uint32_t)active_splits(plan_pages(seq_lens[r], P, max_pages, dense), C) : 0u;
-    t += readlane(wave_incl_scan(n), 63);
+  PlanPages pp;
+  pp.held = B <= 64 * kPlanRegs;
+#pragma unroll
+  for (int j = 0; j < kPlanRegs; ++j) {
+    const int r = 64 * j + lane;
+    pp.np[j] = (pp.held && r < B) ? plan_pages(seq_lens[r], P, max_pages, dense) : -1;
   }
+  return pp;
+}
+
+// splits of request r's item at C pages per split (0 past the batch)
+__device__ __forceinline__ uint32_t plan_splits(const PlanPages& pp, const int32_t* seq_lens, int B, int P,
+                                                int max_pages, bool dense, int r, int j, int C) {
+  if (r >= B) return 0u;
+  const int np = pp.held ? pp.np[j] : plan_pages(seq_lens[r], P, max_pages, dense);
+  return (uint32_t)active_splits(np, C);
+}
+
+// splits of all requests at C pages per split (one item each), wave-uniform
+__device__ __forceinline__ uint64_t plan_total(const PlanPages& pp, const int32_t* seq_lens, int B, int P,
+                                               int max_pages, bool dense, int C, int lane) {
+  if (pp.held) {
+    uint32_t n = 0;
+#pragma unroll
+    for (int j = 0; j < kPlanRegs; ++j) n += pp.np[j] >= 0 ? (uint32_t)active_splits(pp.np[j], C) : 0u;
+    return readlane(wave_incl_scan(n), 63);
+  }
+  uint64_t t = 0;
+  for (int b0 = 0; b0 < B; b0 += 64) t += readlane(wave_incl_scan(plan_splits(pp, seq_lens, B, P, max_pages, dense,
+                                                                               b0 + lane, 0, C)), 63);
   return t;
 }
 
@@ -63,36 +94,65 @@ __device__ __forceinline__ uint64_t plan_total(const int32_t* seq_lens, int B, i
 // false when the wave has none.
 __device__ __forceinline__ bool plan_work(const SplitPlan& pl, const int32_t* seq_lens, int B, int P, int max_pages,
                                           bool dense, int ipr, int wave_id, int lane, WorkItem& w) {
+  const PlanPages pp = plan_load(seq_lens, B, P, max_pages, dense, lane);
   int C = pl.C_lo;
-  if (pl.C_hi > pl.C_lo && plan_total(seq_lens, B, P, max_pages, dense, C, lane) * ipr > (uint64_t)pl.slots) {
-    int lo = pl.C_lo + 1, hi = pl.C_hi;   // the total only falls as C grows
+  if (pl.C_hi > pl.C_lo) {
+    // With N = ipr * (pages of the batch) and `items` = ipr * B, the splits at C lie between
+    // N / C and N / C + items (the total only falls as C grows): no C below N / slots fits,
+    // and every C from N / (slots - items) on does. Search between the two.
+    uint64_t npg = 0;
+    if (pp.held) {
+      uint32_t n = 0;
+#pragma unroll
+      for (int j = 0; j < kPlanRegs; ++j) n += pp.np[j] > 0 ? (uint32_t)pp.np[j] : 0u;
+      npg = readlane(wave_incl_scan(n), 63);
+    } else {
+      for (int b0 = 0; b0 < B; b0 += 64) {
+        const int r = b0 + lane;
+        npg += readlane(wave_incl_scan(r < B ? (uint32_t)plan_pages(seq_lens[r], P, max_pages, dense) : 0u), 63);
+      }
+    }
+    const uint64_t N = npg * (uint64_t)ipr, items = (uint64_t)B * ipr, slots = (uint64_t)pl.slots;
+    int lo = (int)min((uint64_t)pl.C_hi, max((uint64_t)pl.C_lo, (N + slots - 1) / slots));
+    int hi = pl.C_hi;
+    if (slots > items) hi = (int)min((uint64_t)hi, max((uint64_t)lo, (N + slots - items - 1) / (slots - items)));
     while (lo < hi) {
       const int mid = (lo + hi) >> 1;
-      if (plan_total(seq_lens, B, P, max_pages, dense, mid, lane) * ipr <= (uint64_t)pl.slots) hi = mid;
+      if (plan_total(pp, seq_lens, B, P, max_pages, dense, mid, lane) * ipr <= slots) hi = mid;
       else lo = mid + 1;
     }
     C = lo;
   }
   if (wave_id == 0 && lane == 0) *pl.chosen = C;
+  // find the request whose splits hold this wave's number, 64 requests at a time
   uint64_t base = 0;
-  for (int b0 = 0; b0 < B; b0 += 64) {
-    const int r = b0 + lane;
-    const uint32_t sr = r < B ? (uint32_t)active_splits(plan_pages(seq_lens[r], P, max_pages, dense), C) : 0u;
+  auto visit = [&](int b0, uint32_t sr) -> bool {
     const uint32_t cnt = sr * (uint32_t)ipr;
     const uint32_t incl = wave_incl_scan(cnt);
     const uint64_t hit = ballot(base + incl > (uint64_t)wave_id);
-    if (hit) {
-      const int l = __builtin_ctzll(hit);
-      const uint32_t local = (uint32_t)((uint64_t)wave_id - base) - readlane(incl - cnt, l);
-      const uint32_t n = readlane(sr, l);
-      w.r = b0 + l;
-      w.k = (int)(local / n);
-      w.s = (int)(local % n);
-      w.C = C;
-      return true;
+    if (!hit) {
+      base += readlane(incl, 63);
+      return false;
     }
-    base += readlane(incl, 63);
+    const int l = __builtin_ctzll(hit);
+    const uint32_t local = (uint32_t)((uint64_t)wave_id - base) - readlane(incl - cnt, l);
+    const uint32_t n = readlane(sr, l);
+    w.r = b0 + l;
+    w.k = (int)(local / n);
+    w.s = (int)(local % n);
+    w.C = C;
+    return true;
+  };
+  if (pp.held) {
+#pragma unroll
+    for (int j = 0; j < kPlanRegs; ++j) {
+      if (64 * j >= B) break;
+      if (visit(64 * j, pp.np[j] >= 0 ? (uint32_t)active_splits(pp.np[j], C) : 0u)) return true;
+    }
+    return false;
   }
+  for (int b0 = 0; b0 < B; b0 += 64)
+    if (visit(b0, plan_splits(pp, seq_lens, B, P, max_pages, dense, b0 + lane, 0, C))) return true;
   return false;
 }
 

@@ -162,6 +162,32 @@ def test_empty_and_short_requests():
     assert not d16[0].any()
 
 
+@pytest.mark.parametrize("Hq,Hkv", [(4, 4), (8, 2)])
+@pytest.mark.parametrize("B", [70, 300])
+def test_many_ragged_requests(B, Hq, Hkv):
+    """The split kernels number their work from the sequence lengths (a prefix over the requests,
+    64 at a time, held in registers up to 256 requests and re-read beyond): a batch of uneven
+    lengths with empty requests among them, past one and past four blocks of 64, still gives
+    every (request, head) row exactly its attention, and empty requests zeros."""
+    rng = np.random.default_rng(B + Hq)
+    lens = rng.integers(0, 200, size=B)
+    lens[rng.choice(B, size=B // 7, replace=False)] = 0
+    w = make_workload(4, B=B, lens=lens, Hq=Hq, Hkv=Hkv, D=128, n_append=0)
+    kp, vp = w.pages(0), w.pages(1)
+    cache, lt = build_cache(w, kp, vp)
+    q = w.q()
+    o16, o32 = _run(w, cache, lt, q)
+    assert int(cache.status.item()) == 0
+    empty = np.flatnonzero(w.seq_lens == 0)
+    assert not o16[empty].any() and not o32[empty].any()
+    rows = [(r, h) for r in np.flatnonzero(w.seq_lens > 0).tolist() for h in range(w.Hq)]
+    ref = oracle_rows(w, kp, vp, q, rows)
+    idx = np.array([r * w.Hq + h for r, h in rows])
+    check_rows(o16.reshape(-1, w.D)[idx], o32.reshape(-1, w.D)[idx], ref, f"B={B}")
+    d16, d32 = _run(w, None, dev(w.seq_lens), q, dense_pages=(dev(kp), dev(vp)))
+    check_rows(d16.reshape(-1, w.D)[idx], d32.reshape(-1, w.D)[idx], ref, f"dense B={B}")
+
+
 def test_bad_page_id_sets_status():
     w = make_workload(2, B=1, L=64, Hq=2, Hkv=2)
     kp, vp = w.pages(0), w.pages(1)
