@@ -22,6 +22,7 @@
 #include "attn_common.hpp"
 #include "kvz_lanes.hpp"
 #include "mha_core.hpp"
+#include "mha_pool.hpp"
 
 namespace kvz {
 
@@ -132,10 +133,17 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void attn_mha_kernel(
   const int nsteps = (p1 > p0 ? p1 - p0 : 0) * T;
   uint32_t krank = 0, vrank = 0;
   int first_skip = -1, last_skip = -1;
+  int nskip = 0;          // tiles skipped by the main loop
+  int resume = -1;        // step from which the pool-capable loop takes over
   bool bad = false;
-  auto note = [&](const MhaStage<D>& stg) {
+  // Records a skipped (pool) tile. When most tiles so far went to the pool, the wave leaves the
+  // pipelined loop at the next page and walks the rest with the pool-capable loop, which loads
+  // a tile's escapes with its payload instead of reloading the unit after the main loop.
+  auto note = [&](const MhaStage<D>& stg, int done) {
     if (first_skip < 0) first_skip = stg.page;
     last_skip = stg.page;
+    ++nskip;
+    if (nskip >= 2 && 2 * nskip > done) resume = (stg.page - p0 + 1) * T;
   };
   if (nsteps > 0) {
     // load cursor: step ln = (page lp, tile lt); it stays on the last step once there, so the
@@ -158,13 +166,40 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void attn_mha_kernel(
       advance();
       pid = sload<int32_t>(pt_row + lp);
       bad |= !a.ok;
-      if (!mha_compute<D, false>(st, a, P, krank, vrank, lds, pool, pool_cap, scale, lane)) note(a);
-      if (i + 1 >= nsteps) break;
+      if (!mha_compute<D, false>(st, a, P, krank, vrank, lds, pool, pool_cap, scale, lane)) note(a, i + 1);
+      if (i + 1 >= nsteps || resume >= 0) break;
       mha_issue<D>(a, units, pid, lp, lt, H, h, P, num_pages, lane);
       advance();
       pid = sload<int32_t>(pt_row + lp);
       bad |= !b.ok;
-      if (!mha_compute<D, false>(st, b, P, krank, vrank, lds, pool, pool_cap, scale, lane)) note(b);
+      if (!mha_compute<D, false>(st, b, P, krank, vrank, lds, pool, pool_cap, scale, lane)) note(b, i + 2);
+      if (resume >= 0) break;
+    }
+  }
+  if (resume >= 0 && resume < nsteps) {
+    // the rest of the split, every unit as it comes; the next tile's meta window is in flight
+    // while a tile is computed
+    auto unit_of = [&](int n, bool& ok) {
+      const int pid = sload<int32_t>(pt_row + p0 + n / T);
+      ok = pid >= 0 && pid < num_pages;
+      return units + ((size_t)(ok ? pid : 0) * H + h) * unit_bytes(P, D);
+    };
+    bool ok;
+    const uint8_t* u = unit_of(resume, ok);
+    uint32_t meta = load_meta(u, P, D, resume % T, lane);
+    for (int n = resume; n < nsteps; ++n) {
+      bool nok = true;
+      const uint8_t* nu = u;
+      uint32_t nmeta = 0;
+      if (n + 1 < nsteps) {
+        nu = unit_of(n + 1, nok);
+        nmeta = load_meta(nu, P, D, (n + 1) % T, lane);
+      }
+      if (ok) mha_any_tile<D>(st, u, meta, P, n % T, krank, vrank, lds, pool, pool_cap, scale, lane);
+      bad |= !ok;
+      u = nu;
+      ok = nok;
+      meta = nmeta;
     }
   }
   if (bad && lane == 0) atomicOr(status, kStatusBadPage);

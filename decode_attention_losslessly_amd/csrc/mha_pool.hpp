@@ -1,0 +1,174 @@
+// The multi-head kernel's path for caches whose units mostly keep their escapes in the pool
+// (too many for the unit's inline area; the escape lists then live in the pool, values only,
+// in storage order: the pages' format has no escapes, so this is the build's own part of the
+// format).
+//
+// A wave that meets mostly pool units leaves the pipelined loop and walks the rest of its split
+// one tile at a time here. A tile's meta window is loaded one step ahead, so that its header
+// (pool offset and escape counts) is known when the tile's payload loads are issued: the K and
+// V escape windows that can hold the tile's escapes (from each block's cursor, at most a tile's
+// worth) are then loaded in the same round trip and written side by side into the wave's LDS
+// area, and every lane patches its own escaped positions from there with fixed register indices.
+#pragma once
+
+#include "kvz_lanes.hpp"
+#include "mha_core.hpp"
+
+namespace kvz {
+
+// u16 elements of one staged window: a tile's list (at most kTile*D values) from a 16-byte
+// aligned start (up to 7 elements before it). Two windows fill esc_lds_elems<D>().
+template <int D>
+constexpr int win_elems() { return kTile * D + 8; }
+static_assert(2 * win_elems<128>() == esc_lds_elems<128>(), "K and V windows fill the wave's LDS area");
+static_assert(2 * win_elems<64>() == esc_lds_elems<64>(), "K and V windows fill the wave's LDS area");
+
+struct Window {
+  uint32_t mis;     // element `first` sits at window[mis]
+  uint32_t avail;   // elements of the list in the window
+};
+
+template <int D>
+constexpr int win_chunks() { return (win_elems<D>() / 8 + 63) / 64; }   // 16-byte chunks per lane
+
+// One 16-byte chunk of the pool at element e0 (8 elements), read element by element where it
+// would cross the end of the pool.
+__device__ __forceinline__ uint4 pool_chunk(const uint16_t* pool, int64_t pool_cap, uint64_t e0) {
+  if (e0 + 8 <= (uint64_t)pool_cap) return *reinterpret_cast<const uint4*>(pool + e0);
+  uint32_t w[4] = {0, 0, 0, 0};
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+    if (e0 + e < (uint64_t)pool_cap) w[e >> 1] |= (uint32_t)pool[e0 + e] << (16 * (e & 1));
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+// Loads the pool ranges [kfirst, kfirst + kn) and [vfirst, vfirst + vn) (every load of both
+// issued before the first LDS write) into lds[0 ..) and lds[win_elems ..).
+template <int D>
+__device__ __forceinline__ void stage_windows(const uint16_t* pool, int64_t pool_cap, uint64_t kfirst, uint32_t kn,
+                                              uint64_t vfirst, uint32_t vn, uint16_t* lds, Window& kw, Window& vw,
+                                              int lane) {
+  constexpr int NC = win_chunks<D>();
+  const uint64_t ka = kfirst & ~7ull, va = vfirst & ~7ull;
+  kw.mis = (uint32_t)(kfirst - ka);
+  vw.mis = (uint32_t)(vfirst - va);
+  kw.avail = kn;
+  vw.avail = vn;
+  const uint32_t knch = kn ? (kw.mis + kn + 7) / 8 : 0u, vnch = vn ? (vw.mis + vn + 7) / 8 : 0u;
+  uint4 kv[NC], vv[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const uint32_t ch = (uint32_t)lane + 64u * c;
+    kv[c] = ch < knch ? pool_chunk(pool, pool_cap, ka + 8ull * ch) : make_uint4(0, 0, 0, 0);
+    vv[c] = ch < vnch ? pool_chunk(pool, pool_cap, va + 8ull * ch) : make_uint4(0, 0, 0, 0);
+  }
+  uint16_t* vl = lds + win_elems<D>();
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const uint32_t ch = (uint32_t)lane + 64u * c;
+    if (ch < knch) *reinterpret_cast<uint4*>(lds + 8 * ch) = kv[c];
+    if (ch < vnch) *reinterpret_cast<uint4*>(vl + 8 * ch) = vv[c];
+  }
+  wave_lds_sync();
+}
+
+// Patches the escaped positions of one offset word (8 positions: out[k] holds positions 2k,
+// 2k+1) from a staged window; r0 is the list rank of the word's first escape. Returns the
+// word's escape count.
+__device__ __forceinline__ uint32_t patch_word(uint32_t W, uint32_t r0, const uint16_t* win, const Window& w,
+                                               uint32_t* out) {
+  const uint32_t o = flags_in_order(escape_flags(W));   // position j at bit 4*(j/2) + j%2
+  if (o == 0) return 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int b = 4 * (j >> 1) + (j & 1);
+    const uint32_t r = r0 + (uint32_t)__builtin_popcount(o & ((1u << b) - 1u));
+    if (((o >> b) & 1u) && r < w.avail) out[j >> 1] = set_half(out[j >> 1], j & 1, win[w.mis + r]);
+  }
+  return (uint32_t)__builtin_popcount(o);
+}
+
+// K tile (multi-head lane layout: lane l holds pieces l + 64 i): ranks in storage order, then
+// every lane patches its pieces. Returns the tile's escape count.
+template <int D>
+__device__ __forceinline__ uint32_t win_patch_k(uint32_t (&pairs)[KRaw<D>::VK / 2], const KRaw<D>& raw,
+                                                const uint16_t* win, const Window& w) {
+  constexpr int NP = KRaw<D>::NP;
+  uint32_t total = 0;
+#pragma unroll
+  for (int i = 0; i < NP; ++i) {
+    // piece i of every lane precedes piece i + 1 of any lane
+    const uint32_t c0 = popc_flags(escape_flags(raw.nib[2 * i])), c1 = popc_flags(escape_flags(raw.nib[2 * i + 1]));
+    const uint32_t inc = wave_incl_scan(c0 + c1);
+    const uint32_t r = total + inc - (c0 + c1);
+    total += readlane(inc, 63);
+    patch_word(raw.nib[2 * i], r, win, w, &pairs[8 * i]);
+    patch_word(raw.nib[2 * i + 1], r + c0, win, w, &pairs[8 * i + 4]);
+  }
+  return total;
+}
+
+// V tile (lane l holds dims l + 64 s, storage order segment-major then lane). Returns the
+// tile's escape count.
+template <int D>
+__device__ __forceinline__ uint32_t win_patch_v(uint32_t (&pairs)[D / 8], const VRaw<D>& raw, const uint16_t* win,
+                                                const Window& w) {
+  constexpr int NS = D / 64;
+  uint32_t total = 0;
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const uint32_t c0 = popc_flags(escape_flags(raw.seg[s].nib.x)), c1 = popc_flags(escape_flags(raw.seg[s].nib.y));
+    const uint32_t inc = wave_incl_scan(c0 + c1);
+    const uint32_t r = total + inc - (c0 + c1);
+    total += readlane(inc, 63);
+    patch_word(raw.seg[s].nib.x, r, win, w, &pairs[8 * s]);
+    patch_word(raw.seg[s].nib.y, r + c0, win, w, &pairs[8 * s + 4]);
+  }
+  return total;
+}
+
+// One tile of any unit: `meta` is its meta window (already loaded); the payload and, for a
+// pool unit, both escape windows are loaded in one round trip. krank / vrank are the block
+// cursors (escapes in the unit's earlier tiles), reset at tile 0.
+template <int D>
+__device__ __forceinline__ void mha_any_tile(MhaState<D>& st, const uint8_t* unit, uint32_t meta, int P, int tile,
+                                             uint32_t& krank, uint32_t& vrank, uint16_t* lds, const uint16_t* pool,
+                                             int64_t pool_cap, float scale, int lane) {
+  constexpr int VK = KRaw<D>::VK, NS = D / 64;
+  UnitHeader hdr = header_from_meta<D>(meta);
+  clamp_to_pool(hdr, pool_cap);
+  if (tile == 0) { krank = 0; vrank = 0; }
+  KRaw<D> k;
+  VRaw<D> v;
+  load_k<D, false>(unit, P, tile, lane, k);
+  load_v<D>(unit, P, tile, lane, v);
+  const bool in_pool = hdr.off != kInline;
+  Window kw = {0, 0}, vw = {0, 0};
+  if (in_pool) {
+    const uint32_t kr = uniform(krank), vr = uniform(vrank);
+    const uint32_t kn = hdr.kc > kr ? min((uint32_t)(kTile * D), hdr.kc - kr) : 0u;
+    const uint32_t vn = hdr.vc > vr ? min((uint32_t)(kTile * D), hdr.vc - vr) : 0u;
+    stage_windows<D>(pool, pool_cap, hdr.off + kr, kn, hdr.off + hdr.kc + vr, vn, lds, kw, vw, lane);
+  }
+  uint32_t kp[VK / 2];
+  decode_k<D>(k, kp);
+  if (hdr.kc) {
+    if (in_pool) krank = uniform(krank) + win_patch_k<D>(kp, k, lds, kw);
+    else patch_k_tile<D, false, false>(kp, k, meta, hdr, P, tile, krank, lds, pool, pool_cap, lane);
+  }
+  float sc[D / 64];
+  mha_scores<D>(st, kp, scale, sc);
+  uint32_t phi[8], plo[8];
+  mha_softmax<D>(st, sc, phi, plo);
+  uint32_t vp[NS * 8];
+#pragma unroll
+  for (int g = 0; g < NS; ++g) decode_v_seg(v.seg[g], v_bases<D>(meta, g), &vp[8 * g]);
+  if (hdr.vc) {
+    if (in_pool) vrank = uniform(vrank) + win_patch_v<D>(vp, v, lds + win_elems<D>(), vw);
+    else patch_v_tile<D, false>(vp, v, meta, hdr, P, tile, vrank, lds, pool, pool_cap, lane);
+  }
+  mha_accumulate_v<D>(st, vp, phi, plo);
+  if (in_pool) wave_lds_sync();   // the windows are read before the next tile's staging writes
+}
+
+}  // namespace kvz

@@ -17,6 +17,7 @@ SHAPES = [  # (P, D, Hq, Hkv)
     (48, 128, 6, 3),
     (64, 128, 32, 2),
     (256, 128, 4, 1),
+    (32, 128, 4, 4),
     (16, 64, 4, 4),
     (64, 64, 8, 8),
 ]
