@@ -73,19 +73,25 @@ __device__ __forceinline__ void stage_windows(const uint16_t* pool, int64_t pool
 }
 
 // Patches the escaped positions of one offset word (8 positions: out[k] holds positions 2k,
-// 2k+1) from a staged window; r0 is the list rank of the word's first escape. Returns the
-// word's escape count.
-__device__ __forceinline__ uint32_t patch_word(uint32_t W, uint32_t r0, const uint16_t* win, const Window& w,
-                                               uint32_t* out) {
-  const uint32_t o = flags_in_order(escape_flags(W));   // position j at bit 4*(j/2) + j%2
-  if (o == 0) return 0;
+// 2k+1) from a staged window; r0 is the list rank of the word's first escape. The word is
+// walked pair by pair with a running rank, so each escaped half costs a bit test, a compare
+// and an insert.
+__device__ __forceinline__ void patch_word(uint32_t W, uint32_t r0, const uint16_t* win, const Window& w,
+                                          uint32_t* out) {
+  const uint32_t o = flags_in_order(escape_flags(W));   // pair k: bits 4k (low half), 4k+1 (high)
+  if (o == 0) return;
+  const uint32_t lim = w.mis + w.avail;
+  uint32_t r = w.mis + r0;                              // window index of the next escape
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int b = 4 * (j >> 1) + (j & 1);
-    const uint32_t r = r0 + (uint32_t)__builtin_popcount(o & ((1u << b) - 1u));
-    if (((o >> b) & 1u) && r < w.avail) out[j >> 1] = set_half(out[j >> 1], j & 1, win[w.mis + r]);
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t e0 = (o >> (4 * k)) & 1u, e1 = (o >> (4 * k + 1)) & 1u;
+    const uint32_t r1 = r + e0;
+    uint32_t v = out[k];
+    if (e0 && r < lim) v = (v & 0xFFFF0000u) | win[r];
+    if (e1 && r1 < lim) v = (v & 0x0000FFFFu) | ((uint32_t)win[r1] << 16);
+    out[k] = v;
+    r = r1 + e1;
   }
-  return (uint32_t)__builtin_popcount(o);
 }
 
 // K tile (multi-head lane layout: lane l holds pieces l + 64 i): ranks in storage order, then
