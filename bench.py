@@ -188,10 +188,33 @@ def main() -> int:
     out = torch.empty((B, Hq, D), dtype=torch.int16, device=dev)
 
     def run_loop(split_fn, merge_fn, steps):
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
-               torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        """Three timed loops on the launch stream: (1) `steps` whole steps (split kernel then
+        merge) back to back, bracketed by one event pair and the wall clock; (2) `steps` split
+        launches back to back, bracketed by one event pair: the mean launch duration of the
+        split kernel; (3) one event pair around each split and each merge launch, for their
+        spread (each pair adds a few microseconds of its own, which (2) does not carry)."""
+        def pair():
+            return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g0, g1 = pair()
         torch.cuda.synchronize()
         s0 = time.perf_counter()
+        g0.record()
+        for _ in range(steps):
+            split_fn()
+            merge_fn()
+        g1.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - s0
+        step_gpu_us = g0.elapsed_time(g1) * 1e3 / steps
+        a0, a1 = pair()
+        a0.record()
+        for _ in range(steps):
+            split_fn()
+        a1.record()
+        torch.cuda.synchronize()
+        split_mean_us = a0.elapsed_time(a1) * 1e3 / steps
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+               torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
         for e0, e1, e2 in ev:
             e0.record()
             split_fn()
@@ -199,10 +222,9 @@ def main() -> int:
             merge_fn()
             e2.record()
         torch.cuda.synchronize()
-        wall = time.perf_counter() - s0
         attn = np.array([a.elapsed_time(b) for a, b, _ in ev]) * 1e3
         merge = np.array([b.elapsed_time(c) for _, b, c in ev]) * 1e3
-        return wall, attn, merge
+        return wall, attn, merge, split_mean_us, step_gpu_us
 
     c_split = lambda: kvz.decode_attention_splits(q, cache, table, lens, w.sm_scale, ws, pages_per_split=pps)
     c_merge = lambda: kvz.merge_splits(ws, lens, B, Hq, H, D, P, w.max_pages, out, pages_per_split=pps)
@@ -215,7 +237,7 @@ def main() -> int:
     part_bytes, splits_used = partial_bytes(C_used, full)
     small_bytes = int(full.sum()) * H * 4 + B * Hq * D * 2 + part_bytes
     comp_bytes = units_bytes + 2 * pool_esc + tail_bytes + small_bytes
-    wall, attn_us, merge_us = run_loop(c_split, c_merge, args.steps)
+    wall, attn_us, merge_us, split_mean_us, step_gpu_us = run_loop(c_split, c_merge, args.steps)
     ms_per_step = wall / args.steps * 1e3
     assert int(cache.status.item()) == 0
 
@@ -248,14 +270,14 @@ def main() -> int:
         dC = kvz.chosen_pages_per_split(ws, B, Hq, H, D, P, w.max_pages, pps)
         dpages = (L + P - 1) // P
         dense_bytes = dense_kv_bytes + int(dpages.sum()) * H * 4 + B * Hq * D * 2 + partial_bytes(dC, dpages)[0]
-        dwall, dattn, dmerge = run_loop(d_split, d_merge, args.steps)
+        dwall, dattn, dmerge, dsplit_mean, dstep_gpu = run_loop(d_split, d_merge, args.steps)
         dense = dict(ms_per_step=dwall / args.steps * 1e3, attn_us=float(np.median(dattn)),
-                     merge_us=float(np.median(dmerge)), bytes=dense_bytes,
-                     gbps=dense_bytes / (np.mean(dattn) * 1e-6) / 1e9,
-                     pct_peak=100 * dense_bytes / (np.mean(dattn) * 1e-6) / 1e9 / PEAK_HBM_GBPS,
+                     attn_us_mean=dsplit_mean, merge_us=float(np.median(dmerge)), bytes=dense_bytes,
+                     gbps=dense_bytes / (dsplit_mean * 1e-6) / 1e9,
+                     pct_peak=100 * dense_bytes / (dsplit_mean * 1e-6) / 1e9 / PEAK_HBM_GBPS,
                      tokens_per_s=B / (dwall / args.steps))
 
-    attn_mean = float(np.mean(attn_us))
+    attn_mean = split_mean_us   # mean launch duration of the split kernel, back to back
     achieved = comp_bytes / (attn_mean * 1e-6) / 1e9
     traffic = None
     ksrc = "attn_zf.hip" if fmt == kvz.FORMAT_ZIPFUSION else ("attn_mha.hip" if Hq == H else "attn_gqa.hip")
@@ -294,7 +316,9 @@ def main() -> int:
         "compressed_gbps": round(achieved, 1),
         "pct_peak_hbm": round(100 * achieved / PEAK_HBM_GBPS, 2),
         "uncompressed_equiv_gbps": round(dense_kv_bytes / (attn_mean * 1e-6) / 1e9, 1),
-        "attn_us": {"median": round(float(np.median(attn_us)), 2), "p10": round(float(np.percentile(attn_us, 10)), 2),
+        "step_gpu_us": round(step_gpu_us, 2),
+        "attn_us": {"mean": round(attn_mean, 2), "median": round(float(np.median(attn_us)), 2),
+                    "p10": round(float(np.percentile(attn_us, 10)), 2),
                     "p90": round(float(np.percentile(attn_us, 90)), 2), "cold_median": round(float(np.median(cold)), 2) if args.cold_steps else None},
         "merge_us": round(float(np.median(merge_us)), 2),
         "compressed_bytes": comp_bytes,
