@@ -18,8 +18,10 @@ __device__ __forceinline__ void compress_any(const uint16_t* k, const uint16_t* 
     compress_unit_zf(k, v, P, D, units + ((size_t)pid * H + h) * zf_unit_bytes(P, D), pool, pool_cap, cursor, status,
                      sx, smem + 4 * blk, reinterpret_cast<uint16_t*>(smem + 4 * blk + (nb + 1) / 2 * 2), sh);
   } else {
-    compress_unit<0>(k, v, P, D, units + ((size_t)pid * H + h) * unit_bytes(P, D), pool, pool_cap, cursor, status,
-                     sx, smem + 4 * blk, sh);
+    uint8_t* unit = units + ((size_t)pid * H + h) * unit_bytes(P, D);
+    if (D == 128) compress_unit<128>(k, v, P, D, unit, pool, pool_cap, cursor, status, sx, smem + 4 * blk, sh);
+    else if (D == 64) compress_unit<64>(k, v, P, D, unit, pool, pool_cap, cursor, status, sx, smem + 4 * blk, sh);
+    else compress_unit<0>(k, v, P, D, unit, pool, pool_cap, cursor, status, sx, smem + 4 * blk, sh);
   }
 }
 

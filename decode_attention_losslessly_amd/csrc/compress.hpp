@@ -4,9 +4,10 @@
 //
 // One 256-thread workgroup per unit:
 //   1. both source blocks [P][D] are staged in LDS;
-//   2. each wave takes groups (64 values = 64 lanes): every lane counts how many group
-//      exponents fall in [e, e+14] for its own exponent e; the largest count wins, the smallest
-//      exponent on ties; escapes are counted;
+//   2. each wave takes groups (64 values = 64 lanes): a histogram of the group's exponents in
+//      the wave's LDS bins and its running sum give, for every lane's own exponent e, how many
+//      group exponents fall in [e, e+14]; the largest count wins, the smallest exponent on
+//      ties; escapes are counted;
 //   3. the escape list goes inline when K + V escapes fit the meta region, else to the pool at
 //      an atomically bumped cursor;
 //   4. storage positions are encoded 8 per thread (one offset word, 8 sm bytes) in storage
@@ -24,7 +25,32 @@ struct CompressShared {
   uint32_t wave_sum[kCompressThreads / 64];
   uint64_t dest;        // pool offset, kInline, or ~1 when the pool is full
   uint32_t drop;        // 1 when escapes are dropped (pool full)
+  alignas(16) uint32_t bins[kCompressThreads / 64][256];   // per wave: exponent histogram, then its running sum
 };
+
+// Base of one group held one value per lane (exponent e): the exponent b among the lanes'
+// that maximises #{j : b <= e_j <= b + 14}, the smallest on ties. With C[k] = #{j : e_j <= k}
+// (the running sum of the group's exponent histogram), that count for b = e is
+// C[min(e + 14, 255)] - C[e - 1].
+__device__ __forceinline__ uint32_t group_base(uint32_t e, uint32_t* bins, int lane) {
+  reinterpret_cast<uint4*>(bins)[lane] = make_uint4(0, 0, 0, 0);
+  wave_lds_sync();
+  atomicAdd(&bins[e], 1u);
+  wave_lds_sync();
+  const uint4 h = reinterpret_cast<const uint4*>(bins)[lane];   // bins 4l .. 4l+3
+  const uint32_t s0 = h.x, s1 = s0 + h.y, s2 = s1 + h.z, s3 = s2 + h.w;
+  const uint32_t before = wave_incl_scan(s3) - s3;
+  wave_lds_sync();
+  reinterpret_cast<uint4*>(bins)[lane] = make_uint4(before + s0, before + s1, before + s2, before + s3);
+  wave_lds_sync();
+  const uint32_t hi = bins[min(e + 14u, 255u)];
+  const uint32_t lo = e > 0 ? bins[e - 1] : 0u;
+  uint32_t key = ((hi - lo) << 8) | (255u - e);
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) key = max(key, (uint32_t)__shfl_xor((int)key, m));
+  wave_lds_sync();   // the bins are read before the next group clears them
+  return 255u - (uniform(key) & 0xFFu);
+}
 
 // exclusive scan over the workgroup; returns this thread's prefix, *total gets the sum
 __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, CompressShared& sh, uint32_t* total) {
@@ -44,7 +70,8 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, CompressShared& 
   return before + inc - v;
 }
 
-// storage position s (within one block) -> token-major index tok*D + d
+// storage position s (within one block) -> token-major index tok*D + d (inlined where D is a
+// compile-time constant, so that its divisions become shifts)
 template <bool IsV>
 __device__ __forceinline__ int storage_to_index(int s, int D) {
   const int t = s / (kTile * D), r = s % (kTile * D);
@@ -55,9 +82,11 @@ __device__ __forceinline__ int storage_to_index(int s, int D) {
 
 // Writes the block's payload; its escapes go to `inline_dst` as value | position << 16 entries
 // or to `pool_dst` as values (whichever is non-null), starting at entry/element 0.
-template <bool IsV>
-__device__ void encode_block(const uint16_t* X, const uint8_t* bases_meta, int P, int D,
+// DT: the head dim when fixed at compile time, 0 to take it from d_rt
+template <bool IsV, int DT>
+__device__ void encode_block(const uint16_t* X, const uint8_t* bases_meta, int P, int d_rt,
                              uint8_t* payload, uint32_t* inline_dst, uint16_t* pool_dst, CompressShared& sh) {
+  const int D = DT ? DT : d_rt;
   const int G = D / kGroup;
   const int nchunks = P * D / 8;
   uint32_t rank = 0;
@@ -106,13 +135,15 @@ __device__ void encode_block(const uint16_t* X, const uint8_t* bases_meta, int P
   }
 }
 
-// Compresses src_k, src_v ([P][D] token-major raw BF16) into `unit`.
-template <int MaxPD>
-__device__ void compress_unit(const uint16_t* __restrict__ src_k, const uint16_t* __restrict__ src_v, int P,
-                              int D, uint8_t* __restrict__ unit, uint16_t* __restrict__ pool, int64_t pool_cap,
+// Compresses src_k, src_v ([P][D] token-major raw BF16) into `unit`. DT: the head dim when fixed
+// at compile time (64, 128), 0 to take it from d_rt.
+template <int DT>
+__device__ void compress_unit(const uint16_t* __restrict__ src_k, const uint16_t* __restrict__ src_v, int P, int d_rt,
+                              uint8_t* __restrict__ unit, uint16_t* __restrict__ pool, int64_t pool_cap,
                               uint64_t* __restrict__ cursor, uint32_t* __restrict__ status,
                               uint16_t* sh_x /* [2*P*D] */, uint8_t* sh_base /* [2*P*G] */, CompressShared& sh) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int D = DT ? DT : d_rt;
   const int G = D / kGroup, PD = P * D;
   // 1. stage
   for (int i = tid; i < PD / 8; i += kCompressThreads) {
@@ -128,16 +159,7 @@ __device__ void compress_unit(const uint16_t* __restrict__ src_k, const uint16_t
     const int tensor = q / (P * G), rem = q % (P * G), tok = rem / G, g = rem % G;
     const uint16_t x = sh_x[tensor * PD + tok * D + g * kGroup + lane];
     const uint32_t e = (x >> 7) & 0xFFu;
-    uint32_t cov = 0;
-#pragma unroll
-    for (int j = 0; j < 64; ++j) {
-      const uint32_t ej = readlane(e, j);
-      cov += (ej - e) <= 14u ? 1u : 0u;
-    }
-    uint32_t key = (cov << 8) | (255u - e);
-#pragma unroll
-    for (int m = 1; m < 64; m <<= 1) key = max(key, (uint32_t)__shfl_xor((int)key, m));
-    const uint32_t b = 255u - (uniform(key) & 0xFFu);
+    const uint32_t b = group_base(e, sh.bins[wave], lane);
     const uint64_t escm = ballot((e - b) > 14u);
     cnt[tensor] += (uint32_t)__builtin_popcountll(escm);
     if (lane == 0) sh_base[tensor * P * G + (tok / kTile) * kTile * G + g * kTile + (tok % kTile)] = (uint8_t)b;
@@ -172,9 +194,9 @@ __device__ void compress_unit(const uint16_t* __restrict__ src_k, const uint16_t
   uint32_t* inl = (keep && dest == kInline) ? reinterpret_cast<uint32_t*>(unit + hdr + 16) : nullptr;
   uint16_t* pl = (keep && dest != kInline) ? pool + dest : nullptr;
   // 4. payload and escapes
-  encode_block<false>(sh_x, sh_base, P, D, unit + kblock_offset(P, D), inl, pl, sh);
-  encode_block<true>(sh_x + PD, sh_base + P * G, P, D, unit + vblock_offset(P, D), inl ? inl + kc : nullptr,
-                     pl ? pl + kc : nullptr, sh);
+  encode_block<false, DT>(sh_x, sh_base, P, D, unit + kblock_offset(P, D), inl, pl, sh);
+  encode_block<true, DT>(sh_x + PD, sh_base + P * G, P, D, unit + vblock_offset(P, D), inl ? inl + kc : nullptr,
+                         pl ? pl + kc : nullptr, sh);
   // 5. meta: bases, header, zero tail of the inline area
   for (int i = tid; i < 2 * P * G; i += kCompressThreads) unit[i] = sh_base[i];
   const uint32_t used = inl ? 4 * total : 0;
