@@ -265,7 +265,11 @@ int launch_attn_mha(const uint16_t* q, const uint8_t* units, const uint16_t* poo
   } else {
     return -2;
   }
-  if (plan.slots <= 0) plan.slots = B * H * plan.S;
+  // Aim at two waves per resident slot: the multi-head waves run long chains whose lengths in
+  // time differ a little, and a second round lets the slots of early finishers take new work
+  // (measured 1-1.5% faster at 8K and 32K contexts, ragged or not; the grouped-query kernel,
+  // measured the same way, does best with one round).
+  plan.slots = plan.slots > 0 ? 2 * plan.slots : B * H * plan.S;
   const dim3 grid(plan_blocks(plan, (long)B * H, kWavesPerBlock));
   if (D == 128)
     hipLaunchKernelGGL((attn_mha_kernel<128>), grid, block, 0, stream, q, units, pool, pool_cap, k_tail, v_tail, page_table,
