@@ -119,15 +119,16 @@ struct GqaCStage {
 
 // Issues the loads of one (page, tile) step, unconditionally (as in the multi-head kernel), so
 // that the next step's loads stay in flight while the current step is computed.
+// `live` is false for a stage issued past the last step: its loads read nothing.
 __device__ __forceinline__ void gqa_c_issue(GqaCStage& st, const uint8_t* units, int pid, int page, int tile, int H,
-                                            int h, int P, int num_pages, int lane) {
+                                            int h, int P, int num_pages, int lane, bool live = true) {
   st.ok = pid >= 0 && pid < num_pages;
   st.page = page;
   st.unit = units + ((size_t)(st.ok ? pid : 0) * H + h) * unit_bytes(P, 128);
   st.tile = tile;
-  st.meta = load_meta(st.unit, P, 128, tile, lane);
-  load_k<128, true>(st.unit, P, tile, lane, st.k);
-  load_v<128>(st.unit, P, tile, lane, st.v);
+  st.meta = load_meta(st.unit, P, 128, tile, lane, live);
+  load_k<128, true>(st.unit, P, tile, lane, st.k, live);
+  load_v<128>(st.unit, P, tile, lane, st.v, live);
 }
 
 // Returns false, leaving the state untouched, when the unit's escapes are in the pool and POOL
@@ -313,11 +314,14 @@ __global__ __launch_bounds__(64 * kGqaWaves) KVZ_GQA_OCCUPANCY void attn_gqa_ker
   if (nsteps > 0) {
     // load cursor as in the multi-head kernel: stays on the last step once there
     int ln = 0, lp = p0, lt = 0;
+    bool live = true;   // false once the cursor has passed the last step: those stages read nothing
     const int last = nsteps - 1;
     auto advance = [&]() {
       if (ln < last) {
         ++ln;
         if (++lt == T) { lt = 0; ++lp; }
+      } else {
+        live = false;
       }
     };
     GqaCStage a, b;
@@ -326,13 +330,13 @@ __global__ __launch_bounds__(64 * kGqaWaves) KVZ_GQA_OCCUPANCY void attn_gqa_ker
     advance();
     pid = sload<int32_t>(pt_row + lp);
     for (int i = 0; i < nsteps; i += 2) {
-      gqa_c_issue(b, units, pid, lp, lt, H, h, P, num_pages, lane);
+      gqa_c_issue(b, units, pid, lp, lt, H, h, P, num_pages, lane, live);
       advance();
       pid = sload<int32_t>(pt_row + lp);
       bad |= !a.ok;
       if (!gqa_c_compute<false>(st, a, P, krank, vrank, esc_lds, vlds, pool, pool_cap, scale, lane)) note(a);
       if (i + 1 >= nsteps) break;
-      gqa_c_issue(a, units, pid, lp, lt, H, h, P, num_pages, lane);
+      gqa_c_issue(a, units, pid, lp, lt, H, h, P, num_pages, lane, live);
       advance();
       pid = sload<int32_t>(pt_row + lp);
       bad |= !b.ok;
@@ -415,18 +419,22 @@ __global__ __launch_bounds__(64 * kGqaWaves) KVZ_GQA_OCCUPANCY void attn_dense_g
   bool bad = false;
   if (nsteps > 0) {
     int ln = 0, lp = p0, lt = 0;
+    bool live = true;   // false once the cursor has passed the last step
     const int last = nsteps - 1;
     auto advance = [&]() {
       if (ln < last) {
         ++ln;
         if (++lt == T) { lt = 0; ++lp; }
+      } else {
+        live = false;
       }
     };
-    // loads of one step, unconditional: a bad page id reads page 0 and the step is skipped
+    // loads of one step, unconditional: a bad page id reads page 0 and the step is skipped; a
+    // stage past the last step (never computed) has no rows, so its loads all fall on one row
     auto issue = [&](GqaRawStage& stg, int pid, bool& ok) {
       ok = pid >= 0 && pid < num_pages;
       const size_t base = ((size_t)(ok ? pid : 0) * H + h) * P * 128;
-      const int rows = max(0, min(kTile, L - lp * P - lt * kTile));
+      const int rows = live ? max(0, min(kTile, L - lp * P - lt * kTile)) : 0;
       gqa_raw_load(stg, k_pages + base, v_pages + base, lt * kTile, rows, lane);
     };
     GqaRawStage a, b;

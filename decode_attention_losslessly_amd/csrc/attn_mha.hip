@@ -42,16 +42,17 @@ struct MhaStage {
 // Issues the loads of one (page, tile) step. The loads are unconditional (a bad page id reads
 // unit 0 instead and marks the stage), so that every path through the main loop has the same
 // loads in flight and the next step's loads can overlap the current step's compute.
+// `live` is false for a stage issued past the last step: its loads read nothing.
 template <int D>
 __device__ __forceinline__ void mha_issue(MhaStage<D>& st, const uint8_t* units, int pid, int page, int tile, int H,
-                                          int h, int P, int num_pages, int lane) {
+                                          int h, int P, int num_pages, int lane, bool live = true) {
   st.ok = pid >= 0 && pid < num_pages;
   st.page = page;
   st.unit = units + ((size_t)(st.ok ? pid : 0) * H + h) * unit_bytes(P, D);
   st.tile = tile;
-  st.meta = load_meta(st.unit, P, D, tile, lane);
-  load_k<D, false>(st.unit, P, tile, lane, st.k);
-  load_v<D>(st.unit, P, tile, lane, st.v);
+  st.meta = load_meta(st.unit, P, D, tile, lane, live);
+  load_k<D, false>(st.unit, P, tile, lane, st.k, live);
+  load_v<D>(st.unit, P, tile, lane, st.v, live);
 }
 
 // Returns false, leaving the state untouched, when the unit's escapes are in the pool and POOL
@@ -146,14 +147,17 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void attn_mha_kernel(
     if (nskip >= 2 && 2 * nskip > done) resume = (stg.page - p0 + 1) * T;
   };
   if (nsteps > 0) {
-    // load cursor: step ln = (page lp, tile lt); it stays on the last step once there, so the
-    // loads issued past the end re-read that step (from cache) and are never computed
+    // load cursor: step ln = (page lp, tile lt); it stays on the last step once there, and the
+    // stages issued past the end (never computed) read nothing (`live` false)
     int ln = 0, lp = p0, lt = 0;
+    bool live = true;
     const int last = nsteps - 1;
     auto advance = [&]() {
       if (ln < last) {
         ++ln;
         if (++lt == T) { lt = 0; ++lp; }
+      } else {
+        live = false;
       }
     };
     MhaStage<D> a, b;
@@ -162,13 +166,13 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void attn_mha_kernel(
     advance();
     pid = sload<int32_t>(pt_row + lp);   // one step ahead of its use
     for (int i = 0; i < nsteps; i += 2) {
-      mha_issue<D>(b, units, pid, lp, lt, H, h, P, num_pages, lane);
+      mha_issue<D>(b, units, pid, lp, lt, H, h, P, num_pages, lane, live);
       advance();
       pid = sload<int32_t>(pt_row + lp);
       bad |= !a.ok;
       if (!mha_compute<D, false>(st, a, P, krank, vrank, lds, pool, pool_cap, scale, lane)) note(a, i + 1);
       if (i + 1 >= nsteps || resume >= 0) break;
-      mha_issue<D>(a, units, pid, lp, lt, H, h, P, num_pages, lane);
+      mha_issue<D>(a, units, pid, lp, lt, H, h, P, num_pages, lane, live);
       advance();
       pid = sload<int32_t>(pt_row + lp);
       bad |= !b.ok;

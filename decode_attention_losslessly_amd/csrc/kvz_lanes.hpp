@@ -43,6 +43,8 @@ __device__ __forceinline__ uint32_t stream1(const uint8_t* p) { return __builtin
 // sits in SGPRs) and whose extent is the unit's size. The lane's part of an offset is the same
 // for every tile and every unit, so it is computed once; the tile's part is a scalar offset.
 // No vector instruction is then spent on addresses, and a read past the unit returns zeros.
+// A stage that a pipeline issues only to keep its wait counts fixed (past its last step) is
+// given an extent of 0: its loads return zeros without touching memory.
 typedef __amdgpu_buffer_rsrc_t UnitRsrc;
 constexpr int kRsrcWord3 = 0x00020000;   // raw buffer: no swizzle, 32-bit data format field
 constexpr int kNonTemporal = 2;          // cache-policy operand: non-temporal
@@ -89,9 +91,9 @@ template <int D>
 __device__ __forceinline__ int piece_dim(int piece) { return (16 * piece) % D; }
 
 template <int D, bool GQA>
-__device__ __forceinline__ void load_k(const uint8_t* unit, int P, int tile, int lane, KRaw<D>& r) {
+__device__ __forceinline__ void load_k(const uint8_t* unit, int P, int tile, int lane, KRaw<D>& r, bool live = true) {
   constexpr int NP = KRaw<D>::NP;
-  const UnitRsrc u = unit_rsrc(unit, unit_bytes(P, D));
+  const UnitRsrc u = unit_rsrc(unit, live ? unit_bytes(P, D) : 0u);
   const uint32_t tb = kblock_offset(P, D) + tile * tile_bytes(D);   // scalar parts
   const uint32_t bases = kbase_offset(D, tile);
 #pragma unroll
@@ -119,7 +121,7 @@ __device__ __forceinline__ void load_k(const uint8_t* unit, int P, int tile, int
 //   lanes [4G, 8G)        V bases of the tile
 //   lanes [8G, 8G + 32)   header (4 dwords) then the inline escapes
 // (lanes past the meta region read bytes of the unit that are not used).
-__device__ __forceinline__ uint32_t load_meta(const uint8_t* unit, int P, int D, int tile, int lane) {
+__device__ __forceinline__ uint32_t load_meta(const uint8_t* unit, int P, int D, int tile, int lane, bool live = true) {
   const int G = D / kGroup;
   // the K and V base tables both advance by kTile*G bytes per tile (the scalar offset); the
   // header lanes take it back out
@@ -129,7 +131,7 @@ __device__ __forceinline__ uint32_t load_meta(const uint8_t* unit, int P, int D,
   else if (lane < 8 * G) off = vbase_offset(P, D, 0) + 4 * (lane - 4 * G);
   else if (lane < 8 * G + 32) off = hdr_offset(P, D) + 4 * (lane - 8 * G) - toff;
   else off = -toff;
-  return uload4(unit_rsrc(unit, unit_bytes(P, D)), off, toff);
+  return uload4(unit_rsrc(unit, live ? unit_bytes(P, D) : 0u), off, toff);
 }
 template <int D>
 __device__ __forceinline__ int hdr_lane() { return 8 * (D / kGroup); }
@@ -157,8 +159,8 @@ struct VRaw {
 };
 
 template <int D>
-__device__ __forceinline__ void load_v(const uint8_t* unit, int P, int tile, int lane, VRaw<D>& r) {
-  const UnitRsrc u = unit_rsrc(unit, unit_bytes(P, D));
+__device__ __forceinline__ void load_v(const uint8_t* unit, int P, int tile, int lane, VRaw<D>& r, bool live = true) {
+  const UnitRsrc u = unit_rsrc(unit, live ? unit_bytes(P, D) : 0u);
   const uint32_t tb = vblock_offset(P, D) + tile * tile_bytes(D);
 #pragma unroll
   for (int s = 0; s < VRaw<D>::NS; ++s) {
