@@ -94,9 +94,21 @@ __device__ __forceinline__ uint64_t plan_total(const PlanPages& pp, const int32_
 // false when the wave has none.
 __device__ __forceinline__ bool plan_work(const SplitPlan& pl, const int32_t* seq_lens, int B, int P, int max_pages,
                                           bool dense, int ipr, int wave_id, int lane, WorkItem& w) {
-  const PlanPages pp = plan_load(seq_lens, B, P, max_pages, dense, lane);
+  const uint64_t items = (uint64_t)B * ipr, slots = (uint64_t)pl.slots;
   int C = pl.C_lo;
-  if (pl.C_hi > pl.C_lo) {
+  if (pl.C_hi > pl.C_lo && items >= slots) C = pl.C_hi;   // no split fits: one per item
+  if (C >= max_pages) {
+    // every request has exactly one split (an empty one too): numbering is direct
+    if (wave_id == 0 && lane == 0) *pl.chosen = C;
+    if ((uint64_t)wave_id >= items) return false;
+    w.r = wave_id / ipr;
+    w.k = wave_id % ipr;
+    w.s = 0;
+    w.C = C;
+    return true;
+  }
+  const PlanPages pp = plan_load(seq_lens, B, P, max_pages, dense, lane);
+  if (pl.C_hi > pl.C_lo && C < pl.C_hi) {
     // With N = ipr * (pages of the batch) and `items` = ipr * B, the splits at C lie between
     // N / C and N / C + items (the total only falls as C grows): no C below N / slots fits,
     // and every C from N / (slots - items) on does. Search between the two.
@@ -112,7 +124,7 @@ __device__ __forceinline__ bool plan_work(const SplitPlan& pl, const int32_t* se
         npg += readlane(wave_incl_scan(r < B ? (uint32_t)plan_pages(seq_lens[r], P, max_pages, dense) : 0u), 63);
       }
     }
-    const uint64_t N = npg * (uint64_t)ipr, items = (uint64_t)B * ipr, slots = (uint64_t)pl.slots;
+    const uint64_t N = npg * (uint64_t)ipr;
     int lo = (int)min((uint64_t)pl.C_hi, max((uint64_t)pl.C_lo, (N + slots - 1) / slots));
     int hi = pl.C_hi;
     if (slots > items) hi = (int)min((uint64_t)hi, max((uint64_t)lo, (N + slots - items - 1) / (slots - items)));

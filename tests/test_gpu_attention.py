@@ -162,13 +162,13 @@ def test_empty_and_short_requests():
     assert not d16[0].any()
 
 
-@pytest.mark.parametrize("Hq,Hkv", [(4, 4), (8, 2)])
-@pytest.mark.parametrize("B", [70, 300])
+@pytest.mark.parametrize("B,Hq,Hkv", [(70, 4, 4), (70, 8, 2), (300, 4, 4), (300, 8, 2), (300, 32, 32)])
 def test_many_ragged_requests(B, Hq, Hkv):
     """The split kernels number their work from the sequence lengths (a prefix over the requests,
-    64 at a time, held in registers up to 256 requests and re-read beyond): a batch of uneven
-    lengths with empty requests among them, past one and past four blocks of 64, still gives
-    every (request, head) row exactly its attention, and empty requests zeros."""
+    64 at a time, held in registers up to 256 requests and re-read beyond; directly, one split
+    per item, when the items alone fill the resident waves, as 300 x 32 heads do): a batch of
+    uneven lengths with empty requests among them still gives every (request, head) row exactly
+    its attention, and empty requests zeros."""
     rng = np.random.default_rng(B + Hq)
     lens = rng.integers(0, 200, size=B)
     lens[rng.choice(B, size=B // 7, replace=False)] = 0
