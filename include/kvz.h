@@ -129,8 +129,9 @@ int32_t kvz_inline_capacity(int32_t P, int32_t D);
  * initialisation. pages_per_split > 0 fixes the pages per split; 0 lets the kernels choose per
  * call from the sequence lengths: the smallest split, no smaller than a bound the library sets
  * from the shapes, whose splits over the whole batch fit the waves the kernel keeps resident,
- * so that batches of uneven lengths fill the GPU in one pass. The same value must be passed to
- * the attention call. */
+ * so that batches of uneven lengths fill the GPU in one pass. The resident waves come from the
+ * runtime's occupancy query, made on the host once per device and kernel at the first call.
+ * The same value must be passed to the attention call. */
 size_t kvz_workspace_bytes(int32_t B, int32_t H_q, int32_t H_kv, int32_t D, int32_t P,
                            int32_t max_pages_per_seq, int32_t pages_per_split);
 
