@@ -143,7 +143,13 @@ __device__ __forceinline__ float wave_max(float v) {
 // sm bytes, the exponent field (bits 7..14 and 23..30) from offset + base.
 constexpr uint32_t kSmMask = 0x807F807Fu;
 
-// Base term for a packed pair whose low value has base b0 and high value base b1.
+// Hides x from the optimiser (no instruction): after `x = W & m`, the compiler would otherwise
+// rewrite (W & m) << s as (W << s) & (m << s), and the shift could no longer fuse with the add
+// that follows it into one v_lshl_add_u32.
+__device__ __forceinline__ uint32_t opaque(uint32_t x) {
+  asm("" : "+v"(x));
+  return x;
+}
 
 // Rebuilds the 8 values of one offset word: S0 holds the sm bytes of positions 0..3, S1 those
 // of 4..7, W the offset word; bb[k] the base term of pair k. out[k] = (pos 2k, pos 2k+1) as a
@@ -155,11 +161,13 @@ __device__ __forceinline__ void decode8(uint32_t S0, uint32_t S1, uint32_t W, ui
   const uint32_t x1 = __builtin_amdgcn_perm(S0, S0, 0x03030202u);   // [s2, s2, s3, s3]
   const uint32_t x2 = __builtin_amdgcn_perm(S1, S1, 0x01010000u);
   const uint32_t x3 = __builtin_amdgcn_perm(S1, S1, 0x03030202u);
+  // offsets of pair k at bits 0 and 16 (k even) or 4 and 20 (k odd) of W or W >> 8: a mask,
+  // then one shift-and-add puts them at bits 7 and 23 on top of the base term
   const uint32_t W8 = W >> 8;
-  const uint32_t e0 = ((W & 0x000F000Fu) << 7) + bb0;
-  const uint32_t e1 = ((W & 0x00F000F0u) << 3) + bb1;
-  const uint32_t e2 = ((W8 & 0x000F000Fu) << 7) + bb2;
-  const uint32_t e3 = ((W8 & 0x00F000F0u) << 3) + bb3;
+  const uint32_t e0 = (opaque(W & 0x000F000Fu) << 7) + bb0;
+  const uint32_t e1 = (opaque(W & 0x00F000F0u) << 3) + bb1;
+  const uint32_t e2 = (opaque(W8 & 0x000F000Fu) << 7) + bb2;
+  const uint32_t e3 = (opaque(W8 & 0x00F000F0u) << 3) + bb3;
   out[0] = (x0 & kSmMask) | (e0 & ~kSmMask);
   out[1] = (x1 & kSmMask) | (e1 & ~kSmMask);
   out[2] = (x2 & kSmMask) | (e2 & ~kSmMask);

@@ -140,7 +140,7 @@ template <int D>
 __device__ __forceinline__ void decode_k(const KRaw<D>& r, uint32_t (&pairs)[KRaw<D>::VK / 2]) {
 #pragma unroll
   for (int i = 0; i < KRaw<D>::NP; ++i) {
-    const uint32_t bb = r.base[i] * 0x00800080u;
+    const uint32_t bb = opaque(r.base[i] * 0x00800080u);   // once per piece, not folded into each pair
     decode8(r.sm[4 * i], r.sm[4 * i + 1], r.nib[2 * i], bb, bb, bb, bb, &pairs[8 * i]);
     decode8(r.sm[4 * i + 2], r.sm[4 * i + 3], r.nib[2 * i + 1], bb, bb, bb, bb, &pairs[8 * i + 4]);
   }

@@ -24,9 +24,10 @@ __device__ __forceinline__ float token_sum(float v) {
   else return quad_sum(v);
 }
 
-// Softmax update for one tile given this lane's scores s[i] (token of piece i; -inf when
-// masked); returns the hi/lo probability pairs of the 8 token pairs as wave-uniform values.
-template <int D>
+// Softmax update for one tile given this lane's scores s[i] (token of piece i; with MASKED,
+// -inf for a token past the end); returns the hi/lo probability pairs of the 8 token pairs as
+// wave-uniform values.
+template <int D, bool MASKED = false>
 __device__ __forceinline__ void mha_softmax(MhaState<D>& st, const float (&s)[D / 64], uint32_t (&phi)[8],
                                             uint32_t (&plo)[8]) {
   constexpr int NP = D / 64, LPT = D / 16;   // pieces per lane, lanes per token
@@ -45,7 +46,8 @@ __device__ __forceinline__ void mha_softmax(MhaState<D>& st, const float (&s)[D 
 #pragma unroll
   for (int i = 0; i < NP; ++i) {
     // piece i holds tokens (64 / LPT) i + l / LPT; the next token sits LPT lanes up
-    const float p = s[i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(s[i] - st.m);
+    // a masked token's p is 0 even while the running max is still -inf
+    const float p = (MASKED && s[i] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(s[i] - st.m);
     const float pn = dpp_f<LPT == 8 ? kRowShl8 : kRowShl4>(p);
     const uint32_t hi = pack_bf16(p, pn);
     const float h_own = bf16lo_to_f32(hi), h_nb = bf16hi_to_f32(hi);
@@ -114,7 +116,7 @@ __device__ __forceinline__ void mha_tail(MhaState<D>& st, const uint16_t* tk, co
 #pragma unroll
     for (int i = 0; i < NP; ++i) sc[i] = valid[i] ? sc[i] : -INFINITY;
     uint32_t phi[8], plo[8];
-    mha_softmax<D>(st, sc, phi, plo);
+    mha_softmax<D, true>(st, sc, phi, plo);
     uint32_t vp[NS * 8];
 #pragma unroll
     for (int g = 0; g < NS; ++g) {
