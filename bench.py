@@ -186,7 +186,10 @@ def main() -> int:
     dense_kv_bytes = int(L.sum()) * H * D * 2 * 2
 
     def partial_bytes(C, pages):
-        # (m, l, acc) written per (request, query head, split) at C pages per split
+        # (m, l, acc) written per (request, query head, split): at C pages per split, or -C
+        # chunks per row when the kernel used the ranked schedule (C < 0)
+        if C < 0:
+            return len(pages) * Hq * (-C) * (D + 2) * 4, -C
         splits = np.where(pages > 0, (pages + C - 1) // C, 1)
         return int(splits.sum()) * Hq * (D + 2) * 4, int(splits.max())
 
@@ -319,7 +322,8 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": w.name, "batch": B, "q_heads": Hq, "kv_heads": H, "head_dim": D,
                    "context": int(w.seq_lens.max()), "page_size": P, "splits": splits_used,
-                   "pages_per_split": C_used, "parallelism": "none (1 GPU)"},
+                   "schedule": "ranked" if C_used < 0 else "split",
+                   "pages_per_split": C_used if C_used > 0 else None, "parallelism": "none (1 GPU)"},
         "compressed_gbps": round(achieved, 1),
         "pct_peak_hbm": round(100 * achieved / PEAK_HBM_GBPS, 2),
         "uncompressed_equiv_gbps": round(dense_kv_bytes / (attn_mean * 1e-6) / 1e9, 1),

@@ -32,15 +32,48 @@ struct SplitPlan {
   int S;           // partial slots per (request, query head)
   int C_lo, C_hi;  // bounds on the pages per split
   int slots;       // waves of the kernel resident at once on the device
-  int* chosen;     // the pages per split used, written by the launch's first wave
+  int ranks;       // > 0: the ranked schedule below may be used, with this many big ranks
+  int rank_min;    // ... when a big chunk holds at least this many pages on average (0: always)
+  int* chosen;     // the pages per split used (or minus the chunks per item when ranked),
+                   // written by the launch's first wave
 };
 
 struct WorkItem {
   int r;    // request
   int k;    // item within the request
-  int s;    // split of the item
-  int C;    // pages per split
+  int s;    // split of the item (the chunk's rank when ranked)
+  int C;    // pages per split; minus the chunks per item when ranked
 };
+
+// ---------------------------------------------------------------- ranked schedule
+// A wave's speed depends on its age on its SIMD (the issue arbiter favours the oldest wave), so
+// waves given equal work finish far apart, and the end of a launch runs with too few waves to
+// keep HBM busy. The ranked schedule cuts every item into 2R chunks and numbers the waves rank
+// by rank (every item's chunk 0, then every item's chunk 1, ...), so the hardware starts them
+// in that order: the first R ranks (one round of resident waves when R = resident waves /
+// items) take 80% of each item's pages in equal chunks, and the last R ranks take the rest in
+// chunks that shrink linearly to a fifth of the first, which fill the slots of early finishers
+// and end close together. Chunks are proportional to each request's own length.
+constexpr uint32_t kRankOne = 1u << 20;                 // shares are in units of 2^-20
+constexpr uint32_t kRankBig = kRankOne / 5 * 4;         // share of the first R ranks
+constexpr int kRankTaper = 5;                           // first / last tail chunk
+
+// share of an item's pages in its chunks before rank k (k in [0, 2R])
+__device__ __forceinline__ uint32_t rank_share(int k, int R) {
+  if (k <= R) return (uint32_t)((uint64_t)kRankBig * k / R);
+  // tail chunk i weighs (taper - 1)(R - 1 - i) + (R - 1); n of them weigh wsum(n)
+  const uint64_t i = (uint64_t)(k - R), c = (uint64_t)(R - 1), a = kRankTaper - 1;
+  const uint64_t rest = kRankOne - kRankBig;
+  if (c == 0) return kRankBig + (uint32_t)(rest * i);   // R = 1: one tail chunk
+  auto wsum = [&](uint64_t n) { return a * (n * c - n * (n - 1) / 2) + n * c; };
+  return kRankBig + (uint32_t)(rest * wsum(i) / wsum((uint64_t)R));
+}
+
+// pages [p0, p1) of chunk k of an item with np pages
+__device__ __forceinline__ void rank_range(int np, int k, int R, int& p0, int& p1) {
+  p0 = (int)(((uint64_t)np * rank_share(k, R)) >> 20);
+  p1 = (int)(((uint64_t)np * rank_share(k + 1, R)) >> 20);
+}
 
 __device__ __forceinline__ int plan_pages(int32_t L, int P, int max_pages, bool dense) {
   L = L < 0 ? 0 : min(L, max_pages * P);
@@ -92,9 +125,47 @@ __device__ __forceinline__ uint64_t plan_total(const PlanPages& pp, const int32_
 
 // This wave's split (waves are numbered request by request, item by item, split by split);
 // false when the wave has none.
+__device__ __forceinline__ uint64_t plan_page_sum(const PlanPages& pp, const int32_t* seq_lens, int B, int P,
+                                                  int max_pages, bool dense, int lane) {
+  uint64_t npg = 0;
+  if (pp.held) {
+    uint32_t n = 0;
+#pragma unroll
+    for (int j = 0; j < kPlanRegs; ++j) n += pp.np[j] > 0 ? (uint32_t)pp.np[j] : 0u;
+    npg = readlane(wave_incl_scan(n), 63);
+  } else {
+    for (int b0 = 0; b0 < B; b0 += 64) {
+      const int r = b0 + lane;
+      npg += readlane(wave_incl_scan(r < B ? (uint32_t)plan_pages(seq_lens[r], P, max_pages, dense) : 0u), 63);
+    }
+  }
+  return npg;
+}
+
 __device__ __forceinline__ bool plan_work(const SplitPlan& pl, const int32_t* seq_lens, int B, int P, int max_pages,
                                           bool dense, int ipr, int wave_id, int lane, WorkItem& w) {
   const uint64_t items = (uint64_t)B * ipr, slots = (uint64_t)pl.slots;
+  if (pl.ranks > 0) {
+    // ranked when forced, or when a big chunk would hold at least rank_min pages on average:
+    // big share * pages of the batch / (B * R) >= rank_min
+    bool use = pl.rank_min <= 0;
+    if (!use) {
+      const PlanPages pp = plan_load(seq_lens, B, P, max_pages, dense, lane);
+      const uint64_t npg = plan_page_sum(pp, seq_lens, B, P, max_pages, dense, lane);
+      use = npg * kRankBig >= (uint64_t)pl.rank_min * B * pl.ranks * kRankOne;
+    }
+    if (use) {
+      const int n = 2 * pl.ranks;
+      if (wave_id == 0 && lane == 0) *pl.chosen = -n;
+      if ((uint64_t)wave_id >= items * n) return false;
+      const int j = (int)((uint64_t)wave_id % items);
+      w.s = (int)((uint64_t)wave_id / items);
+      w.r = j / ipr;
+      w.k = j % ipr;
+      w.C = -n;
+      return true;
+    }
+  }
   int C = pl.C_lo;
   if (pl.C_hi > pl.C_lo && items >= slots) C = pl.C_hi;   // no split fits: one per item
   if (C >= max_pages) {
@@ -112,19 +183,7 @@ __device__ __forceinline__ bool plan_work(const SplitPlan& pl, const int32_t* se
     // With N = ipr * (pages of the batch) and `items` = ipr * B, the splits at C lie between
     // N / C and N / C + items (the total only falls as C grows): no C below N / slots fits,
     // and every C from N / (slots - items) on does. Search between the two.
-    uint64_t npg = 0;
-    if (pp.held) {
-      uint32_t n = 0;
-#pragma unroll
-      for (int j = 0; j < kPlanRegs; ++j) n += pp.np[j] > 0 ? (uint32_t)pp.np[j] : 0u;
-      npg = readlane(wave_incl_scan(n), 63);
-    } else {
-      for (int b0 = 0; b0 < B; b0 += 64) {
-        const int r = b0 + lane;
-        npg += readlane(wave_incl_scan(r < B ? (uint32_t)plan_pages(seq_lens[r], P, max_pages, dense) : 0u), 63);
-      }
-    }
-    const uint64_t N = npg * (uint64_t)ipr;
+    const uint64_t N = plan_page_sum(pp, seq_lens, B, P, max_pages, dense, lane) * (uint64_t)ipr;
     int lo = (int)min((uint64_t)pl.C_hi, max((uint64_t)pl.C_lo, (N + slots - 1) / slots));
     int hi = pl.C_hi;
     if (slots > items) hi = (int)min((uint64_t)hi, max((uint64_t)lo, (N + slots - items - 1) / (slots - items)));
@@ -185,7 +244,8 @@ inline int resident_waves(F kernel, int threads, int* cache, int ncache) {
 // workgroups to launch: every split the plan can produce gets a wave
 inline unsigned plan_blocks(const SplitPlan& pl, long items, int waves_per_block) {
   const long fixed = items * pl.S;                                   // C fixed: at most S per item
-  const long waves = pl.C_hi > pl.C_lo ? (pl.slots > items ? (long)pl.slots : items) : fixed;
+  long waves = pl.C_hi > pl.C_lo ? (pl.slots > items ? (long)pl.slots : items) : fixed;
+  if (pl.ranks > 0 && items * 2 * pl.ranks > waves) waves = items * 2 * pl.ranks;
   return (unsigned)((waves + waves_per_block - 1) / waves_per_block);
 }
 

@@ -113,9 +113,16 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void attn_mha_kernel(
     if (lane == 0 && s == 0 && h == 0) atomicOr(status, kStatusBadPage);
     nfull = 0;
   }
-  const int Sr = active_splits(nfull, C);
+  const bool ranked = C < 0;
+  const int Sr = ranked ? -C : active_splits(nfull, C);
   if (s >= Sr) return;
-  const int p0 = s * C, p1 = min(p0 + C, nfull);
+  int p0, p1;
+  if (ranked) {
+    rank_range(nfull, s, plan.ranks, p0, p1);
+  } else {
+    p0 = s * C;
+    p1 = min(p0 + C, nfull);
+  }
   const size_t slot = ((size_t)r * H + h) * S + s;
 
   MhaState<D> st;

@@ -65,7 +65,7 @@ int work_items_per_split(int B, int Hq, int Hkv) {
 // workspace, to about twice the split count that would fill kTargetItems waves with the batch's
 // items, and a split to at least 64 tokens.
 int pages_per_split(int B, int Hq, int Hkv, int P, int max_pages, int pps) {
-  if (pps > 0) return pps;
+  if (pps > 0) return pps;   // (pps < 0 asks for the ranked schedule; this bound is then unused by it)
   const long items = work_items_per_split(B, Hq, Hkv);
   const long s_cap = items >= 2 * kTargetItems ? 1 : (2 * kTargetItems + items - 1) / items;
   const int min_c = P >= 64 ? 1 : 64 / P;
@@ -76,6 +76,27 @@ int pages_per_split(int B, int Hq, int Hkv, int P, int max_pages, int pps) {
 }
 
 int split_count(int max_pages, int C) { return max_pages > 0 ? (max_pages + C - 1) / C : 1; }
+
+// Big ranks R of the ranked schedule (0: not used), which the multi-head kernel over the escape
+// format may use: the first round of kTargetItems waves takes R chunks of every item (and the
+// rest R chunks more). The kernel uses it only when a big chunk averages kRankMinPages pages or
+// more over the call's actual lengths; pps < 0 forces it with -pps big ranks.
+constexpr int kRankMinPages = 16;
+constexpr int kMaxForcedRanks = 4096;
+int rank_count(int B, int Hq, int Hkv, int pps) {
+  if (pps < 0) return -pps;
+  if (pps > 0 || Hq != Hkv) return 0;
+  const long items = (long)B * Hkv;
+  if (items >= 2 * kTargetItems) return 0;
+  return items >= kTargetItems ? 1 : (int)(kTargetItems / items);
+}
+
+// split slots per (request, query head): the dynamic schedule's bound and the ranked one's 2R
+int slot_count(int B, int Hq, int Hkv, int P, int max_pages, int pps) {
+  const int S = split_count(max_pages, pages_per_split(B, Hq, Hkv, P, max_pages, pps));
+  const int R = rank_count(B, Hq, Hkv, pps);
+  return 2 * R > S ? 2 * R : S;
+}
 
 bool shape_ok(int P, int D) { return P > 0 && P % 16 == 0 && D > 0 && D % 64 == 0; }
 
@@ -104,7 +125,8 @@ int32_t kvz_inline_capacity(int32_t P, int32_t D) { return shape_ok(P, D) ? kvz:
 int32_t kvz_num_splits(int32_t B, int32_t H_q, int32_t H_kv, int32_t D, int32_t P, int32_t max_pages_per_seq,
                        int32_t pps) {
   if (B <= 0 || H_q <= 0 || H_kv <= 0 || H_q % H_kv || !shape_ok(P, D) || max_pages_per_seq < 0) return 0;
-  return split_count(max_pages_per_seq, pages_per_split(B, H_q, H_kv, P, max_pages_per_seq, pps));
+  if (pps < -kMaxForcedRanks) return 0;
+  return slot_count(B, H_q, H_kv, P, max_pages_per_seq, pps);
 }
 
 // workspace: per (request, query head, split) acc[D] and (m, l) as float, then one 16-byte slot
@@ -120,6 +142,8 @@ static kvz::SplitPlan make_plan(int C, int S, int max_pages, bool fixed, int32_t
   p.C_lo = C;
   p.C_hi = fixed ? C : (max_pages > C ? max_pages : C);
   p.slots = 0;   // filled in by the launch from the kernel's occupancy
+  p.ranks = 0;   // the ranked schedule: set only for the kernel that implements it
+  p.rank_min = 0;
   p.chosen = chosen;
   return p;
 }
@@ -169,25 +193,27 @@ int kvz_decode_attention_splits(const uint16_t* q, const kvz_cache* c, const int
   int rc = check_attention_shape(B, H_q, H, D, P, max_pages);
   if (rc) return rc;
   if (B == 0) return KVZ_OK;
-  if (!q || !page_table || !seq_lens || !workspace || !c->k_tail || !c->v_tail || pps < 0)
+  if (!q || !page_table || !seq_lens || !workspace || !c->k_tail || !c->v_tail || pps < -kMaxForcedRanks)
     return KVZ_ERR_INVALID_ARG;
   if (B > c->max_batch) return KVZ_ERR_INVALID_ARG;
   const int C = pages_per_split(B, H_q, H, P, max_pages, pps);
-  const int S = split_count(max_pages, C);
+  const int S = slot_count(B, H_q, H, P, max_pages, pps);
   if (workspace_bytes < ws_bytes(B, H_q, S, D)) return KVZ_ERR_WORKSPACE;
   float* ws_acc = reinterpret_cast<float*>(workspace);
   float* ws_ml = ws_acc + (size_t)B * H_q * S * D;
   const float scale = sm_scale * 1.4426950408889634f;
-  const kvz::SplitPlan plan = make_plan(C, S, max_pages, pps > 0, ws_chosen(workspace, B, H_q, S, D));
+  kvz::SplitPlan plan = make_plan(C, S, max_pages, pps > 0, ws_chosen(workspace, B, H_q, S, D));
   if (c->format == KVZ_FORMAT_ZIPFUSION) {
     if (H_q != H) return KVZ_ERR_UNSUPPORTED;
     rc = kvz::launch_attn_zf(q, c->units, c->esc_pool, c->esc_capacity, c->k_tail, c->v_tail, page_table, max_pages,
                              seq_lens, B, H, D, P, c->num_pages, plan, scale, ws_acc, ws_ml, c->status,
                              as_stream(stream));
-  } else if (H_q == H)
+  } else if (H_q == H) {
+    plan.ranks = rank_count(B, H_q, H, pps);
+    plan.rank_min = pps < 0 ? 0 : kRankMinPages;
     rc = kvz::launch_attn_mha(q, c->units, c->esc_pool, c->esc_capacity, c->k_tail, c->v_tail, page_table, max_pages, seq_lens, B, H,
                               D, P, c->num_pages, plan, scale, ws_acc, ws_ml, c->status, as_stream(stream));
-  else
+  } else
     rc = kvz::launch_attn_gqa(q, c->units, c->esc_pool, c->esc_capacity, c->k_tail, c->v_tail, page_table, max_pages, seq_lens, B,
                               H_q, H, D, P, c->num_pages, plan, scale, ws_acc, ws_ml, c->status,
                               as_stream(stream));
@@ -202,10 +228,11 @@ int kvz_decode_attention_dense_splits(const uint16_t* q, const uint16_t* k_pages
   int rc = check_attention_shape(B, H_q, H, D, P, max_pages);
   if (rc) return rc;
   if (B == 0) return KVZ_OK;
-  if (!q || !k_pages || !v_pages || !page_table || !seq_lens || !workspace || num_pages < 0 || pps < 0)
+  if (!q || !k_pages || !v_pages || !page_table || !seq_lens || !workspace || num_pages < 0 ||
+      pps < -kMaxForcedRanks)
     return KVZ_ERR_INVALID_ARG;
   const int C = pages_per_split(B, H_q, H, P, max_pages, pps);
-  const int S = split_count(max_pages, C);
+  const int S = slot_count(B, H_q, H, P, max_pages, pps);
   if (workspace_bytes < ws_bytes(B, H_q, S, D)) return KVZ_ERR_WORKSPACE;
   float* ws_acc = reinterpret_cast<float*>(workspace);
   float* ws_ml = ws_acc + (size_t)B * H_q * S * D;
@@ -226,9 +253,8 @@ int kvz_merge_splits(const void* workspace, size_t workspace_bytes, const int32_
   int rc = check_attention_shape(B, H_q, H, D, P, max_pages);
   if (rc) return rc;
   if (B == 0) return KVZ_OK;
-  if (!workspace || !seq_lens || !out || pps < 0) return KVZ_ERR_INVALID_ARG;
-  const int C = pages_per_split(B, H_q, H, P, max_pages, pps);
-  const int S = split_count(max_pages, C);
+  if (!workspace || !seq_lens || !out || pps < -kMaxForcedRanks) return KVZ_ERR_INVALID_ARG;
+  const int S = slot_count(B, H_q, H, P, max_pages, pps);
   if (workspace_bytes < ws_bytes(B, H_q, S, D)) return KVZ_ERR_WORKSPACE;
   const float* ws_acc = reinterpret_cast<const float*>(workspace);
   const float* ws_ml = ws_acc + (size_t)B * H_q * S * D;

@@ -122,8 +122,9 @@ def num_splits(B, Hq, Hkv, D, P, max_pages, pages_per_split=0) -> int:
 
 
 def chosen_pages_per_split(workspace: torch.Tensor, B, Hq, Hkv, D, P, max_pages, pages_per_split=0) -> int:
-    """Pages per split the last split kernel run on `workspace` used (read back from the slot
-    after the partials; synchronises with the device)."""
+    """Pages per split the last split kernel run on `workspace` used, or minus its chunks per
+    (request, query head) when it used the ranked schedule (read back from the slot after the
+    partials; synchronises with the device)."""
     S = num_splits(B, Hq, Hkv, D, P, max_pages, pages_per_split)
     off = B * Hq * S * (D + 2) * 4
     return int(workspace[off:off + 4].view(torch.int32).item())

@@ -125,12 +125,24 @@ int32_t kvz_inline_capacity(int32_t P, int32_t D);
 
 /* Bytes of scratch kvz_decode_attention / kvz_decode_attention_dense need: split partials
  * (acc[D], m, l) in float for every (request, query head, split slot), then 16 bytes where the
- * split kernel records the pages per split it used, for the merge. Its content needs no
- * initialisation. pages_per_split > 0 fixes the pages per split; 0 lets the kernels choose per
- * call from the sequence lengths: the smallest split, no smaller than a bound the library sets
- * from the shapes, whose splits over the whole batch fit the waves the kernel keeps resident,
- * so that batches of uneven lengths fill the GPU in one pass. The resident waves come from the
- * runtime's occupancy query, made on the host once per device and kernel at the first call.
+ * split kernel records the pages per split it used (or minus its chunks per row, below), for
+ * the merge. Its content needs no initialisation.
+ *   pages_per_split > 0  fixes the pages per split.
+ *   pages_per_split = 0  lets the kernels choose per call from the sequence lengths: the
+ *                        smallest split, no smaller than a bound the library sets from the
+ *                        shapes, whose splits over the whole batch fit the waves the kernel
+ *                        keeps resident, so that batches of uneven lengths fill the GPU in one
+ *                        pass (the resident waves come from the runtime's occupancy query,
+ *                        made on the host once per device and kernel at the first call). The
+ *                        multi-head kernel over the escape format instead uses a ranked
+ *                        schedule when the call's pages make its chunks large (on average at
+ *                        least 16 pages): each row is cut into 2R chunks, R = max(1, 4096 /
+ *                        (B H)); the first R take 80% of the request's pages in equal parts and
+ *                        run first, the last R take the rest in shrinking parts, so that the
+ *                        waves, whose speeds differ with their age on the SIMD, end together.
+ *   pages_per_split < 0  asks the multi-head kernel over the escape format for the ranked
+ *                        schedule with R = -pages_per_split (at most 4096); other kernels then
+ *                        choose as with 0.
  * The same value must be passed to the attention call. */
 size_t kvz_workspace_bytes(int32_t B, int32_t H_q, int32_t H_kv, int32_t D, int32_t P,
                            int32_t max_pages_per_seq, int32_t pages_per_split);

@@ -85,6 +85,31 @@ def test_split_count_and_page_order_do_not_change_the_result(cfg):
     assert np.array_equal(again16, base16)
 
 
+@pytest.mark.parametrize("cfg", [1, 2, 3, 5])
+def test_ranked_schedule_matches_oracle(cfg):
+    """The multi-head kernel's ranked schedule (pages_per_split = -R forces it: every row is cut
+    into 2R chunks, each a share of its request's own pages, the last R shrinking) gives the
+    oracle's attention and the default schedule's fp32 result up to reduction order; the kernel
+    records -2R where the merge reads it. Config 5 takes the pool paths inside the chunks."""
+    w = make_workload(cfg, **SMALL[cfg])
+    kp, vp = w.pages(0), w.pages(1)
+    cache, lens = build_cache(w, kp, vp)
+    q = w.q()
+    base16, base32 = _run(w, cache, lens, q)
+    rows = _all_rows(w)
+    ref = oracle_rows(w, kp, vp, q, rows)
+    nrm = np.abs(base32).max(axis=-1, keepdims=True)
+    for pps in [-1, -2, -5]:
+        o16, o32 = _run(w, cache, lens, q, pages_per_split=pps)
+        assert int(cache.status.item()) == 0
+        check_rows(o16.reshape(-1, w.D), o32.reshape(-1, w.D), ref, f"cfg{cfg} ranked {pps}")
+        assert np.all(np.abs(o32 - base32) <= 1e-5 * nrm), pps
+        ws = torch.empty(kvz.workspace_bytes(w.B, w.Hq, w.Hkv, w.D, w.P, w.max_pages, pps), dtype=torch.uint8,
+                         device=DEV)
+        kvz.decode_attention_splits(dev(q), cache, dev(w.page_table), lens, w.sm_scale, ws, pages_per_split=pps)
+        assert kvz.chosen_pages_per_split(ws, w.B, w.Hq, w.Hkv, w.D, w.P, w.max_pages, pps) == 2 * pps
+
+
 def test_dense_and_compressed_agree():
     w = make_workload(3, **SMALL[3])
     kp, vp = w.pages(0), w.pages(1)
@@ -186,6 +211,10 @@ def test_many_ragged_requests(B, Hq, Hkv):
     check_rows(o16.reshape(-1, w.D)[idx], o32.reshape(-1, w.D)[idx], ref, f"B={B}")
     d16, d32 = _run(w, None, dev(w.seq_lens), q, dense_pages=(dev(kp), dev(vp)))
     check_rows(d16.reshape(-1, w.D)[idx], d32.reshape(-1, w.D)[idx], ref, f"dense B={B}")
+    if Hq == Hkv:   # the ranked schedule over the same uneven batch
+        r16, r32 = _run(w, cache, lt, q, pages_per_split=-3)
+        assert not r16[empty].any() and not r32[empty].any()
+        check_rows(r16.reshape(-1, w.D)[idx], r32.reshape(-1, w.D)[idx], ref, f"ranked B={B}")
 
 
 def test_bad_page_id_sets_status():
@@ -219,6 +248,10 @@ def test_full_size_sampled_rows(cfg, full_workloads):
     idx = tuple(np.array(rows).T)
     check_rows(o16[idx], o32[idx], ref, f"cfg{cfg} full compressed")
     assert np.isfinite(o32).all()
+    if cfg in (3, 5):   # these launches take the multi-head kernel's ranked schedule
+        ws = torch.empty(kvz.workspace_bytes(w.B, w.Hq, w.Hkv, w.D, w.P, w.max_pages), dtype=torch.uint8, device=DEV)
+        kvz.decode_attention_splits(dev(q), cache, dev(w.page_table), lens, w.sm_scale, ws)
+        assert kvz.chosen_pages_per_split(ws, w.B, w.Hq, w.Hkv, w.D, w.P, w.max_pages) < 0
     d16, d32 = _run(w, None, dev(w.seq_lens), q, dense_pages=(dev(kp), dev(vp)))
     check_rows(d16[idx], d32[idx], ref, f"cfg{cfg} full dense")
 

@@ -33,7 +33,7 @@ def test_shapes_match_oracle(P, D, Hq, Hkv):
         q = w.q()
         rows = [(r, h) for r in range(w.B) for h in range(w.Hq)]
         ref = oracle_rows(w, kp, vp, q, rows)
-        for pps in (0, 1, 3):
+        for pps in (0, 1, 3, -2):   # -2: the multi-head kernel's ranked schedule
             out = torch.zeros((w.B, w.Hq, w.D), dtype=torch.int16, device=DEV)
             out32 = torch.full((w.B, w.Hq, w.D), float("nan"), dtype=torch.float32, device=DEV)
             kvz.decode_attention(dev(q), cache, dev(w.page_table), seq, w.sm_scale, out, out32, pages_per_split=pps)
