@@ -241,6 +241,16 @@ inline int resident_waves(F kernel, int threads, int* cache, int ncache) {
   return cache[dev];
 }
 
+// Big ranks from the waves the kernel keeps resident (one round of them takes the big chunks),
+// unless the caller fixed them; never more than the workspace's S / 2.
+inline void rank_fit(SplitPlan& pl, int resident, long items) {
+  if (pl.ranks <= 0) return;
+  long R = pl.ranks;
+  if (pl.rank_min > 0 && resident > 0) R = resident / items > 1 ? resident / items : 1;
+  if (R > pl.S / 2) R = pl.S / 2;
+  pl.ranks = (int)R;   // 0 when the workspace holds fewer than two slots: the schedule is not used
+}
+
 // workgroups to launch: every split the plan can produce gets a wave
 inline unsigned plan_blocks(const SplitPlan& pl, long items, int waves_per_block) {
   const long fixed = items * pl.S;                                   // C fixed: at most S per item

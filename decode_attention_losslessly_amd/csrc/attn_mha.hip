@@ -280,6 +280,7 @@ int launch_attn_mha(const uint16_t* q, const uint8_t* units, const uint16_t* poo
   // time differ a little, and a second round lets the slots of early finishers take new work
   // (measured 1-1.5% faster at 8K and 32K contexts, ragged or not; the grouped-query kernel,
   // measured the same way, does best with one round).
+  rank_fit(plan, plan.slots, (long)B * H);
   plan.slots = plan.slots > 0 ? 2 * plan.slots : B * H * plan.S;
   const dim3 grid(plan_blocks(plan, (long)B * H, kWavesPerBlock));
   if (D == 128)

@@ -78,9 +78,12 @@ int pages_per_split(int B, int Hq, int Hkv, int P, int max_pages, int pps) {
 int split_count(int max_pages, int C) { return max_pages > 0 ? (max_pages + C - 1) / C : 1; }
 
 // Big ranks R of the ranked schedule (0: not used), which the multi-head kernel over the escape
-// format may use: the first round of kTargetItems waves takes R chunks of every item (and the
-// rest R chunks more). The kernel uses it only when a big chunk averages kRankMinPages pages or
-// more over the call's actual lengths; pps < 0 forces it with -pps big ranks.
+// format may use: the first round of kTargetItems waves takes R chunks of every item, and the
+// rest R chunks more (the launch lowers R to its own resident waves). The kernel uses it only
+// when a big chunk averages kRankMinPages pages or more over the call's actual lengths;
+// pps < 0 forces it with -pps big ranks. (The grouped-query kernel, whose splits each write
+// the partials of up to 8 query heads, measured slower with it, 3% to 35%, and keeps the
+// split schedule.)
 constexpr int kRankMinPages = 16;
 constexpr int kMaxForcedRanks = 4096;
 int rank_count(int B, int Hq, int Hkv, int pps) {
@@ -213,10 +216,11 @@ int kvz_decode_attention_splits(const uint16_t* q, const kvz_cache* c, const int
     plan.rank_min = pps < 0 ? 0 : kRankMinPages;
     rc = kvz::launch_attn_mha(q, c->units, c->esc_pool, c->esc_capacity, c->k_tail, c->v_tail, page_table, max_pages, seq_lens, B, H,
                               D, P, c->num_pages, plan, scale, ws_acc, ws_ml, c->status, as_stream(stream));
-  } else
+  } else {
     rc = kvz::launch_attn_gqa(q, c->units, c->esc_pool, c->esc_capacity, c->k_tail, c->v_tail, page_table, max_pages, seq_lens, B,
                               H_q, H, D, P, c->num_pages, plan, scale, ws_acc, ws_ml, c->status,
                               as_stream(stream));
+  }
   return rc ? (rc == -2 ? KVZ_ERR_UNSUPPORTED : KVZ_ERR_HIP) : KVZ_OK;
 }
 

@@ -211,10 +211,11 @@ def test_many_ragged_requests(B, Hq, Hkv):
     check_rows(o16.reshape(-1, w.D)[idx], o32.reshape(-1, w.D)[idx], ref, f"B={B}")
     d16, d32 = _run(w, None, dev(w.seq_lens), q, dense_pages=(dev(kp), dev(vp)))
     check_rows(d16.reshape(-1, w.D)[idx], d32.reshape(-1, w.D)[idx], ref, f"dense B={B}")
-    if Hq == Hkv:   # the ranked schedule over the same uneven batch
-        r16, r32 = _run(w, cache, lt, q, pages_per_split=-3)
-        assert not r16[empty].any() and not r32[empty].any()
-        check_rows(r16.reshape(-1, w.D)[idx], r32.reshape(-1, w.D)[idx], ref, f"ranked B={B}")
+    # the ranked schedule (multi-head kernel; the grouped-query one keeps its splits) over the
+    # same uneven batch
+    r16, r32 = _run(w, cache, lt, q, pages_per_split=-3)
+    assert not r16[empty].any() and not r32[empty].any()
+    check_rows(r16.reshape(-1, w.D)[idx], r32.reshape(-1, w.D)[idx], ref, f"pps -3 B={B}")
 
 
 def test_bad_page_id_sets_status():
