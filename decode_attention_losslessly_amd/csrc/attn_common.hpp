@@ -38,35 +38,50 @@ struct SplitPlan {
                    // written by the launch's first wave
 };
 
+constexpr int kLenUnknown = -2147483647 - 1;
+
 struct WorkItem {
   int r;    // request
   int k;    // item within the request
   int s;    // split of the item (the chunk's rank when ranked)
   int C;    // pages per split; minus the chunks per item when ranked
+  int L;    // seq_lens[r] as read by the plan, or kLenUnknown when the plan did not read it
 };
+
+// the request's length: from the plan's registers when it read them, else one scalar load
+__device__ __forceinline__ int request_len(const WorkItem& w, const int32_t* seq_lens) {
+  return w.L != kLenUnknown ? w.L : sload<int32_t>(seq_lens + w.r);
+}
 
 // ---------------------------------------------------------------- ranked schedule
 // A wave's speed depends on its age on its SIMD (the issue arbiter favours the oldest wave), so
 // waves given equal work finish far apart, and the end of a launch runs with too few waves to
-// keep HBM busy. The ranked schedule cuts every item into 2R chunks and numbers the waves rank
-// by rank (every item's chunk 0, then every item's chunk 1, ...), so the hardware starts them
-// in that order: the first R ranks (one round of resident waves when R = resident waves /
-// items) take 80% of each item's pages in equal chunks, and the last R ranks take the rest in
-// chunks that shrink linearly to a fifth of the first, which fill the slots of early finishers
-// and end close together. Chunks are proportional to each request's own length.
+// keep HBM busy. The ranked schedule cuts every item into (1 + kRankTailPer) R chunks and
+// numbers the waves rank by rank (every item's chunk 0, then every item's chunk 1, ...), so the
+// hardware starts them in that order: the first R ranks (one round of resident waves when
+// R = resident waves / items) take 80% of each item's pages in equal chunks, and the
+// kRankTailPer R tail ranks take the rest in chunks that shrink linearly to a fifth of the
+// first, which fill the slots of early finishers and end close together. Chunks are
+// proportional to each request's own length.
 constexpr uint32_t kRankOne = 1u << 20;                 // shares are in units of 2^-20
 constexpr uint32_t kRankBig = kRankOne / 5 * 4;         // share of the first R ranks
 constexpr int kRankTaper = 5;                           // first / last tail chunk
+constexpr int kRankTailPer = 1;                         // tail ranks per big rank
 
-// share of an item's pages in its chunks before rank k (k in [0, 2R])
+// chunks per item with R big ranks
+__host__ __device__ constexpr int rank_chunks(int R) { return (1 + kRankTailPer) * R; }
+
+// share of an item's pages in its chunks before rank k (k in [0, rank_chunks(R)])
 __device__ __forceinline__ uint32_t rank_share(int k, int R) {
   if (k <= R) return (uint32_t)((uint64_t)kRankBig * k / R);
-  // tail chunk i weighs (taper - 1)(R - 1 - i) + (R - 1); n of them weigh wsum(n)
-  const uint64_t i = (uint64_t)(k - R), c = (uint64_t)(R - 1), a = kRankTaper - 1;
+  // with T tail ranks, tail chunk i weighs (taper - 1)(T - 1 - i) + (T - 1); n of them weigh
+  // wsum(n)
+  const int T = kRankTailPer * R;
+  const uint64_t i = (uint64_t)(k - R), c = (uint64_t)(T - 1), a = kRankTaper - 1;
   const uint64_t rest = kRankOne - kRankBig;
-  if (c == 0) return kRankBig + (uint32_t)(rest * i);   // R = 1: one tail chunk
+  if (c == 0) return kRankBig + (uint32_t)(rest * i);   // one tail chunk
   auto wsum = [&](uint64_t n) { return a * (n * c - n * (n - 1) / 2) + n * c; };
-  return kRankBig + (uint32_t)(rest * wsum(i) / wsum((uint64_t)R));
+  return kRankBig + (uint32_t)(rest * wsum(i) / wsum((uint64_t)T));
 }
 
 // pages [p0, p1) of chunk k of an item with np pages
@@ -85,6 +100,7 @@ __device__ __forceinline__ int plan_pages(int32_t L, int P, int max_pages, bool 
 constexpr int kPlanRegs = 4;
 struct PlanPages {
   int np[kPlanRegs];
+  int len[kPlanRegs];   // the lengths as read, so that a wave need not load its own again
   bool held;
 };
 
@@ -95,9 +111,25 @@ __device__ __forceinline__ PlanPages plan_load(const int32_t* seq_lens, int B, i
 #pragma unroll
   for (int j = 0; j < kPlanRegs; ++j) {
     const int r = 64 * j + lane;
-    pp.np[j] = (pp.held && r < B) ? plan_pages(seq_lens[r], P, max_pages, dense) : -1;
+    const bool in = pp.held && r < B;
+    pp.len[j] = in ? seq_lens[r] : 0;
+    pp.np[j] = in ? plan_pages(pp.len[j], P, max_pages, dense) : -1;
   }
   return pp;
+}
+
+// length of request r (wave-uniform) from the registers, or kLenUnknown (one readlane per
+// register, then a scalar select: a select among the vector registers themselves became a
+// dynamically indexed array in scratch memory)
+__device__ __forceinline__ int plan_len(const PlanPages& pp, int r) {
+  if (!pp.held) return kLenUnknown;
+  int v = (int)readlane((uint32_t)pp.len[0], r & 63);
+#pragma unroll
+  for (int j = 1; j < kPlanRegs; ++j) {
+    const int x = (int)readlane((uint32_t)pp.len[j], r & 63);
+    v = (r >> 6) == j ? x : v;
+  }
+  return v;
 }
 
 // splits of request r's item at C pages per split (0 past the batch)
@@ -148,14 +180,14 @@ __device__ __forceinline__ bool plan_work(const SplitPlan& pl, const int32_t* se
   if (pl.ranks > 0) {
     // ranked when forced, or when a big chunk would hold at least rank_min pages on average:
     // big share * pages of the batch / (B * R) >= rank_min
+    const PlanPages pp = plan_load(seq_lens, B, P, max_pages, dense, lane);
     bool use = pl.rank_min <= 0;
     if (!use) {
-      const PlanPages pp = plan_load(seq_lens, B, P, max_pages, dense, lane);
       const uint64_t npg = plan_page_sum(pp, seq_lens, B, P, max_pages, dense, lane);
       use = npg * kRankBig >= (uint64_t)pl.rank_min * B * pl.ranks * kRankOne;
     }
     if (use) {
-      const int n = 2 * pl.ranks;
+      const int n = rank_chunks(pl.ranks);
       if (wave_id == 0 && lane == 0) *pl.chosen = -n;
       if ((uint64_t)wave_id >= items * n) return false;
       const int j = (int)((uint64_t)wave_id % items);
@@ -163,6 +195,7 @@ __device__ __forceinline__ bool plan_work(const SplitPlan& pl, const int32_t* se
       w.r = j / ipr;
       w.k = j % ipr;
       w.C = -n;
+      w.L = plan_len(pp, w.r);
       return true;
     }
   }
@@ -176,6 +209,7 @@ __device__ __forceinline__ bool plan_work(const SplitPlan& pl, const int32_t* se
     w.k = wave_id % ipr;
     w.s = 0;
     w.C = C;
+    w.L = kLenUnknown;
     return true;
   }
   const PlanPages pp = plan_load(seq_lens, B, P, max_pages, dense, lane);
@@ -212,6 +246,7 @@ __device__ __forceinline__ bool plan_work(const SplitPlan& pl, const int32_t* se
     w.k = (int)(local / n);
     w.s = (int)(local % n);
     w.C = C;
+    w.L = plan_len(pp, w.r);
     return true;
   };
   if (pp.held) {
@@ -242,20 +277,20 @@ inline int resident_waves(F kernel, int threads, int* cache, int ncache) {
 }
 
 // Big ranks from the waves the kernel keeps resident (one round of them takes the big chunks),
-// unless the caller fixed them; never more than the workspace's S / 2.
+// unless the caller fixed them; never more chunks than the workspace's S slots.
 inline void rank_fit(SplitPlan& pl, int resident, long items) {
   if (pl.ranks <= 0) return;
   long R = pl.ranks;
   if (pl.rank_min > 0 && resident > 0) R = resident / items > 1 ? resident / items : 1;
-  if (R > pl.S / 2) R = pl.S / 2;
-  pl.ranks = (int)R;   // 0 when the workspace holds fewer than two slots: the schedule is not used
+  while (R > 0 && rank_chunks((int)R) > pl.S) --R;
+  pl.ranks = (int)R;   // 0 when the workspace holds too few slots: the schedule is not used
 }
 
 // workgroups to launch: every split the plan can produce gets a wave
 inline unsigned plan_blocks(const SplitPlan& pl, long items, int waves_per_block) {
   const long fixed = items * pl.S;                                   // C fixed: at most S per item
   long waves = pl.C_hi > pl.C_lo ? (pl.slots > items ? (long)pl.slots : items) : fixed;
-  if (pl.ranks > 0 && items * 2 * pl.ranks > waves) waves = items * 2 * pl.ranks;
+  if (pl.ranks > 0 && items * rank_chunks(pl.ranks) > waves) waves = items * rank_chunks(pl.ranks);
   return (unsigned)((waves + waves_per_block - 1) / waves_per_block);
 }
 

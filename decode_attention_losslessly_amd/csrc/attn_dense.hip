@@ -121,7 +121,7 @@ __global__ __launch_bounds__(64 * kDenseWaves) void attn_dense_mha_kernel(
   if (!plan_work(plan, seq_lens, B, P, max_pages, true, H, (int)uniform(blockIdx.x * kDenseWaves + wave), lane, wi))
     return;
   const int S = plan.S, C = wi.C, s = wi.s, h = wi.k, r = wi.r;
-  int L = sload<int32_t>(seq_lens + r);
+  int L = request_len(wi, seq_lens);
   if (L > max_pages * P || L < 0) {
     if (lane == 0 && s == 0 && h == 0 && status) atomicOr(status, kStatusSeqTooLong);
     L = L < 0 ? 0 : max_pages * P;

@@ -283,7 +283,7 @@ __global__ __launch_bounds__(64 * kGqaWaves) KVZ_GQA_OCCUPANCY void attn_gqa_ker
     return;
   const int S = plan.S, C = wi.C, s = wi.s, qc = wi.k % nchunks, h = wi.k / nchunks, r = wi.r;
   const int hq0 = h * grp + qc * kGqaRows, nq = min(kGqaRows, grp - qc * kGqaRows);
-  int L = sload<int32_t>(seq_lens + r);
+  int L = request_len(wi, seq_lens);
   if (L > max_pages * P || L < 0) {
     if (lane == 0 && s == 0 && h == 0 && qc == 0) atomicOr(status, kStatusSeqTooLong);
     L = L < 0 ? 0 : max_pages * P;
@@ -396,7 +396,7 @@ __global__ __launch_bounds__(64 * kGqaWaves) KVZ_GQA_OCCUPANCY void attn_dense_g
     return;
   const int S = plan.S, C = wi.C, s = wi.s, qc = wi.k % nchunks, h = wi.k / nchunks, r = wi.r;
   const int hq0 = h * grp + qc * kGqaRows, nq = min(kGqaRows, grp - qc * kGqaRows);
-  int L = sload<int32_t>(seq_lens + r);
+  int L = request_len(wi, seq_lens);
   if (L > max_pages * P || L < 0) {
     if (lane == 0 && s == 0 && h == 0 && qc == 0 && status) atomicOr(status, kStatusSeqTooLong);
     L = L < 0 ? 0 : max_pages * P;

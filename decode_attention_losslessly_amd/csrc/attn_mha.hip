@@ -102,7 +102,7 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void attn_mha_kernel(
     return;
   const int S = plan.S, C = wi.C, s = wi.s, h = wi.k, r = wi.r;
   uint16_t* lds = lds_all[wave];
-  int L = sload<int32_t>(seq_lens + r);
+  int L = request_len(wi, seq_lens);
   if (L > max_pages * P || L < 0) {
     if (lane == 0 && s == 0 && h == 0) atomicOr(status, kStatusSeqTooLong);
     L = L < 0 ? 0 : max_pages * P;

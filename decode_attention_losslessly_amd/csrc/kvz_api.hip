@@ -94,11 +94,12 @@ int rank_count(int B, int Hq, int Hkv, int pps) {
   return items >= kTargetItems ? 1 : (int)(kTargetItems / items);
 }
 
-// split slots per (request, query head): the dynamic schedule's bound and the ranked one's 2R
+// split slots per (request, query head): the dynamic schedule's bound, and the ranked one's
+// chunks per row
 int slot_count(int B, int Hq, int Hkv, int P, int max_pages, int pps) {
   const int S = split_count(max_pages, pages_per_split(B, Hq, Hkv, P, max_pages, pps));
-  const int R = rank_count(B, Hq, Hkv, pps);
-  return 2 * R > S ? 2 * R : S;
+  const int n = kvz::rank_chunks(rank_count(B, Hq, Hkv, pps));
+  return n > S ? n : S;
 }
 
 bool shape_ok(int P, int D) { return P > 0 && P % 16 == 0 && D > 0 && D % 64 == 0; }
