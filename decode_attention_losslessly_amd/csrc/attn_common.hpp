@@ -174,17 +174,38 @@ __device__ __forceinline__ uint64_t plan_page_sum(const PlanPages& pp, const int
   return npg;
 }
 
+// most pages of one request in the batch (wave-uniform)
+__device__ __forceinline__ uint32_t plan_page_max(const PlanPages& pp, const int32_t* seq_lens, int B, int P,
+                                                  int max_pages, bool dense, int lane) {
+  uint32_t m = 0;
+  if (pp.held) {
+#pragma unroll
+    for (int j = 0; j < kPlanRegs; ++j) m = max(m, pp.np[j] > 0 ? (uint32_t)pp.np[j] : 0u);
+  } else {
+    for (int b0 = 0; b0 < B; b0 += 64) {
+      const int r = b0 + lane;
+      m = max(m, r < B ? (uint32_t)plan_pages(seq_lens[r], P, max_pages, dense) : 0u);
+    }
+  }
+  return wave_max_u32(m);
+}
+
 __device__ __forceinline__ bool plan_work(const SplitPlan& pl, const int32_t* seq_lens, int B, int P, int max_pages,
                                           bool dense, int ipr, int wave_id, int lane, WorkItem& w) {
   const uint64_t items = (uint64_t)B * ipr, slots = (uint64_t)pl.slots;
   if (pl.ranks > 0) {
-    // ranked when forced, or when a big chunk would hold at least rank_min pages on average:
+    // ranked when forced, or when the lengths are nearly even (the longest request at most
+    // 5/4 of the mean: chunks are shares of each request's pages, so in a ragged batch the
+    // longest requests' chunks would be the longest waves, where the split schedule cuts all
+    // work into equal splits) and a big chunk holds at least rank_min pages on average:
     // big share * pages of the batch / (B * R) >= rank_min
     const PlanPages pp = plan_load(seq_lens, B, P, max_pages, dense, lane);
     bool use = pl.rank_min <= 0;
     if (!use) {
       const uint64_t npg = plan_page_sum(pp, seq_lens, B, P, max_pages, dense, lane);
-      use = npg * kRankBig >= (uint64_t)pl.rank_min * B * pl.ranks * kRankOne;
+      const uint64_t mx = plan_page_max(pp, seq_lens, B, P, max_pages, dense, lane);
+      use = 4 * mx * (uint64_t)B <= 5 * npg &&
+            npg * kRankBig >= (uint64_t)pl.rank_min * B * pl.ranks * kRankOne;
     }
     if (use) {
       const int n = rank_chunks(pl.ranks);

@@ -127,6 +127,13 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
 }
 
+// unsigned max over the 64 lanes, returned wave-uniform
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int k = 1; k < 64; k <<= 1) v = max(v, (uint32_t)__shfl_xor((int)v, k));
+  return uniform(v);
+}
+
 // max over the 64 lanes, returned wave-uniform
 __device__ __forceinline__ float wave_max(float v) {
   v = fmaxf(v, __shfl_xor(v, 1));

@@ -110,6 +110,31 @@ def test_ranked_schedule_matches_oracle(cfg):
         assert kvz.chosen_pages_per_split(ws, w.B, w.Hq, w.Hkv, w.D, w.P, w.max_pages, pps) == 2 * pps
 
 
+@pytest.mark.parametrize("lens,ranked", [([6000] * 8, True), ([4000, 10000, 5000, 9000, 4500, 8000, 6000, 7000], False)])
+def test_schedule_choice(lens, ranked):
+    """Without pages_per_split the multi-head kernel takes the ranked schedule for even lengths
+    whose big chunks would be long (8 x 32 rows: R = 16, 300 of 375 pages in them), and the
+    split schedule when the longest request exceeds 5/4 of the mean, where chunks proportional
+    to each length would make the longest requests' chunks the longest waves. Sampled rows
+    against the oracle either way."""
+    w = make_workload(3, B=8, lens=lens, Hq=32, Hkv=32, n_append=0)
+    kp, vp = w.pages(0), w.pages(1)
+    cache, lt = build_cache(w, kp, vp)
+    q = w.q()
+    ws = torch.empty(kvz.workspace_bytes(w.B, w.Hq, w.Hkv, w.D, w.P, w.max_pages), dtype=torch.uint8, device=DEV)
+    out = torch.zeros((w.B, w.Hq, w.D), dtype=torch.int16, device=DEV)
+    out32 = torch.zeros((w.B, w.Hq, w.D), dtype=torch.float32, device=DEV)
+    kvz.decode_attention_splits(dev(q), cache, dev(w.page_table), lt, w.sm_scale, ws)
+    kvz.merge_splits(ws, lt, w.B, w.Hq, w.Hkv, w.D, w.P, w.max_pages, out, out32)
+    torch.cuda.synchronize()
+    assert int(cache.status.item()) == 0
+    assert (kvz.chosen_pages_per_split(ws, w.B, w.Hq, w.Hkv, w.D, w.P, w.max_pages) < 0) == ranked
+    rows = _sampled_rows(w, 16, 7)
+    ref = oracle_rows(w, kp, vp, q, rows)
+    idx = tuple(np.array(rows).T)
+    check_rows(host16(out)[idx], out32.cpu().numpy()[idx], ref, f"schedule ranked={ranked}")
+
+
 def test_dense_and_compressed_agree():
     w = make_workload(3, **SMALL[3])
     kp, vp = w.pages(0), w.pages(1)
