@@ -135,11 +135,12 @@ int32_t kvz_inline_capacity(int32_t P, int32_t D);
  *                        pass (the resident waves come from the runtime's occupancy query,
  *                        made on the host once per device and kernel at the first call). The
  *                        multi-head kernel over the escape format instead uses a ranked
- *                        schedule when the call's pages make its chunks large (on average at
- *                        least 16 pages): each row is cut into 2R chunks, R = max(1, 4096 /
- *                        (B H)); the first R take 80% of the request's pages in equal parts and
- *                        run first, the last R take the rest in shrinking parts, so that the
- *                        waves, whose speeds differ with their age on the SIMD, end together.
+ *                        schedule when the call's lengths are nearly even (the longest at most
+ *                        5/4 of the mean) and make its chunks large (on average at least 16
+ *                        pages): each row is cut into 2R chunks, R = max(1, 4096 / (B H)); the
+ *                        first R take 80% of the request's pages in equal parts and run first,
+ *                        the last R take the rest in shrinking parts, so that the waves, whose
+ *                        speeds differ with their age on the SIMD, end together.
  *   pages_per_split < 0  asks the multi-head kernel over the escape format for the ranked
  *                        schedule with R = -pages_per_split (at most 4096); other kernels then
  *                        choose as with 0.
