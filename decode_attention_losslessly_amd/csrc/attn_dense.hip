@@ -127,9 +127,16 @@ __global__ __launch_bounds__(64 * kDenseWaves) void attn_dense_mha_kernel(
     L = L < 0 ? 0 : max_pages * P;
   }
   const int npages = (L + P - 1) / P;
-  const int Sr = active_splits(npages, C);
+  const bool ranked = C < 0;   // chunks are shares of all the request's pages, the partial one included
+  const int Sr = ranked ? -C : active_splits(npages, C);
   if (s >= Sr) return;
-  const int p0 = s * C, p1 = min(p0 + C, npages);
+  int p0, p1;
+  if (ranked) {
+    rank_range(npages, s, plan.ranks, p0, p1);
+  } else {
+    p0 = s * C;
+    p1 = min(p0 + C, npages);
+  }
   uint32_t qv[D / 8];
   {
     const uint32_t* qrow = reinterpret_cast<const uint32_t*>(q + ((size_t)r * H + h) * D + (lane & 3) * (D / 4));
@@ -192,6 +199,7 @@ int launch_attn_dense_mha(const uint16_t* q, const uint16_t* k_pages, const uint
   } else {
     return -2;
   }
+  rank_fit(plan, plan.slots, (long)B * H);
   if (plan.slots <= 0) plan.slots = B * H * plan.S;
   const dim3 grid(plan_blocks(plan, (long)B * H, kDenseWaves));
   if (D == 128)

@@ -77,8 +77,8 @@ int pages_per_split(int B, int Hq, int Hkv, int P, int max_pages, int pps) {
 
 int split_count(int max_pages, int C) { return max_pages > 0 ? (max_pages + C - 1) / C : 1; }
 
-// Big ranks R of the ranked schedule (0: not used), which the multi-head kernel over the escape
-// format may use: the first round of kTargetItems waves takes R chunks of every item, and the
+// Big ranks R of the ranked schedule (0: not used), which the multi-head kernels (over the
+// escape format and the uncompressed baseline) may use: the first round of kTargetItems waves takes R chunks of every item, and the
 // rest R chunks more (the launch lowers R to its own resident waves). The kernel uses it only
 // when a big chunk averages kRankMinPages pages or more over the call's actual lengths;
 // pps < 0 forces it with -pps big ranks. (The grouped-query kernel, whose splits each write
@@ -242,13 +242,16 @@ int kvz_decode_attention_dense_splits(const uint16_t* q, const uint16_t* k_pages
   float* ws_acc = reinterpret_cast<float*>(workspace);
   float* ws_ml = ws_acc + (size_t)B * H_q * S * D;
   const float scale = sm_scale * 1.4426950408889634f;
-  const kvz::SplitPlan plan = make_plan(C, S, max_pages, pps > 0, ws_chosen(workspace, B, H_q, S, D));
-  if (H_q == H)
+  kvz::SplitPlan plan = make_plan(C, S, max_pages, pps > 0, ws_chosen(workspace, B, H_q, S, D));
+  if (H_q == H) {
+    plan.ranks = rank_count(B, H_q, H, pps);   // the baseline gets the same schedule as the compressed kernel
+    plan.rank_min = pps < 0 ? 0 : kRankMinPages;
     rc = kvz::launch_attn_dense_mha(q, k_pages, v_pages, page_table, max_pages, seq_lens, B, H, D, P, num_pages, plan,
                                     scale, ws_acc, ws_ml, status, as_stream(stream));
-  else
+  } else {
     rc = kvz::launch_attn_dense_gqa(q, k_pages, v_pages, page_table, max_pages, seq_lens, B, H_q, H, D, P, num_pages,
                                     plan, scale, ws_acc, ws_ml, status, as_stream(stream));
+  }
   return rc ? (rc == -2 ? KVZ_ERR_UNSUPPORTED : KVZ_ERR_HIP) : KVZ_OK;
 }
 

@@ -90,7 +90,8 @@ def test_ranked_schedule_matches_oracle(cfg):
     """The multi-head kernel's ranked schedule (pages_per_split = -R forces it: every row is cut
     into 2R chunks, each a share of its request's own pages, the last R shrinking) gives the
     oracle's attention and the default schedule's fp32 result up to reduction order; the kernel
-    records -2R where the merge reads it. Config 5 takes the pool paths inside the chunks."""
+    records -2R where the merge reads it. Config 5 takes the pool paths inside the chunks. The
+    uncompressed baseline under the same schedule matches the oracle too."""
     w = make_workload(cfg, **SMALL[cfg])
     kp, vp = w.pages(0), w.pages(1)
     cache, lens = build_cache(w, kp, vp)
@@ -108,6 +109,9 @@ def test_ranked_schedule_matches_oracle(cfg):
                          device=DEV)
         kvz.decode_attention_splits(dev(q), cache, dev(w.page_table), lens, w.sm_scale, ws, pages_per_split=pps)
         assert kvz.chosen_pages_per_split(ws, w.B, w.Hq, w.Hkv, w.D, w.P, w.max_pages, pps) == 2 * pps
+        # the uncompressed baseline under the same schedule
+        d16, d32 = _run(w, None, dev(w.seq_lens), q, dense_pages=(dev(kp), dev(vp)), pages_per_split=pps)
+        check_rows(d16.reshape(-1, w.D), d32.reshape(-1, w.D), ref, f"cfg{cfg} dense ranked {pps}")
 
 
 @pytest.mark.parametrize("lens,ranked", [([6000] * 8, True), ([4000, 10000, 5000, 9000, 4500, 8000, 6000, 7000], False)])
