@@ -21,8 +21,10 @@ def _copy(c: kvz.Cache) -> kvz.Cache:
                      c.esc_cursor.clone(), c.k_tail.clone(), c.v_tail.clone(), c.status.clone(), c.fmt)
 
 
-@pytest.mark.parametrize("cfg,Hq,Hkv,lens", [(3, 4, 4, [100, 37, 250]), (4, 8, 2, [60, 17, 200])])
-def test_replayed_decode_steps_match_eager(cfg, Hq, Hkv, lens):
+# pps -2: the multi-head kernel's ranked schedule (chosen on the device, like the split size)
+@pytest.mark.parametrize("cfg,Hq,Hkv,lens,pps", [(3, 4, 4, [100, 37, 250], 0), (3, 4, 4, [100, 37, 250], -2),
+                                                 (4, 8, 2, [60, 17, 200], 0)])
+def test_replayed_decode_steps_match_eager(cfg, Hq, Hkv, lens, pps):
     # the workload holds the final lengths; the cache starts N_STEPS tokens shorter
     w = make_workload(cfg, B=len(lens), lens=np.array(lens) + N_STEPS, Hq=Hq, Hkv=Hkv, D=128, n_append=0)
     kp, vp = w.pages(0), w.pages(1)
@@ -37,7 +39,8 @@ def test_replayed_decode_steps_match_eager(cfg, Hq, Hkv, lens):
     table, q = dev(w.page_table), dev(w.q())
     new_k = [dev(np.stack([w.token(r, int(L0[r]) + i, 0) for r in range(w.B)])) for i in range(N_STEPS)]
     new_v = [dev(np.stack([w.token(r, int(L0[r]) + i, 1) for r in range(w.B)])) for i in range(N_STEPS)]
-    ws = torch.empty(kvz.workspace_bytes(w.B, w.Hq, w.Hkv, w.D, w.P, w.max_pages), dtype=torch.uint8, device=DEV)
+    ws = torch.empty(kvz.workspace_bytes(w.B, w.Hq, w.Hkv, w.D, w.P, w.max_pages, pps), dtype=torch.uint8,
+                     device=DEV)
     torch.cuda.synchronize()
 
     # eager
@@ -47,7 +50,7 @@ def test_replayed_decode_steps_match_eager(cfg, Hq, Hkv, lens):
         out = torch.empty((w.B, w.Hq, w.D), dtype=torch.int16, device=DEV)
         out32 = torch.empty((w.B, w.Hq, w.D), dtype=torch.float32, device=DEV)
         kvz.append_token(ce, new_k[i], new_v[i], table, le)
-        kvz.decode_attention(q, ce, table, le, w.sm_scale, out, out32, workspace=ws)
+        kvz.decode_attention(q, ce, table, le, w.sm_scale, out, out32, workspace=ws, pages_per_split=pps)
         eager.append((out, out32))
     torch.cuda.synchronize()
 
@@ -63,7 +66,7 @@ def test_replayed_decode_steps_match_eager(cfg, Hq, Hkv, lens):
     with torch.cuda.stream(side):
         with torch.cuda.graph(graph, stream=side):
             kvz.append_token(cg, k_in, v_in, table, lg)
-            kvz.decode_attention(q, cg, table, lg, w.sm_scale, out_g, out32_g, workspace=ws_g)
+            kvz.decode_attention(q, cg, table, lg, w.sm_scale, out_g, out32_g, workspace=ws_g, pages_per_split=pps)
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
     assert np.array_equal(lg.cpu().numpy(), L0), "capturing must not run the step"
