@@ -6,10 +6,10 @@
 // schedule) are read from where it recorded them.
 // Output in BF16 (round to nearest even) and optionally in fp32; zeros when the request is empty.
 //
-// W waves per row: every wave reads all the maxima (one vector load per 64 splits) and takes the
-// splits s = w, w + W, ...; their acc rows are loaded 8 at a time, all 8 issued before the first
-// is used, so a row with many splits costs a few round trips rather than one per split; the W
-// partial sums meet in LDS. Rows with at most 8 splits take one wave each (4 rows per
+// W waves per row: each takes the splits s = w, w + W, ... in one pass, eight at a time (all 8
+// loads issued before the first is used), keeping its own running maximum, so a row costs one
+// round trip per 8 of a wave's splits; the W partial results meet in LDS, rescaled to the
+// largest maximum. Rows with at most 8 splits take one wave each (4 rows per
 // workgroup); otherwise few rows (a small batch, where the splits are many) get 16 waves per
 // row, and more rows 4.
 #include "attn_common.hpp"
@@ -24,7 +24,7 @@ __global__ __launch_bounds__(64 * W * R) void merge_kernel(const float* __restri
                                                        float* __restrict__ out_f32) {
   constexpr int NV = D / 64;
   __shared__ float sh_num[W][D];
-  __shared__ float sh_den[W];
+  __shared__ float sh_den[W], sh_max[W];
   static_assert(W == 1 || R == 1, "several waves per row: one row per workgroup");
   const int lane = threadIdx.x & 63;
   const int wave = W == 1 ? 0 : (int)(threadIdx.x >> 6);
@@ -38,48 +38,64 @@ __global__ __launch_bounds__(64 * W * R) void merge_kernel(const float* __restri
   const int Sr = min(c < 0 ? -c : active_splits(npages, max(1, c)), S);
   const float* ml = ws_ml + (size_t)row * S * 2;
   const float* acc = ws_acc + (size_t)row * S * D;
-  float M = -INFINITY;
-  for (int s0 = 0; s0 < Sr; s0 += 64)
-    if (s0 + lane < Sr) M = fmaxf(M, ml[2 * (s0 + lane)]);
-  M = wave_max(M);
-  float num[NV], den = 0.f;
+  // One pass: the wave's splits s = wave + W * k, eight at a time (all loads of a batch issued
+  // before the first is used), folded into a running maximum M, weight sum den and weighted
+  // sum num; a batch that raises M rescales what came before by 2^(M_old - M_new).
+  float M = -INFINITY, den = 0.f, num[NV];
 #pragma unroll
   for (int i = 0; i < NV; ++i) num[i] = 0.f;
-  if (M != -INFINITY) {
-    // this wave's splits s = wave + W * k, eight at a time
-    for (int k0 = 0; wave + W * k0 < Sr; k0 += 8) {
-      float wgt[8], a[8][NV];
+  for (int k0 = 0; wave + W * k0 < Sr; k0 += 8) {
+    float m[8], l[8], a[8][NV];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int s = wave + W * (k0 + j);
-        const bool ok = s < Sr;
-        const int sc = ok ? s : 0;
-        wgt[j] = ok ? __builtin_amdgcn_exp2f(ml[2 * sc] - M) : 0.f;
-        den += ok ? wgt[j] * ml[2 * sc + 1] : 0.f;
+    for (int j = 0; j < 8; ++j) {
+      const int s = wave + W * (k0 + j);
+      const int sc = s < Sr ? s : 0;
+      m[j] = s < Sr ? ml[2 * sc] : -INFINITY;
+      l[j] = ml[2 * sc + 1];
 #pragma unroll
-        for (int i = 0; i < NV; ++i) a[j][i] = acc[(size_t)sc * D + lane + 64 * i];
-      }
+      for (int i = 0; i < NV; ++i) a[j][i] = acc[(size_t)sc * D + lane + 64 * i];
+    }
+    float mb = M;
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
+    for (int j = 0; j < 8; ++j) mb = fmaxf(mb, m[j]);
+    if (mb == -INFINITY) continue;   // nothing but empty splits so far
+    const float f = __builtin_amdgcn_exp2f(M - mb);   // 0 while M is -inf
+    den *= f;
 #pragma unroll
-        for (int i = 0; i < NV; ++i) num[i] += wgt[j] * a[j][i];
+    for (int i = 0; i < NV; ++i) num[i] *= f;
+    M = mb;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float wj = __builtin_amdgcn_exp2f(m[j] - M);   // 0 for an empty split or a padded slot
+      den += wj * l[j];
+#pragma unroll
+      for (int i = 0; i < NV; ++i) num[i] += wj * a[j][i];
     }
   }
   float dsum = den;
   if constexpr (W > 1) {
 #pragma unroll
     for (int i = 0; i < NV; ++i) sh_num[wave][lane + 64 * i] = num[i];
-    if (lane == 0) sh_den[wave] = den;
+    if (lane == 0) {
+      sh_den[wave] = den;
+      sh_max[wave] = M;
+    }
     __syncthreads();
     if (wave != 0) return;
+    float Mt = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < W; ++w) Mt = fmaxf(Mt, sh_max[w]);
+    float fw[W];
+#pragma unroll
+    for (int w = 0; w < W; ++w) fw[w] = Mt == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sh_max[w] - Mt);
     dsum = 0.f;
 #pragma unroll
-    for (int w = 0; w < W; ++w) dsum += sh_den[w];
+    for (int w = 0; w < W; ++w) dsum += fw[w] * sh_den[w];
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       float n = 0.f;
 #pragma unroll
-      for (int w = 0; w < W; ++w) n += sh_num[w][lane + 64 * i];
+      for (int w = 0; w < W; ++w) n += fw[w] * sh_num[w][lane + 64 * i];
       num[i] = n;
     }
   }
