@@ -62,7 +62,9 @@ __device__ __forceinline__ int request_len(const WorkItem& w, const int32_t* seq
 // R = resident waves / items) take 80% of each item's pages in equal chunks, and the
 // kRankTailPer R tail ranks take the rest in chunks that shrink linearly to a fifth of the
 // first, which fill the slots of early finishers and end close together. Chunks are
-// proportional to each request's own length.
+// proportional to each request's own length, so the schedule suits batches of nearly even
+// lengths (the plan checks that); the multi-head kernels use it, the grouped-query ones keep
+// their split schedule.
 constexpr uint32_t kRankOne = 1u << 20;                 // shares are in units of 2^-20
 constexpr uint32_t kRankBig = kRankOne / 5 * 4;         // share of the first R ranks
 constexpr int kRankTaper = 5;                           // first / last tail chunk

@@ -134,15 +134,16 @@ int32_t kvz_inline_capacity(int32_t P, int32_t D);
  *                        keeps resident, so that batches of uneven lengths fill the GPU in one
  *                        pass (the resident waves come from the runtime's occupancy query,
  *                        made on the host once per device and kernel at the first call). The
- *                        multi-head kernel over the escape format instead uses a ranked
- *                        schedule when the call's lengths are nearly even (the longest at most
- *                        5/4 of the mean) and make its chunks large (on average at least 16
- *                        pages): each row is cut into 2R chunks, R = max(1, 4096 / (B H)); the
+ *                        multi-head kernels (compressed and uncompressed) instead use a
+ *                        ranked schedule when the call's lengths are nearly even (the longest
+ *                        at most 5/4 of the mean) and make its chunks large (on average at
+ *                        least 16 pages): each row is cut into 2R chunks, R = max(1, the
+ *                        kernel's resident waves / (B H)), at most max(1, 4096 / (B H)); the
  *                        first R take 80% of the request's pages in equal parts and run first,
  *                        the last R take the rest in shrinking parts, so that the waves, whose
  *                        speeds differ with their age on the SIMD, end together.
- *   pages_per_split < 0  asks the multi-head kernel over the escape format for the ranked
- *                        schedule with R = -pages_per_split (at most 4096); other kernels then
+ *   pages_per_split < 0  asks the multi-head kernels for the ranked schedule with
+ *                        R = -pages_per_split (at most 4096); the grouped-query kernels then
  *                        choose as with 0.
  * The same value must be passed to the attention call. */
 size_t kvz_workspace_bytes(int32_t B, int32_t H_q, int32_t H_kv, int32_t D, int32_t P,
