@@ -157,8 +157,7 @@ __device__ __forceinline__ uint64_t plan_total(const PlanPages& pp, const int32_
   return t;
 }
 
-// This wave's split (waves are numbered request by request, item by item, split by split);
-// false when the wave has none.
+// pages of all requests in the batch (wave-uniform)
 __device__ __forceinline__ uint64_t plan_page_sum(const PlanPages& pp, const int32_t* seq_lens, int B, int P,
                                                   int max_pages, bool dense, int lane) {
   uint64_t npg = 0;
@@ -192,6 +191,12 @@ __device__ __forceinline__ uint32_t plan_page_max(const PlanPages& pp, const int
   return wave_max_u32(m);
 }
 
+// This wave's split; false when the wave has none. Waves are numbered request by request, then,
+// for the compressed kernels, split by split and item by item: the four waves of a workgroup
+// then take the same split of four items of one request, which have the same length, so they
+// end together and free their workgroup's slots at once (a workgroup's slots are given back
+// only when all its waves are done). On a batch of uneven lengths with 32 heads this was 3.9%
+// faster; the uncompressed baseline measured 2.3% slower with it and keeps item by item.
 __device__ __forceinline__ bool plan_work(const SplitPlan& pl, const int32_t* seq_lens, int B, int P, int max_pages,
                                           bool dense, int ipr, int wave_id, int lane, WorkItem& w) {
   const uint64_t items = (uint64_t)B * ipr, slots = (uint64_t)pl.slots;
@@ -266,8 +271,13 @@ __device__ __forceinline__ bool plan_work(const SplitPlan& pl, const int32_t* se
     const uint32_t local = (uint32_t)((uint64_t)wave_id - base) - readlane(incl - cnt, l);
     const uint32_t n = readlane(sr, l);
     w.r = b0 + l;
-    w.k = (int)(local / n);
-    w.s = (int)(local % n);
+    if (dense) {   // item by item, split by split
+      w.k = (int)(local / n);
+      w.s = (int)(local % n);
+    } else {       // split by split, item by item
+      w.s = (int)(local / (uint32_t)ipr);
+      w.k = (int)(local % (uint32_t)ipr);
+    }
     w.C = C;
     w.L = plan_len(pp, w.r);
     return true;
