@@ -1,8 +1,9 @@
 // Pieces shared by the decode-attention kernels: split geometry, partial results, merge.
 //
 // Split-K over the sequence (flash-decoding): work item (request r, head, split s) covers the
-// full pages [s*C, min((s+1)*C, L/P)) of the request; the split that holds the last full page
-// (split 0 when there is none) also covers the L mod P tail rows. It leaves (m, l, acc[D]):
+// full pages [s*C, min((s+1)*C, L/P)) of the request, or under the ranked schedule below a
+// chunk whose pages are a share of the request's; the last split or chunk also covers the
+// L mod P tail rows. It leaves (m, l, acc[D]):
 // the running maximum of the log2-domain scores, the sum of exp2(score - m) and the weighted
 // sum of values. A second kernel merges the partials (the pages count this merge inside
 // attention's cost: ZipFusion summary, §IV.B "Attention Kernel Performance").

@@ -6,7 +6,8 @@
 // this one is organised for CDNA4 wave64 VALU work, because with one query row per KV head the
 // contraction is a matrix-vector product that does not fill a matrix core:
 //
-//   * one wave per (request, head, split); four independent waves per workgroup;
+//   * one wave per (request, head, split), or per (request, head, chunk) under the ranked
+//     schedule (attn_common.hpp); four independent waves per workgroup;
 //   * K tile (16 tokens x D): lane l rebuilds the storage pieces l + 64 i (16 dims of one
 //     token each: tokens l/8 and 8 + l/8 at D = 128, token l/4 at D = 64), so every load
 //     instruction reads whole cache lines; it dots them with its 16 dims of q in
@@ -82,7 +83,7 @@ __device__ __forceinline__ bool mha_compute(MhaState<D>& st, const MhaStage<D>& 
   return true;
 }
 
-// One wave per (request, head, split). The main loop handles units whose escapes are inline
+// One wave per (request, head, split or chunk). The main loop handles units whose escapes are inline
 // and skips a unit whose escapes are in the pool, remembering the first and last such page;
 // after the loop (when the pipeline's registers are free again) the wave adds those two pages
 // and any other pool unit between them, found by reading the unit headers 64 at a time. The
@@ -276,10 +277,11 @@ int launch_attn_mha(const uint16_t* q, const uint8_t* units, const uint16_t* poo
   } else {
     return -2;
   }
-  // Aim at two waves per resident slot: the multi-head waves run long chains whose lengths in
-  // time differ a little, and a second round lets the slots of early finishers take new work
-  // (measured 1-1.5% faster at 8K and 32K contexts, ragged or not; the grouped-query kernel,
-  // measured the same way, does best with one round).
+  // The ranked schedule's big ranks: one round of the resident waves. The split schedule aims
+  // at two waves per resident slot: waves on one SIMD run at different speeds, and a second
+  // round lets the slots of early finishers take new work (measured 1-1.5% faster at 8K and 32K
+  // contexts, ragged or not; the grouped-query kernel, measured the same way, does best with
+  // one round).
   rank_fit(plan, plan.slots, (long)B * H);
   plan.slots = plan.slots > 0 ? 2 * plan.slots : B * H * plan.S;
   const dim3 grid(plan_blocks(plan, (long)B * H, kWavesPerBlock));
