@@ -6,11 +6,11 @@ threads without changing any value.
 
 Draw recipe (numpy PCG64, one SeedSequence per item):
   * per-channel scales        SeedSequence([seed, 40 + tensor])      tensor: 0 = K, 1 = V
-  * outlier channels (cfg 2)  SeedSequence([seed, 50])
+  * outlier channels          SeedSequence([seed, 50])       (the workloads with outlier K channels)
   * page contents             SeedSequence([seed, 100 + tensor, page_id])
   * queries                   SeedSequence([seed, 10])
   * page-table permutation    SeedSequence([seed, 20])
-  * sequence lengths (cfg 4)  SeedSequence([seed, 30])
+  * sequence lengths          SeedSequence([seed, 30])       (the workload of uneven lengths)
 FP32 samples are rounded to BF16 with round-to-nearest-even.
 
 The workload shapes follow the serving setting of the ZipFusion summary (16-token pages,
@@ -204,7 +204,7 @@ def make_workload(cfg: int, *, B: int | None = None, L: int | None = None, seed:
         seq = np.full(B, L, np.int32)
     elif c["L"] is not None:
         seq = np.full(B, c["L"], np.int32)
-    else:  # config 4: uniform lengths in [1024, 8192]
+    else:  # the uneven-length workload: lengths uniform in [1024, 8192]
         seq = _rng(seed, 30).integers(1024, 8193, size=B).astype(np.int32)
     npr = (seq + P - 1) // P
     num_pages = int(npr.sum())

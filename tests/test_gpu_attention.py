@@ -90,7 +90,8 @@ def test_ranked_schedule_matches_oracle(cfg):
     """The multi-head kernel's ranked schedule (pages_per_split = -R forces it: every row is cut
     into 2R chunks, each a share of its request's own pages, the last R shrinking) gives the
     oracle's attention and the default schedule's fp32 result up to reduction order; the kernel
-    records -2R where the merge reads it. Config 5 takes the pool paths inside the chunks. The
+    records -2R where the merge reads it. The escape-stress workload takes the pool paths inside
+    the chunks. The
     uncompressed baseline under the same schedule matches the oracle too."""
     w = make_workload(cfg, **SMALL[cfg])
     kp, vp = w.pages(0), w.pages(1)
