@@ -91,8 +91,7 @@ def test_ranked_schedule_matches_oracle(cfg):
     into 2R chunks, each a share of its request's own pages, the last R shrinking) gives the
     oracle's attention and the default schedule's fp32 result up to reduction order; the kernel
     records -2R where the merge reads it. The escape-stress workload takes the pool paths inside
-    the chunks. The
-    uncompressed baseline under the same schedule matches the oracle too."""
+    the chunks. The uncompressed baseline under the same schedule matches the oracle too."""
     w = make_workload(cfg, **SMALL[cfg])
     kp, vp = w.pages(0), w.pages(1)
     cache, lens = build_cache(w, kp, vp)
