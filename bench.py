@@ -11,7 +11,7 @@ attention (ZipFusion summary, §IV.B: attention, fused reconstruction and split 
 the initial compression and the append are set-up (excluded there too, §IV.A) and are reported
 as separate fields.
 
-Prints one JSON line. `python bench.py --gpus N` with N > 1 exits with a message: this build
+Prints one JSON line. `python bench.py --gpus N` with N > 1 exits with a message: the library
 runs on one GPU.
 """
 from __future__ import annotations
@@ -78,7 +78,7 @@ def main() -> int:
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
-              "this build has no multi-GPU path", file=sys.stderr, flush=True)
+              "the library has no multi-GPU path", file=sys.stderr, flush=True)
         return 2
 
     import numpy as np
