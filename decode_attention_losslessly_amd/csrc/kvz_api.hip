@@ -86,7 +86,7 @@ int split_count(int max_pages, int C) { return max_pages > 0 ? (max_pages + C - 
 // query heads, measured slower with it, 3% to 35%, and so did the ZipFusion-format kernel, which
 // reads raw blocks from the pool: 925 -> 1114 us on the 8K batch of 32; both keep the split
 // schedule.)
-constexpr int kRankMinPages = 16;
+constexpr int kRankMinPages = 5;    // measured: ranked won at 6.4 pages per big chunk, lost at 3.2
 constexpr int kMaxForcedRanks = 4096;
 int rank_count(int B, int Hq, int Hkv, int pps) {
   if (pps < 0) return -pps;

@@ -137,7 +137,7 @@ int32_t kvz_inline_capacity(int32_t P, int32_t D);
  *                        multi-head kernels (compressed and uncompressed) instead use a
  *                        ranked schedule when the call's lengths are nearly even (the longest
  *                        at most 5/4 of the mean) and make its chunks large (on average at
- *                        least 16 pages): each row is cut into 2R chunks, R = max(1, the
+ *                        least 5 pages): each row is cut into 2R chunks, R = max(1, the
  *                        kernel's resident waves / (B H)), at most max(1, 4096 / (B H)); the
  *                        first R take 80% of the request's pages in equal parts and run first,
  *                        the last R take the rest in shrinking parts, so that the waves, whose
