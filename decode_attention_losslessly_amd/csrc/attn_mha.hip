@@ -88,9 +88,10 @@ __device__ __forceinline__ bool mha_compute(MhaState<D>& st, const MhaStage<D>& 
 // after the loop (when the pipeline's registers are free again) the wave adds those two pages
 // and any other pool unit between them, found by reading the unit headers 64 at a time. The
 // pool path thus costs registers only outside the loop, and the rare pool unit costs only its
-// own work.
+// own work. Four waves per SIMD is the register budget (128 VGPRs at D = 128): the streaming rate
+// needs them, and the pool-capable loop is fitted into it.
 template <int D>
-__global__ __launch_bounds__(64 * kWavesPerBlock) void attn_mha_kernel(
+__global__ __launch_bounds__(64 * kWavesPerBlock) __attribute__((amdgpu_waves_per_eu(4))) void attn_mha_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ units, const uint16_t* __restrict__ pool,
     int64_t pool_cap, const uint16_t* __restrict__ k_tail, const uint16_t* __restrict__ v_tail,
     const int32_t* __restrict__ page_table, int max_pages, const int32_t* __restrict__ seq_lens, int B, int H, int P,

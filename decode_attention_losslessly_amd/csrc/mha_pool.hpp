@@ -42,8 +42,10 @@ __device__ __forceinline__ uint4 pool_chunk(const uint16_t* pool, int64_t pool_c
   return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
-// Loads the pool ranges [kfirst, kfirst + kn) and [vfirst, vfirst + vn) (every load of both
-// issued before the first LDS write) into lds[0 ..) and lds[win_elems ..).
+// Loads the pool ranges [kfirst, kfirst + kn) and [vfirst, vfirst + vn) into lds[0 ..) and
+// lds[win_elems ..). Windows clear of the pool's end (all but the last few of a pool) go
+// straight from memory to LDS, 16 bytes per lane, with no registers held; a window that
+// reaches the end is read chunk by chunk, element by element at the end, through registers.
 template <int D>
 __device__ __forceinline__ void stage_windows(const uint16_t* pool, int64_t pool_cap, uint64_t kfirst, uint32_t kn,
                                               uint64_t vfirst, uint32_t vn, uint16_t* lds, Window& kw, Window& vw,
@@ -55,42 +57,62 @@ __device__ __forceinline__ void stage_windows(const uint16_t* pool, int64_t pool
   kw.avail = kn;
   vw.avail = vn;
   const uint32_t knch = kn ? (kw.mis + kn + 7) / 8 : 0u, vnch = vn ? (vw.mis + vn + 7) / 8 : 0u;
-  uint4 kv[NC], vv[NC];
-#pragma unroll
-  for (int c = 0; c < NC; ++c) {
-    const uint32_t ch = (uint32_t)lane + 64u * c;
-    kv[c] = ch < knch ? pool_chunk(pool, pool_cap, ka + 8ull * ch) : make_uint4(0, 0, 0, 0);
-    vv[c] = ch < vnch ? pool_chunk(pool, pool_cap, va + 8ull * ch) : make_uint4(0, 0, 0, 0);
-  }
   uint16_t* vl = lds + win_elems<D>();
+  if (ka + 8ull * knch <= (uint64_t)pool_cap && va + 8ull * vnch <= (uint64_t)pool_cap) {
+    // chunk ch = lane + 64 c lands at element 8 ch: row c of 64 lanes from element 512 c
 #pragma unroll
-  for (int c = 0; c < NC; ++c) {
-    const uint32_t ch = (uint32_t)lane + 64u * c;
-    if (ch < knch) *reinterpret_cast<uint4*>(lds + 8 * ch) = kv[c];
-    if (ch < vnch) *reinterpret_cast<uint4*>(vl + 8 * ch) = vv[c];
+    for (int c = 0; c < NC; ++c) {
+      const uint32_t ch = (uint32_t)lane + 64u * c;
+      if (ch < knch)
+        __builtin_amdgcn_global_load_lds(pool + ka + 8ull * ch, (__attribute__((address_space(3))) void*)(lds + 512 * c),
+                                         16, 0, 0);
+      if (ch < vnch)
+        __builtin_amdgcn_global_load_lds(pool + va + 8ull * ch, (__attribute__((address_space(3))) void*)(vl + 512 * c),
+                                         16, 0, 0);
+    }
+  } else {
+    uint4 kv[NC], vv[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const uint32_t ch = (uint32_t)lane + 64u * c;
+      kv[c] = ch < knch ? pool_chunk(pool, pool_cap, ka + 8ull * ch) : make_uint4(0, 0, 0, 0);
+      vv[c] = ch < vnch ? pool_chunk(pool, pool_cap, va + 8ull * ch) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const uint32_t ch = (uint32_t)lane + 64u * c;
+      if (ch < knch) *reinterpret_cast<uint4*>(lds + 8 * ch) = kv[c];
+      if (ch < vnch) *reinterpret_cast<uint4*>(vl + 8 * ch) = vv[c];
+    }
   }
   wave_lds_sync();
 }
 
 // Patches the escaped positions of one offset word (8 positions: out[k] holds positions 2k,
-// 2k+1) from a staged window; r0 is the list rank of the word's first escape. The word is
-// walked pair by pair with a running rank, so each escaped half costs a bit test, a compare
-// and an insert.
+// 2k+1) from a staged window; r0 is the list rank of the word's first escape. A word's escapes
+// are consecutive in the window from there, so every position reads the slot given by the
+// escapes before it (all eight reads issued together), and a per-half mask made from the
+// escape flags keeps the window value for an escaped position and the rebuilt value otherwise.
+// An index counts only the tile's own offset nibbles, so it stays below mis + kTile * D, inside
+// the window, whatever the data; slots past the staged list (a unit whose pool data were
+// dropped) hold stale values.
 __device__ __forceinline__ void patch_word(uint32_t W, uint32_t r0, const uint16_t* win, const Window& w,
                                           uint32_t* out) {
-  const uint32_t o = flags_in_order(escape_flags(W));   // pair k: bits 4k (low half), 4k+1 (high)
-  if (o == 0) return;
-  const uint32_t lim = w.mis + w.avail;
-  uint32_t r = w.mis + r0;                              // window index of the next escape
+  const uint32_t f = escape_flags(W);   // position 2k: bit 4k + 3; position 2k + 1: bit 4k + 19
+  uint32_t x[8];
+  uint32_t r = w.mis + r0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    x[j] = win[r];
+    r += (f >> (4 * (j >> 1) + 3 + 16 * (j & 1))) & 1u;
+  }
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    const uint32_t e0 = (o >> (4 * k)) & 1u, e1 = (o >> (4 * k + 1)) & 1u;
-    const uint32_t r1 = r + e0;
-    uint32_t v = out[k];
-    if (e0 && r < lim) v = (v & 0xFFFF0000u) | win[r];
-    if (e1 && r1 < lim) v = (v & 0x0000FFFFu) | ((uint32_t)win[r1] << 16);
-    out[k] = v;
-    r = r1 + e1;
+    // the flags of positions 2k, 2k + 1 moved to bits 15 and 31; selectors 8 and 9 spread them
+    // over the low and the high half
+    const uint32_t m = __builtin_amdgcn_perm(0u, f << (12 - 4 * k), 0x09090808u);
+    const uint32_t val = x[2 * k] | (x[2 * k + 1] << 16);
+    out[k] = (val & m) | (out[k] & ~m);
   }
 }
 
