@@ -99,18 +99,19 @@ __device__ __forceinline__ void stage_windows(const uint16_t* pool, int64_t pool
 __device__ __forceinline__ void patch_word(uint32_t W, uint32_t r0, const uint16_t* win, const Window& w,
                                           uint32_t* out) {
   const uint32_t f = escape_flags(W);   // position 2k: bit 4k + 3; position 2k + 1: bit 4k + 19
+  const char* p = reinterpret_cast<const char*>(win + w.mis + r0);
+  int e[8];        // -1 where the position is escaped, else 0
   uint32_t x[8];
-  uint32_t r = w.mis + r0;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    x[j] = win[r];
-    r += (f >> (4 * (j >> 1) + 3 + 16 * (j & 1))) & 1u;
+    e[j] = __builtin_amdgcn_sbfe((int)f, 4 * (j >> 1) + 3 + 16 * (j & 1), 1);
+    x[j] = *reinterpret_cast<const uint16_t*>(p);
+    p += __mul24(e[j], -2);   // the next slot follows an escaped position
   }
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    // the flags of positions 2k, 2k + 1 moved to bits 15 and 31; selectors 8 and 9 spread them
-    // over the low and the high half
-    const uint32_t m = __builtin_amdgcn_perm(0u, f << (12 - 4 * k), 0x09090808u);
+    // low half from position 2k's flag, high half from position 2k + 1's
+    const uint32_t m = __builtin_amdgcn_perm((uint32_t)e[2 * k + 1], (uint32_t)e[2 * k], 0x07060100u);
     const uint32_t val = x[2 * k] | (x[2 * k + 1] << 16);
     out[k] = (val & m) | (out[k] & ~m);
   }
