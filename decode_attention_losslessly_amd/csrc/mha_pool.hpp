@@ -58,17 +58,20 @@ __device__ __forceinline__ void stage_windows(const uint16_t* pool, int64_t pool
   vw.avail = vn;
   const uint32_t knch = kn ? (kw.mis + kn + 7) / 8 : 0u, vnch = vn ? (vw.mis + vn + 7) / 8 : 0u;
   uint16_t* vl = lds + win_elems<D>();
+  // chunk ch = lane + 64 c is pool element base + 8 ch and lands at window element 8 ch: a
+  // wave-uniform base per row c plus the lane's own 8 * lane
+  const uint16_t* kb = pool + ka;
+  const uint16_t* vb = pool + va;
+  const uint32_t lo = 8u * (uint32_t)lane;
   if (ka + 8ull * knch <= (uint64_t)pool_cap && va + 8ull * vnch <= (uint64_t)pool_cap) {
-    // chunk ch = lane + 64 c lands at element 8 ch: row c of 64 lanes from element 512 c
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-      const uint32_t ch = (uint32_t)lane + 64u * c;
-      if (ch < knch)
-        __builtin_amdgcn_global_load_lds(pool + ka + 8ull * ch, (__attribute__((address_space(3))) void*)(lds + 512 * c),
-                                         16, 0, 0);
-      if (ch < vnch)
-        __builtin_amdgcn_global_load_lds(pool + va + 8ull * ch, (__attribute__((address_space(3))) void*)(vl + 512 * c),
-                                         16, 0, 0);
+      if ((uint32_t)lane + 64u * c < knch)
+        __builtin_amdgcn_global_load_lds(kb + 512 * c + lo, (__attribute__((address_space(3))) void*)(lds + 512 * c), 16, 0,
+                                         0);
+      if ((uint32_t)lane + 64u * c < vnch)
+        __builtin_amdgcn_global_load_lds(vb + 512 * c + lo, (__attribute__((address_space(3))) void*)(vl + 512 * c), 16, 0,
+                                         0);
     }
   } else {
     uint4 kv[NC], vv[NC];
@@ -80,9 +83,8 @@ __device__ __forceinline__ void stage_windows(const uint16_t* pool, int64_t pool
     }
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-      const uint32_t ch = (uint32_t)lane + 64u * c;
-      if (ch < knch) *reinterpret_cast<uint4*>(lds + 8 * ch) = kv[c];
-      if (ch < vnch) *reinterpret_cast<uint4*>(vl + 8 * ch) = vv[c];
+      if ((uint32_t)lane + 64u * c < knch) *reinterpret_cast<uint4*>(lds + 512 * c + lo) = kv[c];
+      if ((uint32_t)lane + 64u * c < vnch) *reinterpret_cast<uint4*>(vl + 512 * c + lo) = vv[c];
     }
   }
   wave_lds_sync();
