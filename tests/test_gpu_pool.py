@@ -2,13 +2,14 @@
 units point at it; attention of the live requests is bit-identical before and after, with the old
 pool overwritten so that any read of it would show. Both cache formats (escape lists; ZipFusion
 raw blocks), on escape-heavy data. An undersized new pool drops the data of the units that do not
-fit (status bit set) and nothing reads past a pool."""
+fit (status bit set) and nothing reads past a pool. A pool filled exactly to its capacity, ending
+inside a 16-byte chunk, still gives attention within tolerance of the fp64 oracle."""
 import numpy as np
 import pytest
 import torch
 
 import decode_attention_losslessly_amd as kvz
-from kvz_testlib import DEV, build_cache, dev, full_page_ids
+from kvz_testlib import DEV, build_cache, check_rows, dev, full_page_ids, host16, oracle_rows
 from synth import make_workload
 
 pytestmark = pytest.mark.gpu
@@ -78,3 +79,30 @@ def test_undersized_pool_drops_and_stays_in_bounds(fmt):
     assert int(cache.status.item()) & kvz.kvz.STATUS_ESC_POOL_FULL
     assert int(cache.esc_cursor.item()) > 1000          # the cursor counts every request
     _attend(w, cache, lens, dev(w.q()))   # outputs unspecified (status says so); the run must stay in bounds
+
+
+@pytest.mark.parametrize("D,P", [(128, 16), (64, 32)])
+@pytest.mark.parametrize("pps", [0, 64])
+def test_pool_filled_to_capacity_matches_oracle(D, P, pps):
+    """The pool holds exactly what the cache needs and ends inside a 16-byte chunk, so the escape
+    windows of the last units reach its end and are read element by element up to the capacity.
+    pages_per_split 64 gives each row one split, whose wave walks most pages in the pool-capable
+    loop; 0 lets the device choose (shorter splits, more units through the per-unit path)."""
+    w = make_workload(5, n_append=0, B=2, L=12 * P, Hq=4, Hkv=4, D=D, P=P)
+    kp, vp = w.pages(0), w.pages(1)
+    probe, _ = build_cache(w, kp, vp)
+    need = int(probe.esc_cursor.item())
+    del probe
+    assert need % 8 != 0, need
+    cache, lens = build_cache(w, kp, vp, esc_capacity=need)
+    assert int(cache.status.item()) == 0 and int(cache.esc_cursor.item()) == need
+    q = w.q()
+    out = torch.zeros((w.B, w.Hq, w.D), dtype=torch.int16, device=DEV)
+    out32 = torch.full((w.B, w.Hq, w.D), float("nan"), dtype=torch.float32, device=DEV)
+    kvz.decode_attention(dev(q), cache, dev(w.page_table), lens, w.sm_scale, out, out32, pages_per_split=pps)
+    torch.cuda.synchronize()
+    assert int(cache.status.item()) == 0
+    rows = [(r, h) for r in range(w.B) for h in range(w.Hq)]
+    ref = oracle_rows(w, kp, vp, q, rows)
+    check_rows(host16(out).reshape(-1, D), out32.cpu().numpy().reshape(-1, D), ref,
+               f"D={D} P={P} pps={pps}, pool of {need} elements")
