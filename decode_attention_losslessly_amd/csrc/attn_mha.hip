@@ -148,12 +148,21 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) __attribute__((amdgpu_waves_pe
   bool bad = false;
   // Records a skipped (pool) tile. When most tiles so far went to the pool, the wave leaves the
   // pipelined loop at the next page and walks the rest with the pool-capable loop, which loads
-  // a tile's escapes with its payload instead of reloading the unit after the main loop.
+  // a tile's escapes with its payload instead of reloading the unit after the main loop. When
+  // every tile so far went to the pool, that loop starts over from the first step and nothing is
+  // left for after it.
   auto note = [&](const MhaStage<D>& stg, int done) {
     if (first_skip < 0) first_skip = stg.page;
     last_skip = stg.page;
     ++nskip;
-    if (nskip >= 2 && 2 * nskip > done) resume = (stg.page - p0 + 1) * T;
+    if (nskip >= 2 && 2 * nskip > done) {
+      if (nskip == done) {
+        resume = 0;
+        first_skip = last_skip = -1;
+      } else {
+        resume = (stg.page - p0 + 1) * T;
+      }
+    }
   };
   if (nsteps > 0) {
     // load cursor: step ln = (page lp, tile lt); it stays on the last step once there, and the
