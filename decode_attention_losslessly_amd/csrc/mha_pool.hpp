@@ -4,11 +4,12 @@
 // format).
 //
 // A wave that meets mostly pool units leaves the pipelined loop and walks the rest of its split
-// one tile at a time here. A tile's meta window is loaded one step ahead, so that its header
-// (pool offset and escape counts) is known when the tile's payload loads are issued: the K and
-// V escape windows that can hold the tile's escapes (from each block's cursor, at most a tile's
-// worth) are then loaded in the same round trip and written side by side into the wave's LDS
-// area, and every lane patches its own escaped positions from there with fixed register indices.
+// (all of it, when every tile so far went to the pool) one tile at a time here. A tile's meta
+// window is loaded one step ahead, so that its header (pool offset and escape counts) is known
+// when the tile's payload loads are issued: the K and V escape windows that can hold the tile's
+// escapes (from each block's cursor, at most a tile's worth) are then copied in the same round
+// trip, side by side, into the wave's LDS area, and every lane patches its own escaped positions
+// from there with fixed register indices.
 #pragma once
 
 #include "kvz_lanes.hpp"
@@ -24,8 +25,7 @@ static_assert(2 * win_elems<128>() == esc_lds_elems<128>(), "K and V windows fil
 static_assert(2 * win_elems<64>() == esc_lds_elems<64>(), "K and V windows fill the wave's LDS area");
 
 struct Window {
-  uint32_t mis;     // element `first` sits at window[mis]
-  uint32_t avail;   // elements of the list in the window
+  uint32_t mis;     // the list's first element sits at window[mis]
 };
 
 template <int D>
@@ -46,6 +46,8 @@ __device__ __forceinline__ uint4 pool_chunk(const uint16_t* pool, int64_t pool_c
 // lds[win_elems ..). Windows clear of the pool's end (all but the last few of a pool) go
 // straight from memory to LDS, 16 bytes per lane, with no registers held; a window that
 // reaches the end is read chunk by chunk, element by element at the end, through registers.
+// The wave-local fence at the end waits for the copies (they count as memory loads): the
+// compiler does not order a later LDS read after such a copy by itself.
 template <int D>
 __device__ __forceinline__ void stage_windows(const uint16_t* pool, int64_t pool_cap, uint64_t kfirst, uint32_t kn,
                                               uint64_t vfirst, uint32_t vn, uint16_t* lds, Window& kw, Window& vw,
@@ -54,8 +56,6 @@ __device__ __forceinline__ void stage_windows(const uint16_t* pool, int64_t pool
   const uint64_t ka = kfirst & ~7ull, va = vfirst & ~7ull;
   kw.mis = (uint32_t)(kfirst - ka);
   vw.mis = (uint32_t)(vfirst - va);
-  kw.avail = kn;
-  vw.avail = vn;
   const uint32_t knch = kn ? (kw.mis + kn + 7) / 8 : 0u, vnch = vn ? (vw.mis + vn + 7) / 8 : 0u;
   uint16_t* vl = lds + win_elems<D>();
   // chunk ch = lane + 64 c is pool element base + 8 ch and lands at window element 8 ch: a
@@ -96,8 +96,8 @@ __device__ __forceinline__ void stage_windows(const uint16_t* pool, int64_t pool
 // escapes before it (all eight reads issued together), and a per-half mask made from the
 // escape flags keeps the window value for an escaped position and the rebuilt value otherwise.
 // An index counts only the tile's own offset nibbles, so it stays below mis + kTile * D, inside
-// the window, whatever the data; slots past the staged list (a unit whose pool data were
-// dropped) hold stale values.
+// the window, whatever the data; slots past the staged list (a damaged unit whose escape
+// counts disagree with its offset codes) hold stale values.
 __device__ __forceinline__ void patch_word(uint32_t W, uint32_t r0, const uint16_t* win, const Window& w,
                                           uint32_t* out) {
   const uint32_t f = escape_flags(W);   // position 2k: bit 4k + 3; position 2k + 1: bit 4k + 19
@@ -174,7 +174,7 @@ __device__ __forceinline__ void mha_any_tile(MhaState<D>& st, const uint8_t* uni
   load_k<D, false>(unit, P, tile, lane, k);
   load_v<D>(unit, P, tile, lane, v);
   const bool in_pool = hdr.off != kInline;
-  Window kw = {0, 0}, vw = {0, 0};
+  Window kw = {0}, vw = {0};
   if (in_pool) {
     const uint32_t kr = uniform(krank), vr = uniform(vrank);
     const uint32_t kn = hdr.kc > kr ? min((uint32_t)(kTile * D), hdr.kc - kr) : 0u;
