@@ -320,11 +320,14 @@ inline void rank_fit(SplitPlan& pl, int resident, long items) {
   pl.ranks = (int)R;   // 0 when the workspace holds too few slots: the schedule is not used
 }
 
-// workgroups to launch: every split the plan can produce gets a wave
+// workgroups to launch: every split the plan can produce gets a wave. No item has more than S
+// splits or chunks (C >= C_lo; rank_fit keeps the chunks within S), so a small batch, whose
+// splits cannot fill the slots, launches no waves that would only exit.
 inline unsigned plan_blocks(const SplitPlan& pl, long items, int waves_per_block) {
   const long fixed = items * pl.S;                                   // C fixed: at most S per item
   long waves = pl.C_hi > pl.C_lo ? (pl.slots > items ? (long)pl.slots : items) : fixed;
   if (pl.ranks > 0 && items * rank_chunks(pl.ranks) > waves) waves = items * rank_chunks(pl.ranks);
+  if (waves > fixed) waves = fixed;
   return (unsigned)((waves + waves_per_block - 1) / waves_per_block);
 }
 

@@ -88,19 +88,25 @@ int split_count(int max_pages, int C) { return max_pages > 0 ? (max_pages + C - 
 // schedule.)
 constexpr int kRankMinPages = 5;    // measured: ranked won at 6.4 pages per big chunk, lost at 3.2
 constexpr int kMaxForcedRanks = 4096;
-int rank_count(int B, int Hq, int Hkv, int pps) {
+// No ranked slots are reserved when even requests of the table's full width would give big
+// chunks of less than half kRankMinPages pages (the launch sizes R from its own resident waves,
+// which may differ from kTargetItems by that much): the grid and the workspace then hold the
+// split schedule's waves only.
+int rank_count(int B, int Hq, int Hkv, int max_pages, int pps) {
   if (pps < 0) return -pps;
   if (pps > 0 || Hq != Hkv) return 0;
   const long items = (long)B * Hkv;
   if (items >= 2 * kTargetItems) return 0;
-  return items >= kTargetItems ? 1 : (int)(kTargetItems / items);
+  const int R = items >= kTargetItems ? 1 : (int)(kTargetItems / items);
+  if ((uint64_t)max_pages * kvz::kRankBig * 2 < (uint64_t)kRankMinPages * R * kvz::kRankOne) return 0;
+  return R;
 }
 
 // split slots per (request, query head): the dynamic schedule's bound, and the ranked one's
 // chunks per row
 int slot_count(int B, int Hq, int Hkv, int P, int max_pages, int pps) {
   const int S = split_count(max_pages, pages_per_split(B, Hq, Hkv, P, max_pages, pps));
-  const int n = kvz::rank_chunks(rank_count(B, Hq, Hkv, pps));
+  const int n = kvz::rank_chunks(rank_count(B, Hq, Hkv, max_pages, pps));
   return n > S ? n : S;
 }
 
@@ -215,7 +221,7 @@ int kvz_decode_attention_splits(const uint16_t* q, const kvz_cache* c, const int
                              seq_lens, B, H, D, P, c->num_pages, plan, scale, ws_acc, ws_ml, c->status,
                              as_stream(stream));
   } else if (H_q == H) {
-    plan.ranks = rank_count(B, H_q, H, pps);
+    plan.ranks = rank_count(B, H_q, H, max_pages, pps);
     plan.rank_min = pps < 0 ? 0 : kRankMinPages;
     rc = kvz::launch_attn_mha(q, c->units, c->esc_pool, c->esc_capacity, c->k_tail, c->v_tail, page_table, max_pages, seq_lens, B, H,
                               D, P, c->num_pages, plan, scale, ws_acc, ws_ml, c->status, as_stream(stream));
@@ -246,7 +252,7 @@ int kvz_decode_attention_dense_splits(const uint16_t* q, const uint16_t* k_pages
   const float scale = sm_scale * 1.4426950408889634f;
   kvz::SplitPlan plan = make_plan(C, S, max_pages, pps > 0, ws_chosen(workspace, B, H_q, S, D));
   if (H_q == H) {
-    plan.ranks = rank_count(B, H_q, H, pps);   // the baseline gets the same schedule as the compressed kernel
+    plan.ranks = rank_count(B, H_q, H, max_pages, pps);   // the baseline gets the same schedule as the compressed kernel
     plan.rank_min = pps < 0 ? 0 : kRankMinPages;
     rc = kvz::launch_attn_dense_mha(q, k_pages, v_pages, page_table, max_pages, seq_lens, B, H, D, P, num_pages, plan,
                                     scale, ws_acc, ws_ml, status, as_stream(stream));
