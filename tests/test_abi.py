@@ -57,6 +57,30 @@ def test_split_geometry():
     assert kvz.num_splits(1, 32, 32, 128, 16, 256) >= 32
 
 
+def test_ranked_slots_reserved_only_when_usable():
+    # Multi-head calls reserve slots for the ranked schedule's chunks (two per big rank, R big
+    # ranks from about 4096 waves over the batch's items) only when requests of the table's full
+    # width could give big chunks (80% of a row over R) of at least half the ranked minimum of
+    # 5 pages; otherwise the workspace, and the grid, hold the split schedule's slots only.
+    def split_only(B, Hq, mp):   # the split schedule's slots: C >= ceil(mp / (2 * 4096 / items))
+        cap = (2 * 4096 + B * Hq - 1) // (B * Hq)
+        c = max(4, (mp + cap - 1) // cap)
+        return (mp + c - 1) // c
+    # batch 1 x 4K: R = 128, 204.8 pages of big chunks < 320: split slots only
+    assert kvz.num_splits(1, 32, 32, 128, 16, 256) == split_only(1, 32, 256) == 64
+    # batch 1 x 16K: R = 128, 819.2 >= 320: 2 R = 256 chunk slots
+    assert kvz.num_splits(1, 32, 32, 128, 16, 1024) == 256
+    # 32 x 8K: R = 4, 8 chunk slots; the split schedule needs 8 as well
+    assert kvz.num_splits(32, 32, 32, 128, 16, 513) == 8
+    # 4 x 32K: R = 32, 64 chunk slots
+    assert kvz.num_splits(4, 32, 32, 128, 16, 2048) == 64
+    # grouped-query calls and fixed split sizes never reserve them
+    assert kvz.num_splits(1, 32, 8, 128, 16, 1024) == split_only(1, 8, 1024)
+    assert kvz.num_splits(1, 32, 32, 128, 16, 1024, pages_per_split=4) == 256
+    # a negative split size forces -pps big ranks: 2 chunks each
+    assert kvz.num_splits(1, 32, 32, 128, 16, 256, pages_per_split=-3) == max(6, split_only(1, 32, 256))
+
+
 def test_invalid_arguments_enqueue_nothing():
     L = binding.lib()
     assert L.kvz_compress_pages(None, None, None, None, 0, None) == binding.KVZ_ERR_INVALID_ARG
