@@ -141,7 +141,10 @@ int32_t kvz_inline_capacity(int32_t P, int32_t D);
  *                        kernel's resident waves / (B H)), at most max(1, 4096 / (B H)); the
  *                        first R take 80% of the request's pages in equal parts and run first,
  *                        the last R take the rest in shrinking parts, so that the waves, whose
- *                        speeds differ with their age on the SIMD, end together.
+ *                        speeds differ with their age on the SIMD, end together. The workspace
+ *                        holds slots for those chunks only when requests as long as the page
+ *                        table is wide could make big chunks of 2.5 pages or more (R counted
+ *                        from 4096 waves); otherwise these calls take the split schedule.
  *   pages_per_split < 0  asks the multi-head kernels for the ranked schedule with
  *                        R = -pages_per_split (at most 4096); the grouped-query kernels then
  *                        choose as with 0.
