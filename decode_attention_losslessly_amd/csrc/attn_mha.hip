@@ -150,12 +150,19 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) __attribute__((amdgpu_waves_pe
   // pipelined loop at the next page and walks the rest with the pool-capable loop, which loads
   // a tile's escapes with its payload instead of reloading the unit after the main loop. When
   // every tile so far went to the pool, that loop starts over from the first step and nothing is
-  // left for after it.
+  // left for after it. A first unit with a quarter or more of its values escaped starts it at
+  // once: that marks an escape-heavy cache (a unit goes to the pool as soon as its escapes
+  // outgrow the few inline entries).
   auto note = [&](const MhaStage<D>& stg, int done) {
     if (first_skip < 0) first_skip = stg.page;
     last_skip = stg.page;
     ++nskip;
-    if (nskip >= 2 && 2 * nskip > done) {
+    bool heavy = false;
+    if (nskip == 1 && done == 1) {
+      const UnitHeader hd = header_from_meta<D>(stg.meta);
+      heavy = (uint64_t)hd.kc + hd.vc >= (uint64_t)P * D / 2;
+    }
+    if (heavy || (nskip >= 2 && 2 * nskip > done)) {
       if (nskip == done) {
         resume = 0;
         first_skip = last_skip = -1;
