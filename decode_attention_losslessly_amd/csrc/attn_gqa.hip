@@ -18,6 +18,7 @@
 //   * output rows r and r+8 are summed at the end.
 #include "attn_common.hpp"
 #include "kvz_lanes.hpp"
+#include "mha_pool.hpp"
 
 namespace kvz {
 
@@ -158,6 +159,77 @@ __device__ __forceinline__ bool gqa_c_compute(GqaState& st, const GqaCStage& stg
   const int vdim[2] = {lane, lane + 64};
   gqa_tile(st, kp, vdim, vp, kTile, scale, vlds, lane);
   return true;
+}
+
+// K tile of a pool unit in this kernel's lane layout (lane l holds the adjacent storage pieces
+// 2c, 2c + 1, c = 4 (l % 16) + l / 16): ranks in storage order from one scan in chunk order,
+// then every lane patches its four offset words from the staged window. Returns the tile's
+// escape count.
+__device__ __forceinline__ uint32_t win_patch_k_gqa(uint32_t (&pairs)[16], const KRaw<128>& raw, const uint16_t* win,
+                                                    const Window& w, int lane) {
+  uint32_t c0[2], c1[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    c0[i] = popc_flags(escape_flags(raw.nib[2 * i]));
+    c1[i] = popc_flags(escape_flags(raw.nib[2 * i + 1]));
+  }
+  const uint32_t cl = c0[0] + c1[0] + c0[1] + c1[1];
+  const uint32_t c_ord = (uint32_t)__shfl((int)cl, 16 * (lane & 3) + (lane >> 2));   // chunk `lane`'s count
+  const uint32_t inc = wave_incl_scan(c_ord);
+  const uint32_t total = readlane(inc, 63);
+  uint32_t r = (uint32_t)__shfl((int)(inc - c_ord), 4 * (lane & 15) + (lane >> 4));  // this lane's chunk
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    patch_word(raw.nib[2 * i], r, win, w, &pairs[8 * i]);
+    patch_word(raw.nib[2 * i + 1], r + c0[i], win, w, &pairs[8 * i + 4]);
+    r += c0[i] + c1[i];
+  }
+  return total;
+}
+
+// One tile of any unit for the pool-capable loop: `meta` is its meta window (loaded a step
+// ahead); the payload and, for a pool unit, both escape windows go out in one round trip.
+// krank / vrank are the block cursors, reset at tile 0.
+__device__ __forceinline__ void gqa_any_tile(GqaState& st, const uint8_t* unit, uint32_t meta, int P, int tile,
+                                             uint32_t& krank, uint32_t& vrank, uint16_t* lds, uint32_t* vlds,
+                                             const uint16_t* pool, int64_t pool_cap, float scale, int lane) {
+  UnitHeader hdr = header_from_meta<128>(meta);
+  clamp_to_pool(hdr, pool_cap);
+  if (tile == 0) { krank = 0; vrank = 0; }
+  KRaw<128> k;
+  VRaw<128> v;
+  load_k<128, true>(unit, P, tile, lane, k);
+  load_v<128>(unit, P, tile, lane, v);
+  const bool in_pool = hdr.off != kInline;
+  Window kw = {0}, vw = {0};
+  if (in_pool) {
+    const uint32_t kr = uniform(krank), vr = uniform(vrank);
+    const uint32_t kn = hdr.kc > kr ? min((uint32_t)(kTile * 128), hdr.kc - kr) : 0u;
+    const uint32_t vn = hdr.vc > vr ? min((uint32_t)(kTile * 128), hdr.vc - vr) : 0u;
+    stage_windows<128>(pool, pool_cap, hdr.off + kr, kn, hdr.off + hdr.kc + vr, vn, lds, kw, vw, lane);
+  }
+  uint32_t kp[16];
+  decode_k<128>(k, kp);
+  if (hdr.kc) {
+    if (in_pool) krank = uniform(krank) + win_patch_k_gqa(kp, k, lds, kw, lane);
+    else patch_k_tile<128, true, false>(kp, k, meta, hdr, P, tile, krank, lds, pool, pool_cap, lane);
+  }
+  uint32_t vflat[16];
+#pragma unroll
+  for (int g = 0; g < 2; ++g) decode_v_seg(v.seg[g], v_bases<128>(meta, g), &vflat[8 * g]);
+  if (hdr.vc) {
+    if (in_pool) vrank = uniform(vrank) + win_patch_v<128>(vflat, v, lds + win_elems<128>(), vw);
+    else patch_v_tile<128, false, 2>(vflat, v, meta, hdr, P, tile, vrank, lds, pool, pool_cap, lane);
+  }
+  if (in_pool) wave_lds_sync();   // the window reads are complete before the next staging writes
+  uint32_t vp[2][8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    vp[0][j] = vflat[j];
+    vp[1][j] = vflat[8 + j];
+  }
+  const int vdim[2] = {lane, lane + 64};
+  gqa_tile(st, kp, vdim, vp, kTile, scale, vlds, lane);
 }
 
 // ---------------------------------------------------------------- raw (dense / tail) source
@@ -306,10 +378,30 @@ __global__ __launch_bounds__(64 * kGqaWaves) KVZ_GQA_OCCUPANCY void attn_gqa_ker
   uint32_t* vlds = vlds_all[wave];
   const int nsteps = (p1 > p0 ? p1 - p0 : 0) * T;
   int first_skip = -1, last_skip = -1;
+  int nskip = 0;          // tiles skipped by the main loop
+  int resume = -1;        // step from which the pool-capable loop takes over
   bool bad = false;
-  auto note = [&](const GqaCStage& stg) {
+  // Records a skipped (pool) tile; the same rules as the multi-head kernel: most tiles so far in
+  // the pool sends the wave to the pool-capable loop at the next page, from the split's first
+  // step when every tile so far went there, and at once when the first unit has a quarter or
+  // more of its values escaped.
+  auto note = [&](const GqaCStage& stg, int done) {
     if (first_skip < 0) first_skip = stg.page;
     last_skip = stg.page;
+    ++nskip;
+    bool heavy = false;
+    if (nskip == 1 && done == 1) {
+      const UnitHeader hd = header_from_meta<128>(stg.meta);
+      heavy = (uint64_t)hd.kc + hd.vc >= (uint64_t)P * 128 / 2;
+    }
+    if (heavy || (nskip >= 2 && 2 * nskip > done)) {
+      if (nskip == done) {
+        resume = 0;
+        first_skip = last_skip = -1;
+      } else {
+        resume = (stg.page - p0 + 1) * T;
+      }
+    }
   };
   if (nsteps > 0) {
     // load cursor as in the multi-head kernel: stays on the last step once there
@@ -334,13 +426,40 @@ __global__ __launch_bounds__(64 * kGqaWaves) KVZ_GQA_OCCUPANCY void attn_gqa_ker
       advance();
       pid = sload<int32_t>(pt_row + lp);
       bad |= !a.ok;
-      if (!gqa_c_compute<false>(st, a, P, krank, vrank, esc_lds, vlds, pool, pool_cap, scale, lane)) note(a);
-      if (i + 1 >= nsteps) break;
+      if (!gqa_c_compute<false>(st, a, P, krank, vrank, esc_lds, vlds, pool, pool_cap, scale, lane)) note(a, i + 1);
+      if (i + 1 >= nsteps || resume >= 0) break;
       gqa_c_issue(a, units, pid, lp, lt, H, h, P, num_pages, lane, live);
       advance();
       pid = sload<int32_t>(pt_row + lp);
       bad |= !b.ok;
-      if (!gqa_c_compute<false>(st, b, P, krank, vrank, esc_lds, vlds, pool, pool_cap, scale, lane)) note(b);
+      if (!gqa_c_compute<false>(st, b, P, krank, vrank, esc_lds, vlds, pool, pool_cap, scale, lane)) note(b, i + 2);
+      if (resume >= 0) break;
+    }
+  }
+  if (resume >= 0 && resume < nsteps) {
+    // the rest of the split, every unit as it comes; the next tile's meta window is in flight
+    // while a tile is computed
+    auto unit_of = [&](int n, bool& ok) {
+      const int pid = sload<int32_t>(pt_row + p0 + n / T);
+      ok = pid >= 0 && pid < num_pages;
+      return units + ((size_t)(ok ? pid : 0) * H + h) * unit_bytes(P, 128);
+    };
+    bool ok;
+    const uint8_t* u = unit_of(resume, ok);
+    uint32_t meta = load_meta(u, P, 128, resume % T, lane);
+    for (int n = resume; n < nsteps; ++n) {
+      bool nok = true;
+      const uint8_t* nu = u;
+      uint32_t nmeta = 0;
+      if (n + 1 < nsteps) {
+        nu = unit_of(n + 1, nok);
+        nmeta = load_meta(nu, P, 128, (n + 1) % T, lane);
+      }
+      if (ok) gqa_any_tile(st, u, meta, P, n % T, krank, vrank, esc_lds, vlds, pool, pool_cap, scale, lane);
+      bad |= !ok;
+      u = nu;
+      ok = nok;
+      meta = nmeta;
     }
   }
   if (bad && lane == 0) atomicOr(status, kStatusBadPage);

@@ -74,17 +74,21 @@ __device__ __forceinline__ void stage_windows(const uint16_t* pool, int64_t pool
                                          0);
     }
   } else {
-    uint4 kv[NC], vv[NC];
+    // K's window, then V's (one tensor's chunks in registers at a time)
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      const uint32_t ch = (uint32_t)lane + 64u * c;
-      kv[c] = ch < knch ? pool_chunk(pool, pool_cap, ka + 8ull * ch) : make_uint4(0, 0, 0, 0);
-      vv[c] = ch < vnch ? pool_chunk(pool, pool_cap, va + 8ull * ch) : make_uint4(0, 0, 0, 0);
-    }
+    for (int t = 0; t < 2; ++t) {
+      const uint64_t a0 = t ? va : ka;
+      const uint32_t nch = t ? vnch : knch;
+      uint16_t* dst = t ? vl : lds;
+      uint4 x[NC];
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      if ((uint32_t)lane + 64u * c < knch) *reinterpret_cast<uint4*>(lds + 512 * c + lo) = kv[c];
-      if ((uint32_t)lane + 64u * c < vnch) *reinterpret_cast<uint4*>(vl + 512 * c + lo) = vv[c];
+      for (int c = 0; c < NC; ++c) {
+        const uint32_t ch = (uint32_t)lane + 64u * c;
+        x[c] = ch < nch ? pool_chunk(pool, pool_cap, a0 + 8ull * ch) : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+        if ((uint32_t)lane + 64u * c < nch) *reinterpret_cast<uint4*>(dst + 512 * c + lo) = x[c];
     }
   }
   wave_lds_sync();
