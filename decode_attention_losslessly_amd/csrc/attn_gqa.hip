@@ -337,8 +337,9 @@ __device__ __forceinline__ void gqa_store(const GqaState& st, int r, int Hq, int
 #define KVZ_GQA_OCCUPANCY __attribute__((amdgpu_waves_per_eu(3)))
 
 // One wave per (request, KV head, chunk of query heads, split). As in the multi-head kernel,
-// the main loop skips units whose escapes are in the pool, and the wave adds them after the
-// loop, when the pipeline's registers are free.
+// the main loop skips units whose escapes are in the pool and the wave adds them after the
+// loop, when the pipeline's registers are free; a split that meets mostly such units goes on
+// in the pool-capable loop instead.
 __global__ __launch_bounds__(64 * kGqaWaves) KVZ_GQA_OCCUPANCY void attn_gqa_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ units, const uint16_t* __restrict__ pool,
     int64_t pool_cap, const uint16_t* __restrict__ k_tail, const uint16_t* __restrict__ v_tail,

@@ -1,7 +1,8 @@
-// The multi-head kernel's path for caches whose units mostly keep their escapes in the pool
-// (too many for the unit's inline area; the escape lists then live in the pool, values only,
-// in storage order: the pages' format has no escapes, so this is the build's own part of the
-// format).
+// The path for caches whose units mostly keep their escapes in the pool (too many for the
+// unit's inline area; the escape lists then live in the pool, values only, in storage order:
+// the pages' format has no escapes, so this is the build's own part of the format). The
+// multi-head kernel's tile is here; the window staging, the word patch and the V patch also
+// serve the grouped-query kernel, whose V lanes are laid out the same way.
 //
 // A wave that meets mostly pool units leaves the pipelined loop and walks the rest of its split
 // (all of it, when every tile so far went to the pool) one tile at a time here. A tile's meta
