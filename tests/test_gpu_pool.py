@@ -3,7 +3,8 @@ units point at it; attention of the live requests is bit-identical before and af
 pool overwritten so that any read of it would show. Both cache formats (escape lists; ZipFusion
 raw blocks), on escape-heavy data. An undersized new pool drops the data of the units that do not
 fit (status bit set) and nothing reads past a pool. A pool filled exactly to its capacity, ending
-inside a 16-byte chunk, still gives attention within tolerance of the fp64 oracle."""
+inside a 16-byte chunk, and escape-heavy units under grouped-query attention still give attention
+within tolerance of the fp64 oracle."""
 import numpy as np
 import pytest
 import torch
@@ -106,3 +107,24 @@ def test_pool_filled_to_capacity_matches_oracle(D, P, pps):
     ref = oracle_rows(w, kp, vp, q, rows)
     check_rows(host16(out).reshape(-1, D), out32.cpu().numpy().reshape(-1, D), ref,
                f"D={D} P={P} pps={pps}, pool of {need} elements")
+
+
+@pytest.mark.parametrize("P", [16, 32])
+@pytest.mark.parametrize("pps", [0, 64])
+def test_grouped_query_pool_loop_matches_oracle(P, pps):
+    """Escape-heavy units under grouped-query attention (8 query heads over 2 KV heads): the
+    first unit has a quarter or more of its values escaped, so a wave moves to the pool-capable
+    loop at once; with 32-token pages a unit spans two tiles, whose escape windows start at the
+    block cursors. One split per row (64) or the device's choice (0)."""
+    w = make_workload(5, n_append=0, B=3, lens=np.array([10 * P + 5, 7 * P, 12 * P + 9]), Hq=8, Hkv=2, D=128, P=P)
+    kp, vp = w.pages(0), w.pages(1)
+    cache, lens = build_cache(w, kp, vp)
+    q = w.q()
+    out = torch.zeros((w.B, w.Hq, w.D), dtype=torch.int16, device=DEV)
+    out32 = torch.full((w.B, w.Hq, w.D), float("nan"), dtype=torch.float32, device=DEV)
+    kvz.decode_attention(dev(q), cache, dev(w.page_table), lens, w.sm_scale, out, out32, pages_per_split=pps)
+    torch.cuda.synchronize()
+    assert int(cache.status.item()) == 0
+    rows = [(r, h) for r in range(w.B) for h in range(w.Hq)]
+    ref = oracle_rows(w, kp, vp, q, rows)
+    check_rows(host16(out).reshape(-1, w.D), out32.cpu().numpy().reshape(-1, w.D), ref, f"P={P} pps={pps}")
