@@ -161,32 +161,6 @@ __device__ __forceinline__ bool gqa_c_compute(GqaState& st, const GqaCStage& stg
   return true;
 }
 
-// K tile of a pool unit in this kernel's lane layout (lane l holds the adjacent storage pieces
-// 2c, 2c + 1, c = 4 (l % 16) + l / 16): ranks in storage order from one scan in chunk order,
-// then every lane patches its four offset words from the staged window. Returns the tile's
-// escape count.
-__device__ __forceinline__ uint32_t win_patch_k_gqa(uint32_t (&pairs)[16], const KRaw<128>& raw, const uint16_t* win,
-                                                    const Window& w, int lane) {
-  uint32_t c0[2], c1[2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    c0[i] = popc_flags(escape_flags(raw.nib[2 * i]));
-    c1[i] = popc_flags(escape_flags(raw.nib[2 * i + 1]));
-  }
-  const uint32_t cl = c0[0] + c1[0] + c0[1] + c1[1];
-  const uint32_t c_ord = (uint32_t)__shfl((int)cl, 16 * (lane & 3) + (lane >> 2));   // chunk `lane`'s count
-  const uint32_t inc = wave_incl_scan(c_ord);
-  const uint32_t total = readlane(inc, 63);
-  uint32_t r = (uint32_t)__shfl((int)(inc - c_ord), 4 * (lane & 15) + (lane >> 4));  // this lane's chunk
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    patch_word(raw.nib[2 * i], r, win, w, &pairs[8 * i]);
-    patch_word(raw.nib[2 * i + 1], r + c0[i], win, w, &pairs[8 * i + 4]);
-    r += c0[i] + c1[i];
-  }
-  return total;
-}
-
 // One tile of any unit for the pool-capable loop: `meta` is its meta window (loaded a step
 // ahead); the payload and, for a pool unit, both escape windows go out in one round trip.
 // krank / vrank are the block cursors, reset at tile 0.
@@ -200,27 +174,12 @@ __device__ __forceinline__ void gqa_any_tile(GqaState& st, const uint8_t* unit, 
   VRaw<128> v;
   load_k<128, true>(unit, P, tile, lane, k);
   load_v<128>(unit, P, tile, lane, v);
-  const bool in_pool = hdr.off != kInline;
-  Window kw = {0}, vw = {0};
-  if (in_pool) {
-    const uint32_t kr = uniform(krank), vr = uniform(vrank);
-    const uint32_t kn = hdr.kc > kr ? min((uint32_t)(kTile * 128), hdr.kc - kr) : 0u;
-    const uint32_t vn = hdr.vc > vr ? min((uint32_t)(kTile * 128), hdr.vc - vr) : 0u;
-    stage_windows<128>(pool, pool_cap, hdr.off + kr, kn, hdr.off + hdr.kc + vr, vn, lds, kw, vw, lane);
-  }
+  Window kw, vw;
+  const bool in_pool = any_stage<128>(hdr, krank, vrank, lds, pool, pool_cap, kw, vw, lane);
   uint32_t kp[16];
-  decode_k<128>(k, kp);
-  if (hdr.kc) {
-    if (in_pool) krank = uniform(krank) + win_patch_k_gqa(kp, k, lds, kw, lane);
-    else patch_k_tile<128, true, false>(kp, k, meta, hdr, P, tile, krank, lds, pool, pool_cap, lane);
-  }
+  any_rebuild_k<128, true>(kp, k, meta, hdr, in_pool, kw, P, tile, krank, lds, pool, pool_cap, lane);
   uint32_t vflat[16];
-#pragma unroll
-  for (int g = 0; g < 2; ++g) decode_v_seg(v.seg[g], v_bases<128>(meta, g), &vflat[8 * g]);
-  if (hdr.vc) {
-    if (in_pool) vrank = uniform(vrank) + win_patch_v<128>(vflat, v, lds + win_elems<128>(), vw);
-    else patch_v_tile<128, false, 2>(vflat, v, meta, hdr, P, tile, vrank, lds, pool, pool_cap, lane);
-  }
+  any_rebuild_v<128>(vflat, v, meta, hdr, in_pool, vw, P, tile, vrank, lds, pool, pool_cap, lane);
   if (in_pool) wave_lds_sync();   // the window reads are complete before the next staging writes
   uint32_t vp[2][8];
 #pragma unroll
@@ -363,11 +322,13 @@ __global__ __launch_bounds__(64 * kGqaWaves) KVZ_GQA_OCCUPANCY void attn_gqa_ker
   }
   int nfull = L / P;
   const int rows = L % P;
-  if (num_pages <= 0 && nfull > 0) {   // no unit slots: every full page is a bad id
+  // the splits the plan and the merge count for this row; with no unit slots every full page is
+  // a bad id and is skipped, but every counted split still writes its (empty) partial
+  const int Sr = active_splits(nfull, C);
+  if (num_pages <= 0 && nfull > 0) {
     if (lane == 0 && s == 0 && h == 0 && qc == 0) atomicOr(status, kStatusBadPage);
     nfull = 0;
   }
-  const int Sr = active_splits(nfull, C);
   if (s >= Sr) return;
   const int p0 = s * C, p1 = min(p0 + C, nfull);
   GqaState st;
@@ -522,11 +483,11 @@ __global__ __launch_bounds__(64 * kGqaWaves) KVZ_GQA_OCCUPANCY void attn_dense_g
     L = L < 0 ? 0 : max_pages * P;
   }
   int npages = (L + P - 1) / P;
+  const int Sr = active_splits(npages, C);   // as the merge counts them (see the compressed kernel)
   if (num_pages <= 0 && npages > 0) {   // no pages: every page id is bad
     if (lane == 0 && s == 0 && h == 0 && qc == 0 && status) atomicOr(status, kStatusBadPage);
     npages = 0;
   }
-  const int Sr = active_splits(npages, C);
   if (s >= Sr) return;
   const int p0 = s * C, p1 = min(p0 + C, npages);
   GqaState st;

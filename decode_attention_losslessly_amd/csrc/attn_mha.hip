@@ -111,12 +111,14 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) __attribute__((amdgpu_waves_pe
   }
   int nfull = L / P;
   const int rows = L % P;
-  if (num_pages <= 0 && nfull > 0) {   // no unit slots: every full page is a bad id
+  // the splits the plan and the merge count for this row; with no unit slots every full page is
+  // a bad id and is skipped, but every counted split still writes its (empty) partial
+  const int Sr = C < 0 ? -C : active_splits(nfull, C);
+  if (num_pages <= 0 && nfull > 0) {
     if (lane == 0 && s == 0 && h == 0) atomicOr(status, kStatusBadPage);
     nfull = 0;
   }
   const bool ranked = C < 0;
-  const int Sr = ranked ? -C : active_splits(nfull, C);
   if (s >= Sr) return;
   int p0, p1;
   if (ranked) {

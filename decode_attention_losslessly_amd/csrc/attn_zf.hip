@@ -110,11 +110,11 @@ __global__ __launch_bounds__(64 * kZfWaves) void attn_zf_kernel(
   }
   int nfull = L / P;
   const int rows = L % P;
+  const int Sr = active_splits(nfull, C);   // as the merge counts them (see the escape-format kernel)
   if (num_pages <= 0 && nfull > 0) {
     if (lane == 0 && s == 0 && h == 0) atomicOr(status, kStatusBadPage);
     nfull = 0;
   }
-  const int Sr = active_splits(nfull, C);
   if (s >= Sr) return;
   const int p0 = s * C, p1 = min(p0 + C, nfull);
   const size_t slot = ((size_t)r * H + h) * S + s;

@@ -122,6 +122,7 @@ hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
 }  // namespace
 
+
 extern "C" {
 
 size_t kvz_unit_bytes(int32_t P, int32_t D) { return shape_ok(P, D) ? kvz::unit_bytes(P, D) : 0; }
@@ -131,6 +132,7 @@ size_t kvz_unit_bytes_for(int32_t format, int32_t P, int32_t D) {
   if (format == KVZ_FORMAT_ZIPFUSION) return kvz::zf_unit_bytes(P, D);
   return 0;
 }
+size_t kvz_payload_bytes(int32_t P, int32_t D) { return shape_ok(P, D) ? kvz::block_bytes(P, D) : 0; }
 size_t kvz_meta_bytes(int32_t P, int32_t D) { return shape_ok(P, D) ? kvz::meta_bytes(P, D) : 0; }
 int32_t kvz_inline_capacity(int32_t P, int32_t D) { return shape_ok(P, D) ? kvz::inline_capacity(P, D) : 0; }
 
@@ -311,9 +313,9 @@ int kvz_decode_attention_dense(const uint16_t* q, const uint16_t* k_pages, const
 int kvz_decompress_pages(const kvz_cache* c, const int32_t* page_ids, int32_t n, int32_t lane_map, uint16_t* k_dst,
                          uint16_t* v_dst, void* stream) {
   if (!cache_ok(c) || n < 0 || (n > 0 && (!page_ids || !k_dst || !v_dst))) return KVZ_ERR_INVALID_ARG;
-  if (lane_map != 0 && lane_map != 1) return KVZ_ERR_INVALID_ARG;
+  if (lane_map < 0 || lane_map > 3) return KVZ_ERR_INVALID_ARG;
   const int D = c->head_dim;
-  if ((D != 64 && D != 128) || (lane_map == 1 && D != 128)) return KVZ_ERR_UNSUPPORTED;
+  if ((D != 64 && D != 128) || ((lane_map & 1) && D != 128)) return KVZ_ERR_UNSUPPORTED;
   if (n == 0) return KVZ_OK;
   if (c->format == KVZ_FORMAT_ZIPFUSION) {
     if (lane_map != 0) return KVZ_ERR_UNSUPPORTED;

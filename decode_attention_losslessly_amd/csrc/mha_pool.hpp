@@ -163,6 +163,86 @@ __device__ __forceinline__ uint32_t win_patch_v(uint32_t (&pairs)[D / 8], const 
   return total;
 }
 
+// K tile of a pool unit in the grouped-query lane layout (D = 128; lane l holds the adjacent
+// storage pieces 2c, 2c + 1, c = 4 (l % 16) + l / 16): ranks in storage order from one scan in
+// chunk order, then every lane patches its four offset words from the staged window. Returns
+// the tile's escape count.
+__device__ __forceinline__ uint32_t win_patch_k_gqa(uint32_t (&pairs)[16], const KRaw<128>& raw, const uint16_t* win,
+                                                    const Window& w, int lane) {
+  uint32_t c0[2], c1[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    c0[i] = popc_flags(escape_flags(raw.nib[2 * i]));
+    c1[i] = popc_flags(escape_flags(raw.nib[2 * i + 1]));
+  }
+  const uint32_t cl = c0[0] + c1[0] + c0[1] + c1[1];
+  const uint32_t c_ord = (uint32_t)__shfl((int)cl, 16 * (lane & 3) + (lane >> 2));   // chunk `lane`'s count
+  const uint32_t inc = wave_incl_scan(c_ord);
+  const uint32_t total = readlane(inc, 63);
+  uint32_t r = (uint32_t)__shfl((int)(inc - c_ord), 4 * (lane & 15) + (lane >> 4));  // this lane's chunk
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    patch_word(raw.nib[2 * i], r, win, w, &pairs[8 * i]);
+    patch_word(raw.nib[2 * i + 1], r + c0[i], win, w, &pairs[8 * i + 4]);
+    r += c0[i] + c1[i];
+  }
+  return total;
+}
+
+// ---------------------------------------------------------------- one tile of any unit
+// The steps of the pool-capable loops (multi-head and grouped-query), shared with the test
+// decode so that the rebuilt values can be checked bit for bit. The tile's payload loads are
+// issued first; for a pool unit, both escape windows (from the block cursors krank / vrank, at
+// most a tile's worth each) are then staged in the same round trip. Returns whether the unit's
+// escapes are in the pool.
+template <int D>
+__device__ __forceinline__ bool any_stage(const UnitHeader& hdr, uint32_t krank, uint32_t vrank, uint16_t* lds,
+                                          const uint16_t* pool, int64_t pool_cap, Window& kw, Window& vw, int lane) {
+  const bool in_pool = hdr.off != kInline;
+  kw.mis = 0;
+  vw.mis = 0;
+  if (in_pool) {
+    const uint32_t kr = uniform(krank), vr = uniform(vrank);
+    const uint32_t kn = hdr.kc > kr ? min((uint32_t)(kTile * D), hdr.kc - kr) : 0u;
+    const uint32_t vn = hdr.vc > vr ? min((uint32_t)(kTile * D), hdr.vc - vr) : 0u;
+    stage_windows<D>(pool, pool_cap, hdr.off + kr, kn, hdr.off + hdr.kc + vr, vn, lds, kw, vw, lane);
+  }
+  return in_pool;
+}
+
+// Rebuilds the tile's K pairs in the given lane layout and patches its escapes: from the staged
+// K window for a pool unit, else from the inline list.
+template <int D, bool GQA>
+__device__ __forceinline__ void any_rebuild_k(uint32_t (&kp)[KRaw<D>::VK / 2], const KRaw<D>& k, uint32_t meta,
+                                              const UnitHeader& hdr, bool in_pool, const Window& kw, int P, int tile,
+                                              uint32_t& krank, uint16_t* lds, const uint16_t* pool, int64_t pool_cap,
+                                              int lane) {
+  decode_k<D>(k, kp);
+  if (hdr.kc) {
+    if (in_pool) {
+      if constexpr (GQA) krank = uniform(krank) + win_patch_k_gqa(kp, k, lds, kw, lane);
+      else krank = uniform(krank) + win_patch_k<D>(kp, k, lds, kw);
+    } else {
+      patch_k_tile<D, GQA, false>(kp, k, meta, hdr, P, tile, krank, lds, pool, pool_cap, lane);
+    }
+  }
+}
+
+// Rebuilds the tile's V pairs (lane l: dims l + 64 s, token pairs) and patches its escapes: from
+// the staged V window for a pool unit, else from the inline list.
+template <int D>
+__device__ __forceinline__ void any_rebuild_v(uint32_t (&vp)[D / 8], const VRaw<D>& v, uint32_t meta,
+                                              const UnitHeader& hdr, bool in_pool, const Window& vw, int P, int tile,
+                                              uint32_t& vrank, uint16_t* lds, const uint16_t* pool, int64_t pool_cap,
+                                              int lane) {
+#pragma unroll
+  for (int g = 0; g < D / 64; ++g) decode_v_seg(v.seg[g], v_bases<D>(meta, g), &vp[8 * g]);
+  if (hdr.vc) {
+    if (in_pool) vrank = uniform(vrank) + win_patch_v<D>(vp, v, lds + win_elems<D>(), vw);
+    else patch_v_tile<D, false>(vp, v, meta, hdr, P, tile, vrank, lds, pool, pool_cap, lane);
+  }
+}
+
 // One tile of any unit: `meta` is its meta window (already loaded); the payload and, for a
 // pool unit, both escape windows are loaded in one round trip. krank / vrank are the block
 // cursors (escapes in the unit's earlier tiles), reset at tile 0.
@@ -178,31 +258,16 @@ __device__ __forceinline__ void mha_any_tile(MhaState<D>& st, const uint8_t* uni
   VRaw<D> v;
   load_k<D, false>(unit, P, tile, lane, k);
   load_v<D>(unit, P, tile, lane, v);
-  const bool in_pool = hdr.off != kInline;
-  Window kw = {0}, vw = {0};
-  if (in_pool) {
-    const uint32_t kr = uniform(krank), vr = uniform(vrank);
-    const uint32_t kn = hdr.kc > kr ? min((uint32_t)(kTile * D), hdr.kc - kr) : 0u;
-    const uint32_t vn = hdr.vc > vr ? min((uint32_t)(kTile * D), hdr.vc - vr) : 0u;
-    stage_windows<D>(pool, pool_cap, hdr.off + kr, kn, hdr.off + hdr.kc + vr, vn, lds, kw, vw, lane);
-  }
+  Window kw, vw;
+  const bool in_pool = any_stage<D>(hdr, krank, vrank, lds, pool, pool_cap, kw, vw, lane);
   uint32_t kp[VK / 2];
-  decode_k<D>(k, kp);
-  if (hdr.kc) {
-    if (in_pool) krank = uniform(krank) + win_patch_k<D>(kp, k, lds, kw);
-    else patch_k_tile<D, false, false>(kp, k, meta, hdr, P, tile, krank, lds, pool, pool_cap, lane);
-  }
+  any_rebuild_k<D, false>(kp, k, meta, hdr, in_pool, kw, P, tile, krank, lds, pool, pool_cap, lane);
   float sc[D / 64];
   mha_scores<D>(st, kp, scale, sc);
   uint32_t phi[8], plo[8];
   mha_softmax<D>(st, sc, phi, plo);
   uint32_t vp[NS * 8];
-#pragma unroll
-  for (int g = 0; g < NS; ++g) decode_v_seg(v.seg[g], v_bases<D>(meta, g), &vp[8 * g]);
-  if (hdr.vc) {
-    if (in_pool) vrank = uniform(vrank) + win_patch_v<D>(vp, v, lds + win_elems<D>(), vw);
-    else patch_v_tile<D, false>(vp, v, meta, hdr, P, tile, vrank, lds, pool, pool_cap, lane);
-  }
+  any_rebuild_v<D>(vp, v, meta, hdr, in_pool, vw, P, tile, vrank, lds, pool, pool_cap, lane);
   mha_accumulate_v<D>(st, vp, phi, plo);
   if (in_pool) wave_lds_sync();   // the windows are read before the next tile's staging writes
 }

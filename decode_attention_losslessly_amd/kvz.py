@@ -19,8 +19,8 @@ KVZ_OK, KVZ_ERR_INVALID_ARG, KVZ_ERR_UNSUPPORTED, KVZ_ERR_WORKSPACE, KVZ_ERR_HIP
 STATUS_ESC_POOL_FULL, STATUS_BAD_PAGE_ID, STATUS_SEQ_TOO_LONG = 1, 2, 4
 FORMAT_ESCAPE, FORMAT_ZIPFUSION = 0, 1
 
-EXPORTS = ("kvz_unit_bytes", "kvz_meta_bytes", "kvz_inline_capacity", "kvz_workspace_bytes", "kvz_num_splits",
-           "kvz_compress_pages", "kvz_append_token", "kvz_decode_attention", "kvz_decode_attention_dense",
+EXPORTS = ("kvz_payload_bytes", "kvz_unit_bytes", "kvz_meta_bytes", "kvz_inline_capacity", "kvz_workspace_bytes",
+           "kvz_num_splits", "kvz_compress_pages", "kvz_append_token", "kvz_decode_attention", "kvz_decode_attention_dense",
            "kvz_decompress_pages", "kvz_strerror", "kvz_decode_attention_splits",
            "kvz_decode_attention_dense_splits", "kvz_merge_splits", "kvz_unit_bytes_for", "kvz_compact_pool")
 
@@ -52,6 +52,7 @@ def lib() -> ctypes.CDLL:
         i32, i64, sz, f32, vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float, ctypes.c_void_p
         cp = ctypes.POINTER(_CacheStruct)
         sig = {
+            "kvz_payload_bytes": (sz, [i32, i32]),
             "kvz_unit_bytes": (sz, [i32, i32]),
             "kvz_unit_bytes_for": (sz, [i32, i32, i32]),
             "kvz_compact_pool": (ctypes.c_int, [cp, vp, i32, vp, i64, vp, vp]),
@@ -95,6 +96,15 @@ def _stream(stream) -> ctypes.c_void_p:
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def _scratch(nbytes: int, device, stream) -> torch.Tensor:
+    """A workspace for one call on `stream`: allocated from the caching allocator on that stream,
+    so that its memory is not handed out again before the call's kernels are done with it."""
+    if stream is None:
+        return torch.empty(max(nbytes, 4), dtype=torch.uint8, device=device)
+    with torch.cuda.stream(stream):
+        return torch.empty(max(nbytes, 4), dtype=torch.uint8, device=device)
+
+
 def _check(rc: int, what: str):
     if rc != KVZ_OK:
         raise KvzError(rc, what)
@@ -103,6 +113,10 @@ def _check(rc: int, what: str):
 # ---------------------------------------------------------------- sizes
 def unit_bytes(P: int, D: int, fmt: int = FORMAT_ESCAPE) -> int:
     return int(lib().kvz_unit_bytes_for(fmt, P, D))
+
+
+def payload_bytes(P: int, D: int) -> int:
+    return int(lib().kvz_payload_bytes(P, D))
 
 
 def meta_bytes(P: int, D: int) -> int:
@@ -197,9 +211,8 @@ def decode_attention(q: torch.Tensor, cache: Cache, page_table: torch.Tensor, se
     """q, out: int16 [B, Hq, D] (BF16 bits); out_f32 optional float32 [B, Hq, D]."""
     B, Hq, D = q.shape
     max_pages = page_table.shape[1]
-    need = workspace_bytes(B, Hq, cache.H, D, cache.P, max_pages, pages_per_split)
     if workspace is None:
-        workspace = torch.empty(max(need, 4), dtype=torch.uint8, device=q.device)
+        workspace = _scratch(workspace_bytes(B, Hq, cache.H, D, cache.P, max_pages, pages_per_split), q.device, stream)
     cs = cache.struct()
     _check(lib().kvz_decode_attention(_ptr(q), ctypes.byref(cs), _ptr(page_table), max_pages, _ptr(seq_lens), B, Hq,
                                       float(sm_scale), pages_per_split, _ptr(out), _ptr(out_f32), _ptr(workspace),
@@ -215,9 +228,8 @@ def decode_attention_dense(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torc
     B, Hq, D = q.shape
     num_pages, H, P, _ = k_pages.shape
     max_pages = page_table.shape[1]
-    need = workspace_bytes(B, Hq, H, D, P, max_pages, pages_per_split)
     if workspace is None:
-        workspace = torch.empty(max(need, 4), dtype=torch.uint8, device=q.device)
+        workspace = _scratch(workspace_bytes(B, Hq, H, D, P, max_pages, pages_per_split), q.device, stream)
     _check(lib().kvz_decode_attention_dense(_ptr(q), _ptr(k_pages), _ptr(v_pages), num_pages, H, D, P,
                                             _ptr(page_table), max_pages, _ptr(seq_lens), B, Hq, float(sm_scale),
                                             pages_per_split, _ptr(out), _ptr(out_f32), _ptr(workspace),
@@ -260,12 +272,17 @@ def merge_splits(workspace: torch.Tensor, seq_lens: torch.Tensor, B: int, Hq: in
 
 def compact_pool(cache: Cache, page_ids: torch.Tensor, new_capacity: int, stream=None) -> None:
     """Moves the pool data of the units page_ids (int32 [n], all heads) into a new pool of
-    new_capacity u16 elements and installs it in `cache` (the old pool is then released)."""
-    new_pool = torch.zeros(max(1, new_capacity), dtype=torch.int16, device=cache.esc_pool.device)
-    new_cursor = torch.zeros(1, dtype=torch.int64, device=cache.esc_pool.device)
+    new_capacity u16 elements and installs it in `cache` (the old pool is then released). The new
+    buffers are allocated and cleared on the call's stream, and the old pool is kept from reuse
+    until the work enqueued there so far is done."""
+    s = torch.cuda.current_stream() if stream is None else stream
+    with torch.cuda.stream(s):
+        new_pool = torch.zeros(max(1, new_capacity), dtype=torch.int16, device=cache.esc_pool.device)
+        new_cursor = torch.zeros(1, dtype=torch.int64, device=cache.esc_pool.device)
     cs = cache.struct()
     _check(lib().kvz_compact_pool(ctypes.byref(cs), _ptr(page_ids), int(page_ids.numel()), _ptr(new_pool),
-                                  new_pool.numel(), _ptr(new_cursor), _stream(stream)), "kvz_compact_pool")
+                                  new_pool.numel(), _ptr(new_cursor), _stream(s)), "kvz_compact_pool")
+    cache.esc_pool.record_stream(s)
     cache.esc_pool, cache.esc_cursor = new_pool, new_cursor
 
 

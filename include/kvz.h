@@ -116,7 +116,14 @@ typedef struct kvz_cache {
   uint32_t* status;      /* [1] sticky KVZ_STATUS_* bits */
 } kvz_cache;
 
-/* Sizes of the format (host functions, no device work). */
+/* Sizes of the format (host functions, no device work; 0 for an unsupported shape). Every value
+ * keeps 12 bits (sign/mantissa byte and offset nibble, §III.B: the retained bits and a small code
+ * per value), so
+ *   kvz_payload_bytes   one block's sm bytes and offset words: 1.5 * P * D
+ *   kvz_meta_bytes      the unit's meta region (bases, header, inline escapes)
+ *   kvz_unit_bytes      kvz_meta_bytes + 2 * kvz_payload_bytes (meta, then the K and V blocks)
+ *   kvz_inline_capacity escapes a unit's meta region holds inline */
+size_t kvz_payload_bytes(int32_t P, int32_t D);
 size_t kvz_unit_bytes(int32_t P, int32_t D);
 /* unit size in the given format (0 for an unsupported shape or format) */
 size_t kvz_unit_bytes_for(int32_t format, int32_t P, int32_t D);
@@ -238,12 +245,20 @@ int kvz_merge_splits(const void* workspace, size_t workspace_bytes, const int32_
                      uint16_t* out, float* out_f32, void* stream);
 
 /* Test entry point: runs the attention kernels' own in-register decode on n units and writes
- * the rebuilt values, so that decode can be compared bit for bit.
+ * the rebuilt values, so that decode can be compared bit for bit (§II.A, §III.B: every BF16 bit
+ * pattern comes back; §III.C: values rebuilt with bit operations inside the kernel).
  *   page_ids      [n]
- *   lane_map      0: the lane layout of the multi-head kernel, 1: that of the grouped-query
- *                 kernel (D = 128 only) for K
+ *   lane_map      which of the kernels' decode routes runs:
+ *                 0  multi-head lane layout; escapes as the main loops and the per-unit path
+ *                    after them patch them (inline list, or a pool list staged whole)
+ *                 1  the same route with the grouped-query kernel's K layout (D = 128 only)
+ *                 2  multi-head lane layout through the pool-capable loop's route (a pool
+ *                    unit's escape windows staged with the payload, every offset word patched
+ *                    from them)
+ *                 3  the route of 2 with the grouped-query kernel's K layout (D = 128 only)
  *   k_dst, v_dst  [n][H][P][D] raw BF16, token-major
- * Supported: D in {64, 128}. */
+ * Supported: D in {64, 128}; lane_map 0 only for KVZ_FORMAT_ZIPFUSION. Errors:
+ * KVZ_ERR_INVALID_ARG (lane_map outside 0..3), KVZ_ERR_UNSUPPORTED. Device status: BAD_PAGE_ID. */
 int kvz_decompress_pages(const kvz_cache* cache, const int32_t* page_ids, int32_t n,
                          int32_t lane_map, uint16_t* k_dst, uint16_t* v_dst, void* stream);
 

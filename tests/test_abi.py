@@ -30,8 +30,24 @@ def test_library_exports_every_declared_symbol():
     assert set(binding.EXPORTS) == set(names)
 
 
+# the calls the hot path's boundary is built from: sizes, compress, append, attention over the
+# compressed cache and over the uncompressed baseline, the test decode, error strings
+BOUNDARY = ("kvz_payload_bytes", "kvz_meta_bytes", "kvz_workspace_bytes", "kvz_compress_pages", "kvz_append_token",
+            "kvz_decode_attention", "kvz_decode_attention_dense", "kvz_decompress_pages", "kvz_strerror")
+
+
+def test_boundary_calls_are_declared_and_exported():
+    names = set(_declared())
+    L = ctypes.CDLL(binding.LIB_PATH)
+    for n in BOUNDARY:
+        assert n in names, n
+        assert hasattr(L, n), n
+
+
 @pytest.mark.parametrize("P,D", [(16, 64), (16, 128), (32, 128), (256, 64), (16, 256)])
 def test_sizes_agree_with_format(P, D):
+    assert kvz.payload_bytes(P, D) == 3 * P * D // 2          # 12 bits per value
+    assert kvz.unit_bytes(P, D) == kvz.meta_bytes(P, D) + 2 * kvz.payload_bytes(P, D)
     assert kvz.unit_bytes(P, D) == codec.unit_bytes(P, D)
     assert kvz.meta_bytes(P, D) == codec.meta_bytes(P, D)
     assert kvz.inline_capacity(P, D) == codec.inline_capacity(P, D)
@@ -40,6 +56,7 @@ def test_sizes_agree_with_format(P, D):
 def test_unsupported_shapes_have_zero_size():
     assert kvz.unit_bytes(15, 128) == 0
     assert kvz.unit_bytes(16, 96) == 0
+    assert kvz.payload_bytes(16, 96) == 0 and kvz.payload_bytes(8, 128) == 0
 
 
 def test_split_geometry():

@@ -299,3 +299,61 @@ def test_two_phase_calls_equal_the_one_call():
     kvz.merge_splits(ws, lens, w.B, w.Hq, w.Hkv, w.D, w.P, w.max_pages, out, out32)
     torch.cuda.synchronize()
     assert np.array_equal(host16(out), o16) and np.array_equal(out32.cpu().numpy(), o32)
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(4, 4), (8, 2)])
+def test_sequence_longer_than_the_page_table(Hq, Hkv):
+    """A length beyond max_pages_per_seq * P sets KVZ_STATUS_SEQ_TOO_LONG and is clamped to the
+    pages the table holds: the result is attention over those tokens. Compressed and dense."""
+    w = make_workload(2, B=2, lens=[100, 60], Hq=Hq, Hkv=Hkv, n_append=0)
+    kp, vp = w.pages(0), w.pages(1)
+    cache, _ = build_cache(w, kp, vp)
+    table = np.ascontiguousarray(w.page_table[:, :5])          # 5 pages = 80 tokens per request
+    lens = dev(w.seq_lens)
+    q = w.q()
+    out = torch.zeros((w.B, w.Hq, w.D), dtype=torch.int16, device=DEV)
+    out32 = torch.zeros((w.B, w.Hq, w.D), dtype=torch.float32, device=DEV)
+    kvz.decode_attention(dev(q), cache, dev(table), lens, w.sm_scale, out, out32)
+    torch.cuda.synchronize()
+    assert int(cache.status.item()) == kvz.kvz.STATUS_SEQ_TOO_LONG
+    assert np.array_equal(lens.cpu().numpy(), w.seq_lens)        # the lengths are not written
+    rows = _all_rows(w)
+    from oracle import c_oracle
+    ref = c_oracle.dense_attention_rows(q, kp, vp, table, np.array([80, 60], np.int32), w.sm_scale, rows)
+    check_rows(host16(out).reshape(-1, w.D), out32.cpu().numpy().reshape(-1, w.D), ref, "clamped")
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    kvz.decode_attention_dense(dev(q), dev(kp), dev(vp), dev(table), lens, w.sm_scale, out, out32, status=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == kvz.kvz.STATUS_SEQ_TOO_LONG
+    check_rows(host16(out).reshape(-1, w.D), out32.cpu().numpy().reshape(-1, w.D), ref, "dense clamped")
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(4, 4), (8, 2)])
+@pytest.mark.parametrize("pps", [0, 1])
+def test_cache_without_unit_slots(Hq, Hkv, pps):
+    """num_pages = 0: every full page is a bad id (KVZ_STATUS_BAD_PAGE_ID) and is skipped; each
+    split the merge counts still leaves an empty partial, so the result is attention over the
+    tail rows alone (one split per page with pages_per_split 1)."""
+    P, D = 16, 128
+    w = make_workload(2, B=2, lens=[3 * P + 5, 7], Hq=Hq, Hkv=Hkv, n_append=0)
+    kp, vp = w.pages(0), w.pages(1)
+    cache = kvz.Cache.allocate(P, Hkv, D, 1, w.B, esc_capacity=16, device=DEV)
+    cache.num_pages = 0
+    rows_k = np.zeros((w.B, Hkv, P, D), np.uint16)
+    rows_v = np.zeros_like(rows_k)
+    for r, L in enumerate(w.seq_lens):
+        pid = w.page_table[r, L // P]
+        rows_k[r], rows_v[r] = kp[pid], vp[pid]
+    cache.k_tail.copy_(dev(rows_k))
+    cache.v_tail.copy_(dev(rows_v))
+    q = w.q()
+    out = torch.zeros((w.B, w.Hq, w.D), dtype=torch.int16, device=DEV)
+    out32 = torch.full((w.B, w.Hq, w.D), float("nan"), dtype=torch.float32, device=DEV)
+    kvz.decode_attention(dev(q), cache, dev(w.page_table), dev(w.seq_lens), w.sm_scale, out, out32,
+                         pages_per_split=pps)
+    torch.cuda.synchronize()
+    assert int(cache.status.item()) == kvz.kvz.STATUS_BAD_PAGE_ID
+    from oracle import c_oracle
+    tail_table = np.arange(w.B, dtype=np.int32).reshape(w.B, 1)
+    ref = c_oracle.dense_attention_rows(q, rows_k, rows_v, tail_table, w.seq_lens % P, w.sm_scale, _all_rows(w))
+    check_rows(host16(out).reshape(-1, w.D), out32.cpu().numpy().reshape(-1, w.D), ref, f"tail only, pps {pps}")

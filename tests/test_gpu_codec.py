@@ -1,5 +1,10 @@
 """GPU codec parity: kvz_compress_pages is byte-exact against the CPU oracle and the attention
-kernels' in-register decode (kvz_decompress_pages) gives back every input bit pattern."""
+kernels' in-register decode (kvz_decompress_pages) gives back every input bit pattern, through
+every decode route the attention kernels take:
+  lane maps 0 / 1   multi-head / grouped-query lane layout, escapes patched as the main loops and
+                    the per-unit path after them do (inline list walk; pool list staged whole);
+  lane maps 2 / 3   the same layouts through the pool-capable loops' route (a pool unit's escape
+                    windows staged with its payload, every offset word patched from them)."""
 import numpy as np
 import pytest
 import torch
@@ -45,18 +50,33 @@ def test_compress_matches_oracle(cfg):
 
 
 def _pattern_pages(P, D, n, seed):
-    """All 65,536 patterns spread over n pages x 2 tensors x H=2, plus permutations."""
+    """n pages x (K, V) x H=2 heads of P x D values, page by page: all 65,536 patterns in order,
+    twice (consecutive patterns share their exponent, so these units have no escapes and stay
+    inline), then seeded permutations of them (escapes everywhere: pool units)."""
     rng = np.random.default_rng(seed)
     allp = np.arange(65536, dtype=np.uint32).astype(np.uint16)
     need = n * 2 * 2 * P * D
-    vals = np.concatenate([allp] + [rng.permutation(allp) for _ in range(need // 65536 + 1)])[:need]
-    x = vals.reshape(2, n, 2, P, D)
-    return x[0], x[1]
+    vals = np.concatenate([allp, allp] + [rng.permutation(allp) for _ in range(need // 65536)])[:need]
+    x = vals.reshape(n, 2, 2, P, D)
+    return np.ascontiguousarray(x[:, 0]), np.ascontiguousarray(x[:, 1])
 
 
-@pytest.mark.parametrize("P,D", [(16, 128), (16, 64), (256, 64)])
+def lane_maps(D):
+    return [0, 1, 2, 3] if D == 128 else [0, 2]
+
+
+def decode_units(cache, ids, H, P, D, lane_map):
+    """The kernels' rebuilt K and V of units `ids` (uint16 [n, H, P, D] each)."""
+    kd = torch.zeros((len(ids), H, P, D), dtype=torch.int16, device=DEV)
+    vd = torch.zeros_like(kd)
+    kvz.decompress_pages(cache, dev(np.asarray(ids, np.int32)), kd, vd, lane_map=lane_map)
+    torch.cuda.synchronize()
+    return host16(kd), host16(vd)
+
+
+@pytest.mark.parametrize("P,D", [(16, 128), (32, 128), (16, 64), (256, 64)])
 def test_compress_all_bit_patterns(P, D):
-    n = max(2, 65536 // (2 * 2 * P * D) * 2)
+    n = max(4, 65536 // (P * D))
     kp, vp = _pattern_pages(P, D, n, P + D)
     ids = np.arange(n, dtype=np.int32)[::-1].copy()
     cache = kvz.Cache.allocate(P, 2, D, n, 1, esc_capacity=4 * n * 2 * P * D, device=DEV)
@@ -69,14 +89,13 @@ def test_compress_all_bit_patterns(P, D):
     for i, pid in enumerate(ids):
         for h in range(2):
             assert unit_equal(units[pid, h], pool, ref_units[i, h], ref_pool, P, D), (pid, h)
-    # the in-kernel decode gives every pattern back
-    for lane_map in ([0, 1] if D == 128 else [0]):
-        kd = torch.zeros((n, 2, P, D), dtype=torch.int16, device=DEV)
-        vd = torch.zeros_like(kd)
-        kvz.decompress_pages(cache, dev(ids), kd, vd, lane_map=lane_map)
-        torch.cuda.synchronize()
-        assert np.array_equal(host16(kd), kp[ids]), lane_map
-        assert np.array_equal(host16(vd), vp[ids]), lane_map
+    heads = [codec.unit_header(units[pid, h], P, D) for pid in ids for h in range(2)]
+    assert any(off == codec.INLINE for _, _, off in heads) and any(off != codec.INLINE for _, _, off in heads)
+    # the in-kernel decode gives every pattern back, on every route
+    for lane_map in lane_maps(D):
+        kd, vd = decode_units(cache, ids, 2, P, D, lane_map)
+        assert np.array_equal(kd, kp[ids]), lane_map
+        assert np.array_equal(vd, vp[ids]), lane_map
 
 
 @pytest.mark.parametrize("cfg", sorted(SMALL))
@@ -85,13 +104,37 @@ def test_in_kernel_decode_is_bit_exact(cfg):
     kp, vp = w.pages(0), w.pages(1)
     cache, _ = build_cache(w, kp, vp)
     ids = full_page_ids(w, w.seq_lens - w.n_append)
-    for lane_map in ([0, 1] if w.D == 128 else [0]):
-        kd = torch.zeros((len(ids), w.Hkv, w.P, w.D), dtype=torch.int16, device=DEV)
-        vd = torch.zeros_like(kd)
-        kvz.decompress_pages(cache, dev(ids), kd, vd, lane_map=lane_map)
-        torch.cuda.synchronize()
-        assert np.array_equal(host16(kd), kp[ids])
-        assert np.array_equal(host16(vd), vp[ids])
+    for lane_map in lane_maps(w.D):
+        kd, vd = decode_units(cache, ids, w.Hkv, w.P, w.D, lane_map)
+        assert np.array_equal(kd, kp[ids]), lane_map
+        assert np.array_equal(vd, vp[ids]), lane_map
+
+
+@pytest.mark.parametrize("P,D", [(16, 128), (32, 128), (16, 64)])
+def test_decode_from_a_pool_filled_to_capacity(P, D):
+    """Escape-heavy units (every one keeps its escapes in the pool) in a pool sized to exactly
+    what they need, ending inside a 16-byte chunk: the windows of the last units reach the pool's
+    end and are read element by element up to it. Every route gives every value back."""
+    for L in range(12 * P, 20 * P, P):
+        w = make_workload(5, n_append=0, B=2, L=L, Hq=2, Hkv=2, D=D, P=P)
+        kp, vp = w.pages(0), w.pages(1)
+        probe, _ = build_cache(w, kp, vp)
+        need = int(probe.esc_cursor.item())
+        del probe
+        if need % 8:
+            break
+    assert need % 8, need
+    cache, _ = build_cache(w, kp, vp, esc_capacity=need)
+    assert int(cache.status.item()) == 0 and int(cache.esc_cursor.item()) == need
+    ids = full_page_ids(w)
+    units = cache.units.cpu().numpy()
+    heads = [codec.unit_header(units[pid, h], P, D) for pid in ids for h in range(w.Hkv)]
+    assert all(off != codec.INLINE for _, _, off in heads)
+    assert max(off + kc + vc for kc, vc, off in heads) == need     # some unit's list ends at the pool's end
+    for lane_map in lane_maps(D):
+        kd, vd = decode_units(cache, ids, w.Hkv, P, D, lane_map)
+        assert np.array_equal(kd, kp[ids]), lane_map
+        assert np.array_equal(vd, vp[ids]), lane_map
 
 
 def test_escape_pool_overflow_sets_status_and_stays_in_bounds():
@@ -122,15 +165,15 @@ def test_bad_page_id_sets_status():
     assert int(cache.status.item()) & kvz.kvz.STATUS_BAD_PAGE_ID
 
 
-@pytest.mark.parametrize("cfg", [3, 5])
+@pytest.mark.parametrize("cfg", [2, 3, 4, 5, 6])
 def test_compress_full_size_sampled(cfg, full_workloads):
+    """Full shapes: sampled units byte-exact against the oracle and rebuilt bit for bit by every
+    decode route of the kernel that serves the workload (multi-head or grouped-query)."""
     w, kp, vp, cache, _ = full_workloads(cfg)
     ids = full_page_ids(w, w.seq_lens - w.n_append)
     rng = np.random.default_rng(cfg)
     sample = ids[rng.choice(len(ids), size=min(96, len(ids)), replace=False)]
     _compare_units(w, cache, kp, vp, sample)
-    kd = torch.zeros((len(sample), w.Hkv, w.P, w.D), dtype=torch.int16, device=DEV)
-    vd = torch.zeros_like(kd)
-    kvz.decompress_pages(cache, dev(sample), kd, vd, lane_map=0)
-    torch.cuda.synchronize()
-    assert np.array_equal(host16(kd), kp[sample]) and np.array_equal(host16(vd), vp[sample])
+    for lane_map in ([1, 3] if w.Hq > w.Hkv else [0, 2]):
+        kd, vd = decode_units(cache, sample, w.Hkv, w.P, w.D, lane_map)
+        assert np.array_equal(kd, kp[sample]) and np.array_equal(vd, vp[sample]), lane_map

@@ -3,8 +3,9 @@ units point at it; attention of the live requests is bit-identical before and af
 pool overwritten so that any read of it would show. Both cache formats (escape lists; ZipFusion
 raw blocks), on escape-heavy data. An undersized new pool drops the data of the units that do not
 fit (status bit set) and nothing reads past a pool. A pool filled exactly to its capacity, ending
-inside a 16-byte chunk, and escape-heavy units under grouped-query attention still give attention
-within tolerance of the fp64 oracle."""
+inside a 16-byte chunk, escape-heavy units under grouped-query attention, and splits that start on
+inline units and go on into pool units (both pool routes in one wave) still give attention within
+tolerance of the fp64 oracle."""
 import numpy as np
 import pytest
 import torch
@@ -87,8 +88,9 @@ def test_undersized_pool_drops_and_stays_in_bounds(fmt):
 def test_pool_filled_to_capacity_matches_oracle(D, P, pps):
     """The pool holds exactly what the cache needs and ends inside a 16-byte chunk, so the escape
     windows of the last units reach its end and are read element by element up to the capacity.
-    pages_per_split 64 gives each row one split, whose wave walks most pages in the pool-capable
-    loop; 0 lets the device choose (shorter splits, more units through the per-unit path)."""
+    pages_per_split 64 gives each row one split; 0 lets the device choose (shorter splits). Every
+    split starts with an escape-heavy unit, so either way its wave walks it in the pool-capable
+    loop from the first step."""
     w = make_workload(5, n_append=0, B=2, L=12 * P, Hq=4, Hkv=4, D=D, P=P)
     kp, vp = w.pages(0), w.pages(1)
     probe, _ = build_cache(w, kp, vp)
@@ -128,3 +130,49 @@ def test_grouped_query_pool_loop_matches_oracle(P, pps):
     rows = [(r, h) for r in range(w.B) for h in range(w.Hq)]
     ref = oracle_rows(w, kp, vp, q, rows)
     check_rows(host16(out).reshape(-1, w.D), out32.cpu().numpy().reshape(-1, w.D), ref, f"P={P} pps={pps}")
+
+
+def _mixed_pages(w, light_pages):
+    """K and V pages of escape-stress workload w, except that the logical pages light_pages[r]
+    of request r hold light data (per-channel log-normal values, whose few escapes stay in the
+    unit's inline list)."""
+    kp, vp = w.pages(0), w.pages(1)
+    light = make_workload(3, n_append=0, B=w.B, lens=w.seq_lens, Hq=w.Hq, Hkv=w.Hkv, D=w.D, P=w.P)
+    for r in range(w.B):
+        for i in light_pages[r]:
+            pid = int(w.page_table[r, i])
+            kp[pid], vp[pid] = light.page(pid, 0), light.page(pid, 1)
+    return kp, vp
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(4, 4), (8, 2)])
+@pytest.mark.parametrize("P", [16, 32])
+@pytest.mark.parametrize("pps", [0, 64])
+def test_splits_from_inline_into_pool_units(Hq, Hkv, P, pps):
+    """Requests whose first pages are light (inline escapes) and whose later pages are escape-heavy
+    (pool lists): the main loop computes the light pages and skips the first heavy ones until most
+    tiles seen went to the pool; the wave then walks the rest of its split in the pool-capable loop
+    (which also meets light pages here: request 1 has some between heavy ones) and, after it, adds
+    the skipped heavy pages through the per-unit path. Multi-head and grouped-query kernels; one
+    split per row (64) or the device's choice (0)."""
+    lens = np.array([24 * P + 5, 20 * P, 30 * P + 11])
+    w = make_workload(5, n_append=0, B=3, lens=lens, Hq=Hq, Hkv=Hkv, D=128, P=P)
+    light = [range(0, 3), list(range(0, 4)) + [9, 10, 15], range(0, 8)]
+    kp, vp = _mixed_pages(w, light)
+    cache, lt = build_cache(w, kp, vp)
+    units = cache.units.cpu().numpy()
+    hdr = 2 * P * 2
+    inline = [[bool((units[w.page_table[r, i], :, hdr + 8:hdr + 16].view(np.uint64) == (1 << 64) - 1).all())
+               for i in range(int(lens[r]) // P)] for r in range(w.B)]
+    for r in range(w.B):
+        assert [i for i, x in enumerate(inline[r]) if x] == list(light[r]), r
+    q = w.q()
+    out = torch.zeros((w.B, w.Hq, w.D), dtype=torch.int16, device=DEV)
+    out32 = torch.full((w.B, w.Hq, w.D), float("nan"), dtype=torch.float32, device=DEV)
+    kvz.decode_attention(dev(q), cache, dev(w.page_table), lt, w.sm_scale, out, out32, pages_per_split=pps)
+    torch.cuda.synchronize()
+    assert int(cache.status.item()) == 0
+    rows = [(r, h) for r in range(w.B) for h in range(w.Hq)]
+    ref = oracle_rows(w, kp, vp, q, rows)
+    check_rows(host16(out).reshape(-1, w.D), out32.cpu().numpy().reshape(-1, w.D), ref,
+               f"Hq={Hq} Hkv={Hkv} P={P} pps={pps}")
