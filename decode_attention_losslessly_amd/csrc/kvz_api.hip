@@ -2,6 +2,9 @@
 // allocates device memory and never synchronises; every call enqueues on the caller's stream.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "kvz.h"
 #include "attn_common.hpp"
 #include "zf.hpp"
@@ -122,6 +125,35 @@ hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
 }  // namespace
 
+// ---------------------------------------------------------------- allocation-free attention
+// The split partials of kvz_decode_attention_noalloc: a file-scope device array, one copy on every
+// GPU the library runs on, held until the process ends. In host code its name is only a stand-in
+// for the symbol, not a device address: each GPU's copy has its own address, which
+// hipGetSymbolAddress gives once per device (with that device current) and which is kept here.
+static __device__ __align__(256) uint8_t scratch[KVZ_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// The current device's copy of `scratch`; nullptr when the runtime cannot give its address.
+void* scratch_on_current_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  p = g_scratch[dev].load(std::memory_order_relaxed);
+  if (!p) {
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    g_scratch[dev].store(p, std::memory_order_release);
+  }
+  return p;
+}
+
+}  // namespace
 
 extern "C" {
 
@@ -294,6 +326,22 @@ int kvz_decode_attention(const uint16_t* q, const kvz_cache* c, const int32_t* p
                           max_pages, pps, 0, out, out_f32, stream);
 }
 
+int kvz_decode_attention_noalloc(const uint16_t* q, const kvz_cache* c, const int32_t* page_table,
+                                 int32_t max_pages, const int32_t* seq_lens, int32_t B, int32_t H_q, float sm_scale,
+                                 int32_t pps, uint16_t* out, float* out_f32, void* stream) {
+  if (!cache_ok(c)) return KVZ_ERR_INVALID_ARG;
+  const int rc = check_attention_shape(B, H_q, c->num_kv_heads, c->head_dim, c->page_size, max_pages);
+  if (rc) return rc;
+  if (pps < -kMaxForcedRanks) return KVZ_ERR_INVALID_ARG;
+  const size_t need = kvz_workspace_bytes(B, H_q, c->num_kv_heads, c->head_dim, c->page_size, max_pages, pps);
+  if (need > KVZ_NOALLOC_SCRATCH_BYTES) return KVZ_ERR_SCRATCH;
+  if (B == 0) return KVZ_OK;
+  void* ws = scratch_on_current_device();
+  if (!ws) return KVZ_ERR_HIP;
+  return kvz_decode_attention(q, c, page_table, max_pages, seq_lens, B, H_q, sm_scale, pps, out, out_f32, ws,
+                              KVZ_NOALLOC_SCRATCH_BYTES, stream);
+}
+
 int kvz_decode_attention_dense(const uint16_t* q, const uint16_t* k_pages, const uint16_t* v_pages, int32_t num_pages,
                                int32_t H, int32_t D, int32_t P, const int32_t* page_table, int32_t max_pages,
                                const int32_t* seq_lens, int32_t B, int32_t H_q, float sm_scale, int32_t pps,
@@ -347,6 +395,7 @@ const char* kvz_strerror(int code) {
     case KVZ_ERR_UNSUPPORTED: return "unsupported shape";
     case KVZ_ERR_WORKSPACE: return "workspace too small";
     case KVZ_ERR_HIP: return "HIP runtime error";
+    case KVZ_ERR_SCRATCH: return "call needs more scratch than the library's own array holds";
     default: return "unknown error";
   }
 }

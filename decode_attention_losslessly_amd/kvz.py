@@ -15,14 +15,16 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libkvz.so")
 
-KVZ_OK, KVZ_ERR_INVALID_ARG, KVZ_ERR_UNSUPPORTED, KVZ_ERR_WORKSPACE, KVZ_ERR_HIP = 0, -1, -2, -3, -4
+KVZ_OK, KVZ_ERR_INVALID_ARG, KVZ_ERR_UNSUPPORTED, KVZ_ERR_WORKSPACE, KVZ_ERR_HIP, KVZ_ERR_SCRATCH = 0, -1, -2, -3, -4, -5
+NOALLOC_SCRATCH_BYTES = 32 << 20   # KVZ_NOALLOC_SCRATCH_BYTES
 STATUS_ESC_POOL_FULL, STATUS_BAD_PAGE_ID, STATUS_SEQ_TOO_LONG = 1, 2, 4
 FORMAT_ESCAPE, FORMAT_ZIPFUSION = 0, 1
 
 EXPORTS = ("kvz_payload_bytes", "kvz_unit_bytes", "kvz_meta_bytes", "kvz_inline_capacity", "kvz_workspace_bytes",
            "kvz_num_splits", "kvz_compress_pages", "kvz_append_token", "kvz_decode_attention", "kvz_decode_attention_dense",
            "kvz_decompress_pages", "kvz_strerror", "kvz_decode_attention_splits",
-           "kvz_decode_attention_dense_splits", "kvz_merge_splits", "kvz_unit_bytes_for", "kvz_compact_pool")
+           "kvz_decode_attention_dense_splits", "kvz_merge_splits", "kvz_unit_bytes_for", "kvz_compact_pool",
+           "kvz_decode_attention_noalloc")
 
 
 class KvzError(RuntimeError):
@@ -63,6 +65,7 @@ def lib() -> ctypes.CDLL:
             "kvz_compress_pages": (ctypes.c_int, [cp, vp, vp, vp, i32, vp]),
             "kvz_append_token": (ctypes.c_int, [cp, vp, vp, vp, i32, vp, i32, vp]),
             "kvz_decode_attention": (ctypes.c_int, [vp, cp, vp, i32, vp, i32, i32, f32, i32, vp, vp, vp, sz, vp]),
+            "kvz_decode_attention_noalloc": (ctypes.c_int, [vp, cp, vp, i32, vp, i32, i32, f32, i32, vp, vp, vp]),
             "kvz_decode_attention_dense": (ctypes.c_int, [vp, vp, vp, i32, i32, i32, i32, vp, i32, vp, i32, i32,
                                                           f32, i32, vp, vp, vp, sz, vp, vp]),
             "kvz_decompress_pages": (ctypes.c_int, [cp, vp, i32, i32, vp, vp, vp]),
@@ -218,6 +221,18 @@ def decode_attention(q: torch.Tensor, cache: Cache, page_table: torch.Tensor, se
                                       float(sm_scale), pages_per_split, _ptr(out), _ptr(out_f32), _ptr(workspace),
                                       workspace.numel() * workspace.element_size(), _stream(stream)),
            "kvz_decode_attention")
+
+
+def decode_attention_noalloc(q: torch.Tensor, cache: Cache, page_table: torch.Tensor, seq_lens: torch.Tensor,
+                             sm_scale: float, out: torch.Tensor, out_f32: torch.Tensor | None = None,
+                             pages_per_split: int = 0, stream=None) -> None:
+    """decode_attention with its workspace in the library's own per-GPU scratch array: nothing is
+    allocated, here or in the library (for callers that cannot allocate device memory)."""
+    B, Hq, D = q.shape
+    cs = cache.struct()
+    _check(lib().kvz_decode_attention_noalloc(_ptr(q), ctypes.byref(cs), _ptr(page_table), page_table.shape[1],
+                                              _ptr(seq_lens), B, Hq, float(sm_scale), pages_per_split, _ptr(out),
+                                              _ptr(out_f32), _stream(stream)), "kvz_decode_attention_noalloc")
 
 
 def decode_attention_dense(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Tensor, page_table: torch.Tensor,

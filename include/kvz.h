@@ -84,7 +84,9 @@ enum {
   KVZ_ERR_INVALID_ARG = -1, /* null pointer, negative size, bad stride */
   KVZ_ERR_UNSUPPORTED = -2, /* shape outside what the kernels handle (see each call) */
   KVZ_ERR_WORKSPACE = -3,   /* workspace smaller than kvz_workspace_bytes(...) */
-  KVZ_ERR_HIP = -4          /* a HIP runtime call failed */
+  KVZ_ERR_HIP = -4,         /* a HIP runtime call failed */
+  KVZ_ERR_SCRATCH = -5      /* kvz_decode_attention_noalloc: the call needs more than
+                               KVZ_NOALLOC_SCRATCH_BYTES of scratch */
 };
 
 enum {
@@ -203,6 +205,27 @@ int kvz_decode_attention(const uint16_t* q, const kvz_cache* cache, const int32_
                          int32_t max_pages_per_seq, const int32_t* seq_lens, int32_t B,
                          int32_t H_q, float sm_scale, int32_t pages_per_split, uint16_t* out,
                          float* out_f32, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of the scratch array the library holds on each GPU for kvz_decode_attention_noalloc. */
+#define KVZ_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+/* kvz_decode_attention without the workspace argument, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that forbid allocation.
+ * The workspace this call needs (kvz_workspace_bytes of its arguments: the split partials and the
+ * slot where the split kernel records its split size) is a scratch array of
+ * KVZ_NOALLOC_SCRATCH_BYTES in device memory that the library holds on every GPU it runs on until
+ * the process ends. The call allocates nothing and calls no allocating routine; the caller still
+ * passes every input and output. All calls on one GPU share that GPU's array, which keeps the last
+ * call's contents (a call needs none of them: it writes every partial it reads). Calls that
+ * overlap on one GPU (on different streams or from different host threads) race on the array and
+ * give unspecified results; calls on one stream are ordered and safe.
+ * Arguments, results, errors and status as kvz_decode_attention, and KVZ_ERR_SCRATCH (nothing
+ * enqueued) when kvz_workspace_bytes(B, H_q, H, D, P, max_pages_per_seq, pages_per_split) exceeds
+ * KVZ_NOALLOC_SCRATCH_BYTES; KVZ_ERR_HIP when the runtime cannot give the array's address. */
+int kvz_decode_attention_noalloc(const uint16_t* q, const kvz_cache* cache, const int32_t* page_table,
+                                 int32_t max_pages_per_seq, const int32_t* seq_lens, int32_t B, int32_t H_q,
+                                 float sm_scale, int32_t pages_per_split, uint16_t* out, float* out_f32,
+                                 void* stream);
 
 /* The same attention over an uncompressed paged cache: the baseline the compressed path is
  * measured against (the pages compare with production FlashInfer, §IV.B).
