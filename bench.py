@@ -11,6 +11,14 @@ attention (ZipFusion summary, §IV.B: attention, fused reconstruction and split 
 the initial compression and the append are set-up (excluded there too, §IV.A) and are reported
 as separate fields.
 
+Order: set-up; whole steps for --settle-seconds of wall time while the clocks ramp up (set-up);
+--warmup untimed steps; exactly --steps timed steps (the headline `value` and `ms_per_step`);
+the split kernel's mean launch duration over --steps launches back to back (`roofline`); the
+same for the uncompressed baseline; --rounds rounds of alternated compressed and dense loops
+(`interleaved`); cache-flushed launches; the streaming-read ceiling (`read_ceiling`); the CPU
+oracle on this host (`cpu_baseline`), whose fp64 outputs check the timed call (`parity`: a
+failure exits with status 1); appends.
+
 Prints one JSON line. `python bench.py --gpus N` with N > 1 exits with a message: the library
 runs on one GPU.
 """
@@ -63,6 +71,11 @@ def parse():
     ap.add_argument("--no-dense", action="store_true", help="skip the uncompressed baseline")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-requests", type=int, default=32, help="requests in the CPU baseline sample")
+    ap.add_argument("--settle-seconds", type=float, default=0.3,
+                    help="wall seconds of whole steps run before the warm-up, while the clocks ramp up (set-up)")
+    ap.add_argument("--rounds", type=int, default=3,
+                    help="rounds of alternated compressed / dense whole-step loops of --steps steps each")
+    ap.add_argument("--no-ceiling", action="store_true", help="skip the streaming-read ceiling kernel")
     ap.add_argument("--cold-steps", type=int, default=20,
                     help="extra launches timed after a 1 GiB cache flush each (reported as attn_us.cold_median)")
     ap.add_argument("--graph-layers", type=int, default=0, metavar="N",
@@ -190,14 +203,13 @@ def main() -> int:
     ws = torch.empty(kvz.workspace_bytes(B, Hq, H, D, P, w.max_pages, pps), dtype=torch.uint8, device=dev)
     out = torch.empty((B, Hq, D), dtype=torch.int16, device=dev)
 
-    def run_loop(split_fn, merge_fn, steps):
-        """Three timed loops on the launch stream: (1) `steps` whole steps (split kernel then
-        merge) back to back, bracketed by one event pair and the wall clock; (2) `steps` split
-        launches back to back, bracketed by one event pair: the mean launch duration of the
-        split kernel; (3) one event pair around each split and each merge launch, for their
-        spread (each pair adds a few microseconds of its own, which (2) does not carry)."""
-        def pair():
-            return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    def pair():
+        return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def timed_steps(split_fn, merge_fn, steps):
+        """`steps` whole steps (split kernel then merge) launched back to back, bracketed by a
+        device synchronisation on both sides: wall seconds, and GPU microseconds per step from
+        one event pair on the launch stream."""
         g0, g1 = pair()
         torch.cuda.synchronize()
         s0 = time.perf_counter()
@@ -207,8 +219,12 @@ def main() -> int:
             merge_fn()
         g1.record()
         torch.cuda.synchronize()
-        wall = time.perf_counter() - s0
-        step_gpu_us = g0.elapsed_time(g1) * 1e3 / steps
+        return time.perf_counter() - s0, g0.elapsed_time(g1) * 1e3 / steps
+
+    def launch_stats(split_fn, merge_fn, steps):
+        """(1) `steps` split launches back to back under one event pair: the split kernel's mean
+        launch duration; (2) an event pair around each split and each merge launch, for their
+        spread (each pair adds a few microseconds of its own, which (1) does not carry)."""
         a0, a1 = pair()
         a0.record()
         for _ in range(steps):
@@ -227,29 +243,83 @@ def main() -> int:
         torch.cuda.synchronize()
         attn = np.array([a.elapsed_time(b) for a, b, _ in ev]) * 1e3
         merge = np.array([b.elapsed_time(c) for _, b, c in ev]) * 1e3
-        return wall, attn, merge, split_mean_us, step_gpu_us
+        return split_mean_us, attn, merge
+
+    def settle(split_fn, merge_fn, seconds):
+        """Keeps the device busy with whole steps for `seconds` of wall time: the clocks ramp up
+        over the first tens of milliseconds of work after an idle set-up, and steps timed before
+        they settle run up to 20% slower. Part of the set-up, like the compression; returns the
+        steps it ran."""
+        n, s0 = 0, time.perf_counter()
+        while time.perf_counter() - s0 < seconds:
+            for _ in range(10):
+                split_fn()
+                merge_fn()
+            torch.cuda.synchronize()
+            n += 10
+        return n
 
     c_split = lambda: kvz.decode_attention_splits(q, cache, table, lens, w.sm_scale, ws, pages_per_split=pps)
     c_merge = lambda: kvz.merge_splits(ws, lens, B, Hq, H, D, P, w.max_pages, out, pages_per_split=pps)
+    d_split = lambda: kvz.decode_attention_dense_splits(q, kd, vd, table, lens, w.sm_scale, ws, pages_per_split=pps)
+    d_merge = lambda: kvz.merge_splits(ws, lens, B, Hq, H, D, P, w.max_pages, out, dense=True, pages_per_split=pps)
+    settle_steps = settle(c_split, c_merge, args.settle_seconds)
+    # the headline: W warm-up steps, then exactly K timed steps of the compressed path
     for _ in range(args.warmup):
         c_split()
         c_merge()
+    wall, step_gpu_us = timed_steps(c_split, c_merge, args.steps)
+    ms_per_step = wall / args.steps * 1e3
     # the split size the kernel chose for this batch, and the bytes that follow from it:
     # page-table entries, q and the partials
     C_used = kvz.chosen_pages_per_split(ws, B, Hq, H, D, P, w.max_pages, pps)
     part_bytes, splits_used = partial_bytes(C_used, full)
     small_bytes = int(full.sum()) * H * 4 + B * Hq * D * 2 + part_bytes
     comp_bytes = units_bytes + 2 * pool_esc + tail_bytes + small_bytes
-    wall, attn_us, merge_us, split_mean_us, step_gpu_us = run_loop(c_split, c_merge, args.steps)
-    ms_per_step = wall / args.steps * 1e3
+    split_mean_us, attn_us, merge_us = launch_stats(c_split, c_merge, args.steps)
     assert int(cache.status.item()) == 0
+
+    # the output of the timed call, with its fp32 copy, for the parity check against the oracle
+    out_bf16 = out.clone()
+    out32 = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
+    kvz.decode_attention(q, cache, table, lens, w.sm_scale, out, out32, workspace=ws, pages_per_split=pps)
+    torch.cuda.synchronize()
+    same_bits = bool(torch.equal(out, out_bf16))
+
+    dense = None
+    if not args.no_dense:
+        for _ in range(args.warmup):
+            d_split()
+            d_merge()
+        dwall, dstep_gpu = timed_steps(d_split, d_merge, args.steps)
+        dC = kvz.chosen_pages_per_split(ws, B, Hq, H, D, P, w.max_pages, pps)
+        dpages = (L + P - 1) // P
+        dense_bytes = dense_kv_bytes + int(dpages.sum()) * H * 4 + B * Hq * D * 2 + partial_bytes(dC, dpages)[0]
+        dsplit_mean, dattn, dmerge = launch_stats(d_split, d_merge, args.steps)
+        dense = dict(ms_per_step=dwall / args.steps * 1e3, step_gpu_us=round(dstep_gpu, 2),
+                     attn_us=float(np.median(dattn)), attn_us_mean=dsplit_mean, merge_us=float(np.median(dmerge)),
+                     bytes=dense_bytes, gbps=dense_bytes / (dsplit_mean * 1e-6) / 1e9,
+                     pct_peak=100 * dense_bytes / (dsplit_mean * 1e-6) / 1e9 / PEAK_HBM_GBPS,
+                     tokens_per_s=B / (dwall / args.steps))
+
+    # compressed and dense whole-step loops alternated, K steps each, after all of the above:
+    # neither path's figure can carry a clock ramp or another transient alone
+    inter = None
+    if dense is not None and args.rounds > 0:
+        cw, dw = [], []
+        for _ in range(args.rounds):
+            cw.append(timed_steps(c_split, c_merge, args.steps)[0] / args.steps * 1e3)
+            dw.append(timed_steps(d_split, d_merge, args.steps)[0] / args.steps * 1e3)
+        inter = {"rounds": args.rounds, "ms_per_step_median": round(float(np.median(cw)), 4),
+                 "dense_ms_per_step_median": round(float(np.median(dw)), 4),
+                 "speedup_vs_dense_median": round(float(np.median(np.array(dw) / np.array(cw))), 4)}
 
     # same kernel with the caches flushed before every launch (the pages clear L2, §IV.B)
     flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
     cold = []
     for _ in range(args.cold_steps):
         flush.zero_()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0, e1 = pair()
         e0.record()
         c_split()
         e1.record()
@@ -259,26 +329,11 @@ def main() -> int:
     cold = np.array(cold) if cold else np.array([np.nan])
     del flush
 
-    layers = layer_loop(kvz, cache, q, table, lens, w, ws, pps, args.graph_layers, dev) if args.graph_layers > 0 else None
+    ceiling = None
+    if fmt == kvz.FORMAT_ESCAPE and not args.no_ceiling:
+        ceiling = read_ceiling(kvz, cache, table, lens, full, H, U, args.steps, dev, pair)
 
-    dense = None
-    if not args.no_dense:
-        d_split = lambda: kvz.decode_attention_dense_splits(q, kd, vd, table, lens, w.sm_scale, ws,
-                                                            pages_per_split=pps)
-        d_merge = lambda: kvz.merge_splits(ws, lens, B, Hq, H, D, P, w.max_pages, out, dense=True,
-                                           pages_per_split=pps)
-        for _ in range(args.warmup):
-            d_split()
-            d_merge()
-        dC = kvz.chosen_pages_per_split(ws, B, Hq, H, D, P, w.max_pages, pps)
-        dpages = (L + P - 1) // P
-        dense_bytes = dense_kv_bytes + int(dpages.sum()) * H * 4 + B * Hq * D * 2 + partial_bytes(dC, dpages)[0]
-        dwall, dattn, dmerge, dsplit_mean, dstep_gpu = run_loop(d_split, d_merge, args.steps)
-        dense = dict(ms_per_step=dwall / args.steps * 1e3, attn_us=float(np.median(dattn)),
-                     attn_us_mean=dsplit_mean, merge_us=float(np.median(dmerge)), bytes=dense_bytes,
-                     gbps=dense_bytes / (dsplit_mean * 1e-6) / 1e9,
-                     pct_peak=100 * dense_bytes / (dsplit_mean * 1e-6) / 1e9 / PEAK_HBM_GBPS,
-                     tokens_per_s=B / (dwall / args.steps))
+    layers = layer_loop(kvz, cache, q, table, lens, w, ws, pps, args.graph_layers, dev) if args.graph_layers > 0 else None
 
     attn_mean = split_mean_us   # mean launch duration of the split kernel, back to back
     achieved = comp_bytes / (attn_mean * 1e-6) / 1e9
@@ -295,10 +350,14 @@ def main() -> int:
                     achieved=round(achieved, 1), peak=PEAK_HBM_GBPS, unit="GB/s",
                     frac=round(achieved / PEAK_HBM_GBPS, 4), traffic=traffic,
                     algorithmic_bytes_per_launch=comp_bytes, attn_us_mean=round(attn_mean, 2))
+    if ceiling is not None:
+        ceiling["pct_of_read_ceiling"] = round(100 * achieved / ceiling["gbps"], 2)
 
-    cpu = None
+    cpu = parity = None
     if not args.no_cpu and fmt == kvz.FORMAT_ESCAPE:   # the CPU oracle baseline decodes the library's format
-        cpu = cpu_baseline(w, kp, vp, min(args.cpu_requests, B), log)
+        cpu, ref_rows, ref = cpu_baseline(w, kp, vp, min(args.cpu_requests, B), units_bytes, pool_esc, tail_bytes, log)
+        parity = parity_check(out_bf16.cpu().numpy().view(np.uint16), out32.cpu().numpy(), ref_rows, ref, same_bits)
+        log(f"parity: {parity}")
 
     # Appends in steady state, after everything else (they overwrite the tails): up to one page
     # of tokens, each call timed alone; a call in which some request's tail fills compresses
@@ -345,6 +404,10 @@ def main() -> int:
         "pct_peak_hbm": round(100 * achieved / PEAK_HBM_GBPS, 2),
         "uncompressed_equiv_gbps": round(dense_kv_bytes / (attn_mean * 1e-6) / 1e9, 1),
         "step_gpu_us": round(step_gpu_us, 2),
+        "settle_steps": settle_steps,
+        "interleaved": inter,
+        "read_ceiling": ceiling,
+        "parity": parity,
         "attn_us": {"mean": round(attn_mean, 2), "median": round(float(np.median(attn_us)), 2),
                     "p10": round(float(np.percentile(attn_us, 10)), 2),
                     "p90": round(float(np.percentile(attn_us, 90)), 2), "cold_median": round(float(np.median(cold)), 2) if args.cold_steps else None},
@@ -367,7 +430,61 @@ def main() -> int:
         "source_digest": source_digest(ksrc),
     }
     print(json.dumps(res), flush=True)
+    if parity is not None and not parity["ok"]:
+        log("parity check against the oracle FAILED")
+        return 1
     return 0
+
+
+def read_ceiling(kvz, cache, table, lens, full, H, U, steps, dev, pair):
+    """The streaming-read ceiling (kvzb_read_units): the same unit bytes and page-table entries,
+    read in the attention kernels' pattern, with 1, 2, 4, 8 and 16 waves per SIMD of the device
+    (the kernel keeps up to 8 resident); the best rate is the ceiling."""
+    import numpy as np
+    import torch
+
+    from decode_attention_losslessly_amd import kvz_bench
+    B = int(lens.numel())
+    rows = B * H
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    nbytes = int(full.sum()) * H * (U + 4)
+    best = None
+    for waves_per_simd in (1, 2, 4, 8, 16):
+        chunks = max(1, round(waves_per_simd * 4 * cus / rows))
+        sink = torch.empty(rows * chunks * 64, dtype=torch.int32, device=dev)
+        fn = lambda: kvz_bench.read_units(cache, table, lens, chunks, sink)
+        for _ in range(5):
+            fn()
+        e0, e1 = pair()
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / steps
+        gbps = nbytes / (us * 1e-6) / 1e9
+        if best is None or gbps > best["gbps"]:
+            best = {"gbps": round(gbps, 1), "us": round(us, 2), "chunks_per_row": chunks,
+                    "waves": rows * chunks, "bytes": nbytes}
+    best["pct_peak"] = round(100 * best["gbps"] / PEAK_HBM_GBPS, 2)
+    return best
+
+
+def parity_check(out16, out32, rows, ref, same_bits):
+    """The timed call's output against this run's oracle rows (the CPU baseline's): BF16 within
+    max(2e-2, 2^-7 |o|) per element, fp32 within 1e-4 max_d |o| per row."""
+    import numpy as np
+    idx = tuple(np.array(rows).T)
+    got16 = (out16[idx].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    got32 = out32[idx].astype(np.float64)
+    err16 = np.abs(got16 - ref)
+    ok16 = bool(np.all(err16 <= np.maximum(2e-2, 2.0 ** -7 * np.abs(ref))))
+    nrm = np.abs(ref).max(axis=-1)
+    e32 = np.abs(got32 - ref).max(axis=-1) / np.where(nrm > 0, nrm, 1.0)
+    ok32 = bool(np.all(e32 <= 1e-4))
+    return {"rows": len(rows), "max_bf16_abs_err": float(err16.max()), "max_f32_normwise_err": float(e32.max()),
+            "bf16_ok": ok16, "f32_ok": ok32, "timed_output_reproduced": same_bits,
+            "ok": ok16 and ok32 and same_bits}
 
 
 def layer_loop(kvz, cache, q, table, lens, w, ws, pps, nl, dev, reps=20):
@@ -429,9 +546,10 @@ def _host_cpu() -> str:
     return "unknown"
 
 
-def cpu_baseline(w, kp, vp, n_req, log):
+def cpu_baseline(w, kp, vp, n_req, units_bytes, pool_esc, tail_bytes, log):
     """The C oracle (scalar decode of the compressed units + fp64 attention, OpenMP over rows) on
-    the rows of the first n_req requests; scaled to the whole batch."""
+    the rows of the first n_req requests, timed, and scaled to the whole batch. Returns the
+    baseline record, the rows and their fp64 outputs (this run's parity reference)."""
     import numpy as np
 
     from oracle import c_oracle
@@ -453,10 +571,14 @@ def cpu_baseline(w, kp, vp, n_req, log):
     rows = [(r, h) for r in reqs for h in range(w.Hq)]
     q = w.q()
     t0 = time.perf_counter()
-    c_oracle.decode_attention_rows(q, units, pool_s, w.page_table, L, tk, tv, w.Hkv, w.P, w.sm_scale, rows)
+    ref = c_oracle.decode_attention_rows(q, units, pool_s, w.page_table, L, tk, tv, w.Hkv, w.P, w.sm_scale, rows)
     dt = time.perf_counter() - t0
     threads = c_oracle.num_threads()
-    step_s = dt * (w.B * w.Hq) / len(rows)
+    scale = (w.B * w.Hq) / len(rows)
+    step_s = dt * scale
+    # what the whole batch's call processes: its compressed bytes (units, pool escapes, tail
+    # rows) and its context tokens
+    comp = units_bytes + 2 * pool_esc + tail_bytes
     log(f"cpu oracle: {len(rows)} rows in {dt:.2f}s on {threads} threads (encode set-up {enc_s:.1f}s)")
     # the same oracle on one core, over the first request's rows
     one = rows[:w.Hq]
@@ -467,14 +589,18 @@ def cpu_baseline(w, kp, vp, n_req, log):
     c_oracle.set_num_threads(threads)
     step1_s = dt1 * (w.B * w.Hq) / len(one)
     log(f"cpu oracle on 1 core: {len(one)} rows in {dt1:.2f}s")
-    return {"value": round(w.B / step_s, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{len(rows)} of {w.B * w.Hq} (request, head) rows: scalar decode of their compressed "
-                      f"pages + fp64 attention, {dt:.2f}s wall, scaled to the full batch",
-            "cpu_seconds": round(dt * threads, 2),
-            "one_core": {"value": round(w.B / step1_s, 3), "unit": "tokens/s",
-                         "sample": f"{len(one)} rows of request 0, {dt1:.2f}s, scaled to the full batch"},
-            "host_cpu": _host_cpu()}
-
+    rec = {"value": round(w.B / step_s, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+           "sample": f"{len(rows)} of {w.B * w.Hq} (request, head) rows: scalar decode of their compressed "
+                     f"pages + fp64 attention, {dt:.2f}s wall, scaled to the full batch",
+           "cpu_seconds": round(dt * threads, 2),
+           "kv_tokens_per_s": round(float(L.sum()) / step_s, 1),
+           "compressed_gbps": round(comp / step_s / 1e9, 4),
+           "one_core": {"value": round(w.B / step1_s, 3), "unit": "tokens/s",
+                        "kv_tokens_per_s": round(float(L.sum()) / step1_s, 1),
+                        "compressed_gbps": round(comp / step1_s / 1e9, 4),
+                        "sample": f"{len(one)} rows of request 0, {dt1:.2f}s, scaled to the full batch"},
+           "host_cpu": _host_cpu()}
+    return rec, rows, ref
 
 if __name__ == "__main__":
     sys.exit(main())

@@ -1,7 +1,8 @@
-"""Builds the HIP library libkvz.so for gfx950, in-tree next to this file.
+"""Builds the HIP libraries for gfx950, in-tree next to this file.
 
-hipcc compiles each source of csrc/ (device code for gfx950 only) and links them into one
-shared library exporting the C ABI of include/kvz.h.
+hipcc compiles each source of csrc/ (device code for gfx950 only) and links them into
+libkvz.so, the shared library exporting the C ABI of include/kvz.h, and libkvz_bench.so, the
+measurement kernels of include/kvz_bench.h.
 """
 import os
 import subprocess
@@ -15,6 +16,8 @@ BUILD = os.path.join(HERE, "_build")
 OUT = os.path.join(HERE, "libkvz.so")
 SOURCES = ["kvz_api.hip", "compress.hip", "decompress.hip", "attn_mha.hip", "attn_gqa.hip", "attn_dense.hip",
            "merge.hip", "attn_zf.hip", "pool.hip"]
+BENCH_OUT = os.path.join(HERE, "libkvz_bench.so")
+BENCH_SOURCES = ["read_ceiling.hip"]
 ARCH = os.environ.get("KVZ_OFFLOAD_ARCH", "gfx950")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-mcode-object-version=5",
@@ -38,15 +41,21 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    with ThreadPoolExecutor(min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", OUT + ".tmp"]
+def _link(objs, out: str, verbose: bool) -> None:
+    cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", out + ".tmp"]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(OUT + ".tmp", OUT)
+    os.replace(out + ".tmp", out)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = SOURCES + BENCH_SOURCES
+    with ThreadPoolExecutor(min(8, len(srcs))) as ex:
+        objs = dict(zip(srcs, ex.map(lambda s: _compile(s, verbose), srcs)))
+    _link([objs[s] for s in SOURCES], OUT, verbose)
+    _link([objs[s] for s in BENCH_SOURCES], BENCH_OUT, verbose)
     return OUT
 
 

@@ -30,6 +30,19 @@ def test_library_exports_every_declared_symbol():
     assert set(binding.EXPORTS) == set(names)
 
 
+def test_bench_library_exports_every_declared_symbol():
+    from decode_attention_losslessly_amd import kvz_bench
+    text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "kvz_bench.h")).read(), flags=re.S)
+    names = sorted(set(re.findall(r"\b(kvzb_[a-z_0-9]+)\s*\(", text)))
+    assert names and set(kvz_bench.EXPORTS) == set(names)
+    L = ctypes.CDLL(kvz_bench.LIB_PATH)
+    for n in names:
+        assert hasattr(L, n), n
+    # argument checks come before any device work
+    assert kvz_bench.lib().kvzb_read_units(None, 1, 6272, None, 1, None, 1, 1, 16, 1, None, None) == \
+        binding.KVZ_ERR_INVALID_ARG
+
+
 # the calls the hot path's boundary is built from: sizes, compress, append, attention over the
 # compressed cache and over the uncompressed baseline, the test decode, error strings
 BOUNDARY = ("kvz_payload_bytes", "kvz_meta_bytes", "kvz_workspace_bytes", "kvz_compress_pages", "kvz_append_token",
