@@ -129,9 +129,6 @@ def main() -> int:
     n_units = len(ids) * H
     fmt = kvz.FORMAT_ZIPFUSION if args.format == "zipfusion" else kvz.FORMAT_ESCAPE
     if fmt == kvz.FORMAT_ZIPFUSION:
-        if Hq != H:
-            print("the ZipFusion-format kernel is multi-head only", file=sys.stderr, flush=True)
-            return 2
         w.name = f"{w.name}+zipfusion"
         pool_cap = (n_units + B * H) * 2 * P * D          # room for every block raw
     else:
@@ -344,8 +341,10 @@ def main() -> int:
         t = json.load(open(tfile))
         if t.get("source_digest") == source_digest(ksrc):
             traffic = t.get("bytes_per_launch")
-    kname = f"attn_zf_kernel<{D}>" if fmt == kvz.FORMAT_ZIPFUSION else (f"attn_mha_kernel<{D}>" if Hq == H
-                                                                        else "attn_gqa_kernel")
+    if fmt == kvz.FORMAT_ZIPFUSION:
+        kname = f"attn_zf_kernel<{D}>" if Hq == H else "attn_zf_gqa_kernel"
+    else:
+        kname = f"attn_mha_kernel<{D}>" if Hq == H else "attn_gqa_kernel"
     roofline = dict(kernel=kname, bound="hbm",
                     achieved=round(achieved, 1), peak=PEAK_HBM_GBPS, unit="GB/s",
                     frac=round(achieved / PEAK_HBM_GBPS, 4), traffic=traffic,

@@ -9,7 +9,15 @@
 // the SIMD cover. Handling them in the main loop measured faster than a second sweep after it,
 // because with this format most units hold some raw block.
 //
-// Also the test kernel that writes the rebuilt values of whole units back out.
+// The grouped-query kernel over this format has the skeleton of the escape format's
+// grouped-query kernel (attn_gqa.hip, gqa_core.hpp: S^T = K Q^T and P.V on the matrix cores) with
+// this format's loads and rebuild: lane l rebuilds the 32 K values of token l % 16, dims
+// 32 (l / 16) .. + 31 (the matrix-core A operand, the pages' Tensor-Core operand rebuild) from
+// one block's low bytes and codes, and V dims l and l + 64 as in the multi-head kernel.
+//
+// Also the test kernel that writes the rebuilt values of whole units back out, in either K lane
+// layout.
+#include "gqa_core.hpp"
 #include "mha_core.hpp"
 #include "zf.hpp"
 
@@ -180,9 +188,152 @@ __global__ __launch_bounds__(64 * kZfWaves) void attn_zf_kernel(
   }
 }
 
+// ---------------------------------------------------------------- grouped queries
+struct ZgStage {
+  const uint8_t* unit;
+  int tile;
+  bool ok;           // false when the page id was out of range: a stand-in unit was read
+  uint32_t rawlo;    // low dword of the unit's raw-pool offset: all ones when it has no raw block
+  ZPair k;           // token l % 16, dims 32 (l / 16) .. + 31
+  ZPiece v[2];       // dims l, l + 64
+};
+
+__device__ __forceinline__ void zf_gqa_issue(ZgStage& st, const uint8_t* units, int pid, int tile, int H, int h, int P,
+                                             int num_pages, int lane) {
+  st.ok = pid >= 0 && pid < num_pages;
+  st.tile = tile;
+  st.unit = units + ((size_t)(st.ok ? pid : 0) * H + h) * zf_unit_bytes(P, 128);
+  st.rawlo = stream4(st.unit + zf_rawoff_offset(P, 128));
+  zf_load_pair(st.unit, P, 128, tile, k_piece<128, true>(lane, 0), st.k);
+#pragma unroll
+  for (int s = 0; s < 2; ++s) zf_load_piece(st.unit, P, 128, true, tile, lane + 64 * s, st.v[s]);
+}
+
+// Rebuilds this lane's K pairs (A-operand layout) and V pairs (dims l, l + 64); with RAW, raw
+// blocks are read from the pool (bounds-checked against its capacity; a unit whose raw blocks
+// were dropped reads zeros).
+template <bool RAW>
+__device__ __forceinline__ void zf_gqa_rebuild(const ZgStage& stg, int P, const uint16_t* pool, int64_t pool_cap,
+                                               int lane, uint32_t (&kp)[16], uint32_t (&vp)[2][8]) {
+  uint64_t off = 0;
+  if constexpr (RAW) off = zf_raw_offset(stg.unit, P, 128);
+  if (RAW && stg.k.meta == kZfRaw) {
+    const int pc = k_piece<128, true>(lane, 0);
+    const uint32_t rank = zf_raw_rank(stg.unit, zf_block_index(false, P, 128, stg.tile, (16 * pc) / kZfBlock));
+    if (off != kInline && off + (uint64_t)(rank + 1) * kZfBlock <= (uint64_t)pool_cap) {
+      zf_raw_piece(pool, off, rank, pc, &kp[0]);
+      zf_raw_piece(pool, off, rank, pc + 1, &kp[8]);
+    } else {
+      for (int j = 0; j < 16; ++j) kp[j] = 0;
+    }
+  } else {
+    zf_decode_pair(stg.k, kp);
+  }
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    if (RAW && stg.v[s].meta == kZfRaw) {
+      const int d = lane + 64 * s;
+      const uint32_t rank = zf_raw_rank(stg.unit, zf_block_index(true, P, 128, stg.tile, (16 * d) / kZfBlock));
+      if (off != kInline && off + (uint64_t)(rank + 1) * kZfBlock <= (uint64_t)pool_cap)
+        zf_raw_piece(pool, off, rank, d, vp[s]);
+      else
+        for (int j = 0; j < 8; ++j) vp[s][j] = 0;
+    } else {
+      zf_decode_piece(stg.v[s], vp[s]);
+    }
+  }
+}
+
+__device__ __forceinline__ void zf_gqa_compute(GqaState& st, const ZgStage& stg, int P, const uint16_t* pool,
+                                               int64_t pool_cap, float scale, uint32_t* vlds, int lane) {
+  if (!stg.ok) return;
+  uint32_t kp[16], vp[2][8];
+  if (uniform(stg.rawlo) == 0xFFFFFFFFu) zf_gqa_rebuild<false>(stg, P, pool, pool_cap, lane, kp, vp);
+  else zf_gqa_rebuild<true>(stg, P, pool, pool_cap, lane, kp, vp);
+  const int vdim[2] = {lane, lane + 64};
+  gqa_tile(st, kp, vdim, vp, kTile, scale, vlds, lane);
+}
+
+// One wave per (request, KV head, chunk of up to 8 query heads, split), as the escape format's
+// grouped-query kernel (3 waves per SIMD: see there), with the next tile's loads issued before
+// the current tile is computed.
+__global__ __launch_bounds__(64 * kZfWaves) __attribute__((amdgpu_waves_per_eu(3))) void attn_zf_gqa_kernel(
+    const uint16_t* __restrict__ q, const uint8_t* __restrict__ units, const uint16_t* __restrict__ pool,
+    int64_t pool_cap, const uint16_t* __restrict__ k_tail, const uint16_t* __restrict__ v_tail,
+    const int32_t* __restrict__ page_table, int max_pages, const int32_t* __restrict__ seq_lens, int B, int Hq, int H,
+    int P, int num_pages, SplitPlan plan, float scale, float* __restrict__ ws_acc, float* __restrict__ ws_ml,
+    uint32_t* __restrict__ status) {
+  __shared__ uint32_t vlds_all[kZfWaves][128 * 8];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int grp = Hq / H, nchunks = (grp + kGqaRows - 1) / kGqaRows;
+  WorkItem wi;
+  if (!plan_work(plan, seq_lens, B, P, max_pages, false, H * nchunks, (int)uniform(blockIdx.x * kZfWaves + wave),
+                 lane, wi))
+    return;
+  const int S = plan.S, C = wi.C, s = wi.s, qc = wi.k % nchunks, h = wi.k / nchunks, r = wi.r;
+  const int hq0 = h * grp + qc * kGqaRows, nq = min(kGqaRows, grp - qc * kGqaRows);
+  int L = request_len(wi, seq_lens);
+  if (L > max_pages * P || L < 0) {
+    if (lane == 0 && s == 0 && h == 0 && qc == 0) atomicOr(status, kStatusSeqTooLong);
+    L = L < 0 ? 0 : max_pages * P;
+  }
+  int nfull = L / P;
+  const int rows = L % P;
+  const int Sr = active_splits(nfull, C);   // as the merge counts them (see the escape-format kernels)
+  if (num_pages <= 0 && nfull > 0) {
+    if (lane == 0 && s == 0 && h == 0 && qc == 0) atomicOr(status, kStatusBadPage);
+    nfull = 0;
+  }
+  if (s >= Sr) return;
+  const int p0 = s * C, p1 = min(p0 + C, nfull);
+  GqaState st;
+  gqa_init(st, q, r, Hq, hq0, nq, lane);
+  uint32_t* vlds = vlds_all[wave];
+  const int32_t* pt_row = page_table + (size_t)r * max_pages;
+  const int T = P / kTile;
+  const int nsteps = (p1 > p0 ? p1 - p0 : 0) * T;
+  bool bad = false;
+  if (nsteps > 0) {
+    int ln = 0, lp = p0, lt = 0;
+    const int last = nsteps - 1;
+    auto advance = [&]() {
+      if (ln < last) {
+        ++ln;
+        if (++lt == T) { lt = 0; ++lp; }
+      }
+    };
+    ZgStage a, b;
+    int pid = sload<int32_t>(pt_row + lp);
+    zf_gqa_issue(a, units, pid, lt, H, h, P, num_pages, lane);
+    advance();
+    pid = sload<int32_t>(pt_row + lp);
+    for (int i = 0; i < nsteps; i += 2) {
+      zf_gqa_issue(b, units, pid, lt, H, h, P, num_pages, lane);
+      advance();
+      pid = sload<int32_t>(pt_row + lp);
+      bad |= !a.ok;
+      zf_gqa_compute(st, a, P, pool, pool_cap, scale, vlds, lane);
+      if (i + 1 >= nsteps) break;
+      zf_gqa_issue(a, units, pid, lt, H, h, P, num_pages, lane);
+      advance();
+      pid = sload<int32_t>(pt_row + lp);
+      bad |= !b.ok;
+      zf_gqa_compute(st, b, P, pool, pool_cap, scale, vlds, lane);
+    }
+  }
+  if (bad && lane == 0) atomicOr(status, kStatusBadPage);
+  if (s == Sr - 1 && rows > 0) {
+    const size_t toff = ((size_t)r * H + h) * P * 128;
+    for (int t0 = 0; t0 < rows; t0 += kTile)
+      gqa_raw_tile(st, k_tail + toff, v_tail + toff, t0, min(kTile, rows - t0), scale, vlds, lane);
+  }
+  gqa_store(st, r, Hq, hq0, nq, S, s, ws_acc, ws_ml, lane);
+}
+
 // Test kernel: one wave per (unit, head) writes the rebuilt K and V of whole units (the same
-// loads and rebuild as the attention kernel, raw blocks from the pool).
-template <int D>
+// loads and rebuild as the attention kernels, raw blocks from the pool), with the multi-head or
+// (GQA) the grouped-query K lane layout.
+template <int D, bool GQA>
 __global__ __launch_bounds__(64) void decompress_zf_kernel(const uint8_t* __restrict__ units,
                                                            const uint16_t* __restrict__ pool, int64_t pool_cap,
                                                            const int32_t* __restrict__ page_ids, int H, int P,
@@ -198,13 +349,25 @@ __global__ __launch_bounds__(64) void decompress_zf_kernel(const uint8_t* __rest
   uint16_t* kd = k_dst + ((size_t)i * H + h) * P * D;
   uint16_t* vd = v_dst + ((size_t)i * H + h) * P * D;
   for (int t = 0; t < P / kTile; ++t) {
-    ZStage<D> st;
-    zf_issue<D>(st, units, pid, 0, t, H, h, P, num_pages, lane);
     uint32_t kp[D / 8], vp[D / 8];
-    zf_rebuild<D, true>(st, P, pool, pool_cap, lane, kp, vp);
+    if constexpr (GQA) {
+      ZgStage st;
+      zf_gqa_issue(st, units, pid, t, H, h, P, num_pages, lane);
+      uint32_t v2[2][8];
+      zf_gqa_rebuild<true>(st, P, pool, pool_cap, lane, kp, v2);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        vp[j] = v2[0][j];
+        vp[8 + j] = v2[1][j];
+      }
+    } else {
+      ZStage<D> st;
+      zf_issue<D>(st, units, pid, 0, t, H, h, P, num_pages, lane);
+      zf_rebuild<D, true>(st, P, pool, pool_cap, lane, kp, vp);
+    }
 #pragma unroll
     for (int p = 0; p < D / 64; ++p) {
-      const int pc = k_piece<D, false>(lane, p);
+      const int pc = k_piece<D, GQA>(lane, p);
       uint32_t* dst = reinterpret_cast<uint32_t*>(kd + (size_t)(t * kTile + piece_token<D>(pc)) * D + piece_dim<D>(pc));
 #pragma unroll
       for (int j = 0; j < 8; ++j) dst[j] = kp[8 * p + j];
@@ -245,16 +408,35 @@ int launch_attn_zf(const uint16_t* q, const uint8_t* units, const uint16_t* pool
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 
+int launch_attn_zf_gqa(const uint16_t* q, const uint8_t* units, const uint16_t* pool, int64_t pool_cap,
+                       const uint16_t* k_tail, const uint16_t* v_tail, const int32_t* page_table, int max_pages,
+                       const int32_t* seq_lens, int B, int Hq, int H, int D, int P, int num_pages, SplitPlan plan,
+                       float scale, float* ws_acc, float* ws_ml, uint32_t* status, hipStream_t stream) {
+  if (D != 128) return -2;
+  static int slots[64];
+  const dim3 block(64 * kZfWaves);
+  const long items = (long)B * H * ((Hq / H + kGqaRows - 1) / kGqaRows);
+  plan.slots = resident_waves(attn_zf_gqa_kernel, block.x, slots, 64);
+  if (plan.slots <= 0) plan.slots = (int)(items * plan.S);
+  hipLaunchKernelGGL(attn_zf_gqa_kernel, dim3(plan_blocks(plan, items, kZfWaves)), block, 0, stream, q, units, pool,
+                     pool_cap, k_tail, v_tail, page_table, max_pages, seq_lens, B, Hq, H, P, num_pages, plan, scale,
+                     ws_acc, ws_ml, status);
+  return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
 int launch_decompress_zf(const uint8_t* units, const uint16_t* pool, int64_t pool_cap, const int32_t* page_ids, int n,
-                         int H, int P, int D, int num_pages, uint16_t* k_dst, uint16_t* v_dst, uint32_t* status,
-                         hipStream_t stream) {
+                         int H, int P, int D, int num_pages, int lane_map, uint16_t* k_dst, uint16_t* v_dst,
+                         uint32_t* status, hipStream_t stream) {
   dim3 grid((unsigned)n * H), block(64);
-  if (D == 128)
-    hipLaunchKernelGGL((decompress_zf_kernel<128>), grid, block, 0, stream, units, pool, pool_cap, page_ids, H, P,
-                       num_pages, k_dst, v_dst, status);
-  else if (D == 64)
-    hipLaunchKernelGGL((decompress_zf_kernel<64>), grid, block, 0, stream, units, pool, pool_cap, page_ids, H, P,
-                       num_pages, k_dst, v_dst, status);
+  if (D == 128 && lane_map == 1)
+    hipLaunchKernelGGL((decompress_zf_kernel<128, true>), grid, block, 0, stream, units, pool, pool_cap, page_ids, H,
+                       P, num_pages, k_dst, v_dst, status);
+  else if (D == 128 && lane_map == 0)
+    hipLaunchKernelGGL((decompress_zf_kernel<128, false>), grid, block, 0, stream, units, pool, pool_cap, page_ids, H,
+                       P, num_pages, k_dst, v_dst, status);
+  else if (D == 64 && lane_map == 0)
+    hipLaunchKernelGGL((decompress_zf_kernel<64, false>), grid, block, 0, stream, units, pool, pool_cap, page_ids, H,
+                       P, num_pages, k_dst, v_dst, status);
   else
     return -2;
   return hipGetLastError() == hipSuccess ? 0 : -4;

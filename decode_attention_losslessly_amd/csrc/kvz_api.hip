@@ -24,9 +24,13 @@ int launch_attn_zf(const uint16_t* q, const uint8_t* units, const uint16_t* pool
                    const uint16_t* k_tail, const uint16_t* v_tail, const int32_t* page_table, int max_pages,
                    const int32_t* seq_lens, int B, int H, int D, int P, int num_pages, SplitPlan plan, float scale,
                    float* ws_acc, float* ws_ml, uint32_t* status, hipStream_t stream);
+int launch_attn_zf_gqa(const uint16_t* q, const uint8_t* units, const uint16_t* pool, int64_t pool_cap,
+                       const uint16_t* k_tail, const uint16_t* v_tail, const int32_t* page_table, int max_pages,
+                       const int32_t* seq_lens, int B, int Hq, int H, int D, int P, int num_pages, SplitPlan plan,
+                       float scale, float* ws_acc, float* ws_ml, uint32_t* status, hipStream_t stream);
 int launch_decompress_zf(const uint8_t* units, const uint16_t* pool, int64_t pool_cap, const int32_t* page_ids, int n,
-                         int H, int P, int D, int num_pages, uint16_t* k_dst, uint16_t* v_dst, uint32_t* status,
-                         hipStream_t stream);
+                         int H, int P, int D, int num_pages, int lane_map, uint16_t* k_dst, uint16_t* v_dst,
+                         uint32_t* status, hipStream_t stream);
 int launch_attn_mha(const uint16_t* q, const uint8_t* units, const uint16_t* pool, int64_t pool_cap, const uint16_t* k_tail,
                     const uint16_t* v_tail, const int32_t* page_table, int max_pages, const int32_t* seq_lens,
                     int B, int H, int D, int P, int num_pages, SplitPlan plan, float scale, float* ws_acc,
@@ -249,8 +253,11 @@ int kvz_decode_attention_splits(const uint16_t* q, const kvz_cache* c, const int
   float* ws_ml = ws_acc + (size_t)B * H_q * S * D;
   const float scale = sm_scale * 1.4426950408889634f;
   kvz::SplitPlan plan = make_plan(C, S, max_pages, pps > 0, ws_chosen(workspace, B, H_q, S, D));
-  if (c->format == KVZ_FORMAT_ZIPFUSION) {
-    if (H_q != H) return KVZ_ERR_UNSUPPORTED;
+  if (c->format == KVZ_FORMAT_ZIPFUSION && H_q != H) {
+    rc = kvz::launch_attn_zf_gqa(q, c->units, c->esc_pool, c->esc_capacity, c->k_tail, c->v_tail, page_table,
+                                 max_pages, seq_lens, B, H_q, H, D, P, c->num_pages, plan, scale, ws_acc, ws_ml,
+                                 c->status, as_stream(stream));
+  } else if (c->format == KVZ_FORMAT_ZIPFUSION) {
     rc = kvz::launch_attn_zf(q, c->units, c->esc_pool, c->esc_capacity, c->k_tail, c->v_tail, page_table, max_pages,
                              seq_lens, B, H, D, P, c->num_pages, plan, scale, ws_acc, ws_ml, c->status,
                              as_stream(stream));
@@ -366,9 +373,9 @@ int kvz_decompress_pages(const kvz_cache* c, const int32_t* page_ids, int32_t n,
   if ((D != 64 && D != 128) || ((lane_map & 1) && D != 128)) return KVZ_ERR_UNSUPPORTED;
   if (n == 0) return KVZ_OK;
   if (c->format == KVZ_FORMAT_ZIPFUSION) {
-    if (lane_map != 0) return KVZ_ERR_UNSUPPORTED;
+    if (lane_map > 1) return KVZ_ERR_UNSUPPORTED;   // the format has no escape routes
     const int rc = kvz::launch_decompress_zf(c->units, c->esc_pool, c->esc_capacity, page_ids, n, c->num_kv_heads,
-                                             c->page_size, D, c->num_pages, k_dst, v_dst, c->status,
+                                             c->page_size, D, c->num_pages, lane_map, k_dst, v_dst, c->status,
                                              as_stream(stream));
     return rc == -2 ? KVZ_ERR_UNSUPPORTED : (rc ? KVZ_ERR_HIP : KVZ_OK);
   }

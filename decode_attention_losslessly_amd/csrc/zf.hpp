@@ -59,6 +59,25 @@ __device__ __forceinline__ void zf_load_piece(const uint8_t* unit, int P, int D,
   z.meta = stream1(unit + idx);
 }
 
+// The grouped-query K layout (lane l: token l % 16, dims 32 (l / 16) .. + 31, i.e. the adjacent
+// pieces 2c, 2c + 1 of chunk c = 4 (l % 16) + l / 16): 32 values of one block, 32 low bytes,
+// 16 code bytes and the block's meta byte.
+struct ZPair {
+  uint4 low0, low1;
+  uint4 code;
+  uint32_t meta;
+};
+
+__device__ __forceinline__ void zf_load_pair(const uint8_t* unit, int P, int D, int tile, int piece0, ZPair& z) {
+  const int j = (16 * piece0) / kZfBlock, o = (16 * piece0) % kZfBlock;
+  const int idx = zf_block_index(false, P, D, tile, j);
+  const uint8_t* slot = unit + zf_meta_bytes(P, D) + (size_t)idx * kZfSlot;
+  z.low0 = stream16(slot + o);
+  z.low1 = stream16(slot + o + 16);
+  z.code = stream16(slot + kZfBlock + o / 2);
+  z.meta = stream1(unit + idx);
+}
+
 // ---------------------------------------------------------------- rebuild
 // 8 values from their low bytes (L0: values 0..3, L1: 4..7) and codes (W: value i in nibble i,
 // the even value of each byte in its low nibble): high byte = sign << 7 | (b/2 + k), where
@@ -82,6 +101,15 @@ __device__ __forceinline__ void zf_decode_piece(const ZPiece& z, uint32_t* pairs
   const uint32_t B = z.meta * 0x01010101u;
   zf_decode8(z.low.x, z.low.y, z.code.x, B, pairs);
   zf_decode8(z.low.z, z.low.w, z.code.y, B, pairs + 4);
+}
+
+// 32 values of a pair into 16 BF16 pairs (meta must not be kZfRaw)
+__device__ __forceinline__ void zf_decode_pair(const ZPair& z, uint32_t* pairs) {
+  const uint32_t B = z.meta * 0x01010101u;
+  zf_decode8(z.low0.x, z.low0.y, z.code.x, B, pairs);
+  zf_decode8(z.low0.z, z.low0.w, z.code.y, B, pairs + 4);
+  zf_decode8(z.low1.x, z.low1.y, z.code.z, B, pairs + 8);
+  zf_decode8(z.low1.z, z.low1.w, z.code.w, B, pairs + 12);
 }
 
 // the piece's 16 values straight from the pool (its block is raw); rank = the block's rank

@@ -46,7 +46,7 @@
  *             alike) holding the L mod P newest tokens
  *
  * Second format, kvz_cache.format = KVZ_FORMAT_ZIPFUSION: ZipFusion's own block format
- * (§III.B), for comparison with the pages' design. Multi-head attention only.
+ * (§III.B), for comparison with the pages' design; multi-head and grouped-query attention.
  *   block     512 consecutive storage positions of a tile (same storage order as above: K
  *             token-major, V dim-major); compressed when every exponent lies in [b, b+15],
  *             b = the block's smallest exponent rounded down to even, else kept raw
@@ -280,8 +280,9 @@ int kvz_merge_splits(const void* workspace, size_t workspace_bytes, const int32_
  *                    from them)
  *                 3  the route of 2 with the grouped-query kernel's K layout (D = 128 only)
  *   k_dst, v_dst  [n][H][P][D] raw BF16, token-major
- * Supported: D in {64, 128}; lane_map 0 only for KVZ_FORMAT_ZIPFUSION. Errors:
- * KVZ_ERR_INVALID_ARG (lane_map outside 0..3), KVZ_ERR_UNSUPPORTED. Device status: BAD_PAGE_ID. */
+ * Supported: D in {64, 128}; lane maps 0 and 1 only for KVZ_FORMAT_ZIPFUSION (it has no
+ * escapes). Errors: KVZ_ERR_INVALID_ARG (lane_map outside 0..3), KVZ_ERR_UNSUPPORTED. Device
+ * status: BAD_PAGE_ID. */
 int kvz_decompress_pages(const kvz_cache* cache, const int32_t* page_ids, int32_t n,
                          int32_t lane_map, uint16_t* k_dst, uint16_t* v_dst, void* stream);
 

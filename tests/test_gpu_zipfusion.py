@@ -1,9 +1,11 @@
 """GPU parity of the second cache format, ZipFusion's block format (include/kvz.h,
 KVZ_FORMAT_ZIPFUSION; oracle/zipfusion.py): compression byte-exact against the oracle (raw
-blocks compared at the pool offset the library chose), the attention kernel's in-register
-rebuild bit-exact, attention against the fp64 oracle within the stated tolerance, and append
-with compress-on-fill. Workloads cover mostly compressed blocks (smooth values) and all-raw
-blocks (the escape-stress distribution)."""
+blocks compared at the pool offset the library chose), the attention kernels' in-register
+rebuild bit-exact in both K lane layouts (multi-head and grouped-query), attention of the
+multi-head and grouped-query kernels against the fp64 oracle within the stated tolerance
+(reduced workloads, and sampled rows of the full grouped-query workloads), and append with
+compress-on-fill. Workloads cover mostly compressed blocks (smooth values) and all-raw blocks
+(the escape-stress distribution)."""
 import numpy as np
 import pytest
 import torch
@@ -16,18 +18,26 @@ from synth import make_workload
 pytestmark = pytest.mark.gpu
 ZF = kvz.FORMAT_ZIPFUSION
 
-SMALL = {  # multi-head workloads (the block format's kernel is multi-head)
+SMALL = {
     1: dict(),
     2: dict(L=100),
     3: dict(B=3, L=97),
+    4: dict(B=5, lens=[1, 16, 33, 150, 47]),     # grouped queries, 28 over 4 KV heads
     5: dict(B=2, L=70),
     6: dict(B=2, L=70, Hq=8, Hkv=8),
+    7: dict(cfg=6, B=3, lens=[70, 161, 16]),        # grouped queries, 32 over 8 KV heads
+    8: dict(cfg=5, B=2, L=70, Hq=8, Hkv=2),         # grouped queries, every block raw
 }
+
+
+def _workload(key):
+    a = dict(SMALL[key])
+    return make_workload(a.pop("cfg", key), **a)
 
 
 @pytest.mark.parametrize("cfg", sorted(SMALL))
 def test_compress_matches_oracle(cfg):
-    w = make_workload(cfg, **SMALL[cfg])
+    w = _workload(cfg)
     kp, vp = w.pages(0), w.pages(1)
     cache, _ = build_cache(w, kp, vp, fmt=ZF)
     assert int(cache.status.item()) == 0
@@ -49,20 +59,21 @@ def test_compress_matches_oracle(cfg):
 
 @pytest.mark.parametrize("cfg", sorted(SMALL))
 def test_in_kernel_rebuild_is_bit_exact(cfg):
-    w = make_workload(cfg, **SMALL[cfg])
+    w = _workload(cfg)
     kp, vp = w.pages(0), w.pages(1)
     cache, _ = build_cache(w, kp, vp, fmt=ZF)
     ids = full_page_ids(w, w.seq_lens - w.n_append)
-    kd = torch.empty((len(ids), w.Hkv, w.P, w.D), dtype=torch.int16, device=DEV)
-    vd = torch.empty_like(kd)
-    kvz.decompress_pages(cache, dev(ids), kd, vd)
-    torch.cuda.synchronize()
-    assert np.array_equal(host16(kd), kp[ids]) and np.array_equal(host16(vd), vp[ids])
+    for lane_map in ([0, 1] if w.D == 128 else [0]):
+        kd = torch.empty((len(ids), w.Hkv, w.P, w.D), dtype=torch.int16, device=DEV)
+        vd = torch.empty_like(kd)
+        kvz.decompress_pages(cache, dev(ids), kd, vd, lane_map=lane_map)
+        torch.cuda.synchronize()
+        assert np.array_equal(host16(kd), kp[ids]) and np.array_equal(host16(vd), vp[ids]), lane_map
 
 
 @pytest.mark.parametrize("cfg", sorted(SMALL))
 def test_attention_matches_oracle(cfg):
-    w = make_workload(cfg, **SMALL[cfg])
+    w = _workload(cfg)
     kp, vp = w.pages(0), w.pages(1)
     cache, lens = build_cache(w, kp, vp, fmt=ZF)
     q = w.q()
@@ -126,10 +137,31 @@ def test_mixed_units_and_page_fills(P, D):
     check_rows(host16(out).reshape(-1, D), out32.cpu().numpy().reshape(-1, D), ref, f"zf mixed P{P} D{D}")
 
 
-def test_grouped_queries_are_unsupported():
-    w = make_workload(4, B=1, L=40, Hq=8, Hkv=2)
-    cache = kvz.Cache.allocate(w.P, w.Hkv, w.D, w.num_pages, w.B, 1 << 16, device=DEV, fmt=ZF)
+@pytest.mark.parametrize("cfg", [4, 6])
+def test_grouped_queries_full_size_sampled(cfg):
+    """The grouped-query workloads at full size in this format (the pages' benchmark shape,
+    32 query over 8 KV heads at 64 x 8192, and 28 over 4 at 64 requests of 1K-8K tokens):
+    sampled units rebuilt bit for bit in the grouped-query K layout, sampled rows against the
+    fp64 oracle."""
+    w = make_workload(cfg)
+    kp, vp = w.pages(0), w.pages(1)
+    cache, lens = build_cache(w, kp, vp, fmt=ZF)
+    assert int(cache.status.item()) == 0
+    rng = np.random.default_rng(cfg)
+    ids = full_page_ids(w)
+    sample = ids[rng.choice(len(ids), size=64, replace=False)]
+    kd = torch.empty((len(sample), w.Hkv, w.P, w.D), dtype=torch.int16, device=DEV)
+    vd = torch.empty_like(kd)
+    kvz.decompress_pages(cache, dev(sample), kd, vd, lane_map=1)
+    torch.cuda.synchronize()
+    assert np.array_equal(host16(kd), kp[sample]) and np.array_equal(host16(vd), vp[sample])
+    q = w.q()
     out = torch.zeros((w.B, w.Hq, w.D), dtype=torch.int16, device=DEV)
-    with pytest.raises(kvz.KvzError) as e:
-        kvz.decode_attention(dev(w.q()), cache, dev(w.page_table), dev(w.seq_lens), w.sm_scale, out)
-    assert e.value.code == kvz.kvz.KVZ_ERR_UNSUPPORTED
+    out32 = torch.full((w.B, w.Hq, w.D), float("nan"), dtype=torch.float32, device=DEV)
+    kvz.decode_attention(dev(q), cache, dev(w.page_table), lens, w.sm_scale, out, out32)
+    torch.cuda.synchronize()
+    assert int(cache.status.item()) == 0 and np.isfinite(out32.cpu().numpy()).all()
+    rows = sorted(set(zip(rng.integers(0, w.B, 24).tolist(), rng.integers(0, w.Hq, 24).tolist())))
+    ref = oracle_rows(w, kp, vp, q, rows)
+    idx = tuple(np.array(rows).T)
+    check_rows(host16(out)[idx], out32.cpu().numpy()[idx], ref, f"zf full cfg{cfg}")
