@@ -88,7 +88,7 @@ __device__ __forceinline__ void gqa_any_tile(GqaState& st, const uint8_t* unit, 
   if (tile == 0) { krank = 0; vrank = 0; }
   KRaw<128> k;
   VRaw<128> v;
-  load_k<128, true>(unit, P, tile, lane, k);
+  load_k<128, true, false>(unit, P, tile, lane, k);
   load_v<128>(unit, P, tile, lane, v);
   Window kw, vw;
   const bool in_pool = any_stage<128>(hdr, krank, vrank, lds, pool, pool_cap, kw, vw, lane);
@@ -119,10 +119,10 @@ __device__ __forceinline__ void gqa_any_tile(GqaState& st, const uint8_t* unit, 
 // in the pool-capable loop instead.
 __global__ __launch_bounds__(64 * kGqaWaves) KVZ_GQA_OCCUPANCY void attn_gqa_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ units, const uint16_t* __restrict__ pool,
-    int64_t pool_cap, const uint16_t* __restrict__ k_tail, const uint16_t* __restrict__ v_tail,
-    const int32_t* __restrict__ page_table, int max_pages, const int32_t* __restrict__ seq_lens, int B, int Hq, int H,
-    int P, int num_pages, SplitPlan plan, float scale, float* __restrict__ ws_acc, float* __restrict__ ws_ml,
-    uint32_t* __restrict__ status) {
+    int64_t pool_cap, const uint64_t* __restrict__ esc_cursor, const uint16_t* __restrict__ k_tail,
+    const uint16_t* __restrict__ v_tail, const int32_t* __restrict__ page_table, int max_pages,
+    const int32_t* __restrict__ seq_lens, int B, int Hq, int H, int P, int num_pages, SplitPlan plan, float scale,
+    float* __restrict__ ws_acc, float* __restrict__ ws_ml, uint32_t* __restrict__ status) {
   __shared__ __align__(16) uint16_t esc_all[kGqaWaves][esc_lds_elems<128>()];
   __shared__ uint32_t vlds_all[kGqaWaves][128 * 8];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -183,7 +183,9 @@ __global__ __launch_bounds__(64 * kGqaWaves) KVZ_GQA_OCCUPANCY void attn_gqa_ker
       }
     }
   };
-  if (nsteps > 0) {
+  // an escape-heavy cache starts every split in the pool-capable loop (as in the multi-head kernel)
+  if (nsteps > 0 && sload<uint64_t>(esc_cursor) >= (uint64_t)num_pages * H * (uint64_t)(P * 128 / 2)) resume = 0;
+  if (nsteps > 0 && resume < 0) {
     // load cursor as in the multi-head kernel: stays on the last step once there
     int ln = 0, lp = p0, lt = 0;
     bool live = true;   // false once the cursor has passed the last step: those stages read nothing
@@ -362,7 +364,8 @@ __global__ __launch_bounds__(64 * kGqaWaves) KVZ_GQA_OCCUPANCY void attn_dense_g
 
 static int gqa_items(int B, int Hq, int H) { return B * H * ((Hq / H + kGqaRows - 1) / kGqaRows); }
 
-int launch_attn_gqa(const uint16_t* q, const uint8_t* units, const uint16_t* pool, int64_t pool_cap, const uint16_t* k_tail,
+int launch_attn_gqa(const uint16_t* q, const uint8_t* units, const uint16_t* pool, int64_t pool_cap,
+                    const uint64_t* esc_cursor, const uint16_t* k_tail,
                     const uint16_t* v_tail, const int32_t* page_table, int max_pages, const int32_t* seq_lens,
                     int B, int Hq, int H, int D, int P, int num_pages, SplitPlan plan, float scale, float* ws_acc,
                     float* ws_ml, uint32_t* status, hipStream_t stream) {
@@ -372,7 +375,7 @@ int launch_attn_gqa(const uint16_t* q, const uint8_t* units, const uint16_t* poo
   plan.slots = resident_waves(attn_gqa_kernel, block.x, slots, 64);
   if (plan.slots <= 0) plan.slots = gqa_items(B, Hq, H) * plan.S;
   hipLaunchKernelGGL(attn_gqa_kernel, dim3(plan_blocks(plan, gqa_items(B, Hq, H), kGqaWaves)), block, 0, stream, q, units,
-                     pool, pool_cap, k_tail, v_tail, page_table, max_pages, seq_lens, B, Hq, H, P, num_pages, plan, scale,
+                     pool, pool_cap, esc_cursor, k_tail, v_tail, page_table, max_pages, seq_lens, B, Hq, H, P, num_pages, plan, scale,
                      ws_acc, ws_ml, status);
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }

@@ -93,10 +93,10 @@ __device__ __forceinline__ bool mha_compute(MhaState<D>& st, const MhaStage<D>& 
 template <int D>
 __global__ __launch_bounds__(64 * kWavesPerBlock) __attribute__((amdgpu_waves_per_eu(4))) void attn_mha_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ units, const uint16_t* __restrict__ pool,
-    int64_t pool_cap, const uint16_t* __restrict__ k_tail, const uint16_t* __restrict__ v_tail,
-    const int32_t* __restrict__ page_table, int max_pages, const int32_t* __restrict__ seq_lens, int B, int H, int P,
-    int num_pages, SplitPlan plan, float scale, float* __restrict__ ws_acc, float* __restrict__ ws_ml,
-    uint32_t* __restrict__ status) {
+    int64_t pool_cap, const uint64_t* __restrict__ esc_cursor, const uint16_t* __restrict__ k_tail,
+    const uint16_t* __restrict__ v_tail, const int32_t* __restrict__ page_table, int max_pages,
+    const int32_t* __restrict__ seq_lens, int B, int H, int P, int num_pages, SplitPlan plan, float scale,
+    float* __restrict__ ws_acc, float* __restrict__ ws_ml, uint32_t* __restrict__ status) {
   __shared__ __align__(16) uint16_t lds_all[kWavesPerBlock][esc_lds_elems<D>()];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   WorkItem wi;
@@ -173,7 +173,12 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) __attribute__((amdgpu_waves_pe
       }
     }
   };
-  if (nsteps > 0) {
+  // An escape-heavy cache (its pool holds, averaged over the unit slots, a quarter of a unit's
+  // values or more) sends every split to the pool-capable loop from its first step: otherwise
+  // the pipelined loop would load a split's first two tiles only to find them in the pool, and
+  // the pool-capable loop would load them again.
+  if (nsteps > 0 && sload<uint64_t>(esc_cursor) >= (uint64_t)num_pages * H * (uint64_t)(P * D / 2)) resume = 0;
+  if (nsteps > 0 && resume < 0) {
     // load cursor: step ln = (page lp, tile lt); it stays on the last step once there, and the
     // stages issued past the end (never computed) read nothing (`live` false)
     int ln = 0, lp = p0, lt = 0;
@@ -283,7 +288,8 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) __attribute__((amdgpu_waves_pe
   }
 }
 
-int launch_attn_mha(const uint16_t* q, const uint8_t* units, const uint16_t* pool, int64_t pool_cap, const uint16_t* k_tail,
+int launch_attn_mha(const uint16_t* q, const uint8_t* units, const uint16_t* pool, int64_t pool_cap,
+                    const uint64_t* esc_cursor, const uint16_t* k_tail,
                     const uint16_t* v_tail, const int32_t* page_table, int max_pages, const int32_t* seq_lens,
                     int B, int H, int D, int P, int num_pages, SplitPlan plan, float scale, float* ws_acc,
                     float* ws_ml, uint32_t* status, hipStream_t stream) {
@@ -305,10 +311,10 @@ int launch_attn_mha(const uint16_t* q, const uint8_t* units, const uint16_t* poo
   plan.slots = plan.slots > 0 ? 2 * plan.slots : B * H * plan.S;
   const dim3 grid(plan_blocks(plan, (long)B * H, kWavesPerBlock));
   if (D == 128)
-    hipLaunchKernelGGL((attn_mha_kernel<128>), grid, block, 0, stream, q, units, pool, pool_cap, k_tail, v_tail, page_table,
+    hipLaunchKernelGGL((attn_mha_kernel<128>), grid, block, 0, stream, q, units, pool, pool_cap, esc_cursor, k_tail, v_tail, page_table,
                        max_pages, seq_lens, B, H, P, num_pages, plan, scale, ws_acc, ws_ml, status);
   else
-    hipLaunchKernelGGL((attn_mha_kernel<64>), grid, block, 0, stream, q, units, pool, pool_cap, k_tail, v_tail, page_table,
+    hipLaunchKernelGGL((attn_mha_kernel<64>), grid, block, 0, stream, q, units, pool, pool_cap, esc_cursor, k_tail, v_tail, page_table,
                        max_pages, seq_lens, B, H, P, num_pages, plan, scale, ws_acc, ws_ml, status);
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }

@@ -41,7 +41,7 @@ __global__ __launch_bounds__(64) void decompress_kernel(const uint8_t* __restric
     constexpr int NS = D / 64;
     uint32_t vp[NS * 8];
     if constexpr (WIN) {
-      load_k<D, GQA>(unit, P, t, lane, kr);
+      load_k<D, GQA, false>(unit, P, t, lane, kr);
       load_v<D>(unit, P, t, lane, vr);
       Window kw, vw;
       const bool in_pool = any_stage<D>(hdr, krank, vrank, lds, pool, pool_cap, kw, vw, lane);

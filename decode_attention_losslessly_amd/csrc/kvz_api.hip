@@ -31,11 +31,13 @@ int launch_attn_zf_gqa(const uint16_t* q, const uint8_t* units, const uint16_t* 
 int launch_decompress_zf(const uint8_t* units, const uint16_t* pool, int64_t pool_cap, const int32_t* page_ids, int n,
                          int H, int P, int D, int num_pages, int lane_map, uint16_t* k_dst, uint16_t* v_dst,
                          uint32_t* status, hipStream_t stream);
-int launch_attn_mha(const uint16_t* q, const uint8_t* units, const uint16_t* pool, int64_t pool_cap, const uint16_t* k_tail,
+int launch_attn_mha(const uint16_t* q, const uint8_t* units, const uint16_t* pool, int64_t pool_cap,
+                    const uint64_t* esc_cursor, const uint16_t* k_tail,
                     const uint16_t* v_tail, const int32_t* page_table, int max_pages, const int32_t* seq_lens,
                     int B, int H, int D, int P, int num_pages, SplitPlan plan, float scale, float* ws_acc,
                     float* ws_ml, uint32_t* status, hipStream_t stream);
-int launch_attn_gqa(const uint16_t* q, const uint8_t* units, const uint16_t* pool, int64_t pool_cap, const uint16_t* k_tail,
+int launch_attn_gqa(const uint16_t* q, const uint8_t* units, const uint16_t* pool, int64_t pool_cap,
+                    const uint64_t* esc_cursor, const uint16_t* k_tail,
                     const uint16_t* v_tail, const int32_t* page_table, int max_pages, const int32_t* seq_lens,
                     int B, int Hq, int Hkv, int D, int P, int num_pages, SplitPlan plan, float scale, float* ws_acc,
                     float* ws_ml, uint32_t* status, hipStream_t stream);
@@ -264,10 +266,10 @@ int kvz_decode_attention_splits(const uint16_t* q, const kvz_cache* c, const int
   } else if (H_q == H) {
     plan.ranks = rank_count(B, H_q, H, max_pages, pps);
     plan.rank_min = pps < 0 ? 0 : kRankMinPages;
-    rc = kvz::launch_attn_mha(q, c->units, c->esc_pool, c->esc_capacity, c->k_tail, c->v_tail, page_table, max_pages, seq_lens, B, H,
+    rc = kvz::launch_attn_mha(q, c->units, c->esc_pool, c->esc_capacity, c->esc_cursor, c->k_tail, c->v_tail, page_table, max_pages, seq_lens, B, H,
                               D, P, c->num_pages, plan, scale, ws_acc, ws_ml, c->status, as_stream(stream));
   } else {
-    rc = kvz::launch_attn_gqa(q, c->units, c->esc_pool, c->esc_capacity, c->k_tail, c->v_tail, page_table, max_pages, seq_lens, B,
+    rc = kvz::launch_attn_gqa(q, c->units, c->esc_pool, c->esc_capacity, c->esc_cursor, c->k_tail, c->v_tail, page_table, max_pages, seq_lens, B,
                               H_q, H, D, P, c->num_pages, plan, scale, ws_acc, ws_ml, c->status,
                               as_stream(stream));
   }

@@ -90,7 +90,11 @@ __device__ __forceinline__ int piece_token(int piece) { return (16 * piece) / D;
 template <int D>
 __device__ __forceinline__ int piece_dim(int piece) { return (16 * piece) % D; }
 
-template <int D, bool GQA>
+// BASES: the pieces' bases are loaded with the payload (the pipelined loops, whose meta window
+// arrives in the same round trip); without, the caller takes them from the tile's meta window
+// (k_bases_from_meta), which the pool-capable loops load a step ahead: a second read of those
+// bytes a step later could miss the caches and fetch the line again.
+template <int D, bool GQA, bool BASES = true>
 __device__ __forceinline__ void load_k(const uint8_t* unit, int P, int tile, int lane, KRaw<D>& r, bool live = true) {
   constexpr int NP = KRaw<D>::NP;
   const UnitRsrc u = unit_rsrc(unit, live ? unit_bytes(P, D) : 0u);
@@ -104,14 +108,15 @@ __device__ __forceinline__ void load_k(const uint8_t* unit, int P, int tile, int
     if constexpr (!GQA) {
       const uint2 n = uload8(u, 16 * D + 8 * pc, tb);
       r.nib[2 * i] = n.x; r.nib[2 * i + 1] = n.y;
-      r.base[i] = uload1(u, (piece_dim<D>(pc) / kGroup) * kTile + piece_token<D>(pc), bases);
+      if constexpr (BASES) r.base[i] = uload1(u, (piece_dim<D>(pc) / kGroup) * kTile + piece_token<D>(pc), bases);
     }
   }
   if constexpr (GQA) {   // the two pieces are adjacent: one 16-byte offset load, one base
     const int pc = k_piece<D, GQA>(lane, 0);
     const uint4 n = uload16(u, 16 * D + 8 * pc, tb);
     r.nib[0] = n.x; r.nib[1] = n.y; r.nib[2] = n.z; r.nib[3] = n.w;
-    r.base[0] = r.base[1] = uload1(u, (piece_dim<D>(pc) / kGroup) * kTile + piece_token<D>(pc), bases);
+    if constexpr (BASES)
+      r.base[0] = r.base[1] = uload1(u, (piece_dim<D>(pc) / kGroup) * kTile + piece_token<D>(pc), bases);
   }
 }
 
@@ -120,21 +125,43 @@ __device__ __forceinline__ void load_k(const uint8_t* unit, int P, int tile, int
 //   lanes [0, 4G)         K bases of the tile (16*G bytes)
 //   lanes [4G, 8G)        V bases of the tile
 //   lanes [8G, 8G + 32)   header (4 dwords) then the inline escapes
-// (lanes past the meta region read bytes of the unit that are not used).
+// (the other lanes read the region's first dword; they are not used).
 __device__ __forceinline__ uint32_t load_meta(const uint8_t* unit, int P, int D, int tile, int lane, bool live = true) {
   const int G = D / kGroup;
   // the K and V base tables both advance by kTile*G bytes per tile (the scalar offset); the
   // header lanes take it back out
   const uint32_t toff = kbase_offset(D, tile);
+  // lanes past the meta region's end (inline entries beyond kvz_inline_capacity, never read)
+  // read its start instead, so that the window stays on the region's cache lines
   uint32_t off;
   if (lane < 4 * G) off = kbase_offset(D, 0) + 4 * lane;
   else if (lane < 8 * G) off = vbase_offset(P, D, 0) + 4 * (lane - 4 * G);
-  else if (lane < 8 * G + 32) off = hdr_offset(P, D) + 4 * (lane - 8 * G) - toff;
+  else if (lane < 8 * G + 32 && hdr_offset(P, D) + 4 * (lane - 8 * G) < meta_bytes(P, D))
+    off = hdr_offset(P, D) + 4 * (lane - 8 * G) - toff;
   else off = -toff;
   return uload4(unit_rsrc(unit, live ? unit_bytes(P, D) : 0u), off, toff);
 }
 template <int D>
 __device__ __forceinline__ int hdr_lane() { return 8 * (D / kGroup); }
+
+// Base of the group of storage piece pc of a K tile, from the tile's meta window (lanes [0, 4G)
+// hold the tile's K base bytes, g * 16 + tok): one cross-lane read instead of a byte load.
+template <int D>
+__device__ __forceinline__ uint32_t k_piece_base(uint32_t meta, int pc) {
+  const int idx = (piece_dim<D>(pc) / kGroup) * kTile + piece_token<D>(pc);
+  return ((uint32_t)__shfl((int)meta, idx >> 2) >> (8 * (idx & 3))) & 0xFFu;
+}
+
+// the bases of a K tile loaded without them (load_k<D, GQA, false>)
+template <int D, bool GQA>
+__device__ __forceinline__ void k_bases_from_meta(KRaw<D>& r, uint32_t meta, int lane) {
+  if constexpr (GQA) {   // the lane's two pieces are one token's adjacent dims: one group
+    r.base[0] = r.base[1] = k_piece_base<D>(meta, k_piece<D, GQA>(lane, 0));
+  } else {
+#pragma unroll
+    for (int i = 0; i < KRaw<D>::NP; ++i) r.base[i] = k_piece_base<D>(meta, k_piece<D, GQA>(lane, i));
+  }
+}
 
 template <int D>
 __device__ __forceinline__ void decode_k(const KRaw<D>& r, uint32_t (&pairs)[KRaw<D>::VK / 2]) {

@@ -210,13 +210,15 @@ __device__ __forceinline__ bool any_stage(const UnitHeader& hdr, uint32_t krank,
   return in_pool;
 }
 
-// Rebuilds the tile's K pairs in the given lane layout and patches its escapes: from the staged
-// K window for a pool unit, else from the inline list.
+// Rebuilds the tile's K pairs in the given lane layout (k loaded without its bases, which come
+// from the meta window) and patches its escapes: from the staged K window for a pool unit, else
+// from the inline list.
 template <int D, bool GQA>
-__device__ __forceinline__ void any_rebuild_k(uint32_t (&kp)[KRaw<D>::VK / 2], const KRaw<D>& k, uint32_t meta,
+__device__ __forceinline__ void any_rebuild_k(uint32_t (&kp)[KRaw<D>::VK / 2], KRaw<D>& k, uint32_t meta,
                                               const UnitHeader& hdr, bool in_pool, const Window& kw, int P, int tile,
                                               uint32_t& krank, uint16_t* lds, const uint16_t* pool, int64_t pool_cap,
                                               int lane) {
+  k_bases_from_meta<D, GQA>(k, meta, lane);
   decode_k<D>(k, kp);
   if (hdr.kc) {
     if (in_pool) {
@@ -256,7 +258,7 @@ __device__ __forceinline__ void mha_any_tile(MhaState<D>& st, const uint8_t* uni
   if (tile == 0) { krank = 0; vrank = 0; }
   KRaw<D> k;
   VRaw<D> v;
-  load_k<D, false>(unit, P, tile, lane, k);
+  load_k<D, false, false>(unit, P, tile, lane, k);
   load_v<D>(unit, P, tile, lane, v);
   Window kw, vw;
   const bool in_pool = any_stage<D>(hdr, krank, vrank, lds, pool, pool_cap, kw, vw, lane);

@@ -49,10 +49,11 @@ def tails(w, kp, vp, lens=None):
     return tk, tv
 
 
-def build_cache(w, kp, vp, esc_capacity=None, fmt=0):
+def build_cache(w, kp, vp, esc_capacity=None, fmt=0, num_pages=None):
     """Compressed cache of workload w on the device: full pages through kvz_compress_pages, the
     tail rows copied raw, then the appended token (if any) through kvz_append_token.
     fmt 1 = ZipFusion's block format (its pool then holds raw blocks: room for all of them).
+    num_pages: unit slots of the cache (default: the workload's pages).
     Returns (cache, seq_lens tensor)."""
     L0 = w.seq_lens - w.n_append
     ids = full_page_ids(w, L0)
@@ -62,7 +63,7 @@ def build_cache(w, kp, vp, esc_capacity=None, fmt=0):
         cap = (max(1, len(ids)) + w.B) * w.Hkv * 2 * w.P * w.D
     else:
         cap = escape_capacity(w, max(1, len(ids) * w.Hkv))
-    cache = kvz.Cache.allocate(w.P, w.Hkv, w.D, w.num_pages, w.B, cap, device=DEV, fmt=fmt)
+    cache = kvz.Cache.allocate(w.P, w.Hkv, w.D, num_pages or w.num_pages, w.B, cap, device=DEV, fmt=fmt)
     if len(ids):
         step = max(1, (1 << 30) // (w.Hkv * w.P * w.D * 2))      # ~1 GiB of each of K, V per copy
         for s in range(0, len(ids), step):

@@ -148,18 +148,25 @@ def _mixed_pages(w, light_pages):
 @pytest.mark.parametrize("Hq,Hkv", [(4, 4), (8, 2)])
 @pytest.mark.parametrize("P", [16, 32])
 @pytest.mark.parametrize("pps", [0, 64])
-def test_splits_from_inline_into_pool_units(Hq, Hkv, P, pps):
+@pytest.mark.parametrize("spare", [0, 3])
+def test_splits_from_inline_into_pool_units(Hq, Hkv, P, pps, spare):
     """Requests whose first pages are light (inline escapes) and whose later pages are escape-heavy
-    (pool lists): the main loop computes the light pages and skips the first heavy ones until most
-    tiles seen went to the pool; the wave then walks the rest of its split in the pool-capable loop
-    (which also meets light pages here: request 1 has some between heavy ones) and, after it, adds
-    the skipped heavy pages through the per-unit path. Multi-head and grouped-query kernels; one
-    split per row (64) or the device's choice (0)."""
+    (pool lists). With `spare` times the workload's unit slots in the cache, its pool holds less
+    than a quarter of a unit's values per slot, so the splits start in the pipelined loop: it
+    computes the light pages and skips the first heavy ones until most tiles seen went to the
+    pool; the wave then walks the rest of its split in the pool-capable loop (which also meets
+    light pages here: request 1 has some between heavy ones) and, after it, adds the skipped heavy
+    pages through the per-unit path (a split that starts on a heavy page goes to the pool-capable
+    loop at once). Without spare slots the cache counts as escape-heavy and every split starts in
+    the pool-capable loop. Multi-head and grouped-query kernels; one split per row (64) or the
+    device's choice (0)."""
     lens = np.array([24 * P + 5, 20 * P, 30 * P + 11])
     w = make_workload(5, n_append=0, B=3, lens=lens, Hq=Hq, Hkv=Hkv, D=128, P=P)
     light = [range(0, 3), list(range(0, 4)) + [9, 10, 15], range(0, 8)]
     kp, vp = _mixed_pages(w, light)
-    cache, lt = build_cache(w, kp, vp)
+    cache, lt = build_cache(w, kp, vp, num_pages=w.num_pages * (1 + spare))
+    heavy_cache = int(cache.esc_cursor.item()) >= cache.num_pages * Hkv * P * 128 // 2
+    assert heavy_cache == (spare == 0)
     units = cache.units.cpu().numpy()
     hdr = 2 * P * 2
     inline = [[bool((units[w.page_table[r, i], :, hdr + 8:hdr + 16].view(np.uint64) == (1 << 64) - 1).all())
