@@ -443,6 +443,8 @@ def read_ceiling(kvz, cache, table, lens, full, H, U, steps, dev, pair):
     import torch
 
     from decode_attention_losslessly_amd import kvz_bench
+    if U > 16384 or U % 16:
+        return None   # the read kernel holds a whole unit in registers: at most 16 KB
     B = int(lens.numel())
     rows = B * H
     cus = torch.cuda.get_device_properties(dev).multi_processor_count
