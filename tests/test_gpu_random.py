@@ -3,18 +3,20 @@ fp64 oracle within the stated tolerance: page sizes of one to four tiles, head d
 query groups from 1 to 16 heads, uneven lengths with empty requests and partial pages, the
 value distributions of all five workloads (the escape-stress one included, for the pool paths)
 and every kind of split choice (chosen on the device, fixed, and the ranked schedule forced).
+Each case also rebuilds its units bit for bit through every decode route of the kernels, and runs
+again over the same pages in ZipFusion's block format (multi-head or grouped-query kernel).
 Each case is drawn from its own seed, so a failure names a reproducible case."""
 import numpy as np
 import pytest
 import torch
 
 import decode_attention_losslessly_amd as kvz
-from kvz_testlib import DEV, build_cache, check_rows, dev, host16, oracle_rows
+from kvz_testlib import DEV, build_cache, check_rows, dev, full_page_ids, host16, oracle_rows
 from synth import make_workload
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 16
+N_CASES = 24
 
 
 def _case(seed):
@@ -56,3 +58,28 @@ def test_random_shapes_match_oracle(seed):
     torch.cuda.synchronize()
     assert int(status.item()) == 0, what
     check_rows(host16(out).reshape(-1, w.D), out32.cpu().numpy().reshape(-1, w.D), ref, what + " dense")
+    # the kernels' own decode of every full page, on every route of this head dim
+    ids = full_page_ids(w)
+    if len(ids):
+        for lane_map in ([0, 1, 2, 3] if w.D == 128 else [0, 2]):
+            kd = torch.zeros((len(ids), w.Hkv, w.P, w.D), dtype=torch.int16, device=DEV)
+            vd = torch.zeros_like(kd)
+            kvz.decompress_pages(cache, dev(ids), kd, vd, lane_map=lane_map)
+            torch.cuda.synchronize()
+            assert np.array_equal(host16(kd), kp[ids]) and np.array_equal(host16(vd), vp[ids]), f"{what} lane map {lane_map}"
+    # the same pages in ZipFusion's block format
+    zc, zl = build_cache(w, kp, vp, fmt=kvz.FORMAT_ZIPFUSION)
+    assert int(zc.status.item()) == 0, what
+    kvz.decode_attention(dev(q), zc, dev(w.page_table), zl, w.sm_scale, out, out32,
+                         pages_per_split=max(pps, 0))
+    torch.cuda.synchronize()
+    assert int(zc.status.item()) == 0, what
+    check_rows(host16(out).reshape(-1, w.D), out32.cpu().numpy().reshape(-1, w.D), ref, what + " zipfusion")
+    if len(ids):
+        for lane_map in ([0, 1] if w.D == 128 else [0]):
+            kd = torch.zeros((len(ids), w.Hkv, w.P, w.D), dtype=torch.int16, device=DEV)
+            vd = torch.zeros_like(kd)
+            kvz.decompress_pages(zc, dev(ids), kd, vd, lane_map=lane_map)
+            torch.cuda.synchronize()
+            assert np.array_equal(host16(kd), kp[ids]) and np.array_equal(host16(vd), vp[ids]), \
+                f"{what} zipfusion lane map {lane_map}"
