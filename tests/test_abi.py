@@ -130,6 +130,24 @@ def test_invalid_arguments_enqueue_nothing():
     assert kvz.kvz.strerror(binding.KVZ_ERR_WORKSPACE) == "workspace too small"
 
 
+def test_noalloc_checks_come_before_any_device_work():
+    L = binding.lib()
+    assert L.kvz_decode_attention_noalloc(None, None, None, 0, None, 0, 1, 1.0, 0, None, None, None) == \
+        binding.KVZ_ERR_INVALID_ARG
+    # a well-formed description (the pointers are never dereferenced on the host) whose call would
+    # need more than the library's scratch array: refused with KVZ_ERR_SCRATCH, nothing enqueued
+    fake = 256
+    cs = binding._CacheStruct(16, 32, 128, 1, 8, 0, fake, fake, 16, fake, fake, fake, fake)
+    need = kvz.workspace_bytes(8, 32, 32, 128, 16, 1024, 1)
+    assert need > binding.NOALLOC_SCRATCH_BYTES
+    rc = L.kvz_decode_attention_noalloc(fake, ctypes.byref(cs), fake, 1024, fake, 8, 32, 0.1, 1, fake, None, None)
+    assert rc == binding.KVZ_ERR_SCRATCH
+    assert "scratch" in kvz.kvz.strerror(binding.KVZ_ERR_SCRATCH)
+    # unsupported shapes are refused first
+    rc = L.kvz_decode_attention_noalloc(fake, ctypes.byref(cs), fake, 1024, fake, 8, 33, 0.1, 0, fake, None, None)
+    assert rc == binding.KVZ_ERR_UNSUPPORTED
+
+
 def test_cache_struct_layout_matches_header():
     # field order and sizes of kvz_cache: 6 int32, then pointers/int64 (8 bytes each)
     s = binding._CacheStruct
