@@ -88,13 +88,14 @@ def test_attention_matches_oracle(cfg):
         check_rows(host16(out).reshape(-1, w.D), out32.cpu().numpy().reshape(-1, w.D), ref, f"zf cfg{cfg} pps{pps}")
 
 
-@pytest.mark.parametrize("P,D", [(16, 128), (48, 128), (64, 64)])
-def test_mixed_units_and_page_fills(P, D):
-    # half the requests smooth (compressed blocks), half escape-stress (raw blocks); appends cross page fills
+@pytest.mark.parametrize("P,D,Hq", [(16, 128, 4), (48, 128, 4), (64, 64, 4), (16, 128, 16), (48, 128, 8)])
+def test_mixed_units_and_page_fills(P, D, Hq):
+    # half the requests smooth (compressed blocks), half escape-stress (raw blocks); appends cross
+    # page fills; 4 KV heads under 4 query heads (multi-head kernel) or 8 and 16 (grouped-query)
     n_steps = P + 3
     lens = np.array([3 * P - 2, P + 5, 2 * P, 4 * P + 7])
-    smooth = make_workload(1, B=4, lens=lens + n_steps, Hq=4, Hkv=4, D=D, P=P, n_append=0)
-    stress = make_workload(5, B=4, lens=lens + n_steps, Hq=4, Hkv=4, D=D, P=P, n_append=0)
+    smooth = make_workload(1, B=4, lens=lens + n_steps, Hq=Hq, Hkv=4, D=D, P=P, n_append=0)
+    stress = make_workload(5, B=4, lens=lens + n_steps, Hq=Hq, Hkv=4, D=D, P=P, n_append=0)
     kp, vp = smooth.pages(0), smooth.pages(1)
     ks, vs = stress.pages(0), stress.pages(1)
     odd = np.zeros(smooth.num_pages, bool)
@@ -124,7 +125,7 @@ def test_mixed_units_and_page_fills(P, D):
     full = full_page_ids(w)
     kd = torch.empty((len(full), w.Hkv, P, D), dtype=torch.int16, device=DEV)
     vd = torch.empty_like(kd)
-    kvz.decompress_pages(cache, dev(full), kd, vd)
+    kvz.decompress_pages(cache, dev(full), kd, vd, lane_map=1 if Hq > w.Hkv else 0)
     torch.cuda.synchronize()
     assert np.array_equal(host16(kd), kp[full]) and np.array_equal(host16(vd), vp[full])
     q = w.q()

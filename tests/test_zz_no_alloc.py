@@ -72,3 +72,36 @@ def test_noalloc_refuses_more_than_its_scratch():
     assert e.value.code == kvz.kvz.KVZ_ERR_SCRATCH
     torch.cuda.synchronize()
     assert bool((out == 7).all()) and int(cache.status.item()) == 0      # nothing was enqueued
+
+
+def test_noalloc_under_graph_capture():
+    """The caller this entry point is for: a decode step captured in a HIP graph. One eager call
+    first (the library takes the array's device address there), then the captured call replayed
+    three times with eager work between the replays; every replay equals the workspace call."""
+    w = make_workload(3, B=3, L=161, Hq=8, Hkv=8, n_append=0)
+    kp, vp = w.pages(0), w.pages(1)
+    cache, lens = build_cache(w, kp, vp)
+    q, table = dev(w.q()), dev(w.page_table)
+    shape = (w.B, w.Hq, w.D)
+    want16, want32 = torch.zeros(shape, dtype=torch.int16, device=DEV), torch.zeros(shape, device=DEV)
+    kvz.decode_attention(q, cache, table, lens, w.sm_scale, want16, want32)
+    out16, out32 = torch.zeros_like(want16), torch.zeros_like(want32)
+    kvz.decode_attention_noalloc(q, cache, table, lens, w.sm_scale, out16, out32)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            kvz.decode_attention_noalloc(q, cache, table, lens, w.sm_scale, out16, out32)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    other16, other32 = torch.zeros_like(want16), torch.zeros_like(want32)
+    for rep in range(3):
+        out16.zero_()
+        out32.zero_()
+        graph.replay()
+        kvz.decode_attention_noalloc(q, cache, table, lens, w.sm_scale, other16, other32)   # eager, same array
+        torch.cuda.synchronize()
+        assert torch.equal(out16, want16) and torch.equal(out32.view(torch.int32), want32.view(torch.int32)), rep
+        assert torch.equal(other16, want16), rep
