@@ -26,9 +26,15 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-mcode-object-
          "-I", CSRC, "-I", os.path.join(ROOT, "include")]
 
 
-def _compile(src: str, verbose: bool) -> str:
-    obj = os.path.join(BUILD, src + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+# Host code only (the C-ABI validation and launch code) under AddressSanitizer and
+# UndefinedBehaviorSanitizer, every report fatal: each flag applies to the host pass alone.
+SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+            "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def _compile(src: str, verbose: bool, build_dir: str = BUILD, extra=()) -> str:
+    obj = os.path.join(build_dir, src + ".o")
+    cmd = [HIPCC, *FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -41,8 +47,8 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def _link(objs, out: str, verbose: bool) -> None:
-    cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", out + ".tmp"]
+def _link(objs, out: str, verbose: bool, extra=()) -> None:
+    cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *extra, *objs, "-o", out + ".tmp"]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
@@ -57,6 +63,25 @@ def build(verbose: bool = False) -> str:
     _link([objs[s] for s in SOURCES], OUT, verbose)
     _link([objs[s] for s in BENCH_SOURCES], BENCH_OUT, verbose)
     return OUT
+
+
+def build_sanitized(out: str, verbose: bool = False) -> str:
+    """libkvz with its host code under ASan and UBSan, at `out` (for the CPU test of the C-ABI host
+    code; a process that loads it must preload sanitizer_runtime())."""
+    build_dir = os.path.join(os.path.dirname(out), "_build_sanitized")
+    os.makedirs(build_dir, exist_ok=True)
+    with ThreadPoolExecutor(min(8, len(SOURCES))) as ex:
+        objs = list(ex.map(lambda s: _compile(s, verbose, build_dir, SANITIZE), SOURCES))
+    _link(objs, out, verbose, ["-shared-libasan", "-fsanitize=address,undefined"])
+    return out
+
+
+def sanitizer_runtime() -> str:
+    """hipcc's (clang's) AddressSanitizer runtime, to preload into a process that loads a
+    sanitized libkvz."""
+    r = subprocess.run([HIPCC, "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True,
+                       check=True)
+    return r.stdout.strip()
 
 
 if __name__ == "__main__":

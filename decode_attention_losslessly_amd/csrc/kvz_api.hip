@@ -62,10 +62,10 @@ namespace {
 constexpr int kTargetItems = 4096;   // splits aimed for: ~16 waves per CU on 256 CUs
 constexpr int kGqaRows = 8;          // query heads per grouped-query wave
 
-int work_items_per_split(int B, int Hq, int Hkv) {
+int64_t work_items_per_split(int B, int Hq, int Hkv) {
   const int grp = Hq / Hkv;
-  const int chunks = grp > 1 ? (grp + kGqaRows - 1) / kGqaRows : 1;
-  return B * Hkv * chunks;
+  const int64_t chunks = grp > 1 ? ((int64_t)grp + kGqaRows - 1) / kGqaRows : 1;
+  return (int64_t)B * Hkv * chunks;
 }
 
 // Pages per split: `pps` when the caller fixes it, else the smallest the kernels may choose.
@@ -75,16 +75,16 @@ int work_items_per_split(int B, int Hq, int Hkv) {
 // items, and a split to at least 64 tokens.
 int pages_per_split(int B, int Hq, int Hkv, int P, int max_pages, int pps) {
   if (pps > 0) return pps;   // (pps < 0 asks for the ranked schedule; this bound is then unused by it)
-  const long items = work_items_per_split(B, Hq, Hkv);
-  const long s_cap = items >= 2 * kTargetItems ? 1 : (2 * kTargetItems + items - 1) / items;
+  const int64_t items = work_items_per_split(B, Hq, Hkv);
+  const int64_t s_cap = items >= 2 * kTargetItems ? 1 : (2 * kTargetItems + items - 1) / items;
   const int min_c = P >= 64 ? 1 : 64 / P;
-  long c = (max_pages + s_cap - 1) / s_cap;
+  int64_t c = ((int64_t)max_pages + s_cap - 1) / s_cap;
   if (c < min_c) c = min_c;
   if (c < 1) c = 1;
   return (int)c;
 }
 
-int split_count(int max_pages, int C) { return max_pages > 0 ? (max_pages + C - 1) / C : 1; }
+int split_count(int max_pages, int C) { return max_pages > 0 ? (int)(((int64_t)max_pages + C - 1) / C) : 1; }
 
 // Big ranks R of the ranked schedule (0: not used), which the multi-head kernels over the
 // escape format and the uncompressed baseline may use: the first round of kTargetItems
@@ -104,7 +104,7 @@ constexpr int kMaxForcedRanks = 4096;
 int rank_count(int B, int Hq, int Hkv, int max_pages, int pps) {
   if (pps < 0) return -pps;
   if (pps > 0 || Hq != Hkv) return 0;
-  const long items = (long)B * Hkv;
+  const int64_t items = (int64_t)B * Hkv;
   if (items >= 2 * kTargetItems) return 0;
   const int R = items >= kTargetItems ? 1 : (int)(kTargetItems / items);
   if ((uint64_t)max_pages * kvz::kRankBig * 2 < (uint64_t)kRankMinPages * R * kvz::kRankOne) return 0;
@@ -119,7 +119,11 @@ int slot_count(int B, int Hq, int Hkv, int P, int max_pages, int pps) {
   return n > S ? n : S;
 }
 
-bool shape_ok(int P, int D) { return P > 0 && P % 16 == 0 && D > 0 && D % 64 == 0; }
+// the format's shapes: an inline escape keeps its storage position in 16 bits, so a block holds at
+// most 65536 values
+bool shape_ok(int P, int D) {
+  return P > 0 && P % 16 == 0 && D > 0 && D % 64 == 0 && (int64_t)P * D <= 65536;
+}
 
 bool cache_ok(const kvz_cache* c) {
   return c && c->units && c->status && shape_ok(c->page_size, c->head_dim) && c->num_kv_heads > 0 &&
@@ -182,9 +186,16 @@ int32_t kvz_num_splits(int32_t B, int32_t H_q, int32_t H_kv, int32_t D, int32_t 
 }
 
 // workspace: per (request, query head, split) acc[D] and (m, l) as float, then one 16-byte slot
-// where the split kernel records the pages per split it used
+// where the split kernel records the pages per split it used. ws_bytes is 0 when the size does
+// not fit in size_t (arguments validated by the caller: all positive).
 static size_t ws_partial_bytes(int B, int Hq, int S, int D) { return (size_t)B * Hq * S * (D + 2) * sizeof(float); }
-static size_t ws_bytes(int B, int Hq, int S, int D) { return ws_partial_bytes(B, Hq, S, D) + 16; }
+static size_t ws_bytes(int B, int Hq, int S, int D) {
+  size_t n = (size_t)B;
+  if (__builtin_mul_overflow(n, (size_t)Hq, &n) || __builtin_mul_overflow(n, (size_t)S, &n) ||
+      __builtin_mul_overflow(n, (size_t)(D + 2) * sizeof(float), &n) || __builtin_add_overflow(n, (size_t)16, &n))
+    return 0;
+  return n;
+}
 static int32_t* ws_chosen(void* ws, int B, int Hq, int S, int D) {
   return reinterpret_cast<int32_t*>(static_cast<char*>(ws) + ws_partial_bytes(B, Hq, S, D));
 }
@@ -203,7 +214,7 @@ static kvz::SplitPlan make_plan(int C, int S, int max_pages, bool fixed, int32_t
 size_t kvz_workspace_bytes(int32_t B, int32_t H_q, int32_t H_kv, int32_t D, int32_t P, int32_t max_pages_per_seq,
                            int32_t pps) {
   const int S = kvz_num_splits(B, H_q, H_kv, D, P, max_pages_per_seq, pps);
-  return ws_bytes(B, H_q, S, D);
+  return S > 0 ? ws_bytes(B, H_q, S, D) : 0;
 }
 
 int kvz_compress_pages(const kvz_cache* c, const uint16_t* k_src, const uint16_t* v_src, const int32_t* ids,
@@ -250,6 +261,7 @@ int kvz_decode_attention_splits(const uint16_t* q, const kvz_cache* c, const int
   if (B > c->max_batch) return KVZ_ERR_INVALID_ARG;
   const int C = pages_per_split(B, H_q, H, P, max_pages, pps);
   const int S = slot_count(B, H_q, H, P, max_pages, pps);
+  if (ws_bytes(B, H_q, S, D) == 0) return KVZ_ERR_INVALID_ARG;
   if (workspace_bytes < ws_bytes(B, H_q, S, D)) return KVZ_ERR_WORKSPACE;
   float* ws_acc = reinterpret_cast<float*>(workspace);
   float* ws_ml = ws_acc + (size_t)B * H_q * S * D;
@@ -289,6 +301,7 @@ int kvz_decode_attention_dense_splits(const uint16_t* q, const uint16_t* k_pages
     return KVZ_ERR_INVALID_ARG;
   const int C = pages_per_split(B, H_q, H, P, max_pages, pps);
   const int S = slot_count(B, H_q, H, P, max_pages, pps);
+  if (ws_bytes(B, H_q, S, D) == 0) return KVZ_ERR_INVALID_ARG;
   if (workspace_bytes < ws_bytes(B, H_q, S, D)) return KVZ_ERR_WORKSPACE;
   float* ws_acc = reinterpret_cast<float*>(workspace);
   float* ws_ml = ws_acc + (size_t)B * H_q * S * D;
@@ -314,6 +327,7 @@ int kvz_merge_splits(const void* workspace, size_t workspace_bytes, const int32_
   if (B == 0) return KVZ_OK;
   if (!workspace || !seq_lens || !out || pps < -kMaxForcedRanks) return KVZ_ERR_INVALID_ARG;
   const int S = slot_count(B, H_q, H, P, max_pages, pps);
+  if (ws_bytes(B, H_q, S, D) == 0) return KVZ_ERR_INVALID_ARG;
   if (workspace_bytes < ws_bytes(B, H_q, S, D)) return KVZ_ERR_WORKSPACE;
   const float* ws_acc = reinterpret_cast<const float*>(workspace);
   const float* ws_ml = ws_acc + (size_t)B * H_q * S * D;
@@ -342,9 +356,10 @@ int kvz_decode_attention_noalloc(const uint16_t* q, const kvz_cache* c, const in
   const int rc = check_attention_shape(B, H_q, c->num_kv_heads, c->head_dim, c->page_size, max_pages);
   if (rc) return rc;
   if (pps < -kMaxForcedRanks) return KVZ_ERR_INVALID_ARG;
-  const size_t need = kvz_workspace_bytes(B, H_q, c->num_kv_heads, c->head_dim, c->page_size, max_pages, pps);
-  if (need > KVZ_NOALLOC_SCRATCH_BYTES) return KVZ_ERR_SCRATCH;
   if (B == 0) return KVZ_OK;
+  const size_t need = kvz_workspace_bytes(B, H_q, c->num_kv_heads, c->head_dim, c->page_size, max_pages, pps);
+  if (need == 0) return KVZ_ERR_INVALID_ARG;
+  if (need > KVZ_NOALLOC_SCRATCH_BYTES) return KVZ_ERR_SCRATCH;
   void* ws = scratch_on_current_device();
   if (!ws) return KVZ_ERR_HIP;
   return kvz_decode_attention(q, c, page_table, max_pages, seq_lens, B, H_q, sm_scale, pps, out, out_f32, ws,

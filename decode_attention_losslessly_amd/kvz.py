@@ -13,7 +13,8 @@ from dataclasses import dataclass
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libkvz.so")
+# KVZ_LIB names another build of the same sources (the host-sanitized one of the tests)
+LIB_PATH = os.environ.get("KVZ_LIB") or os.path.join(_HERE, "libkvz.so")
 
 KVZ_OK, KVZ_ERR_INVALID_ARG, KVZ_ERR_UNSUPPORTED, KVZ_ERR_WORKSPACE, KVZ_ERR_HIP, KVZ_ERR_SCRATCH = 0, -1, -2, -3, -4, -5
 NOALLOC_SCRATCH_BYTES = 32 << 20   # KVZ_NOALLOC_SCRATCH_BYTES
