@@ -158,15 +158,17 @@ int32_t kvz_inline_capacity(int32_t P, int32_t D);
  *   pages_per_split < 0  asks the multi-head kernels for the ranked schedule with
  *                        R = -pages_per_split (at most 4096); the grouped-query kernels then
  *                        choose as with 0.
- * The same value must be passed to the attention call. Returns 0 for arguments the attention
- * calls reject (B, H_q or H_kv not positive, H_q not a multiple of H_kv, an unsupported P or D,
- * max_pages_per_seq < 0, pages_per_split < -4096) and when the size does not fit in size_t;
- * the attention calls then return KVZ_ERR_INVALID_ARG. */
+ * The same value must be passed to the attention call. Returns 0 when B = 0 (an attention call
+ * over an empty batch reads no workspace), for arguments the attention calls reject (B < 0, H_q
+ * or H_kv not positive, H_q not a multiple of H_kv, an unsupported P or D, max_pages_per_seq < 0,
+ * pages_per_split < -4096), and when the size does not fit in size_t, which the attention calls
+ * reject with KVZ_ERR_INVALID_ARG. */
 size_t kvz_workspace_bytes(int32_t B, int32_t H_q, int32_t H_kv, int32_t D, int32_t P,
                            int32_t max_pages_per_seq, int32_t pages_per_split);
 
 /* Split slots per (request, query head) in the workspace: the most splits an attention call
- * with these arguments can use (host function); 0 for the arguments kvz_workspace_bytes rejects. */
+ * with these arguments can use (host function); 0 for B = 0 and for rejected arguments, as
+ * kvz_workspace_bytes. */
 int32_t kvz_num_splits(int32_t B, int32_t H_q, int32_t H_kv, int32_t D, int32_t P,
                        int32_t max_pages_per_seq, int32_t pages_per_split);
 
