@@ -426,6 +426,7 @@ def main() -> int:
         "append_fill_us": round(append_fill_us, 1) if append_fill_us is not None else None,
         "compress_gbps_dense_input": round(len(ids) * H * P * D * 4 / compress_s / 1e9, 1),
         "gpu": f"{torch.cuda.get_device_name(0)} ({torch.cuda.get_device_properties(0).gcnArchName})",
+        "software": {"torch": torch.__version__, "hip": torch.version.hip},
         "source_digest": source_digest(ksrc),
     }
     print(json.dumps(res), flush=True)

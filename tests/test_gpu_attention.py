@@ -70,7 +70,7 @@ def test_dense_matches_oracle(cfg):
 
 
 @pytest.mark.parametrize("cfg", [2, 4])
-def test_split_count_and_page_order_do_not_change_the_result(cfg):
+def test_split_count_does_not_change_the_result_and_runs_repeat(cfg):
     w = make_workload(cfg, **SMALL[cfg])
     kp, vp = w.pages(0), w.pages(1)
     cache, lens = build_cache(w, kp, vp)
@@ -83,6 +83,48 @@ def test_split_count_and_page_order_do_not_change_the_result(cfg):
     again16, again32 = _run(w, cache, lens, q)
     assert np.array_equal(again32.view(np.uint32), base32.view(np.uint32))    # repeatable bit for bit
     assert np.array_equal(again16, base16)
+
+
+def _run_table(w, cache, lens, q, table, fmt_pps=0):
+    out = torch.zeros((w.B, w.Hq, w.D), dtype=torch.int16, device=DEV)
+    out32 = torch.full((w.B, w.Hq, w.D), float("nan"), dtype=torch.float32, device=DEV)
+    kvz.decode_attention(dev(q), cache, dev(table), lens, w.sm_scale, out, out32, pages_per_split=fmt_pps)
+    torch.cuda.synchronize()
+    assert int(cache.status.item()) == 0
+    return host16(out), out32.cpu().numpy()
+
+
+@pytest.mark.parametrize("cfg,fmt", [(2, kvz.FORMAT_ESCAPE), (4, kvz.FORMAT_ESCAPE), (5, kvz.FORMAT_ESCAPE),
+                                     (6, kvz.FORMAT_ESCAPE), (4, kvz.FORMAT_ZIPFUSION)])
+def test_unit_placement_and_token_order(cfg, fmt):
+    """Moving every unit to another slot (the page table follows it; pool offsets inside the units
+    stay valid) gives the same result bit for bit: the kernels depend on a page's slot only for its
+    address. Shuffling the order of each request's full pages in the page table permutes its
+    tokens, which attention does not see: the result moves by fp32 rounding order only."""
+    w = make_workload(cfg, **SMALL[cfg])
+    kp, vp = w.pages(0), w.pages(1)
+    cache, lens = build_cache(w, kp, vp, fmt=fmt)
+    q = w.q()
+    base16, base32 = _run_table(w, cache, lens, q, w.page_table)
+    rng = np.random.default_rng(11)
+    perm = rng.permutation(w.num_pages).astype(np.int32)          # slot pid moves to perm[pid]
+    moved = cache.units[torch.from_numpy(np.argsort(perm)).to(DEV)].clone()
+    cache.units.copy_(moved)
+    ok = (w.page_table >= 0) & (w.page_table < w.num_pages)
+    table = np.where(ok, perm[np.clip(w.page_table, 0, w.num_pages - 1)], w.page_table).astype(np.int32)
+    m16, m32 = _run_table(w, cache, lens, q, table)
+    assert np.array_equal(m32.view(np.uint32), base32.view(np.uint32)) and np.array_equal(m16, base16)
+    shuffled = table.copy()
+    L = lens.cpu().numpy()
+    for r in range(w.B):
+        nfull = int(L[r]) // w.P
+        shuffled[r, :nfull] = table[r, rng.permutation(nfull)]
+    ref = oracle_rows(w, kp, vp, q, _all_rows(w))      # over the tokens in their original order
+    for pps in (0, 1):
+        s16, s32 = _run_table(w, cache, lens, q, shuffled, pps)
+        nrm = np.abs(base32).max(axis=-1, keepdims=True)
+        assert np.all(np.abs(s32 - base32) <= 1e-5 * nrm), pps
+        check_rows(s16.reshape(-1, w.D), s32.reshape(-1, w.D), ref, f"cfg {cfg} fmt {fmt} shuffled pages, pps {pps}")
 
 
 @pytest.mark.parametrize("cfg", [1, 2, 3, 5])
