@@ -125,6 +125,9 @@ bool shape_ok(int P, int D) {
   return P > 0 && P % 16 == 0 && D > 0 && D % 64 == 0 && (int64_t)P * D <= 65536;
 }
 
+// the kernels hold a request's length, at most max_pages * P tokens, in 32 bits
+bool table_fits(int max_pages, int P) { return (int64_t)max_pages * P <= INT32_MAX; }
+
 bool cache_ok(const kvz_cache* c) {
   return c && c->units && c->status && shape_ok(c->page_size, c->head_dim) && c->num_kv_heads > 0 &&
          c->num_pages >= 0 && c->max_batch >= 0 && c->esc_capacity >= 0 && c->esc_cursor &&
@@ -230,6 +233,7 @@ int kvz_compress_pages(const kvz_cache* c, const uint16_t* k_src, const uint16_t
 int kvz_append_token(const kvz_cache* c, const uint16_t* k_new, const uint16_t* v_new, const int32_t* page_table,
                      int32_t max_pages, int32_t* seq_lens, int32_t B, void* stream) {
   if (!cache_ok(c) || B < 0 || max_pages < 0 || !c->k_tail || !c->v_tail) return KVZ_ERR_INVALID_ARG;
+  if (!table_fits(max_pages, c->page_size)) return KVZ_ERR_UNSUPPORTED;
   if (B > 0 && (!k_new || !v_new || !page_table || !seq_lens)) return KVZ_ERR_INVALID_ARG;
   if (B > c->max_batch) return KVZ_ERR_INVALID_ARG;
   if ((size_t)c->page_size * c->head_dim > 32768) return KVZ_ERR_UNSUPPORTED;
@@ -241,7 +245,7 @@ int kvz_append_token(const kvz_cache* c, const uint16_t* k_new, const uint16_t* 
 
 static int check_attention_shape(int B, int Hq, int Hkv, int D, int P, int max_pages) {
   if (B < 0 || Hq <= 0 || Hkv <= 0 || max_pages < 0) return KVZ_ERR_INVALID_ARG;
-  if (!shape_ok(P, D) || Hq % Hkv) return KVZ_ERR_UNSUPPORTED;
+  if (!shape_ok(P, D) || Hq % Hkv || !table_fits(max_pages, P)) return KVZ_ERR_UNSUPPORTED;
   if (D != 64 && D != 128) return KVZ_ERR_UNSUPPORTED;
   const int grp = Hq / Hkv;
   if (grp > 1 && (D != 128 || grp > 16)) return KVZ_ERR_UNSUPPORTED;

@@ -62,7 +62,7 @@ extern "C" int kvzb_read_units(const uint8_t* units, int32_t num_pages, size_t u
                                int32_t max_pages, const int32_t* seq_lens, int32_t B, int32_t H, int32_t P,
                                int32_t chunks, uint32_t* sink, void* stream) {
   if (!units || !page_table || !seq_lens || !sink || num_pages <= 0 || B < 0 || H <= 0 || P <= 0 || max_pages < 0 ||
-      chunks <= 0 || unit_bytes == 0 || unit_bytes % 16 || unit_bytes > 16384)
+      chunks <= 0 || unit_bytes == 0 || unit_bytes % 16 || unit_bytes > 16384 || (long)max_pages * P > INT32_MAX)
     return KVZ_ERR_INVALID_ARG;
   const long waves = (long)B * H * chunks;
   if (waves == 0) return KVZ_OK;

@@ -190,8 +190,9 @@ int kvz_compress_pages(const kvz_cache* cache, const uint16_t* k_src, const uint
  *   k_new, v_new   [B][H][D] raw BF16
  *   page_table     [B][max_pages_per_seq]
  *   seq_lens       [B], updated on the device
- * B must not exceed max_batch. Errors: KVZ_ERR_INVALID_ARG, KVZ_ERR_UNSUPPORTED. Device status:
- * ESC_POOL_FULL, BAD_PAGE_ID, SEQ_TOO_LONG (no write). */
+ * B must not exceed max_batch; max_pages_per_seq * P must fit in int32 (a request's length is
+ * held in 32 bits), else KVZ_ERR_UNSUPPORTED. Errors: KVZ_ERR_INVALID_ARG, KVZ_ERR_UNSUPPORTED.
+ * Device status: ESC_POOL_FULL, BAD_PAGE_ID, SEQ_TOO_LONG (no write). */
 int kvz_append_token(const kvz_cache* cache, const uint16_t* k_new, const uint16_t* v_new,
                      const int32_t* page_table, int32_t max_pages_per_seq, int32_t* seq_lens,
                      int32_t B, void* stream);
@@ -204,7 +205,8 @@ int kvz_append_token(const kvz_cache* cache, const uint16_t* k_new, const uint16
  *   out          [B][H_q][D] BF16 (round to nearest even); a request with no token gets zeros
  *   out_f32      nullable [B][H_q][D] float, the same result before rounding
  *   workspace    >= kvz_workspace_bytes(B, H_q, H, D, P, max_pages_per_seq, pages_per_split)
- * Supported: D in {64, 128}; for H_q > H (grouped queries) D = 128 and H_q / H <= 16.
+ * Supported: D in {64, 128}; for H_q > H (grouped queries) D = 128 and H_q / H <= 16;
+ * max_pages_per_seq * P within int32 (as for kvz_append_token).
  * Errors: KVZ_ERR_INVALID_ARG, KVZ_ERR_UNSUPPORTED, KVZ_ERR_WORKSPACE. Device status:
  * BAD_PAGE_ID, SEQ_TOO_LONG. */
 int kvz_decode_attention(const uint16_t* q, const kvz_cache* cache, const int32_t* page_table,

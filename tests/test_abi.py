@@ -128,6 +128,23 @@ def test_invalid_arguments_enqueue_nothing():
     assert rc == binding.KVZ_ERR_UNSUPPORTED       # group of 32 > 16
     assert L.kvz_compact_pool(None, None, 0, None, 0, None, None) == binding.KVZ_ERR_INVALID_ARG
     assert kvz.kvz.strerror(binding.KVZ_ERR_WORKSPACE) == "workspace too small"
+    # a page table whose width times P overflows a 32-bit length
+    wide = (1 << 31) // 16
+    rc = L.kvz_decode_attention_dense(None, None, None, 0, 4, 128, 16, None, wide, None, 1, 4, 1.0, 0, None, None,
+                                      None, 0, None, None)
+    assert rc == binding.KVZ_ERR_UNSUPPORTED
+    fake = 256
+    cs = binding._CacheStruct(16, 4, 128, 1, 8, 0, fake, fake, 16, fake, fake, fake, fake)
+    assert L.kvz_append_token(ctypes.byref(cs), fake, fake, fake, wide, fake, 1, None) == binding.KVZ_ERR_UNSUPPORTED
+    assert L.kvz_decode_attention(fake, ctypes.byref(cs), fake, wide, fake, 1, 4, 0.1, 0, fake, None, fake, 1 << 40,
+                                  None) == binding.KVZ_ERR_UNSUPPORTED
+    # a workspace that does not fit in size_t: zero size, and the call refuses it
+    big = (1 << 31) - 1
+    assert kvz.workspace_bytes(big, 1024, 1024, 128, 16, 1 << 20, 1) == 0
+    huge = binding._CacheStruct(16, 1024, 128, 1, big, 0, fake, fake, 16, fake, fake, fake, fake)
+    rc = L.kvz_decode_attention_splits(fake, ctypes.byref(huge), fake, 1 << 20, fake, big, 1024, 0.1, 1, fake,
+                                       (1 << 64) - 1, None)
+    assert rc == binding.KVZ_ERR_INVALID_ARG
 
 
 def test_noalloc_checks_come_before_any_device_work():
