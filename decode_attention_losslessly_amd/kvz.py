@@ -91,8 +91,39 @@ def strerror(code: int) -> str:
 def _ptr(t: torch.Tensor | None):
     if t is None:
         return None
-    assert t.is_contiguous(), "tensors passed to libkvz must be contiguous"
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to libkvz must be contiguous")
     return ctypes.c_void_p(t.data_ptr())
+
+
+_HALF = (torch.int16, torch.bfloat16)   # BF16 values, as bits or as bfloat16
+
+
+def _arg(t: torch.Tensor | None, name: str, dtypes, numel: int, device) -> None:
+    """Checks a device buffer the library reads or writes: its type, that it holds at least `numel`
+    elements (the library touches exactly that many) and that it is on the call's device, so that
+    a wrong argument raises here instead of being read or written past its end."""
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name}: dtype {t.dtype}, expected one of {dtypes}")
+    if t.numel() < numel:
+        raise ValueError(f"{name}: {t.numel()} elements, the call needs {numel}")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, the call runs on {device}")
+
+
+def _on(t: torch.Tensor | None, name: str, device) -> None:
+    if t is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, the call runs on {device}")
+
+
+def _table(page_table: torch.Tensor, B: int, device) -> int:
+    """max_pages of a [B, max_pages] int32 page table"""
+    if page_table.dim() != 2 or page_table.shape[0] < B:
+        raise ValueError(f"page_table: shape {tuple(page_table.shape)}, expected [>= {B}, max_pages]")
+    _arg(page_table, "page_table", (torch.int32,), 0, device)
+    return int(page_table.shape[1])
 
 
 def _stream(stream) -> ctypes.c_void_p:
@@ -191,10 +222,39 @@ class Cache:
 
 
 # ---------------------------------------------------------------- entry points
+def _io(q, page_table, seq_lens, out, out_f32, device) -> int:
+    """Checks an attention call's query, table, lengths and outputs; returns max_pages."""
+    if q.dim() != 3:
+        raise ValueError(f"q: shape {tuple(q.shape)}, expected [B, H_q, D]")
+    B, Hq, D = q.shape
+    _arg(q, "q", _HALF, 0, device)
+    max_pages = _table(page_table, B, device)
+    _arg(seq_lens, "seq_lens", (torch.int32,), B, device)
+    if out is not None:
+        _arg(out, "out", _HALF, B * Hq * D, device)
+    if out_f32 is not None:
+        _arg(out_f32, "out_f32", (torch.float32,), B * Hq * D, device)
+    return max_pages
+
+
+def _dense_pages(k_pages, v_pages, status, device) -> None:
+    if k_pages.dim() != 4 or v_pages.shape != k_pages.shape:
+        raise ValueError(f"k_pages, v_pages: shapes {tuple(k_pages.shape)}, {tuple(v_pages.shape)}, "
+                         "expected two equal [num_pages, H, P, D]")
+    _arg(k_pages, "k_pages", _HALF, 0, device)
+    _arg(v_pages, "v_pages", _HALF, 0, device)
+    if status is not None:
+        _arg(status, "status", (torch.int32,), 1, device)
+
+
 def compress_pages(cache: Cache, k_src: torch.Tensor, v_src: torch.Tensor, dst_page_ids: torch.Tensor,
                    stream=None) -> None:
     """k_src, v_src: int16 [n, H, P, D]; dst_page_ids: int32 [n]."""
     n = int(dst_page_ids.numel())
+    dev, blk = cache.units.device, n * cache.H * cache.P * cache.D
+    _arg(k_src, "k_src", _HALF, blk, dev)
+    _arg(v_src, "v_src", _HALF, blk, dev)
+    _arg(dst_page_ids, "dst_page_ids", (torch.int32,), n, dev)
     cs = cache.struct()
     _check(lib().kvz_compress_pages(ctypes.byref(cs), _ptr(k_src), _ptr(v_src), _ptr(dst_page_ids), n,
                                     _stream(stream)), "kvz_compress_pages")
@@ -203,7 +263,12 @@ def compress_pages(cache: Cache, k_src: torch.Tensor, v_src: torch.Tensor, dst_p
 def append_token(cache: Cache, k_new: torch.Tensor, v_new: torch.Tensor, page_table: torch.Tensor,
                  seq_lens: torch.Tensor, stream=None) -> None:
     """k_new, v_new: int16 [B, H, D]; page_table int32 [B, max_pages]; seq_lens int32 [B] (updated)."""
-    B, max_pages = page_table.shape
+    dev = cache.units.device
+    B = int(page_table.shape[0])
+    max_pages = _table(page_table, B, dev)
+    _arg(k_new, "k_new", _HALF, B * cache.H * cache.D, dev)
+    _arg(v_new, "v_new", _HALF, B * cache.H * cache.D, dev)
+    _arg(seq_lens, "seq_lens", (torch.int32,), B, dev)
     cs = cache.struct()
     _check(lib().kvz_append_token(ctypes.byref(cs), _ptr(k_new), _ptr(v_new), _ptr(page_table), max_pages,
                                   _ptr(seq_lens), B, _stream(stream)), "kvz_append_token")
@@ -214,7 +279,8 @@ def decode_attention(q: torch.Tensor, cache: Cache, page_table: torch.Tensor, se
                      workspace: torch.Tensor | None = None, pages_per_split: int = 0, stream=None) -> None:
     """q, out: int16 [B, Hq, D] (BF16 bits); out_f32 optional float32 [B, Hq, D]."""
     B, Hq, D = q.shape
-    max_pages = page_table.shape[1]
+    max_pages = _io(q, page_table, seq_lens, out, out_f32, cache.units.device)
+    _on(workspace, "workspace", cache.units.device)
     if workspace is None:
         workspace = _scratch(workspace_bytes(B, Hq, cache.H, D, cache.P, max_pages, pages_per_split), q.device, stream)
     cs = cache.struct()
@@ -230,8 +296,9 @@ def decode_attention_noalloc(q: torch.Tensor, cache: Cache, page_table: torch.Te
     """decode_attention with its workspace in the library's own per-GPU scratch array: nothing is
     allocated, here or in the library (for callers that cannot allocate device memory)."""
     B, Hq, D = q.shape
+    max_pages = _io(q, page_table, seq_lens, out, out_f32, cache.units.device)
     cs = cache.struct()
-    _check(lib().kvz_decode_attention_noalloc(_ptr(q), ctypes.byref(cs), _ptr(page_table), page_table.shape[1],
+    _check(lib().kvz_decode_attention_noalloc(_ptr(q), ctypes.byref(cs), _ptr(page_table), max_pages,
                                               _ptr(seq_lens), B, Hq, float(sm_scale), pages_per_split, _ptr(out),
                                               _ptr(out_f32), _stream(stream)), "kvz_decode_attention_noalloc")
 
@@ -243,7 +310,9 @@ def decode_attention_dense(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torc
     """k_pages, v_pages: int16 [num_pages, H, P, D]; other arguments as decode_attention."""
     B, Hq, D = q.shape
     num_pages, H, P, _ = k_pages.shape
-    max_pages = page_table.shape[1]
+    max_pages = _io(q, page_table, seq_lens, out, out_f32, q.device)
+    _dense_pages(k_pages, v_pages, status, q.device)
+    _on(workspace, "workspace", q.device)
     if workspace is None:
         workspace = _scratch(workspace_bytes(B, Hq, H, D, P, max_pages, pages_per_split), q.device, stream)
     _check(lib().kvz_decode_attention_dense(_ptr(q), _ptr(k_pages), _ptr(v_pages), num_pages, H, D, P,
@@ -257,8 +326,10 @@ def decode_attention_splits(q: torch.Tensor, cache: Cache, page_table: torch.Ten
                             sm_scale: float, workspace: torch.Tensor, pages_per_split: int = 0, stream=None) -> None:
     """First phase of decode_attention: the split kernel, partials into `workspace`."""
     B, Hq, D = q.shape
+    max_pages = _io(q, page_table, seq_lens, None, None, cache.units.device)
+    _on(workspace, "workspace", cache.units.device)
     cs = cache.struct()
-    _check(lib().kvz_decode_attention_splits(_ptr(q), ctypes.byref(cs), _ptr(page_table), page_table.shape[1],
+    _check(lib().kvz_decode_attention_splits(_ptr(q), ctypes.byref(cs), _ptr(page_table), max_pages,
                                              _ptr(seq_lens), B, Hq, float(sm_scale), pages_per_split,
                                              _ptr(workspace), workspace.numel() * workspace.element_size(),
                                              _stream(stream)), "kvz_decode_attention_splits")
@@ -270,8 +341,11 @@ def decode_attention_dense_splits(q: torch.Tensor, k_pages: torch.Tensor, v_page
                                   pages_per_split: int = 0, stream=None) -> None:
     B, Hq, D = q.shape
     num_pages, H, P, _ = k_pages.shape
+    max_pages = _io(q, page_table, seq_lens, None, None, q.device)
+    _dense_pages(k_pages, v_pages, status, q.device)
+    _on(workspace, "workspace", q.device)
     _check(lib().kvz_decode_attention_dense_splits(_ptr(q), _ptr(k_pages), _ptr(v_pages), num_pages, H, D, P,
-                                                   _ptr(page_table), page_table.shape[1], _ptr(seq_lens), B, Hq,
+                                                   _ptr(page_table), max_pages, _ptr(seq_lens), B, Hq,
                                                    float(sm_scale), pages_per_split, _ptr(workspace),
                                                    workspace.numel() * workspace.element_size(), _ptr(status),
                                                    _stream(stream)), "kvz_decode_attention_dense_splits")
@@ -281,6 +355,11 @@ def merge_splits(workspace: torch.Tensor, seq_lens: torch.Tensor, B: int, Hq: in
                  max_pages: int, out: torch.Tensor, out_f32: torch.Tensor | None = None, dense: bool = False,
                  pages_per_split: int = 0, stream=None) -> None:
     """Second phase: merges the partials left by one of the split kernels."""
+    dev = workspace.device
+    _arg(seq_lens, "seq_lens", (torch.int32,), B, dev)
+    _arg(out, "out", _HALF, B * Hq * D, dev)
+    if out_f32 is not None:
+        _arg(out_f32, "out_f32", (torch.float32,), B * Hq * D, dev)
     _check(lib().kvz_merge_splits(_ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(seq_lens), B,
                                   Hq, H, D, P, max_pages, pages_per_split, 1 if dense else 0, _ptr(out),
                                   _ptr(out_f32), _stream(stream)), "kvz_merge_splits")
@@ -291,6 +370,7 @@ def compact_pool(cache: Cache, page_ids: torch.Tensor, new_capacity: int, stream
     new_capacity u16 elements and installs it in `cache` (the old pool is then released). The new
     buffers are allocated and cleared on the call's stream, and the old pool is kept from reuse
     until the work enqueued there so far is done."""
+    _arg(page_ids, "page_ids", (torch.int32,), int(page_ids.numel()), cache.units.device)
     s = torch.cuda.current_stream() if stream is None else stream
     with torch.cuda.stream(s):
         new_pool = torch.zeros(max(1, new_capacity), dtype=torch.int16, device=cache.esc_pool.device)
@@ -305,6 +385,10 @@ def compact_pool(cache: Cache, page_ids: torch.Tensor, new_capacity: int, stream
 def decompress_pages(cache: Cache, page_ids: torch.Tensor, k_dst: torch.Tensor, v_dst: torch.Tensor,
                      lane_map: int = 0, stream=None) -> None:
     """Test entry point: the attention kernels' in-register decode written out as BF16 bits."""
+    n, dev = int(page_ids.numel()), cache.units.device
+    _arg(page_ids, "page_ids", (torch.int32,), n, dev)
+    _arg(k_dst, "k_dst", _HALF, n * cache.H * cache.P * cache.D, dev)
+    _arg(v_dst, "v_dst", _HALF, n * cache.H * cache.P * cache.D, dev)
     cs = cache.struct()
     _check(lib().kvz_decompress_pages(ctypes.byref(cs), _ptr(page_ids), int(page_ids.numel()), lane_map,
                                       _ptr(k_dst), _ptr(v_dst), _stream(stream)), "kvz_decompress_pages")

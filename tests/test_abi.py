@@ -147,6 +147,34 @@ def test_invalid_arguments_enqueue_nothing():
     assert rc == binding.KVZ_ERR_INVALID_ARG
 
 
+def test_binding_checks_buffers_before_calling_the_library():
+    """Wrong types, too-small buffers and mixed devices raise in the binding; nothing reaches the
+    library (these calls never get past their checks, so they run without a GPU)."""
+    cache = kvz.Cache.allocate(16, 4, 128, 8, 2, 64, device="cpu")
+    q = torch.zeros((2, 8, 128), dtype=torch.int16)
+    table = torch.zeros((2, 4), dtype=torch.int32)
+    lens = torch.zeros(2, dtype=torch.int32)
+    out = torch.zeros((2, 8, 128), dtype=torch.int16)
+    bad = [dict(q=q.float()), dict(page_table=table.long()), dict(seq_lens=lens[:1]), dict(out=out[:1]),
+           dict(out_f32=torch.zeros((2, 8, 128), dtype=torch.float16)), dict(page_table=table[:1]),
+           dict(q=q[:, :, :64].transpose(0, 1))]
+    for b in bad:
+        args = dict(q=q, page_table=table, seq_lens=lens, out=out, out_f32=None)
+        args.update(b)
+        with pytest.raises(ValueError):
+            kvz.decode_attention(args["q"], cache, args["page_table"], args["seq_lens"], 0.1, args["out"],
+                                 args["out_f32"])
+    with pytest.raises(ValueError):
+        kvz.append_token(cache, torch.zeros((2, 4, 64), dtype=torch.int16), torch.zeros((2, 4, 128), dtype=torch.int16),
+                         table, lens)
+    with pytest.raises(ValueError):
+        kvz.compress_pages(cache, torch.zeros((1, 4, 16, 128), dtype=torch.int16),
+                           torch.zeros((1, 4, 16, 128), dtype=torch.int16), torch.zeros(2, dtype=torch.int32))
+    with pytest.raises(ValueError):
+        kvz.decompress_pages(cache, torch.zeros(2, dtype=torch.int32), torch.zeros((1, 4, 16, 128), dtype=torch.int16),
+                             torch.zeros((2, 4, 16, 128), dtype=torch.int16))
+
+
 def test_noalloc_checks_come_before_any_device_work():
     L = binding.lib()
     assert L.kvz_decode_attention_noalloc(None, None, None, 0, None, 0, 1, 1.0, 0, None, None, None) == \
