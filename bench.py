@@ -256,10 +256,13 @@ def main() -> int:
             n += 10
         return n
 
-    c_split = lambda: kvz.decode_attention_splits(q, cache, table, lens, w.sm_scale, ws, pages_per_split=pps)
-    c_merge = lambda: kvz.merge_splits(ws, lens, B, Hq, H, D, P, w.max_pages, out, pages_per_split=pps)
-    d_split = lambda: kvz.decode_attention_dense_splits(q, kd, vd, table, lens, w.sm_scale, ws, pages_per_split=pps)
-    d_merge = lambda: kvz.merge_splits(ws, lens, B, Hq, H, D, P, w.max_pages, out, dense=True, pages_per_split=pps)
+    # the two paths as prepared calls (arguments checked and marshalled once), so that a short step
+    # is not paced by Python: the split kernel and the merge, on the current stream
+    c_step = kvz.prepare_decode_attention(q, cache, table, lens, w.sm_scale, out, workspace=ws, pages_per_split=pps)
+    d_step = kvz.prepare_decode_attention_dense(q, kd, vd, table, lens, w.sm_scale, out, workspace=ws,
+                                                pages_per_split=pps)
+    c_split, c_merge = c_step.splits, c_step.merge
+    d_split, d_merge = d_step.splits, d_step.merge
     settle_steps = settle(c_split, c_merge, args.settle_seconds)
     # the headline: W warm-up steps, then exactly K timed steps of the compressed path
     for _ in range(args.warmup):

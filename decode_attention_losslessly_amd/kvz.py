@@ -392,3 +392,86 @@ def decompress_pages(cache: Cache, page_ids: torch.Tensor, k_dst: torch.Tensor, 
     cs = cache.struct()
     _check(lib().kvz_decompress_pages(ctypes.byref(cs), _ptr(page_ids), int(page_ids.numel()), lane_map,
                                       _ptr(k_dst), _ptr(v_dst), _stream(stream)), "kvz_decompress_pages")
+
+
+# ---------------------------------------------------------------- prepared calls
+class PreparedAttention:
+    """One decode-attention call, its buffers checked and its arguments marshalled once, for a loop
+    that repeats it (the same buffers every step, their contents changing on the device: a decode
+    loop reads its lengths and page table from memory each call). `splits()` enqueues the split
+    kernel, `merge()` the merge, a call both, on the stream given at preparation (default: the
+    current stream then). It keeps its buffers alive and holds their addresses: prepare again after
+    anything replaces a buffer (kvz_compact_pool installs a new pool)."""
+
+    def __init__(self, split_fn, split_args, merge_args, keep, what):
+        self._split = split_fn
+        self._split_args = split_args
+        self._merge = lib().kvz_merge_splits
+        self._merge_args = merge_args
+        self._keep = keep          # the tensors and the cache description the addresses point into
+        self._what = what
+
+    def splits(self) -> None:
+        rc = self._split(*self._split_args)
+        if rc:
+            raise KvzError(rc, self._what)
+
+    def merge(self) -> None:
+        rc = self._merge(*self._merge_args)
+        if rc:
+            raise KvzError(rc, "kvz_merge_splits")
+
+    def __call__(self) -> None:
+        self.splits()
+        self.merge()
+
+
+def _merge_args(workspace, seq_lens, B, Hq, H, D, P, max_pages, pps, dense, out, out_f32, s):
+    return (_ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(seq_lens), B, Hq, H, D, P, max_pages,
+            pps, 1 if dense else 0, _ptr(out), _ptr(out_f32), s)
+
+
+def prepare_decode_attention(q: torch.Tensor, cache: Cache, page_table: torch.Tensor, seq_lens: torch.Tensor,
+                             sm_scale: float, out: torch.Tensor, out_f32: torch.Tensor | None = None,
+                             workspace: torch.Tensor | None = None, pages_per_split: int = 0,
+                             stream=None) -> PreparedAttention:
+    """decode_attention as a PreparedAttention (arguments as decode_attention)."""
+    B, Hq, D = q.shape
+    dev = cache.units.device
+    max_pages = _io(q, page_table, seq_lens, out, out_f32, dev)
+    _on(workspace, "workspace", dev)
+    s = torch.cuda.current_stream() if stream is None else stream
+    if workspace is None:
+        workspace = _scratch(workspace_bytes(B, Hq, cache.H, D, cache.P, max_pages, pages_per_split), q.device, s)
+    cs = cache.struct()
+    st = _stream(s)
+    split = (_ptr(q), ctypes.byref(cs), _ptr(page_table), max_pages, _ptr(seq_lens), B, Hq, float(sm_scale),
+             pages_per_split, _ptr(workspace), workspace.numel() * workspace.element_size(), st)
+    merge = _merge_args(workspace, seq_lens, B, Hq, cache.H, D, cache.P, max_pages, pages_per_split, False, out,
+                        out_f32, st)
+    keep = (q, cache, cs, page_table, seq_lens, out, out_f32, workspace, s)
+    return PreparedAttention(lib().kvz_decode_attention_splits, split, merge, keep, "kvz_decode_attention_splits")
+
+
+def prepare_decode_attention_dense(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torch.Tensor,
+                                   page_table: torch.Tensor, seq_lens: torch.Tensor, sm_scale: float,
+                                   out: torch.Tensor, out_f32: torch.Tensor | None = None,
+                                   workspace: torch.Tensor | None = None, status: torch.Tensor | None = None,
+                                   pages_per_split: int = 0, stream=None) -> PreparedAttention:
+    """decode_attention_dense as a PreparedAttention (arguments as decode_attention_dense)."""
+    B, Hq, D = q.shape
+    num_pages, H, P, _ = k_pages.shape
+    max_pages = _io(q, page_table, seq_lens, out, out_f32, q.device)
+    _dense_pages(k_pages, v_pages, status, q.device)
+    _on(workspace, "workspace", q.device)
+    s = torch.cuda.current_stream() if stream is None else stream
+    if workspace is None:
+        workspace = _scratch(workspace_bytes(B, Hq, H, D, P, max_pages, pages_per_split), q.device, s)
+    st = _stream(s)
+    split = (_ptr(q), _ptr(k_pages), _ptr(v_pages), num_pages, H, D, P, _ptr(page_table), max_pages, _ptr(seq_lens),
+             B, Hq, float(sm_scale), pages_per_split, _ptr(workspace), workspace.numel() * workspace.element_size(),
+             _ptr(status), st)
+    merge = _merge_args(workspace, seq_lens, B, Hq, H, D, P, max_pages, pages_per_split, True, out, out_f32, st)
+    keep = (q, k_pages, v_pages, page_table, seq_lens, out, out_f32, workspace, status, s)
+    return PreparedAttention(lib().kvz_decode_attention_dense_splits, split, merge, keep,
+                             "kvz_decode_attention_dense_splits")

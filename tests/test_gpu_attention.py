@@ -343,6 +343,42 @@ def test_two_phase_calls_equal_the_one_call():
     assert np.array_equal(host16(out), o16) and np.array_equal(out32.cpu().numpy(), o32)
 
 
+@pytest.mark.parametrize("cfg", [2, 4])
+def test_prepared_calls_equal_the_one_call(cfg):
+    """A prepared call (buffers checked and marshalled once) gives the one-call result bit for bit,
+    and keeps doing so while appends change the lengths in device memory between its calls (it
+    reads them at every call), for the compressed path and the uncompressed baseline."""
+    kw = dict(SMALL[cfg], **({"lens": [1, 15, 16, 17, 300, 1000]} if cfg == 4 else {}))   # room to append
+    w = make_workload(cfg, n_append=0, **kw)
+    kp, vp = w.pages(0), w.pages(1)
+    cache, lens = build_cache(w, kp, vp)
+    q, table = dev(w.q()), dev(w.page_table)
+    kd, vd = dev(kp), dev(vp)
+    out = torch.zeros((w.B, w.Hq, w.D), dtype=torch.int16, device=DEV)
+    out32 = torch.zeros((w.B, w.Hq, w.D), dtype=torch.float32, device=DEV)
+    dense_lens = dev(w.seq_lens.astype(np.int32))
+    step = kvz.prepare_decode_attention(q, cache, table, lens, w.sm_scale, out, out32)
+    dstep = kvz.prepare_decode_attention_dense(q, kd, vd, table, dense_lens, w.sm_scale, out, out32)
+    rng = np.random.default_rng(5)
+    for it in range(3):
+        ref16 = torch.zeros_like(out)
+        ref32 = torch.zeros_like(out32)
+        kvz.decode_attention(q, cache, table, lens, w.sm_scale, ref16, ref32)
+        step()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref16) and torch.equal(out32, ref32), it
+        kvz.decode_attention_dense(q, kd, vd, table, dense_lens, w.sm_scale, ref16, ref32)
+        dstep()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref16) and torch.equal(out32, ref32), it
+        # one more token per request (its tail row only: the lengths stay within the pages laid out)
+        assert ((w.max_pages * w.P - lens.cpu().numpy()) > 0).all()
+        kn = torch.from_numpy(rng.integers(0, 1 << 14, size=(w.B, w.Hkv, w.D)).astype(np.int16)).to(DEV)
+        kvz.append_token(cache, kn, kn, table, lens)
+        torch.cuda.synchronize()
+        assert int(cache.status.item()) == 0
+
+
 @pytest.mark.parametrize("Hq,Hkv", [(4, 4), (8, 2)])
 def test_sequence_longer_than_the_page_table(Hq, Hkv):
     """A length beyond max_pages_per_seq * P sets KVZ_STATUS_SEQ_TOO_LONG and is clamped to the
