@@ -495,9 +495,10 @@ def parity_check(out16, out32, rows, ref, same_bits):
 def layer_loop(kvz, cache, q, table, lens, w, ws, pps, nl, dev, reps=20):
     """One decode step of an nl-layer model's attention: nl calls of decode_attention (split
     kernel + merge), one per layer, each on its own copy of the cache (separate memory, as the
-    layers of a model hold). Timed launched one call after another from Python, then captured
-    once as a HIP graph and replayed; the replayed outputs must equal the eager ones bit for bit.
-    Launch overhead is what a decode step at batch 1 pays per layer."""
+    layers of a model hold). Timed launched one call after another from Python (prepared calls:
+    one C call per launch), then captured once as a HIP graph and replayed; the replayed outputs
+    must equal the eager ones bit for bit. Launch overhead is what a decode step at batch 1 pays
+    per layer."""
     import torch
 
     caches = [cache] + [kvz.Cache(cache.P, cache.H, cache.D, cache.num_pages, cache.max_batch, cache.units.clone(),
@@ -509,6 +510,13 @@ def layer_loop(kvz, cache, q, table, lens, w, ws, pps, nl, dev, reps=20):
     def step():
         for i, c in enumerate(caches):
             kvz.decode_attention(q, c, table, lens, w.sm_scale, outs[i], workspace=ws, pages_per_split=pps)
+
+    prepared = [kvz.prepare_decode_attention(q, c, table, lens, w.sm_scale, outs[i], workspace=ws, pages_per_split=pps)
+                for i, c in enumerate(caches)]
+
+    def eager_step():   # the same calls, each launched as one prepared C call
+        for p in prepared:
+            p()
 
     def timed(fn):
         for _ in range(3):
@@ -522,7 +530,7 @@ def layer_loop(kvz, cache, q, table, lens, w, ws, pps, nl, dev, reps=20):
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) * 1e3 / reps / nl
 
-    eager_us = timed(step)
+    eager_us = timed(eager_step)
     ref = outs.clone()
     outs.zero_()
     graph = torch.cuda.CUDAGraph()
@@ -536,7 +544,7 @@ def layer_loop(kvz, cache, q, table, lens, w, ws, pps, nl, dev, reps=20):
     graph_us = timed(graph.replay)
     assert torch.equal(outs, ref), "graph replay differs from the eager layers"
     assert all(int(c.status.item()) == 0 for c in caches)
-    del graph, caches
+    del graph, caches, prepared
     return {"layers": nl, "eager_us_per_layer": round(eager_us, 2), "graph_us_per_layer": round(graph_us, 2),
             "graph_tokens_per_s": round(B / (graph_us * 1e-6), 1)}
 
