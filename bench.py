@@ -139,6 +139,10 @@ def main() -> int:
     torch.cuda.synchronize()
     kd_sel, vd_sel = kd[ids_d.long()], vd[ids_d.long()]
     torch.cuda.synchronize()
+    # one unit first, so that the timed call does not carry the kernel's first-launch cost (the
+    # timed call compresses that unit again, into the same slot)
+    kvz.compress_pages(cache, kd_sel[:1].contiguous(), vd_sel[:1].contiguous(), ids_d[:1].contiguous())
+    torch.cuda.synchronize()
     ce0, ce1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     ce0.record()
     kvz.compress_pages(cache, kd_sel, vd_sel, ids_d)
