@@ -343,15 +343,16 @@ def test_two_phase_calls_equal_the_one_call():
     assert np.array_equal(host16(out), o16) and np.array_equal(out32.cpu().numpy(), o32)
 
 
-@pytest.mark.parametrize("cfg", [2, 4])
-def test_prepared_calls_equal_the_one_call(cfg):
+@pytest.mark.parametrize("cfg,fmt", [(2, kvz.FORMAT_ESCAPE), (4, kvz.FORMAT_ESCAPE), (4, kvz.FORMAT_ZIPFUSION)])
+def test_prepared_calls_equal_the_one_call(cfg, fmt):
     """A prepared call (buffers checked and marshalled once) gives the one-call result bit for bit,
     and keeps doing so while appends change the lengths in device memory between its calls (it
-    reads them at every call), for the compressed path and the uncompressed baseline."""
+    reads them at every call), for the compressed path in both formats and the uncompressed
+    baseline."""
     kw = dict(SMALL[cfg], **({"lens": [1, 15, 16, 17, 300, 1000]} if cfg == 4 else {}))   # room to append
     w = make_workload(cfg, n_append=0, **kw)
     kp, vp = w.pages(0), w.pages(1)
-    cache, lens = build_cache(w, kp, vp)
+    cache, lens = build_cache(w, kp, vp, fmt=fmt)
     q, table = dev(w.q()), dev(w.page_table)
     kd, vd = dev(kp), dev(vp)
     out = torch.zeros((w.B, w.Hq, w.D), dtype=torch.int16, device=DEV)
