@@ -30,7 +30,8 @@ struct ZStage {
   const uint8_t* unit;
   int page, tile;
   bool ok;           // false when the page id was out of range: a stand-in unit was read
-  uint32_t rawlo;    // low dword of the unit's raw-pool offset: all ones when it has no raw block
+  uint32_t rawlo;    // low dword of the unit's raw-pool offset (a scalar load, read when the tile is
+                     // computed): all ones when the unit has no raw block
   ZPiece k[D / 64];
   ZPiece v[D / 64];
 };
@@ -43,7 +44,7 @@ __device__ __forceinline__ void zf_issue(ZStage<D>& st, const uint8_t* units, in
   st.page = page;
   st.tile = tile;
   st.unit = units + ((size_t)(st.ok ? pid : 0) * H + h) * zf_unit_bytes(P, D);
-  st.rawlo = stream4(st.unit + zf_rawoff_offset(P, D));
+  st.rawlo = sload<uint32_t>(st.unit + zf_rawoff_offset(P, D));
 #pragma unroll
   for (int i = 0; i < D / 64; ++i) zf_load_piece(st.unit, P, D, false, tile, k_piece<D, false>(lane, i), st.k[i]);
 #pragma unroll
@@ -55,13 +56,24 @@ __device__ __forceinline__ void zf_issue(ZStage<D>& st, const uint8_t* units, in
 template <int D, bool RAW>
 __device__ __forceinline__ void zf_rebuild(const ZStage<D>& stg, int P, const uint16_t* pool, int64_t pool_cap,
                                            int lane, uint32_t (&kp)[D / 8], uint32_t (&vp)[D / 8]) {
+  // a unit of at most 8 blocks: one 16-byte scalar load gives the raw offset and every rank
+  const bool in_head = zf_head_holds_meta(P, D);
+  uint32_t raw_mask = 0;
   uint64_t off = 0;
-  if constexpr (RAW) off = zf_raw_offset(stg.unit, P, D);
+  if constexpr (RAW) {
+    if (in_head) {
+      const uint4 head = sload4(stg.unit);
+      off = zf_head_offset(head);
+      raw_mask = zf_head_raw_mask(head);
+    } else {
+      off = zf_raw_offset(stg.unit, P, D);
+    }
+  }
 #pragma unroll
   for (int i = 0; i < D / 64; ++i) {
     if (RAW && stg.k[i].meta == kZfRaw) {
       const int pc = k_piece<D, false>(lane, i);
-      const uint32_t rank = zf_raw_rank(stg.unit, zf_block_index(false, P, D, stg.tile, (16 * pc) / kZfBlock));
+      const uint32_t rank = zf_rank(raw_mask, stg.unit, in_head, zf_block_index(false, P, D, stg.tile, (16 * pc) / kZfBlock));
       if (off != kInline && off + (uint64_t)(rank + 1) * kZfBlock <= (uint64_t)pool_cap)
         zf_raw_piece(pool, off, rank, pc, &kp[8 * i]);
       else
@@ -74,7 +86,7 @@ __device__ __forceinline__ void zf_rebuild(const ZStage<D>& stg, int P, const ui
   for (int s = 0; s < D / 64; ++s) {
     if (RAW && stg.v[s].meta == kZfRaw) {
       const int d = lane + 64 * s;
-      const uint32_t rank = zf_raw_rank(stg.unit, zf_block_index(true, P, D, stg.tile, (16 * d) / kZfBlock));
+      const uint32_t rank = zf_rank(raw_mask, stg.unit, in_head, zf_block_index(true, P, D, stg.tile, (16 * d) / kZfBlock));
       if (off != kInline && off + (uint64_t)(rank + 1) * kZfBlock <= (uint64_t)pool_cap)
         zf_raw_piece(pool, off, rank, d, &vp[8 * s]);
       else
@@ -198,12 +210,16 @@ struct ZgStage {
   ZPiece v[2];       // dims l, l + 64
 };
 
+// HEAD (a unit of at most 8 blocks): the raw offset's low dword is a scalar load, read when the
+// tile is computed (no vector register held for it while the stage is in flight)
+template <bool HEAD = false>
 __device__ __forceinline__ void zf_gqa_issue(ZgStage& st, const uint8_t* units, int pid, int tile, int H, int h, int P,
                                              int num_pages, int lane) {
   st.ok = pid >= 0 && pid < num_pages;
   st.tile = tile;
   st.unit = units + ((size_t)(st.ok ? pid : 0) * H + h) * zf_unit_bytes(P, 128);
-  st.rawlo = stream4(st.unit + zf_rawoff_offset(P, 128));
+  if constexpr (HEAD) st.rawlo = sload<uint32_t>(st.unit + zf_rawoff_offset(P, 128));
+  else st.rawlo = stream4(st.unit + zf_rawoff_offset(P, 128));
   zf_load_pair(st.unit, P, 128, tile, k_piece<128, true>(lane, 0), st.k);
 #pragma unroll
   for (int s = 0; s < 2; ++s) zf_load_piece(st.unit, P, 128, true, tile, lane + 64 * s, st.v[s]);
@@ -212,14 +228,26 @@ __device__ __forceinline__ void zf_gqa_issue(ZgStage& st, const uint8_t* units, 
 // Rebuilds this lane's K pairs (A-operand layout) and V pairs (dims l, l + 64); with RAW, raw
 // blocks are read from the pool (bounds-checked against its capacity; a unit whose raw blocks
 // were dropped reads zeros).
-template <bool RAW>
+// HEAD: the unit has at most 8 blocks (its first 16 bytes give the raw offset and the ranks;
+// a compile-time choice here, so that the kernel carries one raw path only).
+template <bool RAW, bool HEAD>
 __device__ __forceinline__ void zf_gqa_rebuild(const ZgStage& stg, int P, const uint16_t* pool, int64_t pool_cap,
                                                int lane, uint32_t (&kp)[16], uint32_t (&vp)[2][8]) {
+  constexpr bool in_head = HEAD;
+  uint32_t raw_mask = 0;
   uint64_t off = 0;
-  if constexpr (RAW) off = zf_raw_offset(stg.unit, P, 128);
+  if constexpr (RAW) {
+    if constexpr (HEAD) {
+      const uint4 head = sload4(stg.unit);
+      off = zf_head_offset(head);
+      raw_mask = zf_head_raw_mask(head);
+    } else {
+      off = zf_raw_offset(stg.unit, P, 128);
+    }
+  }
   if (RAW && stg.k.meta == kZfRaw) {
     const int pc = k_piece<128, true>(lane, 0);
-    const uint32_t rank = zf_raw_rank(stg.unit, zf_block_index(false, P, 128, stg.tile, (16 * pc) / kZfBlock));
+    const uint32_t rank = zf_rank(raw_mask, stg.unit, in_head, zf_block_index(false, P, 128, stg.tile, (16 * pc) / kZfBlock));
     if (off != kInline && off + (uint64_t)(rank + 1) * kZfBlock <= (uint64_t)pool_cap) {
       zf_raw_piece(pool, off, rank, pc, &kp[0]);
       zf_raw_piece(pool, off, rank, pc + 1, &kp[8]);
@@ -233,7 +261,7 @@ __device__ __forceinline__ void zf_gqa_rebuild(const ZgStage& stg, int P, const 
   for (int s = 0; s < 2; ++s) {
     if (RAW && stg.v[s].meta == kZfRaw) {
       const int d = lane + 64 * s;
-      const uint32_t rank = zf_raw_rank(stg.unit, zf_block_index(true, P, 128, stg.tile, (16 * d) / kZfBlock));
+      const uint32_t rank = zf_rank(raw_mask, stg.unit, in_head, zf_block_index(true, P, 128, stg.tile, (16 * d) / kZfBlock));
       if (off != kInline && off + (uint64_t)(rank + 1) * kZfBlock <= (uint64_t)pool_cap)
         zf_raw_piece(pool, off, rank, d, vp[s]);
       else
@@ -244,12 +272,13 @@ __device__ __forceinline__ void zf_gqa_rebuild(const ZgStage& stg, int P, const 
   }
 }
 
+template <bool HEAD>
 __device__ __forceinline__ void zf_gqa_compute(GqaState& st, const ZgStage& stg, int P, const uint16_t* pool,
                                                int64_t pool_cap, float scale, uint32_t* vlds, int lane) {
   if (!stg.ok) return;
   uint32_t kp[16], vp[2][8];
-  if (uniform(stg.rawlo) == 0xFFFFFFFFu) zf_gqa_rebuild<false>(stg, P, pool, pool_cap, lane, kp, vp);
-  else zf_gqa_rebuild<true>(stg, P, pool, pool_cap, lane, kp, vp);
+  if (uniform(stg.rawlo) == 0xFFFFFFFFu) zf_gqa_rebuild<false, HEAD>(stg, P, pool, pool_cap, lane, kp, vp);
+  else zf_gqa_rebuild<true, HEAD>(stg, P, pool, pool_cap, lane, kp, vp);
   const int vdim[2] = {lane, lane + 64};
   gqa_tile(st, kp, vdim, vp, kTile, scale, vlds, lane);
 }
@@ -257,6 +286,7 @@ __device__ __forceinline__ void zf_gqa_compute(GqaState& st, const ZgStage& stg,
 // One wave per (request, KV head, chunk of up to 8 query heads, split), as the escape format's
 // grouped-query kernel (3 waves per SIMD: see there), with the next tile's loads issued before
 // the current tile is computed.
+template <bool HEAD>
 __global__ __launch_bounds__(64 * kZfWaves) __attribute__((amdgpu_waves_per_eu(3))) void attn_zf_gqa_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ units, const uint16_t* __restrict__ pool,
     int64_t pool_cap, const uint16_t* __restrict__ k_tail, const uint16_t* __restrict__ v_tail,
@@ -304,21 +334,21 @@ __global__ __launch_bounds__(64 * kZfWaves) __attribute__((amdgpu_waves_per_eu(3
     };
     ZgStage a, b;
     int pid = sload<int32_t>(pt_row + lp);
-    zf_gqa_issue(a, units, pid, lt, H, h, P, num_pages, lane);
+    zf_gqa_issue<HEAD>(a, units, pid, lt, H, h, P, num_pages, lane);
     advance();
     pid = sload<int32_t>(pt_row + lp);
     for (int i = 0; i < nsteps; i += 2) {
-      zf_gqa_issue(b, units, pid, lt, H, h, P, num_pages, lane);
+      zf_gqa_issue<HEAD>(b, units, pid, lt, H, h, P, num_pages, lane);
       advance();
       pid = sload<int32_t>(pt_row + lp);
       bad |= !a.ok;
-      zf_gqa_compute(st, a, P, pool, pool_cap, scale, vlds, lane);
+      zf_gqa_compute<HEAD>(st, a, P, pool, pool_cap, scale, vlds, lane);
       if (i + 1 >= nsteps) break;
-      zf_gqa_issue(a, units, pid, lt, H, h, P, num_pages, lane);
+      zf_gqa_issue<HEAD>(a, units, pid, lt, H, h, P, num_pages, lane);
       advance();
       pid = sload<int32_t>(pt_row + lp);
       bad |= !b.ok;
-      zf_gqa_compute(st, b, P, pool, pool_cap, scale, vlds, lane);
+      zf_gqa_compute<HEAD>(st, b, P, pool, pool_cap, scale, vlds, lane);
     }
   }
   if (bad && lane == 0) atomicOr(status, kStatusBadPage);
@@ -354,7 +384,8 @@ __global__ __launch_bounds__(64) void decompress_zf_kernel(const uint8_t* __rest
       ZgStage st;
       zf_gqa_issue(st, units, pid, t, H, h, P, num_pages, lane);
       uint32_t v2[2][8];
-      zf_gqa_rebuild<true>(st, P, pool, pool_cap, lane, kp, v2);
+      if (zf_head_holds_meta(P, 128)) zf_gqa_rebuild<true, true>(st, P, pool, pool_cap, lane, kp, v2);
+      else zf_gqa_rebuild<true, false>(st, P, pool, pool_cap, lane, kp, v2);
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         vp[j] = v2[0][j];
@@ -413,14 +444,21 @@ int launch_attn_zf_gqa(const uint16_t* q, const uint8_t* units, const uint16_t* 
                        const int32_t* seq_lens, int B, int Hq, int H, int D, int P, int num_pages, SplitPlan plan,
                        float scale, float* ws_acc, float* ws_ml, uint32_t* status, hipStream_t stream) {
   if (D != 128) return -2;
-  static int slots[64];
+  static int slots_head[64], slots[64];
   const dim3 block(64 * kZfWaves);
   const long items = (long)B * H * ((Hq / H + kGqaRows - 1) / kGqaRows);
-  plan.slots = resident_waves(attn_zf_gqa_kernel, block.x, slots, 64);
+  const bool head = zf_head_holds_meta(P, 128);
+  plan.slots = head ? resident_waves(attn_zf_gqa_kernel<true>, block.x, slots_head, 64)
+                    : resident_waves(attn_zf_gqa_kernel<false>, block.x, slots, 64);
   if (plan.slots <= 0) plan.slots = (int)(items * plan.S);
-  hipLaunchKernelGGL(attn_zf_gqa_kernel, dim3(plan_blocks(plan, items, kZfWaves)), block, 0, stream, q, units, pool,
-                     pool_cap, k_tail, v_tail, page_table, max_pages, seq_lens, B, Hq, H, P, num_pages, plan, scale,
-                     ws_acc, ws_ml, status);
+  if (head)
+    hipLaunchKernelGGL(attn_zf_gqa_kernel<true>, dim3(plan_blocks(plan, items, kZfWaves)), block, 0, stream, q, units,
+                       pool, pool_cap, k_tail, v_tail, page_table, max_pages, seq_lens, B, Hq, H, P, num_pages, plan,
+                       scale, ws_acc, ws_ml, status);
+  else
+    hipLaunchKernelGGL(attn_zf_gqa_kernel<false>, dim3(plan_blocks(plan, items, kZfWaves)), block, 0, stream, q, units,
+                       pool, pool_cap, k_tail, v_tail, page_table, max_pages, seq_lens, B, Hq, H, P, num_pages, plan,
+                       scale, ws_acc, ws_ml, status);
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 

@@ -122,11 +122,38 @@ __device__ __forceinline__ void zf_raw_piece(const uint16_t* pool, uint64_t off,
   pairs[4] = b.x; pairs[5] = b.y; pairs[6] = b.z; pairs[7] = b.w;
 }
 
+// A unit of at most 8 blocks keeps its blocks' meta bytes in bytes 0..7 and its raw-pool offset in
+// bytes 8..15: its first 16 bytes (`head`) then give a raw block's pool offset and rank with no
+// further load.
+__host__ __device__ constexpr bool zf_head_holds_meta(int P, int D) { return zf_nblocks(P, D) <= 8; }
+
+__device__ __forceinline__ uint64_t zf_head_offset(const uint4& head) {
+  return (uint64_t)head.z | ((uint64_t)head.w << 32);
+}
+
+// bit i set when block i (< 8) is raw: meta bytes 0..7 of the head equal to kZfRaw
+__device__ __forceinline__ uint32_t zf_head_raw_mask(const uint4& head) {
+  const uint64_t e = ~((uint64_t)head.x | ((uint64_t)head.y << 32));   // raw bytes become zero
+  const uint64_t hi = 0x8080808080808080ull, lo7 = 0x7F7F7F7F7F7F7F7Full;
+  const uint64_t raw = ~((((e & lo7) + lo7) | e) & hi) & hi;          // bit 7 of each raw byte
+  return (uint32_t)((raw * 0x0002040810204081ull) >> 56);            // gather bit 7 of byte i into bit i
+}
+
+// rank of block idx (< 8) among the unit's raw blocks, from the head's raw-block mask
+__device__ __forceinline__ uint32_t zf_head_rank(uint32_t raw_mask, int idx) {
+  return (uint32_t)__builtin_popcount(raw_mask & ((1u << idx) - 1u));
+}
+
 // rank of block idx among the raw blocks of the unit (counts meta bytes equal to kZfRaw below idx)
 __device__ __forceinline__ uint32_t zf_raw_rank(const uint8_t* unit, int idx) {
   uint32_t r = 0;
   for (int i = 0; i < idx; ++i) r += unit[i] == kZfRaw ? 1u : 0u;
   return r;
+}
+
+// rank of block idx among the unit's raw blocks, from the head's mask when it holds the metas
+__device__ __forceinline__ uint32_t zf_rank(uint32_t raw_mask, const uint8_t* unit, bool in_head, int idx) {
+  return in_head ? zf_head_rank(raw_mask, idx) : zf_raw_rank(unit, idx);
 }
 
 __device__ __forceinline__ uint64_t zf_raw_offset(const uint8_t* unit, int P, int D) {
