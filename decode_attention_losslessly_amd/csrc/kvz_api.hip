@@ -125,6 +125,15 @@ bool shape_ok(int P, int D) {
   return P > 0 && P % 16 == 0 && D > 0 && D % 64 == 0 && (int64_t)P * D <= 65536;
 }
 
+// Compression stages a unit's values in LDS (160 KB per workgroup): the wave compressor (first
+// format, head dim 64 or 128) holds the V block, up to the format's largest block of 65536
+// values; the workgroup compressor (other head dims, the block format) holds K and V, half that.
+bool compress_fits(const kvz_cache* c) {
+  const int64_t n = (int64_t)c->page_size * c->head_dim;
+  const bool wave = c->format == KVZ_FORMAT_ESCAPE && (c->head_dim == 64 || c->head_dim == 128);
+  return n <= (wave ? 65536 : 32768);
+}
+
 // the kernels hold a request's length, at most max_pages * P tokens, in 32 bits
 bool table_fits(int max_pages, int P) { return (int64_t)max_pages * P <= INT32_MAX; }
 
@@ -223,7 +232,7 @@ size_t kvz_workspace_bytes(int32_t B, int32_t H_q, int32_t H_kv, int32_t D, int3
 int kvz_compress_pages(const kvz_cache* c, const uint16_t* k_src, const uint16_t* v_src, const int32_t* ids,
                        int32_t n, void* stream) {
   if (!cache_ok(c) || n < 0 || (n > 0 && (!k_src || !v_src || !ids))) return KVZ_ERR_INVALID_ARG;
-  if ((size_t)c->page_size * c->head_dim > 32768) return KVZ_ERR_UNSUPPORTED;
+  if (!compress_fits(c)) return KVZ_ERR_UNSUPPORTED;
   if (n == 0) return KVZ_OK;
   return kvz::launch_compress(k_src, v_src, ids, n, c->num_kv_heads, c->page_size, c->head_dim, c->num_pages,
                               c->units, c->esc_pool, c->esc_capacity, c->esc_cursor, c->status, c->format,
@@ -236,7 +245,7 @@ int kvz_append_token(const kvz_cache* c, const uint16_t* k_new, const uint16_t* 
   if (!table_fits(max_pages, c->page_size)) return KVZ_ERR_UNSUPPORTED;
   if (B > 0 && (!k_new || !v_new || !page_table || !seq_lens)) return KVZ_ERR_INVALID_ARG;
   if (B > c->max_batch) return KVZ_ERR_INVALID_ARG;
-  if ((size_t)c->page_size * c->head_dim > 32768) return KVZ_ERR_UNSUPPORTED;
+  if (!compress_fits(c)) return KVZ_ERR_UNSUPPORTED;
   if (B == 0) return KVZ_OK;
   return kvz::launch_append(k_new, v_new, page_table, max_pages, seq_lens, B, c->num_kv_heads, c->page_size,
                             c->head_dim, c->num_pages, c->units, c->esc_pool, c->esc_capacity, c->esc_cursor,

@@ -178,7 +178,9 @@ int32_t kvz_num_splits(int32_t B, int32_t H_q, int32_t H_kv, int32_t D, int32_t 
  *   dst_page_ids   [n] unit slots to write, each in [0, num_pages)
  * Escapes that do not fit inline are appended to the pool at *esc_cursor (bumped atomically,
  * so their place in the pool depends on scheduling; everything else is deterministic).
- * Errors: KVZ_ERR_INVALID_ARG, KVZ_ERR_UNSUPPORTED (P % 16, D % 64). Device status:
+ * Supported: P * D up to 65536 (the format's limit) for the first format at D = 64 or 128,
+ * up to 32768 otherwise (the block format, other head dims): a unit's values are staged in
+ * on-chip memory. Errors: KVZ_ERR_INVALID_ARG, KVZ_ERR_UNSUPPORTED. Device status:
  * ESC_POOL_FULL, BAD_PAGE_ID. */
 int kvz_compress_pages(const kvz_cache* cache, const uint16_t* k_src, const uint16_t* v_src,
                        const int32_t* dst_page_ids, int32_t n, void* stream);
@@ -191,7 +193,7 @@ int kvz_compress_pages(const kvz_cache* cache, const uint16_t* k_src, const uint
  *   page_table     [B][max_pages_per_seq]
  *   seq_lens       [B], updated on the device
  * B must not exceed max_batch; max_pages_per_seq * P must fit in int32 (a request's length is
- * held in 32 bits), else KVZ_ERR_UNSUPPORTED. Errors: KVZ_ERR_INVALID_ARG, KVZ_ERR_UNSUPPORTED.
+ * held in 32 bits) and P * D within the limits of kvz_compress_pages, else KVZ_ERR_UNSUPPORTED. Errors: KVZ_ERR_INVALID_ARG, KVZ_ERR_UNSUPPORTED.
  * Device status: ESC_POOL_FULL, BAD_PAGE_ID, SEQ_TOO_LONG (no write). */
 int kvz_append_token(const kvz_cache* cache, const uint16_t* k_new, const uint16_t* v_new,
                      const int32_t* page_table, int32_t max_pages_per_seq, int32_t* seq_lens,

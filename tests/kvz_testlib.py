@@ -116,3 +116,18 @@ def unit_equal(gpu_unit: np.ndarray, gpu_pool: np.ndarray, ref_unit: np.ndarray,
     ea = codec.unit_escapes(gpu_unit, gpu_pool, P, D)
     eb = codec.unit_escapes(ref_unit, ref_pool, P, D)
     return all(np.array_equal(x, y) for x, y in zip(ea, eb))
+
+
+def lane_maps(D):
+    """kvz_decompress_pages lane maps: multi-head and grouped-query layouts (the latter at D = 128
+    only), each through the main loops' route and the pool-capable loops' route."""
+    return [0, 1, 2, 3] if D == 128 else [0, 2]
+
+
+def decode_units(cache, ids, H, P, D, lane_map):
+    """The kernels' rebuilt K and V of units `ids` (uint16 [n, H, P, D] each)."""
+    kd = torch.zeros((len(ids), H, P, D), dtype=torch.int16, device=DEV)
+    vd = torch.zeros_like(kd)
+    kvz.decompress_pages(cache, dev(np.asarray(ids, np.int32)), kd, vd, lane_map=lane_map)
+    torch.cuda.synchronize()
+    return host16(kd), host16(vd)

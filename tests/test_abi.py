@@ -138,6 +138,14 @@ def test_invalid_arguments_enqueue_nothing():
     assert L.kvz_append_token(ctypes.byref(cs), fake, fake, fake, wide, fake, 1, None) == binding.KVZ_ERR_UNSUPPORTED
     assert L.kvz_decode_attention(fake, ctypes.byref(cs), fake, wide, fake, 1, 4, 0.1, 0, fake, None, fake, 1 << 40,
                                   None) == binding.KVZ_ERR_UNSUPPORTED
+    # compression stages a unit on chip: up to the format's largest block (P * D = 65536) for the
+    # first format at head dim 64 or 128, half of it otherwise (n = 0: checked, nothing enqueued)
+    for fmt, P, D, want in ((0, 512, 128, binding.KVZ_OK), (0, 1024, 64, binding.KVZ_OK),
+                            (1, 512, 128, binding.KVZ_ERR_UNSUPPORTED), (1, 256, 128, binding.KVZ_OK),
+                            (0, 256, 192, binding.KVZ_ERR_UNSUPPORTED), (0, 128, 192, binding.KVZ_OK)):
+        c = binding._CacheStruct(P, 4, D, 1, 8, fmt, fake, fake, 16, fake, fake, fake, fake)
+        assert L.kvz_compress_pages(ctypes.byref(c), fake, fake, fake, 0, None) == want, (fmt, P, D)
+        assert L.kvz_append_token(ctypes.byref(c), fake, fake, fake, 4, fake, 0, None) == want, (fmt, P, D)
     # a workspace that does not fit in size_t: zero size, and the call refuses it
     big = (1 << 31) - 1
     assert kvz.workspace_bytes(big, 1024, 1024, 128, 16, 1 << 20, 1) == 0

@@ -13,7 +13,7 @@ import decode_attention_losslessly_amd as kvz
 from oracle import c_oracle, codec
 from synth import make_workload
 
-from kvz_testlib import DEV, build_cache, dev, full_page_ids, host16, unit_equal
+from kvz_testlib import DEV, build_cache, decode_units, dev, full_page_ids, host16, lane_maps, unit_equal
 
 pytestmark = pytest.mark.gpu
 
@@ -59,19 +59,6 @@ def _pattern_pages(P, D, n, seed):
     vals = np.concatenate([allp, allp] + [rng.permutation(allp) for _ in range(need // 65536)])[:need]
     x = vals.reshape(n, 2, 2, P, D)
     return np.ascontiguousarray(x[:, 0]), np.ascontiguousarray(x[:, 1])
-
-
-def lane_maps(D):
-    return [0, 1, 2, 3] if D == 128 else [0, 2]
-
-
-def decode_units(cache, ids, H, P, D, lane_map):
-    """The kernels' rebuilt K and V of units `ids` (uint16 [n, H, P, D] each)."""
-    kd = torch.zeros((len(ids), H, P, D), dtype=torch.int16, device=DEV)
-    vd = torch.zeros_like(kd)
-    kvz.decompress_pages(cache, dev(np.asarray(ids, np.int32)), kd, vd, lane_map=lane_map)
-    torch.cuda.synchronize()
-    return host16(kd), host16(vd)
 
 
 @pytest.mark.parametrize("P,D", [(16, 128), (32, 128), (16, 64), (256, 64)])

@@ -1,13 +1,17 @@
 """Attention parity on shapes the five workloads do not reach: pages of several 16-token tiles
 (including a count that is not a power of two), query groups of 2 and 16 heads (16 = two MFMA
 row chunks), head_dim 64, and ragged lengths around page boundaries. Compressed and dense paths
-against the fp64 oracle within the stated tolerance."""
+against the fp64 oracle within the stated tolerance. Blocks of the format's largest size (65,536
+values: 512-token pages at head dim 128, 1,024-token pages at 64) are also compressed byte-exact,
+appended into and rebuilt bit for bit."""
 import numpy as np
 import pytest
 import torch
 
 import decode_attention_losslessly_amd as kvz
-from kvz_testlib import DEV, build_cache, check_rows, dev, host16, oracle_rows
+from kvz_testlib import (DEV, build_cache, check_rows, decode_units, dev, full_page_ids, host16, lane_maps,
+                         oracle_rows, unit_equal)
+from oracle import c_oracle
 from synth import make_workload
 
 pytestmark = pytest.mark.gpu
@@ -48,3 +52,40 @@ def test_shapes_match_oracle(P, D, Hq, Hkv):
         assert int(status.item()) == 0
         check_rows(host16(out).reshape(-1, D), out32.cpu().numpy().reshape(-1, D), ref,
                    f"cfg{cfg} P{P} D{D} {Hq}/{Hkv} dense")
+
+
+@pytest.mark.parametrize("P,D,Hq,Hkv", [(512, 128, 2, 2), (512, 128, 8, 2), (1024, 64, 2, 2)])
+@pytest.mark.parametrize("cfg", [1, 5])
+def test_largest_blocks(P, D, Hq, Hkv, cfg):
+    """P * D = 65536, where a storage position takes all 16 bits of an inline escape entry and
+    compression stages 128 KB of V per wave. The last token is appended through kvz_append_token,
+    which fills request 1's second page and compresses it. Units byte-exact against the oracle
+    (escape-stress data puts them in the pool), every decode route bit-exact, attention within
+    tolerance under every split choice."""
+    lens = [P - 1, 2 * P, 2 * P + 5]
+    w = make_workload(cfg, B=len(lens), lens=lens, Hq=Hq, Hkv=Hkv, D=D, P=P, n_append=1)
+    kp, vp = w.pages(0), w.pages(1)
+    ids = full_page_ids(w)
+    assert len(ids) == 4
+    cache, seq = build_cache(w, kp, vp, esc_capacity=len(ids) * Hkv * 2 * P * D)   # room for every value
+    assert int(cache.status.item()) == 0
+    units = cache.units.cpu().numpy()
+    pool = host16(cache.esc_pool)
+    ref_units, ref_pool, _ = c_oracle.encode_pages(kp[ids], vp[ids])
+    for i, pid in enumerate(ids):
+        for h in range(Hkv):
+            assert unit_equal(units[pid, h], pool, ref_units[i, h], ref_pool, P, D), (int(pid), h)
+    for lane_map in lane_maps(D):
+        kd, vd = decode_units(cache, ids, Hkv, P, D, lane_map)
+        assert np.array_equal(kd, kp[ids]) and np.array_equal(vd, vp[ids]), lane_map
+    q = w.q()
+    rows = [(r, h) for r in range(w.B) for h in range(w.Hq)]
+    ref = oracle_rows(w, kp, vp, q, rows)
+    for pps in (0, 1, -2):
+        out = torch.zeros((w.B, w.Hq, D), dtype=torch.int16, device=DEV)
+        out32 = torch.full((w.B, w.Hq, D), float("nan"), dtype=torch.float32, device=DEV)
+        kvz.decode_attention(dev(q), cache, dev(w.page_table), seq, w.sm_scale, out, out32, pages_per_split=pps)
+        torch.cuda.synchronize()
+        assert int(cache.status.item()) == 0
+        check_rows(host16(out).reshape(-1, D), out32.cpu().numpy().reshape(-1, D), ref,
+                   f"cfg{cfg} P{P} D{D} {Hq}/{Hkv} pps{pps}")
