@@ -113,8 +113,12 @@ def _arg(t: torch.Tensor | None, name: str, dtypes, numel: int, device) -> None:
         raise ValueError(f"{name} is on {t.device}, the call runs on {device}")
 
 
-def _on(t: torch.Tensor | None, name: str, device) -> None:
-    if t is not None and t.device != device:
+def _on(t: torch.Tensor | None, name: str, device, required: bool = False) -> None:
+    if t is None:
+        if required:
+            raise ValueError(f"{name} is required")
+        return
+    if t.device != device:
         raise ValueError(f"{name} is on {t.device}, the call runs on {device}")
 
 
@@ -222,11 +226,15 @@ class Cache:
 
 
 # ---------------------------------------------------------------- entry points
-def _io(q, page_table, seq_lens, out, out_f32, device) -> int:
-    """Checks an attention call's query, table, lengths and outputs; returns max_pages."""
+def _io(q, page_table, seq_lens, out, out_f32, device, D_kv: int) -> int:
+    """Checks an attention call's query, table, lengths and outputs against the head dim D_kv of
+    the keys and values (the library reads q and writes the outputs with that head dim); returns
+    max_pages."""
     if q.dim() != 3:
         raise ValueError(f"q: shape {tuple(q.shape)}, expected [B, H_q, D]")
     B, Hq, D = q.shape
+    if D != D_kv:
+        raise ValueError(f"q: head dim {D}, the keys and values have {D_kv}")
     _arg(q, "q", _HALF, 0, device)
     max_pages = _table(page_table, B, device)
     _arg(seq_lens, "seq_lens", (torch.int32,), B, device)
@@ -279,7 +287,7 @@ def decode_attention(q: torch.Tensor, cache: Cache, page_table: torch.Tensor, se
                      workspace: torch.Tensor | None = None, pages_per_split: int = 0, stream=None) -> None:
     """q, out: int16 [B, Hq, D] (BF16 bits); out_f32 optional float32 [B, Hq, D]."""
     B, Hq, D = q.shape
-    max_pages = _io(q, page_table, seq_lens, out, out_f32, cache.units.device)
+    max_pages = _io(q, page_table, seq_lens, out, out_f32, cache.units.device, cache.D)
     _on(workspace, "workspace", cache.units.device)
     if workspace is None:
         workspace = _scratch(workspace_bytes(B, Hq, cache.H, D, cache.P, max_pages, pages_per_split), q.device, stream)
@@ -296,7 +304,7 @@ def decode_attention_noalloc(q: torch.Tensor, cache: Cache, page_table: torch.Te
     """decode_attention with its workspace in the library's own per-GPU scratch array: nothing is
     allocated, here or in the library (for callers that cannot allocate device memory)."""
     B, Hq, D = q.shape
-    max_pages = _io(q, page_table, seq_lens, out, out_f32, cache.units.device)
+    max_pages = _io(q, page_table, seq_lens, out, out_f32, cache.units.device, cache.D)
     cs = cache.struct()
     _check(lib().kvz_decode_attention_noalloc(_ptr(q), ctypes.byref(cs), _ptr(page_table), max_pages,
                                               _ptr(seq_lens), B, Hq, float(sm_scale), pages_per_split, _ptr(out),
@@ -310,7 +318,7 @@ def decode_attention_dense(q: torch.Tensor, k_pages: torch.Tensor, v_pages: torc
     """k_pages, v_pages: int16 [num_pages, H, P, D]; other arguments as decode_attention."""
     B, Hq, D = q.shape
     num_pages, H, P, _ = k_pages.shape
-    max_pages = _io(q, page_table, seq_lens, out, out_f32, q.device)
+    max_pages = _io(q, page_table, seq_lens, out, out_f32, q.device, k_pages.shape[-1])
     _dense_pages(k_pages, v_pages, status, q.device)
     _on(workspace, "workspace", q.device)
     if workspace is None:
@@ -326,8 +334,8 @@ def decode_attention_splits(q: torch.Tensor, cache: Cache, page_table: torch.Ten
                             sm_scale: float, workspace: torch.Tensor, pages_per_split: int = 0, stream=None) -> None:
     """First phase of decode_attention: the split kernel, partials into `workspace`."""
     B, Hq, D = q.shape
-    max_pages = _io(q, page_table, seq_lens, None, None, cache.units.device)
-    _on(workspace, "workspace", cache.units.device)
+    max_pages = _io(q, page_table, seq_lens, None, None, cache.units.device, cache.D)
+    _on(workspace, "workspace", cache.units.device, required=True)
     cs = cache.struct()
     _check(lib().kvz_decode_attention_splits(_ptr(q), ctypes.byref(cs), _ptr(page_table), max_pages,
                                              _ptr(seq_lens), B, Hq, float(sm_scale), pages_per_split,
@@ -341,9 +349,9 @@ def decode_attention_dense_splits(q: torch.Tensor, k_pages: torch.Tensor, v_page
                                   pages_per_split: int = 0, stream=None) -> None:
     B, Hq, D = q.shape
     num_pages, H, P, _ = k_pages.shape
-    max_pages = _io(q, page_table, seq_lens, None, None, q.device)
+    max_pages = _io(q, page_table, seq_lens, None, None, q.device, k_pages.shape[-1])
     _dense_pages(k_pages, v_pages, status, q.device)
-    _on(workspace, "workspace", q.device)
+    _on(workspace, "workspace", q.device, required=True)
     _check(lib().kvz_decode_attention_dense_splits(_ptr(q), _ptr(k_pages), _ptr(v_pages), num_pages, H, D, P,
                                                    _ptr(page_table), max_pages, _ptr(seq_lens), B, Hq,
                                                    float(sm_scale), pages_per_split, _ptr(workspace),
@@ -355,6 +363,7 @@ def merge_splits(workspace: torch.Tensor, seq_lens: torch.Tensor, B: int, Hq: in
                  max_pages: int, out: torch.Tensor, out_f32: torch.Tensor | None = None, dense: bool = False,
                  pages_per_split: int = 0, stream=None) -> None:
     """Second phase: merges the partials left by one of the split kernels."""
+    _on(workspace, "workspace", seq_lens.device, required=True)
     dev = workspace.device
     _arg(seq_lens, "seq_lens", (torch.int32,), B, dev)
     _arg(out, "out", _HALF, B * Hq * D, dev)
@@ -438,7 +447,7 @@ def prepare_decode_attention(q: torch.Tensor, cache: Cache, page_table: torch.Te
     """decode_attention as a PreparedAttention (arguments as decode_attention)."""
     B, Hq, D = q.shape
     dev = cache.units.device
-    max_pages = _io(q, page_table, seq_lens, out, out_f32, dev)
+    max_pages = _io(q, page_table, seq_lens, out, out_f32, dev, cache.D)
     _on(workspace, "workspace", dev)
     s = torch.cuda.current_stream() if stream is None else stream
     if workspace is None:
@@ -461,7 +470,7 @@ def prepare_decode_attention_dense(q: torch.Tensor, k_pages: torch.Tensor, v_pag
     """decode_attention_dense as a PreparedAttention (arguments as decode_attention_dense)."""
     B, Hq, D = q.shape
     num_pages, H, P, _ = k_pages.shape
-    max_pages = _io(q, page_table, seq_lens, out, out_f32, q.device)
+    max_pages = _io(q, page_table, seq_lens, out, out_f32, q.device, k_pages.shape[-1])
     _dense_pages(k_pages, v_pages, status, q.device)
     _on(workspace, "workspace", q.device)
     s = torch.cuda.current_stream() if stream is None else stream

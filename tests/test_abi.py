@@ -172,6 +172,22 @@ def test_binding_checks_buffers_before_calling_the_library():
         with pytest.raises(ValueError):
             kvz.decode_attention(args["q"], cache, args["page_table"], args["seq_lens"], 0.1, args["out"],
                                  args["out_f32"])
+    # a query of another head dim than the cache's: the library would read q and write out with
+    # the cache's head dim, past the end of both
+    q64, out64 = torch.zeros((2, 8, 64), dtype=torch.int16), torch.zeros((2, 8, 64), dtype=torch.int16)
+    with pytest.raises(ValueError):
+        kvz.decode_attention(q64, cache, table, lens, 0.1, out64)
+    with pytest.raises(ValueError):
+        kvz.prepare_decode_attention(q64, cache, table, lens, 0.1, out64)
+    with pytest.raises(ValueError):
+        kvz.decode_attention_splits(q64, cache, table, lens, 0.1, torch.zeros(1 << 20, dtype=torch.uint8))
+    kp = torch.zeros((8, 4, 16, 128), dtype=torch.int16)
+    with pytest.raises(ValueError):
+        kvz.decode_attention_dense(q64, kp, kp, table, lens, 0.1, out64)
+    with pytest.raises(ValueError):
+        kvz.decode_attention_splits(q, cache, table, lens, 0.1, None)        # the two-phase calls take a workspace
+    with pytest.raises(ValueError):
+        kvz.merge_splits(None, lens, 2, 8, 4, 128, 16, 4, out)
     with pytest.raises(ValueError):
         kvz.append_token(cache, torch.zeros((2, 4, 64), dtype=torch.int16), torch.zeros((2, 4, 128), dtype=torch.int16),
                          table, lens)
