@@ -138,7 +138,9 @@ bool compress_fits(const kvz_cache* c) {
 bool table_fits(int max_pages, int P) { return (int64_t)max_pages * P <= INT32_MAX; }
 
 bool cache_ok(const kvz_cache* c) {
-  return c && c->units && c->status && shape_ok(c->page_size, c->head_dim) && c->num_kv_heads > 0 &&
+  // a cache without unit slots (every request shorter than a page) may have no unit array
+  return c && (c->units || c->num_pages == 0) && c->status && shape_ok(c->page_size, c->head_dim) &&
+         c->num_kv_heads > 0 &&
          c->num_pages >= 0 && c->max_batch >= 0 && c->esc_capacity >= 0 && c->esc_cursor &&
          (c->format == KVZ_FORMAT_ESCAPE || c->format == KVZ_FORMAT_ZIPFUSION);
 }
@@ -309,7 +311,8 @@ int kvz_decode_attention_dense_splits(const uint16_t* q, const uint16_t* k_pages
   int rc = check_attention_shape(B, H_q, H, D, P, max_pages);
   if (rc) return rc;
   if (B == 0) return KVZ_OK;
-  if (!q || !k_pages || !v_pages || !page_table || !seq_lens || !workspace || num_pages < 0 ||
+  // pages may be absent only when there are none (every page id is then bad and skipped)
+  if (!q || (num_pages > 0 && (!k_pages || !v_pages)) || !page_table || !seq_lens || !workspace || num_pages < 0 ||
       pps < -kMaxForcedRanks)
     return KVZ_ERR_INVALID_ARG;
   const int C = pages_per_split(B, H_q, H, P, max_pages, pps);

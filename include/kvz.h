@@ -110,7 +110,8 @@ typedef struct kvz_cache {
   int32_t num_pages;     /* unit slots per head */
   int32_t max_batch;     /* tail rows */
   int32_t format;        /* KVZ_FORMAT_* of the units and the pool */
-  uint8_t* units;        /* [num_pages][H][kvz_unit_bytes(P, D)], 256-byte aligned */
+  uint8_t* units;        /* [num_pages][H][kvz_unit_bytes(P, D)], 256-byte aligned; may be
+                            null when num_pages is 0 (tails only) */
   uint16_t* esc_pool;    /* escape pool, esc_capacity u16 elements */
   int64_t esc_capacity;
   uint64_t* esc_cursor;  /* [1] u16 elements of the pool in use; bumped by the library */
@@ -239,7 +240,7 @@ int kvz_decode_attention_noalloc(const uint16_t* q, const kvz_cache* cache, cons
 
 /* The same attention over an uncompressed paged cache: the baseline the compressed path is
  * measured against (the pages compare with production FlashInfer, §IV.B).
- *   k_pages, v_pages  [num_pages][H][P][D] raw BF16, token-major
+ *   k_pages, v_pages  [num_pages][H][P][D] raw BF16, token-major (may be null when num_pages is 0)
  *   page_table        [B][max_pages_per_seq]; the first ceil(seq_lens[r] / P) entries are used
  *   status            nullable [1] sticky bits (BAD_PAGE_ID, SEQ_TOO_LONG)
  * Other arguments as kvz_decode_attention. Supported: D in {64, 128}; H_q / H <= 16. */

@@ -146,6 +146,10 @@ def test_invalid_arguments_enqueue_nothing():
         c = binding._CacheStruct(P, 4, D, 1, 8, fmt, fake, fake, 16, fake, fake, fake, fake)
         assert L.kvz_compress_pages(ctypes.byref(c), fake, fake, fake, 0, None) == want, (fmt, P, D)
         assert L.kvz_append_token(ctypes.byref(c), fake, fake, fake, 4, fake, 0, None) == want, (fmt, P, D)
+    # a cache without unit slots needs no unit array; with slots it does
+    for npages, units, want in ((0, None, binding.KVZ_OK), (1, None, binding.KVZ_ERR_INVALID_ARG)):
+        c = binding._CacheStruct(16, 4, 128, npages, 8, 0, units, fake, 16, fake, fake, fake, fake)
+        assert L.kvz_compress_pages(ctypes.byref(c), fake, fake, fake, 0, None) == want, npages
     # a workspace that does not fit in size_t: zero size, and the call refuses it
     big = (1 << 31) - 1
     assert kvz.workspace_bytes(big, 1024, 1024, 128, 16, 1 << 20, 1) == 0

@@ -408,6 +408,43 @@ def test_sequence_longer_than_the_page_table(Hq, Hkv):
 
 
 @pytest.mark.parametrize("Hq,Hkv", [(4, 4), (8, 2)])
+@pytest.mark.parametrize("fmt", [kvz.FORMAT_ESCAPE, kvz.FORMAT_ZIPFUSION])
+def test_cache_of_tails_only(Hq, Hkv, fmt):
+    """A cache allocated with no unit slots (no unit array) serves requests shorter than a page:
+    attention over their tail rows, appends that do not fill a page, status clear."""
+    P, D = 16, 128
+    w = make_workload(3, B=3, lens=[5, 0, 13], Hq=Hq, Hkv=Hkv, n_append=0)
+    kp, vp = w.pages(0), w.pages(1)
+    cache = kvz.Cache.allocate(P, Hkv, D, 0, w.B, esc_capacity=0, device=DEV, fmt=fmt)
+    assert cache.units.numel() == 0
+    lens = w.seq_lens.copy()
+    rows_k = np.zeros((w.B, Hkv, P, D), np.uint16)
+    rows_v = np.zeros_like(rows_k)
+    for r, L in enumerate(lens):
+        rows_k[r], rows_v[r] = kp[w.page_table[r, 0]], vp[w.page_table[r, 0]]
+    cache.k_tail.copy_(dev(rows_k))
+    cache.v_tail.copy_(dev(rows_v))
+    lens_d = dev((lens - 1).clip(0).astype(np.int32))
+    table = dev(np.zeros((w.B, 1), np.int32))
+    nxt_k = np.stack([rows_k[r][:, max(int(L) - 1, 0)] for r, L in enumerate(lens)])
+    nxt_v = np.stack([rows_v[r][:, max(int(L) - 1, 0)] for r, L in enumerate(lens)])
+    kvz.append_token(cache, dev(nxt_k), dev(nxt_v), table, lens_d)      # row L-1 of each request again
+    torch.cuda.synchronize()
+    assert np.array_equal(lens_d.cpu().numpy(), lens.clip(1)) and int(cache.status.item()) == 0
+    lens_d = dev(lens.astype(np.int32))
+    q = w.q()
+    out = torch.zeros((w.B, w.Hq, w.D), dtype=torch.int16, device=DEV)
+    out32 = torch.full((w.B, w.Hq, w.D), float("nan"), dtype=torch.float32, device=DEV)
+    kvz.decode_attention(dev(q), cache, table, lens_d, w.sm_scale, out, out32)
+    torch.cuda.synchronize()
+    assert int(cache.status.item()) == 0
+    from oracle import c_oracle
+    tail_table = np.arange(w.B, dtype=np.int32).reshape(w.B, 1)
+    ref = c_oracle.dense_attention_rows(q, rows_k, rows_v, tail_table, lens, w.sm_scale, _all_rows(w))
+    check_rows(host16(out).reshape(-1, w.D), out32.cpu().numpy().reshape(-1, w.D), ref, f"tails only, format {fmt}")
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(4, 4), (8, 2)])
 @pytest.mark.parametrize("pps", [0, 1])
 def test_cache_without_unit_slots(Hq, Hkv, pps):
     """num_pages = 0: every full page is a bad id (KVZ_STATUS_BAD_PAGE_ID) and is skipped; each
