@@ -362,7 +362,8 @@ def main() -> int:
     cpu = parity = None
     if not args.no_cpu and fmt == kvz.FORMAT_ESCAPE:   # the CPU oracle baseline decodes the library's format
         cpu, ref_rows, ref = cpu_baseline(w, kp, vp, min(args.cpu_requests, B), units_bytes, pool_esc, tail_bytes, log)
-        parity = parity_check(out_bf16.cpu().numpy().view(np.uint16), out32.cpu().numpy(), ref_rows, ref, same_bits)
+        parity = parity_check(out_bf16.cpu().numpy().view(np.uint16), out32.cpu().numpy(), ref_rows, ref, same_bits,
+                              score_bound_of(w, kp, vp, ref_rows))
         log(f"parity: {parity}")
 
     # Appends in steady state, after everything else (they overwrite the tails): up to one page
@@ -479,21 +480,46 @@ def read_ceiling(kvz, cache, table, lens, full, H, U, steps, dev, pair):
     return best
 
 
-def parity_check(out16, out32, rows, ref, same_bits):
+def parity_check(out16, out32, rows, ref, same_bits, bound_of=None):
     """The timed call's output against this run's oracle rows (the CPU baseline's): BF16 within
-    max(2e-2, 2^-7 |o|) per element, fp32 within 1e-4 max_d |o| per row."""
+    max(2e-2, 2^-7 |o|) + 1e-4 max_d |o| per element (the row's fp32 budget: a rounded fp32
+    result is no closer to o than the fp32 result), fp32 within 1e-4 max_d |o| per row. A row
+    that misses them may pass within those bounds plus its first-order score-rounding bound
+    (bound_of(i); rows whose top logits nearly tie at a large scale): counted apart."""
     import numpy as np
     idx = tuple(np.array(rows).T)
     got16 = (out16[idx].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
     got32 = out32[idx].astype(np.float64)
     err16 = np.abs(got16 - ref)
-    ok16 = bool(np.all(err16 <= np.maximum(2e-2, 2.0 ** -7 * np.abs(ref))))
     nrm = np.abs(ref).max(axis=-1)
-    e32 = np.abs(got32 - ref).max(axis=-1) / np.where(nrm > 0, nrm, 1.0)
-    ok32 = bool(np.all(e32 <= 1e-4))
-    return {"rows": len(rows), "max_bf16_abs_err": float(err16.max()), "max_f32_normwise_err": float(e32.max()),
-            "bf16_ok": ok16, "f32_ok": ok32, "timed_output_reproduced": same_bits,
-            "ok": ok16 and ok32 and same_bits}
+    tol16 = np.maximum(2e-2, 2.0 ** -7 * np.abs(ref)) + 1e-4 * nrm[:, None]
+    e32 = np.abs(got32 - ref).max(axis=-1)
+    miss = (err16 > tol16).any(axis=-1) | (e32 > 1e-4 * nrm)
+    n_bound = 0
+    if bound_of is not None:
+        for i in np.flatnonzero(miss):
+            e = bound_of(int(i))
+            if (err16[i] <= tol16[i] + e).all() and e32[i] <= 1e-4 * nrm[i] + e:
+                miss[i] = False
+                n_bound += 1
+    ok16 = bool(not ((err16 > tol16) & miss[:, None]).any())
+    ok32 = bool(not (miss & (e32 > 1e-4 * nrm)).any())
+    rel = e32 / np.where(nrm > 0, nrm, 1.0)
+    return {"rows": len(rows), "max_bf16_abs_err": float(err16.max()), "max_f32_normwise_err": float(rel.max()),
+            "rows_within_first_order_bound": n_bound, "bf16_ok": ok16, "f32_ok": ok32,
+            "timed_output_reproduced": same_bits, "ok": ok16 and ok32 and same_bits}
+
+
+def score_bound_of(w, kp, vp, rows):
+    """bound_of(i) for parity_check: the oracle's first-order score-rounding bound of row i."""
+    from oracle import attention as oa
+    q, grp = w.q(), w.Hq // w.Hkv
+
+    def bound_of(i):
+        r, h = rows[i]
+        K, V = oa.gather_dense(kp, vp, w.page_table[r], int(w.seq_lens[r]), w.P)
+        return oa.score_rounding_bound(q[r, h], K[:, h // grp], V[:, h // grp], w.sm_scale)
+    return bound_of
 
 
 def layer_loop(kvz, cache, q, table, lens, w, ws, pps, nl, dev, reps=20):

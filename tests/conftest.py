@@ -13,6 +13,13 @@ def pytest_configure(config):
     config.addinivalue_line("markers", "slow: full-size workload")
 
 
+def pytest_terminal_summary(terminalreporter):
+    kvz_testlib = sys.modules.get("kvz_testlib")
+    if kvz_testlib is not None and kvz_testlib.CONDITIONED:
+        terminalreporter.write_line(f"attention rows that passed only under their first-order score-rounding bound: "
+                                    f"{len(kvz_testlib.CONDITIONED)}")
+
+
 _FULL = {}
 
 

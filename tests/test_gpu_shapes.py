@@ -89,3 +89,36 @@ def test_largest_blocks(P, D, Hq, Hkv, cfg):
         assert int(cache.status.item()) == 0
         check_rows(host16(out).reshape(-1, D), out32.cpu().numpy().reshape(-1, D), ref,
                    f"cfg{cfg} P{P} D{D} {Hq}/{Hkv} pps{pps}")
+
+
+@pytest.mark.parametrize("kw", [
+    dict(B=12, lens=[26, 32, 5, 53, 0, 1, 24, 13, 50, 53, 42, 55], Hq=16, Hkv=8, P=32),
+    dict(B=3, lens=[37, 0, 48], Hq=40, Hkv=5, P=16),
+])
+def test_wide_dynamic_range_batch(kw):
+    """Escape-stress batches with rows of test_tolerance.py: the first has the row whose small
+    elements need the fp32 budget in the BF16 bound (16 query heads over 8 KV heads, 32-token
+    pages, requests with a tail only, with one full page, and empty); the second a near-tie row,
+    (0, 29), that only its first-order score-rounding bound admits (40 query heads over 5). Every
+    row within the bounds, compressed under the device's split choice, one page per split and
+    two, and dense."""
+    kw = dict(kw)
+    w = make_workload(5, n_append=0, lens=np.array(kw.pop("lens")), D=128, **kw)
+    kp, vp = w.pages(0), w.pages(1)
+    cache, seq = build_cache(w, kp, vp)
+    q = w.q()
+    rows = [(r, h) for r in range(w.B) for h in range(w.Hq)]
+    ref = oracle_rows(w, kp, vp, q, rows)
+    out = torch.zeros((w.B, w.Hq, w.D), dtype=torch.int16, device=DEV)
+    out32 = torch.zeros((w.B, w.Hq, w.D), dtype=torch.float32, device=DEV)
+    for pps in (0, 1, 2):
+        kvz.decode_attention(dev(q), cache, dev(w.page_table), seq, w.sm_scale, out, out32, pages_per_split=pps)
+        torch.cuda.synchronize()
+        assert int(cache.status.item()) == 0
+        check_rows(host16(out).reshape(-1, w.D), out32.cpu().numpy().reshape(-1, w.D), ref, f"compressed pps{pps}")
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    kvz.decode_attention_dense(dev(q), dev(kp), dev(vp), dev(w.page_table), dev(w.seq_lens), w.sm_scale, out, out32,
+                               status=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    check_rows(host16(out).reshape(-1, w.D), out32.cpu().numpy().reshape(-1, w.D), ref, "dense")
