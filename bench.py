@@ -389,6 +389,27 @@ def main() -> int:
         append_us = float(np.median(nofill))
     if fill:
         append_fill_us = float(np.median(fill))
+    # the same number of calls back to back through a prepared call, as a decode loop issues them
+    # (every request's tail fills once among P calls, so the mean includes that request's page
+    # compression)
+    append_steady_us = None
+    n_app = 0
+    lens2.copy_(lens)   # from the same lengths again (the tails and units hold zeros by now)
+    lh = lens2.cpu().numpy().astype(np.int64)
+    for _ in range(P):
+        if np.any(lh + 1 > w.max_pages * P):
+            break
+        lh += 1
+        n_app += 1
+    if n_app:
+        app = kvz.prepare_append_token(cache, kz, kz, table, lens2)
+        a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a0.record()
+        for _ in range(n_app):
+            app()
+        a1.record()
+        torch.cuda.synchronize()
+        append_steady_us = a0.elapsed_time(a1) * 1e3 / n_app
 
     res = {
         "metric": "decode-attn tokens/s + compressed HBM GB/s (% peak), 8K ctx batch 32",
@@ -432,6 +453,7 @@ def main() -> int:
         "layers": layers,
         "append_us": round(append_us, 1) if append_us is not None else None,
         "append_fill_us": round(append_fill_us, 1) if append_fill_us is not None else None,
+        "append_steady_us": round(append_steady_us, 2) if append_steady_us is not None else None,
         "compress_gbps_dense_input": round(len(ids) * H * P * D * 4 / compress_s / 1e9, 1),
         "gpu": f"{torch.cuda.get_device_name(0)} ({torch.cuda.get_device_properties(0).gcnArchName})",
         "software": {"torch": torch.__version__, "hip": torch.version.hip},

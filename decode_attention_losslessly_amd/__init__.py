@@ -9,4 +9,5 @@ from .kvz import (FORMAT_ESCAPE, FORMAT_ZIPFUSION, Cache, KvzError, append_token
                   compact_pool, compress_pages, decode_attention, decode_attention_noalloc,
                   decode_attention_dense, decode_attention_dense_splits, decode_attention_splits,
                   decompress_pages, merge_splits, inline_capacity, meta_bytes, num_splits, payload_bytes, unit_bytes,
-                  workspace_bytes, PreparedAttention, prepare_decode_attention, prepare_decode_attention_dense)
+                  workspace_bytes, PreparedAttention, prepare_decode_attention, prepare_decode_attention_dense,
+                  PreparedAppend, prepare_append_token)

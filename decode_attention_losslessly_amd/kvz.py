@@ -435,6 +435,39 @@ class PreparedAttention:
         self.merge()
 
 
+class PreparedAppend:
+    """One append_token call, its buffers checked and its arguments marshalled once, for a decode
+    loop that appends the new token's K and V from the same buffers every step (the lengths
+    advance on the device). A call enqueues kvz_append_token on the stream given at preparation.
+    It keeps its buffers alive and holds their addresses: prepare again after anything replaces a
+    buffer (kvz_compact_pool installs a new pool)."""
+
+    def __init__(self, args, keep):
+        self._fn = lib().kvz_append_token
+        self._args = args
+        self._keep = keep
+
+    def __call__(self) -> None:
+        rc = self._fn(*self._args)
+        if rc:
+            raise KvzError(rc, "kvz_append_token")
+
+
+def prepare_append_token(cache: Cache, k_new: torch.Tensor, v_new: torch.Tensor, page_table: torch.Tensor,
+                         seq_lens: torch.Tensor, stream=None) -> PreparedAppend:
+    """append_token as a PreparedAppend (arguments as append_token)."""
+    dev = cache.units.device
+    B = int(page_table.shape[0])
+    max_pages = _table(page_table, B, dev)
+    _arg(k_new, "k_new", _HALF, B * cache.H * cache.D, dev)
+    _arg(v_new, "v_new", _HALF, B * cache.H * cache.D, dev)
+    _arg(seq_lens, "seq_lens", (torch.int32,), B, dev)
+    s = torch.cuda.current_stream() if stream is None else stream
+    cs = cache.struct()
+    args = (ctypes.byref(cs), _ptr(k_new), _ptr(v_new), _ptr(page_table), max_pages, _ptr(seq_lens), B, _stream(s))
+    return PreparedAppend(args, (cache, cs, k_new, v_new, page_table, seq_lens, s))
+
+
 def _merge_args(workspace, seq_lens, B, Hq, H, D, P, max_pages, pps, dense, out, out_f32, s):
     return (_ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(seq_lens), B, Hq, H, D, P, max_pages,
             pps, 1 if dense else 0, _ptr(out), _ptr(out_f32), s)

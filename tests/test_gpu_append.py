@@ -15,8 +15,11 @@ from kvz_testlib import DEV, check_rows, dev, full_page_ids, host16, oracle_rows
 pytestmark = pytest.mark.gpu
 
 
+@pytest.mark.parametrize("prepared", [False, True])
 @pytest.mark.parametrize("cfg,H,Hq", [(3, 4, 4), (4, 2, 14), (5, 2, 2)])
-def test_append_across_page_fill(cfg, H, Hq):
+def test_append_across_page_fill(cfg, H, Hq, prepared):
+    """prepared: the steps go through one prepare_append_token call, the new rows copied into the
+    buffers it was prepared with."""
     n_app = 19
     L0 = np.array([14, 15, 31, 0, 40], np.int32)
     w = make_workload(cfg, B=5, lens=L0 + n_app, Hq=Hq, Hkv=H, n_append=0)
@@ -30,10 +33,18 @@ def test_append_across_page_fill(cfg, H, Hq):
     cache.v_tail.copy_(dev(tv))
     lens = dev(L0)
     table = dev(w.page_table)
+    kbuf = torch.zeros((w.B, w.Hkv, w.D), dtype=torch.int16, device=DEV)
+    vbuf = torch.zeros_like(kbuf)
+    app = kvz.prepare_append_token(cache, kbuf, vbuf, table, lens) if prepared else None
     for j in range(n_app):
         kn = np.stack([w.token(r, int(L0[r]) + j, 0) for r in range(w.B)])
         vn = np.stack([w.token(r, int(L0[r]) + j, 1) for r in range(w.B)])
-        kvz.append_token(cache, dev(kn), dev(vn), table, lens)
+        if prepared:
+            kbuf.copy_(dev(kn))
+            vbuf.copy_(dev(vn))
+            app()
+        else:
+            kvz.append_token(cache, dev(kn), dev(vn), table, lens)
     torch.cuda.synchronize()
     assert int(cache.status.item()) == 0
     assert np.array_equal(lens.cpu().numpy(), L0 + n_app)
