@@ -33,6 +33,7 @@ struct SplitPlan {
   int S;           // partial slots per (request, query head)
   int C_lo, C_hi;  // bounds on the pages per split
   int slots;       // waves of the kernel resident at once on the device
+  int slots_pref;  // > 0: a smaller wave count to aim for first (see plan_work)
   int ranks;       // > 0: the ranked schedule below may be used, with this many big ranks
   int rank_min;    // ... when a big chunk holds at least this many pages on average (0: always)
   int* chosen;     // the pages per split used (or minus the chunks per item when ranked),
@@ -244,18 +245,34 @@ __device__ __forceinline__ bool plan_work(const SplitPlan& pl, const int32_t* se
   const PlanPages pp = plan_load(seq_lens, B, P, max_pages, dense, lane);
   if (pl.C_hi > pl.C_lo && C < pl.C_hi) {
     // With N = ipr * (pages of the batch) and `items` = ipr * B, the splits at C lie between
-    // N / C and N / C + items (the total only falls as C grows): no C below N / slots fits,
-    // and every C from N / (slots - items) on does. Search between the two.
+    // N / C and N / C + items (the total only falls as C grows): no C below N / s fits s waves,
+    // and every C from N / (s - items) on does. Search between the two.
     const uint64_t N = plan_page_sum(pp, seq_lens, B, P, max_pages, dense, lane) * (uint64_t)ipr;
-    int lo = (int)min((uint64_t)pl.C_hi, max((uint64_t)pl.C_lo, (N + slots - 1) / slots));
-    int hi = pl.C_hi;
-    if (slots > items) hi = (int)min((uint64_t)hi, max((uint64_t)lo, (N + slots - items - 1) / (slots - items)));
-    while (lo < hi) {
-      const int mid = (lo + hi) >> 1;
-      if (plan_total(pp, seq_lens, B, P, max_pages, dense, mid, lane) * ipr <= slots) hi = mid;
-      else lo = mid + 1;
+    auto smallest_fit = [&](uint64_t s) {
+      int lo = (int)min((uint64_t)pl.C_hi, max((uint64_t)pl.C_lo, (N + s - 1) / s));
+      int hi = pl.C_hi;
+      if (s > items) hi = (int)min((uint64_t)hi, max((uint64_t)lo, (N + s - items - 1) / (s - items)));
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (plan_total(pp, seq_lens, B, P, max_pages, dense, mid, lane) * ipr <= s) hi = mid;
+        else lo = mid + 1;
+      }
+      return lo;
+    };
+    // A kernel may prefer fewer waves than it can hold (slots_pref: the grouped-query kernel
+    // streams faster at two waves per SIMD than at three, measured): that target is kept when
+    // its splits come to at least 7/8 of it, else the batch's items divide it badly (96 requests
+    // of 8 KV heads: 1,536 waves) and the full count is used.
+    bool done = false;
+    const uint64_t pref = (uint64_t)pl.slots_pref;
+    if (pref > items && pref < slots) {
+      const int Cp = smallest_fit(pref);
+      if (8 * plan_total(pp, seq_lens, B, P, max_pages, dense, Cp, lane) * ipr >= 7 * pref) {
+        C = Cp;
+        done = true;
+      }
     }
-    C = lo;
+    if (!done) C = smallest_fit(slots);
   }
   if (wave_id == 0 && lane == 0) *pl.chosen = C;
   // find the request whose splits hold this wave's number, 64 requests at a time

@@ -373,6 +373,7 @@ int launch_attn_gqa(const uint16_t* q, const uint8_t* units, const uint16_t* poo
   static int slots[64];
   const dim3 block(64 * kGqaWaves);
   plan.slots = resident_waves(attn_gqa_kernel, block.x, slots, 64);
+  plan.slots_pref = 2 * plan.slots / 3;   // two of its three waves per SIMD (see plan_work)
   if (plan.slots <= 0) plan.slots = gqa_items(B, Hq, H) * plan.S;
   hipLaunchKernelGGL(attn_gqa_kernel, dim3(plan_blocks(plan, gqa_items(B, Hq, H), kGqaWaves)), block, 0, stream, q, units,
                      pool, pool_cap, esc_cursor, k_tail, v_tail, page_table, max_pages, seq_lens, B, Hq, H, P, num_pages, plan, scale,
@@ -388,6 +389,7 @@ int launch_attn_dense_gqa(const uint16_t* q, const uint16_t* k_pages, const uint
   static int slots[64];
   const dim3 block(64 * kGqaWaves);
   plan.slots = resident_waves(attn_dense_gqa_kernel, block.x, slots, 64);
+  plan.slots_pref = 2 * plan.slots / 3;   // as the compressed kernel (measured: as fast or faster)
   if (plan.slots <= 0) plan.slots = gqa_items(B, Hq, H) * plan.S;
   hipLaunchKernelGGL(attn_dense_gqa_kernel, dim3(plan_blocks(plan, gqa_items(B, Hq, H), kGqaWaves)), block, 0, stream,
                      q, k_pages, v_pages, pt, max_pages, seq_lens, B, Hq, H, P, num_pages, plan, scale, ws_acc, ws_ml,

@@ -450,6 +450,7 @@ int launch_attn_zf_gqa(const uint16_t* q, const uint8_t* units, const uint16_t* 
   const bool head = zf_head_holds_meta(P, 128);
   plan.slots = head ? resident_waves(attn_zf_gqa_kernel<true>, block.x, slots_head, 64)
                     : resident_waves(attn_zf_gqa_kernel<false>, block.x, slots, 64);
+  plan.slots_pref = 2 * plan.slots / 3;   // two of its three waves per SIMD, as attn_gqa_kernel
   if (plan.slots <= 0) plan.slots = (int)(items * plan.S);
   if (head)
     hipLaunchKernelGGL(attn_zf_gqa_kernel<true>, dim3(plan_blocks(plan, items, kZfWaves)), block, 0, stream, q, units,

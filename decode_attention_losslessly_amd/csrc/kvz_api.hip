@@ -219,6 +219,7 @@ static kvz::SplitPlan make_plan(int C, int S, int max_pages, bool fixed, int32_t
   p.C_lo = C;
   p.C_hi = fixed ? C : (max_pages > C ? max_pages : C);
   p.slots = 0;   // filled in by the launch from the kernel's occupancy
+  p.slots_pref = 0;
   p.ranks = 0;   // the ranked schedule: set only for the kernel that implements it
   p.rank_min = 0;
   p.chosen = chosen;
