@@ -5,7 +5,8 @@ value distributions of all five workloads (the escape-stress one included, for t
 and every kind of split choice (chosen on the device, fixed, and the ranked schedule forced).
 Each case also rebuilds its units bit for bit through every decode route of the kernels, and runs
 again over the same pages in ZipFusion's block format (multi-head or grouped-query kernel).
-Each case is drawn from its own seed, so a failure names a reproducible case."""
+Each case is drawn from its own seed, so a failure names a reproducible case. A second set draws
+larger batches, longer requests and pages of up to 512 tokens."""
 import numpy as np
 import pytest
 import torch
@@ -34,9 +35,35 @@ def _case(seed):
     return dict(cfg=cfg, B=B, lens=lens, Hq=Hkv * grp, Hkv=Hkv, D=D, P=P), pps
 
 
+def _large_case(seed):
+    """larger batches (up to 39 requests), longer requests (up to 40 pages), pages of up to 256
+    tokens (512 at head dim 64), two requests ending on a page boundary"""
+    rng = np.random.default_rng(90000 + seed)
+    D = int(rng.choice([64, 128]))
+    P = int(rng.choice([16, 16, 32, 64, 128, 256] + ([512] if D == 64 else [])))
+    grp = 1 if D == 64 else int(rng.choice([1, 2, 4, 7, 8, 16]))
+    Hkv = int(rng.integers(1, 5))
+    B = int(rng.integers(1, 40))
+    lens = rng.integers(0, int(rng.choice([3, 10, 40])) * P + 1, size=B)
+    for _ in range(2):
+        k = rng.integers(0, B)
+        lens[k] = (lens[k] // P) * P
+    cfg = int(rng.integers(1, 7))
+    pps = int(rng.choice([0, 0, 0, 1, 4, 9, -1, -4]))
+    return dict(cfg=cfg, B=B, lens=lens, Hq=Hkv * grp, Hkv=Hkv, D=D, P=P), pps
+
+
 @pytest.mark.parametrize("seed", range(N_CASES))
 def test_random_shapes_match_oracle(seed):
-    kw, pps = _case(seed)
+    _check_case(seed, *_case(seed))
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_random_large_shapes_match_oracle(seed):
+    _check_case(seed, *_large_case(seed))
+
+
+def _check_case(seed, kw, pps):
     cfg = kw.pop("cfg")
     what = f"seed {seed}: cfg{cfg} B={kw['B']} {kw['Hq']}/{kw['Hkv']} D={kw['D']} P={kw['P']} pps={pps}"
     print(what, flush=True)
