@@ -68,6 +68,8 @@ def parse():
                     help="pages per split-K work item (0: the library's choice)")
     ap.add_argument("--batch", type=int, default=None, help="override the workload's batch size")
     ap.add_argument("--context", type=int, default=None, help="override the workload's context length")
+    ap.add_argument("--q-heads", type=int, default=None, help="override the workload's query heads")
+    ap.add_argument("--kv-heads", type=int, default=None, help="override the workload's KV heads")
     ap.add_argument("--no-dense", action="store_true", help="skip the uncompressed baseline")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-requests", type=int, default=32, help="requests in the CPU baseline sample")
@@ -113,9 +115,9 @@ def main() -> int:
     log = lambda *a: print("[bench]", *a, file=sys.stderr, flush=True)
     t16 = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16 if a.dtype == np.uint16 else a.dtype)).to(dev)
 
-    w = make_workload(args.config, B=args.batch, L=args.context)
-    if args.batch is not None or args.context is not None:
-        w.name = f"{w.name}@b{w.B}_ctx{int(w.seq_lens.max())}"
+    w = make_workload(args.config, B=args.batch, L=args.context, Hq=args.q_heads, Hkv=args.kv_heads)
+    if args.batch is not None or args.context is not None or args.q_heads is not None or args.kv_heads is not None:
+        w.name = f"{w.name}@b{w.B}_ctx{int(w.seq_lens.max())}_h{w.Hq}x{w.Hkv}"
     B, Hq, H, D, P = w.B, w.Hq, w.Hkv, w.D, w.P
     t0 = time.perf_counter()
     kp, vp = w.pages(0), w.pages(1)

@@ -259,8 +259,7 @@ static int check_attention_shape(int B, int Hq, int Hkv, int D, int P, int max_p
   if (B < 0 || Hq <= 0 || Hkv <= 0 || max_pages < 0) return KVZ_ERR_INVALID_ARG;
   if (!shape_ok(P, D) || Hq % Hkv || !table_fits(max_pages, P)) return KVZ_ERR_UNSUPPORTED;
   if (D != 64 && D != 128) return KVZ_ERR_UNSUPPORTED;
-  const int grp = Hq / Hkv;
-  if (grp > 1 && (D != 128 || grp > 16)) return KVZ_ERR_UNSUPPORTED;
+  if (Hq > Hkv && D != 128) return KVZ_ERR_UNSUPPORTED;   // grouped queries: the MFMA kernels, head dim 128
   return KVZ_OK;
 }
 

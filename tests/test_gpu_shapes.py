@@ -122,3 +122,34 @@ def test_wide_dynamic_range_batch(kw):
     torch.cuda.synchronize()
     assert int(status.item()) == 0
     check_rows(host16(out).reshape(-1, w.D), out32.cpu().numpy().reshape(-1, w.D), ref, "dense")
+
+
+@pytest.mark.parametrize("Hq,Hkv,P", [(24, 1, 32), (32, 1, 16), (64, 2, 16)])
+def test_large_query_groups(Hq, Hkv, P):
+    """Query groups beyond 16 heads (3, 4 and 8 chunks of 8 query heads per KV head; the last two
+    multi-query shapes): both cache formats and the uncompressed baseline against the oracle, smooth
+    and escape-stress data, under the device's split choice and one page per split."""
+    lens = [1, P - 1, 3 * P + 5, 7 * P]
+    for cfg in (1, 5):
+        w = make_workload(cfg, B=len(lens), lens=lens, Hq=Hq, Hkv=Hkv, D=128, P=P, n_append=0)
+        kp, vp = w.pages(0), w.pages(1)
+        q = w.q()
+        rows = [(r, h) for r in range(w.B) for h in range(w.Hq)]
+        ref = oracle_rows(w, kp, vp, q, rows)
+        out = torch.zeros((w.B, w.Hq, w.D), dtype=torch.int16, device=DEV)
+        out32 = torch.full((w.B, w.Hq, w.D), float("nan"), dtype=torch.float32, device=DEV)
+        for fmt in (kvz.FORMAT_ESCAPE, kvz.FORMAT_ZIPFUSION):
+            cache, seq = build_cache(w, kp, vp, fmt=fmt)
+            for pps in (0, 1):
+                kvz.decode_attention(dev(q), cache, dev(w.page_table), seq, w.sm_scale, out, out32,
+                                     pages_per_split=pps)
+                torch.cuda.synchronize()
+                assert int(cache.status.item()) == 0
+                check_rows(host16(out).reshape(-1, w.D), out32.cpu().numpy().reshape(-1, w.D), ref,
+                           f"cfg{cfg} {Hq}/{Hkv} P{P} format {fmt} pps{pps}")
+        status = torch.zeros(1, dtype=torch.int32, device=DEV)
+        kvz.decode_attention_dense(dev(q), dev(kp), dev(vp), dev(w.page_table), dev(w.seq_lens), w.sm_scale, out,
+                                   out32, status=status)
+        torch.cuda.synchronize()
+        assert int(status.item()) == 0
+        check_rows(host16(out).reshape(-1, w.D), out32.cpu().numpy().reshape(-1, w.D), ref, f"cfg{cfg} {Hq}/{Hkv} dense")
