@@ -70,6 +70,7 @@ def parse():
     ap.add_argument("--context", type=int, default=None, help="override the workload's context length")
     ap.add_argument("--q-heads", type=int, default=None, help="override the workload's query heads")
     ap.add_argument("--kv-heads", type=int, default=None, help="override the workload's KV heads")
+    ap.add_argument("--head-dim", type=int, default=None, help="override the workload's head dim (64 or 128)")
     ap.add_argument("--no-dense", action="store_true", help="skip the uncompressed baseline")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-requests", type=int, default=32, help="requests in the CPU baseline sample")
@@ -115,9 +116,9 @@ def main() -> int:
     log = lambda *a: print("[bench]", *a, file=sys.stderr, flush=True)
     t16 = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16 if a.dtype == np.uint16 else a.dtype)).to(dev)
 
-    w = make_workload(args.config, B=args.batch, L=args.context, Hq=args.q_heads, Hkv=args.kv_heads)
-    if args.batch is not None or args.context is not None or args.q_heads is not None or args.kv_heads is not None:
-        w.name = f"{w.name}@b{w.B}_ctx{int(w.seq_lens.max())}_h{w.Hq}x{w.Hkv}"
+    w = make_workload(args.config, B=args.batch, L=args.context, Hq=args.q_heads, Hkv=args.kv_heads, D=args.head_dim)
+    if any(a is not None for a in (args.batch, args.context, args.q_heads, args.kv_heads, args.head_dim)):
+        w.name = f"{w.name}@b{w.B}_ctx{int(w.seq_lens.max())}_h{w.Hq}x{w.Hkv}_d{w.D}"
     B, Hq, H, D, P = w.B, w.Hq, w.Hkv, w.D, w.P
     t0 = time.perf_counter()
     kp, vp = w.pages(0), w.pages(1)
@@ -344,16 +345,17 @@ def main() -> int:
     attn_mean = split_mean_us   # mean launch duration of the split kernel, back to back
     achieved = comp_bytes / (attn_mean * 1e-6) / 1e9
     traffic = None
-    ksrc = "attn_zf.hip" if fmt == kvz.FORMAT_ZIPFUSION else ("attn_mha.hip" if Hq == H else "attn_gqa.hip")
+    mha = Hq == H or D != 128   # grouped queries at head dim 64 run on the multi-head kernels
+    ksrc = "attn_zf.hip" if fmt == kvz.FORMAT_ZIPFUSION else ("attn_mha.hip" if mha else "attn_gqa.hip")
     tfile = os.path.join(ROOT, "profiles", f"traffic_{w.name}.json")
     if os.path.exists(tfile):
         t = json.load(open(tfile))
         if t.get("source_digest") == source_digest(ksrc):
             traffic = t.get("bytes_per_launch")
     if fmt == kvz.FORMAT_ZIPFUSION:
-        kname = f"attn_zf_kernel<{D}>" if Hq == H else "attn_zf_gqa_kernel"
+        kname = f"attn_zf_kernel<{D}>" if mha else "attn_zf_gqa_kernel"
     else:
-        kname = f"attn_mha_kernel<{D}>" if Hq == H else "attn_gqa_kernel"
+        kname = f"attn_mha_kernel<{D}>" if mha else "attn_gqa_kernel"
     roofline = dict(kernel=kname, bound="hbm",
                     achieved=round(achieved, 1), peak=PEAK_HBM_GBPS, unit="GB/s",
                     frac=round(achieved / PEAK_HBM_GBPS, 4), traffic=traffic,

@@ -113,17 +113,18 @@ __device__ __forceinline__ void dense_compute(DenseState& st, const uint32_t (&q
 template <int D>
 __global__ __launch_bounds__(64 * kDenseWaves) void attn_dense_mha_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_pages, const uint16_t* __restrict__ v_pages,
-    const int32_t* __restrict__ page_table, int max_pages, const int32_t* __restrict__ seq_lens, int B, int H, int P,
-    int num_pages, SplitPlan plan, float scale, float* __restrict__ ws_acc, float* __restrict__ ws_ml,
-    uint32_t* __restrict__ status) {
+    const int32_t* __restrict__ page_table, int max_pages, const int32_t* __restrict__ seq_lens, int B, int H,
+    int grp, int P, int num_pages, SplitPlan plan, float scale, float* __restrict__ ws_acc,
+    float* __restrict__ ws_ml, uint32_t* __restrict__ status) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int Hq = H * grp;   // query heads, one wave each; grp of them read each KV head
   WorkItem wi;
-  if (!plan_work(plan, seq_lens, B, P, max_pages, true, H, (int)uniform(blockIdx.x * kDenseWaves + wave), lane, wi))
+  if (!plan_work(plan, seq_lens, B, P, max_pages, true, Hq, (int)uniform(blockIdx.x * kDenseWaves + wave), lane, wi))
     return;
-  const int S = plan.S, C = wi.C, s = wi.s, h = wi.k, r = wi.r;
+  const int S = plan.S, C = wi.C, s = wi.s, hq = wi.k, h = hq / grp, r = wi.r;
   int L = request_len(wi, seq_lens);
   if (L > max_pages * P || L < 0) {
-    if (lane == 0 && s == 0 && h == 0 && status) atomicOr(status, kStatusSeqTooLong);
+    if (lane == 0 && s == 0 && hq == 0 && status) atomicOr(status, kStatusSeqTooLong);
     L = L < 0 ? 0 : max_pages * P;
   }
   const int npages = (L + P - 1) / P;
@@ -139,7 +140,7 @@ __global__ __launch_bounds__(64 * kDenseWaves) void attn_dense_mha_kernel(
   }
   uint32_t qv[D / 8];
   {
-    const uint32_t* qrow = reinterpret_cast<const uint32_t*>(q + ((size_t)r * H + h) * D + (lane & 3) * (D / 4));
+    const uint32_t* qrow = reinterpret_cast<const uint32_t*>(q + ((size_t)r * Hq + hq) * D + (lane & 3) * (D / 4));
 #pragma unroll
     for (int j = 0; j < D / 8; ++j) qv[j] = qrow[j];
   }
@@ -174,7 +175,7 @@ __global__ __launch_bounds__(64 * kDenseWaves) void attn_dense_mha_kernel(
   lsum += __shfl_xor(lsum, 8);
   lsum += __shfl_xor(lsum, 16);
   lsum += __shfl_xor(lsum, 32);
-  const size_t row = (size_t)r * H + h;
+  const size_t row = (size_t)r * Hq + hq;
   float* acc = ws_acc + (row * S + s) * D;
   if (D == 128 || lane < 32) {
     acc[2 * (D == 128 ? lane : (lane & 31)) + 0] = st.acc[0];
@@ -187,10 +188,11 @@ __global__ __launch_bounds__(64 * kDenseWaves) void attn_dense_mha_kernel(
 }
 
 int launch_attn_dense_mha(const uint16_t* q, const uint16_t* k_pages, const uint16_t* v_pages, const int32_t* pt,
-                          int max_pages, const int32_t* seq_lens, int B, int H, int D, int P, int num_pages,
-                          SplitPlan plan, float scale, float* ws_acc, float* ws_ml, uint32_t* status,
+                          int max_pages, const int32_t* seq_lens, int B, int Hq, int H, int D, int P,
+                          int num_pages, SplitPlan plan, float scale, float* ws_acc, float* ws_ml, uint32_t* status,
                           hipStream_t stream) {
   static int slots128[64], slots64[64];
+  if (H <= 0 || Hq % H) return -2;
   const dim3 block(64 * kDenseWaves);
   if (D == 128) {
     plan.slots = resident_waves(attn_dense_mha_kernel<128>, block.x, slots128, 64);
@@ -199,15 +201,15 @@ int launch_attn_dense_mha(const uint16_t* q, const uint16_t* k_pages, const uint
   } else {
     return -2;
   }
-  rank_fit(plan, plan.slots, (long)B * H);
-  if (plan.slots <= 0) plan.slots = B * H * plan.S;
-  const dim3 grid(plan_blocks(plan, (long)B * H, kDenseWaves));
+  rank_fit(plan, plan.slots, (long)B * Hq);
+  if (plan.slots <= 0) plan.slots = B * Hq * plan.S;
+  const dim3 grid(plan_blocks(plan, (long)B * Hq, kDenseWaves));
   if (D == 128)
     hipLaunchKernelGGL((attn_dense_mha_kernel<128>), grid, block, 0, stream, q, k_pages, v_pages, pt, max_pages,
-                       seq_lens, B, H, P, num_pages, plan, scale, ws_acc, ws_ml, status);
+                       seq_lens, B, H, Hq / H, P, num_pages, plan, scale, ws_acc, ws_ml, status);
   else
     hipLaunchKernelGGL((attn_dense_mha_kernel<64>), grid, block, 0, stream, q, k_pages, v_pages, pt, max_pages,
-                       seq_lens, B, H, P, num_pages, plan, scale, ws_acc, ws_ml, status);
+                       seq_lens, B, H, Hq / H, P, num_pages, plan, scale, ws_acc, ws_ml, status);
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 

@@ -95,18 +95,19 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) __attribute__((amdgpu_waves_pe
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ units, const uint16_t* __restrict__ pool,
     int64_t pool_cap, const uint64_t* __restrict__ esc_cursor, const uint16_t* __restrict__ k_tail,
     const uint16_t* __restrict__ v_tail, const int32_t* __restrict__ page_table, int max_pages,
-    const int32_t* __restrict__ seq_lens, int B, int H, int P, int num_pages, SplitPlan plan, float scale,
+    const int32_t* __restrict__ seq_lens, int B, int H, int grp, int P, int num_pages, SplitPlan plan, float scale,
     float* __restrict__ ws_acc, float* __restrict__ ws_ml, uint32_t* __restrict__ status) {
   __shared__ __align__(16) uint16_t lds_all[kWavesPerBlock][esc_lds_elems<D>()];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int Hq = H * grp;   // query heads: grp of them read each KV head (one wave each)
   WorkItem wi;
-  if (!plan_work(plan, seq_lens, B, P, max_pages, false, H, (int)uniform(blockIdx.x * kWavesPerBlock + wave), lane, wi))
+  if (!plan_work(plan, seq_lens, B, P, max_pages, false, Hq, (int)uniform(blockIdx.x * kWavesPerBlock + wave), lane, wi))
     return;
-  const int S = plan.S, C = wi.C, s = wi.s, h = wi.k, r = wi.r;
+  const int S = plan.S, C = wi.C, s = wi.s, hq = wi.k, h = hq / grp, r = wi.r;
   uint16_t* lds = lds_all[wave];
   int L = request_len(wi, seq_lens);
   if (L > max_pages * P || L < 0) {
-    if (lane == 0 && s == 0 && h == 0) atomicOr(status, kStatusSeqTooLong);
+    if (lane == 0 && s == 0 && hq == 0) atomicOr(status, kStatusSeqTooLong);
     L = L < 0 ? 0 : max_pages * P;
   }
   int nfull = L / P;
@@ -115,7 +116,7 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) __attribute__((amdgpu_waves_pe
   // a bad id and is skipped, but every counted split still writes its (empty) partial
   const int Sr = C < 0 ? -C : active_splits(nfull, C);
   if (num_pages <= 0 && nfull > 0) {
-    if (lane == 0 && s == 0 && h == 0) atomicOr(status, kStatusBadPage);
+    if (lane == 0 && s == 0 && hq == 0) atomicOr(status, kStatusBadPage);
     nfull = 0;
   }
   const bool ranked = C < 0;
@@ -127,11 +128,11 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) __attribute__((amdgpu_waves_pe
     p0 = s * C;
     p1 = min(p0 + C, nfull);
   }
-  const size_t slot = ((size_t)r * H + h) * S + s;
+  const size_t slot = ((size_t)r * Hq + hq) * S + s;
 
   MhaState<D> st;
   {
-    const uint4* qrow = reinterpret_cast<const uint4*>(q + ((size_t)r * H + h) * D + (16 * lane) % D);
+    const uint4* qrow = reinterpret_cast<const uint4*>(q + ((size_t)r * Hq + hq) * D + (16 * lane) % D);
     const uint4 a = qrow[0], b = qrow[1];
     st.q[0] = a.x; st.q[1] = a.y; st.q[2] = a.z; st.q[3] = a.w;
     st.q[4] = b.x; st.q[5] = b.y; st.q[6] = b.z; st.q[7] = b.w;
@@ -291,9 +292,10 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) __attribute__((amdgpu_waves_pe
 int launch_attn_mha(const uint16_t* q, const uint8_t* units, const uint16_t* pool, int64_t pool_cap,
                     const uint64_t* esc_cursor, const uint16_t* k_tail,
                     const uint16_t* v_tail, const int32_t* page_table, int max_pages, const int32_t* seq_lens,
-                    int B, int H, int D, int P, int num_pages, SplitPlan plan, float scale, float* ws_acc,
+                    int B, int Hq, int H, int D, int P, int num_pages, SplitPlan plan, float scale, float* ws_acc,
                     float* ws_ml, uint32_t* status, hipStream_t stream) {
   static int slots128[64], slots64[64];
+  if (H <= 0 || Hq % H) return -2;
   const dim3 block(64 * kWavesPerBlock);
   if (D == 128) {
     plan.slots = resident_waves(attn_mha_kernel<128>, block.x, slots128, 64);
@@ -306,16 +308,16 @@ int launch_attn_mha(const uint16_t* q, const uint8_t* units, const uint16_t* poo
   // at two waves per resident slot: waves on one SIMD run at different speeds, and a second
   // round lets the slots of early finishers take new work (measured 1-1.5% faster at 8K and 32K
   // contexts, ragged or not; the grouped-query kernel, measured the same way, does best with
-  // one round).
-  rank_fit(plan, plan.slots, (long)B * H);
-  plan.slots = plan.slots > 0 ? 2 * plan.slots : B * H * plan.S;
-  const dim3 grid(plan_blocks(plan, (long)B * H, kWavesPerBlock));
+  // two thirds of one round). Query groups (head dim 64 only) make one item per query head.
+  rank_fit(plan, plan.slots, (long)B * Hq);
+  plan.slots = plan.slots > 0 ? 2 * plan.slots : B * Hq * plan.S;
+  const dim3 grid(plan_blocks(plan, (long)B * Hq, kWavesPerBlock));
   if (D == 128)
     hipLaunchKernelGGL((attn_mha_kernel<128>), grid, block, 0, stream, q, units, pool, pool_cap, esc_cursor, k_tail, v_tail, page_table,
-                       max_pages, seq_lens, B, H, P, num_pages, plan, scale, ws_acc, ws_ml, status);
+                       max_pages, seq_lens, B, H, Hq / H, P, num_pages, plan, scale, ws_acc, ws_ml, status);
   else
     hipLaunchKernelGGL((attn_mha_kernel<64>), grid, block, 0, stream, q, units, pool, pool_cap, esc_cursor, k_tail, v_tail, page_table,
-                       max_pages, seq_lens, B, H, P, num_pages, plan, scale, ws_acc, ws_ml, status);
+                       max_pages, seq_lens, B, H, Hq / H, P, num_pages, plan, scale, ws_acc, ws_ml, status);
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 

@@ -115,33 +115,34 @@ template <int D>
 __global__ __launch_bounds__(64 * kZfWaves) void attn_zf_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ units, const uint16_t* __restrict__ pool,
     int64_t pool_cap, const uint16_t* __restrict__ k_tail, const uint16_t* __restrict__ v_tail,
-    const int32_t* __restrict__ page_table, int max_pages, const int32_t* __restrict__ seq_lens, int B, int H, int P,
-    int num_pages, SplitPlan plan, float scale, float* __restrict__ ws_acc, float* __restrict__ ws_ml,
-    uint32_t* __restrict__ status) {
+    const int32_t* __restrict__ page_table, int max_pages, const int32_t* __restrict__ seq_lens, int B, int H,
+    int grp, int P, int num_pages, SplitPlan plan, float scale, float* __restrict__ ws_acc,
+    float* __restrict__ ws_ml, uint32_t* __restrict__ status) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int Hq = H * grp;   // query heads, one wave each; grp of them read each KV head
   WorkItem wi;
-  if (!plan_work(plan, seq_lens, B, P, max_pages, false, H, (int)uniform(blockIdx.x * kZfWaves + wave), lane, wi))
+  if (!plan_work(plan, seq_lens, B, P, max_pages, false, Hq, (int)uniform(blockIdx.x * kZfWaves + wave), lane, wi))
     return;
-  const int S = plan.S, C = wi.C, s = wi.s, h = wi.k, r = wi.r;
+  const int S = plan.S, C = wi.C, s = wi.s, hq = wi.k, h = hq / grp, r = wi.r;
   int L = request_len(wi, seq_lens);
   if (L > max_pages * P || L < 0) {
-    if (lane == 0 && s == 0 && h == 0) atomicOr(status, kStatusSeqTooLong);
+    if (lane == 0 && s == 0 && hq == 0) atomicOr(status, kStatusSeqTooLong);
     L = L < 0 ? 0 : max_pages * P;
   }
   int nfull = L / P;
   const int rows = L % P;
   const int Sr = active_splits(nfull, C);   // as the merge counts them (see the escape-format kernel)
   if (num_pages <= 0 && nfull > 0) {
-    if (lane == 0 && s == 0 && h == 0) atomicOr(status, kStatusBadPage);
+    if (lane == 0 && s == 0 && hq == 0) atomicOr(status, kStatusBadPage);
     nfull = 0;
   }
   if (s >= Sr) return;
   const int p0 = s * C, p1 = min(p0 + C, nfull);
-  const size_t slot = ((size_t)r * H + h) * S + s;
+  const size_t slot = ((size_t)r * Hq + hq) * S + s;
 
   MhaState<D> st;
   {
-    const uint4* qrow = reinterpret_cast<const uint4*>(q + ((size_t)r * H + h) * D + (16 * lane) % D);
+    const uint4* qrow = reinterpret_cast<const uint4*>(q + ((size_t)r * Hq + hq) * D + (16 * lane) % D);
     const uint4 a = qrow[0], b = qrow[1];
     st.q[0] = a.x; st.q[1] = a.y; st.q[2] = a.z; st.q[3] = a.w;
     st.q[4] = b.x; st.q[5] = b.y; st.q[6] = b.z; st.q[7] = b.w;
@@ -417,9 +418,10 @@ __global__ __launch_bounds__(64) void decompress_zf_kernel(const uint8_t* __rest
 
 int launch_attn_zf(const uint16_t* q, const uint8_t* units, const uint16_t* pool, int64_t pool_cap,
                    const uint16_t* k_tail, const uint16_t* v_tail, const int32_t* page_table, int max_pages,
-                   const int32_t* seq_lens, int B, int H, int D, int P, int num_pages, SplitPlan plan, float scale,
-                   float* ws_acc, float* ws_ml, uint32_t* status, hipStream_t stream) {
+                   const int32_t* seq_lens, int B, int Hq, int H, int D, int P, int num_pages, SplitPlan plan,
+                   float scale, float* ws_acc, float* ws_ml, uint32_t* status, hipStream_t stream) {
   static int slots128[64], slots64[64];
+  if (H <= 0 || Hq % H) return -2;
   const dim3 block(64 * kZfWaves);
   if (D == 128) {
     plan.slots = resident_waves(attn_zf_kernel<128>, block.x, slots128, 64);
@@ -428,14 +430,14 @@ int launch_attn_zf(const uint16_t* q, const uint8_t* units, const uint16_t* pool
   } else {
     return -2;
   }
-  if (plan.slots <= 0) plan.slots = B * H * plan.S;
-  const dim3 grid(plan_blocks(plan, (long)B * H, kZfWaves));
+  if (plan.slots <= 0) plan.slots = B * Hq * plan.S;
+  const dim3 grid(plan_blocks(plan, (long)B * Hq, kZfWaves));
   if (D == 128)
     hipLaunchKernelGGL((attn_zf_kernel<128>), grid, block, 0, stream, q, units, pool, pool_cap, k_tail, v_tail,
-                       page_table, max_pages, seq_lens, B, H, P, num_pages, plan, scale, ws_acc, ws_ml, status);
+                       page_table, max_pages, seq_lens, B, H, Hq / H, P, num_pages, plan, scale, ws_acc, ws_ml, status);
   else
     hipLaunchKernelGGL((attn_zf_kernel<64>), grid, block, 0, stream, q, units, pool, pool_cap, k_tail, v_tail,
-                       page_table, max_pages, seq_lens, B, H, P, num_pages, plan, scale, ws_acc, ws_ml, status);
+                       page_table, max_pages, seq_lens, B, H, Hq / H, P, num_pages, plan, scale, ws_acc, ws_ml, status);
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 

@@ -22,8 +22,8 @@ int launch_append(const uint16_t* k_new, const uint16_t* v_new, const int32_t* p
                   int format, hipStream_t stream);
 int launch_attn_zf(const uint16_t* q, const uint8_t* units, const uint16_t* pool, int64_t pool_cap,
                    const uint16_t* k_tail, const uint16_t* v_tail, const int32_t* page_table, int max_pages,
-                   const int32_t* seq_lens, int B, int H, int D, int P, int num_pages, SplitPlan plan, float scale,
-                   float* ws_acc, float* ws_ml, uint32_t* status, hipStream_t stream);
+                   const int32_t* seq_lens, int B, int Hq, int H, int D, int P, int num_pages, SplitPlan plan,
+                   float scale, float* ws_acc, float* ws_ml, uint32_t* status, hipStream_t stream);
 int launch_attn_zf_gqa(const uint16_t* q, const uint8_t* units, const uint16_t* pool, int64_t pool_cap,
                        const uint16_t* k_tail, const uint16_t* v_tail, const int32_t* page_table, int max_pages,
                        const int32_t* seq_lens, int B, int Hq, int H, int D, int P, int num_pages, SplitPlan plan,
@@ -34,7 +34,7 @@ int launch_decompress_zf(const uint8_t* units, const uint16_t* pool, int64_t poo
 int launch_attn_mha(const uint16_t* q, const uint8_t* units, const uint16_t* pool, int64_t pool_cap,
                     const uint64_t* esc_cursor, const uint16_t* k_tail,
                     const uint16_t* v_tail, const int32_t* page_table, int max_pages, const int32_t* seq_lens,
-                    int B, int H, int D, int P, int num_pages, SplitPlan plan, float scale, float* ws_acc,
+                    int B, int Hq, int H, int D, int P, int num_pages, SplitPlan plan, float scale, float* ws_acc,
                     float* ws_ml, uint32_t* status, hipStream_t stream);
 int launch_attn_gqa(const uint16_t* q, const uint8_t* units, const uint16_t* pool, int64_t pool_cap,
                     const uint64_t* esc_cursor, const uint16_t* k_tail,
@@ -42,8 +42,8 @@ int launch_attn_gqa(const uint16_t* q, const uint8_t* units, const uint16_t* poo
                     int B, int Hq, int Hkv, int D, int P, int num_pages, SplitPlan plan, float scale, float* ws_acc,
                     float* ws_ml, uint32_t* status, hipStream_t stream);
 int launch_attn_dense_mha(const uint16_t* q, const uint16_t* k_pages, const uint16_t* v_pages, const int32_t* pt,
-                          int max_pages, const int32_t* seq_lens, int B, int H, int D, int P, int num_pages,
-                          SplitPlan plan, float scale, float* ws_acc, float* ws_ml, uint32_t* status,
+                          int max_pages, const int32_t* seq_lens, int B, int Hq, int H, int D, int P,
+                          int num_pages, SplitPlan plan, float scale, float* ws_acc, float* ws_ml, uint32_t* status,
                           hipStream_t stream);
 int launch_attn_dense_gqa(const uint16_t* q, const uint16_t* k_pages, const uint16_t* v_pages, const int32_t* pt,
                           int max_pages, const int32_t* seq_lens, int B, int Hq, int Hkv, int D, int P,
@@ -62,8 +62,11 @@ namespace {
 constexpr int kTargetItems = 4096;   // splits aimed for: ~16 waves per CU on 256 CUs
 constexpr int kGqaRows = 8;          // query heads per grouped-query wave
 
-int64_t work_items_per_split(int B, int Hq, int Hkv) {
+// waves per split of the batch: one per (request, KV head, chunk of up to 8 query heads) in the
+// grouped-query kernels (head dim 128), one per (request, query head) in the multi-head ones
+int64_t work_items_per_split(int B, int Hq, int Hkv, int D) {
   const int grp = Hq / Hkv;
+  if (grp > 1 && D != 128) return (int64_t)B * Hq;
   const int64_t chunks = grp > 1 ? ((int64_t)grp + kGqaRows - 1) / kGqaRows : 1;
   return (int64_t)B * Hkv * chunks;
 }
@@ -73,9 +76,9 @@ int64_t work_items_per_split(int B, int Hq, int Hkv) {
 // splits fit their resident waves); this lower bound keeps the splits of one item, and so the
 // workspace, to about twice the split count that would fill kTargetItems waves with the batch's
 // items, and a split to at least 64 tokens.
-int pages_per_split(int B, int Hq, int Hkv, int P, int max_pages, int pps) {
+int pages_per_split(int B, int Hq, int Hkv, int D, int P, int max_pages, int pps) {
   if (pps > 0) return pps;   // (pps < 0 asks for the ranked schedule; this bound is then unused by it)
-  const int64_t items = work_items_per_split(B, Hq, Hkv);
+  const int64_t items = work_items_per_split(B, Hq, Hkv, D);
   const int64_t s_cap = items >= 2 * kTargetItems ? 1 : (2 * kTargetItems + items - 1) / items;
   const int min_c = P >= 64 ? 1 : 64 / P;
   int64_t c = ((int64_t)max_pages + s_cap - 1) / s_cap;
@@ -113,8 +116,8 @@ int rank_count(int B, int Hq, int Hkv, int max_pages, int pps) {
 
 // split slots per (request, query head): the dynamic schedule's bound, and the ranked one's
 // chunks per row
-int slot_count(int B, int Hq, int Hkv, int P, int max_pages, int pps) {
-  const int S = split_count(max_pages, pages_per_split(B, Hq, Hkv, P, max_pages, pps));
+int slot_count(int B, int Hq, int Hkv, int D, int P, int max_pages, int pps) {
+  const int S = split_count(max_pages, pages_per_split(B, Hq, Hkv, D, P, max_pages, pps));
   const int n = kvz::rank_chunks(rank_count(B, Hq, Hkv, max_pages, pps));
   return n > S ? n : S;
 }
@@ -196,7 +199,7 @@ int32_t kvz_num_splits(int32_t B, int32_t H_q, int32_t H_kv, int32_t D, int32_t 
                        int32_t pps) {
   if (B <= 0 || H_q <= 0 || H_kv <= 0 || H_q % H_kv || !shape_ok(P, D) || max_pages_per_seq < 0) return 0;
   if (pps < -kMaxForcedRanks) return 0;
-  return slot_count(B, H_q, H_kv, P, max_pages_per_seq, pps);
+  return slot_count(B, H_q, H_kv, D, P, max_pages_per_seq, pps);
 }
 
 // workspace: per (request, query head, split) acc[D] and (m, l) as float, then one 16-byte slot
@@ -259,7 +262,6 @@ static int check_attention_shape(int B, int Hq, int Hkv, int D, int P, int max_p
   if (B < 0 || Hq <= 0 || Hkv <= 0 || max_pages < 0) return KVZ_ERR_INVALID_ARG;
   if (!shape_ok(P, D) || Hq % Hkv || !table_fits(max_pages, P)) return KVZ_ERR_UNSUPPORTED;
   if (D != 64 && D != 128) return KVZ_ERR_UNSUPPORTED;
-  if (Hq > Hkv && D != 128) return KVZ_ERR_UNSUPPORTED;   // grouped queries: the MFMA kernels, head dim 128
   return KVZ_OK;
 }
 
@@ -274,27 +276,31 @@ int kvz_decode_attention_splits(const uint16_t* q, const kvz_cache* c, const int
   if (!q || !page_table || !seq_lens || !workspace || !c->k_tail || !c->v_tail || pps < -kMaxForcedRanks)
     return KVZ_ERR_INVALID_ARG;
   if (B > c->max_batch) return KVZ_ERR_INVALID_ARG;
-  const int C = pages_per_split(B, H_q, H, P, max_pages, pps);
-  const int S = slot_count(B, H_q, H, P, max_pages, pps);
+  const int C = pages_per_split(B, H_q, H, D, P, max_pages, pps);
+  const int S = slot_count(B, H_q, H, D, P, max_pages, pps);
   if (ws_bytes(B, H_q, S, D) == 0) return KVZ_ERR_INVALID_ARG;
   if (workspace_bytes < ws_bytes(B, H_q, S, D)) return KVZ_ERR_WORKSPACE;
   float* ws_acc = reinterpret_cast<float*>(workspace);
   float* ws_ml = ws_acc + (size_t)B * H_q * S * D;
   const float scale = sm_scale * 1.4426950408889634f;
   kvz::SplitPlan plan = make_plan(C, S, max_pages, pps > 0, ws_chosen(workspace, B, H_q, S, D));
-  if (c->format == KVZ_FORMAT_ZIPFUSION && H_q != H) {
+  // grouped queries go to the MFMA kernels at head dim 128; at head dim 64 the multi-head kernels
+  // take one wave per query head (each reads its KV head's units)
+  const bool gqa = H_q != H && D == 128;
+  if (c->format == KVZ_FORMAT_ZIPFUSION && gqa) {
     rc = kvz::launch_attn_zf_gqa(q, c->units, c->esc_pool, c->esc_capacity, c->k_tail, c->v_tail, page_table,
                                  max_pages, seq_lens, B, H_q, H, D, P, c->num_pages, plan, scale, ws_acc, ws_ml,
                                  c->status, as_stream(stream));
   } else if (c->format == KVZ_FORMAT_ZIPFUSION) {
     rc = kvz::launch_attn_zf(q, c->units, c->esc_pool, c->esc_capacity, c->k_tail, c->v_tail, page_table, max_pages,
-                             seq_lens, B, H, D, P, c->num_pages, plan, scale, ws_acc, ws_ml, c->status,
+                             seq_lens, B, H_q, H, D, P, c->num_pages, plan, scale, ws_acc, ws_ml, c->status,
                              as_stream(stream));
-  } else if (H_q == H) {
+  } else if (!gqa) {
     plan.ranks = rank_count(B, H_q, H, max_pages, pps);
     plan.rank_min = pps < 0 ? 0 : kRankMinPages;
-    rc = kvz::launch_attn_mha(q, c->units, c->esc_pool, c->esc_capacity, c->esc_cursor, c->k_tail, c->v_tail, page_table, max_pages, seq_lens, B, H,
-                              D, P, c->num_pages, plan, scale, ws_acc, ws_ml, c->status, as_stream(stream));
+    rc = kvz::launch_attn_mha(q, c->units, c->esc_pool, c->esc_capacity, c->esc_cursor, c->k_tail, c->v_tail,
+                              page_table, max_pages, seq_lens, B, H_q, H, D, P, c->num_pages, plan, scale, ws_acc,
+                              ws_ml, c->status, as_stream(stream));
   } else {
     rc = kvz::launch_attn_gqa(q, c->units, c->esc_pool, c->esc_capacity, c->esc_cursor, c->k_tail, c->v_tail, page_table, max_pages, seq_lens, B,
                               H_q, H, D, P, c->num_pages, plan, scale, ws_acc, ws_ml, c->status,
@@ -315,19 +321,19 @@ int kvz_decode_attention_dense_splits(const uint16_t* q, const uint16_t* k_pages
   if (!q || (num_pages > 0 && (!k_pages || !v_pages)) || !page_table || !seq_lens || !workspace || num_pages < 0 ||
       pps < -kMaxForcedRanks)
     return KVZ_ERR_INVALID_ARG;
-  const int C = pages_per_split(B, H_q, H, P, max_pages, pps);
-  const int S = slot_count(B, H_q, H, P, max_pages, pps);
+  const int C = pages_per_split(B, H_q, H, D, P, max_pages, pps);
+  const int S = slot_count(B, H_q, H, D, P, max_pages, pps);
   if (ws_bytes(B, H_q, S, D) == 0) return KVZ_ERR_INVALID_ARG;
   if (workspace_bytes < ws_bytes(B, H_q, S, D)) return KVZ_ERR_WORKSPACE;
   float* ws_acc = reinterpret_cast<float*>(workspace);
   float* ws_ml = ws_acc + (size_t)B * H_q * S * D;
   const float scale = sm_scale * 1.4426950408889634f;
   kvz::SplitPlan plan = make_plan(C, S, max_pages, pps > 0, ws_chosen(workspace, B, H_q, S, D));
-  if (H_q == H) {
+  if (H_q == H || D != 128) {   // as the compressed path: grouped queries at head dim 64 one query head per wave
     plan.ranks = rank_count(B, H_q, H, max_pages, pps);   // the baseline gets the same schedule as the compressed kernel
     plan.rank_min = pps < 0 ? 0 : kRankMinPages;
-    rc = kvz::launch_attn_dense_mha(q, k_pages, v_pages, page_table, max_pages, seq_lens, B, H, D, P, num_pages, plan,
-                                    scale, ws_acc, ws_ml, status, as_stream(stream));
+    rc = kvz::launch_attn_dense_mha(q, k_pages, v_pages, page_table, max_pages, seq_lens, B, H_q, H, D, P, num_pages,
+                                    plan, scale, ws_acc, ws_ml, status, as_stream(stream));
   } else {
     rc = kvz::launch_attn_dense_gqa(q, k_pages, v_pages, page_table, max_pages, seq_lens, B, H_q, H, D, P, num_pages,
                                     plan, scale, ws_acc, ws_ml, status, as_stream(stream));
@@ -342,7 +348,7 @@ int kvz_merge_splits(const void* workspace, size_t workspace_bytes, const int32_
   if (rc) return rc;
   if (B == 0) return KVZ_OK;
   if (!workspace || !seq_lens || !out || pps < -kMaxForcedRanks) return KVZ_ERR_INVALID_ARG;
-  const int S = slot_count(B, H_q, H, P, max_pages, pps);
+  const int S = slot_count(B, H_q, H, D, P, max_pages, pps);
   if (ws_bytes(B, H_q, S, D) == 0) return KVZ_ERR_INVALID_ARG;
   if (workspace_bytes < ws_bytes(B, H_q, S, D)) return KVZ_ERR_WORKSPACE;
   const float* ws_acc = reinterpret_cast<const float*>(workspace);

@@ -208,9 +208,10 @@ int kvz_append_token(const kvz_cache* cache, const uint16_t* k_new, const uint16
  *   out          [B][H_q][D] BF16 (round to nearest even); a request with no token gets zeros
  *   out_f32      nullable [B][H_q][D] float, the same result before rounding
  *   workspace    >= kvz_workspace_bytes(B, H_q, H, D, P, max_pages_per_seq, pages_per_split)
- * Supported: D in {64, 128}; for H_q > H (grouped queries) D = 128. A wave takes up to 8 query
- * heads of one KV head; with up to 16, or 25 to 32, query heads per KV head a unit's waves share
- * one workgroup, other group sizes spread them over workgroups that may each read the unit;
+ * Supported: D in {64, 128}, any H_q multiple of H. Grouped queries (H_q > H) at D = 128: a wave
+ * takes up to 8 query heads of one KV head; with up to 16, or 25 to 32, query heads per KV head a
+ * unit's waves share one workgroup, other group sizes spread them over workgroups that may each
+ * read the unit. At D = 64 each query head has its own wave, which reads its KV head's units;
  * max_pages_per_seq * P within int32 (as for kvz_append_token).
  * Errors: KVZ_ERR_INVALID_ARG, KVZ_ERR_UNSUPPORTED, KVZ_ERR_WORKSPACE. Device status:
  * BAD_PAGE_ID, SEQ_TOO_LONG. */
@@ -245,7 +246,7 @@ int kvz_decode_attention_noalloc(const uint16_t* q, const kvz_cache* cache, cons
  *   k_pages, v_pages  [num_pages][H][P][D] raw BF16, token-major (may be null when num_pages is 0)
  *   page_table        [B][max_pages_per_seq]; the first ceil(seq_lens[r] / P) entries are used
  *   status            nullable [1] sticky bits (BAD_PAGE_ID, SEQ_TOO_LONG)
- * Other arguments as kvz_decode_attention. Supported: D in {64, 128}; D = 128 when H_q > H. */
+ * Other arguments as kvz_decode_attention. Supported: D in {64, 128}, any H_q multiple of H. */
 int kvz_decode_attention_dense(const uint16_t* q, const uint16_t* k_pages,
                                const uint16_t* v_pages, int32_t num_pages, int32_t H,
                                int32_t D, int32_t P, const int32_t* page_table,

@@ -128,7 +128,7 @@ def test_invalid_arguments_enqueue_nothing():
     assert rc == binding.KVZ_ERR_INVALID_ARG       # a group of 32 is served; the null pointers are not
     rc = L.kvz_decode_attention_dense(None, None, None, 0, 2, 64, 16, None, 0, None, 1, 8, 1.0, 0, None, None, None,
                                       0, None, None)
-    assert rc == binding.KVZ_ERR_UNSUPPORTED       # grouped queries at head dim 64
+    assert rc == binding.KVZ_ERR_INVALID_ARG       # grouped queries at head dim 64 are served too
     assert L.kvz_compact_pool(None, None, 0, None, 0, None, None) == binding.KVZ_ERR_INVALID_ARG
     assert kvz.kvz.strerror(binding.KVZ_ERR_WORKSPACE) == "workspace too small"
     # a page table whose width times P overflows a 32-bit length

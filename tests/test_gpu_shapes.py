@@ -24,6 +24,8 @@ SHAPES = [  # (P, D, Hq, Hkv)
     (32, 128, 4, 4),
     (16, 64, 4, 4),
     (64, 64, 8, 8),
+    (16, 64, 8, 2),     # grouped queries at head dim 64: one wave per query head
+    (48, 64, 6, 1),
 ]
 
 
@@ -124,14 +126,16 @@ def test_wide_dynamic_range_batch(kw):
     check_rows(host16(out).reshape(-1, w.D), out32.cpu().numpy().reshape(-1, w.D), ref, "dense")
 
 
-@pytest.mark.parametrize("Hq,Hkv,P", [(24, 1, 32), (32, 1, 16), (64, 2, 16)])
-def test_large_query_groups(Hq, Hkv, P):
-    """Query groups beyond 16 heads (3, 4 and 8 chunks of 8 query heads per KV head; the last two
-    multi-query shapes): both cache formats and the uncompressed baseline against the oracle, smooth
-    and escape-stress data, under the device's split choice and one page per split."""
+@pytest.mark.parametrize("Hq,Hkv,P,D", [(24, 1, 32, 128), (32, 1, 16, 128), (64, 2, 16, 128), (32, 4, 32, 64),
+                                        (16, 1, 16, 64)])
+def test_large_query_groups(Hq, Hkv, P, D):
+    """Query groups beyond 16 heads at head dim 128 (3, 4 and 8 chunks of 8 query heads per KV
+    head; the last two multi-query shapes) and grouped queries at head dim 64 (a wave per query
+    head): both cache formats and the uncompressed baseline against the oracle, smooth and
+    escape-stress data, under the device's split choice and one page per split."""
     lens = [1, P - 1, 3 * P + 5, 7 * P]
     for cfg in (1, 5):
-        w = make_workload(cfg, B=len(lens), lens=lens, Hq=Hq, Hkv=Hkv, D=128, P=P, n_append=0)
+        w = make_workload(cfg, B=len(lens), lens=lens, Hq=Hq, Hkv=Hkv, D=D, P=P, n_append=0)
         kp, vp = w.pages(0), w.pages(1)
         q = w.q()
         rows = [(r, h) for r in range(w.B) for h in range(w.Hq)]
