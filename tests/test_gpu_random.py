@@ -37,11 +37,12 @@ def _case(seed):
 
 def _large_case(seed):
     """larger batches (up to 39 requests), longer requests (up to 40 pages), pages of up to 256
-    tokens (512 at head dim 64), two requests ending on a page boundary"""
+    tokens (512 at head dim 64), two requests ending on a page boundary, query groups of up to 32
+    heads (and grouped queries at head dim 64)"""
     rng = np.random.default_rng(90000 + seed)
     D = int(rng.choice([64, 128]))
     P = int(rng.choice([16, 16, 32, 64, 128, 256] + ([512] if D == 64 else [])))
-    grp = 1 if D == 64 else int(rng.choice([1, 2, 4, 7, 8, 16]))
+    grp = int(rng.choice([1, 2, 4])) if D == 64 else int(rng.choice([1, 2, 4, 7, 8, 16, 24, 32]))
     Hkv = int(rng.integers(1, 5))
     B = int(rng.integers(1, 40))
     lens = rng.integers(0, int(rng.choice([3, 10, 40])) * P + 1, size=B)
