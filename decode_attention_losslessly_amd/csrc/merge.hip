@@ -10,8 +10,8 @@
 // loads issued before the first is used), keeping its own running maximum, so a row costs one
 // round trip per 8 of a wave's splits; the W partial results meet in LDS, rescaled to the
 // largest maximum. Rows with at most 8 splits take one wave each (4 rows per
-// workgroup); otherwise few rows (a small batch, where the splits are many) get 16 waves per
-// row, and more rows 4.
+// workgroup); otherwise few rows (a small batch, where the splits are many) get 8 waves per
+// row up to 64 splits and 16 beyond, and more rows 4.
 #include "attn_common.hpp"
 
 namespace kvz {
@@ -113,16 +113,21 @@ int launch_merge(const float* ws_acc, const float* ws_ml, const int32_t* seq_len
                  int max_pages, int S, const int32_t* chosen, int dense, uint16_t* out, float* out_f32,
                  hipStream_t stream) {
   const int rows = B * Hq;
-  const int shape = S <= 8 ? 0 : (rows < 1024 ? 2 : 1);   // 0: a wave per row, 1: 4 waves, 2: 16 waves
+  // 0: a wave per row, 1: 4 waves, 2: 16 waves, 3: 8 waves (few rows of up to 64 splits: one batch
+  // of eight loads per wave, half the workgroup of 16 to reduce; batch 1 at 4K, 64 splits a row:
+  // the merge 6.3 -> 6.0 us and the step 16.4 -> 16.0 us)
+  const int shape = S <= 8 ? 0 : (rows < 1024 ? (S <= 64 ? 3 : 2) : 1);
   const unsigned blocks = shape == 0 ? (unsigned)(rows + 3) / 4 : (unsigned)rows;
-  const unsigned threads = shape == 2 ? 1024 : 256;
+  const unsigned threads = shape == 2 ? 1024 : (shape == 3 ? 512 : 256);
 #define KVZ_MERGE(DD, WW, RR)                                                                                  \
   hipLaunchKernelGGL((merge_kernel<DD, WW, RR>), dim3(blocks), dim3(threads), 0, stream, ws_acc, ws_ml, seq_lens, \
                      B, Hq, P, max_pages, S, chosen, dense, out, out_f32)
   if (D == 128) {
-    if (shape == 0) KVZ_MERGE(128, 1, 4); else if (shape == 1) KVZ_MERGE(128, 4, 1); else KVZ_MERGE(128, 16, 1);
+    if (shape == 0) KVZ_MERGE(128, 1, 4); else if (shape == 1) KVZ_MERGE(128, 4, 1);
+    else if (shape == 3) KVZ_MERGE(128, 8, 1); else KVZ_MERGE(128, 16, 1);
   } else if (D == 64) {
-    if (shape == 0) KVZ_MERGE(64, 1, 4); else if (shape == 1) KVZ_MERGE(64, 4, 1); else KVZ_MERGE(64, 16, 1);
+    if (shape == 0) KVZ_MERGE(64, 1, 4); else if (shape == 1) KVZ_MERGE(64, 4, 1);
+    else if (shape == 3) KVZ_MERGE(64, 8, 1); else KVZ_MERGE(64, 16, 1);
   } else {
     return -2;
   }
