@@ -41,6 +41,12 @@ The layout itself is this repository's (the pages' own 12-bit layout is prior ar
                                the position (within its block) repeating what the offset
                                codes already say; unused bytes zero
              MR = round_up(2PG + 16, 128)
+
+Second geometry, the channel groups (format 2; group shape: §III.B fixes a block's exponent
+range, not the shape of the values that share a base): a group is the 16 tokens of one tile
+over 4 adjacent dims [4j, 4j + 4), still 64 values, so every size above is unchanged; the base
+of tile t's group j is byte t*16G + j of the block's base table (16G = D/4 groups per tile).
+Everything else (sm bytes, offsets, storage order, escapes, meta) is the same.
 """
 from __future__ import annotations
 
@@ -48,6 +54,8 @@ import numpy as np
 
 GROUP = 64
 TILE = 16
+CHANNEL_DIMS = 4           # dims of a channel group (over the TILE tokens of a tile)
+TOKEN, CHANNEL = "token", "channel"
 ESCAPE = 15
 MAX_OFFSET = 14
 INLINE = 0xFFFF_FFFF_FFFF_FFFF
@@ -165,15 +173,36 @@ def unit_bytes(P: int, D: int) -> int:
     return meta_bytes(P, D) + 2 * block_bytes(P, D)
 
 
-def encode_block(X: np.ndarray, kind: int, with_positions: bool = False):
+def group_values(A: np.ndarray, geometry: str = TOKEN) -> np.ndarray:
+    """Block array [P][D] -> its groups [n_groups][64], in base-table order."""
+    P, D = A.shape
+    if geometry == TOKEN:        # token t's dims [64g, 64g + 64); table order t*16G + g*16 + tok
+        g = A.reshape(P // TILE, TILE, D // GROUP, GROUP).transpose(0, 2, 1, 3)
+    else:                        # tile t's tokens over dims [4j, 4j + 4); table order t*16G + j
+        g = A.reshape(P // TILE, TILE, D // CHANNEL_DIMS, CHANNEL_DIMS).transpose(0, 2, 1, 3)
+    return g.reshape(-1, GROUP)
+
+
+def value_bases(bases: np.ndarray, P: int, D: int, geometry: str = TOKEN) -> np.ndarray:
+    """Base table [P*G] (table order) -> the base of every value, [P][D]."""
+    b = np.asarray(bases, np.int32)
+    tok, dim = np.meshgrid(np.arange(P), np.arange(D), indexing="ij")
+    if geometry == TOKEN:
+        idx = (tok // TILE) * TILE * (D // GROUP) + (dim // GROUP) * TILE + tok % TILE
+    else:
+        idx = (tok // TILE) * (D // CHANNEL_DIMS) + dim // CHANNEL_DIMS
+    return b[idx]
+
+
+def encode_block(X: np.ndarray, kind: int, with_positions: bool = False, geometry: str = TOKEN):
     """Block [P][D] BF16 bits -> (base bytes [P*G], block payload bytes, escapes u16
     [, storage positions of the escapes])."""
     X = np.asarray(X, np.uint16)
     P, D = X.shape
-    G = D // GROUP
-    e = exponent(X).reshape(P, G, GROUP)
-    base = choose_bases(e)                                   # [P][G]
-    off = offsets(e, base).reshape(P, D)
+    bases = choose_bases(group_values(exponent(X), geometry))          # table order
+    e = exponent(X)
+    d = e - value_bases(bases, P, D, geometry)
+    off = np.where((d >= 0) & (d <= MAX_OFFSET), d, ESCAPE).astype(np.uint8)
     sm = sm_byte(X)
     order = storage_order(P, D, kind)
     sm_s, off_s, x_s = sm.reshape(-1)[order], off.reshape(-1)[order], X.reshape(-1)[order]
@@ -182,7 +211,6 @@ def encode_block(X: np.ndarray, kind: int, with_positions: bool = False):
         sl = slice(t * per_tile, (t + 1) * per_tile)
         payload.append(sm_s[sl])
         payload.append(pack_offsets(off_s[sl]).astype('<u4').view(np.uint8))
-    bases = np.concatenate([base[t * TILE:(t + 1) * TILE].T.reshape(-1) for t in range(P // TILE)])
     esc = off_s == ESCAPE
     out = (bases.astype(np.uint8), np.concatenate(payload), x_s[esc].copy())
     if with_positions:
@@ -191,8 +219,7 @@ def encode_block(X: np.ndarray, kind: int, with_positions: bool = False):
 
 
 def decode_block(bases: np.ndarray, payload: np.ndarray, escapes: np.ndarray, P: int, D: int,
-                 kind: int) -> np.ndarray:
-    G = D // GROUP
+                 kind: int, geometry: str = TOKEN) -> np.ndarray:
     per_tile = TILE * D
     sm_s, off_s = [], []
     for t in range(P // TILE):
@@ -200,12 +227,8 @@ def decode_block(bases: np.ndarray, payload: np.ndarray, escapes: np.ndarray, P:
         sm_s.append(chunk[:per_tile])
         off_s.append(unpack_offsets(chunk[per_tile:].view('<u4')))
     sm_s, off_s = np.concatenate(sm_s), np.concatenate(off_s)
-    base = np.empty((P, G), np.int32)
-    for t in range(P // TILE):
-        base[t * TILE:(t + 1) * TILE] = bases[t * TILE * G:(t + 1) * TILE * G].reshape(G, TILE).T
     order = storage_order(P, D, kind)
-    tok, dim = order // D, order % D
-    b_s = base[tok, dim // GROUP]
+    b_s = value_bases(bases, P, D, geometry).reshape(-1)[order]
     x_s = rebuild(sm_s, (b_s + np.minimum(off_s, MAX_OFFSET)) & 0xFF)
     esc = off_s == ESCAPE
     assert int(esc.sum()) == len(escapes)
@@ -215,16 +238,16 @@ def decode_block(bases: np.ndarray, payload: np.ndarray, escapes: np.ndarray, P:
     return X.reshape(P, D)
 
 
-def encode_unit(K: np.ndarray, V: np.ndarray, pool_offset: int | None = None):
-    """One (page, head) unit from its K and V blocks [P][D].
+def encode_unit(K: np.ndarray, V: np.ndarray, pool_offset: int | None = None, geometry: str = TOKEN):
+    """One (page, head) unit from its K and V blocks [P][D], with token or channel groups.
 
     Returns (unit bytes uint8[unit_bytes], escapes that go to the pool: u16, K's then V's).
     When the escapes do not fit inline they go to the pool at `pool_offset` (0 when None).
     """
     P, D = K.shape
     G = D // GROUP
-    kb, kp, ke, kpos = encode_block(K, K_KIND, with_positions=True)
-    vb, vp, ve, vpos = encode_block(V, V_KIND, with_positions=True)
+    kb, kp, ke, kpos = encode_block(K, K_KIND, with_positions=True, geometry=geometry)
+    vb, vp, ve, vpos = encode_block(V, V_KIND, with_positions=True, geometry=geometry)
     meta = np.zeros(meta_bytes(P, D), np.uint8)
     meta[:P * G] = kb
     meta[P * G:2 * P * G] = vb
@@ -272,12 +295,12 @@ def inline_positions(unit: np.ndarray, P: int, D: int):
     return pos[:kc], pos[kc:]
 
 
-def decode_unit(unit: np.ndarray, pool: np.ndarray | None, P: int, D: int):
+def decode_unit(unit: np.ndarray, pool: np.ndarray | None, P: int, D: int, geometry: str = TOKEN):
     """Unit bytes (+ escape pool) -> (K [P][D], V [P][D]) BF16 bits."""
     unit = np.asarray(unit, np.uint8)
     G = D // GROUP
     mb, bb = meta_bytes(P, D), block_bytes(P, D)
     ke, ve = unit_escapes(unit, pool, P, D)
-    K = decode_block(unit[:P * G], unit[mb:mb + bb], ke, P, D, K_KIND)
-    V = decode_block(unit[P * G:2 * P * G], unit[mb + bb:mb + 2 * bb], ve, P, D, V_KIND)
+    K = decode_block(unit[:P * G], unit[mb:mb + bb], ke, P, D, K_KIND, geometry)
+    V = decode_block(unit[P * G:2 * P * G], unit[mb + bb:mb + 2 * bb], ve, P, D, V_KIND, geometry)
     return K, V

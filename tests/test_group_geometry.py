@@ -51,3 +51,28 @@ def test_channel_major_groups_win_only_under_escape_stress():
     w = make_workload(5, n_append=0, B=1, L=256)
     tok, chan, esc_t, esc_c = _bits_per_value(w, 0)
     assert chan < tok and esc_t > 0.4 * 256 * w.D * w.Hkv, (tok, chan, esc_t)
+
+
+def _escapes_by_geometry(w, kind):
+    """(token groups, channel groups of 4 dims x 16 tokens) escapes over every full page"""
+    pages = w.pages(kind)
+    esc_t = esc_c = n = 0
+    for r in range(w.B):
+        npg = int(w.seq_lens[r]) // w.P
+        for h in range(w.Hkv):
+            e = exponent(np.concatenate([pages[i, h] for i in w.page_table[r, :npg]]))
+            T, D = e.shape
+            esc_t += _escapes(e.reshape(T, D // 64, 64))
+            esc_c += _escapes(e.reshape(T // 16, 16, D // 4, 4).transpose(0, 2, 1, 3).reshape(T // 16, D // 4, 64))
+            n += T * D
+    return esc_t, esc_c, n
+
+
+@pytest.mark.parametrize("cfg,kw,ratio", [(2, dict(L=1024), 2.0), (3, dict(B=2, L=512), 1.2), (6, dict(B=2, L=512), 2.0)])
+def test_channel_groups_of_four_dims_cut_escapes_at_equal_size(cfg, kw, ratio):
+    """Groups of 4 adjacent dims over a tile's 16 tokens (format 2) keep 64 values per base byte,
+    so a unit has the same size; on K pages whose channels carry their own scales (and x20
+    outlier channels) they escape less often than token rows."""
+    w = make_workload(cfg, n_append=0, **kw)
+    esc_t, esc_c, n = _escapes_by_geometry(w, 0)
+    assert esc_c * ratio < esc_t, (esc_c, esc_t, n)
