@@ -37,6 +37,7 @@ struct GqaCStage {
 // Issues the loads of one (page, tile) step, unconditionally (as in the multi-head kernel), so
 // that the next step's loads stay in flight while the current step is computed.
 // `live` is false for a stage issued past the last step: its loads read nothing.
+template <bool CH>
 __device__ __forceinline__ void gqa_c_issue(GqaCStage& st, const uint8_t* units, int pid, int page, int tile, int H,
                                             int h, int P, int num_pages, int lane, bool live = true) {
   st.ok = pid >= 0 && pid < num_pages;
@@ -44,13 +45,13 @@ __device__ __forceinline__ void gqa_c_issue(GqaCStage& st, const uint8_t* units,
   st.unit = units + ((size_t)(st.ok ? pid : 0) * H + h) * unit_bytes(P, 128);
   st.tile = tile;
   st.meta = load_meta(st.unit, P, 128, tile, lane, live);
-  load_k<128, true>(st.unit, P, tile, lane, st.k, live);
+  load_k<128, true, true, CH>(st.unit, P, tile, lane, st.k, live);
   load_v<128>(st.unit, P, tile, lane, st.v, live);
 }
 
 // Returns false, leaving the state untouched, when the unit's escapes are in the pool and POOL
 // is off.
-template <bool POOL>
+template <bool POOL, bool CH>
 __device__ __forceinline__ bool gqa_c_compute(GqaState& st, const GqaCStage& stg, int P, uint32_t& krank,
                                               uint32_t& vrank, uint16_t* esc_lds, uint32_t* vlds,
                                               const uint16_t* pool, int64_t pool_cap, float scale, int lane) {
@@ -60,11 +61,11 @@ __device__ __forceinline__ bool gqa_c_compute(GqaState& st, const GqaCStage& stg
   if (POOL) clamp_to_pool(hdr, pool_cap);
   if (stg.tile == 0) { krank = 0; vrank = 0; }
   uint32_t kp[16];
-  decode_k<128>(stg.k, kp);
+  decode_k<128, CH>(stg.k, kp);
   if (hdr.kc) patch_k_tile<128, true, POOL>(kp, stg.k, stg.meta, hdr, P, stg.tile, krank, esc_lds, pool, pool_cap, lane);
   uint32_t vflat[16];
 #pragma unroll
-  for (int g = 0; g < 2; ++g) decode_v_seg(stg.v.seg[g], v_bases<128>(stg.meta, g), &vflat[8 * g]);
+  for (int g = 0; g < 2; ++g) decode_v_seg(stg.v.seg[g], v_bases<128, CH>(stg.meta, g), &vflat[8 * g]);
   if (hdr.vc) patch_v_tile<128, POOL, 2>(vflat, stg.v, stg.meta, hdr, P, stg.tile, vrank, esc_lds, pool, pool_cap, lane);
   uint32_t vp[2][8];
 #pragma unroll
@@ -80,6 +81,7 @@ __device__ __forceinline__ bool gqa_c_compute(GqaState& st, const GqaCStage& stg
 // One tile of any unit for the pool-capable loop: `meta` is its meta window (loaded a step
 // ahead); the payload and, for a pool unit, both escape windows go out in one round trip.
 // krank / vrank are the block cursors, reset at tile 0.
+template <bool CH>
 __device__ __forceinline__ void gqa_any_tile(GqaState& st, const uint8_t* unit, uint32_t meta, int P, int tile,
                                              uint32_t& krank, uint32_t& vrank, uint16_t* lds, uint32_t* vlds,
                                              const uint16_t* pool, int64_t pool_cap, float scale, int lane) {
@@ -93,9 +95,9 @@ __device__ __forceinline__ void gqa_any_tile(GqaState& st, const uint8_t* unit, 
   Window kw, vw;
   const bool in_pool = any_stage<128>(hdr, krank, vrank, lds, pool, pool_cap, kw, vw, lane);
   uint32_t kp[16];
-  any_rebuild_k<128, true>(kp, k, meta, hdr, in_pool, kw, P, tile, krank, lds, pool, pool_cap, lane);
+  any_rebuild_k<128, true, CH>(kp, k, meta, hdr, in_pool, kw, P, tile, krank, lds, pool, pool_cap, lane);
   uint32_t vflat[16];
-  any_rebuild_v<128>(vflat, v, meta, hdr, in_pool, vw, P, tile, vrank, lds, pool, pool_cap, lane);
+  any_rebuild_v<128, CH>(vflat, v, meta, hdr, in_pool, vw, P, tile, vrank, lds, pool, pool_cap, lane);
   if (in_pool) wave_lds_sync();   // the window reads are complete before the next staging writes
   uint32_t vp[2][8];
 #pragma unroll
@@ -116,7 +118,8 @@ __device__ __forceinline__ void gqa_any_tile(GqaState& st, const uint8_t* unit, 
 // One wave per (request, KV head, chunk of query heads, split). As in the multi-head kernel,
 // the main loop skips units whose escapes are in the pool and the wave adds them after the
 // loop, when the pipeline's registers are free; a split that meets mostly such units goes on
-// in the pool-capable loop instead.
+// in the pool-capable loop instead. CH: channel groups (format 2).
+template <bool CH>
 __global__ __launch_bounds__(64 * kGqaWaves) KVZ_GQA_OCCUPANCY void attn_gqa_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ units, const uint16_t* __restrict__ pool,
     int64_t pool_cap, const uint64_t* __restrict__ esc_cursor, const uint16_t* __restrict__ k_tail,
@@ -200,21 +203,21 @@ __global__ __launch_bounds__(64 * kGqaWaves) KVZ_GQA_OCCUPANCY void attn_gqa_ker
     };
     GqaCStage a, b;
     int pid = sload<int32_t>(pt_row + lp);
-    gqa_c_issue(a, units, pid, lp, lt, H, h, P, num_pages, lane);
+    gqa_c_issue<CH>(a, units, pid, lp, lt, H, h, P, num_pages, lane);
     advance();
     pid = sload<int32_t>(pt_row + lp);
     for (int i = 0; i < nsteps; i += 2) {
-      gqa_c_issue(b, units, pid, lp, lt, H, h, P, num_pages, lane, live);
+      gqa_c_issue<CH>(b, units, pid, lp, lt, H, h, P, num_pages, lane, live);
       advance();
       pid = sload<int32_t>(pt_row + lp);
       bad |= !a.ok;
-      if (!gqa_c_compute<false>(st, a, P, krank, vrank, esc_lds, vlds, pool, pool_cap, scale, lane)) note(a, i + 1);
+      if (!gqa_c_compute<false, CH>(st, a, P, krank, vrank, esc_lds, vlds, pool, pool_cap, scale, lane)) note(a, i + 1);
       if (i + 1 >= nsteps || resume >= 0) break;
-      gqa_c_issue(a, units, pid, lp, lt, H, h, P, num_pages, lane, live);
+      gqa_c_issue<CH>(a, units, pid, lp, lt, H, h, P, num_pages, lane, live);
       advance();
       pid = sload<int32_t>(pt_row + lp);
       bad |= !b.ok;
-      if (!gqa_c_compute<false>(st, b, P, krank, vrank, esc_lds, vlds, pool, pool_cap, scale, lane)) note(b, i + 2);
+      if (!gqa_c_compute<false, CH>(st, b, P, krank, vrank, esc_lds, vlds, pool, pool_cap, scale, lane)) note(b, i + 2);
       if (resume >= 0) break;
     }
   }
@@ -237,7 +240,7 @@ __global__ __launch_bounds__(64 * kGqaWaves) KVZ_GQA_OCCUPANCY void attn_gqa_ker
         nu = unit_of(n + 1, nok);
         nmeta = load_meta(nu, P, 128, (n + 1) % T, lane);
       }
-      if (ok) gqa_any_tile(st, u, meta, P, n % T, krank, vrank, esc_lds, vlds, pool, pool_cap, scale, lane);
+      if (ok) gqa_any_tile<CH>(st, u, meta, P, n % T, krank, vrank, esc_lds, vlds, pool, pool_cap, scale, lane);
       bad |= !ok;
       u = nu;
       ok = nok;
@@ -251,8 +254,8 @@ __global__ __launch_bounds__(64 * kGqaWaves) KVZ_GQA_OCCUPANCY void attn_gqa_ker
       const int pid = sload<int32_t>(pt_row + page);
       for (int t = 0; t < T; ++t) {
         GqaCStage a;
-        gqa_c_issue(a, units, pid, page, t, H, h, P, num_pages, lane);
-        gqa_c_compute<true>(st, a, P, krank, vrank, esc_lds, vlds, pool, pool_cap, scale, lane);
+        gqa_c_issue<CH>(a, units, pid, page, t, H, h, P, num_pages, lane);
+        gqa_c_compute<true, CH>(st, a, P, krank, vrank, esc_lds, vlds, pool, pool_cap, scale, lane);
       }
     };
     do_page(first_skip);
@@ -368,14 +371,15 @@ int launch_attn_gqa(const uint16_t* q, const uint8_t* units, const uint16_t* poo
                     const uint64_t* esc_cursor, const uint16_t* k_tail,
                     const uint16_t* v_tail, const int32_t* page_table, int max_pages, const int32_t* seq_lens,
                     int B, int Hq, int H, int D, int P, int num_pages, SplitPlan plan, float scale, float* ws_acc,
-                    float* ws_ml, uint32_t* status, hipStream_t stream) {
+                    float* ws_ml, uint32_t* status, bool channel, hipStream_t stream) {
   if (D != 128) return -2;
-  static int slots[64];
+  static int slots[64], slots_c[64];
   const dim3 block(64 * kGqaWaves);
-  plan.slots = resident_waves(attn_gqa_kernel, block.x, slots, 64);
+  auto kernel = channel ? attn_gqa_kernel<true> : attn_gqa_kernel<false>;
+  plan.slots = resident_waves(kernel, block.x, channel ? slots_c : slots, 64);
   plan.slots_pref = 2 * plan.slots / 3;   // two of its three waves per SIMD (see plan_work)
   if (plan.slots <= 0) plan.slots = gqa_items(B, Hq, H) * plan.S;
-  hipLaunchKernelGGL(attn_gqa_kernel, dim3(plan_blocks(plan, gqa_items(B, Hq, H), kGqaWaves)), block, 0, stream, q, units,
+  hipLaunchKernelGGL(kernel, dim3(plan_blocks(plan, gqa_items(B, Hq, H), kGqaWaves)), block, 0, stream, q, units,
                      pool, pool_cap, esc_cursor, k_tail, v_tail, page_table, max_pages, seq_lens, B, Hq, H, P, num_pages, plan, scale,
                      ws_acc, ws_ml, status);
   return hipGetLastError() == hipSuccess ? 0 : -4;

@@ -44,7 +44,7 @@ struct MhaStage {
 // unit 0 instead and marks the stage), so that every path through the main loop has the same
 // loads in flight and the next step's loads can overlap the current step's compute.
 // `live` is false for a stage issued past the last step: its loads read nothing.
-template <int D>
+template <int D, bool CH>
 __device__ __forceinline__ void mha_issue(MhaStage<D>& st, const uint8_t* units, int pid, int page, int tile, int H,
                                           int h, int P, int num_pages, int lane, bool live = true) {
   st.ok = pid >= 0 && pid < num_pages;
@@ -52,13 +52,13 @@ __device__ __forceinline__ void mha_issue(MhaStage<D>& st, const uint8_t* units,
   st.unit = units + ((size_t)(st.ok ? pid : 0) * H + h) * unit_bytes(P, D);
   st.tile = tile;
   st.meta = load_meta(st.unit, P, D, tile, lane, live);
-  load_k<D, false>(st.unit, P, tile, lane, st.k, live);
+  load_k<D, false, true, CH>(st.unit, P, tile, lane, st.k, live);
   load_v<D>(st.unit, P, tile, lane, st.v, live);
 }
 
 // Returns false, leaving the state untouched, when the unit's escapes are in the pool and POOL
 // is off.
-template <int D, bool POOL>
+template <int D, bool POOL, bool CH>
 __device__ __forceinline__ bool mha_compute(MhaState<D>& st, const MhaStage<D>& stg, int P, uint32_t& krank,
                                             uint32_t& vrank, uint16_t* lds, const uint16_t* pool, int64_t pool_cap,
                                             float scale, int lane) {
@@ -69,7 +69,7 @@ __device__ __forceinline__ bool mha_compute(MhaState<D>& st, const MhaStage<D>& 
   if (POOL) clamp_to_pool(hdr, pool_cap);
   if (stg.tile == 0) { krank = 0; vrank = 0; }
   uint32_t kp[VK / 2];
-  decode_k<D>(stg.k, kp);
+  decode_k<D, CH>(stg.k, kp);
   if (hdr.kc) patch_k_tile<D, false, POOL>(kp, stg.k, stg.meta, hdr, P, stg.tile, krank, lds, pool, pool_cap, lane);
   float sc[D / 64];
   mha_scores<D>(st, kp, scale, sc);
@@ -77,7 +77,7 @@ __device__ __forceinline__ bool mha_compute(MhaState<D>& st, const MhaStage<D>& 
   mha_softmax<D>(st, sc, phi, plo);
   uint32_t vp[NS * 8];
 #pragma unroll
-  for (int g = 0; g < NS; ++g) decode_v_seg(stg.v.seg[g], v_bases<D>(stg.meta, g), &vp[8 * g]);
+  for (int g = 0; g < NS; ++g) decode_v_seg(stg.v.seg[g], v_bases<D, CH>(stg.meta, g), &vp[8 * g]);
   if (hdr.vc) patch_v_tile<D, POOL>(vp, stg.v, stg.meta, hdr, P, stg.tile, vrank, lds, pool, pool_cap, lane);
   mha_accumulate_v<D>(st, vp, phi, plo);
   return true;
@@ -89,8 +89,8 @@ __device__ __forceinline__ bool mha_compute(MhaState<D>& st, const MhaStage<D>& 
 // and any other pool unit between them, found by reading the unit headers 64 at a time. The
 // pool path thus costs registers only outside the loop, and the rare pool unit costs only its
 // own work. Four waves per SIMD is the register budget (128 VGPRs at D = 128): the streaming rate
-// needs them, and the pool-capable loop is fitted into it.
-template <int D>
+// needs them, and the pool-capable loop is fitted into it. CH: channel groups (format 2).
+template <int D, bool CH>
 __global__ __launch_bounds__(64 * kWavesPerBlock) __attribute__((amdgpu_waves_per_eu(4))) void attn_mha_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ units, const uint16_t* __restrict__ pool,
     int64_t pool_cap, const uint64_t* __restrict__ esc_cursor, const uint16_t* __restrict__ k_tail,
@@ -195,21 +195,21 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) __attribute__((amdgpu_waves_pe
     };
     MhaStage<D> a, b;
     int pid = sload<int32_t>(pt_row + lp);
-    mha_issue<D>(a, units, pid, lp, lt, H, h, P, num_pages, lane);
+    mha_issue<D, CH>(a, units, pid, lp, lt, H, h, P, num_pages, lane);
     advance();
     pid = sload<int32_t>(pt_row + lp);   // one step ahead of its use
     for (int i = 0; i < nsteps; i += 2) {
-      mha_issue<D>(b, units, pid, lp, lt, H, h, P, num_pages, lane, live);
+      mha_issue<D, CH>(b, units, pid, lp, lt, H, h, P, num_pages, lane, live);
       advance();
       pid = sload<int32_t>(pt_row + lp);
       bad |= !a.ok;
-      if (!mha_compute<D, false>(st, a, P, krank, vrank, lds, pool, pool_cap, scale, lane)) note(a, i + 1);
+      if (!mha_compute<D, false, CH>(st, a, P, krank, vrank, lds, pool, pool_cap, scale, lane)) note(a, i + 1);
       if (i + 1 >= nsteps || resume >= 0) break;
-      mha_issue<D>(a, units, pid, lp, lt, H, h, P, num_pages, lane, live);
+      mha_issue<D, CH>(a, units, pid, lp, lt, H, h, P, num_pages, lane, live);
       advance();
       pid = sload<int32_t>(pt_row + lp);
       bad |= !b.ok;
-      if (!mha_compute<D, false>(st, b, P, krank, vrank, lds, pool, pool_cap, scale, lane)) note(b, i + 2);
+      if (!mha_compute<D, false, CH>(st, b, P, krank, vrank, lds, pool, pool_cap, scale, lane)) note(b, i + 2);
       if (resume >= 0) break;
     }
   }
@@ -232,7 +232,7 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) __attribute__((amdgpu_waves_pe
         nu = unit_of(n + 1, nok);
         nmeta = load_meta(nu, P, D, (n + 1) % T, lane);
       }
-      if (ok) mha_any_tile<D>(st, u, meta, P, n % T, krank, vrank, lds, pool, pool_cap, scale, lane);
+      if (ok) mha_any_tile<D, CH>(st, u, meta, P, n % T, krank, vrank, lds, pool, pool_cap, scale, lane);
       bad |= !ok;
       u = nu;
       ok = nok;
@@ -246,8 +246,8 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) __attribute__((amdgpu_waves_pe
       const int pid = sload<int32_t>(pt_row + page);
       for (int t = 0; t < T; ++t) {
         MhaStage<D> a;
-        mha_issue<D>(a, units, pid, page, t, H, h, P, num_pages, lane);
-        mha_compute<D, true>(st, a, P, krank, vrank, lds, pool, pool_cap, scale, lane);
+        mha_issue<D, CH>(a, units, pid, page, t, H, h, P, num_pages, lane);
+        mha_compute<D, true, CH>(st, a, P, krank, vrank, lds, pool, pool_cap, scale, lane);
       }
     };
     do_page(first_skip);
@@ -293,14 +293,16 @@ int launch_attn_mha(const uint16_t* q, const uint8_t* units, const uint16_t* poo
                     const uint64_t* esc_cursor, const uint16_t* k_tail,
                     const uint16_t* v_tail, const int32_t* page_table, int max_pages, const int32_t* seq_lens,
                     int B, int Hq, int H, int D, int P, int num_pages, SplitPlan plan, float scale, float* ws_acc,
-                    float* ws_ml, uint32_t* status, hipStream_t stream) {
-  static int slots128[64], slots64[64];
+                    float* ws_ml, uint32_t* status, bool channel, hipStream_t stream) {
+  static int slots128[64], slots64[64], slots128c[64], slots64c[64];
   if (H <= 0 || Hq % H) return -2;
   const dim3 block(64 * kWavesPerBlock);
   if (D == 128) {
-    plan.slots = resident_waves(attn_mha_kernel<128>, block.x, slots128, 64);
+    plan.slots = channel ? resident_waves(attn_mha_kernel<128, true>, block.x, slots128c, 64)
+                         : resident_waves(attn_mha_kernel<128, false>, block.x, slots128, 64);
   } else if (D == 64) {
-    plan.slots = resident_waves(attn_mha_kernel<64>, block.x, slots64, 64);
+    plan.slots = channel ? resident_waves(attn_mha_kernel<64, true>, block.x, slots64c, 64)
+                         : resident_waves(attn_mha_kernel<64, false>, block.x, slots64, 64);
   } else {
     return -2;
   }
@@ -312,12 +314,10 @@ int launch_attn_mha(const uint16_t* q, const uint8_t* units, const uint16_t* poo
   rank_fit(plan, plan.slots, (long)B * Hq);
   plan.slots = plan.slots > 0 ? 2 * plan.slots : B * Hq * plan.S;
   const dim3 grid(plan_blocks(plan, (long)B * Hq, kWavesPerBlock));
-  if (D == 128)
-    hipLaunchKernelGGL((attn_mha_kernel<128>), grid, block, 0, stream, q, units, pool, pool_cap, esc_cursor, k_tail, v_tail, page_table,
-                       max_pages, seq_lens, B, H, Hq / H, P, num_pages, plan, scale, ws_acc, ws_ml, status);
-  else
-    hipLaunchKernelGGL((attn_mha_kernel<64>), grid, block, 0, stream, q, units, pool, pool_cap, esc_cursor, k_tail, v_tail, page_table,
-                       max_pages, seq_lens, B, H, Hq / H, P, num_pages, plan, scale, ws_acc, ws_ml, status);
+  auto kernel = D == 128 ? (channel ? attn_mha_kernel<128, true> : attn_mha_kernel<128, false>)
+                         : (channel ? attn_mha_kernel<64, true> : attn_mha_kernel<64, false>);
+  hipLaunchKernelGGL(kernel, grid, block, 0, stream, q, units, pool, pool_cap, esc_cursor, k_tail, v_tail, page_table,
+                     max_pages, seq_lens, B, H, Hq / H, P, num_pages, plan, scale, ws_acc, ws_ml, status);
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 

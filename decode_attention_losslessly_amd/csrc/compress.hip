@@ -1,7 +1,7 @@
-// kvz_compress_pages and kvz_append_token kernels, for both cache formats (0: exponent offsets
-// with escapes, compress.hpp; 1: ZipFusion blocks, zf.hpp). Units of the first format with head
-// dim 64 or 128 are compressed one wave per unit (compress_wave.hpp); the workgroup compressor
-// serves the other head dims and the block format.
+// kvz_compress_pages and kvz_append_token kernels, for the three cache formats (0: exponent
+// offsets with escapes, compress.hpp; 1: ZipFusion blocks, zf.hpp; 2: format 0 with channel
+// groups, compress.hpp). Units of format 0 with head dim 64 or 128 are compressed one wave per
+// unit (compress_wave.hpp); the workgroup compressor serves the other head dims and formats.
 #include "compress.hpp"
 #include "compress_wave.hpp"
 #include "zf.hpp"
@@ -20,6 +20,11 @@ __device__ __forceinline__ void compress_any(const uint16_t* k, const uint16_t* 
     const int nb = zf_nblocks(P, D);
     compress_unit_zf(k, v, P, D, units + ((size_t)pid * H + h) * zf_unit_bytes(P, D), pool, pool_cap, cursor, status,
                      sx, smem + 4 * blk, reinterpret_cast<uint16_t*>(smem + 4 * blk + (nb + 1) / 2 * 2), sh);
+  } else if (format == 2) {
+    uint8_t* unit = units + ((size_t)pid * H + h) * unit_bytes(P, D);
+    if (D == 128) compress_unit<128, true>(k, v, P, D, unit, pool, pool_cap, cursor, status, sx, smem + 4 * blk, sh);
+    else if (D == 64) compress_unit<64, true>(k, v, P, D, unit, pool, pool_cap, cursor, status, sx, smem + 4 * blk, sh);
+    else compress_unit<0, true>(k, v, P, D, unit, pool, pool_cap, cursor, status, sx, smem + 4 * blk, sh);
   } else {
     uint8_t* unit = units + ((size_t)pid * H + h) * unit_bytes(P, D);
     if (D == 128) compress_unit<128>(k, v, P, D, unit, pool, pool_cap, cursor, status, sx, smem + 4 * blk, sh);

@@ -12,6 +12,8 @@
 //      an atomically bumped cursor;
 //   4. storage positions are encoded 8 per thread (one offset word, 8 sm bytes) in storage
 //      order, with a workgroup scan giving each escape its rank.
+// CH selects the channel groups (format 2): a group is a tile's 16 tokens over 4 adjacent dims
+// instead of one token's 64 dims; its base is byte tile * D/4 + dim/4 of the block's base table.
 #pragma once
 
 #include "kvz_device.hpp"
@@ -80,14 +82,20 @@ __device__ __forceinline__ int storage_to_index(int s, int D) {
   return (t * kTile + tok) * D + d;
 }
 
+// Index in a block's base table of the group holding (token tok, dim d).
+template <bool CH>
+__device__ __forceinline__ int base_index(int tok, int d, int D) {
+  if (CH) return (tok / kTile) * (D / 4) + d / 4;
+  return (tok / kTile) * kTile * (D / kGroup) + (d / kGroup) * kTile + (tok % kTile);
+}
+
 // Writes the block's payload; its escapes go to `inline_dst` as value | position << 16 entries
 // or to `pool_dst` as values (whichever is non-null), starting at entry/element 0.
 // DT: the head dim when fixed at compile time, 0 to take it from d_rt
-template <bool IsV, int DT>
+template <bool IsV, int DT, bool CH = false>
 __device__ void encode_block(const uint16_t* X, const uint8_t* bases_meta, int P, int d_rt,
                              uint8_t* payload, uint32_t* inline_dst, uint16_t* pool_dst, CompressShared& sh) {
   const int D = DT ? DT : d_rt;
-  const int G = D / kGroup;
   const int nchunks = P * D / 8;
   uint32_t rank = 0;
   for (int c0 = 0; c0 < nchunks; c0 += kCompressThreads) {
@@ -104,7 +112,7 @@ __device__ void encode_block(const uint16_t* X, const uint8_t* bases_meta, int P
         const int tok = idx / D, d = idx % D;
         const uint16_t x = X[idx];
         xs[j] = x;
-        const int b = bases_meta[(tok / kTile) * kTile * G + (d / kGroup) * kTile + (tok % kTile)];
+        const int b = bases_meta[base_index<CH>(tok, d, D)];
         const int e = (x >> 7) & 0xFF;
         int off = e - b;
         if (off < 0 || off > 14) { off = kEscape; escmask |= 1u << j; ++ne; }
@@ -137,7 +145,7 @@ __device__ void encode_block(const uint16_t* X, const uint8_t* bases_meta, int P
 
 // Compresses src_k, src_v ([P][D] token-major raw BF16) into `unit`. DT: the head dim when fixed
 // at compile time (64, 128), 0 to take it from d_rt.
-template <int DT>
+template <int DT, bool CH = false>
 __device__ void compress_unit(const uint16_t* __restrict__ src_k, const uint16_t* __restrict__ src_v, int P, int d_rt,
                               uint8_t* __restrict__ unit, uint16_t* __restrict__ pool, int64_t pool_cap,
                               uint64_t* __restrict__ cursor, uint32_t* __restrict__ status,
@@ -156,13 +164,16 @@ __device__ void compress_unit(const uint16_t* __restrict__ src_k, const uint16_t
   uint32_t cnt[2] = {0, 0};
   const int ngroups = 2 * P * G;
   for (int q = wave; q < ngroups; q += kCompressThreads / 64) {
-    const int tensor = q / (P * G), rem = q % (P * G), tok = rem / G, g = rem % G;
-    const uint16_t x = sh_x[tensor * PD + tok * D + g * kGroup + lane];
+    const int tensor = q / (P * G), rem = q % (P * G);
+    int tok, d;   // this lane's value of the group
+    if (CH) { tok = (rem / (D / 4)) * kTile + lane / 4; d = 4 * (rem % (D / 4)) + lane % 4; }
+    else { tok = rem / G; d = (rem % G) * kGroup + lane; }
+    const uint16_t x = sh_x[tensor * PD + tok * D + d];
     const uint32_t e = (x >> 7) & 0xFFu;
     const uint32_t b = group_base(e, sh.bins[wave], lane);
     const uint64_t escm = ballot((e - b) > 14u);
     cnt[tensor] += (uint32_t)__builtin_popcountll(escm);
-    if (lane == 0) sh_base[tensor * P * G + (tok / kTile) * kTile * G + g * kTile + (tok % kTile)] = (uint8_t)b;
+    if (lane == 0) sh_base[tensor * P * G + base_index<CH>(tok, d, D)] = (uint8_t)b;
   }
   if (lane == 0) {
     atomicAdd(&sh.esc_count[0], cnt[0]);
@@ -194,9 +205,9 @@ __device__ void compress_unit(const uint16_t* __restrict__ src_k, const uint16_t
   uint32_t* inl = (keep && dest == kInline) ? reinterpret_cast<uint32_t*>(unit + hdr + 16) : nullptr;
   uint16_t* pl = (keep && dest != kInline) ? pool + dest : nullptr;
   // 4. payload and escapes
-  encode_block<false, DT>(sh_x, sh_base, P, D, unit + kblock_offset(P, D), inl, pl, sh);
-  encode_block<true, DT>(sh_x + PD, sh_base + P * G, P, D, unit + vblock_offset(P, D), inl ? inl + kc : nullptr,
-                         pl ? pl + kc : nullptr, sh);
+  encode_block<false, DT, CH>(sh_x, sh_base, P, D, unit + kblock_offset(P, D), inl, pl, sh);
+  encode_block<true, DT, CH>(sh_x + PD, sh_base + P * G, P, D, unit + vblock_offset(P, D), inl ? inl + kc : nullptr,
+                             pl ? pl + kc : nullptr, sh);
   // 5. meta: bases, header, zero tail of the inline area
   for (int i = tid; i < 2 * P * G; i += kCompressThreads) unit[i] = sh_base[i];
   const uint32_t used = inl ? 4 * total : 0;

@@ -7,12 +7,13 @@
 //              pairs in LDS (patch_k_tile / patch_v_tile);
 //   WIN true   the pool-capable loops: a pool unit's escape windows staged with the payload and
 //              every offset word patched from them (any_stage / any_rebuild_k / any_rebuild_v).
+// CH: channel groups (format 2).
 #include "kvz_lanes.hpp"
 #include "mha_pool.hpp"
 
 namespace kvz {
 
-template <int D, bool GQA, bool WIN>
+template <int D, bool GQA, bool WIN, bool CH>
 __global__ __launch_bounds__(64) void decompress_kernel(const uint8_t* __restrict__ units,
                                                         const uint16_t* __restrict__ pool, int64_t pool_cap,
                                                         const int32_t* __restrict__ page_ids, int H,
@@ -45,16 +46,16 @@ __global__ __launch_bounds__(64) void decompress_kernel(const uint8_t* __restric
       load_v<D>(unit, P, t, lane, vr);
       Window kw, vw;
       const bool in_pool = any_stage<D>(hdr, krank, vrank, lds, pool, pool_cap, kw, vw, lane);
-      any_rebuild_k<D, GQA>(kp, kr, meta, hdr, in_pool, kw, P, t, krank, lds, pool, pool_cap, lane);
-      any_rebuild_v<D>(vp, vr, meta, hdr, in_pool, vw, P, t, vrank, lds, pool, pool_cap, lane);
+      any_rebuild_k<D, GQA, CH>(kp, kr, meta, hdr, in_pool, kw, P, t, krank, lds, pool, pool_cap, lane);
+      any_rebuild_v<D, CH>(vp, vr, meta, hdr, in_pool, vw, P, t, vrank, lds, pool, pool_cap, lane);
       if (in_pool) wave_lds_sync();
     } else {
-      load_k<D, GQA>(unit, P, t, lane, kr);
-      decode_k<D>(kr, kp);
+      load_k<D, GQA, true, CH>(unit, P, t, lane, kr);
+      decode_k<D, CH>(kr, kp);
       if (hdr.kc) patch_k_tile<D, GQA>(kp, kr, meta, hdr, P, t, krank, lds, pool, pool_cap, lane);
       load_v<D>(unit, P, t, lane, vr);
 #pragma unroll
-      for (int s = 0; s < NS; ++s) decode_v_seg(vr.seg[s], v_bases<D>(meta, s), &vp[8 * s]);
+      for (int s = 0; s < NS; ++s) decode_v_seg(vr.seg[s], v_bases<D, CH>(meta, s), &vp[8 * s]);
       if (hdr.vc) patch_v_tile<D>(vp, vr, meta, hdr, P, t, vrank, lds, pool, pool_cap, lane);
     }
 #pragma unroll
@@ -78,13 +79,13 @@ __global__ __launch_bounds__(64) void decompress_kernel(const uint8_t* __restric
 
 int launch_decompress(const uint8_t* units, const uint16_t* pool, int64_t pool_cap, const int32_t* page_ids, int n, int H,
                       int P, int D, int num_pages, int lane_map, uint16_t* k_dst, uint16_t* v_dst,
-                      uint32_t* status, hipStream_t stream) {
+                      uint32_t* status, bool channel, hipStream_t stream) {
   // lane_map: 0 / 1 = multi-head / grouped-query layout through the main loops' route,
   //           2 / 3 = the same layouts through the pool-capable loops' route
   const dim3 grid((unsigned)n * H), block(64);
-#define KVZ_DECOMPRESS(d, gqa, win)                                                                                  \
-  hipLaunchKernelGGL((decompress_kernel<d, gqa, win>), grid, block, 0, stream, units, pool, pool_cap, page_ids, H, P, \
-                     num_pages, k_dst, v_dst, status)
+#define KVZ_DECOMPRESS(d, gqa, win)                                                                          \
+  hipLaunchKernelGGL((channel ? decompress_kernel<d, gqa, win, true> : decompress_kernel<d, gqa, win, false>), grid, \
+                     block, 0, stream, units, pool, pool_cap, page_ids, H, P, num_pages, k_dst, v_dst, status)
   if (D == 128) {
     switch (lane_map) {
       case 0: KVZ_DECOMPRESS(128, false, false); break;

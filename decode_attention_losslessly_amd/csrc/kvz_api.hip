@@ -12,7 +12,7 @@
 namespace kvz {
 int launch_decompress(const uint8_t* units, const uint16_t* pool, int64_t pool_cap, const int32_t* page_ids, int n, int H, int P,
                       int D, int num_pages, int lane_map, uint16_t* k_dst, uint16_t* v_dst, uint32_t* status,
-                      hipStream_t stream);
+                      bool channel, hipStream_t stream);
 int launch_compress(const uint16_t* k_src, const uint16_t* v_src, const int32_t* ids, int n, int H, int P, int D,
                     int num_pages, uint8_t* units, uint16_t* pool, int64_t pool_cap, uint64_t* cursor,
                     uint32_t* status, int format, hipStream_t stream);
@@ -35,12 +35,12 @@ int launch_attn_mha(const uint16_t* q, const uint8_t* units, const uint16_t* poo
                     const uint64_t* esc_cursor, const uint16_t* k_tail,
                     const uint16_t* v_tail, const int32_t* page_table, int max_pages, const int32_t* seq_lens,
                     int B, int Hq, int H, int D, int P, int num_pages, SplitPlan plan, float scale, float* ws_acc,
-                    float* ws_ml, uint32_t* status, hipStream_t stream);
+                    float* ws_ml, uint32_t* status, bool channel, hipStream_t stream);
 int launch_attn_gqa(const uint16_t* q, const uint8_t* units, const uint16_t* pool, int64_t pool_cap,
                     const uint64_t* esc_cursor, const uint16_t* k_tail,
                     const uint16_t* v_tail, const int32_t* page_table, int max_pages, const int32_t* seq_lens,
                     int B, int Hq, int Hkv, int D, int P, int num_pages, SplitPlan plan, float scale, float* ws_acc,
-                    float* ws_ml, uint32_t* status, hipStream_t stream);
+                    float* ws_ml, uint32_t* status, bool channel, hipStream_t stream);
 int launch_attn_dense_mha(const uint16_t* q, const uint16_t* k_pages, const uint16_t* v_pages, const int32_t* pt,
                           int max_pages, const int32_t* seq_lens, int B, int Hq, int H, int D, int P,
                           int num_pages, SplitPlan plan, float scale, float* ws_acc, float* ws_ml, uint32_t* status,
@@ -130,7 +130,8 @@ bool shape_ok(int P, int D) {
 
 // Compression stages a unit's values in LDS (160 KB per workgroup): the wave compressor (first
 // format, head dim 64 or 128) holds the V block, up to the format's largest block of 65536
-// values; the workgroup compressor (other head dims, the block format) holds K and V, half that.
+// values; the workgroup compressor (other head dims, the block format, channel groups) holds K
+// and V, half that.
 bool compress_fits(const kvz_cache* c) {
   const int64_t n = (int64_t)c->page_size * c->head_dim;
   const bool wave = c->format == KVZ_FORMAT_ESCAPE && (c->head_dim == 64 || c->head_dim == 128);
@@ -145,7 +146,7 @@ bool cache_ok(const kvz_cache* c) {
   return c && (c->units || c->num_pages == 0) && c->status && shape_ok(c->page_size, c->head_dim) &&
          c->num_kv_heads > 0 &&
          c->num_pages >= 0 && c->max_batch >= 0 && c->esc_capacity >= 0 && c->esc_cursor &&
-         (c->format == KVZ_FORMAT_ESCAPE || c->format == KVZ_FORMAT_ZIPFUSION);
+         (c->format == KVZ_FORMAT_ESCAPE || c->format == KVZ_FORMAT_ZIPFUSION || c->format == KVZ_FORMAT_CHANNEL);
 }
 
 hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
@@ -187,7 +188,7 @@ extern "C" {
 size_t kvz_unit_bytes(int32_t P, int32_t D) { return shape_ok(P, D) ? kvz::unit_bytes(P, D) : 0; }
 size_t kvz_unit_bytes_for(int32_t format, int32_t P, int32_t D) {
   if (!shape_ok(P, D)) return 0;
-  if (format == KVZ_FORMAT_ESCAPE) return kvz::unit_bytes(P, D);
+  if (format == KVZ_FORMAT_ESCAPE || format == KVZ_FORMAT_CHANNEL) return kvz::unit_bytes(P, D);
   if (format == KVZ_FORMAT_ZIPFUSION) return kvz::zf_unit_bytes(P, D);
   return 0;
 }
@@ -300,11 +301,11 @@ int kvz_decode_attention_splits(const uint16_t* q, const kvz_cache* c, const int
     plan.rank_min = pps < 0 ? 0 : kRankMinPages;
     rc = kvz::launch_attn_mha(q, c->units, c->esc_pool, c->esc_capacity, c->esc_cursor, c->k_tail, c->v_tail,
                               page_table, max_pages, seq_lens, B, H_q, H, D, P, c->num_pages, plan, scale, ws_acc,
-                              ws_ml, c->status, as_stream(stream));
+                              ws_ml, c->status, c->format == KVZ_FORMAT_CHANNEL, as_stream(stream));
   } else {
     rc = kvz::launch_attn_gqa(q, c->units, c->esc_pool, c->esc_capacity, c->esc_cursor, c->k_tail, c->v_tail, page_table, max_pages, seq_lens, B,
                               H_q, H, D, P, c->num_pages, plan, scale, ws_acc, ws_ml, c->status,
-                              as_stream(stream));
+                              c->format == KVZ_FORMAT_CHANNEL, as_stream(stream));
   }
   return rc ? (rc == -2 ? KVZ_ERR_UNSUPPORTED : KVZ_ERR_HIP) : KVZ_OK;
 }
@@ -419,7 +420,8 @@ int kvz_decompress_pages(const kvz_cache* c, const int32_t* page_ids, int32_t n,
     return rc == -2 ? KVZ_ERR_UNSUPPORTED : (rc ? KVZ_ERR_HIP : KVZ_OK);
   }
   const int rc = kvz::launch_decompress(c->units, c->esc_pool, c->esc_capacity, page_ids, n, c->num_kv_heads, c->page_size, D,
-                                        c->num_pages, lane_map, k_dst, v_dst, c->status, as_stream(stream));
+                                        c->num_pages, lane_map, k_dst, v_dst, c->status,
+                                        c->format == KVZ_FORMAT_CHANNEL, as_stream(stream));
   return rc == -2 ? KVZ_ERR_UNSUPPORTED : (rc ? KVZ_ERR_HIP : KVZ_OK);
 }
 

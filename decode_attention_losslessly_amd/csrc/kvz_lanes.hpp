@@ -67,6 +67,10 @@ __device__ __forceinline__ uint32_t uload1(UnitRsrc r, uint32_t voff, uint32_t s
 }
 
 // ---------------------------------------------------------------- K
+// Channel groups (CH, format 2): a base covers 4 adjacent dims over the tile's 16 tokens, so the
+// 16 dims of a piece take 4 bases, one dword of the tile's base table (byte dim/4): base[i] then
+// holds that dword for piece i. In the multi-head layout a lane's pieces share their dims, and
+// so their dword.
 template <int D>
 struct KRaw {
   static constexpr int VK = 2 * (D / kGroup) * 8;   // values per lane: D / 4
@@ -94,7 +98,7 @@ __device__ __forceinline__ int piece_dim(int piece) { return (16 * piece) % D; }
 // arrives in the same round trip); without, the caller takes them from the tile's meta window
 // (k_bases_from_meta), which the pool-capable loops load a step ahead: a second read of those
 // bytes a step later could miss the caches and fetch the line again.
-template <int D, bool GQA, bool BASES = true>
+template <int D, bool GQA, bool BASES = true, bool CH = false>
 __device__ __forceinline__ void load_k(const uint8_t* unit, int P, int tile, int lane, KRaw<D>& r, bool live = true) {
   constexpr int NP = KRaw<D>::NP;
   const UnitRsrc u = unit_rsrc(unit, live ? unit_bytes(P, D) : 0u);
@@ -108,15 +112,25 @@ __device__ __forceinline__ void load_k(const uint8_t* unit, int P, int tile, int
     if constexpr (!GQA) {
       const uint2 n = uload8(u, 16 * D + 8 * pc, tb);
       r.nib[2 * i] = n.x; r.nib[2 * i + 1] = n.y;
-      if constexpr (BASES) r.base[i] = uload1(u, (piece_dim<D>(pc) / kGroup) * kTile + piece_token<D>(pc), bases);
+      if constexpr (BASES && !CH) r.base[i] = uload1(u, (piece_dim<D>(pc) / kGroup) * kTile + piece_token<D>(pc), bases);
     }
+  }
+  if constexpr (!GQA && BASES && CH) {   // the pieces' dims are the same: one dword for all
+    const uint32_t b = uload4(u, piece_dim<D>(k_piece<D, GQA>(lane, 0)) / 4, bases);
+#pragma unroll
+    for (int i = 0; i < NP; ++i) r.base[i] = b;
   }
   if constexpr (GQA) {   // the two pieces are adjacent: one 16-byte offset load, one base
     const int pc = k_piece<D, GQA>(lane, 0);
     const uint4 n = uload16(u, 16 * D + 8 * pc, tb);
     r.nib[0] = n.x; r.nib[1] = n.y; r.nib[2] = n.z; r.nib[3] = n.w;
-    if constexpr (BASES)
+    if constexpr (BASES && CH) {   // 32 dims: two dwords of the base table
+      const uint2 b = uload8(u, piece_dim<D>(pc) / 4, bases);
+      r.base[0] = b.x;
+      r.base[1] = b.y;
+    } else if constexpr (BASES) {
       r.base[0] = r.base[1] = uload1(u, (piece_dim<D>(pc) / kGroup) * kTile + piece_token<D>(pc), bases);
+    }
   }
 }
 
@@ -152,10 +166,15 @@ __device__ __forceinline__ uint32_t k_piece_base(uint32_t meta, int pc) {
   return ((uint32_t)__shfl((int)meta, idx >> 2) >> (8 * (idx & 3))) & 0xFFu;
 }
 
-// the bases of a K tile loaded without them (load_k<D, GQA, false>)
-template <int D, bool GQA>
+// the bases of a K tile loaded without them (load_k<D, GQA, false>); with channel groups, a
+// piece's dword of the base table is window lane piece_dim / 16
+template <int D, bool GQA, bool CH = false>
 __device__ __forceinline__ void k_bases_from_meta(KRaw<D>& r, uint32_t meta, int lane) {
-  if constexpr (GQA) {   // the lane's two pieces are one token's adjacent dims: one group
+  if constexpr (CH) {
+#pragma unroll
+    for (int i = 0; i < KRaw<D>::NP; ++i)
+      r.base[i] = (uint32_t)__shfl((int)meta, piece_dim<D>(k_piece<D, GQA>(lane, i)) / 16);
+  } else if constexpr (GQA) {   // the lane's two pieces are one token's adjacent dims: one group
     r.base[0] = r.base[1] = k_piece_base<D>(meta, k_piece<D, GQA>(lane, 0));
   } else {
 #pragma unroll
@@ -163,13 +182,27 @@ __device__ __forceinline__ void k_bases_from_meta(KRaw<D>& r, uint32_t meta, int
   }
 }
 
-template <int D>
+// base byte k of a dword as the term b << 7 | b << 23 of a pair whose two values share it
+template <int k>
+__device__ __forceinline__ uint32_t byte_base_term(uint32_t w) {
+  return __builtin_amdgcn_perm(0u, w, 0x0C000C00u | (uint32_t)(k * 0x00010001)) << 7;
+}
+
+template <int D, bool CH = false>
 __device__ __forceinline__ void decode_k(const KRaw<D>& r, uint32_t (&pairs)[KRaw<D>::VK / 2]) {
 #pragma unroll
   for (int i = 0; i < KRaw<D>::NP; ++i) {
-    const uint32_t bb = opaque(r.base[i] * 0x00800080u);   // once per piece, not folded into each pair
-    decode8(r.sm[4 * i], r.sm[4 * i + 1], r.nib[2 * i], bb, bb, bb, bb, &pairs[8 * i]);
-    decode8(r.sm[4 * i + 2], r.sm[4 * i + 3], r.nib[2 * i + 1], bb, bb, bb, bb, &pairs[8 * i + 4]);
+    if constexpr (CH) {   // dims 4k .. 4k+3 of the piece (pairs 2k, 2k+1) share base byte k
+      const uint32_t w = r.base[i];
+      const uint32_t b0 = byte_base_term<0>(w), b1 = byte_base_term<1>(w);
+      const uint32_t b2 = byte_base_term<2>(w), b3 = byte_base_term<3>(w);
+      decode8(r.sm[4 * i], r.sm[4 * i + 1], r.nib[2 * i], b0, b0, b1, b1, &pairs[8 * i]);
+      decode8(r.sm[4 * i + 2], r.sm[4 * i + 3], r.nib[2 * i + 1], b2, b2, b3, b3, &pairs[8 * i + 4]);
+    } else {
+      const uint32_t bb = opaque(r.base[i] * 0x00800080u);   // once per piece, not folded into each pair
+      decode8(r.sm[4 * i], r.sm[4 * i + 1], r.nib[2 * i], bb, bb, bb, bb, &pairs[8 * i]);
+      decode8(r.sm[4 * i + 2], r.sm[4 * i + 3], r.nib[2 * i + 1], bb, bb, bb, bb, &pairs[8 * i + 4]);
+    }
   }
 }
 
@@ -205,9 +238,20 @@ struct VBases {
   uint32_t bb[8];
 };
 
-template <int D>
+// With channel groups (CH) every token of the lane's dim d = lane + 64 g shares one base, byte
+// d/4 of the tile's V base table: window lane 4G + d/16.
+template <int D, bool CH = false>
 __device__ __forceinline__ VBases v_bases(uint32_t meta, int g) {
   constexpr int G = D / kGroup;
+  if constexpr (CH) {
+    const int d = lane_id() + 64 * g;
+    const uint32_t w = (uint32_t)__shfl((int)meta, 4 * G + d / 16);
+    const uint32_t t = ((w >> (8 * ((d >> 2) & 3))) & 0xFFu) * 0x00800080u;
+    VBases r;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) r.bb[i] = t;
+    return r;
+  }
   const uint32_t lo = __builtin_amdgcn_perm(0u, meta, 0x0C010C00u) << 7;
   const uint32_t hi = __builtin_amdgcn_perm(0u, meta, 0x0C030C02u) << 7;
   VBases r;

@@ -213,13 +213,13 @@ __device__ __forceinline__ bool any_stage(const UnitHeader& hdr, uint32_t krank,
 // Rebuilds the tile's K pairs in the given lane layout (k loaded without its bases, which come
 // from the meta window) and patches its escapes: from the staged K window for a pool unit, else
 // from the inline list.
-template <int D, bool GQA>
+template <int D, bool GQA, bool CH = false>
 __device__ __forceinline__ void any_rebuild_k(uint32_t (&kp)[KRaw<D>::VK / 2], KRaw<D>& k, uint32_t meta,
                                               const UnitHeader& hdr, bool in_pool, const Window& kw, int P, int tile,
                                               uint32_t& krank, uint16_t* lds, const uint16_t* pool, int64_t pool_cap,
                                               int lane) {
-  k_bases_from_meta<D, GQA>(k, meta, lane);
-  decode_k<D>(k, kp);
+  k_bases_from_meta<D, GQA, CH>(k, meta, lane);
+  decode_k<D, CH>(k, kp);
   if (hdr.kc) {
     if (in_pool) {
       if constexpr (GQA) krank = uniform(krank) + win_patch_k_gqa(kp, k, lds, kw, lane);
@@ -232,13 +232,13 @@ __device__ __forceinline__ void any_rebuild_k(uint32_t (&kp)[KRaw<D>::VK / 2], K
 
 // Rebuilds the tile's V pairs (lane l: dims l + 64 s, token pairs) and patches its escapes: from
 // the staged V window for a pool unit, else from the inline list.
-template <int D>
+template <int D, bool CH = false>
 __device__ __forceinline__ void any_rebuild_v(uint32_t (&vp)[D / 8], const VRaw<D>& v, uint32_t meta,
                                               const UnitHeader& hdr, bool in_pool, const Window& vw, int P, int tile,
                                               uint32_t& vrank, uint16_t* lds, const uint16_t* pool, int64_t pool_cap,
                                               int lane) {
 #pragma unroll
-  for (int g = 0; g < D / 64; ++g) decode_v_seg(v.seg[g], v_bases<D>(meta, g), &vp[8 * g]);
+  for (int g = 0; g < D / 64; ++g) decode_v_seg(v.seg[g], v_bases<D, CH>(meta, g), &vp[8 * g]);
   if (hdr.vc) {
     if (in_pool) vrank = uniform(vrank) + win_patch_v<D>(vp, v, lds + win_elems<D>(), vw);
     else patch_v_tile<D, false>(vp, v, meta, hdr, P, tile, vrank, lds, pool, pool_cap, lane);
@@ -248,7 +248,7 @@ __device__ __forceinline__ void any_rebuild_v(uint32_t (&vp)[D / 8], const VRaw<
 // One tile of any unit: `meta` is its meta window (already loaded); the payload and, for a
 // pool unit, both escape windows are loaded in one round trip. krank / vrank are the block
 // cursors (escapes in the unit's earlier tiles), reset at tile 0.
-template <int D>
+template <int D, bool CH = false>
 __device__ __forceinline__ void mha_any_tile(MhaState<D>& st, const uint8_t* unit, uint32_t meta, int P, int tile,
                                              uint32_t& krank, uint32_t& vrank, uint16_t* lds, const uint16_t* pool,
                                              int64_t pool_cap, float scale, int lane) {
@@ -263,13 +263,13 @@ __device__ __forceinline__ void mha_any_tile(MhaState<D>& st, const uint8_t* uni
   Window kw, vw;
   const bool in_pool = any_stage<D>(hdr, krank, vrank, lds, pool, pool_cap, kw, vw, lane);
   uint32_t kp[VK / 2];
-  any_rebuild_k<D, false>(kp, k, meta, hdr, in_pool, kw, P, tile, krank, lds, pool, pool_cap, lane);
+  any_rebuild_k<D, false, CH>(kp, k, meta, hdr, in_pool, kw, P, tile, krank, lds, pool, pool_cap, lane);
   float sc[D / 64];
   mha_scores<D>(st, kp, scale, sc);
   uint32_t phi[8], plo[8];
   mha_softmax<D>(st, sc, phi, plo);
   uint32_t vp[NS * 8];
-  any_rebuild_v<D>(vp, v, meta, hdr, in_pool, vw, P, tile, vrank, lds, pool, pool_cap, lane);
+  any_rebuild_v<D, CH>(vp, v, meta, hdr, in_pool, vw, P, tile, vrank, lds, pool, pool_cap, lane);
   mha_accumulate_v<D>(st, vp, phi, plo);
   if (in_pool) wave_lds_sync();   // the windows are read before the next tile's staging writes
 }

@@ -19,7 +19,7 @@ LIB_PATH = os.environ.get("KVZ_LIB") or os.path.join(_HERE, "libkvz.so")
 KVZ_OK, KVZ_ERR_INVALID_ARG, KVZ_ERR_UNSUPPORTED, KVZ_ERR_WORKSPACE, KVZ_ERR_HIP, KVZ_ERR_SCRATCH = 0, -1, -2, -3, -4, -5
 NOALLOC_SCRATCH_BYTES = 32 << 20   # KVZ_NOALLOC_SCRATCH_BYTES
 STATUS_ESC_POOL_FULL, STATUS_BAD_PAGE_ID, STATUS_SEQ_TOO_LONG = 1, 2, 4
-FORMAT_ESCAPE, FORMAT_ZIPFUSION = 0, 1
+FORMAT_ESCAPE, FORMAT_ZIPFUSION, FORMAT_CHANNEL = 0, 1, 2
 
 EXPORTS = ("kvz_payload_bytes", "kvz_unit_bytes", "kvz_meta_bytes", "kvz_inline_capacity", "kvz_workspace_bytes",
            "kvz_num_splits", "kvz_compress_pages", "kvz_append_token", "kvz_decode_attention", "kvz_decode_attention_dense",
@@ -198,7 +198,7 @@ class Cache:
     k_tail: torch.Tensor       # int16 [max_batch, H, P, D]
     v_tail: torch.Tensor
     status: torch.Tensor       # int32 [1]
-    fmt: int = FORMAT_ESCAPE   # FORMAT_ESCAPE or FORMAT_ZIPFUSION (esc_pool then holds raw blocks)
+    fmt: int = FORMAT_ESCAPE   # FORMAT_ESCAPE, FORMAT_ZIPFUSION (esc_pool then holds raw blocks) or FORMAT_CHANNEL
 
     @classmethod
     def allocate(cls, P: int, H: int, D: int, num_pages: int, max_batch: int, esc_capacity: int,

@@ -61,6 +61,14 @@
  *   pool      esc_pool holds raw blocks, 512 values each, a unit's raw blocks contiguous in
  *             block order; esc_cursor must start at a multiple of 8
  *
+ * Third format, kvz_cache.format = KVZ_FORMAT_CHANNEL: the first format with channel groups
+ * (§III.B fixes a block's exponent range, not which values share a base). A group is the 16
+ * tokens of one tile over 4 adjacent dims [4j, 4j+4), still 64 values, so units, pool and sizes
+ * are those of the first format (kvz_unit_bytes); only the base table changes: the base of tile
+ * t's group j is byte t*16G + j of the K (or V) base bytes. Channels carry their own scales, so
+ * these groups escape less often (about a third as often on K with outlier channels). Head dims
+ * 64 and 128 for attention; compression and appends use the workgroup compressor.
+ *
  * Conventions for every entry point:
  *   - pointers are device pointers unless marked (host); the caller owns all memory;
  *   - calls are asynchronous on `stream` (a hipStream_t passed as void*; NULL = the default
@@ -92,7 +100,8 @@ enum {
 
 enum {
   KVZ_FORMAT_ESCAPE = 0,     /* exponent offsets with escapes (the format described above) */
-  KVZ_FORMAT_ZIPFUSION = 1   /* ZipFusion's block format (see above) */
+  KVZ_FORMAT_ZIPFUSION = 1,  /* ZipFusion's block format (see above) */
+  KVZ_FORMAT_CHANNEL = 2     /* the first format with channel groups (see above) */
 };
 
 enum {
@@ -180,8 +189,8 @@ int32_t kvz_num_splits(int32_t B, int32_t H_q, int32_t H_kv, int32_t D, int32_t 
  * Escapes that do not fit inline are appended to the pool at *esc_cursor (bumped atomically,
  * so their place in the pool depends on scheduling; everything else is deterministic).
  * Supported: P * D up to 65536 (the format's limit) for the first format at D = 64 or 128,
- * up to 32768 otherwise (the block format, other head dims): a unit's values are staged in
- * on-chip memory. Errors: KVZ_ERR_INVALID_ARG, KVZ_ERR_UNSUPPORTED. Device status:
+ * up to 32768 otherwise (the block format, channel groups, other head dims): a unit's values
+ * are staged in on-chip memory. Errors: KVZ_ERR_INVALID_ARG, KVZ_ERR_UNSUPPORTED. Device status:
  * ESC_POOL_FULL, BAD_PAGE_ID. */
 int kvz_compress_pages(const kvz_cache* cache, const uint16_t* k_src, const uint16_t* v_src,
                        const int32_t* dst_page_ids, int32_t n, void* stream);

@@ -64,6 +64,8 @@ def test_sizes_agree_with_format(P, D):
     assert kvz.unit_bytes(P, D) == codec.unit_bytes(P, D)
     assert kvz.meta_bytes(P, D) == codec.meta_bytes(P, D)
     assert kvz.inline_capacity(P, D) == codec.inline_capacity(P, D)
+    # channel groups change which values share a base, not the sizes
+    assert kvz.unit_bytes(P, D, kvz.FORMAT_CHANNEL) == kvz.unit_bytes(P, D)
 
 
 def test_unsupported_shapes_have_zero_size():
@@ -145,6 +147,8 @@ def test_invalid_arguments_enqueue_nothing():
     # first format at head dim 64 or 128, half of it otherwise (n = 0: checked, nothing enqueued)
     for fmt, P, D, want in ((0, 512, 128, binding.KVZ_OK), (0, 1024, 64, binding.KVZ_OK),
                             (1, 512, 128, binding.KVZ_ERR_UNSUPPORTED), (1, 256, 128, binding.KVZ_OK),
+                            (2, 512, 128, binding.KVZ_ERR_UNSUPPORTED), (2, 256, 128, binding.KVZ_OK),
+                            (3, 16, 128, binding.KVZ_ERR_INVALID_ARG),
                             (0, 256, 192, binding.KVZ_ERR_UNSUPPORTED), (0, 128, 192, binding.KVZ_OK)):
         c = binding._CacheStruct(P, 4, D, 1, 8, fmt, fake, fake, 16, fake, fake, fake, fake)
         assert L.kvz_compress_pages(ctypes.byref(c), fake, fake, fake, 0, None) == want, (fmt, P, D)
