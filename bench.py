@@ -62,8 +62,9 @@ def parse():
     # the first ~30 launches after set-up run up to 20 % slower while the clocks settle
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--config", type=int, default=3, help="workload number (3 = the headline workload)")
-    ap.add_argument("--format", choices=["escape", "zipfusion"], default="escape",
-                    help="cache format: exponent offsets with escapes (the library's), or ZipFusion's blocks")
+    ap.add_argument("--format", choices=["escape", "zipfusion", "channel"], default="escape",
+                    help="cache format: exponent offsets with escapes (the library's), ZipFusion's blocks, or "
+                         "the first with channel groups (4 dims over a tile's 16 tokens per base)")
     ap.add_argument("--pages-per-split", type=int, default=0,
                     help="pages per split-K work item (0: the library's choice)")
     ap.add_argument("--batch", type=int, default=None, help="override the workload's batch size")
@@ -130,9 +131,10 @@ def main() -> int:
     kd, vd = t16(kp), t16(vp)
     ids = np.array([w.page_table[r, i] for r in range(B) for i in range(int(L0[r]) // P)], np.int32)
     n_units = len(ids) * H
-    fmt = kvz.FORMAT_ZIPFUSION if args.format == "zipfusion" else kvz.FORMAT_ESCAPE
+    fmt = {"escape": kvz.FORMAT_ESCAPE, "zipfusion": kvz.FORMAT_ZIPFUSION, "channel": kvz.FORMAT_CHANNEL}[args.format]
+    if fmt != kvz.FORMAT_ESCAPE:
+        w.name = f"{w.name}+{args.format}"
     if fmt == kvz.FORMAT_ZIPFUSION:
-        w.name = f"{w.name}+zipfusion"
         pool_cap = (n_units + B * H) * 2 * P * D          # room for every block raw
     else:
         frac = 0.6 if w.k_dist == "log_uniform" else 0.02
@@ -337,7 +339,7 @@ def main() -> int:
     del flush
 
     ceiling = None
-    if fmt == kvz.FORMAT_ESCAPE and not args.no_ceiling:
+    if fmt != kvz.FORMAT_ZIPFUSION and not args.no_ceiling:   # the channel format's units read alike
         ceiling = read_ceiling(kvz, cache, table, lens, full, H, U, args.steps, dev, pair)
 
     layers = layer_loop(kvz, cache, q, table, lens, w, ws, pps, args.graph_layers, dev) if args.graph_layers > 0 else None
@@ -355,7 +357,8 @@ def main() -> int:
     if fmt == kvz.FORMAT_ZIPFUSION:
         kname = f"attn_zf_kernel<{D}>" if mha else "attn_zf_gqa_kernel"
     else:
-        kname = f"attn_mha_kernel<{D}>" if mha else "attn_gqa_kernel"
+        ch = "true" if fmt == kvz.FORMAT_CHANNEL else "false"
+        kname = f"attn_mha_kernel<{D}, {ch}>" if mha else f"attn_gqa_kernel<{ch}>"
     roofline = dict(kernel=kname, bound="hbm",
                     achieved=round(achieved, 1), peak=PEAK_HBM_GBPS, unit="GB/s",
                     frac=round(achieved / PEAK_HBM_GBPS, 4), traffic=traffic,

@@ -185,7 +185,7 @@ __device__ __forceinline__ void k_bases_from_meta(KRaw<D>& r, uint32_t meta, int
 // base byte k of a dword as the term b << 7 | b << 23 of a pair whose two values share it
 template <int k>
 __device__ __forceinline__ uint32_t byte_base_term(uint32_t w) {
-  return __builtin_amdgcn_perm(0u, w, 0x0C000C00u | (uint32_t)(k * 0x00010001)) << 7;
+  return ((w >> (8 * k)) & 0xFFu) * 0x00800080u;
 }
 
 template <int D, bool CH = false>
