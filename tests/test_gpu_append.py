@@ -2,14 +2,14 @@
 tail fills, compresses it into the unit the page table names (ZipFusion summary, §III.D "KV Cache
 Management and Scheduling": partially filled pages stay uncompressed; a full page is compressed).
 The units it writes are byte-exact against the oracle and attention afterwards matches it. Seeded
-random cases run appends across page fills in both cache formats, then a pool compaction that
+random cases run appends across page fills in all three cache formats, then a pool compaction that
 keeps a random half of the requests."""
 import numpy as np
 import pytest
 import torch
 
 import decode_attention_losslessly_amd as kvz
-from oracle import c_oracle
+from oracle import c_oracle, codec
 from synth import make_workload
 
 from kvz_testlib import (DEV, check_rows, decode_units, dev, full_page_ids, host16, lane_maps, oracle_rows, tails,
@@ -105,11 +105,22 @@ def _append_case(seed):
 
 @pytest.mark.parametrize("seed", range(16))
 def test_random_append_and_compaction(seed):
-    """Random shapes and both formats: n appends from lengths L0 (crossing page fills), every full
-    page byte-exact against the oracle and rebuilt bit for bit on every decode route, attention
-    within tolerance; then the pool is compacted to a random half of the requests and their
-    attention is bit-identical."""
+    """Random shapes and the first two formats: n appends from lengths L0 (crossing page fills),
+    every full page byte-exact against the oracle and rebuilt bit for bit on every decode route,
+    attention within tolerance; then the pool is compacted to a random half of the requests and
+    their attention is bit-identical."""
+    _random_append_case(seed)
+
+
+@pytest.mark.parametrize("seed", range(16, 24))
+def test_random_append_and_compaction_channel_groups(seed):
+    """The same random cases with the channel-group format."""
+    _random_append_case(seed, kvz.FORMAT_CHANNEL)
+
+
+def _random_append_case(seed, force_fmt=None):
     cfg, D, P, Hq, Hkv, B, fmt, n, L0 = _append_case(seed)
+    fmt = fmt if force_fmt is None else force_fmt
     what = f"seed {seed}: cfg{cfg} D={D} P={P} {Hq}/{Hkv} B={B} fmt={fmt} n={n} L0={L0.tolist()}"
     print(what, flush=True)
     w = make_workload(cfg, n_append=0, B=B, lens=L0 + n, Hq=Hq, Hkv=Hkv, D=D, P=P)
@@ -137,6 +148,11 @@ def test_random_append_and_compaction(seed):
             for i, pid in enumerate(ids):
                 for h in range(Hkv):
                     assert unit_equal(units[pid, h], pool, ref_units[i, h], ref_pool, P, D), (what, pid, h)
+        elif fmt == kvz.FORMAT_CHANNEL:
+            for pid in ids:
+                for h in range(Hkv):
+                    ref, ref_pool = codec.encode_unit(kp[pid, h], vp[pid, h], geometry=codec.CHANNEL)
+                    assert unit_equal(units[pid, h], pool, ref, ref_pool, P, D), (what, pid, h)
         else:
             for pid in ids:
                 for h in range(Hkv):
@@ -145,7 +161,7 @@ def test_random_append_and_compaction(seed):
                     want, raw = zf.encode_unit(kp[pid, h], vp[pid, h], pool_offset=off)
                     assert got == want, (what, pid, h)
                     assert not raw.size or np.array_equal(pool[off:off + raw.size], raw), (what, pid, h)
-        for lm in (lane_maps(D) if fmt == kvz.FORMAT_ESCAPE else ([0, 1] if D == 128 else [0])):
+        for lm in (lane_maps(D) if fmt != kvz.FORMAT_ZIPFUSION else ([0, 1] if D == 128 else [0])):
             kd, vd = decode_units(cache, ids, Hkv, P, D, lm)
             assert np.array_equal(kd, kp[ids]) and np.array_equal(vd, vp[ids]), (what, lm)
     q = w.q()

@@ -1,7 +1,7 @@
 """kvz_compact_pool: the pool data of the units still in use moves to a new, smaller pool and the
 units point at it; attention of the live requests is bit-identical before and after, with the old
-pool overwritten so that any read of it would show. Both cache formats (escape lists; ZipFusion
-raw blocks), on escape-heavy data. An undersized new pool drops the data of the units that do not
+pool overwritten so that any read of it would show. All three cache formats (escape lists with
+token or channel groups; ZipFusion raw blocks), on escape-heavy data. An undersized new pool drops the data of the units that do not
 fit (status bit set) and nothing reads past a pool. A pool filled exactly to its capacity, ending
 inside a 16-byte chunk, escape-heavy units under grouped-query attention, and splits that start on
 inline units and go on into pool units (both pool routes in one wave) still give attention within
@@ -44,7 +44,7 @@ def _pool_use(cache, w, ids, fmt):
     return total
 
 
-@pytest.mark.parametrize("fmt", [kvz.FORMAT_ESCAPE, kvz.FORMAT_ZIPFUSION])
+@pytest.mark.parametrize("fmt", [kvz.FORMAT_ESCAPE, kvz.FORMAT_ZIPFUSION, kvz.FORMAT_CHANNEL])
 def test_compaction_keeps_live_results(fmt):
     w = make_workload(5, B=4, lens=[70, 45, 100, 33], Hq=4, Hkv=4, D=128)
     kp, vp = w.pages(0), w.pages(1)
@@ -70,7 +70,7 @@ def test_compaction_keeps_live_results(fmt):
     assert not n16[[1, 3]].any()
 
 
-@pytest.mark.parametrize("fmt", [kvz.FORMAT_ESCAPE, kvz.FORMAT_ZIPFUSION])
+@pytest.mark.parametrize("fmt", [kvz.FORMAT_ESCAPE, kvz.FORMAT_ZIPFUSION, kvz.FORMAT_CHANNEL])
 def test_undersized_pool_drops_and_stays_in_bounds(fmt):
     w = make_workload(5, B=2, L=64, Hq=4, Hkv=4, D=128)
     kp, vp = w.pages(0), w.pages(1)
