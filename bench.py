@@ -17,7 +17,7 @@ the split kernel's mean launch duration over --steps launches back to back (`roo
 same for the uncompressed baseline; --rounds rounds of alternated compressed and dense loops
 (`interleaved`); cache-flushed launches; the streaming-read ceiling (`read_ceiling`); the CPU
 oracle on this host (`cpu_baseline`), whose fp64 outputs check the timed call (`parity`: a
-failure exits with status 1); appends.
+failure exits with status 1; for the other cache formats, fp64 rows from the raw pages); appends.
 
 Prints one JSON line. `python bench.py --gpus N` with N > 1 exits with a message: the library
 runs on one GPU.
@@ -369,6 +369,15 @@ def main() -> int:
     cpu = parity = None
     if not args.no_cpu and fmt == kvz.FORMAT_ESCAPE:   # the CPU oracle baseline decodes the library's format
         cpu, ref_rows, ref = cpu_baseline(w, kp, vp, min(args.cpu_requests, B), units_bytes, pool_esc, tail_bytes, log)
+        parity = parity_check(out_bf16.cpu().numpy().view(np.uint16), out32.cpu().numpy(), ref_rows, ref, same_bits,
+                              score_bound_of(w, kp, vp, ref_rows))
+        log(f"parity: {parity}")
+    elif not args.no_cpu:
+        # the other formats: no CPU baseline of their own (the oracle's timed decode is the first
+        # format's), but the timed call is still checked against fp64 rows from the raw pages
+        from oracle import c_oracle
+        ref_rows = [(r, h) for r in range(min(args.cpu_requests, B)) for h in range(Hq)]
+        ref = c_oracle.dense_attention_rows(w.q(), kp, vp, w.page_table, w.seq_lens, w.sm_scale, ref_rows)
         parity = parity_check(out_bf16.cpu().numpy().view(np.uint16), out32.cpu().numpy(), ref_rows, ref, same_bits,
                               score_bound_of(w, kp, vp, ref_rows))
         log(f"parity: {parity}")
