@@ -4,7 +4,8 @@ query groups from 1 to 16 heads, uneven lengths with empty requests and partial 
 value distributions of all five workloads (the escape-stress one included, for the pool paths)
 and every kind of split choice (chosen on the device, fixed, and the ranked schedule forced).
 Each case also rebuilds its units bit for bit through every decode route of the kernels, and runs
-again over the same pages in ZipFusion's block format (multi-head or grouped-query kernel).
+again over the same pages in ZipFusion's block format (multi-head or grouped-query kernel) and
+with channel groups (same schedule, every decode route).
 Each case is drawn from its own seed, so a failure names a reproducible case. A second set draws
 larger batches, longer requests and pages of up to 512 tokens."""
 import numpy as np
@@ -111,3 +112,18 @@ def _check_case(seed, kw, pps):
             torch.cuda.synchronize()
             assert np.array_equal(host16(kd), kp[ids]) and np.array_equal(host16(vd), vp[ids]), \
                 f"{what} zipfusion lane map {lane_map}"
+    # the same pages with channel groups, the same schedule
+    cc, cl = build_cache(w, kp, vp, fmt=kvz.FORMAT_CHANNEL)
+    assert int(cc.status.item()) == 0, what
+    kvz.decode_attention(dev(q), cc, dev(w.page_table), cl, w.sm_scale, out, out32, pages_per_split=pps)
+    torch.cuda.synchronize()
+    assert int(cc.status.item()) == 0, what
+    check_rows(host16(out).reshape(-1, w.D), out32.cpu().numpy().reshape(-1, w.D), ref, what + " channel")
+    if len(ids):
+        for lane_map in ([0, 1, 2, 3] if w.D == 128 else [0, 2]):
+            kd = torch.zeros((len(ids), w.Hkv, w.P, w.D), dtype=torch.int16, device=DEV)
+            vd = torch.zeros_like(kd)
+            kvz.decompress_pages(cc, dev(ids), kd, vd, lane_map=lane_map)
+            torch.cuda.synchronize()
+            assert np.array_equal(host16(kd), kp[ids]) and np.array_equal(host16(vd), vp[ids]), \
+                f"{what} channel lane map {lane_map}"
