@@ -14,6 +14,8 @@ ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 
 def build(verbose: bool = False) -> str:
     pkg, orc = os.path.join(ROOT, "decode_attention_losslessly_amd"), os.path.join(ROOT, "oracle")
+    # gcc is not hipcc, so the HIP runtime header needs to be told which runtime it declares
+    # (the AMD one; this is the only platform the library is built for)
     cmd = ["gcc", "-std=c11", "-O2", "-Wall", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROOT, "include"),
            "-I", os.path.join(ROCM, "include"), SRC, "-L", pkg, "-lkvz", "-L", orc, "-lkvz_oracle",
            "-L", os.path.join(ROCM, "lib"), "-lamdhip64", "-lm",
