@@ -72,6 +72,7 @@ def parse():
     ap.add_argument("--q-heads", type=int, default=None, help="override the workload's query heads")
     ap.add_argument("--kv-heads", type=int, default=None, help="override the workload's KV heads")
     ap.add_argument("--head-dim", type=int, default=None, help="override the workload's head dim (64 or 128)")
+    ap.add_argument("--page-size", type=int, default=None, help="override the workload's page size (a multiple of 16)")
     ap.add_argument("--no-dense", action="store_true", help="skip the uncompressed baseline")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-requests", type=int, default=32, help="requests in the CPU baseline sample")
@@ -117,9 +118,11 @@ def main() -> int:
     log = lambda *a: print("[bench]", *a, file=sys.stderr, flush=True)
     t16 = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16 if a.dtype == np.uint16 else a.dtype)).to(dev)
 
-    w = make_workload(args.config, B=args.batch, L=args.context, Hq=args.q_heads, Hkv=args.kv_heads, D=args.head_dim)
-    if any(a is not None for a in (args.batch, args.context, args.q_heads, args.kv_heads, args.head_dim)):
-        w.name = f"{w.name}@b{w.B}_ctx{int(w.seq_lens.max())}_h{w.Hq}x{w.Hkv}_d{w.D}"
+    w = make_workload(args.config, B=args.batch, L=args.context, Hq=args.q_heads, Hkv=args.kv_heads, D=args.head_dim,
+                      P=args.page_size)
+    if any(a is not None for a in (args.batch, args.context, args.q_heads, args.kv_heads, args.head_dim,
+                                   args.page_size)):
+        w.name = f"{w.name}@b{w.B}_ctx{int(w.seq_lens.max())}_h{w.Hq}x{w.Hkv}_d{w.D}_p{w.P}"
     B, Hq, H, D, P = w.B, w.Hq, w.Hkv, w.D, w.P
     t0 = time.perf_counter()
     kp, vp = w.pages(0), w.pages(1)
@@ -279,10 +282,10 @@ def main() -> int:
         c_merge()
     wall, step_gpu_us = timed_steps(c_split, c_merge, args.steps)
     ms_per_step = wall / args.steps * 1e3
-    # the split size the kernel chose for this batch, and the bytes that follow from it:
-    # page-table entries, q and the partials
-    C_used = kvz.chosen_pages_per_split(ws, B, Hq, H, D, P, w.max_pages, pps)
-    part_bytes, splits_used = partial_bytes(C_used, full)
+    # the split size the kernel chose for this batch (in pages, or in 16-token tiles when it
+    # counted tiles), and the bytes that follow from it: page-table entries, q and the partials
+    C_used, tpp_used = kvz.chosen_split(ws, B, Hq, H, D, P, w.max_pages, pps)
+    part_bytes, splits_used = partial_bytes(C_used, full * tpp_used)
     small_bytes = int(full.sum()) * H * 4 + B * Hq * D * 2 + part_bytes
     comp_bytes = units_bytes + 2 * pool_esc + tail_bytes + small_bytes
     split_mean_us, attn_us, merge_us = launch_stats(c_split, c_merge, args.steps)
@@ -443,7 +446,9 @@ def main() -> int:
         "config": {"workload": w.name, "batch": B, "q_heads": Hq, "kv_heads": H, "head_dim": D,
                    "context": int(w.seq_lens.max()), "page_size": P, "splits": splits_used,
                    "schedule": "ranked" if C_used < 0 else "split",
-                   "pages_per_split": C_used if C_used > 0 else None, "parallelism": "none (1 GPU)"},
+                   "pages_per_split": C_used if C_used > 0 and tpp_used == 1 else None,
+                   "tiles_per_split": C_used if C_used > 0 and tpp_used > 1 else None,
+                   "parallelism": "none (1 GPU)"},
         "compressed_gbps": round(achieved, 1),
         "pct_peak_hbm": round(100 * achieved / PEAK_HBM_GBPS, 2),
         "uncompressed_equiv_gbps": round(dense_kv_bytes / (attn_mean * 1e-6) / 1e9, 1),

@@ -28,7 +28,12 @@ __device__ __forceinline__ int active_splits(int nfull, int C) { return nfull > 
 // that a batch of uneven lengths still fills the GPU in one pass rather than leaving waves idle
 // behind its longest requests. C_lo bounds the splits of one item (the workspace holds S of
 // them); C_lo == C_hi fixes C. The launch's first wave records C after the partials, where the
-// merge reads it.
+// merge reads it, and the plan's tiles per page after it.
+//
+// A plan page is normally one page of the table. The compressed multi-head kernel can also count
+// its splits in 16-token tiles (tpp = P / 16 plan pages per page of the table), so that a batch
+// of few, large pages is not left to one wave per page walking its tiles in a row: a split may
+// then start and end inside a unit.
 struct SplitPlan {
   int S;           // partial slots per (request, query head)
   int C_lo, C_hi;  // bounds on the pages per split
@@ -36,9 +41,15 @@ struct SplitPlan {
   int slots_pref;  // > 0: a smaller wave count to aim for first (see plan_work)
   int ranks;       // > 0: the ranked schedule below may be used, with this many big ranks
   int rank_min;    // ... when a big chunk holds at least this many pages on average (0: always)
-  int* chosen;     // the pages per split used (or minus the chunks per item when ranked),
-                   // written by the launch's first wave
+  int tpp;         // plan pages per page of the table: 1, or P / 16 (splits counted in tiles)
+  int* chosen;     // [0]: the plan pages per split used (or minus the chunks per item when
+                   // ranked), [1]: tpp; written by the launch's first wave
 };
+
+__device__ __forceinline__ void plan_record(const SplitPlan& pl, int C) {
+  pl.chosen[0] = C;
+  pl.chosen[1] = pl.tpp;
+}
 
 constexpr int kLenUnknown = -2147483647 - 1;
 
@@ -94,9 +105,11 @@ __device__ __forceinline__ void rank_range(int np, int k, int R, int& p0, int& p
   p1 = (int)(((uint64_t)np * rank_share(k + 1, R)) >> 20);
 }
 
-__device__ __forceinline__ int plan_pages(int32_t L, int P, int max_pages, bool dense) {
+// plan pages of a request of length L: its pages (every page for the uncompressed baseline,
+// the full ones for the compressed kernels), tpp plan pages to each full page
+__device__ __forceinline__ int plan_pages(int32_t L, int P, int max_pages, bool dense, int tpp = 1) {
   L = L < 0 ? 0 : min(L, max_pages * P);
-  return dense ? (L + P - 1) / P : L / P;
+  return dense ? (L + P - 1) / P : L / P * tpp;
 }
 
 // Pages of the requests, read once: up to kPlanRegs requests per lane are held in registers
@@ -106,18 +119,20 @@ struct PlanPages {
   int np[kPlanRegs];
   int len[kPlanRegs];   // the lengths as read, so that a wave need not load its own again
   bool held;
+  int tpp;              // plan pages per page of the table
 };
 
 __device__ __forceinline__ PlanPages plan_load(const int32_t* seq_lens, int B, int P, int max_pages, bool dense,
-                                               int lane) {
+                                               int lane, int tpp = 1) {
   PlanPages pp;
   pp.held = B <= 64 * kPlanRegs;
+  pp.tpp = tpp;
 #pragma unroll
   for (int j = 0; j < kPlanRegs; ++j) {
     const int r = 64 * j + lane;
     const bool in = pp.held && r < B;
     pp.len[j] = in ? seq_lens[r] : 0;
-    pp.np[j] = in ? plan_pages(pp.len[j], P, max_pages, dense) : -1;
+    pp.np[j] = in ? plan_pages(pp.len[j], P, max_pages, dense, tpp) : -1;
   }
   return pp;
 }
@@ -140,7 +155,7 @@ __device__ __forceinline__ int plan_len(const PlanPages& pp, int r) {
 __device__ __forceinline__ uint32_t plan_splits(const PlanPages& pp, const int32_t* seq_lens, int B, int P,
                                                 int max_pages, bool dense, int r, int j, int C) {
   if (r >= B) return 0u;
-  const int np = pp.held ? pp.np[j] : plan_pages(seq_lens[r], P, max_pages, dense);
+  const int np = pp.held ? pp.np[j] : plan_pages(seq_lens[r], P, max_pages, dense, pp.tpp);
   return (uint32_t)active_splits(np, C);
 }
 
@@ -171,7 +186,8 @@ __device__ __forceinline__ uint64_t plan_page_sum(const PlanPages& pp, const int
   } else {
     for (int b0 = 0; b0 < B; b0 += 64) {
       const int r = b0 + lane;
-      npg += readlane(wave_incl_scan(r < B ? (uint32_t)plan_pages(seq_lens[r], P, max_pages, dense) : 0u), 63);
+      npg += readlane(wave_incl_scan(r < B ? (uint32_t)plan_pages(seq_lens[r], P, max_pages, dense, pp.tpp) : 0u),
+                      63);
     }
   }
   return npg;
@@ -187,7 +203,7 @@ __device__ __forceinline__ uint32_t plan_page_max(const PlanPages& pp, const int
   } else {
     for (int b0 = 0; b0 < B; b0 += 64) {
       const int r = b0 + lane;
-      m = max(m, r < B ? (uint32_t)plan_pages(seq_lens[r], P, max_pages, dense) : 0u);
+      m = max(m, r < B ? (uint32_t)plan_pages(seq_lens[r], P, max_pages, dense, pp.tpp) : 0u);
     }
   }
   return wave_max_u32(m);
@@ -208,7 +224,7 @@ __device__ __forceinline__ bool plan_work(const SplitPlan& pl, const int32_t* se
     // longest requests' chunks would be the longest waves, where the split schedule cuts all
     // work into equal splits) and a big chunk holds at least rank_min pages on average:
     // big share * pages of the batch / (B * R) >= rank_min
-    const PlanPages pp = plan_load(seq_lens, B, P, max_pages, dense, lane);
+    const PlanPages pp = plan_load(seq_lens, B, P, max_pages, dense, lane, pl.tpp);
     bool use = pl.rank_min <= 0;
     if (!use) {
       const uint64_t npg = plan_page_sum(pp, seq_lens, B, P, max_pages, dense, lane);
@@ -218,7 +234,7 @@ __device__ __forceinline__ bool plan_work(const SplitPlan& pl, const int32_t* se
     }
     if (use) {
       const int n = rank_chunks(pl.ranks);
-      if (wave_id == 0 && lane == 0) *pl.chosen = -n;
+      if (wave_id == 0 && lane == 0) plan_record(pl, -n);
       if ((uint64_t)wave_id >= items * n) return false;
       const int j = (int)((uint64_t)wave_id % items);
       w.s = (int)((uint64_t)wave_id / items);
@@ -231,9 +247,9 @@ __device__ __forceinline__ bool plan_work(const SplitPlan& pl, const int32_t* se
   }
   int C = pl.C_lo;
   if (pl.C_hi > pl.C_lo && items >= slots) C = pl.C_hi;   // no split fits: one per item
-  if (C >= max_pages) {
+  if (C >= max_pages * pl.tpp) {
     // every request has exactly one split (an empty one too): numbering is direct
-    if (wave_id == 0 && lane == 0) *pl.chosen = C;
+    if (wave_id == 0 && lane == 0) plan_record(pl, C);
     if ((uint64_t)wave_id >= items) return false;
     w.r = wave_id / ipr;
     w.k = wave_id % ipr;
@@ -242,7 +258,7 @@ __device__ __forceinline__ bool plan_work(const SplitPlan& pl, const int32_t* se
     w.L = kLenUnknown;
     return true;
   }
-  const PlanPages pp = plan_load(seq_lens, B, P, max_pages, dense, lane);
+  const PlanPages pp = plan_load(seq_lens, B, P, max_pages, dense, lane, pl.tpp);
   if (pl.C_hi > pl.C_lo && C < pl.C_hi) {
     // With N = ipr * (pages of the batch) and `items` = ipr * B, the splits at C lie between
     // N / C and N / C + items (the total only falls as C grows): no C below N / s fits s waves,
@@ -274,7 +290,7 @@ __device__ __forceinline__ bool plan_work(const SplitPlan& pl, const int32_t* se
     }
     if (!done) C = smallest_fit(slots);
   }
-  if (wave_id == 0 && lane == 0) *pl.chosen = C;
+  if (wave_id == 0 && lane == 0) plan_record(pl, C);
   // find the request whose splits hold this wave's number, 64 requests at a time
   uint64_t base = 0;
   auto visit = [&](int b0, uint32_t sr) -> bool {

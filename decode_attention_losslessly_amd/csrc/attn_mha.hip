@@ -112,22 +112,26 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) __attribute__((amdgpu_waves_pe
   }
   int nfull = L / P;
   const int rows = L % P;
+  const int T = P / kTile;
+  const int tpp = plan.tpp;   // plan pages per page: 1, or T when the splits count tiles
   // the splits the plan and the merge count for this row; with no unit slots every full page is
   // a bad id and is skipped, but every counted split still writes its (empty) partial
-  const int Sr = C < 0 ? -C : active_splits(nfull, C);
+  const int Sr = C < 0 ? -C : active_splits(nfull * tpp, C);
   if (num_pages <= 0 && nfull > 0) {
     if (lane == 0 && s == 0 && hq == 0) atomicOr(status, kStatusBadPage);
     nfull = 0;
   }
   const bool ranked = C < 0;
   if (s >= Sr) return;
-  int p0, p1;
+  int p0, p1;   // plan pages
   if (ranked) {
-    rank_range(nfull, s, plan.ranks, p0, p1);
+    rank_range(nfull * tpp, s, plan.ranks, p0, p1);
   } else {
     p0 = s * C;
-    p1 = min(p0 + C, nfull);
+    p1 = min(p0 + C, nfull * tpp);
   }
+  // the split's tiles [a0, a1), counted over the request's full pages
+  const int a0 = p0 * (T / tpp), a1 = max(p0, p1) * (T / tpp);
   const size_t slot = ((size_t)r * Hq + hq) * S + s;
 
   MhaState<D> st;
@@ -142,9 +146,16 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) __attribute__((amdgpu_waves_pe
 #pragma unroll
   for (int i = 0; i < D / 64; ++i) st.acc[i] = 0.f;
   const int32_t* pt_row = page_table + (size_t)r * max_pages;
-  const int T = P / kTile;
-  const int nsteps = (p1 > p0 ? p1 - p0 : 0) * T;
-  uint32_t krank = 0, vrank = 0;
+  const int nsteps = a1 - a0;
+  // escape cursors of the split's first tile: 0 at a unit's start, else the escapes of the
+  // unit's tiles before it
+  uint32_t krank0 = 0, vrank0 = 0;
+  if (nsteps > 0 && a0 % T != 0) {
+    const int pid = sload<int32_t>(pt_row + a0 / T);
+    if (pid >= 0 && pid < num_pages)
+      escapes_before<D>(units + ((size_t)pid * H + h) * unit_bytes(P, D), P, a0 % T, lane, krank0, vrank0);
+  }
+  uint32_t krank = krank0, vrank = vrank0;
   int first_skip = -1, last_skip = -1;
   int nskip = 0;          // tiles skipped by the main loop
   int resume = -1;        // step from which the pool-capable loop takes over
@@ -170,7 +181,7 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) __attribute__((amdgpu_waves_pe
         resume = 0;
         first_skip = last_skip = -1;
       } else {
-        resume = (stg.page - p0 + 1) * T;
+        resume = (stg.page + 1) * T - a0;
       }
     }
   };
@@ -182,7 +193,7 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) __attribute__((amdgpu_waves_pe
   if (nsteps > 0 && resume < 0) {
     // load cursor: step ln = (page lp, tile lt); it stays on the last step once there, and the
     // stages issued past the end (never computed) read nothing (`live` false)
-    int ln = 0, lp = p0, lt = 0;
+    int ln = 0, lp = a0 / T, lt = a0 % T;
     bool live = true;
     const int last = nsteps - 1;
     auto advance = [&]() {
@@ -217,22 +228,26 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) __attribute__((amdgpu_waves_pe
     // the rest of the split, every unit as it comes; the next tile's meta window is in flight
     // while a tile is computed
     auto unit_of = [&](int n, bool& ok) {
-      const int pid = sload<int32_t>(pt_row + p0 + n / T);
+      const int pid = sload<int32_t>(pt_row + (a0 + n) / T);
       ok = pid >= 0 && pid < num_pages;
       return units + ((size_t)(ok ? pid : 0) * H + h) * unit_bytes(P, D);
     };
+    if (resume == 0) {   // from the split's first tile again
+      krank = krank0;
+      vrank = vrank0;
+    }
     bool ok;
     const uint8_t* u = unit_of(resume, ok);
-    uint32_t meta = load_meta(u, P, D, resume % T, lane);
+    uint32_t meta = load_meta(u, P, D, (a0 + resume) % T, lane);
     for (int n = resume; n < nsteps; ++n) {
       bool nok = true;
       const uint8_t* nu = u;
       uint32_t nmeta = 0;
       if (n + 1 < nsteps) {
         nu = unit_of(n + 1, nok);
-        nmeta = load_meta(nu, P, D, (n + 1) % T, lane);
+        nmeta = load_meta(nu, P, D, (a0 + n + 1) % T, lane);
       }
-      if (ok) mha_any_tile<D, CH>(st, u, meta, P, n % T, krank, vrank, lds, pool, pool_cap, scale, lane);
+      if (ok) mha_any_tile<D, CH>(st, u, meta, P, (a0 + n) % T, krank, vrank, lds, pool, pool_cap, scale, lane);
       bad |= !ok;
       u = nu;
       ok = nok;
@@ -241,10 +256,16 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) __attribute__((amdgpu_waves_pe
   }
   if (bad && lane == 0) atomicOr(status, kStatusBadPage);
   if (first_skip >= 0) {
-    // units whose escapes are in the pool: the recorded pages, then any between them
+    // units whose escapes are in the pool: the recorded pages, then any between them (the
+    // split's tiles of each: its first page may begin and its last end inside the unit)
     auto do_page = [&](int page) {
       const int pid = sload<int32_t>(pt_row + page);
-      for (int t = 0; t < T; ++t) {
+      const int tb = max(0, a0 - page * T), te = min(T, a1 - page * T);
+      if (tb > 0) {
+        krank = krank0;
+        vrank = vrank0;
+      }
+      for (int t = tb; t < te; ++t) {
         MhaStage<D> a;
         mha_issue<D, CH>(a, units, pid, page, t, H, h, P, num_pages, lane);
         mha_compute<D, true, CH>(st, a, P, krank, vrank, lds, pool, pool_cap, scale, lane);

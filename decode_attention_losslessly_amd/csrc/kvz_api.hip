@@ -114,12 +114,47 @@ int rank_count(int B, int Hq, int Hkv, int max_pages, int pps) {
   return R;
 }
 
-// split slots per (request, query head): the dynamic schedule's bound, and the ranked one's
-// chunks per row
+constexpr int64_t kTileSplitWaves = 2048;
+
+// Tiles per plan page of the compressed multi-head kernel. With pages of more than one tile and
+// a batch whose items, even at the table's full width, hold fewer than kTileSplitWaves pages,
+// splits of whole pages would leave most of the GPU idle while each wave walks a page's tiles in
+// a row (256-token pages: 16 tiles). That kernel can start and end a split inside a unit, so
+// there its splits are counted in 16-token tiles. The other kernels, a fixed split size
+// (pps > 0) and the ranked schedule keep whole pages, and so does a batch with pages enough
+// (1 x 32 heads x 4K tokens in 64-token pages: 2,048 splits of one page, 12.2 us, against
+// 12.6 us counted in tiles, whose split-size search then only costs time).
+int split_tiles(int B, int Hq, int Hkv, int D, int P, int max_pages, int pps) {
+  if (pps != 0 || P <= kvz::kTile || (Hq != Hkv && D == 128)) return 1;
+  if (work_items_per_split(B, Hq, Hkv, D) * (int64_t)max_pages >= kTileSplitWaves) return 1;
+  return P / kvz::kTile;
+}
+
+// Smallest split, in tiles, when splits are counted in tiles: the fewest tiles whose splits,
+// over the batch's items at the table's full width, come to at most kTileSplitWaves. A split
+// that starts inside a unit first counts the escapes of the unit's earlier tiles (their offset
+// codes: a third of their bytes), so short splits cost extra reads as well as their start-up.
+// Measured (whole decode step, 1 x 2 heads x one 256-token page, and 1 x 32 heads x 4K tokens in
+// 256-token pages): 1 tile 11.9 and 38.1 us, 2 tiles 12.9 and 30.6, 4 tiles 16.1 and 28.1 (the
+// second with whole pages per split: 52.5); the best of each is the one with at most 2,048 waves.
+int tile_split_min(int B, int Hq, int Hkv, int D, int max_pages, int tpp) {
+  const int64_t tiles = work_items_per_split(B, Hq, Hkv, D) * (int64_t)max_pages * tpp;
+  const int64_t c = (tiles + kTileSplitWaves - 1) / kTileSplitWaves;
+  return (int)(c < 1 ? 1 : c);
+}
+
+// split slots per (request, query head): the dynamic schedule's bound (in pages, or in tiles
+// where the multi-head kernel counts tiles), and the ranked one's chunks per row
 int slot_count(int B, int Hq, int Hkv, int D, int P, int max_pages, int pps) {
-  const int S = split_count(max_pages, pages_per_split(B, Hq, Hkv, D, P, max_pages, pps));
+  int S = split_count(max_pages, pages_per_split(B, Hq, Hkv, D, P, max_pages, pps));
   const int n = kvz::rank_chunks(rank_count(B, Hq, Hkv, max_pages, pps));
-  return n > S ? n : S;
+  if (n > S) S = n;
+  const int t = split_tiles(B, Hq, Hkv, D, P, max_pages, pps);
+  if (t > 1) {
+    const int St = split_count(max_pages * t, tile_split_min(B, Hq, Hkv, D, max_pages, t));
+    if (St > S) S = St;
+  }
+  return S;
 }
 
 // the format's shapes: an inline escape keeps its storage position in 16 bits, so a block holds at
@@ -226,6 +261,7 @@ static kvz::SplitPlan make_plan(int C, int S, int max_pages, bool fixed, int32_t
   p.slots_pref = 0;
   p.ranks = 0;   // the ranked schedule: set only for the kernel that implements it
   p.rank_min = 0;
+  p.tpp = 1;
   p.chosen = chosen;
   return p;
 }
@@ -297,8 +333,15 @@ int kvz_decode_attention_splits(const uint16_t* q, const kvz_cache* c, const int
                              seq_lens, B, H_q, H, D, P, c->num_pages, plan, scale, ws_acc, ws_ml, c->status,
                              as_stream(stream));
   } else if (!gqa) {
-    plan.ranks = rank_count(B, H_q, H, max_pages, pps);
-    plan.rank_min = pps < 0 ? 0 : kRankMinPages;
+    const int tpp = split_tiles(B, H_q, H, D, P, max_pages, pps);
+    if (tpp > 1) {   // splits counted in tiles
+      plan = make_plan(tile_split_min(B, H_q, H, D, max_pages, tpp), S, max_pages * tpp, false,
+                       ws_chosen(workspace, B, H_q, S, D));
+      plan.tpp = tpp;
+    } else {
+      plan.ranks = rank_count(B, H_q, H, max_pages, pps);
+      plan.rank_min = pps < 0 ? 0 : kRankMinPages;
+    }
     rc = kvz::launch_attn_mha(q, c->units, c->esc_pool, c->esc_capacity, c->esc_cursor, c->k_tail, c->v_tail,
                               page_table, max_pages, seq_lens, B, H_q, H, D, P, c->num_pages, plan, scale, ws_acc,
                               ws_ml, c->status, c->format == KVZ_FORMAT_CHANNEL, as_stream(stream));

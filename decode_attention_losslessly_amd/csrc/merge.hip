@@ -2,8 +2,8 @@
 // (the pages merge split results after attention and count the merge in its time: ZipFusion
 // summary, §IV.B "Attention Kernel Performance").
 //   M = max_s m_s,  w_s = 2^(m_s - M),  o = sum_s w_s acc_s / sum_s w_s l_s
-// The pages per split that the split kernel used (or its chunk count, when it used the ranked
-// schedule) are read from where it recorded them.
+// The plan pages per split that the split kernel used (or its chunk count, when it used the
+// ranked schedule) and its plan pages per page of the table are read from where it recorded them.
 // Output in BF16 (round to nearest even) and optionally in fp32; zeros when the request is empty.
 //
 // W waves per row: each takes the splits s = w, w + W, ... in one pass, eight at a time (all 8
@@ -33,8 +33,9 @@ __global__ __launch_bounds__(64 * W * R) void merge_kernel(const float* __restri
   const int r = row / Hq;
   int L = sload<int32_t>(seq_lens + r);
   L = L < 0 ? 0 : min(L, max_pages * P);
-  const int npages = dense ? (L + P - 1) / P : L / P;
   const int c = sload<int32_t>(chosen);   // < 0: the split kernel used -c ranked chunks
+  const int tpp = max(1, sload<int32_t>(chosen + 1));   // plan pages per page of the table
+  const int npages = dense ? (L + P - 1) / P : L / P * tpp;
   const int Sr = min(c < 0 ? -c : active_splits(npages, max(1, c)), S);
   const float* ml = ws_ml + (size_t)row * S * 2;
   const float* acc = ws_acc + (size_t)row * S * D;

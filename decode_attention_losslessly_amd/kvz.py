@@ -174,13 +174,21 @@ def num_splits(B, Hq, Hkv, D, P, max_pages, pages_per_split=0) -> int:
     return int(lib().kvz_num_splits(B, Hq, Hkv, D, P, max_pages, pages_per_split))
 
 
-def chosen_pages_per_split(workspace: torch.Tensor, B, Hq, Hkv, D, P, max_pages, pages_per_split=0) -> int:
-    """Pages per split the last split kernel run on `workspace` used, or minus its chunks per
-    (request, query head) when it used the ranked schedule (read back from the slot after the
-    partials; synchronises with the device)."""
+def chosen_split(workspace: torch.Tensor, B, Hq, Hkv, D, P, max_pages, pages_per_split=0) -> tuple[int, int]:
+    """What the last split kernel run on `workspace` recorded in the slot after the partials:
+    (plan pages per split, or minus its chunks per (request, query head) when it used the ranked
+    schedule; plan pages per page of the table, P // 16 when it counted its splits in 16-token
+    tiles, else 1). Synchronises with the device."""
     S = num_splits(B, Hq, Hkv, D, P, max_pages, pages_per_split)
     off = B * Hq * S * (D + 2) * 4
-    return int(workspace[off:off + 4].view(torch.int32).item())
+    c, tpp = workspace[off:off + 8].view(torch.int32).tolist()
+    return int(c), int(tpp)
+
+
+def chosen_pages_per_split(workspace: torch.Tensor, B, Hq, Hkv, D, P, max_pages, pages_per_split=0) -> int:
+    """The first element of chosen_split: plan pages per split (pages, or 16-token tiles when the
+    kernel counted tiles), or minus the chunks per row under the ranked schedule."""
+    return chosen_split(workspace, B, Hq, Hkv, D, P, max_pages, pages_per_split)[0]
 
 
 # ---------------------------------------------------------------- cache

@@ -89,6 +89,21 @@ def test_split_geometry():
     assert kvz.num_splits(1, 32, 32, 128, 16, 256) >= 32
 
 
+def test_tile_split_slots():
+    # Pages of several 16-token tiles that give fewer than 2,048 (item, page) waves at the table's
+    # full width: the multi-head kernel counts its splits in tiles, each at least the fewest tiles
+    # that keep the splits at full width to 2,048 waves, and the workspace holds those slots.
+    # Grouped queries at head dim 128, fixed split sizes and batches with pages enough keep
+    # whole pages.
+    assert kvz.num_splits(1, 2, 2, 64, 256, 1) == 16            # 32 tiles: 1-tile splits
+    assert kvz.num_splits(1, 32, 32, 128, 256, 16) == 64        # 8,192 tiles: 4-tile splits, 256 / 4
+    assert kvz.num_splits(1, 32, 32, 128, 128, 32) == 64        # 1,024 pages of 8 tiles: 4-tile splits
+    assert kvz.num_splits(1, 32, 32, 128, 64, 64) == 64         # 2,048 pages: one page a split
+    assert kvz.num_splits(1, 32, 8, 128, 256, 16) == 16         # grouped queries: whole pages
+    assert kvz.num_splits(1, 2, 2, 64, 256, 1, pages_per_split=1) == 1
+    assert kvz.workspace_bytes(1, 2, 2, 64, 256, 1) == 2 * 16 * (64 + 2) * 4 + 16
+
+
 def test_ranked_slots_reserved_only_when_usable():
     # Multi-head calls reserve slots for the ranked schedule's chunks (two per big rank, R big
     # ranks from about 4096 waves over the batch's items) only when requests of the table's full
