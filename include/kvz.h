@@ -145,8 +145,16 @@ int32_t kvz_inline_capacity(int32_t P, int32_t D);
 
 /* Bytes of scratch kvz_decode_attention / kvz_decode_attention_dense need: split partials
  * (acc[D], m, l) in float for every (request, query head, split slot), then 16 bytes where the
- * split kernel records the pages per split it used (or minus its chunks per row, below), for
- * the merge. Its content needs no initialisation.
+ * split kernel records, for the merge, the plan pages per split it used (or minus its chunks per
+ * row, below) and the plan pages per page of the table (int32 each). Its content needs no
+ * initialisation. A plan page is a page of the table, except where the multi-head kernel over
+ * the compressed cache (KVZ_FORMAT_ESCAPE, KVZ_FORMAT_CHANNEL; not grouped queries at head dim
+ * 128) counts its splits in 16-token tiles: with P > 16, pages_per_split = 0, and fewer than
+ * 2048 pages over the batch's (request, query head) rows at the table's full width, a plan page
+ * is a tile (P / 16 to a page), splits may start and end inside a unit, and the smallest split
+ * is the fewest tiles whose splits at full width come to at most 2048 (ZipFusion summary,
+ * §III.C: the kernel rebuilds a tile from its own bytes; a split that starts inside a unit
+ * first counts the escapes of the unit's earlier tiles).
  *   pages_per_split > 0  fixes the pages per split.
  *   pages_per_split = 0  lets the kernels choose per call from the sequence lengths: the
  *                        smallest split, no smaller than a bound the library sets from the
