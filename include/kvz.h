@@ -152,9 +152,8 @@ int32_t kvz_inline_capacity(int32_t P, int32_t D);
  * 128) counts its splits in 16-token tiles: with P > 16, pages_per_split = 0, and fewer than
  * 2048 pages over the batch's (request, query head) rows at the table's full width, a plan page
  * is a tile (P / 16 to a page), splits may start and end inside a unit, and the smallest split
- * is the fewest tiles whose splits at full width come to at most 2048 (ZipFusion summary,
- * §III.C: the kernel rebuilds a tile from its own bytes; a split that starts inside a unit
- * first counts the escapes of the unit's earlier tiles).
+ * is the fewest tiles whose splits at full width come to at most 2048 (a split that starts
+ * inside a unit first counts the escapes of the unit's earlier tiles, which locate its own).
  *   pages_per_split > 0  fixes the pages per split.
  *   pages_per_split = 0  lets the kernels choose per call from the sequence lengths: the
  *                        smallest split, no smaller than a bound the library sets from the
